@@ -1,0 +1,277 @@
+"""Seeded synthetic inputs for the varlen attention forward pass.
+
+This module only draws inputs: packed bf16 Q/K/V tensors and the
+``cu_seqlens`` offsets that split them into segments.  It holds none of the
+attention arithmetic, so both the fp64 oracle (under ``oracle/``) and the HIP
+path can consume its tensors without sharing any compute code.
+
+Shapes follow the workloads on the pages:
+
+* ViT / multimodal-encoder attention: 16 heads, head dims 64/72/80/128,
+  non-causal, full and windowed layouts, image token counts from the warmup
+  candidate list {64, 256, 576, 1024, 2304, 4096, 9216, 16384, 36864, 65536}
+  (vLLM PR "FA4 attention for ViT", section (2), kernel_warmup) and the ViT
+  speed tables (SGLang PR #41344, "Speed Tests and Profiling").
+* MLA prefill: causal, qk head dim 192 = 128 nope + 64 rope, v head dim 128,
+  softmax scale 192^-0.5 (vLLM MLA prefill docs, FA4MLAPrefillKernel.dispatch
+  and FlashAttnPrefillBackend.supports_mla_dimensions).
+
+All values are standard normal draws rounded to bf16.  Generation always runs
+on the CPU with a ``torch.Generator`` so that every machine sees bit-identical
+inputs; callers move the tensors to the GPU themselves.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional, Sequence
+
+import torch
+
+VIT_SEQLEN_CHOICES = (576, 1024, 2304, 4096)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """A named synthetic configuration.
+
+    ``seqlens_q``/``seqlens_k`` list the per-segment lengths in packing order.
+    ``window`` is ``(left, right)`` with -1 meaning unbounded on that side.
+    """
+
+    name: str
+    seed: int
+    seqlens_q: tuple
+    seqlens_k: tuple
+    num_heads: int
+    head_dim_qk: int
+    head_dim_v: int
+    causal: bool
+    window: tuple = (-1, -1)
+    return_lse: bool = True
+    softmax_scale: Optional[float] = None
+    description: str = ""
+
+    @property
+    def batch(self) -> int:
+        return len(self.seqlens_q)
+
+    @property
+    def total_q(self) -> int:
+        return int(sum(self.seqlens_q))
+
+    @property
+    def total_k(self) -> int:
+        return int(sum(self.seqlens_k))
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return int(max(self.seqlens_q)) if self.seqlens_q else 0
+
+    @property
+    def max_seqlen_k(self) -> int:
+        return int(max(self.seqlens_k)) if self.seqlens_k else 0
+
+    @property
+    def scale(self) -> float:
+        if self.softmax_scale is not None:
+            return float(self.softmax_scale)
+        return self.head_dim_qk ** -0.5
+
+
+def _vit_full_seqlens(seed: int) -> tuple:
+    g = torch.Generator().manual_seed(seed)
+    idx = torch.randint(0, len(VIT_SEQLEN_CHOICES), (8,), generator=g)
+    return tuple(VIT_SEQLEN_CHOICES[i] for i in idx.tolist())
+
+
+def _named_workloads() -> dict:
+    vit_full = _vit_full_seqlens(2)
+    ws = [
+        Workload(
+            name="tiny_varlen_d64",
+            seed=1,
+            seqlens_q=(64, 256),
+            seqlens_k=(64, 256),
+            num_heads=16,
+            head_dim_qk=64,
+            head_dim_v=64,
+            causal=False,
+            description="2 packed segments [64, 256], 16 heads, d=64, non-causal",
+        ),
+        Workload(
+            name="vit_full_d80",
+            seed=2,
+            seqlens_q=vit_full,
+            seqlens_k=vit_full,
+            num_heads=16,
+            head_dim_qk=80,
+            head_dim_v=80,
+            causal=False,
+            description="8 ViT images, lengths drawn from {576,1024,2304,4096} "
+            "(seed 2), 16 heads, d=80, non-causal",
+        ),
+        Workload(
+            name="vit_window256_d80",
+            seed=3,
+            seqlens_q=(256,) * 36,
+            seqlens_k=(256,) * 36,
+            num_heads=16,
+            head_dim_qk=80,
+            head_dim_v=80,
+            causal=False,
+            description="one 9216-token image as 36 block-diagonal windows of "
+            "256 tokens, 16 heads, d=80",
+        ),
+        Workload(
+            name="vit_long65536_d128",
+            seed=4,
+            seqlens_q=(65536,),
+            seqlens_k=(65536,),
+            num_heads=16,
+            head_dim_qk=128,
+            head_dim_v=128,
+            causal=False,
+            description="one 65536-token image, 16 heads, d=128, non-causal",
+        ),
+        Workload(
+            name="mla_causal_192_128",
+            seed=5,
+            seqlens_q=(4096,) * 4,
+            seqlens_k=(4096,) * 4,
+            num_heads=128,
+            head_dim_qk=192,
+            head_dim_v=128,
+            causal=True,
+            description="MLA-style causal prefill, 4 x 4096 tokens, 128 heads, "
+            "qk dim 192 (128 nope + 64 rope), v dim 128, LSE returned",
+        ),
+    ]
+    return {w.name: w for w in ws}
+
+
+WORKLOADS = _named_workloads()
+WORKLOAD_ORDER = (
+    "tiny_varlen_d64",
+    "vit_full_d80",
+    "vit_window256_d80",
+    "vit_long65536_d128",
+    "mla_causal_192_128",
+)
+
+
+def cu_seqlens(seqlens: Sequence[int]) -> torch.Tensor:
+    """Exclusive prefix offsets ``[0, L0, L0+L1, ...]`` as int32 (CPU)."""
+    out = [0]
+    for n in seqlens:
+        out.append(out[-1] + int(n))
+    return torch.tensor(out, dtype=torch.int32)
+
+
+@dataclasses.dataclass
+class Inputs:
+    q: torch.Tensor  # [total_q, H, d_qk] bf16
+    k: torch.Tensor  # [total_k, H, d_qk] bf16
+    v: torch.Tensor  # [total_k, H, d_v] bf16
+    cu_seqlens_q: torch.Tensor  # [B+1] int32
+    cu_seqlens_k: torch.Tensor  # [B+1] int32
+    max_seqlen_q: int
+    max_seqlen_k: int
+    softmax_scale: float
+    causal: bool
+    window: tuple
+
+    def to(self, device) -> "Inputs":
+        return dataclasses.replace(
+            self,
+            q=self.q.to(device),
+            k=self.k.to(device),
+            v=self.v.to(device),
+            cu_seqlens_q=self.cu_seqlens_q.to(device),
+            cu_seqlens_k=self.cu_seqlens_k.to(device),
+        )
+
+
+def make_inputs(
+    seqlens_q: Sequence[int],
+    seqlens_k: Sequence[int],
+    num_heads: int,
+    head_dim_qk: int,
+    head_dim_v: int,
+    seed: int,
+    causal: bool = False,
+    window: tuple = (-1, -1),
+    softmax_scale: Optional[float] = None,
+    std: float = 1.0,
+) -> Inputs:
+    """Draw Q, K, V ~ N(0, std^2) in float32 (in that order) and round to bf16."""
+    assert len(seqlens_q) == len(seqlens_k)
+    g = torch.Generator().manual_seed(seed)
+    tq, tk = int(sum(seqlens_q)), int(sum(seqlens_k))
+    q = torch.randn((tq, num_heads, head_dim_qk), generator=g, dtype=torch.float32)
+    k = torch.randn((tk, num_heads, head_dim_qk), generator=g, dtype=torch.float32)
+    v = torch.randn((tk, num_heads, head_dim_v), generator=g, dtype=torch.float32)
+    if std != 1.0:
+        q, k, v = q * std, k * std, v * std
+    scale = head_dim_qk ** -0.5 if softmax_scale is None else float(softmax_scale)
+    return Inputs(
+        q=q.to(torch.bfloat16),
+        k=k.to(torch.bfloat16),
+        v=v.to(torch.bfloat16),
+        cu_seqlens_q=cu_seqlens(seqlens_q),
+        cu_seqlens_k=cu_seqlens(seqlens_k),
+        max_seqlen_q=int(max(seqlens_q)) if len(seqlens_q) else 0,
+        max_seqlen_k=int(max(seqlens_k)) if len(seqlens_k) else 0,
+        softmax_scale=scale,
+        causal=causal,
+        window=tuple(window),
+    )
+
+
+def workload_inputs(w: Workload) -> Inputs:
+    """The seeded tensors of a named workload (the seed is part of ``w``)."""
+    if w.name == "vit_full_d80":
+        # Keep the generator stream identical to drawing the lengths first and
+        # then Q, K, V from the same generator.
+        g = torch.Generator().manual_seed(w.seed)
+        torch.randint(0, len(VIT_SEQLEN_CHOICES), (8,), generator=g)
+        return _draw_with(g, w)
+    g = torch.Generator().manual_seed(w.seed)
+    return _draw_with(g, w)
+
+
+def _draw_with(g: torch.Generator, w: Workload) -> Inputs:
+    q = torch.randn((w.total_q, w.num_heads, w.head_dim_qk), generator=g, dtype=torch.float32)
+    q = q.to(torch.bfloat16)
+    k = torch.randn((w.total_k, w.num_heads, w.head_dim_qk), generator=g, dtype=torch.float32)
+    k = k.to(torch.bfloat16)
+    v = torch.randn((w.total_k, w.num_heads, w.head_dim_v), generator=g, dtype=torch.float32)
+    v = v.to(torch.bfloat16)
+    return Inputs(
+        q=q,
+        k=k,
+        v=v,
+        cu_seqlens_q=cu_seqlens(w.seqlens_q),
+        cu_seqlens_k=cu_seqlens(w.seqlens_k),
+        max_seqlen_q=w.max_seqlen_q,
+        max_seqlen_k=w.max_seqlen_k,
+        softmax_scale=w.scale,
+        causal=w.causal,
+        window=w.window,
+    )
+
+
+def random_seqlens(seed: int, batch: int, lo: int, hi: int) -> List[int]:
+    """``batch`` lengths drawn uniformly from ``[lo, hi]`` (inclusive)."""
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(lo, hi + 1, (batch,), generator=g).tolist()
+
+
+def with_guard_rows(x: torch.Tensor, rows: int = 256, value: float = math.nan) -> torch.Tensor:
+    """A view of ``x`` whose storage is followed by ``rows`` rows of ``value``.
+
+    Used to check that no kernel reads past the last packed row: any such read
+    pulls NaN into the result.
+    """
+    pad = torch.full((rows,) + tuple(x.shape[1:]), value, dtype=x.dtype, device=x.device)
+    return torch.cat([x, pad], dim=0)[: x.shape[0]]

@@ -1,0 +1,152 @@
+/*
+ * varlen_attn.h -- C interface of the MI355X (gfx950) fused variable-length
+ * attention forward pass.
+ *
+ * The operation.  For sequences packed back to back along the token axis and
+ * delimited by prefix offsets cu_seqlens, for every segment b and head h:
+ *
+ *     O   = softmax(scale * Q K^T + mask) V          (bf16 out, fp32 math)
+ *     LSE = ln sum_j exp(scale * q . k_j)            (fp32, per query row)
+ *
+ * This is the forward computed by FA4's flash_attn_varlen_func as the vLLM
+ * MLA-prefill docs page ("vllm.v1.attention.backends.mla.prefill.flash_attn",
+ * FA4MLAPrefillKernel.dispatch and FlashAttnPrefillBackend) calls it: packed
+ * q/k/v of shape [total, heads, dim], cu_seqlens_q/k of shape [batch + 1],
+ * max_seqlen_q/k, softmax_scale (default qk_head_dim^-0.5), causal,
+ * window_size, an optional caller-provided out and an optional LSE.  The
+ * same call serves ViT encoder attention (non-causal, no LSE, 16 heads,
+ * head dims 64/72/80/128; SGLang PR #41344, "Speed Tests and Profiling")
+ * and MLA prefill (causal, qk head dim 192 = 128 nope + 64 rope, v head dim
+ * 128; vLLM docs page, FlashAttnPrefillBackend.supports_mla_dimensions).
+ *
+ * Masking (readings where the pages are silent):
+ *   - query row i of a segment with Lq queries and Lk keys sits at key
+ *     position p = i + Lk - Lq (bottom-right alignment, so chunked prefill
+ *     with q < k lets the new queries see the whole context);
+ *   - causal: key j is visible only if j <= p;
+ *   - window (left, right): visible only if p - left <= j <= p + right,
+ *     -1 meaning unbounded on that side; causal caps the right side at p;
+ *   - a row that sees no key gets O = 0 and LSE = -inf.
+ *
+ * Execution.  Every call enqueues at most one kernel on `stream` and returns
+ * without synchronising, allocating device memory, or reading cu_seqlens on
+ * the host, so it may be recorded into a HIP graph.  The library keeps no
+ * state and no pointer between calls; it is reentrant.
+ *
+ * Errors.  Arguments are validated on the host before any HIP call; a
+ * failing check returns a negative VA_ERR_* code and nothing is launched.
+ * VA_ERR_LAUNCH reports a failed kernel launch.  Nothing is printed and
+ * nothing aborts.  varlen_attn_status_string() names every code.
+ */
+#ifndef VARLEN_ATTN_H
+#define VARLEN_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VA_OK 0
+#define VA_ERR_NULL (-1)    /* a required pointer is NULL */
+#define VA_ERR_SHAPE (-2)   /* rows/heads disagree between tensors, or sizes out of range */
+#define VA_ERR_HEADDIM (-3) /* (head_dim_qk, head_dim_v) is not a supported pair */
+#define VA_ERR_STRIDE (-4)  /* a stride is not positive */
+#define VA_ERR_ALIGN (-5)   /* a pointer or stride breaks the 16-byte alignment rule */
+#define VA_ERR_ARG (-6)     /* a scalar argument is out of range */
+#define VA_ERR_LAUNCH (-7)  /* the HIP kernel launch failed */
+
+/*
+ * A packed bf16 tensor [rows, heads, dim] in device memory.  Element (t, h, c)
+ * lives at data + t * row_stride + h * head_stride + c (strides in elements;
+ * the last dimension is contiguous).  `data`, row_stride and head_stride must
+ * be multiples of 16 bytes (8 elements).  Strided views are accepted, e.g. V
+ * interleaved with the nope part of K as in MLA (vLLM docs page,
+ * FA4MLAPrefillKernel.dispatch, v_stride = (H * (nope + v), nope + v, 1)).
+ * The caller owns the memory.
+ */
+typedef struct va_tensor {
+  void* data;
+  int64_t rows;
+  int32_t heads;
+  int32_t dim;
+  int64_t row_stride;
+  int64_t head_stride;
+} va_tensor;
+
+/*
+ * varlen_attn_fwd -- fused varlen attention forward.
+ *
+ *   q, k, v        bf16 [total_q, H, d_qk], [total_k, H, d_qk], [total_k, H, d_v]
+ *   cu_seqlens_q   device int32 [batch + 1]: segment b owns q rows
+ *                  [cu_seqlens_q[b], cu_seqlens_q[b + 1]); same for _k
+ *   batch          number of segments (>= 0)
+ *   max_seqlen_q   host upper bound on every segment's query count (>= 0);
+ *                  sizes the grid only
+ *   max_seqlen_k   host upper bound on every segment's key count (>= 0)
+ *   softmax_scale  finite, > 0 (the Python layer defaults it to d_qk^-0.5)
+ *   causal         0 or 1
+ *   window_left,
+ *   window_right   >= 0, or -1 for unbounded
+ *   out            bf16 [total_q, H, d_v], written only on rows that belong
+ *                  to a segment; other rows are left untouched
+ *   lse            NULL (not computed) or device fp32 [H, total_q] contiguous:
+ *                  lse[h * total_q + t]; rows outside every segment untouched
+ *   stream         hipStream_t (NULL = the default stream)
+ *
+ * Supported (d_qk, d_v): (64,64), (72,72), (80,80), (128,128), (192,128).
+ * Heads: k->heads == v->heads == out->heads == q->heads (no grouped KV).
+ *
+ * Preconditions that are documented but not checked (checking would need a
+ * device-to-host copy): cu_seqlens are non-decreasing and start at 0; every
+ * segment's rows lie inside the tensors; every segment has at most
+ * max_seqlen_q queries (rows past that bound are not computed); inputs are
+ * finite; out and lse do not overlap the inputs.
+ *
+ * Returns VA_OK or a VA_ERR_* code.  batch == 0, max_seqlen_q == 0 or
+ * total_q == 0 return VA_OK without launching.
+ */
+int varlen_attn_fwd(const va_tensor* q, const va_tensor* k, const va_tensor* v,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                    int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                    int32_t causal, int32_t window_left, int32_t window_right,
+                    const va_tensor* out, float* lse, void* stream);
+
+/* Static, never-NULL description of a status code. */
+const char* varlen_attn_status_string(int status);
+
+/*
+ * The kernel's tile schedule for one block of query rows, computed on the
+ * host by the same function the kernel runs (exported for tests).
+ *
+ * Rows [row_begin, row_end) of a segment with seqlen_q queries and seqlen_k
+ * keys (0 <= row_begin < row_end <= seqlen_q).  Key tiles are block_n keys
+ * wide.  On return the block visits key tiles [*kt_begin, *kt_end); tiles in
+ * [*full_begin, *full_end) need no mask (every valid row sees every key of
+ * the tile); the other visited tiles are masked.  An empty visit range means
+ * no row of the block sees any key.  Returns VA_OK or VA_ERR_ARG / VA_ERR_NULL.
+ * Host only; makes no HIP call.
+ */
+int varlen_attn_tile_range(int32_t seqlen_q, int32_t seqlen_k, int32_t row_begin, int32_t row_end,
+                           int32_t causal, int32_t window_left, int32_t window_right,
+                           int32_t block_n, int32_t* kt_begin, int32_t* kt_end,
+                           int32_t* full_begin, int32_t* full_end);
+
+/* Launch shape varlen_attn_fwd would use (host only; makes no HIP call). */
+typedef struct va_plan {
+  int32_t block_m;       /* query rows per workgroup */
+  int32_t block_n;       /* keys per K/V tile */
+  int32_t threads;       /* threads per workgroup */
+  int32_t lds_bytes;     /* LDS per workgroup */
+  int64_t grid;          /* workgroups launched (some exit at once on short segments) */
+  const char* kernel;    /* kernel symbol family name */
+} va_plan;
+
+int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch, int32_t num_heads,
+                     int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t causal, va_plan* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VARLEN_ATTN_H */

@@ -133,9 +133,9 @@ def attention_fwd(
 
     Returns ``(out [total_q, H, d_v], lse [H, total_q])`` as float64.
     """
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
+    # Inputs may be float32 (an exact image of bf16); each slice is upcast to
+    # float64 where it is used, so large inputs are never copied whole.
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
     cu_q = [int(x) for x in cu_seqlens_q]
     cu_k = [int(x) for x in cu_seqlens_k]
     assert len(cu_q) == len(cu_k)
@@ -166,7 +166,13 @@ def attention_fwd(
             j = np.arange(Lk)[None, :]
             mask = (j >= lo[:, None]) & (j <= hi[:, None])
             for h in head_list:
-                o, l = _segment_head(q[q0 + idx, h, :], k[k0:k1, h, :], v[k0:k1, h, :], scale, mask)
+                o, l = _segment_head(
+                    q[q0 + idx, h, :].astype(np.float64),
+                    k[k0:k1, h, :].astype(np.float64),
+                    v[k0:k1, h, :].astype(np.float64),
+                    scale,
+                    mask,
+                )
                 out[q0 + idx, h, :] = o
                 lse[h, q0 + idx] = l
     return out, lse

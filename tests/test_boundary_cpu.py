@@ -1,0 +1,250 @@
+"""Host-side tests of the C interface (no GPU needed).
+
+* the built library loads and exports every function include/varlen_attn.h
+  declares;
+* argument validation returns the documented status codes before any HIP
+  call (only failing or no-launch cases are used here, so nothing is ever
+  launched with the placeholder pointers);
+* the kernel's tile schedule (the same __host__ __device__ function the
+  kernel runs, exported as varlen_attn_tile_range) equals brute force over
+  the oracle's visibility mask: the visited key tiles are exactly those with
+  at least one visible (row, key) pair, and the unmasked ones exactly those
+  whose every pair is visible.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import varlen_attention_forward_amd as pkg
+from varlen_attention_forward_amd import _binding as B
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "varlen_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(varlen_attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert declared, "no declarations parsed"
+    assert sorted(pkg.EXPORTED_SYMBOLS) == declared
+    lib = ctypes.CDLL(pkg.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(-7, 1):
+        s = pkg.status_string(code)
+        assert isinstance(s, str) and s
+    assert pkg.status_string(12345) == "unknown status"
+    assert pkg.status_string(B.VA_ERR_HEADDIM).startswith("unsupported")
+
+
+# ---------------------------------------------------------------------------
+# validation (placeholder pointers; every call below must fail or return
+# before launching)
+# ---------------------------------------------------------------------------
+FAKE = 0x100000  # 16-byte aligned, never dereferenced
+
+
+def _t(rows=10, heads=2, dim=64, row_stride=None, head_stride=None, data=FAKE):
+    hs = dim if head_stride is None else head_stride
+    rs = heads * dim if row_stride is None else row_stride
+    return B.VaTensor(data, rows, heads, dim, rs, hs)
+
+
+def _call(q=None, k=None, v=None, out=None, cu_q=FAKE, cu_k=FAKE, batch=1, mq=10, mk=10,
+          scale=0.125, causal=0, wl=-1, wr=-1, lse=0):
+    q = q if q is not None else _t()
+    k = k if k is not None else _t()
+    v = v if v is not None else _t()
+    out = out if out is not None else _t()
+    return B.raw_fwd(q, k, v, cu_q, cu_k, batch, mq, mk, scale, causal, wl, wr, out, lse, 0)
+
+
+def _lib_call_null(which):
+    lib = pkg.library()
+    t = _t()
+    args = [ctypes.byref(t)] * 3
+    args[which] = None
+    return lib.varlen_attn_fwd(*args, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 1, 10, 10,
+                               ctypes.c_float(0.125), 0, -1, -1, ctypes.byref(t), None, None)
+
+
+@pytest.mark.parametrize("which", [0, 1, 2])
+def test_null_descriptor(which):
+    assert _lib_call_null(which) == B.VA_ERR_NULL
+
+
+def test_null_out_descriptor():
+    lib = pkg.library()
+    t = _t()
+    st = lib.varlen_attn_fwd(ctypes.byref(t), ctypes.byref(t), ctypes.byref(t), ctypes.c_void_p(FAKE),
+                             ctypes.c_void_p(FAKE), 1, 10, 10, ctypes.c_float(0.125), 0, -1, -1, None, None, None)
+    assert st == B.VA_ERR_NULL
+
+
+def test_null_data_and_cu_seqlens():
+    assert _call(q=_t(data=0)) == B.VA_ERR_NULL
+    assert _call(k=_t(data=0)) == B.VA_ERR_NULL
+    assert _call(out=_t(data=0)) == B.VA_ERR_NULL
+    assert _call(cu_q=0) == B.VA_ERR_NULL
+    assert _call(cu_k=0) == B.VA_ERR_NULL
+
+
+@pytest.mark.parametrize("dims", [(32, 32), (96, 96), (256, 256), (192, 192), (128, 64), (80, 64), (0, 0)])
+def test_unsupported_head_dims(dims):
+    dqk, dv = dims
+    st = _call(q=_t(dim=dqk), k=_t(dim=dqk), v=_t(dim=dv), out=_t(dim=dv))
+    assert st == B.VA_ERR_HEADDIM
+
+
+def test_shape_mismatches():
+    assert _call(k=_t(heads=1, dim=64)) == B.VA_ERR_SHAPE  # grouped KV heads are not supported
+    assert _call(v=_t(rows=11)) == B.VA_ERR_SHAPE
+    assert _call(out=_t(rows=9)) == B.VA_ERR_SHAPE
+    assert _call(k=_t(dim=80)) == B.VA_ERR_SHAPE
+    assert _call(out=_t(dim=128)) == B.VA_ERR_SHAPE
+    assert _call(q=_t(heads=0)) == B.VA_ERR_SHAPE
+    assert _call(q=_t(rows=-1), out=_t(rows=-1)) == B.VA_ERR_SHAPE
+
+
+def test_strides_and_alignment():
+    assert _call(q=_t(row_stride=0)) == B.VA_ERR_STRIDE
+    assert _call(v=_t(head_stride=-64)) == B.VA_ERR_STRIDE
+    assert _call(k=_t(row_stride=132)) == B.VA_ERR_ALIGN  # not a multiple of 8 elements
+    assert _call(out=_t(head_stride=68)) == B.VA_ERR_ALIGN
+    assert _call(q=_t(data=FAKE + 8)) == B.VA_ERR_ALIGN
+    assert _call(lse=FAKE + 2) == B.VA_ERR_ALIGN
+
+
+def test_scalar_arguments():
+    assert _call(scale=0.0) == B.VA_ERR_ARG
+    assert _call(scale=-0.1) == B.VA_ERR_ARG
+    assert _call(scale=float("nan")) == B.VA_ERR_ARG
+    assert _call(scale=float("inf")) == B.VA_ERR_ARG
+    assert _call(causal=2) == B.VA_ERR_ARG
+    assert _call(wl=-2) == B.VA_ERR_ARG
+    assert _call(wr=-5) == B.VA_ERR_ARG
+    assert _call(batch=-1) == B.VA_ERR_ARG
+    assert _call(mq=-1) == B.VA_ERR_ARG
+    assert _call(mk=-1) == B.VA_ERR_ARG
+
+
+def test_empty_work_returns_ok_without_launch():
+    # batch == 0, max_seqlen_q == 0 and total_q == 0 are valid no-ops.
+    assert _call(batch=0) == B.VA_OK
+    assert _call(mq=0) == B.VA_OK
+    assert _call(q=_t(rows=0, data=0), out=_t(rows=0, data=0)) == B.VA_OK
+    assert _call(batch=0, cu_q=0, cu_k=0) == B.VA_OK
+
+
+def test_plan():
+    p = pkg.plan(80, 80, 8, 16, 4096, 4096)
+    assert p["block_n"] == 64 and p["threads"] == 256 and p["kernel"] == "varlen_attn_fwd_kernel"
+    assert p["grid"] == 8 * 16 * -(-4096 // p["block_m"])
+    with pytest.raises(ValueError):
+        pkg.plan(96, 96, 1, 1, 10, 10)
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+
+    q = torch.zeros((4, 2, 64), dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises((TypeError, ValueError)):
+        pkg.varlen_attn_fwd(q, q, q, cu, cu, 4, 4)
+
+
+# ---------------------------------------------------------------------------
+# tile schedule vs brute force
+# ---------------------------------------------------------------------------
+
+
+def _brute(Lq, Lk, r0, r1, causal, wl, wr, bn):
+    m = oracle.visible_mask(Lq, Lk, causal, wl, wr)[r0:r1]
+    ntiles = max(1, -(-max(Lk, 1) // bn)) + 1
+    visited, full = set(), set()
+    for t in range(ntiles):
+        block = np.zeros((r1 - r0, bn), dtype=bool)
+        lo, hi = t * bn, min((t + 1) * bn, Lk)
+        if hi > lo:
+            block[:, : hi - lo] = m[:, lo:hi]
+        if block.any():
+            visited.add(t)
+            if block.all():
+                full.add(t)
+    return visited, full
+
+
+def _kernel_sets(Lq, Lk, r0, r1, causal, wl, wr, bn):
+    kb, ke, fb, fe = pkg.tile_range(Lq, Lk, r0, r1, causal, wl, wr, bn)
+    return set(range(kb, ke)), set(range(fb, fe))
+
+
+def test_tile_range_exhaustive_small():
+    bn = 4
+    count = 0
+    for Lq in range(1, 10):
+        for Lk in range(0, 11):
+            for causal in (0, 1):
+                for wl in (-1, 0, 1, 2, 5):
+                    for wr in (-1, 0, 1, 3):
+                        for r0 in range(0, Lq, 3):
+                            for r1 in (min(r0 + 3, Lq), min(r0 + 5, Lq), Lq):
+                                if r1 <= r0:
+                                    continue
+                                got = _kernel_sets(Lq, Lk, r0, r1, causal, wl, wr, bn)
+                                want = _brute(Lq, Lk, r0, r1, causal, wl, wr, bn)
+                                assert got == want, (Lq, Lk, r0, r1, causal, wl, wr, got, want)
+                                count += 1
+    assert count > 10000
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_tile_range_random_kernel_shapes(seed):
+    """Kernel-sized tiles (64 keys, 128-row blocks) on random lengths and masks."""
+    rng = np.random.default_rng(seed)
+    for _ in range(150):
+        Lq = int(rng.integers(1, 700))
+        Lk = int(rng.integers(0, 700))
+        causal = int(rng.integers(0, 2))
+        wl = int(rng.choice([-1, 0, 1, 63, 64, 65, 200]))
+        wr = int(rng.choice([-1, 0, 1, 63, 64, 100]))
+        bm = 128
+        for r0 in range(0, Lq, bm):
+            r1 = min(r0 + bm, Lq)
+            got = _kernel_sets(Lq, Lk, r0, r1, causal, wl, wr, 64)
+            want = _brute(Lq, Lk, r0, r1, causal, wl, wr, 64)
+            assert got == want, (Lq, Lk, r0, r1, causal, wl, wr)
+
+
+def test_tile_range_config_shapes():
+    # MLA causal 4096: q-tile t of 128 rows visits tiles 0 .. 2t+1 and masks
+    # exactly the two diagonal tiles.
+    for t in range(32):
+        kb, ke, fb, fe = pkg.tile_range(4096, 4096, 128 * t, 128 * (t + 1), 1, -1, -1, 64)
+        assert (kb, ke) == (0, 2 * t + 2)
+        assert (fb, fe) == (0, 2 * t)
+    # full attention on 576 keys: 9 tiles, all unmasked
+    assert pkg.tile_range(576, 576, 0, 128, 0, -1, -1, 64) == (0, 9, 0, 9)
+    # 100 keys: the partial second tile is masked
+    assert pkg.tile_range(100, 100, 0, 100, 0, -1, -1, 64) == (0, 2, 0, 1)
+
+
+def test_tile_range_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        pkg.tile_range(10, 10, 5, 5, 0, -1, -1, 64)
+    with pytest.raises(ValueError):
+        pkg.tile_range(10, 10, 0, 11, 0, -1, -1, 64)
+    with pytest.raises(ValueError):
+        pkg.tile_range(10, 10, 0, 10, 0, -1, -1, 0)

@@ -1,0 +1,347 @@
+"""GPU parity of the HIP path against the fp64 oracle (marked ``gpu``).
+
+Tolerances: max |O_gpu - O_oracle| <= 2e-2 and max |LSE_gpu - LSE_oracle|
+<= 1e-3 for bf16 inputs, with -inf LSE exactly where the oracle has it.
+Mask indexing and tile skipping are checked bit-exactly by probes whose
+results are integers:
+
+* zero-Q count probe: with Q = 0 every visible score is 0, so each p is 1
+  and the row sum is the integer |J_i|; exp(LSE) must round to |J_i|.
+* integer-score probe: scale 1, q = (1, 256, 0, ...), k_j = (j mod 256,
+  j div 256, 0, ...) makes s_j = j exactly in bf16 x bf16 -> fp32, so
+  LSE = j_max + ln sum_{t<n} e^-t and j_max must round to max J_i.
+
+All calls go through the C interface via the ctypes binding.
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import varlen_attention_forward_amd as va
+from varlen_attention_forward_amd import workloads
+from helpers import f64, f32, oracle_on
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 2e-2
+TOL_LSE = 1e-3
+DEV = "cuda:0"
+DIMS = [(64, 64), (72, 72), (80, 80), (128, 128), (192, 128)]
+
+
+def guarded(t: torch.Tensor, rows: int = 256) -> torch.Tensor:
+    """Copy ``t`` to the GPU with ``rows`` NaN rows after its last row."""
+    buf = torch.full((t.shape[0] + rows,) + tuple(t.shape[1:]), float("nan"), dtype=t.dtype, device=DEV)
+    buf[: t.shape[0]].copy_(t)
+    return buf[: t.shape[0]]
+
+
+def run_gpu(inp, out=None, lse_fill=None, return_lse=True, v=None):
+    q, k = guarded(inp.q), guarded(inp.k)
+    v = guarded(inp.v) if v is None else v
+    cu_q, cu_k = inp.cu_seqlens_q.to(DEV), inp.cu_seqlens_k.to(DEV)
+    lse = None
+    if return_lse:
+        lse = torch.full((inp.q.shape[1], inp.q.shape[0]), float("nan") if lse_fill is None else lse_fill,
+                         dtype=torch.float32, device=DEV)
+    res = va.varlen_attn_fwd(
+        q, k, v, cu_q, cu_k, inp.max_seqlen_q, inp.max_seqlen_k,
+        softmax_scale=inp.softmax_scale, causal=inp.causal, window_size=inp.window,
+        out=out, return_lse=return_lse, lse=lse,
+    )
+    torch.cuda.synchronize()
+    return res if return_lse else (res, None)
+
+
+def assert_parity(out, lse, ref_o, ref_lse, rows=None, what=""):
+    o = f64(out)
+    if rows is not None:
+        o, ref_o = o[rows], ref_o[rows]
+    assert np.all(np.isfinite(o)), "%s: non-finite output" % what
+    err_o = float(np.max(np.abs(o - ref_o))) if o.size else 0.0
+    assert err_o <= TOL_O, "%s: max|dO| = %.3e" % (what, err_o)
+    if lse is not None:
+        l = f64(lse)
+        if rows is not None:
+            l, ref_lse = l[:, rows], ref_lse[:, rows]
+        neg = ref_lse == -np.inf
+        assert np.array_equal(l == -np.inf, neg), "%s: -inf LSE rows differ" % what
+        fin = ~neg
+        err_l = float(np.max(np.abs(l[fin] - ref_lse[fin]))) if fin.any() else 0.0
+        assert err_l <= TOL_LSE, "%s: max|dLSE| = %.3e" % (what, err_l)
+        return err_o, err_l
+    return err_o, None
+
+
+# ---------------------------------------------------------------------------
+# small full-oracle parity over head dims, masks and ragged lengths
+# ---------------------------------------------------------------------------
+LEN_SETS = {
+    "ragged": ([1, 63, 64, 65, 127, 128, 129, 255, 256, 257], None),
+    "q_lt_k": ([1, 40, 64, 100, 129], [70, 64, 200, 100, 300]),
+    "q_gt_k": ([64, 130, 300], [10, 129, 65]),
+    "empty_segments": ([0, 37, 0, 190, 5], [0, 0, 50, 190, 0]),
+}
+MODES = {
+    "full": (False, (-1, -1)),
+    "causal": (True, (-1, -1)),
+    "window": (False, (40, 17)),
+    "causal_window": (True, (70, -1)),
+    "left_only": (False, (0, -1)),
+}
+
+
+@pytest.mark.parametrize("dims", DIMS, ids=lambda d: "d%d_%d" % d)
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("lens", list(LEN_SETS))
+def test_small_parity(dims, mode, lens):
+    d_qk, d_v = dims
+    causal, window = MODES[mode]
+    lq, lk = LEN_SETS[lens]
+    lk = lq if lk is None else lk
+    heads = 3 if d_qk < 192 else 2
+    seed = zlib.crc32(repr((dims, mode, lens)).encode()) % 1000
+    inp = workloads.make_inputs(lq, lk, heads, d_qk, d_v, seed=seed, causal=causal, window=window)
+    out, lse = run_gpu(inp)
+    ref_o, ref_lse = oracle_on(inp)
+    assert_parity(out, lse, ref_o, ref_lse, what="%s/%s/%s" % (dims, mode, lens))
+
+
+def test_large_values_and_tiny_scale():
+    """Scores far from 0 (std 4 inputs) and a small scale keep within tolerance."""
+    for std, scale in ((4.0, None), (1.0, 1e-3), (2.0, 0.5)):
+        inp = workloads.make_inputs([300, 77], [300, 77], 2, 128, 128, seed=11, std=std, softmax_scale=scale)
+        out, lse = run_gpu(inp)
+        ref_o, ref_lse = oracle_on(inp)
+        assert_parity(out, lse, ref_o, ref_lse, what="std=%s scale=%s" % (std, scale))
+
+
+# ---------------------------------------------------------------------------
+# exact probes of mask indexing and tile skipping
+# ---------------------------------------------------------------------------
+def _visible_counts(inp):
+    wl, wr = inp.window
+    cu_q, cu_k = inp.cu_seqlens_q.tolist(), inp.cu_seqlens_k.tolist()
+    n = np.full(inp.q.shape[0], -1, dtype=np.int64)
+    jmax = np.full(inp.q.shape[0], -1, dtype=np.int64)
+    for b in range(len(cu_q) - 1):
+        Lq, Lk = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        lo, hi = oracle.visible_interval(np.arange(Lq), Lq, Lk, inp.causal, wl, wr)
+        n[cu_q[b]: cu_q[b + 1]] = np.maximum(hi - lo + 1, 0)
+        jmax[cu_q[b]: cu_q[b + 1]] = hi
+    return n, jmax
+
+
+PROBE_CASES = [
+    ("square_causal", [64, 256, 577, 1000], None, True, (-1, -1)),
+    ("chunked_prefill", [100, 64, 257], [612, 64, 300], True, (-1, -1)),
+    ("q_gt_k_causal", [300, 129], [100, 1], True, (-1, -1)),
+    ("band", [700, 256], [700, 256], False, (100, 63)),
+    ("causal_window", [1000], [1000], True, (127, -1)),
+    ("look_ahead", [333], [400], False, (0, 129)),
+    ("full_ragged", [1, 65, 129, 1023], None, False, (-1, -1)),
+]
+
+
+@pytest.mark.parametrize("case", PROBE_CASES, ids=lambda c: c[0])
+@pytest.mark.parametrize("dims", [(64, 64), (80, 80), (192, 128)], ids=lambda d: "d%d_%d" % d)
+def test_zero_q_count_probe(case, dims):
+    name, lq, lk, causal, window = case
+    lk = lq if lk is None else lk
+    inp = workloads.make_inputs(lq, lk, 2, dims[0], dims[1], seed=3, causal=causal, window=window)
+    inp.q.zero_()
+    out, lse = run_gpu(inp)
+    n, _ = _visible_counts(inp)
+    l = f64(lse)
+    for h in range(2):
+        got = np.where(l[h] == -np.inf, 0, np.rint(np.exp(np.where(l[h] == -np.inf, 0, l[h]))))
+        assert np.array_equal(got.astype(np.int64), n), "%s head %d: visible counts differ" % (name, h)
+    ref_o, ref_lse = oracle_on(inp)
+    assert_parity(out, lse, ref_o, ref_lse, what=name)
+
+
+@pytest.mark.parametrize("case", PROBE_CASES, ids=lambda c: c[0])
+def test_integer_score_probe(case):
+    name, lq, lk, causal, window = case
+    lk = lq if lk is None else lk
+    inp = workloads.make_inputs(lq, lk, 1, 64, 64, seed=4, causal=causal, window=window, softmax_scale=1.0)
+    inp.q.zero_()
+    inp.q[:, :, 0] = 1.0
+    inp.q[:, :, 1] = 256.0
+    inp.k.zero_()
+    cu_k = inp.cu_seqlens_k.tolist()
+    for b in range(len(cu_k) - 1):
+        j = torch.arange(cu_k[b + 1] - cu_k[b])
+        inp.k[cu_k[b]: cu_k[b + 1], 0, 0] = (j % 256).to(torch.bfloat16)
+        inp.k[cu_k[b]: cu_k[b + 1], 0, 1] = (j // 256).to(torch.bfloat16)
+    out, lse = run_gpu(inp)
+    n, jmax = _visible_counts(inp)
+    l = f64(lse)[0]
+    has = n > 0
+    assert np.all(l[~has] == -np.inf)
+    tail = np.log((1 - np.exp(-n[has].astype(np.float64))) / (1 - math.exp(-1)))
+    got = np.rint(l[has] - tail).astype(np.int64)
+    assert np.array_equal(got, jmax[has]), "%s: last visible key differs" % name
+
+
+def test_single_key_is_exact():
+    """Lk = 1: p = exp2(0) = 1 exactly, so O = V[0] bit for bit (also causal row 0)."""
+    for causal in (False, True):
+        # bottom-right causal: with one key only a segment's last row sees it
+        lq = [1, 1, 1] if causal else [5, 70, 1]
+        inp = workloads.make_inputs(lq, [1, 1, 1], 4, 128, 128, seed=5, causal=causal)
+        out, lse = run_gpu(inp)
+        cu_q, cu_k = inp.cu_seqlens_q.tolist(), inp.cu_seqlens_k.tolist()
+        for b in range(len(cu_q) - 1):
+            rows = slice(cu_q[b], cu_q[b + 1])
+            expect = inp.v[cu_k[b]].to(DEV).unsqueeze(0).expand(cu_q[b + 1] - cu_q[b], -1, -1)
+            assert torch.equal(out[rows], expect)
+        ref_o, ref_lse = oracle_on(inp)
+        assert_parity(out, lse, ref_o, ref_lse, what="single key")
+
+
+def test_constant_v():
+    inp = workloads.make_inputs([500, 64], [500, 64], 2, 80, 80, seed=6, causal=True)
+    c = torch.randn((2, 80), generator=torch.Generator().manual_seed(0)).to(torch.bfloat16)
+    inp.v[:] = c
+    out, _ = run_gpu(inp)
+    err = (out.float().cpu() - c.float()).abs().max().item()
+    assert err <= TOL_O
+
+
+def test_key_permutation_invariance():
+    inp = workloads.make_inputs([300], [517], 2, 128, 128, seed=7)
+    out1, lse1 = run_gpu(inp)
+    perm = torch.randperm(517, generator=torch.Generator().manual_seed(1))
+    inp2 = workloads.Inputs(**{**inp.__dict__, "k": inp.k[perm].contiguous(), "v": inp.v[perm].contiguous()})
+    out2, lse2 = run_gpu(inp2)
+    assert (out1.float() - out2.float()).abs().max().item() <= TOL_O
+    assert (lse1 - lse2).abs().max().item() <= TOL_LSE
+
+
+# ---------------------------------------------------------------------------
+# bit-exact invariances: packing, heads, repeat runs, strides
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_packing_invariance_bit_exact(causal):
+    lq, lk = [77, 300, 129, 512], [90, 300, 129, 600]
+    inp = workloads.make_inputs(lq, lk, 4, 80, 80, seed=8, causal=causal)
+    out, lse = run_gpu(inp)
+    cu_q, cu_k = inp.cu_seqlens_q.tolist(), inp.cu_seqlens_k.tolist()
+    for b in range(4):
+        qs, ks = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        one = workloads.Inputs(
+            q=inp.q[qs].clone(), k=inp.k[ks].clone(), v=inp.v[ks].clone(),
+            cu_seqlens_q=workloads.cu_seqlens([lq[b]]), cu_seqlens_k=workloads.cu_seqlens([lk[b]]),
+            max_seqlen_q=lq[b], max_seqlen_k=lk[b], softmax_scale=inp.softmax_scale,
+            causal=causal, window=(-1, -1),
+        )
+        o1, l1 = run_gpu(one)
+        assert torch.equal(out[qs], o1), "segment %d output depends on packing" % b
+        assert torch.equal(lse[:, qs], l1), "segment %d LSE depends on packing" % b
+
+
+def test_determinism_and_head_permutation():
+    inp = workloads.make_inputs([1000, 333], [1000, 333], 6, 128, 128, seed=9, causal=True)
+    o1, l1 = run_gpu(inp)
+    o2, l2 = run_gpu(inp)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    perm = torch.tensor([3, 0, 5, 1, 4, 2])
+    inp2 = workloads.Inputs(**{**inp.__dict__, "q": inp.q[:, perm].contiguous(), "k": inp.k[:, perm].contiguous(),
+                               "v": inp.v[:, perm].contiguous()})
+    o3, l3 = run_gpu(inp2)
+    assert torch.equal(o3, o1[:, perm.to(DEV)]) and torch.equal(l3, l1[perm.to(DEV)])
+
+
+def test_strided_mla_v_and_strided_out():
+    """V as a view into the interleaved [T, H, nope + v] buffer (MLA layout), and
+    a caller-provided strided out; results equal the contiguous call bit for bit."""
+    inp = workloads.make_inputs([257, 1000], [257, 1000], 4, 192, 128, seed=10, causal=True)
+    o_ref, l_ref = run_gpu(inp)
+    T = inp.k.shape[0]
+    kv = torch.full((T, 4, 128 + 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    kv[:, :, 128:] = inp.v.to(DEV)
+    v_view = kv[:, :, 128:]
+    assert v_view.stride() == (4 * 256, 256, 1)
+    big = torch.full((inp.q.shape[0], 4, 256), 7.0, dtype=torch.bfloat16, device=DEV)
+    out_view = big[:, :, 64:192]
+    o2, l2 = run_gpu(inp, out=out_view, v=v_view)
+    assert torch.equal(o2, o_ref) and torch.equal(l2, l_ref)
+    assert torch.all(big[:, :, :64] == 7.0) and torch.all(big[:, :, 192:] == 7.0)
+
+
+def test_rows_outside_segments_untouched():
+    inp = workloads.make_inputs([10, 200], [10, 200], 2, 64, 64, seed=12)
+    # cu_seqlens cover only the first 150 of 210 rows
+    inp = workloads.Inputs(**{**inp.__dict__, "cu_seqlens_q": torch.tensor([0, 10, 150], dtype=torch.int32),
+                              "cu_seqlens_k": torch.tensor([0, 10, 150], dtype=torch.int32),
+                              "max_seqlen_q": 140, "max_seqlen_k": 140})
+    sentinel = torch.full((210, 2, 64), 3.0, dtype=torch.bfloat16, device=DEV)
+    out, lse = run_gpu(inp, out=sentinel, lse_fill=5.0)
+    assert torch.all(out[150:] == 3.0)
+    assert torch.all(lse[:, 150:] == 5.0)
+    ref_o, ref_lse = oracle_on(inp)
+    assert_parity(out, lse, ref_o, ref_lse, rows=np.arange(150), what="partial cover")
+
+
+def test_no_lse_matches_with_lse():
+    inp = workloads.make_inputs([300, 700], [300, 700], 2, 80, 80, seed=13)
+    o1, _ = run_gpu(inp, return_lse=False)
+    o2, _ = run_gpu(inp)
+    assert torch.equal(o1, o2)
+
+
+def test_empty_batch_and_zero_keys():
+    inp = workloads.make_inputs([5, 6], [0, 0], 2, 64, 64, seed=14)
+    out, lse = run_gpu(inp)
+    assert torch.all(out == 0) and torch.all(lse == -float("inf"))
+    e = torch.empty((0, 2, 64), dtype=torch.bfloat16, device=DEV)
+    cu = torch.zeros(1, dtype=torch.int32, device=DEV)
+    assert va.varlen_attn_fwd(e, e, e, cu, cu, 0, 0).shape == (0, 2, 64)
+
+
+# ---------------------------------------------------------------------------
+# the named workloads at full size (sampled rows where the oracle is slow)
+# ---------------------------------------------------------------------------
+def _sample_rows(inp, n_random, seed=0):
+    bm = va.plan(inp.q.shape[2], inp.v.shape[2], len(inp.cu_seqlens_q) - 1, inp.q.shape[1],
+                 inp.max_seqlen_q, inp.max_seqlen_k, inp.causal)["block_m"]
+    cu = inp.cu_seqlens_q.tolist()
+    rows = set()
+    for b in range(len(cu) - 1):
+        L = cu[b + 1] - cu[b]
+        for r in (0, 1, bm - 1, bm, bm + 1, L - 2, L - 1):
+            if 0 <= r < L:
+                rows.add(cu[b] + r)
+    rng = np.random.default_rng(seed)
+    rows.update(rng.integers(0, cu[-1], n_random).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["tiny_varlen_d64", "vit_window256_d80"])
+def test_workload_full_oracle(name):
+    w = workloads.WORKLOADS[name]
+    inp = workloads.workload_inputs(w)
+    out, lse = run_gpu(inp)
+    ref_o, ref_lse = oracle_on(inp)
+    e = assert_parity(out, lse, ref_o, ref_lse, what=name)
+    print("%s: max|dO| %.3e max|dLSE| %.3e" % (name, e[0], e[1]))
+
+
+@pytest.mark.parametrize("name,n_random,heads", [
+    ("vit_full_d80", 384, None),
+    ("vit_long65536_d128", 24, None),
+    ("mla_causal_192_128", 128, None),
+])
+def test_workload_sampled(name, n_random, heads):
+    w = workloads.WORKLOADS[name]
+    inp = workloads.workload_inputs(w)
+    out, lse = run_gpu(inp)
+    rows = _sample_rows(inp, n_random)
+    ref_o, ref_lse = oracle_on(inp, rows=rows, heads=heads)
+    e = assert_parity(out, lse, ref_o, ref_lse, rows=rows, what=name)
+    print("%s: %d rows, max|dO| %.3e max|dLSE| %.3e" % (name, len(rows), e[0], e[1]))

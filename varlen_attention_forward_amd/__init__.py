@@ -1,1 +1,31 @@
-"""MI355X-native fused variable-length attention forward (placeholder, binding follows)."""
+"""MI355X-native fused variable-length attention forward.
+
+The compute runs in ``libvarlen_attn.so`` (hand-written HIP for gfx950, C
+interface in ``include/varlen_attn.h``); this package is a thin ctypes
+binding plus the seeded synthetic workloads used by tests and the bench.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTED_SYMBOLS,
+    LIB_PATH,
+    VaTensor,
+    VarlenAttnError,
+    library,
+    plan,
+    raw_fwd,
+    status_string,
+    tile_range,
+    varlen_attn_fwd,
+)
+
+__all__ = [
+    "varlen_attn_fwd",
+    "status_string",
+    "tile_range",
+    "plan",
+    "library",
+    "raw_fwd",
+    "VaTensor",
+    "VarlenAttnError",
+    "EXPORTED_SYMBOLS",
+    "LIB_PATH",
+]

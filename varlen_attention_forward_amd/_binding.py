@@ -1,0 +1,233 @@
+"""ctypes binding of ``libvarlen_attn.so`` (see include/varlen_attn.h).
+
+Argument marshalling only: every step of the attention runs in the HIP
+library.  There is no fallback: if the library is missing, calls raise.
+PyTorch supplies device memory and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+VA_OK = 0
+VA_ERR_NULL = -1
+VA_ERR_SHAPE = -2
+VA_ERR_HEADDIM = -3
+VA_ERR_STRIDE = -4
+VA_ERR_ALIGN = -5
+VA_ERR_ARG = -6
+VA_ERR_LAUNCH = -7
+
+STATUS_NAMES = {
+    VA_OK: "VA_OK",
+    VA_ERR_NULL: "VA_ERR_NULL",
+    VA_ERR_SHAPE: "VA_ERR_SHAPE",
+    VA_ERR_HEADDIM: "VA_ERR_HEADDIM",
+    VA_ERR_STRIDE: "VA_ERR_STRIDE",
+    VA_ERR_ALIGN: "VA_ERR_ALIGN",
+    VA_ERR_ARG: "VA_ERR_ARG",
+    VA_ERR_LAUNCH: "VA_ERR_LAUNCH",
+}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvarlen_attn.so")
+
+# Every symbol include/varlen_attn.h declares.
+EXPORTED_SYMBOLS = (
+    "varlen_attn_fwd",
+    "varlen_attn_status_string",
+    "varlen_attn_tile_range",
+    "varlen_attn_plan",
+)
+
+
+class VaTensor(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("heads", ctypes.c_int32),
+        ("dim", ctypes.c_int32),
+        ("row_stride", ctypes.c_int64),
+        ("head_stride", ctypes.c_int64),
+    ]
+
+
+class VaPlan(ctypes.Structure):
+    _fields_ = [
+        ("block_m", ctypes.c_int32),
+        ("block_n", ctypes.c_int32),
+        ("threads", ctypes.c_int32),
+        ("lds_bytes", ctypes.c_int32),
+        ("grid", ctypes.c_int64),
+        ("kernel", ctypes.c_char_p),
+    ]
+
+
+class VarlenAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s (%d): %s" % (STATUS_NAMES.get(status, "?"), status, message))
+        self.status = status
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load the HIP library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "libvarlen_attn.so is missing at %s; build it with "
+            "`python -m varlen_attention_forward_amd.build`" % LIB_PATH
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    lib.varlen_attn_fwd.restype = ctypes.c_int
+    lib.varlen_attn_fwd.argtypes = [
+        P(VaTensor), P(VaTensor), P(VaTensor),
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        P(VaTensor), ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    lib.varlen_attn_status_string.restype = ctypes.c_char_p
+    lib.varlen_attn_status_string.argtypes = [ctypes.c_int]
+    lib.varlen_attn_tile_range.restype = ctypes.c_int
+    lib.varlen_attn_tile_range.argtypes = [ctypes.c_int32] * 8 + [P(ctypes.c_int32)] * 4
+    lib.varlen_attn_plan.restype = ctypes.c_int
+    lib.varlen_attn_plan.argtypes = [ctypes.c_int32] * 7 + [P(VaPlan)]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return library().varlen_attn_status_string(int(status)).decode()
+
+
+def _raise_for(status: int) -> None:
+    if status == VA_OK:
+        return
+    msg = status_string(status)
+    if status == VA_ERR_LAUNCH:
+        raise VarlenAttnError(status, msg)
+    err = VarlenAttnError(status, msg)
+    raise ValueError(str(err)) from err
+
+
+def tile_range(seqlen_q, seqlen_k, row_begin, row_end, causal, window_left, window_right, block_n):
+    """The kernel's key-tile schedule for one block of query rows (host call)."""
+    out = [ctypes.c_int32() for _ in range(4)]
+    st = library().varlen_attn_tile_range(
+        seqlen_q, seqlen_k, row_begin, row_end, int(causal), window_left, window_right, block_n,
+        *[ctypes.byref(o) for o in out],
+    )
+    _raise_for(st)
+    return tuple(o.value for o in out)
+
+
+def plan(head_dim_qk, head_dim_v, batch, num_heads, max_seqlen_q, max_seqlen_k, causal=False) -> dict:
+    """Launch shape the library would use (host call, no GPU needed)."""
+    pl = VaPlan()
+    st = library().varlen_attn_plan(
+        head_dim_qk, head_dim_v, batch, num_heads, max_seqlen_q, max_seqlen_k, int(causal), ctypes.byref(pl)
+    )
+    _raise_for(st)
+    return {
+        "block_m": pl.block_m,
+        "block_n": pl.block_n,
+        "threads": pl.threads,
+        "lds_bytes": pl.lds_bytes,
+        "grid": pl.grid,
+        "kernel": pl.kernel.decode(),
+    }
+
+
+def raw_fwd(q: VaTensor, k: VaTensor, v: VaTensor, cu_q_ptr: int, cu_k_ptr: int, batch: int,
+            max_seqlen_q: int, max_seqlen_k: int, softmax_scale: float, causal: int,
+            window_left: int, window_right: int, out: VaTensor, lse_ptr: int, stream: int) -> int:
+    """The C entry point with plain descriptors; returns the status code."""
+    return library().varlen_attn_fwd(
+        ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+        ctypes.c_void_p(cu_q_ptr), ctypes.c_void_p(cu_k_ptr), int(batch),
+        int(max_seqlen_q), int(max_seqlen_k), float(softmax_scale),
+        int(causal), int(window_left), int(window_right),
+        ctypes.byref(out), ctypes.c_void_p(lse_ptr), ctypes.c_void_p(stream),
+    )
+
+
+def _desc(t, name: str) -> VaTensor:
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != torch.bfloat16:
+        raise TypeError("%s must be bfloat16, got %s" % (name, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be on a GPU device" % name)
+    if t.dim() != 3:
+        raise ValueError("%s must be [tokens, heads, dim], got shape %s" % (name, tuple(t.shape)))
+    if t.shape[2] > 1 and t.stride(2) != 1:
+        raise ValueError("%s: the last dimension must be contiguous" % name)
+    row_stride = t.stride(0) if t.shape[0] > 1 else t.shape[1] * t.stride(1)
+    head_stride = t.stride(1) if t.shape[1] > 1 else t.shape[2]
+    return VaTensor(t.data_ptr(), t.shape[0], t.shape[1], t.shape[2], row_stride, head_stride)
+
+
+def varlen_attn_fwd(
+    q,
+    k,
+    v,
+    cu_seqlens_q,
+    cu_seqlens_k,
+    max_seqlen_q: int,
+    max_seqlen_k: int,
+    softmax_scale: Optional[float] = None,
+    causal: bool = False,
+    window_size: Tuple[int, int] = (-1, -1),
+    out=None,
+    return_lse: bool = False,
+    lse=None,
+):
+    """Fused varlen attention forward on the current HIP stream.
+
+    ``q`` [total_q, H, d_qk], ``k`` [total_k, H, d_qk], ``v`` [total_k, H, d_v]
+    in bf16 on the GPU; ``cu_seqlens_q/k`` int32 [batch + 1] on the GPU.
+    Returns ``out`` [total_q, H, d_v] bf16, or ``(out, lse)`` with lse fp32
+    [H, total_q] when ``return_lse``.  ``softmax_scale`` defaults to
+    d_qk^-0.5.  ``window_size`` is ``(left, right)``, -1 for unbounded.
+    """
+    import torch
+
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if not isinstance(cu, torch.Tensor) or cu.dtype != torch.int32 or not cu.is_cuda:
+            raise TypeError("%s must be an int32 GPU tensor" % name)
+        if cu.dim() != 1 or not cu.is_contiguous():
+            raise ValueError("%s must be a contiguous 1-D tensor" % name)
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have batch + 1 entries")
+    batch = cu_seqlens_q.numel() - 1
+    total_q, H, d_qk = q.shape
+    d_v = v.shape[2]
+    if softmax_scale is None:
+        softmax_scale = d_qk ** -0.5
+    if out is None:
+        out = torch.empty((total_q, H, d_v), dtype=torch.bfloat16, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous() or tuple(lse.shape) != (H, total_q):
+            raise ValueError("lse must be a contiguous float32 GPU tensor of shape [H, total_q]")
+    wl, wr = window_size
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = raw_fwd(
+        _desc(q, "q"), _desc(k, "k"), _desc(v, "v"),
+        cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), batch,
+        max_seqlen_q, max_seqlen_k, softmax_scale, int(bool(causal)), wl, wr,
+        _desc(out, "out"), lse.data_ptr() if lse is not None else 0, stream,
+    )
+    _raise_for(st)
+    if return_lse:
+        return out, lse
+    return out

@@ -1,21 +1,26 @@
 // Fused variable-length attention forward for AMD Instinct MI355X (gfx950).
 //
-// One workgroup = 4 wavefronts (256 threads) owns BM = 4 * NQB * 32 query
-// rows of one (segment, head).  It walks the key tiles the rows can see
-// (tile_schedule.h), BN = 64 keys at a time:
+// One workgroup = 8 wavefronts (512 threads, two per SIMD) owns BM = 256
+// query rows of one (segment, head); each wave owns 32 of them.  It walks
+// the key tiles those rows can see (tile_schedule.h), BN = 64 keys at a time:
 //
-//   global K/V tile --(registers, prefetched one tile ahead)--> LDS (double
-//   buffered; V written transposed) --> S^T = K Q^T on v_mfma_f32_32x32x16_bf16
-//   --> online softmax (exp2, log2(e)-prescaled scale, lazy rescale)
-//   --> O^T += V^T P^T on the same MFMA --> epilogue: O = acc / l in bf16,
-//   LSE = (m + log2 l) ln 2 in fp32.
+//   HBM K/V tile --buffer_load ... lds (direct to LDS, out-of-range rows
+//   read as zero)--> LDS, double buffered
+//   --> S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (Q held in registers)
+//   --> online softmax in registers (exp2 with a log2(e)-prescaled scale,
+//       lazy rescale past a threshold)
+//   --> O^T += V^T P^T on the same MFMA, V^T read with ds_read_b64_tr_b16
+//   --> epilogue: O = acc / l in bf16, LSE = (m + log2 l) ln 2 in fp32.
 //
 // Scores are computed transposed (keys on the MFMA M axis, queries on N), so
 // each lane holds one query column: the row max and row sum over the keys a
-// lane holds are plain in-lane reductions, and only one cross-lane step (lane
-// l with lane l ^ 32) is needed per tile.  The same layout makes the
-// probability registers usable directly as the B operand of the PV product
-// once the key order inside each 16-key group is permuted the same way for V.
+// lane holds are in-lane reductions with a single cross-lane step (lane l with
+// lane l ^ 32) per tile.  The probability registers then serve directly as
+// the B operand of the PV product, with the key order inside each 16-key
+// group permuted identically on the V side.
+//
+// While a tile is computed, the next one streams into the other LDS buffer;
+// the two waves on each SIMD overlap one's MFMAs with the other's softmax.
 //
 // Where the pages describe FA4 on Blackwell (TMEM, tcgen05.ld.red row max,
 // 2-CTA MMA) that design is prior art only; what carries over is the online
@@ -33,15 +38,20 @@
 namespace va {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;        // query rows per workgroup
 constexpr int kBN = 64;                 // keys per tile
 constexpr float kRescaleTau = 8.0f;     // lazy rescale threshold, log2 units
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every range: reads 0
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 
 struct Params {
   const uint16_t* q;
@@ -51,35 +61,47 @@ struct Params {
   float* lse;
   const int32_t* cu_q;
   const int32_t* cu_k;
-  int64_t q_row, q_head, k_row, k_head, v_row, v_head, o_row, o_head;
+  int64_t q_row, q_head, k_row, k_head, v_row, v_head, o_row, o_head;  // elements
   int64_t total_q;
   int32_t batch, heads, n_qt, num_blocks;
   int32_t causal, wl, wr;
   float scale_log2;  // softmax_scale * log2(e)
 };
 
-template <int DQK, int DV, int NQB>
+template <int DQK, int DV>
 struct Cfg {
-  static constexpr int DQKP = (DQK + 15) / 16 * 16;  // MFMA K granularity
-  static constexpr int DVP = (DV + 31) / 32 * 32;    // 32-row MFMA blocks of V^T
+  static constexpr int DQKP = (DQK + 15) / 16 * 16;  // MFMA K granularity (72 -> 80)
+  static constexpr int DVP = (DV + 31) / 32 * 32;    // 32-row V^T MFMA blocks (72, 80 -> 96)
   static constexpr int KC = DQKP / 16;               // k-chunks of the QK^T product
   static constexpr int VB = DVP / 32;                // dv blocks of the PV product
-  static constexpr int BM = kWaves * NQB * 32;
-  static constexpr int K_PITCH = DQKP + 8;   // +16 B per row: conflict-free column reads
-  static constexpr int VT_PITCH = kBN + 8;   // V^T rows: 64 keys + 16 B
-  static constexpr int K_TILE = kBN * K_PITCH;
-  static constexpr int VT_TILE = DVP * VT_PITCH;
-  static constexpr int LDS_ELEMS = 2 * (K_TILE + VT_TILE);
-  static constexpr int K_CHUNKS = kBN * (DQKP / 8);       // 16-byte chunks per K tile
-  static constexpr int K_ITERS = (K_CHUNKS + kThreads - 1) / kThreads;
-  static constexpr int V_UNITS = (kBN / 4) * (DV / 8);    // 4 keys x 8 dv per unit
-  static constexpr int V_ITERS = (V_UNITS + kThreads - 1) / kThreads;
+  // K tile: 64 rows of DQKP bf16 = CPR_K 16-byte chunks, plus one pad chunk
+  // per row so the 32 rows an MFMA operand read touches hit distinct banks.
+  static constexpr int CPR_K = DQKP / 8;
+  static constexpr int KPITCH = CPR_K + 1;           // chunks per K row in LDS
+  static constexpr int K_REAL = DQK / 8;             // chunks holding data
+  // V tile: 64 rows of DVP bf16, chunk index XOR-swizzled per row so the
+  // four rows a transposing read touches hit distinct banks.
+  static constexpr int CPR_V = DVP / 8;
+  static constexpr int V_REAL = DV / 8;
+  static constexpr int K_TILE = kBN * KPITCH * 16;   // bytes
+  static constexpr int V_TILE = kBN * CPR_V * 16;
+  static constexpr int LDS_BYTES = 2 * (K_TILE + V_TILE);
+  static constexpr int K_LOADS = (KPITCH + kWaves - 1) / kWaves;  // wave-loads per wave
+  static constexpr int V_LOADS = (CPR_V + kWaves - 1) / kWaves;
+  static_assert(CPR_V == 8 || CPR_V == 12 || CPR_V == 16, "V swizzle defined for 8/12/16 chunks");
 };
 
-// Position of key kappa (0..63) inside a V^T row: bits 2 and 3 swapped, so
-// the 8 keys one lane feeds to one PV MFMA are adjacent (see file comment).
-__device__ __forceinline__ int vt_pos(int kappa) {
-  return (kappa & ~12) | ((kappa & 4) << 1) | ((kappa & 8) >> 1);
+// XOR applied to the chunk index of V row `row` (see Cfg).
+template <int CPR_V>
+__host__ __device__ constexpr int v_swizzle(int row) {
+  return CPR_V == 16 ? 4 * (row & 3) : (CPR_V == 8 ? 4 * ((row >> 1) & 1) : 0);
+}
+
+// 16-byte-per-lane load from a buffer straight into LDS: lane i's bytes land
+// at dst + 16 i; offsets past the buffer's range read as zero.  (A plain
+// device function: inside the kernel template the builtin trips the host pass.)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, lds_char* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
 }
 
 template <bool B>
@@ -95,10 +117,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int DQK, int DV, int NQB>
+__device__ __forceinline__ bf16x8 lds_read_b128(const lds_char* base, int byte_off) {
+  return *(const __attribute__((address_space(3))) bf16x8*)(base + byte_off);
+}
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const lds_char* base, int byte_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(base + byte_off));
+}
+
+template <int DQK, int DV>
 __global__ __launch_bounds__(kThreads) void varlen_attn_fwd_kernel(Params p) {
-  using C = Cfg<DQK, DV, NQB>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  using C = Cfg<DQK, DV>;
+  __shared__ __attribute__((aligned(1024))) char lds_raw[C::LDS_BYTES];
+  lds_char* lds = (lds_char*)lds_raw;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -107,9 +138,9 @@ __global__ __launch_bounds__(kThreads) void varlen_attn_fwd_kernel(Params p) {
   const int g = lane >> 5;
 
   // ---- work unit: XCD-aware remap, then (segment, head, q-tile) ----------
-  // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs;
-  // give each XCD a contiguous run of work ids so the q-tiles of one
-  // (segment, head) share that XCD's L2 while they stream the same K/V.
+  // Workgroup ids are dispatched round-robin over the 8 XCDs; give each XCD
+  // a contiguous run of work ids so the q-tiles of one (segment, head) share
+  // that XCD's L2 while they stream the same K/V.
   const int w = blockIdx.x;
   const int N = p.num_blocks;
   const int per = N >> 3, rem = N & 7;
@@ -126,269 +157,230 @@ __global__ __launch_bounds__(kThreads) void varlen_attn_fwd_kernel(Params p) {
   const int Lq = p.cu_q[b + 1] - q0;
   const int k0 = p.cu_k[b];
   const int Lk = p.cu_k[b + 1] - k0;
-  const int r0 = qt * C::BM;
+  const int r0 = qt * kBM;
   if (r0 >= Lq) return;
-  const int r1 = min(r0 + C::BM, Lq);
+  const int r1 = min(r0 + kBM, Lq);
   const TileRange tr = tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN);
-
-  const int wrow0 = r0 + wave * NQB * 32;
+  const int ntiles = tr.kt_end - tr.kt_begin;
+  const int wrow0 = r0 + wave * 32;
+  const int myrow = wrow0 + l32;
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ---------
-  bf16x8 qf[NQB][C::KC];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int row = wrow0 + qb * 32 + l32;
-    const uint16_t* src = p.q + (int64_t)(q0 + row) * p.q_row + (int64_t)h * p.q_head;
+  bf16x8 qf[C::KC];
+  {
+    const uint16_t* src = p.q + (int64_t)(q0 + myrow) * p.q_row + (int64_t)h * p.q_head;
 #pragma unroll
     for (int c = 0; c < C::KC; ++c) {
       const int d = c * 16 + 8 * g;
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < r1 && d < DQK) x = *(const u32x4*)(src + d);
-      qf[qb][c] = __builtin_bit_cast(bf16x8, x);
+      if (myrow < r1 && d < DQK) x = *(const u32x4*)(src + d);
+      qf[c] = __builtin_bit_cast(bf16x8, x);
     }
   }
 
-  // Padded V^T rows [DV, DVP) only feed output rows that are never stored;
-  // clear them once so the LDS holds no stale data.
-  if constexpr (C::DVP > DV) {
-    constexpr int kPad = (C::DVP - DV) * C::VT_PITCH;
-    for (int i = tid; i < 2 * kPad; i += kThreads) {
-      const int bsel = i / kPad;
-      lds[bsel * (C::K_TILE + C::VT_TILE) + C::K_TILE + DV * C::VT_PITCH + i % kPad] = 0;
-    }
+  // ---- per-lane offsets of the direct-to-LDS tile loads --------------------
+  // K wave-load j covers LDS chunk slots [64 j, 64 j + 64) of the tile; slot
+  // s holds row s / KPITCH, chunk s % KPITCH (the last chunk of a row is pad).
+  const int64_t k_row_b = p.k_row * 2, v_row_b = p.v_row * 2;
+  uint32_t koff[C::K_LOADS];
+  bool kact[C::K_LOADS];
+#pragma unroll
+  for (int i = 0; i < C::K_LOADS; ++i) {
+    const int s = (wave + kWaves * i) * 64 + lane;
+    const int row = s / C::KPITCH, c = s % C::KPITCH;
+    kact[i] = c < C::CPR_K;
+    koff[i] = c < C::K_REAL ? (uint32_t)(row * k_row_b + c * 16) : kOOB;  // 72: chunk 9 -> zeros
   }
-
-  const uint16_t* kbase = p.k + (int64_t)k0 * p.k_row + (int64_t)h * p.k_head;
-  const uint16_t* vbase = p.v + (int64_t)k0 * p.v_row + (int64_t)h * p.v_head;
-
-  u32x4 kreg[C::K_ITERS];
-  u32x4 vreg[C::V_ITERS][4];
-
-  auto load_tile = [&](int t) {
-    const int key0 = t * kBN;
+  uint32_t voff[C::V_LOADS];
+  bool vact[C::V_LOADS];
 #pragma unroll
-    for (int i = 0; i < C::K_ITERS; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c / (C::DQKP / 8);
-      const int col = (c % (C::DQKP / 8)) * 8;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (c < C::K_CHUNKS && key0 + row < Lk && col < DQK)
-        x = *(const u32x4*)(kbase + (int64_t)(key0 + row) * p.k_row + col);
-      kreg[i] = x;
+  for (int i = 0; i < C::V_LOADS; ++i) {
+    const int s = (wave + kWaves * i) * 64 + lane;
+    const int row = s / C::CPR_V;
+    const int c = (s % C::CPR_V) ^ v_swizzle<C::CPR_V>(row);
+    vact[i] = c < C::V_REAL;  // padded dv chunks are never loaded
+    voff[i] = (uint32_t)(row * v_row_b + c * 16);
+  }
+  const char* kseg = (const char*)(p.k + (int64_t)k0 * p.k_row + (int64_t)h * p.k_head);
+  const char* vseg = (const char*)(p.v + (int64_t)k0 * p.v_row + (int64_t)h * p.v_head);
+
+  auto kbuf = [&](int i) { return lds + (i & 1) * (C::K_TILE + C::V_TILE); };
+  auto vbuf = [&](int i) { return lds + (i & 1) * (C::K_TILE + C::V_TILE) + C::K_TILE; };
+
+  auto load_k = [&](int tile, lds_char* dst) {
+    const int key0 = tile * kBN;
+    const int rows = min(Lk - key0, kBN);
+    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kseg + key0 * k_row_b), (short)0, (int)(rows * k_row_b), kBufferFlags);
+#pragma unroll
+    for (int i = 0; i < C::K_LOADS; ++i) {
+      const int wl = wave + kWaves * i;
+      if (wl < C::KPITCH && kact[i])
+        dma16(rs, dst + wl * 1024, koff[i]);
     }
+  };
+  auto load_v = [&](int tile, lds_char* dst) {
+    const int key0 = tile * kBN;
+    const int rows = min(Lk - key0, kBN);
+    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vseg + key0 * v_row_b), (short)0, (int)(rows * v_row_b), kBufferFlags);
 #pragma unroll
-    for (int i = 0; i < C::V_ITERS; ++i) {
-      const int u = tid + i * kThreads;
-      const int kg = u & 15;
-      const int dc = u >> 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = key0 + 4 * kg + e;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (u < C::V_UNITS && key < Lk) x = *(const u32x4*)(vbase + (int64_t)key * p.v_row + dc * 8);
-        vreg[i][e] = x;
-      }
+    for (int i = 0; i < C::V_LOADS; ++i) {
+      const int wl = wave + kWaves * i;
+      if (wl < C::CPR_V && vact[i])
+        dma16(rs, dst + wl * 1024, voff[i]);
     }
   };
 
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = lds + buf * (C::K_TILE + C::VT_TILE);
-    uint16_t* vts = ks + C::K_TILE;
+  // ---- per-lane LDS read offsets -------------------------------------------
+  // K operand: row kb*32 + l32, chunk 2c + g  ->  k_rd + kb*32*KPITCH*16 + 32c
+  const int k_rd = (l32 * C::KPITCH + g) * 16;
+  // V^T operand via transposing reads: lane i of 16-lane group G supplies
+  // row (4g + i/4) [+ 16t + 8h], dv 32vb + 16(G%2) + 4(i%4).
+  int v_rd[C::VB];
+  {
+    const int G = lane >> 4, i = lane & 15;
+    const int vrow = 4 * g + (i >> 2);
+    const int y = 2 * (G & 1) + ((i >> 1) & 1);
 #pragma unroll
-    for (int i = 0; i < C::K_ITERS; ++i) {
-      const int c = tid + i * kThreads;
-      if (c < C::K_CHUNKS) {
-        const int row = c / (C::DQKP / 8);
-        const int col = (c % (C::DQKP / 8)) * 8;
-        *(u32x4*)(ks + row * C::K_PITCH + col) = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::V_ITERS; ++i) {
-      const int u = tid + i * kThreads;
-      if (u < C::V_UNITS) {
-        const int kg = u & 15;
-        const int dc = u >> 4;
-        const int pos = vt_pos(4 * kg);
-#pragma unroll
-        for (int dw = 0; dw < 4; ++dw) {
-          // dv = dc*8 + 2*dw (low halves) and dc*8 + 2*dw + 1 (high halves)
-          const uint32_t a0 = vreg[i][0][dw], a1 = vreg[i][1][dw];
-          const uint32_t a2 = vreg[i][2][dw], a3 = vreg[i][3][dw];
-          u32x2 lo, hi;
-          lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-          lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-          hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-          hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-          const int dv = dc * 8 + 2 * dw;
-          *(u32x2*)(vts + dv * C::VT_PITCH + pos) = lo;
-          *(u32x2*)(vts + (dv + 1) * C::VT_PITCH + pos) = hi;
-        }
-      }
-    }
-  };
+    for (int vb = 0; vb < C::VB; ++vb)
+      v_rd[vb] = (vrow * C::CPR_V + ((4 * vb + y) ^ v_swizzle<C::CPR_V>(vrow))) * 16 + 8 * (i & 1);
+  }
 
   // ---- running state -------------------------------------------------------
-  f32x16 acc[C::VB][NQB];
+  f32x16 acc[C::VB];
 #pragma unroll
   for (int vb = 0; vb < C::VB; ++vb)
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[vb][qb][r] = 0.f;
-  float m_run[NQB], l_run[NQB];
-  int row_lo[NQB], row_hi[NQB];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
-    const RowBounds rb = row_bounds(wrow0 + qb * 32 + l32, Lq, Lk, p.causal, p.wl, p.wr);
-    // clamp into int range: lo in [0, Lk], hi in [-1, Lk - 1]
-    row_lo[qb] = (int)imin64(rb.lo, (int64_t)Lk);
-    row_hi[qb] = (int)imax64(rb.hi, (int64_t)-1);
+    for (int r = 0; r < 16; ++r) acc[vb][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  int row_lo, row_hi;
+  {
+    const RowBounds rb = row_bounds(myrow, Lq, Lk, p.causal, p.wl, p.wr);
+    row_lo = (int)imin64(rb.lo, (int64_t)Lk);  // clamp into int range
+    row_hi = (int)imax64(rb.hi, (int64_t)-1);
   }
 
-  auto process_tile = [&](const uint16_t* ks, const uint16_t* vts, int key0, auto masked_tag) {
-    constexpr bool kMasked = decltype(masked_tag)::value;
-    // S^T = K Q^T : [keys 64 = 2 x 32] x [queries NQB x 32]
-    f32x16 s[2][NQB];
+  auto qk = [&](const lds_char* ks, f32x16 (&s)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
     for (int c = 0; c < C::KC; ++c) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = *(const bf16x8*)(ks + (kb * 32 + l32) * C::K_PITCH + c * 16 + 8 * g);
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][c], s[kb][qb], 0, 0, 0);
-      }
-    }
-
-    // Lane holds, for query column l32 of block qb, keys
-    //   key0 + 32*kb + 8*(r/4) + 4*g + (r%4),  r = 0..15.
-    if constexpr (kMasked) {
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = key0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool vis = (j >= row_lo[qb]) && (j <= row_hi[qb]);
-            s[kb][qb][r] = vis ? s[kb][qb][r] : -INFINITY;
-          }
-    }
-
-    float m_new[NQB];
-    bool need = false;
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      float mx = s[0][qb][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      m_new[qb] = fmaxf(m_run[qb], mx * p.scale_log2);
-      need |= m_new[qb] > m_run[qb] + kRescaleTau;
-    }
-    if (__any(need)) {
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const float alpha = (m_new[qb] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new[qb]);
-        m_run[qb] = m_new[qb];
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int vb = 0; vb < C::VB; ++vb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[vb][qb][r] *= alpha;
-      }
-    }
-
-    // P = exp2(s * scale*log2e - m), packed to bf16 as the PV B operand.
-    bf16x8 pf[NQB][4];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-      float sum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 8 * (t & 1) + 2 * e;
-          const float x0 = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][qb][r], p.scale_log2, -m_use));
-          const float x1 = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][qb][r + 1], p.scale_log2, -m_use));
-          sum += x0 + x1;
-          pk[e] = pack_bf16x2(x0, x1);
-        }
-        pf[qb][t] = __builtin_bit_cast(bf16x8, pk);
-      }
-      l_run[qb] += sum;
-    }
-
-    // O^T += V^T P^T : [dv] x [queries], K = 16 keys per MFMA
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int vb = 0; vb < C::VB; ++vb) {
-        const bf16x8 vf = *(const bf16x8*)(vts + (vb * 32 + l32) * C::VT_PITCH + 16 * t + 8 * g);
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-          acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][t], acc[vb][qb], 0, 0, 0);
+        const bf16x8 kf = lds_read_b128(ks, k_rd + kb * 32 * C::KPITCH * 16 + 32 * c);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
       }
     }
   };
 
-
-  if (tr.kt_begin < tr.kt_end) {
-    load_tile(tr.kt_begin);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int t = tr.kt_begin; t < tr.kt_end; ++t) {
-    const int buf = (t - tr.kt_begin) & 1;
-    const bool more = t + 1 < tr.kt_end;
-    if (more) load_tile(t + 1);
-    const uint16_t* ks = lds + buf * (C::K_TILE + C::VT_TILE);
-    const uint16_t* vts = ks + C::K_TILE;
-    if (t >= tr.full_begin && t < tr.full_end)
-      process_tile(ks, vts, t * kBN, BoolTag<false>{});
-    else
-      process_tile(ks, vts, t * kBN, BoolTag<true>{});
-    if (more) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue ------------------------------------------------------------
+  // Softmax of one tile of scores (lane: query l32, keys
+  // key0 + 32 kb + 8 (r / 4) + 4 g + r % 4) and the PV product.
+  auto softmax_pv = [&](f32x16 (&s)[2], const lds_char* vs, int key0, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    if constexpr (kMasked) {
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const float l = l_run[qb] + __shfl_xor(l_run[qb], 32);
-    const int row = wrow0 + qb * 32 + l32;
-    if (row < r1) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      uint16_t* dst = p.o + (int64_t)(q0 + row) * p.o_row + (int64_t)h * p.o_head;
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = key0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+          s[kb][r] = (j >= row_lo && j <= row_hi) ? s[kb][r] : -INFINITY;
+        }
+    }
+    float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * p.scale_log2);
+    if (__any(m_new > m_run + kRescaleTau)) {
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int vb = 0; vb < C::VB; ++vb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int dv = vb * 32 + 8 * j + 4 * g;
-          if (dv < DV) {
-            u32x2 o2;
-            o2[0] = pack_bf16x2(acc[vb][qb][4 * j] * inv, acc[vb][qb][4 * j + 1] * inv);
-            o2[1] = pack_bf16x2(acc[vb][qb][4 * j + 2] * inv, acc[vb][qb][4 * j + 3] * inv);
-            *(u32x2*)(dst + dv) = o2;
-          }
-        }
-      if (p.lse != nullptr && g == 0) {
-        const float lse = l > 0.f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
-        p.lse[(int64_t)h * p.total_q + q0 + row] = lse;
+        for (int r = 0; r < 16; ++r) acc[vb][r] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    bf16x8 pf[4];
+    float sum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      u32x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 8 * (t & 1) + 2 * e;
+        const float x0 = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][r], p.scale_log2, -m_use));
+        const float x1 = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][r + 1], p.scale_log2, -m_use));
+        sum += x0 + x1;
+        pk[e] = pack_bf16x2(x0, x1);
       }
+      pf[t] = __builtin_bit_cast(bf16x8, pk);
+    }
+    l_run += sum;
+    // O^T += V^T P^T: [dv] x [queries], 16 keys per MFMA.
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int vb = 0; vb < C::VB; ++vb) {
+        const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
+        const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
+        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], acc[vb], 0, 0, 0);
+      }
+    }
+  };
+
+  // Tile j (counted from kt_begin) lives in buffer j % 2; while step i
+  // computes on buffer i % 2, tile i + 1 streams into the other buffer.
+  auto step = [&](int i, auto masked_tag) {
+    if (i + 1 < ntiles) {
+      load_k(tr.kt_begin + i + 1, kbuf(i + 1));
+      load_v(tr.kt_begin + i + 1, vbuf(i + 1));
+    }
+    f32x16 s[2];
+    qk(kbuf(i), s);
+    softmax_pv(s, vbuf(i), (tr.kt_begin + i) * kBN, masked_tag);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  if (ntiles > 0) {
+    load_k(tr.kt_begin, kbuf(0));
+    load_v(tr.kt_begin, vbuf(0));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int i = 0; i < ntiles; ++i) {
+      const int t = tr.kt_begin + i;
+      if (t >= tr.full_begin && t < tr.full_end)
+        step(i, BoolTag<false>{});
+      else
+        step(i, BoolTag<true>{});
+    }
+  }
+
+  // ---- epilogue ------------------------------------------------------------
+  const float l = l_run + __shfl_xor(l_run, 32);
+  if (myrow < r1) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* dst = p.o + (int64_t)(q0 + myrow) * p.o_row + (int64_t)h * p.o_head;
+#pragma unroll
+    for (int vb = 0; vb < C::VB; ++vb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int dv = vb * 32 + 8 * j + 4 * g;
+        if (dv < DV) {
+          u32x2 o2;
+          o2[0] = pack_bf16x2(acc[vb][4 * j] * inv, acc[vb][4 * j + 1] * inv);
+          o2[1] = pack_bf16x2(acc[vb][4 * j + 2] * inv, acc[vb][4 * j + 3] * inv);
+          *(u32x2*)(dst + dv) = o2;
+        }
+      }
+    if (p.lse != nullptr && g == 0) {
+      const float lse = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+      p.lse[(int64_t)h * p.total_q + q0 + myrow] = lse;
     }
   }
 }
@@ -400,48 +392,37 @@ __global__ __launch_bounds__(kThreads) void varlen_attn_fwd_kernel(Params p) {
 // ============================================================================
 namespace va {
 
-template <int DQK, int DV, int NQB>
+template <int DQK, int DV>
 static const void* kernel_ptr() {
-  return (const void*)&varlen_attn_fwd_kernel<DQK, DV, NQB>;
+  return (const void*)&varlen_attn_fwd_kernel<DQK, DV>;
 }
 
 struct Variant {
   const void* fn;
-  int block_m;
   int lds_bytes;
 };
-
-template <int DQK, int DV>
-static Variant pick_nqb(int nqb) {
-  (void)nqb;
-  return {kernel_ptr<DQK, DV, 1>(), Cfg<DQK, DV, 1>::BM, Cfg<DQK, DV, 1>::LDS_ELEMS * 2};
-}
 
 static bool supported_dims(int dqk, int dv) {
   return (dqk == 64 && dv == 64) || (dqk == 72 && dv == 72) || (dqk == 80 && dv == 80) ||
          (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128);
 }
 
-// Query rows per wave, in 32-row blocks.  One block per wave for now: two
-// blocks halve the LDS reads per MFMA but do not fit the register file
-// without spilling in this loop structure.
-static int choose_nqb(int max_seqlen_q) {
-  (void)max_seqlen_q;
-  return 1;
-}
-
-static Variant variant_for(int dqk, int dv, int nqb) {
-  if (dqk == 64) return pick_nqb<64, 64>(nqb);
-  if (dqk == 72) return pick_nqb<72, 72>(nqb);
-  if (dqk == 80) return pick_nqb<80, 80>(nqb);
-  if (dqk == 128) return pick_nqb<128, 128>(nqb);
-  return pick_nqb<192, 128>(nqb);
+static Variant variant_for(int dqk, int dv) {
+  if (dqk == 64) return {kernel_ptr<64, 64>(), Cfg<64, 64>::LDS_BYTES};
+  if (dqk == 72) return {kernel_ptr<72, 72>(), Cfg<72, 72>::LDS_BYTES};
+  if (dqk == 80) return {kernel_ptr<80, 80>(), Cfg<80, 80>::LDS_BYTES};
+  if (dqk == 128) return {kernel_ptr<128, 128>(), Cfg<128, 128>::LDS_BYTES};
+  return {kernel_ptr<192, 128>(), Cfg<192, 128>::LDS_BYTES};
 }
 
 static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
+// Row strides above 2^24 elements would overflow the 32-bit offsets of the
+// per-tile buffer loads (64 rows x stride x 2 bytes).
+static constexpr int64_t kMaxRowStride = (int64_t)1 << 24;
+
 static int check_tensor(const va_tensor* t, bool need_data) {
-  if (t->row_stride <= 0 || t->head_stride <= 0) return VA_ERR_STRIDE;
+  if (t->row_stride <= 0 || t->head_stride <= 0 || t->row_stride > kMaxRowStride) return VA_ERR_STRIDE;
   if ((t->row_stride & 7) != 0 || (t->head_stride & 7) != 0) return VA_ERR_ALIGN;
   if (need_data && t->data == nullptr) return VA_ERR_NULL;
   if (!aligned16(t->data)) return VA_ERR_ALIGN;
@@ -489,12 +470,12 @@ extern "C" int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t
   if (!plan) return VA_ERR_NULL;
   if (!va::supported_dims(head_dim_qk, head_dim_v)) return VA_ERR_HEADDIM;
   if (batch < 0 || num_heads <= 0 || max_seqlen_q < 0) return VA_ERR_ARG;
-  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, va::choose_nqb(max_seqlen_q));
-  plan->block_m = var.block_m;
+  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v);
+  plan->block_m = va::kBM;
   plan->block_n = va::kBN;
   plan->threads = va::kThreads;
   plan->lds_bytes = var.lds_bytes;
-  const int64_t n_qt = ((int64_t)max_seqlen_q + var.block_m - 1) / var.block_m;
+  const int64_t n_qt = ((int64_t)max_seqlen_q + va::kBM - 1) / va::kBM;
   plan->grid = n_qt * num_heads * (int64_t)batch;
   plan->kernel = "varlen_attn_fwd_kernel";
   return VA_OK;
@@ -527,8 +508,8 @@ extern "C" int varlen_attn_fwd(const va_tensor* q, const va_tensor* k, const va_
   if (batch == 0 || max_seqlen_q == 0 || q->rows == 0) return VA_OK;
   if (!cu_seqlens_q || !cu_seqlens_k) return VA_ERR_NULL;
 
-  const Variant var = variant_for(q->dim, v->dim, choose_nqb(max_seqlen_q));
-  const int64_t n_qt = ((int64_t)max_seqlen_q + var.block_m - 1) / var.block_m;
+  const Variant var = variant_for(q->dim, v->dim);
+  const int64_t n_qt = ((int64_t)max_seqlen_q + kBM - 1) / kBM;
   const int64_t grid = n_qt * q->heads * (int64_t)batch;
   if (grid > INT32_MAX) return VA_ERR_SHAPE;
 

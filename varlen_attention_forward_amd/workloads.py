@@ -203,8 +203,10 @@ def make_inputs(
     window: tuple = (-1, -1),
     softmax_scale: Optional[float] = None,
     std: float = 1.0,
+    v_std: float = 1.0,
 ) -> Inputs:
-    """Draw Q, K, V ~ N(0, std^2) in float32 (in that order) and round to bf16."""
+    """Draw Q, K ~ N(0, std^2) and V ~ N(0, v_std^2) in float32 (in that order)
+    and round to bf16."""
     assert len(seqlens_q) == len(seqlens_k)
     g = torch.Generator().manual_seed(seed)
     tq, tk = int(sum(seqlens_q)), int(sum(seqlens_k))
@@ -212,7 +214,9 @@ def make_inputs(
     k = torch.randn((tk, num_heads, head_dim_qk), generator=g, dtype=torch.float32)
     v = torch.randn((tk, num_heads, head_dim_v), generator=g, dtype=torch.float32)
     if std != 1.0:
-        q, k, v = q * std, k * std, v * std
+        q, k = q * std, k * std
+    if v_std != 1.0:
+        v = v * v_std
     scale = head_dim_qk ** -0.5 if softmax_scale is None else float(softmax_scale)
     return Inputs(
         q=q.to(torch.bfloat16),

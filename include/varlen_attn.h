@@ -51,7 +51,7 @@ extern "C" {
 #define VA_ERR_NULL (-1)    /* a required pointer is NULL */
 #define VA_ERR_SHAPE (-2)   /* rows/heads disagree between tensors, or sizes out of range */
 #define VA_ERR_HEADDIM (-3) /* (head_dim_qk, head_dim_v) is not a supported pair */
-#define VA_ERR_STRIDE (-4)  /* a stride is not positive */
+#define VA_ERR_STRIDE (-4)  /* a stride is not positive, or a row stride exceeds 2^24 elements */
 #define VA_ERR_ALIGN (-5)   /* a pointer or stride breaks the 16-byte alignment rule */
 #define VA_ERR_ARG (-6)     /* a scalar argument is out of range */
 #define VA_ERR_LAUNCH (-7)  /* the HIP kernel launch failed */
@@ -131,6 +131,18 @@ int varlen_attn_tile_range(int32_t seqlen_q, int32_t seqlen_k, int32_t row_begin
                            int32_t causal, int32_t window_left, int32_t window_right,
                            int32_t block_n, int32_t* kt_begin, int32_t* kt_end,
                            int32_t* full_begin, int32_t* full_end);
+
+/*
+ * The kernel's workgroup-to-work mapping, computed on the host by the same
+ * function the kernel runs (exported for tests).  For workgroup `block` of
+ * the grid varlen_attn_fwd launches for (batch, num_heads, max_seqlen_q,
+ * causal), returns the segment, head and q-tile (block_m query rows) it
+ * owns, or -1 in all three for a padding workgroup that exits at once.
+ * Returns VA_OK, or VA_ERR_ARG for a block outside the grid / bad sizes.
+ * Host only; makes no HIP call.
+ */
+int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_heads, int32_t max_seqlen_q,
+                          int32_t causal, int32_t* segment, int32_t* head, int32_t* q_tile);
 
 /* Launch shape varlen_attn_fwd would use (host only; makes no HIP call). */
 typedef struct va_plan {

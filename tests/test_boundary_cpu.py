@@ -150,8 +150,11 @@ def test_empty_work_returns_ok_without_launch():
 
 def test_plan():
     p = pkg.plan(80, 80, 8, 16, 4096, 4096)
-    assert p["block_n"] == 64 and p["threads"] == 256 and p["kernel"] == "varlen_attn_fwd_kernel"
+    assert p["block_n"] == 64 and p["threads"] in (256, 512) and p["kernel"] == "varlen_attn_fwd_kernel"
+    # 8 x 16 (segment, head) groups, already a multiple of the 8 XCDs
     assert p["grid"] == 8 * 16 * -(-4096 // p["block_m"])
+    # 3 x 5 = 15 groups pad to 16
+    assert pkg.plan(80, 80, 3, 5, 4096, 4096)["grid"] == 16 * -(-4096 // p["block_m"])
     with pytest.raises(ValueError):
         pkg.plan(96, 96, 1, 1, 10, 10)
 
@@ -248,3 +251,44 @@ def test_tile_range_rejects_bad_arguments():
         pkg.tile_range(10, 10, 0, 11, 0, -1, -1, 64)
     with pytest.raises(ValueError):
         pkg.tile_range(10, 10, 0, 10, 0, -1, -1, 0)
+
+
+# ---------------------------------------------------------------------------
+# workgroup -> (segment, head, q-tile) mapping
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("batch,heads,max_q,causal", [
+    (8, 16, 4096, 0), (36, 16, 256, 0), (1, 16, 65536, 0), (4, 128, 4096, 1), (3, 5, 700, 1), (1, 1, 1, 0),
+])
+def test_work_unit_covers_every_tile_once(batch, heads, max_q, causal):
+    p = pkg.plan(64, 64, batch, heads, max_q, max_q, causal)
+    n_qt = -(-max_q // p["block_m"])
+    seen = {}
+    pad = 0
+    for blk in range(p["grid"]):
+        b, h, qt = pkg.work_unit(blk, batch, heads, max_q, causal)
+        if b < 0:
+            pad += 1
+            continue
+        assert 0 <= b < batch and 0 <= h < heads and 0 <= qt < n_qt
+        key = (b, h, qt)
+        assert key not in seen, (blk, key, seen.get(key))
+        seen[key] = blk
+        # groups are dealt round-robin over the 8 XCDs (block % 8)
+        assert (b * heads + h) % 8 == blk % 8
+    assert len(seen) == batch * heads * n_qt
+    assert pad == p["grid"] - batch * heads * n_qt and pad < 8 * n_qt
+    if causal:
+        # within a group, the q-tile with the most keys is dispatched first
+        first = {}
+        for (b, h, qt), blk in seen.items():
+            if (b, h) not in first or blk < first[(b, h)][0]:
+                first[(b, h)] = (blk, qt)
+        assert all(qt == n_qt - 1 for _, qt in first.values())
+
+
+def test_work_unit_rejects_out_of_grid():
+    p = pkg.plan(64, 64, 2, 3, 100, 100)
+    with pytest.raises(ValueError):
+        pkg.work_unit(p["grid"], 2, 3, 100)
+    with pytest.raises(ValueError):
+        pkg.work_unit(-1, 2, 3, 100)

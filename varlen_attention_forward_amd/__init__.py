@@ -15,12 +15,14 @@ from ._binding import (  # noqa: F401
     status_string,
     tile_range,
     varlen_attn_fwd,
+    work_unit,
 )
 
 __all__ = [
     "varlen_attn_fwd",
     "status_string",
     "tile_range",
+    "work_unit",
     "plan",
     "library",
     "raw_fwd",

@@ -90,4 +90,37 @@ VA_HD TileRange tile_range(int64_t Lq, int64_t Lk, int64_t r0, int64_t r1, int c
   return t;
 }
 
+// ---------------------------------------------------------------------------
+// Workgroup -> (segment, head, q-tile).
+//
+// The hardware dispatches workgroup w to XCD w % 8 (8 XCDs, each with its own
+// L2).  Work is grouped by (segment b, head h), g = b * heads + h, each group
+// owning n_qt q-tiles that stream the same K/V.  Groups are dealt round-robin
+// over the XCDs (group g -> XCD g % 8) so every XCD gets the same mix of
+// segments, and the q-tiles of one group sit next to each other in their
+// XCD's dispatch order so they run together and share that XCD's L2.
+// The grid is padded to a multiple of 8 groups; padding blocks get valid = 0.
+struct WorkUnit {
+  int32_t b, h, qt;
+  int32_t valid;
+};
+
+VA_HD int64_t grid_blocks(int64_t batch, int64_t heads, int64_t n_qt) {
+  const int64_t groups = batch * heads;
+  return 8 * ((groups + 7) / 8) * n_qt;
+}
+
+VA_HD WorkUnit decode_block(int64_t w, int64_t batch, int64_t heads, int64_t n_qt, int causal) {
+  const int64_t x = w & 7, k = w >> 3;
+  const int64_t gl = k / n_qt, qi = k % n_qt;
+  const int64_t g = gl * 8 + x;
+  WorkUnit u;
+  u.valid = g < batch * heads;
+  u.b = (int32_t)(g / heads);
+  u.h = (int32_t)(g % heads);
+  // Causal: the last q-tiles of a segment see the most keys; start them first.
+  u.qt = (int32_t)(causal ? n_qt - 1 - qi : qi);
+  return u;
+}
+
 }  // namespace va

@@ -63,7 +63,7 @@ struct Params {
   const int32_t* cu_k;
   int64_t q_row, q_head, k_row, k_head, v_row, v_head, o_row, o_head;  // elements
   int64_t total_q;
-  int32_t batch, heads, n_qt, num_blocks;
+  int32_t batch, heads, n_qt;
   int32_t causal, wl, wr;
   float scale_log2;  // softmax_scale * log2(e)
 };
@@ -137,21 +137,10 @@ __global__ __launch_bounds__(kThreads) void varlen_attn_fwd_kernel(Params p) {
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  // ---- work unit: XCD-aware remap, then (segment, head, q-tile) ----------
-  // Workgroup ids are dispatched round-robin over the 8 XCDs; give each XCD
-  // a contiguous run of work ids so the q-tiles of one (segment, head) share
-  // that XCD's L2 while they stream the same K/V.
-  const int w = blockIdx.x;
-  const int N = p.num_blocks;
-  const int per = N >> 3, rem = N & 7;
-  const int xcd = w & 7, slot = w >> 3;
-  const int lin = xcd * per + (xcd < rem ? xcd : rem) + slot;
-  const int qt_idx = lin % p.n_qt;
-  const int rest = lin / p.n_qt;
-  const int h = rest % p.heads;
-  const int b = rest / p.heads;
-  // Causal: the last q-tiles see the most keys; start them first.
-  const int qt = p.causal ? (p.n_qt - 1 - qt_idx) : qt_idx;
+  // ---- work unit (see decode_block in tile_schedule.h) -------------------
+  const WorkUnit wu = decode_block(blockIdx.x, p.batch, p.heads, p.n_qt, p.causal);
+  if (!wu.valid) return;
+  const int b = wu.b, h = wu.h, qt = wu.qt;
 
   const int q0 = p.cu_q[b];
   const int Lq = p.cu_q[b + 1] - q0;
@@ -462,6 +451,20 @@ extern "C" int varlen_attn_tile_range(int32_t seqlen_q, int32_t seqlen_k, int32_
   return VA_OK;
 }
 
+extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_heads,
+                                     int32_t max_seqlen_q, int32_t causal, int32_t* segment,
+                                     int32_t* head, int32_t* q_tile) {
+  if (!segment || !head || !q_tile) return VA_ERR_NULL;
+  if (batch < 0 || num_heads <= 0 || max_seqlen_q <= 0 || (causal != 0 && causal != 1)) return VA_ERR_ARG;
+  const int64_t n_qt = ((int64_t)max_seqlen_q + va::kBM - 1) / va::kBM;
+  if (block < 0 || block >= va::grid_blocks(batch, num_heads, n_qt)) return VA_ERR_ARG;
+  const va::WorkUnit u = va::decode_block(block, batch, num_heads, n_qt, causal);
+  *segment = u.valid ? u.b : -1;
+  *head = u.valid ? u.h : -1;
+  *q_tile = u.valid ? u.qt : -1;
+  return VA_OK;
+}
+
 extern "C" int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch,
                                 int32_t num_heads, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                 int32_t causal, va_plan* plan) {
@@ -476,7 +479,7 @@ extern "C" int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t
   plan->threads = va::kThreads;
   plan->lds_bytes = var.lds_bytes;
   const int64_t n_qt = ((int64_t)max_seqlen_q + va::kBM - 1) / va::kBM;
-  plan->grid = n_qt * num_heads * (int64_t)batch;
+  plan->grid = va::grid_blocks(batch, num_heads, n_qt);
   plan->kernel = "varlen_attn_fwd_kernel";
   return VA_OK;
 }
@@ -510,7 +513,7 @@ extern "C" int varlen_attn_fwd(const va_tensor* q, const va_tensor* k, const va_
 
   const Variant var = variant_for(q->dim, v->dim);
   const int64_t n_qt = ((int64_t)max_seqlen_q + kBM - 1) / kBM;
-  const int64_t grid = n_qt * q->heads * (int64_t)batch;
+  const int64_t grid = grid_blocks(batch, q->heads, n_qt);
   if (grid > INT32_MAX) return VA_ERR_SHAPE;
 
   Params p;
@@ -533,7 +536,6 @@ extern "C" int varlen_attn_fwd(const va_tensor* q, const va_tensor* k, const va_
   p.batch = batch;
   p.heads = q->heads;
   p.n_qt = (int32_t)n_qt;
-  p.num_blocks = (int32_t)grid;
   p.causal = causal;
   p.wl = window_left;
   p.wr = window_right;

@@ -25,6 +25,9 @@ HIPCC_FLAGS = [
     "-std=c++17",
     "-shared",
     "-fPIC",
+    # Inputs are finite and masked scores are -inf, never NaN: lets fmaxf map
+    # to v_max3_f32 without NaN-quieting copies.
+    "-fno-honor-nans",
     # Keep the compiler from forming packed fp32 VALU ops in device code.
     "-Xclang",
     "-target-feature",

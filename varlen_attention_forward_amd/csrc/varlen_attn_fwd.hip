@@ -19,8 +19,9 @@
 // the B operand of the PV product, with the key order inside each 16-key
 // group permuted identically on the V side.
 //
-// While a tile is computed, the next one streams into the other LDS buffer;
-// the two waves on each SIMD overlap one's MFMAs with the other's softmax.
+// The two waves on each SIMD run half a tile apart (ping-pong), so one
+// wave's softmax overlaps the other's MFMAs; K/V tiles stream into LDS two
+// phases ahead of use.
 //
 // Where the pages describe FA4 on Blackwell (TMEM, tcgen05.ld.red row max,
 // 2-CTA MMA) that design is prior art only; what carries over is the online
@@ -115,6 +116,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   v[0] = (__bf16)a;  // round to nearest even
   v[1] = (__bf16)b;
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Value of lane l ^ 32 (the other half of the wave), without an LDS trip.
+__device__ __forceinline__ float other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // lanes 0-31 find the upper half's values in r[1], lanes 32-63 the lower
+  // half's in r[0]
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const lds_char* base, int byte_off) {
@@ -250,6 +259,7 @@ __global__ __launch_bounds__(kThreads) void varlen_attn_fwd_kernel(Params p) {
     row_hi = (int)imax64(rb.hi, (int64_t)-1);
   }
 
+  // S^T = K Q^T for one tile: [64 keys = 2 x 32] x [32 queries].
   auto qk = [&](const lds_char* ks, f32x16 (&s)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -265,9 +275,24 @@ __global__ __launch_bounds__(kThreads) void varlen_attn_fwd_kernel(Params p) {
     }
   };
 
-  // Softmax of one tile of scores (lane: query l32, keys
-  // key0 + 32 kb + 8 (r / 4) + 4 g + r % 4) and the PV product.
-  auto softmax_pv = [&](f32x16 (&s)[2], const lds_char* vs, int key0, auto masked_tag) {
+  // O^T += V^T P^T: [dv] x [32 queries], 16 keys per MFMA.
+  auto pv = [&](const lds_char* vs, const bf16x8 (&pf)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int vb = 0; vb < C::VB; ++vb) {
+        const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
+        const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
+        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], acc[vb], 0, 0, 0);
+      }
+    }
+  };
+
+  // Online softmax of one tile of scores.  The lane holds query l32 and keys
+  // key0 + 32 kb + 8 (r / 4) + 4 g + r % 4; it leaves the probabilities in
+  // pf, packed to bf16 as the B operand of the PV product.
+  auto softmax = [&](f32x16 (&s)[2], bf16x8 (&pf)[4], int key0, auto masked_tag) {
     constexpr bool kMasked = decltype(masked_tag)::value;
     if constexpr (kMasked) {
 #pragma unroll
@@ -281,9 +306,12 @@ __global__ __launch_bounds__(kThreads) void varlen_attn_fwd_kernel(Params p) {
     float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = fmaxf(mx, other_half(mx));
     const float m_new = fmaxf(m_run, mx * p.scale_log2);
     if (__any(m_new > m_run + kRescaleTau)) {
+      // Keeps the rescale a real branch: it is rare, and speculating it
+      // would put 16 * VB multiplies on every tile.
+      asm volatile("; lazy rescale" ::: "memory");
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
@@ -293,7 +321,6 @@ __global__ __launch_bounds__(kThreads) void varlen_attn_fwd_kernel(Params p) {
         for (int r = 0; r < 16; ++r) acc[vb][r] *= alpha;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    bf16x8 pf[4];
     float sum = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -309,49 +336,121 @@ __global__ __launch_bounds__(kThreads) void varlen_attn_fwd_kernel(Params p) {
       pf[t] = __builtin_bit_cast(bf16x8, pk);
     }
     l_run += sum;
-    // O^T += V^T P^T: [dv] x [queries], 16 keys per MFMA.
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int vb = 0; vb < C::VB; ++vb) {
-        const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
-        const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
-        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], acc[vb], 0, 0, 0);
-      }
-    }
   };
 
-  // Tile j (counted from kt_begin) lives in buffer j % 2; while step i
-  // computes on buffer i % 2, tile i + 1 streams into the other buffer.
-  auto step = [&](int i, auto masked_tag) {
-    if (i + 1 < ntiles) {
-      load_k(tr.kt_begin + i + 1, kbuf(i + 1));
-      load_v(tr.kt_begin + i + 1, vbuf(i + 1));
-    }
-    f32x16 s[2];
-    qk(kbuf(i), s);
-    softmax_pv(s, vbuf(i), (tr.kt_begin + i) * kBN, masked_tag);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  // ---- ping-pong main loop -------------------------------------------------
+  // Waves 0-3 (group 0) and 4-7 (group 1) put one wave of each group on
+  // every SIMD.  Each wave alternates an MFMA phase (PV of the previous tile,
+  // then QK^T of the current one) and a VALU phase (softmax of the current
+  // tile).  Group 1 runs one phase behind group 0, and every phase ends at a
+  // workgroup barrier, so in each slot one wave per SIMD is in its MFMA phase
+  // while the other is in its softmax.
+  //
+  // Tile j (counted from kt_begin) has K in kbuf(j) and V in vbuf(j).  The
+  // MFMA phase of tile j reads K_j and V_{j-1}; in slot 2j (the slot where
+  // group 0 starts tile j) every wave issues its share of the loads of K_{j+1}
+  // and V_j, and waits for them at the end of slot 2j + 1, so they are
+  // visible from slot 2j + 2 on.  Those buffers last held K_{j-1} and
+  // V_{j-2}, whose readers finished by slot 2j - 1.
+  const int grp = wave >> 2;
+  auto issue_loads = [&](int j) {  // K_{j+1} and V_j
+    if (j + 1 < ntiles) load_k(tr.kt_begin + j + 1, kbuf(j + 1));
+    if (j < ntiles) load_v(tr.kt_begin + j, vbuf(j));
   };
+  auto wait_loads = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   if (ntiles > 0) {
+    f32x16 s[2];
+    bf16x8 pf[4];
+    // One MFMA phase as a single stream of MFMAs: the PV product of the
+    // previous tile (4 * VB MFMAs) then QK^T of this one (2 * KC).  Each MFMA's
+    // LDS operand is read kDepth MFMAs ahead into a ring of registers, and
+    // scheduling barriers keep that order, so every 32-cycle MFMA finds its
+    // operand waiting instead of stalling on LDS latency.
+    auto mfma_phase = [&](int j, auto pv_tag) {  // slot 2j + grp
+      constexpr bool kPV = decltype(pv_tag)::value;
+      constexpr int kPVOps = kPV ? 4 * C::VB : 0;
+      constexpr int kOps = kPVOps + 2 * C::KC;
+      constexpr int kDepth = 6;
+      if (grp == 0) issue_loads(j);
+      const lds_char* vs = vbuf(j - 1);
+      const lds_char* ks = kbuf(j);
+      auto load_op = [&](int i, bf16x8& dst) {
+        if (i < kPVOps) {  // V^T operand of PV MFMA (t, vb)
+          const int t = i / C::VB, vb = i % C::VB;
+          const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
+          const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
+          dst = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {  // K operand of QK MFMA (c, kb)
+          const int c = (i - kPVOps) / 2, kb = (i - kPVOps) % 2;
+          dst = lds_read_b128(ks, k_rd + kb * 32 * C::KPITCH * 16 + 32 * c);
+        }
+      };
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      bf16x8 ring[kDepth];
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int i = 0; i < kDepth && i < kOps; ++i) load_op(i, ring[i]);
+#pragma unroll
+      for (int i = 0; i < kOps; ++i) {
+        if (i < kPVOps) {
+          const int t = i / C::VB, vb = i % C::VB;
+          acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kDepth], pf[t], acc[vb], 0, 0, 0);
+        } else {
+          const int c = (i - kPVOps) / 2, kb = (i - kPVOps) % 2;
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kDepth], qf[c], s[kb], 0, 0, 0);
+        }
+        if (i + kDepth < kOps) load_op(i + kDepth, ring[i % kDepth]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      if (grp == 1) wait_loads();
+      __syncthreads();
+    };
+    auto valu_phase = [&](int j, auto masked_tag) {  // slot 2j + 1 + grp
+      if (grp == 1) issue_loads(j + 1);
+      softmax(s, pf, (tr.kt_begin + j) * kBN, masked_tag);
+      if (grp == 0) wait_loads();
+      __syncthreads();
+    };
     load_k(tr.kt_begin, kbuf(0));
-    load_v(tr.kt_begin, vbuf(0));
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_loads();
     __syncthreads();
-    for (int i = 0; i < ntiles; ++i) {
-      const int t = tr.kt_begin + i;
-      if (t >= tr.full_begin && t < tr.full_end)
-        step(i, BoolTag<false>{});
-      else
-        step(i, BoolTag<true>{});
+    if (grp == 1) {  // slot 0 for group 1: issue its loads of K_1, V_0
+      issue_loads(0);
+      __syncthreads();
     }
+    // Tile 0, then tiles [1, a) masked, [a, b) unmasked, [b, ntiles) masked:
+    // masked tiles only sit at the two ends of the visited range.
+    mfma_phase(0, BoolTag<false>{});
+    if (tr.kt_begin >= tr.full_begin && tr.kt_begin < tr.full_end)
+      valu_phase(0, BoolTag<false>{});
+    else
+      valu_phase(0, BoolTag<true>{});
+    const int a = min(max(tr.full_begin - tr.kt_begin, 1), ntiles);
+    const int bnd = min(max(tr.full_end - tr.kt_begin, a), ntiles);
+    int j = 1;
+    for (; j < a; ++j) {
+      mfma_phase(j, BoolTag<true>{});
+      valu_phase(j, BoolTag<true>{});
+    }
+    for (; j < bnd; ++j) {
+      mfma_phase(j, BoolTag<true>{});
+      valu_phase(j, BoolTag<false>{});
+    }
+    for (; j < ntiles; ++j) {
+      mfma_phase(j, BoolTag<true>{});
+      valu_phase(j, BoolTag<true>{});
+    }
+    pv(vbuf(ntiles - 1), pf);
+    if (grp == 0) __syncthreads();  // matches group 1's extra slot-0 barrier
   }
 
   // ---- epilogue ------------------------------------------------------------
-  const float l = l_run + __shfl_xor(l_run, 32);
+  const float l = l_run + other_half(l_run);
   if (myrow < r1) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     uint16_t* dst = p.o + (int64_t)(q0 + myrow) * p.o_row + (int64_t)h * p.o_head;

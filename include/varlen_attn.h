@@ -135,14 +135,16 @@ int varlen_attn_tile_range(int32_t seqlen_q, int32_t seqlen_k, int32_t row_begin
 /*
  * The kernel's workgroup-to-work mapping, computed on the host by the same
  * function the kernel runs (exported for tests).  For workgroup `block` of
- * the grid varlen_attn_fwd launches for (batch, num_heads, max_seqlen_q,
- * causal), returns the segment, head and q-tile (block_m query rows) it
- * owns, or -1 in all three for a padding workgroup that exits at once.
- * Returns VA_OK, or VA_ERR_ARG for a block outside the grid / bad sizes.
+ * the grid varlen_attn_fwd launches for (batch, num_heads, head dims,
+ * max_seqlen_q, causal), returns the segment, head and q-tile (block_m query
+ * rows, see varlen_attn_plan) it owns, or -1 in all three for a padding
+ * workgroup that exits at once.  Returns VA_OK, VA_ERR_HEADDIM, or
+ * VA_ERR_ARG for a block outside the grid / bad sizes.
  * Host only; makes no HIP call.
  */
-int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_heads, int32_t max_seqlen_q,
-                          int32_t causal, int32_t* segment, int32_t* head, int32_t* q_tile);
+int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_heads, int32_t head_dim_qk,
+                          int32_t head_dim_v, int32_t max_seqlen_q, int32_t causal,
+                          int32_t* segment, int32_t* head, int32_t* q_tile);
 
 /* Launch shape varlen_attn_fwd would use (host only; makes no HIP call). */
 typedef struct va_plan {
@@ -151,7 +153,7 @@ typedef struct va_plan {
   int32_t threads;       /* threads per workgroup */
   int32_t lds_bytes;     /* LDS per workgroup */
   int64_t grid;          /* workgroups launched (some exit at once on short segments) */
-  const char* kernel;    /* kernel symbol family name */
+  const char* kernel;    /* kernel family: "attn_fwd_dual" (head dims <= 80) or "attn_fwd_pingpong" */
 } va_plan;
 
 int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch, int32_t num_heads,

@@ -150,7 +150,13 @@ def test_empty_work_returns_ok_without_launch():
 
 def test_plan():
     p = pkg.plan(80, 80, 8, 16, 4096, 4096)
-    assert p["block_n"] == 64 and p["threads"] in (256, 512) and p["kernel"] == "varlen_attn_fwd_kernel"
+    assert p["block_n"] in (32, 64) and p["threads"] in (256, 512)
+    assert p["kernel"] == "attn_fwd_wide" and p["block_m"] == 512
+    # segments of at most 256 queries take the 256-row kernel
+    short = pkg.plan(80, 80, 36, 16, 256, 256)
+    assert short["kernel"] == "attn_fwd_dual" and short["block_m"] == 256
+    assert pkg.plan(64, 64, 1, 16, 257, 257)["kernel"] == "attn_fwd_wide"
+    assert pkg.plan(128, 128, 1, 16, 4096, 4096)["kernel"] == "attn_fwd_pingpong"
     # 8 x 16 (segment, head) groups, already a multiple of the 8 XCDs
     assert p["grid"] == 8 * 16 * -(-4096 // p["block_m"])
     # 3 x 5 = 15 groups pad to 16
@@ -256,16 +262,17 @@ def test_tile_range_rejects_bad_arguments():
 # ---------------------------------------------------------------------------
 # workgroup -> (segment, head, q-tile) mapping
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("batch,heads,max_q,causal", [
-    (8, 16, 4096, 0), (36, 16, 256, 0), (1, 16, 65536, 0), (4, 128, 4096, 1), (3, 5, 700, 1), (1, 1, 1, 0),
+@pytest.mark.parametrize("batch,heads,max_q,causal,dims", [
+    (8, 16, 4096, 0, (80, 80)), (36, 16, 256, 0, (80, 80)), (1, 16, 65536, 0, (128, 128)),
+    (4, 128, 4096, 1, (192, 128)), (3, 5, 700, 1, (64, 64)), (1, 1, 1, 0, (72, 72)), (3, 5, 700, 0, (128, 128)),
 ])
-def test_work_unit_covers_every_tile_once(batch, heads, max_q, causal):
-    p = pkg.plan(64, 64, batch, heads, max_q, max_q, causal)
+def test_work_unit_covers_every_tile_once(batch, heads, max_q, causal, dims):
+    p = pkg.plan(dims[0], dims[1], batch, heads, max_q, max_q, causal)
     n_qt = -(-max_q // p["block_m"])
     seen = {}
     pad = 0
     for blk in range(p["grid"]):
-        b, h, qt = pkg.work_unit(blk, batch, heads, max_q, causal)
+        b, h, qt = pkg.work_unit(blk, batch, heads, dims[0], dims[1], max_q, causal)
         if b < 0:
             pad += 1
             continue
@@ -289,6 +296,8 @@ def test_work_unit_covers_every_tile_once(batch, heads, max_q, causal):
 def test_work_unit_rejects_out_of_grid():
     p = pkg.plan(64, 64, 2, 3, 100, 100)
     with pytest.raises(ValueError):
-        pkg.work_unit(p["grid"], 2, 3, 100)
+        pkg.work_unit(p["grid"], 2, 3, 64, 64, 100)
     with pytest.raises(ValueError):
-        pkg.work_unit(-1, 2, 3, 100)
+        pkg.work_unit(-1, 2, 3, 64, 64, 100)
+    with pytest.raises(ValueError):
+        pkg.work_unit(0, 2, 3, 96, 96, 100)

@@ -30,11 +30,16 @@
 // threshold") and masking only on the tiles that need it (same section: only
 // unmasked steady-state tiles take the fast path).
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
 #include "tile_schedule.h"
 #include "varlen_attn.h"
+
+// Kernel-local lambdas must inline: out-of-line copies would pass the
+// register arrays they capture through scratch memory.
+#define VA_INLINE __attribute__((always_inline))
 
 namespace va {
 
@@ -45,10 +50,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;        // query rows per workgroup
-constexpr int kBN = 64;                 // keys per tile
 constexpr float kRescaleTau = 8.0f;     // lazy rescale threshold, log2 units
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every range: reads 0
@@ -69,30 +70,36 @@ struct Params {
   float scale_log2;  // softmax_scale * log2(e)
 };
 
-template <int DQK, int DV>
-struct Cfg {
+// Geometry of one K/V tile of BN keys staged in LDS, for a workgroup of
+// WAVES waves.
+template <int DQK, int DV, int BN, int WAVES>
+struct TileGeom {
   static constexpr int DQKP = (DQK + 15) / 16 * 16;  // MFMA K granularity (72 -> 80)
   static constexpr int DVP = (DV + 31) / 32 * 32;    // 32-row V^T MFMA blocks (72, 80 -> 96)
   static constexpr int KC = DQKP / 16;               // k-chunks of the QK^T product
   static constexpr int VB = DVP / 32;                // dv blocks of the PV product
-  // K tile: 64 rows of DQKP bf16 = CPR_K 16-byte chunks, plus one pad chunk
+  // K tile: BN rows of DQKP bf16 = CPR_K 16-byte chunks, plus one pad chunk
   // per row so the 32 rows an MFMA operand read touches hit distinct banks.
   static constexpr int CPR_K = DQKP / 8;
   static constexpr int KPITCH = CPR_K + 1;           // chunks per K row in LDS
   static constexpr int K_REAL = DQK / 8;             // chunks holding data
-  // V tile: 64 rows of DVP bf16, chunk index XOR-swizzled per row so the
+  // V tile: BN rows of DVP bf16, chunk index XOR-swizzled per row so the
   // four rows a transposing read touches hit distinct banks.
   static constexpr int CPR_V = DVP / 8;
   static constexpr int V_REAL = DV / 8;
-  static constexpr int K_TILE = kBN * KPITCH * 16;   // bytes
-  static constexpr int V_TILE = kBN * CPR_V * 16;
-  static constexpr int LDS_BYTES = 2 * (K_TILE + V_TILE);
-  static constexpr int K_LOADS = (KPITCH + kWaves - 1) / kWaves;  // wave-loads per wave
-  static constexpr int V_LOADS = (CPR_V + kWaves - 1) / kWaves;
+  // Tiles are filled by 64-lane x 16-byte LDS-DMA wave-loads (1 KB each).
+  static constexpr int K_SLOTS = BN * KPITCH;
+  static constexpr int V_SLOTS = BN * CPR_V;
+  static constexpr int K_WL = (K_SLOTS + 63) / 64;   // wave-loads per tile
+  static constexpr int V_WL = (V_SLOTS + 63) / 64;
+  static constexpr int K_TILE = K_WL * 1024;         // bytes
+  static constexpr int V_TILE = V_WL * 1024;
+  static constexpr int K_LOADS = (K_WL + WAVES - 1) / WAVES;  // most wave-loads one wave issues
+  static constexpr int V_LOADS = (V_WL + WAVES - 1) / WAVES;
   static_assert(CPR_V == 8 || CPR_V == 12 || CPR_V == 16, "V swizzle defined for 8/12/16 chunks");
 };
 
-// XOR applied to the chunk index of V row `row` (see Cfg).
+// XOR applied to the chunk index of V row `row` (see TileGeom).
 template <int CPR_V>
 __host__ __device__ constexpr int v_swizzle(int row) {
   return CPR_V == 16 ? 4 * (row & 3) : (CPR_V == 8 ? 4 * ((row >> 1) & 1) : 0);
@@ -126,6 +133,19 @@ __device__ __forceinline__ float other_half(float x) {
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
+// Workgroup barrier without __syncthreads()'s release/acquire fences.  With
+// LDS-DMA in flight the release fence turns into s_waitcnt vmcnt(0), making
+// every wave wait for the prefetch it has just issued; the kernels that use
+// this wait for the loads a barrier must cover themselves.  LDS reads are
+// drained first so no stage is overwritten under a read still in flight,
+// and the empty asm statements keep the compiler from moving memory
+// accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ bf16x8 lds_read_b128(const lds_char* base, int byte_off) {
   return *(const __attribute__((address_space(3))) bf16x8*)(base + byte_off);
 }
@@ -134,8 +154,23 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const lds_char* base, int byte_off
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(base + byte_off));
 }
 
+// ============================================================================
+// Ping-pong kernel (head dims >= 128): 8 waves x 32 query rows, 64-key tiles.
+// ============================================================================
+namespace pingpong {
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;  // query rows per workgroup
+constexpr int kBN = 64;           // keys per tile
 template <int DQK, int DV>
-__global__ __launch_bounds__(kThreads) void varlen_attn_fwd_kernel(Params p) {
+struct Cfg : TileGeom<DQK, DV, kBN, kWaves> {
+  static constexpr int LDS_BYTES = 2 * (Cfg::K_TILE + Cfg::V_TILE);
+};
+}  // namespace pingpong
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(pingpong::kThreads) void attn_fwd_pingpong(Params p) {
+  using namespace pingpong;
   using C = Cfg<DQK, DV>;
   __shared__ __attribute__((aligned(1024))) char lds_raw[C::LDS_BYTES];
   lds_char* lds = (lds_char*)lds_raw;
@@ -473,6 +508,863 @@ __global__ __launch_bounds__(kThreads) void varlen_attn_fwd_kernel(Params p) {
   }
 }
 
+// ============================================================================
+// Dual kernel (head dims <= 80): 4 waves x 64 query rows, 32-key tiles, and
+// two workgroups per CU.
+//
+// Each LDS operand read feeds two MFMAs (the wave's two 32-row query
+// blocks), halving LDS read traffic per MFMA against the ping-pong kernel;
+// the small accumulator (d_v <= 96 padded) keeps a wave within 256 VGPRs, so
+// two workgroups share each CU and the two waves on a SIMD overlap one's
+// softmax with the other's MFMAs.  Per 32-key tile a wave runs
+//   S^T = K Q^T -> mask (boundary tiles) + row max -> lazy rescale ->
+//   exp2 / row sum / bf16 pack -> O^T += V^T P^T,
+// while the tile two steps ahead streams into the third LDS stage.
+// ============================================================================
+namespace dual {
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = 64;
+constexpr int kBM = kRowsPerWave * kWaves;  // query rows per workgroup
+constexpr int kBN = 32;                     // keys per tile
+constexpr int kStages = 3;
+template <int DQK, int DV>
+struct Cfg : TileGeom<DQK, DV, kBN, kWaves> {
+  static constexpr int LDS_BYTES = kStages * (Cfg::K_TILE + Cfg::V_TILE);
+};
+}  // namespace dual
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(dual::kThreads, 2) void attn_fwd_dual(Params p) {
+  using namespace dual;
+  using C = Cfg<DQK, DV>;
+  __shared__ __attribute__((aligned(1024))) char lds_raw[C::LDS_BYTES];
+  lds_char* lds = (lds_char*)lds_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  const WorkUnit wu = decode_block(blockIdx.x, p.batch, p.heads, p.n_qt, p.causal);
+  if (!wu.valid) return;
+  const int b = wu.b, h = wu.h, qt = wu.qt;
+  const int q0 = p.cu_q[b];
+  const int Lq = p.cu_q[b + 1] - q0;
+  const int k0 = p.cu_k[b];
+  const int Lk = p.cu_k[b + 1] - k0;
+  const int r0 = qt * kBM;
+  if (r0 >= Lq) return;
+  const int r1 = min(r0 + kBM, Lq);
+  const TileRange tr = tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN);
+  const int ntiles = tr.kt_end - tr.kt_begin;
+  // This lane's query rows: wrow0 + 32 qb + l32, qb = 0, 1.
+  const int wrow0 = r0 + wave * kRowsPerWave;
+
+  // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------
+  bf16x8 qf[2][C::KC];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = wrow0 + 32 * qb + l32;
+    const uint16_t* src = p.q + (int64_t)(q0 + row) * p.q_row + (int64_t)h * p.q_head;
+#pragma unroll
+    for (int c = 0; c < C::KC; ++c) {
+      const int d = c * 16 + 8 * g;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (row < r1 && d < DQK) x = *(const u32x4*)(src + d);
+      qf[qb][c] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  // ---- direct-to-LDS tile loads ---------------------------------------------
+  // Wave-load j of a tile covers LDS slots [64 j, 64 j + 64); lanes whose
+  // slot is past the tile, a pad chunk, or (72) chunk 9 read zeros.
+  const int64_t k_row_b = p.k_row * 2, v_row_b = p.v_row * 2;
+  uint32_t koff[C::K_LOADS], voff[C::V_LOADS];
+#pragma unroll
+  for (int i = 0; i < C::K_LOADS; ++i) {
+    const int s = (wave + kWaves * i) * 64 + lane;
+    const int row = s / C::KPITCH, c = s % C::KPITCH;
+    koff[i] = (s < C::K_SLOTS && c < C::K_REAL) ? (uint32_t)(row * k_row_b + c * 16) : kOOB;
+  }
+#pragma unroll
+  for (int i = 0; i < C::V_LOADS; ++i) {
+    const int s = (wave + kWaves * i) * 64 + lane;
+    const int row = s / C::CPR_V;
+    const int c = (s % C::CPR_V) ^ v_swizzle<C::CPR_V>(row);
+    voff[i] = (s < C::V_SLOTS && c < C::V_REAL) ? (uint32_t)(row * v_row_b + c * 16) : kOOB;
+  }
+  // Wave-loads this wave issues per tile (the last waves may issue fewer).
+  const int nk = (C::K_WL - wave + kWaves - 1) / kWaves;
+  const int nv = (C::V_WL - wave + kWaves - 1) / kWaves;
+  const char* kseg = (const char*)(p.k + (int64_t)k0 * p.k_row + (int64_t)h * p.k_head);
+  const char* vseg = (const char*)(p.v + (int64_t)k0 * p.v_row + (int64_t)h * p.v_head);
+  auto kbuf = [&](int j) VA_INLINE { return lds + (j % kStages) * (C::K_TILE + C::V_TILE); };
+  auto vbuf = [&](int j) VA_INLINE { return lds + (j % kStages) * (C::K_TILE + C::V_TILE) + C::K_TILE; };
+  auto load_tile = [&](int j) VA_INLINE {  // K and V of tile j into stage j % 3
+    const int key0 = (tr.kt_begin + j) * kBN;
+    const int rows = min(Lk - key0, kBN);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kseg + key0 * k_row_b), (short)0, (int)(rows * k_row_b), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vseg + key0 * v_row_b), (short)0, (int)(rows * v_row_b), kBufferFlags);
+    lds_char* kd = kbuf(j);
+    lds_char* vd = vbuf(j);
+#pragma unroll
+    for (int i = 0; i < C::K_LOADS; ++i)
+      if (i < nk) dma16(rk, kd + (wave + kWaves * i) * 1024, koff[i]);
+#pragma unroll
+    for (int i = 0; i < C::V_LOADS; ++i)
+      if (i < nv) dma16(rv, vd + (wave + kWaves * i) * 1024, voff[i]);
+  };
+  // Wait until at most `pending` of this wave's wave-loads are in flight.
+  auto wait_loads_but = [&](int pending) VA_INLINE {
+    static_assert(C::K_LOADS + C::V_LOADS <= 8, "vmcnt cases");
+    switch (pending) {
+      case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+      case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+      case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+      case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+      case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+      case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+      case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    }
+  };
+
+  // ---- LDS operand reads ----------------------------------------------------
+  const int k_rd = (l32 * C::KPITCH + g) * 16;  // K row l32, chunk 2c + g at + 32c
+  int v_rd[C::VB];
+  {
+    const int G = lane >> 4, i = lane & 15;
+    const int vrow = 4 * g + (i >> 2);
+    const int y = 2 * (G & 1) + ((i >> 1) & 1);
+#pragma unroll
+    for (int vb = 0; vb < C::VB; ++vb)
+      v_rd[vb] = (vrow * C::CPR_V + ((4 * vb + y) ^ v_swizzle<C::CPR_V>(vrow))) * 16 + 8 * (i & 1);
+  }
+
+  // ---- running state ----------------------------------------------------------
+  f32x16 acc[C::VB][2];
+#pragma unroll
+  for (int vb = 0; vb < C::VB; ++vb)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[vb][qb][r] = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+  int row_lo[2], row_hi[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const RowBounds rb = row_bounds(wrow0 + 32 * qb + l32, Lq, Lk, p.causal, p.wl, p.wr);
+    row_lo[qb] = (int)imin64(rb.lo, (int64_t)Lk);
+    row_hi[qb] = (int)imax64(rb.hi, (int64_t)-1);
+  }
+
+  // One 32-key tile: the lane holds query block qb's column l32 and keys
+  // key0 + 8 (r / 4) + 4 g + r % 4 in s[qb][r].
+  auto tile = [&](int j, auto masked_tag) VA_INLINE {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    const lds_char* ks = kbuf(j);
+    const lds_char* vs = vbuf(j);
+    // S^T = K Q^T; each K operand feeds both query blocks.
+    f32x16 s[2];
+    const f32x16 zero = {};
+#pragma unroll
+    for (int c = 0; c < C::KC; ++c) {
+      const bf16x8 kf = lds_read_b128(ks, k_rd + 32 * c);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][c], c == 0 ? zero : s[qb], 0, 0, 0);
+    }
+    // mask (boundary tiles only) and row max
+    float m_new[2];
+    bool need = false;
+    const int key0 = (tr.kt_begin + j) * kBN;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      if constexpr (kMasked) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jj = key0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          s[qb][r] = (jj >= row_lo[qb] && jj <= row_hi[qb]) ? s[qb][r] : -INFINITY;
+        }
+      }
+      float m = fmaxf(s[qb][0], s[qb][1]);
+#pragma unroll
+      for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(s[qb][r], s[qb][r + 1]));
+      m = fmaxf(m, other_half(m));
+      m_new[qb] = fmaxf(m_run[qb], m * p.scale_log2);
+      need |= m_new[qb] > m_run[qb] + kRescaleTau;
+    }
+    // lazy rescale: move the running max only when some row's max grew by
+    // more than kRescaleTau (log2 units); otherwise p <= 2^kRescaleTau
+    if (__any(need)) {
+      asm volatile("; lazy rescale" ::: "memory");  // keep the rare rescale a branch
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float alpha = (m_new[qb] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new[qb]);
+        m_run[qb] = m_new[qb];
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int vb = 0; vb < C::VB; ++vb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[vb][qb][r] *= alpha;
+      }
+    }
+    // p = exp2(s * scale * log2(e) - m), row sum, bf16 pack (PV B operand)
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * t + 2 * e;
+          const float x0 = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, -m_use));
+          const float x1 = __builtin_amdgcn_exp2f(fmaf(s[qb][r + 1], p.scale_log2, -m_use));
+          sum += x0 + x1;
+          pk[e] = pack_bf16x2(x0, x1);
+        }
+        pf[qb][t] = __builtin_bit_cast(bf16x8, pk);
+      }
+      l_run[qb] += sum;
+    }
+    // O^T += V^T P^T; each V^T operand feeds both query blocks.
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int vb = 0; vb < C::VB; ++vb) {
+        const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
+        const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
+        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][t], acc[vb][qb], 0, 0, 0);
+      }
+  };
+
+  // ---- main loop ------------------------------------------------------------
+  // Tile j sits in stage j % 3.  Step j computes tile j while tiles j + 1
+  // (loaded during step j - 1) and j + 2 (issued now) are in flight; the
+  // stage of tile j + 2 last held tile j - 1, whose readers finished before
+  // the barrier that ended step j - 1.
+  if (ntiles > 0) {
+    load_tile(0);
+    if (ntiles > 1) load_tile(1);
+    wait_loads_but(0);
+    __syncthreads();
+    auto step = [&](int j, auto masked_tag) VA_INLINE {
+      const bool more = j + 2 < ntiles;
+      if (more) load_tile(j + 2);
+      tile(j, masked_tag);
+      // tile j + 1 must have landed; tile j + 2's loads may stay in flight
+      wait_loads_but(more ? nk + nv : 0);
+      __syncthreads();
+    };
+    // masked tiles sit at the two ends of the visited range
+    const int a = min(max(tr.full_begin - tr.kt_begin, 0), ntiles);
+    const int bnd = min(max(tr.full_end - tr.kt_begin, a), ntiles);
+    int j = 0;
+    for (; j < a; ++j) step(j, BoolTag<true>{});
+    for (; j < bnd; ++j) step(j, BoolTag<false>{});
+    for (; j < ntiles; ++j) step(j, BoolTag<true>{});
+  }
+
+  // ---- epilogue ---------------------------------------------------------------
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float l = l_run[qb] + other_half(l_run[qb]);
+    const int row = wrow0 + 32 * qb + l32;
+    if (row < r1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      uint16_t* dst = p.o + (int64_t)(q0 + row) * p.o_row + (int64_t)h * p.o_head;
+#pragma unroll
+      for (int vb = 0; vb < C::VB; ++vb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int dv = vb * 32 + 8 * jj + 4 * g;
+          if (dv < DV) {
+            u32x2 o2;
+            o2[0] = pack_bf16x2(acc[vb][qb][4 * jj] * inv, acc[vb][qb][4 * jj + 1] * inv);
+            o2[1] = pack_bf16x2(acc[vb][qb][4 * jj + 2] * inv, acc[vb][qb][4 * jj + 3] * inv);
+            *(u32x2*)(dst + dv) = o2;
+          }
+        }
+      if (p.lse != nullptr && g == 0) {
+        const float lse = l > 0.f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
+        p.lse[(int64_t)h * p.total_q + q0 + row] = lse;
+      }
+    }
+  }
+}
+
+// ============================================================================
+// Wide kernel (head dims <= 80, segments longer than 256 queries): 8 waves x
+// 64 query rows (BM = 512), 32-key tiles, six LDS stages.
+//
+// Each LDS operand read feeds two MFMAs (the wave's two 32-row query
+// blocks), and each wave software-pipelines its own work: iteration j runs
+// the PV product of tile j - 1 and QK^T of tile j + 1 on the matrix cores
+// while the VALU computes the softmax of tile j.  Both waves on a SIMD run
+// the same pipeline, so MFMA and VALU overlap inside a wave and across the
+// two; a VALU-only phase per wave (the ping-pong kernel's) is issue-limited,
+// since a single wave issues VALU at roughly half the rate two waves do.
+//
+// The rescale of the accumulator, when the running max moves, is applied at
+// the end of the iteration, after the PV MFMAs of tile j - 1 and before
+// those of tile j, so the interleaved block has no branch.
+//
+// Each K/V stage is its own __shared__ object and the loop is unrolled by
+// the stage count, so every LDS access names its stage statically: the
+// compiler then tells LDS-DMA writes into one stage from transposing reads
+// of another.  With one shared array it must assume they overlap and makes
+// every V read wait for all DMA in flight (s_waitcnt vmcnt(0)).
+// ============================================================================
+namespace wide {
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = 64;
+constexpr int kBM = kRowsPerWave * kWaves;  // query rows per workgroup
+constexpr int kBN = 32;                     // keys per tile
+constexpr int kStages = 6;                  // tile t lives in stage t % 6 (an even count: see the loop)
+constexpr int kAhead = kStages - 2;         // iteration j issues tile j + 4
+constexpr int kDepth = 3;                   // LDS operands read ahead of their MFMA
+template <int DQK, int DV>
+struct Cfg : TileGeom<DQK, DV, kBN, kWaves> {
+  static constexpr int N_WL = Cfg::K_WL + Cfg::V_WL;  // wave-loads per tile (K first)
+  static constexpr int LDS_BYTES = kStages * (Cfg::K_TILE + Cfg::V_TILE);
+  // V chunks past the data (d_v 72, 80 padded to 96) are never loaded; they
+  // are set once, and may hold a ones column (see attn_fwd_wide).
+  static constexpr int V_PAD = Cfg::CPR_V - Cfg::V_REAL;
+  static_assert(N_WL <= 2 * kWaves, "a wave issues at most two wave-loads per tile");
+  static_assert(Cfg::CPR_V != 12 || v_swizzle<12>(1) == 0, "pad chunks sit at fixed positions");
+};
+}  // namespace wide
+
+template <int N>
+struct Int {
+  static constexpr int value = N;
+};
+
+// f(Int<I>{}), ..., f(Int<N - 1>{}) in order, unrolled.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Int<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Cross-half (lane l and lane l ^ 32) max and sum: v_permlane32_swap
+// leaves lane l's and lane l ^ 32's values in the two results.
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Lane l ^ 32's value for lanes 32-63, the lane's own for lanes 0-31:
+// broadcasts what lanes 0-31 hold to the whole wave.
+__device__ __forceinline__ float from_lower_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]);
+}
+
+// SUM_BY_MFMA (d_v 72 and 80, no LSE requested): column d_v of the padded V
+// tile holds ones, so the PV product accumulates each row's probability sum
+// alongside O and the softmax does no adds.  The sum is then over the bf16
+// probabilities the MFMA sees, which moves the LSE by up to ln(1 + 2^-9);
+// with an LSE requested the sum stays in fp32.
+template <int DQK, int DV, bool SUM_BY_MFMA>
+__global__ __launch_bounds__(wide::kThreads, 1) void attn_fwd_wide(Params p) {
+  using namespace wide;
+  using C = Cfg<DQK, DV>;
+  static_assert(!SUM_BY_MFMA || C::V_PAD > 0, "the ones column needs a padded d_v");
+  static_assert(kStages == 6, "stage objects below");
+  __shared__ __attribute__((aligned(1024))) char ks0[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) char ks1[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) char ks2[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) char ks3[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) char ks4[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) char ks5[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) char vs0[C::V_TILE];
+  __shared__ __attribute__((aligned(1024))) char vs1[C::V_TILE];
+  __shared__ __attribute__((aligned(1024))) char vs2[C::V_TILE];
+  __shared__ __attribute__((aligned(1024))) char vs3[C::V_TILE];
+  __shared__ __attribute__((aligned(1024))) char vs4[C::V_TILE];
+  __shared__ __attribute__((aligned(1024))) char vs5[C::V_TILE];
+  auto kst = [&](auto st) VA_INLINE -> lds_char* {
+    constexpr int i = decltype(st)::value % kStages;
+    if constexpr (i == 0) return (lds_char*)ks0;
+    else if constexpr (i == 1) return (lds_char*)ks1;
+    else if constexpr (i == 2) return (lds_char*)ks2;
+    else if constexpr (i == 3) return (lds_char*)ks3;
+    else if constexpr (i == 4) return (lds_char*)ks4;
+    else return (lds_char*)ks5;
+  };
+  auto vst = [&](auto st) VA_INLINE -> lds_char* {
+    constexpr int i = decltype(st)::value % kStages;
+    if constexpr (i == 0) return (lds_char*)vs0;
+    else if constexpr (i == 1) return (lds_char*)vs1;
+    else if constexpr (i == 2) return (lds_char*)vs2;
+    else if constexpr (i == 3) return (lds_char*)vs3;
+    else if constexpr (i == 4) return (lds_char*)vs4;
+    else return (lds_char*)vs5;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  const WorkUnit wu = decode_block(blockIdx.x, p.batch, p.heads, p.n_qt, p.causal);
+  if (!wu.valid) return;
+  const int b = wu.b, h = wu.h, qt = wu.qt;
+  const int q0 = p.cu_q[b];
+  const int Lq = p.cu_q[b + 1] - q0;
+  const int k0 = p.cu_k[b];
+  const int Lk = p.cu_k[b + 1] - k0;
+  const int r0 = qt * kBM;
+  if (r0 >= Lq) return;
+  const int r1 = min(r0 + kBM, Lq);
+  const TileRange tr = tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN);
+  const int ntiles = tr.kt_end - tr.kt_begin;
+  const int wrow0 = r0 + wave * kRowsPerWave;
+  // Waves past the segment's last row still issue their share of the loads
+  // and meet every barrier, but skip the arithmetic.
+  const bool active = wrow0 < r1;
+
+  // ---- padded V chunks: zeros, or a one in column d_v ------------------------
+  if constexpr (C::V_PAD > 0) {
+    static_for<0, kStages>([&](auto st) VA_INLINE {
+      for (int i = tid; i < kBN * C::V_PAD; i += kThreads) {
+        const int row = i / C::V_PAD, c = C::V_REAL + i % C::V_PAD;
+        const u32x4 val = {(SUM_BY_MFMA && c == C::V_REAL) ? 0x3F80u : 0u, 0u, 0u, 0u};  // bf16 1.0
+        *(__attribute__((address_space(3))) u32x4*)(vst(st) + (row * C::CPR_V + c) * 16) = val;
+      }
+    });
+  }
+
+  // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------
+  bf16x8 qf[2][C::KC];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = wrow0 + 32 * qb + l32;
+    const uint16_t* src = p.q + (int64_t)(q0 + row) * p.q_row + (int64_t)h * p.q_head;
+#pragma unroll
+    for (int c = 0; c < C::KC; ++c) {
+      const int d = c * 16 + 8 * g;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (row < r1 && d < DQK) x = *(const u32x4*)(src + d);
+      qf[qb][c] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  // ---- direct-to-LDS tile loads ---------------------------------------------
+  // A tile is K_WL K wave-loads then V_WL V wave-loads, each 64 lanes x 16
+  // bytes: K wave-load i covers K slots [64 i, 64 i + 64), likewise for V.
+  // Wave w issues K wave-load w and V wave-load w every tile; a wave with no
+  // such wave-load (w >= K_WL or w >= V_WL) reads zeros into a dummy area
+  // instead, so every wave issues exactly two loads per tile and every wait
+  // below is a constant.  K pad chunks, chunk 9 of a 72-wide row and slots
+  // past the tile read zeros; lanes on padded V chunks load nothing.
+  __shared__ __attribute__((aligned(1024))) char dummy[1024];
+  const int64_t k_row_b = p.k_row * 2, v_row_b = p.v_row * 2;
+  const bool k_real = wave < C::K_WL, v_real = wave < C::V_WL;
+  uint32_t k_off = kOOB, v_off = kOOB;
+  bool v_on = true;
+  {
+    const int sl = wave * 64 + lane;
+    if (k_real) {
+      const int row = sl / C::KPITCH, c = sl % C::KPITCH;
+      k_off = (sl < C::K_SLOTS && c < C::K_REAL) ? (uint32_t)(row * k_row_b + c * 16) : kOOB;
+    }
+    if (v_real) {
+      const int row = sl / C::CPR_V;
+      const int c = (sl % C::CPR_V) ^ v_swizzle<C::CPR_V>(row);
+      v_on = sl >= C::V_SLOTS || c < C::V_REAL;
+      v_off = (sl < C::V_SLOTS && c < C::V_REAL) ? (uint32_t)(row * v_row_b + c * 16) : kOOB;
+    }
+  }
+  // K/V rows of the next tile to issue, advanced one tile per issue; tiles
+  // past the last get an empty range (all reads zero).
+  const char* k_next =
+      (const char*)(p.k + ((int64_t)k0 + (int64_t)tr.kt_begin * kBN) * p.k_row + (int64_t)h * p.k_head);
+  const char* v_next =
+      (const char*)(p.v + ((int64_t)k0 + (int64_t)tr.kt_begin * kBN) * p.v_row + (int64_t)h * p.v_head);
+  int keys_next = Lk - tr.kt_begin * kBN;
+  auto issue = [&](auto st) VA_INLINE {  // this wave's two loads of the next tile into stage st
+    // (readfirstlane: the clamp compiles to a VALU med3, and a descriptor
+    // the compiler cannot prove uniform costs a waterfall loop per load)
+    const int rows = __builtin_amdgcn_readfirstlane(max(min(keys_next, kBN), 0));
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)k_next, (short)0, (int)(rows * k_row_b), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)v_next, (short)0, (int)(rows * v_row_b), kBufferFlags);
+    dma16(rk, k_real ? kst(st) + wave * 1024 : (lds_char*)dummy, k_off);
+    if (v_on) dma16(rv, v_real ? vst(st) + wave * 1024 : (lds_char*)dummy, v_off);
+    k_next += kBN * k_row_b;
+    v_next += kBN * v_row_b;
+    keys_next -= kBN;
+  };
+  // Every iteration issues two loads per wave, and loads complete in issue
+  // order: "tile t landed" with the loads of n later tiles in flight is
+  // s_waitcnt vmcnt(2 n).
+  auto wait_landed = [&](auto later_tiles) VA_INLINE {
+    constexpr int n = 2 * decltype(later_tiles)::value;
+    static_assert(n == 4 || n == 6, "vmcnt cases below");
+    if constexpr (n == 4)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  };
+
+  // ---- LDS operand reads ----------------------------------------------------
+  const int k_rd = (l32 * C::KPITCH + g) * 16;  // K row l32, chunk 2c + g at + 32c
+  int v_rd[C::VB];
+  {
+    const int G = lane >> 4, i = lane & 15;
+    const int vrow = 4 * g + (i >> 2);
+    const int y = 2 * (G & 1) + ((i >> 1) & 1);
+#pragma unroll
+    for (int vb = 0; vb < C::VB; ++vb)
+      v_rd[vb] = (vrow * C::CPR_V + ((4 * vb + y) ^ v_swizzle<C::CPR_V>(vrow))) * 16 + 8 * (i & 1);
+  }
+
+  // ---- running state ----------------------------------------------------------
+  f32x16 acc[C::VB][2];
+#pragma unroll
+  for (int vb = 0; vb < C::VB; ++vb)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[vb][qb][r] = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY};  // running max of s * scale * log2(e)
+  float nm[2] = {0.f, 0.f};                 // -m_run, or 0 while m_run is -inf
+  float lim[2] = {-FLT_MAX, -FLT_MAX};      // m_run + kRescaleTau, or -FLT_MAX while m_run is -inf
+  float l_run[2] = {0.f, 0.f};              // fp32 row sum (unless SUM_BY_MFMA)
+  int row_lo[2], row_hi[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const RowBounds rb = row_bounds(wrow0 + 32 * qb + l32, Lq, Lk, p.causal, p.wl, p.wr);
+    row_lo[qb] = (int)imin64(rb.lo, (int64_t)Lk);
+    row_hi[qb] = (int)imax64(rb.hi, (int64_t)-1);
+  }
+  // Scores of two tiles (the one in the softmax and the next, which QK^T is
+  // writing): sbuf[t % 2][qb][r] = key 8 (r / 4) + 4 g + r % 4, query l32.
+  f32x16 sbuf[2][2];
+  bf16x8 pf[2][2];  // probabilities, PV B operand per (qb, 16-key half)
+
+  // MFMAs of one iteration: PV of tile j - 1 (2 * VB operands, if kPV) then
+  // QK^T of tile j + 1 (KC operands) into sn, each LDS operand feeding both
+  // query blocks.  Operands are read kDepth ahead into a ring of registers.
+  auto mfma_ops = [&](const lds_char* vs, const lds_char* ks, f32x16 (&sn)[2], auto pv_tag) VA_INLINE {
+    constexpr bool kPV = decltype(pv_tag)::value;
+    constexpr int kPVOps = kPV ? 2 * C::VB : 0;
+    constexpr int kOps = kPVOps + C::KC;
+    auto load_op = [&](int i, bf16x8& dst) VA_INLINE {
+      if (i < kPVOps) {  // V^T operand (t, vb) of PV
+        const int t = i / C::VB, vb = i % C::VB;
+        const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
+        const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
+        dst = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      } else {  // K operand c of QK^T
+        dst = lds_read_b128(ks, k_rd + 32 * (i - kPVOps));
+      }
+    };
+    const f32x16 zero = {};
+    bf16x8 ring[kDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth && i < kOps; ++i) load_op(i, ring[i]);
+#pragma unroll
+    for (int i = 0; i < kOps; ++i) {
+      const bf16x8 op = ring[i % kDepth];
+      if (i + kDepth < kOps) load_op(i + kDepth, ring[i % kDepth]);
+      if (i < kPVOps) {
+        const int t = i / C::VB, vb = i % C::VB;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, pf[qb][t], acc[vb][qb], 0, 0, 0);
+      } else {
+        const int c = i - kPVOps;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qf[qb][c], c == 0 ? zero : sn[qb], 0, 0, 0);
+      }
+    }
+  };
+  // Boundary tiles only: scores of keys a row may not see become -inf.
+  auto mask = [&](int j, f32x16 (&s)[2]) VA_INLINE {
+    const int kt = tr.kt_begin + j;
+    if (kt < tr.full_begin || kt >= tr.full_end) {
+      const int key0 = kt * kBN;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jj = key0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          s[qb][r] = (jj >= row_lo[qb] && jj <= row_hi[qb]) ? s[qb][r] : -INFINITY;
+        }
+    }
+  };
+  // Online softmax of one tile, branch-free: row max, the lazy-rescale
+  // decision (the running max moves only when some row's max grew by more
+  // than kRescaleTau, in log2 units; then every row of the wave moves),
+  // p = exp2(s * scale * log2(e) - m), row sum, bf16 pack into pf.  Returns
+  // whether acc must be rescaled, with alpha per query block.
+  auto softmax = [&](f32x16 (&s)[2], float (&alpha)[2]) VA_INLINE -> bool {
+    float m_new[2];
+    bool need = false;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float m = fmaxf(fmaxf(s[qb][0], s[qb][1]), s[qb][2]);
+#pragma unroll
+      for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, s[qb][r]), s[qb][r + 1]);
+      m = fmaxf(m, s[qb][15]);
+      m_new[qb] = fmaxf(m_run[qb], xhalf_max(m) * p.scale_log2);
+      need |= m_new[qb] > m_run[qb] + kRescaleTau;
+    }
+    const bool move = __any(need);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float m_next = move ? m_new[qb] : m_run[qb];
+      alpha[qb] = (m_next == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_next);
+      m_run[qb] = m_next;
+      nm[qb] = (m_next == -INFINITY) ? 0.f : -m_next;
+      lim[qb] = (m_next == -INFINITY) ? -FLT_MAX : m_next + kRescaleTau;
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * t + 2 * e;
+          const float x0 = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, nm[qb]));
+          const float x1 = __builtin_amdgcn_exp2f(fmaf(s[qb][r + 1], p.scale_log2, nm[qb]));
+          if constexpr (!SUM_BY_MFMA) sum += x0 + x1;
+          pk[e] = pack_bf16x2(x0, x1);
+        }
+        pf[qb][t] = __builtin_bit_cast(bf16x8, pk);
+      }
+      if constexpr (!SUM_BY_MFMA) l_run[qb] = l_run[qb] * alpha[qb] + sum;
+    }
+    return move;
+  };
+  // Fast path of the softmax, free of any dependence on this tile's max:
+  // p = exp2(s * scale * log2(e) - m_run) with the running max as it stands,
+  // computed in place, packed to bf16, and a check that it was valid: no
+  // row's tile max exceeds m_run + kRescaleTau (then p <= 2^kRescaleTau,
+  // exactly what the lazy rescale would have produced) and no row saw its
+  // first visible key (m_run = -inf).  The row sum goes to sum[] and is
+  // committed by the caller only if the check passed.
+  auto softmax_fast = [&](f32x16 (&s)[2], float (&sum)[2]) VA_INLINE -> bool {
+    bool bad = false;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float m = fmaxf(fmaxf(s[qb][0], s[qb][1]), s[qb][2]);
+#pragma unroll
+      for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, s[qb][r]), s[qb][r + 1]);
+      m = fmaxf(m, s[qb][15]);
+      bad |= m * p.scale_log2 > lim[qb];
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      sum[qb] = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[qb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, nm[qb]));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * t + 2 * e;
+          if constexpr (!SUM_BY_MFMA) sum[qb] += s[qb][r] + s[qb][r + 1];
+          pk[e] = pack_bf16x2(s[qb][r], s[qb][r + 1]);
+        }
+        pf[qb][t] = __builtin_bit_cast(bf16x8, pk);
+      }
+    }
+    return __any(bad);
+  };
+  // Instruction order of one iteration's MFMA + softmax block, for the
+  // scheduler: each MFMA (PV of the previous tile, then QK^T of the next)
+  // followed by an even share of the softmax's VALU work, every LDS operand
+  // read kDepth operands ahead of its MFMAs.  Masks: 0x100 LDS read, 0x008
+  // MFMA, 0x402 VALU including transcendentals.
+  auto interleave = [&]() VA_INLINE {
+    constexpr int kPVOps = 2 * C::VB, kOps = kPVOps + C::KC;
+    constexpr int kValu = SUM_BY_MFMA ? 5 : 7;
+    static_for<0, kDepth>([&](auto o) VA_INLINE {
+      __builtin_amdgcn_sched_group_barrier(0x100, decltype(o)::value < kPVOps ? 2 : 1, 0);
+    });
+    static_for<0, kOps>([&](auto o) VA_INLINE {
+      constexpr int i = decltype(o)::value;
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, kValu, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, kValu, 0);
+      if constexpr (i + kDepth < kOps) __builtin_amdgcn_sched_group_barrier(0x100, i + kDepth < kPVOps ? 2 : 1, 0);
+    });
+  };
+  // QK^T of one tile on its own (tile 0, and the slow path below).
+  auto qk_only = [&](const lds_char* ks, f32x16 (&sn)[2]) VA_INLINE {
+    mfma_ops(nullptr, ks, sn, BoolTag<false>{});
+  };
+  // acc *= alpha, after the PV MFMAs of the previous tile (rare).
+  auto rescale = [&](bool move, const float (&alpha)[2]) VA_INLINE {
+    if (move) {
+      asm volatile("; lazy rescale" ::: "memory");  // keep the rare rescale a branch
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int vb = 0; vb < C::VB; ++vb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[vb][qb][r] *= alpha[qb];
+    }
+  };
+
+  // ---- main loop ----------------------------------------------------------------
+  // Iteration j: issue tile j + 4; MFMAs of PV(j - 1) and QK^T(j + 1) with
+  // the softmax of tile j; rescale; wait for this wave's share of tile j + 2;
+  // barrier.  Tile t sits in stage t % 6, which last held tile t - 6: its K
+  // was last read in iteration t - 7, its V in iteration t - 5, both before
+  // iteration t - 4 issues tile t.  Tile j + 2 (read by iteration j + 1's
+  // QK^T) is waited for at the end of iteration j, three iterations after
+  // its issue.  Every iteration issues, past the last tile too (zeros), so
+  // the waits are constants; QK^T of tile ntiles in the last iteration reads
+  // such zeros, already landed, and its result is never used.
+  //
+  // Iteration j's softmax reads sbuf[j % 2] and QK^T writes sbuf[(j + 1) % 2];
+  // the loop is unrolled by the (even) stage count so both are static.
+  if (ntiles > 0) {
+    static_for<0, kAhead>([&](auto t) VA_INLINE { issue(t); });  // tiles 0-3
+    wait_landed(Int<kAhead - 1>{});                                // tile 0
+    lds_barrier();
+    if (active) mfma_ops(nullptr, kst(Int<0>{}), sbuf[0], BoolTag<false>{});  // QK^T(0)
+    wait_landed(Int<kAhead - 2>{});  // tile 1
+    lds_barrier();
+    // iteration 0 (no PV before it)
+    {
+      issue(Int<kAhead % kStages>{});
+      if (active) {
+        mask(0, sbuf[0]);
+        mfma_ops(nullptr, kst(Int<1>{}), sbuf[1], BoolTag<false>{});
+        float alpha[2];
+        const bool move = softmax(sbuf[0], alpha);
+        rescale(move, alpha);
+      }
+      wait_landed(Int<kAhead - 2>{});  // tile 2
+      lds_barrier();
+    }
+    for (int j0 = 1; j0 < ntiles; j0 += kStages) {  // tile j0 + u sits in stage (u + 1) % 6
+      static_for<0, kStages>([&](auto u) VA_INLINE {
+        constexpr int U = decltype(u)::value;
+        const int j = j0 + U;
+        if (U == 0 || j < ntiles) {
+          issue(Int<(U + 1 + kAhead) % kStages>{});  // tile j + 4 (zeros past the last)
+          if (active) {
+            constexpr int cur = (U + 1) % 2;  // j % 2, j0 being odd
+            mask(j, sbuf[cur]);
+            mfma_ops(vst(Int<U % kStages>{}), kst(Int<(U + 2) % kStages>{}), sbuf[cur ^ 1], BoolTag<true>{});
+            float sum[2];
+            const bool slow = softmax_fast(sbuf[cur], sum);
+            // The probabilities are only read in the next iteration; without
+            // this use the compiler sinks their computation past the branch
+            // below, out of reach of the interleave.
+            asm volatile("" ::"v"(pf[0][0]), "v"(pf[0][1]), "v"(pf[1][0]), "v"(pf[1][1]));
+            interleave();
+            // Commit the row sums on one path (the slow path restores them):
+            // two paths merging into l_run cost the register allocator dearly.
+            const float l_prev[2] = {l_run[0], l_run[1]};
+            if constexpr (!SUM_BY_MFMA) {
+              l_run[0] += sum[0];
+              l_run[1] += sum[1];
+            }
+            if (slow) {
+              // Some row's max moved past m_run + kRescaleTau (or a row saw
+              // its first key): recompute this tile's scores from K, still
+              // in its stage, and take the full softmax with the rescale.
+              asm volatile("; softmax slow path" ::: "memory");
+              l_run[0] = l_prev[0];
+              l_run[1] = l_prev[1];
+              qk_only(kst(Int<(U + 1) % kStages>{}), sbuf[cur]);
+              mask(j, sbuf[cur]);
+              float alpha[2];
+              const bool move = softmax(sbuf[cur], alpha);
+              rescale(move, alpha);
+            }
+          }
+          wait_landed(Int<kAhead - 2>{});  // tile j + 2
+          lds_barrier();
+        }
+      });
+    }
+    // The zero loads past the last tile must land before the workgroup's LDS
+    // can be handed to the next workgroup.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (active) {  // PV of the last tile
+      const int last = (ntiles - 1) % kStages;
+      static_for<0, kStages>([&](auto st) VA_INLINE {
+        if (last == decltype(st)::value) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int vb = 0; vb < C::VB; ++vb) {
+              const bf16x4 lo = lds_read_tr(vst(st), v_rd[vb] + (16 * t) * C::CPR_V * 16);
+              const bf16x4 hi = lds_read_tr(vst(st), v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
+              const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+              for (int qb = 0; qb < 2; ++qb)
+                acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][t], acc[vb][qb], 0, 0, 0);
+            }
+        }
+      });
+    }
+  }
+
+  // ---- epilogue ---------------------------------------------------------------
+  // With SUM_BY_MFMA the row sum sits in column d_v of the accumulator:
+  // dv block VB - 1, register 4 * ((d_v % 32) / 8), lanes 0-31.
+  constexpr int kSumReg = 4 * ((DV % 32) / 8);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float l = SUM_BY_MFMA ? from_lower_half(acc[C::VB - 1][qb][kSumReg]) : xhalf_sum(l_run[qb]);
+    const int row = wrow0 + 32 * qb + l32;
+    if (row < r1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      uint16_t* dst = p.o + (int64_t)(q0 + row) * p.o_row + (int64_t)h * p.o_head;
+#pragma unroll
+      for (int vb = 0; vb < C::VB; ++vb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int dv = vb * 32 + 8 * jj + 4 * g;
+          if (dv < DV) {
+            u32x2 o2;
+            o2[0] = pack_bf16x2(acc[vb][qb][4 * jj] * inv, acc[vb][qb][4 * jj + 1] * inv);
+            o2[1] = pack_bf16x2(acc[vb][qb][4 * jj + 2] * inv, acc[vb][qb][4 * jj + 3] * inv);
+            *(u32x2*)(dst + dv) = o2;
+          }
+        }
+      if (p.lse != nullptr && g == 0) {
+        const float lse = l > 0.f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
+        p.lse[(int64_t)h * p.total_q + q0 + row] = lse;
+      }
+    }
+  }
+}
+
 }  // namespace va
 
 // ============================================================================
@@ -480,27 +1372,57 @@ __global__ __launch_bounds__(kThreads) void varlen_attn_fwd_kernel(Params p) {
 // ============================================================================
 namespace va {
 
-template <int DQK, int DV>
-static const void* kernel_ptr() {
-  return (const void*)&varlen_attn_fwd_kernel<DQK, DV>;
-}
-
+// Kernel families.  Head dims <= 80 run the wide ping-pong kernel (64 rows
+// per wave, 512-row blocks) when some segment is longer than 256 queries,
+// else the dual kernel (256-row blocks, two workgroups per CU), which wastes
+// less on short segments.  Larger head dims run the ping-pong kernel (32 rows
+// per wave): 64 rows of a 128-wide accumulator would not fit two waves per
+// SIMD.
 struct Variant {
   const void* fn;
   int lds_bytes;
+  int block_m;
+  int block_n;
+  int threads;
+  const char* name;
 };
+
+template <int DQK, int DV>
+static Variant dual_variant() {
+  return {(const void*)&attn_fwd_dual<DQK, DV>, dual::Cfg<DQK, DV>::LDS_BYTES, dual::kBM, dual::kBN,
+          dual::kThreads, "attn_fwd_dual"};
+}
+template <int DQK, int DV, bool SUM_BY_MFMA = false>
+static Variant wide_variant() {
+  return {(const void*)&attn_fwd_wide<DQK, DV, SUM_BY_MFMA>, wide::Cfg<DQK, DV>::LDS_BYTES, wide::kBM,
+          wide::kBN, wide::kThreads, "attn_fwd_wide"};
+}
+template <int DQK, int DV>
+static Variant pingpong_variant() {
+  return {(const void*)&attn_fwd_pingpong<DQK, DV>, pingpong::Cfg<DQK, DV>::LDS_BYTES, pingpong::kBM,
+          pingpong::kBN, pingpong::kThreads, "attn_fwd_pingpong"};
+}
 
 static bool supported_dims(int dqk, int dv) {
   return (dqk == 64 && dv == 64) || (dqk == 72 && dv == 72) || (dqk == 80 && dv == 80) ||
          (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128);
 }
 
-static Variant variant_for(int dqk, int dv) {
-  if (dqk == 64) return {kernel_ptr<64, 64>(), Cfg<64, 64>::LDS_BYTES};
-  if (dqk == 72) return {kernel_ptr<72, 72>(), Cfg<72, 72>::LDS_BYTES};
-  if (dqk == 80) return {kernel_ptr<80, 80>(), Cfg<80, 80>::LDS_BYTES};
-  if (dqk == 128) return {kernel_ptr<128, 128>(), Cfg<128, 128>::LDS_BYTES};
-  return {kernel_ptr<192, 128>(), Cfg<192, 128>::LDS_BYTES};
+// Segments up to this many queries use 256-row blocks.
+static constexpr int kShortSegment = 256;
+
+// `lse`: whether the caller asked for the LSE (without it, d_v 72 and 80 take
+// the row sum from the PV product; the launch shape is the same either way).
+static Variant variant_for(int dqk, int dv, int max_seqlen_q, bool lse = true) {
+  (void)dv;
+  const bool wide = max_seqlen_q > kShortSegment;
+  if (dqk == 64) return wide ? wide_variant<64, 64>() : dual_variant<64, 64>();
+  if (dqk == 72)
+    return !wide ? dual_variant<72, 72>() : lse ? wide_variant<72, 72>() : wide_variant<72, 72, true>();
+  if (dqk == 80)
+    return !wide ? dual_variant<80, 80>() : lse ? wide_variant<80, 80>() : wide_variant<80, 80, true>();
+  if (dqk == 128) return pingpong_variant<128, 128>();
+  return pingpong_variant<192, 128>();
 }
 
 static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
@@ -551,11 +1473,14 @@ extern "C" int varlen_attn_tile_range(int32_t seqlen_q, int32_t seqlen_k, int32_
 }
 
 extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_heads,
-                                     int32_t max_seqlen_q, int32_t causal, int32_t* segment,
-                                     int32_t* head, int32_t* q_tile) {
+                                     int32_t head_dim_qk, int32_t head_dim_v, int32_t max_seqlen_q,
+                                     int32_t causal, int32_t* segment, int32_t* head,
+                                     int32_t* q_tile) {
   if (!segment || !head || !q_tile) return VA_ERR_NULL;
+  if (!va::supported_dims(head_dim_qk, head_dim_v)) return VA_ERR_HEADDIM;
   if (batch < 0 || num_heads <= 0 || max_seqlen_q <= 0 || (causal != 0 && causal != 1)) return VA_ERR_ARG;
-  const int64_t n_qt = ((int64_t)max_seqlen_q + va::kBM - 1) / va::kBM;
+  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, max_seqlen_q);
+  const int64_t n_qt = ((int64_t)max_seqlen_q + var.block_m - 1) / var.block_m;
   if (block < 0 || block >= va::grid_blocks(batch, num_heads, n_qt)) return VA_ERR_ARG;
   const va::WorkUnit u = va::decode_block(block, batch, num_heads, n_qt, causal);
   *segment = u.valid ? u.b : -1;
@@ -572,14 +1497,14 @@ extern "C" int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t
   if (!plan) return VA_ERR_NULL;
   if (!va::supported_dims(head_dim_qk, head_dim_v)) return VA_ERR_HEADDIM;
   if (batch < 0 || num_heads <= 0 || max_seqlen_q < 0) return VA_ERR_ARG;
-  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v);
-  plan->block_m = va::kBM;
-  plan->block_n = va::kBN;
-  plan->threads = va::kThreads;
+  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, max_seqlen_q);
+  plan->block_m = var.block_m;
+  plan->block_n = var.block_n;
+  plan->threads = var.threads;
   plan->lds_bytes = var.lds_bytes;
-  const int64_t n_qt = ((int64_t)max_seqlen_q + va::kBM - 1) / va::kBM;
+  const int64_t n_qt = ((int64_t)max_seqlen_q + var.block_m - 1) / var.block_m;
   plan->grid = va::grid_blocks(batch, num_heads, n_qt);
-  plan->kernel = "varlen_attn_fwd_kernel";
+  plan->kernel = var.name;
   return VA_OK;
 }
 
@@ -610,8 +1535,8 @@ extern "C" int varlen_attn_fwd(const va_tensor* q, const va_tensor* k, const va_
   if (batch == 0 || max_seqlen_q == 0 || q->rows == 0) return VA_OK;
   if (!cu_seqlens_q || !cu_seqlens_k) return VA_ERR_NULL;
 
-  const Variant var = variant_for(q->dim, v->dim);
-  const int64_t n_qt = ((int64_t)max_seqlen_q + kBM - 1) / kBM;
+  const Variant var = variant_for(q->dim, v->dim, max_seqlen_q, lse != nullptr);
+  const int64_t n_qt = ((int64_t)max_seqlen_q + var.block_m - 1) / var.block_m;
   const int64_t grid = grid_blocks(batch, q->heads, n_qt);
   if (grid > INT32_MAX) return VA_ERR_SHAPE;
 
@@ -641,7 +1566,7 @@ extern "C" int varlen_attn_fwd(const va_tensor* q, const va_tensor* k, const va_
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
 
   void* args[] = {&p};
-  const hipError_t err = hipLaunchKernel(var.fn, dim3((unsigned)grid), dim3(kThreads), args, 0,
+  const hipError_t err = hipLaunchKernel(var.fn, dim3((unsigned)grid), dim3(var.threads), args, 0,
                                          (hipStream_t)stream);
   return err == hipSuccess ? VA_OK : VA_ERR_LAUNCH;
 }

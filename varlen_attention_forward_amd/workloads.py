@@ -108,6 +108,7 @@ def _named_workloads() -> dict:
             head_dim_qk=80,
             head_dim_v=80,
             causal=False,
+            return_lse=False,  # the ViT call takes no LSE
             description="8 ViT images, lengths drawn from {576,1024,2304,4096} "
             "(seed 2), 16 heads, d=80, non-causal",
         ),
@@ -120,6 +121,7 @@ def _named_workloads() -> dict:
             head_dim_qk=80,
             head_dim_v=80,
             causal=False,
+            return_lse=False,  # the ViT call takes no LSE
             description="one 9216-token image as 36 block-diagonal windows of "
             "256 tokens, 16 heads, d=80",
         ),
@@ -132,6 +134,7 @@ def _named_workloads() -> dict:
             head_dim_qk=128,
             head_dim_v=128,
             causal=False,
+            return_lse=False,  # the ViT call takes no LSE
             description="one 65536-token image, 16 heads, d=128, non-causal",
         ),
         Workload(

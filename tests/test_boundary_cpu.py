@@ -156,7 +156,7 @@ def test_plan():
     short = pkg.plan(80, 80, 36, 16, 256, 256)
     assert short["kernel"] == "attn_fwd_dual" and short["block_m"] == 256
     assert pkg.plan(64, 64, 1, 16, 257, 257)["kernel"] == "attn_fwd_wide"
-    assert pkg.plan(128, 128, 1, 16, 4096, 4096)["kernel"] == "attn_fwd_pingpong"
+    assert pkg.plan(128, 128, 1, 16, 4096, 4096)["kernel"] == "attn_fwd_wide"
     # 8 x 16 (segment, head) groups, already a multiple of the 8 XCDs
     assert p["grid"] == 8 * 16 * -(-4096 // p["block_m"])
     # 3 x 5 = 15 groups pad to 16

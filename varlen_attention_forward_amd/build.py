@@ -28,6 +28,11 @@ HIPCC_FLAGS = [
     # Inputs are finite and masked scores are -inf, never NaN: lets fmaxf map
     # to v_max3_f32 without NaN-quieting copies.
     "-fno-honor-nans",
+    # MFMA results in VGPRs even where a wave has more than 256 registers
+    # (one wave per SIMD): the softmax reads the score tiles with plain VALU
+    # ops, which AGPR results would first have to be copied out for.
+    "-mllvm",
+    "-amdgpu-mfma-vgpr-form=1",
     # Keep the compiler from forming packed fp32 VALU ops in device code.
     "-Xclang",
     "-target-feature",

@@ -1,11 +1,11 @@
 // Fused variable-length attention forward for AMD Instinct MI355X (gfx950).
 //
-// One workgroup = 8 wavefronts (512 threads, two per SIMD) owns BM = 256
-// query rows of one (segment, head); each wave owns 32 of them.  It walks
-// the key tiles those rows can see (tile_schedule.h), BN = 64 keys at a time:
+// A workgroup owns a block of query rows of one (segment, head), 64 rows per
+// wavefront, and walks the key tiles those rows can see (tile_schedule.h),
+// 32 keys at a time:
 //
 //   HBM K/V tile --buffer_load ... lds (direct to LDS, out-of-range rows
-//   read as zero)--> LDS, double buffered
+//   read as zero)--> one of six LDS stages, issued four tiles ahead
 //   --> S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (Q held in registers)
 //   --> online softmax in registers (exp2 with a log2(e)-prescaled scale,
 //       lazy rescale past a threshold)
@@ -15,13 +15,15 @@
 // Scores are computed transposed (keys on the MFMA M axis, queries on N), so
 // each lane holds one query column: the row max and row sum over the keys a
 // lane holds are in-lane reductions with a single cross-lane step (lane l with
-// lane l ^ 32) per tile.  The probability registers then serve directly as
-// the B operand of the PV product, with the key order inside each 16-key
-// group permuted identically on the V side.
+// lane l ^ 32).  The probability registers then serve directly as the B
+// operand of the PV product, with the key order inside each 16-key group
+// permuted identically on the V side.  Each LDS operand read feeds the MFMAs
+// of a wave's two 32-row query blocks.
 //
-// The two waves on each SIMD run half a tile apart (ping-pong), so one
-// wave's softmax overlaps the other's MFMAs; K/V tiles stream into LDS two
-// phases ahead of use.
+// Each wave software-pipelines its tiles: iteration j runs PV of tile j - 1
+// and QK^T of tile j + 1 on the matrix cores, interleaved by hand with the
+// softmax of tile j, whose exp does not wait for tile j's max (see
+// fused_block in attn_fwd_wide).
 //
 // Where the pages describe FA4 on Blackwell (TMEM, tcgen05.ld.red row max,
 // 2-CTA MMA) that design is prior art only; what carries over is the online
@@ -117,6 +119,20 @@ struct BoolTag {
   static constexpr bool value = B;
 };
 
+template <int N>
+struct Int {
+  static constexpr int value = N;
+};
+
+// f(Int<I>{}), ..., f(Int<N - 1>{}) in order, unrolled.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Int<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 v;
@@ -152,360 +168,6 @@ __device__ __forceinline__ bf16x8 lds_read_b128(const lds_char* base, int byte_o
 
 __device__ __forceinline__ bf16x4 lds_read_tr(const lds_char* base, int byte_off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(base + byte_off));
-}
-
-// ============================================================================
-// Ping-pong kernel (head dims >= 128): 8 waves x 32 query rows, 64-key tiles.
-// ============================================================================
-namespace pingpong {
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;  // query rows per workgroup
-constexpr int kBN = 64;           // keys per tile
-template <int DQK, int DV>
-struct Cfg : TileGeom<DQK, DV, kBN, kWaves> {
-  static constexpr int LDS_BYTES = 2 * (Cfg::K_TILE + Cfg::V_TILE);
-};
-}  // namespace pingpong
-
-template <int DQK, int DV>
-__global__ __launch_bounds__(pingpong::kThreads) void attn_fwd_pingpong(Params p) {
-  using namespace pingpong;
-  using C = Cfg<DQK, DV>;
-  __shared__ __attribute__((aligned(1024))) char lds_raw[C::LDS_BYTES];
-  lds_char* lds = (lds_char*)lds_raw;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int g = lane >> 5;
-
-  // ---- work unit (see decode_block in tile_schedule.h) -------------------
-  const WorkUnit wu = decode_block(blockIdx.x, p.batch, p.heads, p.n_qt, p.causal);
-  if (!wu.valid) return;
-  const int b = wu.b, h = wu.h, qt = wu.qt;
-
-  const int q0 = p.cu_q[b];
-  const int Lq = p.cu_q[b + 1] - q0;
-  const int k0 = p.cu_k[b];
-  const int Lk = p.cu_k[b + 1] - k0;
-  const int r0 = qt * kBM;
-  if (r0 >= Lq) return;
-  const int r1 = min(r0 + kBM, Lq);
-  const TileRange tr = tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN);
-  const int ntiles = tr.kt_end - tr.kt_begin;
-  const int wrow0 = r0 + wave * 32;
-  const int myrow = wrow0 + l32;
-
-  // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ---------
-  bf16x8 qf[C::KC];
-  {
-    const uint16_t* src = p.q + (int64_t)(q0 + myrow) * p.q_row + (int64_t)h * p.q_head;
-#pragma unroll
-    for (int c = 0; c < C::KC; ++c) {
-      const int d = c * 16 + 8 * g;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (myrow < r1 && d < DQK) x = *(const u32x4*)(src + d);
-      qf[c] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
-
-  // ---- per-lane offsets of the direct-to-LDS tile loads --------------------
-  // K wave-load j covers LDS chunk slots [64 j, 64 j + 64) of the tile; slot
-  // s holds row s / KPITCH, chunk s % KPITCH (the last chunk of a row is pad).
-  const int64_t k_row_b = p.k_row * 2, v_row_b = p.v_row * 2;
-  uint32_t koff[C::K_LOADS];
-  bool kact[C::K_LOADS];
-#pragma unroll
-  for (int i = 0; i < C::K_LOADS; ++i) {
-    const int s = (wave + kWaves * i) * 64 + lane;
-    const int row = s / C::KPITCH, c = s % C::KPITCH;
-    kact[i] = c < C::CPR_K;
-    koff[i] = c < C::K_REAL ? (uint32_t)(row * k_row_b + c * 16) : kOOB;  // 72: chunk 9 -> zeros
-  }
-  uint32_t voff[C::V_LOADS];
-  bool vact[C::V_LOADS];
-#pragma unroll
-  for (int i = 0; i < C::V_LOADS; ++i) {
-    const int s = (wave + kWaves * i) * 64 + lane;
-    const int row = s / C::CPR_V;
-    const int c = (s % C::CPR_V) ^ v_swizzle<C::CPR_V>(row);
-    vact[i] = c < C::V_REAL;  // padded dv chunks are never loaded
-    voff[i] = (uint32_t)(row * v_row_b + c * 16);
-  }
-  const char* kseg = (const char*)(p.k + (int64_t)k0 * p.k_row + (int64_t)h * p.k_head);
-  const char* vseg = (const char*)(p.v + (int64_t)k0 * p.v_row + (int64_t)h * p.v_head);
-
-  auto kbuf = [&](int i) { return lds + (i & 1) * (C::K_TILE + C::V_TILE); };
-  auto vbuf = [&](int i) { return lds + (i & 1) * (C::K_TILE + C::V_TILE) + C::K_TILE; };
-
-  auto load_k = [&](int tile, lds_char* dst) {
-    const int key0 = tile * kBN;
-    const int rows = min(Lk - key0, kBN);
-    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kseg + key0 * k_row_b), (short)0, (int)(rows * k_row_b), kBufferFlags);
-#pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) {
-      const int wl = wave + kWaves * i;
-      if (wl < C::KPITCH && kact[i])
-        dma16(rs, dst + wl * 1024, koff[i]);
-    }
-  };
-  auto load_v = [&](int tile, lds_char* dst) {
-    const int key0 = tile * kBN;
-    const int rows = min(Lk - key0, kBN);
-    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vseg + key0 * v_row_b), (short)0, (int)(rows * v_row_b), kBufferFlags);
-#pragma unroll
-    for (int i = 0; i < C::V_LOADS; ++i) {
-      const int wl = wave + kWaves * i;
-      if (wl < C::CPR_V && vact[i])
-        dma16(rs, dst + wl * 1024, voff[i]);
-    }
-  };
-
-  // ---- per-lane LDS read offsets -------------------------------------------
-  // K operand: row kb*32 + l32, chunk 2c + g  ->  k_rd + kb*32*KPITCH*16 + 32c
-  const int k_rd = (l32 * C::KPITCH + g) * 16;
-  // V^T operand via transposing reads: lane i of 16-lane group G supplies
-  // row (4g + i/4) [+ 16t + 8h], dv 32vb + 16(G%2) + 4(i%4).
-  int v_rd[C::VB];
-  {
-    const int G = lane >> 4, i = lane & 15;
-    const int vrow = 4 * g + (i >> 2);
-    const int y = 2 * (G & 1) + ((i >> 1) & 1);
-#pragma unroll
-    for (int vb = 0; vb < C::VB; ++vb)
-      v_rd[vb] = (vrow * C::CPR_V + ((4 * vb + y) ^ v_swizzle<C::CPR_V>(vrow))) * 16 + 8 * (i & 1);
-  }
-
-  // ---- running state -------------------------------------------------------
-  f32x16 acc[C::VB];
-#pragma unroll
-  for (int vb = 0; vb < C::VB; ++vb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[vb][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  int row_lo, row_hi;
-  {
-    const RowBounds rb = row_bounds(myrow, Lq, Lk, p.causal, p.wl, p.wr);
-    row_lo = (int)imin64(rb.lo, (int64_t)Lk);  // clamp into int range
-    row_hi = (int)imax64(rb.hi, (int64_t)-1);
-  }
-
-  // S^T = K Q^T for one tile: [64 keys = 2 x 32] x [32 queries].
-  auto qk = [&](const lds_char* ks, f32x16 (&s)[2]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-    for (int c = 0; c < C::KC; ++c) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = lds_read_b128(ks, k_rd + kb * 32 * C::KPITCH * 16 + 32 * c);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
-      }
-    }
-  };
-
-  // O^T += V^T P^T: [dv] x [32 queries], 16 keys per MFMA.
-  auto pv = [&](const lds_char* vs, const bf16x8 (&pf)[4]) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int vb = 0; vb < C::VB; ++vb) {
-        const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
-        const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
-        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], acc[vb], 0, 0, 0);
-      }
-    }
-  };
-
-  // Online softmax of one tile of scores.  The lane holds query l32 and keys
-  // key0 + 32 kb + 8 (r / 4) + 4 g + r % 4; it leaves the probabilities in
-  // pf, packed to bf16 as the B operand of the PV product.
-  auto softmax = [&](f32x16 (&s)[2], bf16x8 (&pf)[4], int key0, auto masked_tag) {
-    constexpr bool kMasked = decltype(masked_tag)::value;
-    if constexpr (kMasked) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = key0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-          s[kb][r] = (j >= row_lo && j <= row_hi) ? s[kb][r] : -INFINITY;
-        }
-    }
-    float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-    mx = fmaxf(mx, other_half(mx));
-    const float m_new = fmaxf(m_run, mx * p.scale_log2);
-    if (__any(m_new > m_run + kRescaleTau)) {
-      // Keeps the rescale a real branch: it is rare, and speculating it
-      // would put 16 * VB multiplies on every tile.
-      asm volatile("; lazy rescale" ::: "memory");
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int vb = 0; vb < C::VB; ++vb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[vb][r] *= alpha;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float sum = 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      u32x4 pk;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 8 * (t & 1) + 2 * e;
-        const float x0 = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][r], p.scale_log2, -m_use));
-        const float x1 = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][r + 1], p.scale_log2, -m_use));
-        sum += x0 + x1;
-        pk[e] = pack_bf16x2(x0, x1);
-      }
-      pf[t] = __builtin_bit_cast(bf16x8, pk);
-    }
-    l_run += sum;
-  };
-
-  // ---- ping-pong main loop -------------------------------------------------
-  // Waves 0-3 (group 0) and 4-7 (group 1) put one wave of each group on
-  // every SIMD.  Each wave alternates an MFMA phase (PV of the previous tile,
-  // then QK^T of the current one) and a VALU phase (softmax of the current
-  // tile).  Group 1 runs one phase behind group 0, and every phase ends at a
-  // workgroup barrier, so in each slot one wave per SIMD is in its MFMA phase
-  // while the other is in its softmax.
-  //
-  // Tile j (counted from kt_begin) has K in kbuf(j) and V in vbuf(j).  The
-  // MFMA phase of tile j reads K_j and V_{j-1}; in slot 2j (the slot where
-  // group 0 starts tile j) every wave issues its share of the loads of K_{j+1}
-  // and V_j, and waits for them at the end of slot 2j + 1, so they are
-  // visible from slot 2j + 2 on.  Those buffers last held K_{j-1} and
-  // V_{j-2}, whose readers finished by slot 2j - 1.
-  const int grp = wave >> 2;
-  auto issue_loads = [&](int j) {  // K_{j+1} and V_j
-    if (j + 1 < ntiles) load_k(tr.kt_begin + j + 1, kbuf(j + 1));
-    if (j < ntiles) load_v(tr.kt_begin + j, vbuf(j));
-  };
-  auto wait_loads = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-
-  if (ntiles > 0) {
-    f32x16 s[2];
-    bf16x8 pf[4];
-    // One MFMA phase as a single stream of MFMAs: the PV product of the
-    // previous tile (4 * VB MFMAs) then QK^T of this one (2 * KC).  Each MFMA's
-    // LDS operand is read kDepth MFMAs ahead into a ring of registers, and
-    // scheduling barriers keep that order, so every 32-cycle MFMA finds its
-    // operand waiting instead of stalling on LDS latency.
-    auto mfma_phase = [&](int j, auto pv_tag) {  // slot 2j + grp
-      constexpr bool kPV = decltype(pv_tag)::value;
-      constexpr int kPVOps = kPV ? 4 * C::VB : 0;
-      constexpr int kOps = kPVOps + 2 * C::KC;
-      constexpr int kDepth = 6;
-      if (grp == 0) issue_loads(j);
-      const lds_char* vs = vbuf(j - 1);
-      const lds_char* ks = kbuf(j);
-      auto load_op = [&](int i, bf16x8& dst) {
-        if (i < kPVOps) {  // V^T operand of PV MFMA (t, vb)
-          const int t = i / C::VB, vb = i % C::VB;
-          const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
-          const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
-          dst = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        } else {  // K operand of QK MFMA (c, kb)
-          const int c = (i - kPVOps) / 2, kb = (i - kPVOps) % 2;
-          dst = lds_read_b128(ks, k_rd + kb * 32 * C::KPITCH * 16 + 32 * c);
-        }
-      };
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      bf16x8 ring[kDepth];
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int i = 0; i < kDepth && i < kOps; ++i) load_op(i, ring[i]);
-#pragma unroll
-      for (int i = 0; i < kOps; ++i) {
-        if (i < kPVOps) {
-          const int t = i / C::VB, vb = i % C::VB;
-          acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kDepth], pf[t], acc[vb], 0, 0, 0);
-        } else {
-          const int c = (i - kPVOps) / 2, kb = (i - kPVOps) % 2;
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kDepth], qf[c], s[kb], 0, 0, 0);
-        }
-        if (i + kDepth < kOps) load_op(i + kDepth, ring[i % kDepth]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      if (grp == 1) wait_loads();
-      __syncthreads();
-    };
-    auto valu_phase = [&](int j, auto masked_tag) {  // slot 2j + 1 + grp
-      if (grp == 1) issue_loads(j + 1);
-      softmax(s, pf, (tr.kt_begin + j) * kBN, masked_tag);
-      if (grp == 0) wait_loads();
-      __syncthreads();
-    };
-    load_k(tr.kt_begin, kbuf(0));
-    wait_loads();
-    __syncthreads();
-    if (grp == 1) {  // slot 0 for group 1: issue its loads of K_1, V_0
-      issue_loads(0);
-      __syncthreads();
-    }
-    // Tile 0, then tiles [1, a) masked, [a, b) unmasked, [b, ntiles) masked:
-    // masked tiles only sit at the two ends of the visited range.
-    mfma_phase(0, BoolTag<false>{});
-    if (tr.kt_begin >= tr.full_begin && tr.kt_begin < tr.full_end)
-      valu_phase(0, BoolTag<false>{});
-    else
-      valu_phase(0, BoolTag<true>{});
-    const int a = min(max(tr.full_begin - tr.kt_begin, 1), ntiles);
-    const int bnd = min(max(tr.full_end - tr.kt_begin, a), ntiles);
-    int j = 1;
-    for (; j < a; ++j) {
-      mfma_phase(j, BoolTag<true>{});
-      valu_phase(j, BoolTag<true>{});
-    }
-    for (; j < bnd; ++j) {
-      mfma_phase(j, BoolTag<true>{});
-      valu_phase(j, BoolTag<false>{});
-    }
-    for (; j < ntiles; ++j) {
-      mfma_phase(j, BoolTag<true>{});
-      valu_phase(j, BoolTag<true>{});
-    }
-    pv(vbuf(ntiles - 1), pf);
-    if (grp == 0) __syncthreads();  // matches group 1's extra slot-0 barrier
-  }
-
-  // ---- epilogue ------------------------------------------------------------
-  const float l = l_run + other_half(l_run);
-  if (myrow < r1) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* dst = p.o + (int64_t)(q0 + myrow) * p.o_row + (int64_t)h * p.o_head;
-#pragma unroll
-    for (int vb = 0; vb < C::VB; ++vb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int dv = vb * 32 + 8 * j + 4 * g;
-        if (dv < DV) {
-          u32x2 o2;
-          o2[0] = pack_bf16x2(acc[vb][4 * j] * inv, acc[vb][4 * j + 1] * inv);
-          o2[1] = pack_bf16x2(acc[vb][4 * j + 2] * inv, acc[vb][4 * j + 3] * inv);
-          *(u32x2*)(dst + dv) = o2;
-        }
-      }
-    if (p.lse != nullptr && g == 0) {
-      const float lse = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
-      p.lse[(int64_t)h * p.total_q + q0 + myrow] = lse;
-    }
-  }
 }
 
 // ============================================================================
@@ -827,39 +489,34 @@ __global__ __launch_bounds__(dual::kThreads, 2) void attn_fwd_dual(Params p) {
 // every V read wait for all DMA in flight (s_waitcnt vmcnt(0)).
 // ============================================================================
 namespace wide {
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 64;
-constexpr int kBM = kRowsPerWave * kWaves;  // query rows per workgroup
-constexpr int kBN = 32;                     // keys per tile
-constexpr int kStages = 6;                  // tile t lives in stage t % 6 (an even count: see the loop)
-constexpr int kAhead = kStages - 2;         // iteration j issues tile j + 4
-constexpr int kDepth = 3;                   // LDS operands read ahead of their MFMA
+constexpr int kBN = 32;              // keys per tile
+constexpr int kStages = 6;           // tile t lives in stage t % 6 (an even count: see the loop)
+constexpr int kAhead = kStages - 2;  // iteration j issues tile j + 4
+constexpr int kDepth = 3;            // LDS operands read ahead of their MFMA
+// Head dims <= 80 run 8 waves (two per SIMD, within 256 registers each);
+// 128 and 192 run 4 (one per SIMD), whose 64-row accumulators, Q fragments
+// and two score tiles need more than 256 registers.
+template <int DQK>
+constexpr int waves_for() { return DQK >= 128 ? 4 : 8; }
 template <int DQK, int DV>
-struct Cfg : TileGeom<DQK, DV, kBN, kWaves> {
-  static constexpr int N_WL = Cfg::K_WL + Cfg::V_WL;  // wave-loads per tile (K first)
-  static constexpr int LDS_BYTES = kStages * (Cfg::K_TILE + Cfg::V_TILE);
+struct Cfg : TileGeom<DQK, DV, kBN, waves_for<DQK>()> {
+  static constexpr int WAVES = waves_for<DQK>();
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BM = kRowsPerWave * WAVES;  // query rows per workgroup
+  // Every wave issues NK K and NV V wave-loads per tile (zeros into a dummy
+  // area where the tile has fewer), so LOADS per tile and wave is constant.
+  static constexpr int NK = (Cfg::K_WL + WAVES - 1) / WAVES;
+  static constexpr int NV = (Cfg::V_WL + WAVES - 1) / WAVES;
+  static constexpr int LOADS = NK + NV;
+  static constexpr int LDS_BYTES = kStages * (Cfg::K_TILE + Cfg::V_TILE) + 1024;
   // V chunks past the data (d_v 72, 80 padded to 96) are never loaded; they
   // are set once, and may hold a ones column (see attn_fwd_wide).
   static constexpr int V_PAD = Cfg::CPR_V - Cfg::V_REAL;
-  static_assert(N_WL <= 2 * kWaves, "a wave issues at most two wave-loads per tile");
   static_assert(Cfg::CPR_V != 12 || v_swizzle<12>(1) == 0, "pad chunks sit at fixed positions");
 };
 }  // namespace wide
 
-template <int N>
-struct Int {
-  static constexpr int value = N;
-};
-
-// f(Int<I>{}), ..., f(Int<N - 1>{}) in order, unrolled.
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(Int<I>{});
-    static_for<I + 1, N>(f);
-  }
-}
 
 // Cross-half (lane l and lane l ^ 32) max and sum: v_permlane32_swap
 // leaves lane l's and lane l ^ 32's values in the two results.
@@ -884,7 +541,7 @@ __device__ __forceinline__ float from_lower_half(float x) {
 // probabilities the MFMA sees, which moves the LSE by up to ln(1 + 2^-9);
 // with an LSE requested the sum stays in fp32.
 template <int DQK, int DV, bool SUM_BY_MFMA>
-__global__ __launch_bounds__(wide::kThreads, 1) void attn_fwd_wide(Params p) {
+__global__ __launch_bounds__(64 * wide::waves_for<DQK>(), 1) void attn_fwd_wide(Params p) {
   using namespace wide;
   using C = Cfg<DQK, DV>;
   static_assert(!SUM_BY_MFMA || C::V_PAD > 0, "the ones column needs a padded d_v");
@@ -933,9 +590,9 @@ __global__ __launch_bounds__(wide::kThreads, 1) void attn_fwd_wide(Params p) {
   const int Lq = p.cu_q[b + 1] - q0;
   const int k0 = p.cu_k[b];
   const int Lk = p.cu_k[b + 1] - k0;
-  const int r0 = qt * kBM;
+  const int r0 = qt * C::BM;
   if (r0 >= Lq) return;
-  const int r1 = min(r0 + kBM, Lq);
+  const int r1 = min(r0 + C::BM, Lq);
   const TileRange tr = tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN);
   const int ntiles = tr.kt_end - tr.kt_begin;
   const int wrow0 = r0 + wave * kRowsPerWave;
@@ -946,7 +603,7 @@ __global__ __launch_bounds__(wide::kThreads, 1) void attn_fwd_wide(Params p) {
   // ---- padded V chunks: zeros, or a one in column d_v ------------------------
   if constexpr (C::V_PAD > 0) {
     static_for<0, kStages>([&](auto st) VA_INLINE {
-      for (int i = tid; i < kBN * C::V_PAD; i += kThreads) {
+      for (int i = tid; i < kBN * C::V_PAD; i += C::THREADS) {
         const int row = i / C::V_PAD, c = C::V_REAL + i % C::V_PAD;
         const u32x4 val = {(SUM_BY_MFMA && c == C::V_REAL) ? 0x3F80u : 0u, 0u, 0u, 0u};  // bf16 1.0
         *(__attribute__((address_space(3))) u32x4*)(vst(st) + (row * C::CPR_V + c) * 16) = val;
@@ -972,28 +629,31 @@ __global__ __launch_bounds__(wide::kThreads, 1) void attn_fwd_wide(Params p) {
   // ---- direct-to-LDS tile loads ---------------------------------------------
   // A tile is K_WL K wave-loads then V_WL V wave-loads, each 64 lanes x 16
   // bytes: K wave-load i covers K slots [64 i, 64 i + 64), likewise for V.
-  // Wave w issues K wave-load w and V wave-load w every tile; a wave with no
-  // such wave-load (w >= K_WL or w >= V_WL) reads zeros into a dummy area
-  // instead, so every wave issues exactly two loads per tile and every wait
-  // below is a constant.  K pad chunks, chunk 9 of a 72-wide row and slots
-  // past the tile read zeros; lanes on padded V chunks load nothing.
+  // Wave w issues K wave-loads w + WAVES x (x < NK) and V wave-loads
+  // w + WAVES x (x < NV) every tile; where such a wave-load does not exist
+  // it reads zeros into a dummy area instead, so every wave issues LOADS
+  // loads per tile and every wait below is a constant.  K pad chunks, chunk
+  // 9 of a 72-wide row and slots past the tile read zeros; lanes on padded V
+  // chunks load nothing.
   __shared__ __attribute__((aligned(1024))) char dummy[1024];
   const int64_t k_row_b = p.k_row * 2, v_row_b = p.v_row * 2;
-  const bool k_real = wave < C::K_WL, v_real = wave < C::V_WL;
-  uint32_t k_off = kOOB, v_off = kOOB;
-  bool v_on = true;
-  {
-    const int sl = wave * 64 + lane;
-    if (k_real) {
-      const int row = sl / C::KPITCH, c = sl % C::KPITCH;
-      k_off = (sl < C::K_SLOTS && c < C::K_REAL) ? (uint32_t)(row * k_row_b + c * 16) : kOOB;
-    }
-    if (v_real) {
-      const int row = sl / C::CPR_V;
-      const int c = (sl % C::CPR_V) ^ v_swizzle<C::CPR_V>(row);
-      v_on = sl >= C::V_SLOTS || c < C::V_REAL;
-      v_off = (sl < C::V_SLOTS && c < C::V_REAL) ? (uint32_t)(row * v_row_b + c * 16) : kOOB;
-    }
+  uint32_t k_off[C::NK], v_off[C::NV];
+  bool v_on[C::NV];
+#pragma unroll
+  for (int x = 0; x < C::NK; ++x) {
+    const int i = wave + C::WAVES * x;
+    const int sl = i * 64 + lane;
+    const int row = sl / C::KPITCH, c = sl % C::KPITCH;
+    k_off[x] = (i < C::K_WL && sl < C::K_SLOTS && c < C::K_REAL) ? (uint32_t)(row * k_row_b + c * 16) : kOOB;
+  }
+#pragma unroll
+  for (int x = 0; x < C::NV; ++x) {
+    const int i = wave + C::WAVES * x;
+    const int sl = i * 64 + lane;
+    const int row = sl / C::CPR_V;
+    const int c = (sl % C::CPR_V) ^ v_swizzle<C::CPR_V>(row);
+    v_on[x] = i >= C::V_WL || sl >= C::V_SLOTS || c < C::V_REAL;
+    v_off[x] = (i < C::V_WL && sl < C::V_SLOTS && c < C::V_REAL) ? (uint32_t)(row * v_row_b + c * 16) : kOOB;
   }
   // K/V rows of the next tile to issue, advanced one tile per issue; tiles
   // past the last get an empty range (all reads zero).
@@ -1002,7 +662,7 @@ __global__ __launch_bounds__(wide::kThreads, 1) void attn_fwd_wide(Params p) {
   const char* v_next =
       (const char*)(p.v + ((int64_t)k0 + (int64_t)tr.kt_begin * kBN) * p.v_row + (int64_t)h * p.v_head);
   int keys_next = Lk - tr.kt_begin * kBN;
-  auto issue = [&](auto st) VA_INLINE {  // this wave's two loads of the next tile into stage st
+  auto issue = [&](auto st) VA_INLINE {  // this wave's loads of the next tile into stage st
     // (readfirstlane: the clamp compiles to a VALU med3, and a descriptor
     // the compiler cannot prove uniform costs a waterfall loop per load)
     const int rows = __builtin_amdgcn_readfirstlane(max(min(keys_next, kBN), 0));
@@ -1010,22 +670,27 @@ __global__ __launch_bounds__(wide::kThreads, 1) void attn_fwd_wide(Params p) {
         __builtin_amdgcn_make_buffer_rsrc((void*)k_next, (short)0, (int)(rows * k_row_b), kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv =
         __builtin_amdgcn_make_buffer_rsrc((void*)v_next, (short)0, (int)(rows * v_row_b), kBufferFlags);
-    dma16(rk, k_real ? kst(st) + wave * 1024 : (lds_char*)dummy, k_off);
-    if (v_on) dma16(rv, v_real ? vst(st) + wave * 1024 : (lds_char*)dummy, v_off);
+#pragma unroll
+    for (int x = 0; x < C::NK; ++x) {
+      const int i = wave + C::WAVES * x;
+      dma16(rk, i < C::K_WL ? kst(st) + i * 1024 : (lds_char*)dummy, k_off[x]);
+    }
+#pragma unroll
+    for (int x = 0; x < C::NV; ++x) {
+      const int i = wave + C::WAVES * x;
+      if (v_on[x]) dma16(rv, i < C::V_WL ? vst(st) + i * 1024 : (lds_char*)dummy, v_off[x]);
+    }
     k_next += kBN * k_row_b;
     v_next += kBN * v_row_b;
     keys_next -= kBN;
   };
-  // Every iteration issues two loads per wave, and loads complete in issue
+  // Every iteration issues LOADS loads per wave, and loads complete in issue
   // order: "tile t landed" with the loads of n later tiles in flight is
-  // s_waitcnt vmcnt(2 n).
+  // s_waitcnt vmcnt(n LOADS).
   auto wait_landed = [&](auto later_tiles) VA_INLINE {
-    constexpr int n = 2 * decltype(later_tiles)::value;
-    static_assert(n == 4 || n == 6, "vmcnt cases below");
-    if constexpr (n == 4)
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    constexpr int n = C::LOADS * decltype(later_tiles)::value;
+    static_assert(n < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
   };
 
   // ---- LDS operand reads ----------------------------------------------------
@@ -1162,61 +827,85 @@ __global__ __launch_bounds__(wide::kThreads, 1) void attn_fwd_wide(Params p) {
     }
     return move;
   };
-  // Fast path of the softmax, free of any dependence on this tile's max:
-  // p = exp2(s * scale * log2(e) - m_run) with the running max as it stands,
-  // computed in place, packed to bf16, and a check that it was valid: no
-  // row's tile max exceeds m_run + kRescaleTau (then p <= 2^kRescaleTau,
-  // exactly what the lazy rescale would have produced) and no row saw its
-  // first visible key (m_run = -inf).  The row sum goes to sum[] and is
-  // committed by the caller only if the check passed.
-  auto softmax_fast = [&](f32x16 (&s)[2], float (&sum)[2]) VA_INLINE -> bool {
+  // One iteration's MFMAs and fast-path softmax, interleaved by hand.
+  //
+  // The fast path needs nothing of this tile's max: p = exp2(s * scale *
+  // log2(e) - m_run) with the running max as it stands, in place, packed to
+  // bf16, and a check that this was valid: no row's tile max exceeds m_run +
+  // kRescaleTau (then p <= 2^kRescaleTau, exactly what the lazy rescale would
+  // produce) and no row saw its first visible key (lim = -FLT_MAX while m_run
+  // is -inf).  The row sums go to sum[], committed by the caller only if the
+  // check passed.
+  //
+  // Its VALU work is 64 units in dependency order: 16 row-max steps (8 per
+  // query block, on the raw scores), 32 in-place exps, 16 packs (+ sums).
+  // The MFMAs (PV of the previous tile, then QK^T of the next, two per LDS
+  // operand) each get an even share of the units, in source order pinned by
+  // scheduling barriers: the compiler's own schedule bunches the MFMAs, and
+  // an MFMA hides only a few VALU ops behind it.  The packs, which overwrite
+  // the probabilities PV reads, all fall after the last PV MFMA.
+  auto fused_block = [&](const lds_char* vs, const lds_char* ks, f32x16 (&s)[2], f32x16 (&sn)[2],
+                         float (&sum)[2]) VA_INLINE -> bool {
+    constexpr int kPVOps = 2 * C::VB, kOps = kPVOps + C::KC, kSlots = 2 * kOps, kUnits = 64;
+    static_assert(48 * kSlots / kUnits >= 2 * kPVOps, "packs must follow the PV MFMAs");
+    float m[2];
     bool bad = false;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float m = fmaxf(fmaxf(s[qb][0], s[qb][1]), s[qb][2]);
-#pragma unroll
-      for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, s[qb][r]), s[qb][r + 1]);
-      m = fmaxf(m, s[qb][15]);
-      bad |= m * p.scale_log2 > lim[qb];
-    }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      sum[qb] = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[qb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, nm[qb]));
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 8 * t + 2 * e;
-          if constexpr (!SUM_BY_MFMA) sum[qb] += s[qb][r] + s[qb][r + 1];
-          pk[e] = pack_bf16x2(s[qb][r], s[qb][r + 1]);
+    u32x4 pk[2][2];
+    sum[0] = sum[1] = 0.f;
+    auto unit = [&](auto uu) VA_INLINE {
+      constexpr int u = decltype(uu)::value;
+      if constexpr (u < 16) {  // row max, 8 steps per query block
+        constexpr int qb = u / 8, st = u % 8;
+        if constexpr (st == 0) {
+          m[qb] = fmaxf(fmaxf(s[qb][0], s[qb][1]), s[qb][2]);
+        } else if constexpr (st < 7) {
+          m[qb] = fmaxf(fmaxf(m[qb], s[qb][2 * st + 1]), s[qb][2 * st + 2]);
+        } else {
+          m[qb] = fmaxf(m[qb], s[qb][15]);
+          bad |= m[qb] * p.scale_log2 > lim[qb];
         }
-        pf[qb][t] = __builtin_bit_cast(bf16x8, pk);
+      } else if constexpr (u < 48) {  // p = exp2(s * scale - m_run), in place
+        constexpr int qb = (u - 16) / 16, r = (u - 16) % 16;
+        s[qb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, nm[qb]));
+      } else {  // bf16 pack (and fp32 row sum)
+        constexpr int i = u - 48, qb = i / 8, t = (i / 4) % 2, e = i % 4, r = 8 * t + 2 * e;
+        if constexpr (!SUM_BY_MFMA) sum[qb] += s[qb][r] + s[qb][r + 1];
+        pk[qb][t][e] = pack_bf16x2(s[qb][r], s[qb][r + 1]);
+        if constexpr (e == 3) pf[qb][t] = __builtin_bit_cast(bf16x8, pk[qb][t]);
       }
-    }
+    };
+    auto load_op = [&](int i, bf16x8& dst) VA_INLINE {
+      if (i < kPVOps) {  // V^T operand (t, vb) of PV
+        const int t = i / C::VB, vb = i % C::VB;
+        const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
+        const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
+        dst = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      } else {  // K operand c of QK^T
+        dst = lds_read_b128(ks, k_rd + 32 * (i - kPVOps));
+      }
+    };
+    const f32x16 zero = {};
+    bf16x8 ring[kDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) load_op(i, ring[i]);
+    static_for<0, kOps>([&](auto oo) VA_INLINE {
+      constexpr int i = decltype(oo)::value;
+      const bf16x8 op = ring[i % kDepth];
+      if constexpr (i + kDepth < kOps) load_op(i + kDepth, ring[i % kDepth]);
+      static_for<0, 2>([&](auto qq) VA_INLINE {
+        constexpr int qb = decltype(qq)::value, slot = 2 * i + qb;
+        if constexpr (i < kPVOps) {
+          constexpr int t = i / C::VB, vb = i % C::VB;
+          acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, pf[qb][t], acc[vb][qb], 0, 0, 0);
+        } else {
+          constexpr int c = i - kPVOps;
+          sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qf[qb][c], c == 0 ? zero : sn[qb], 0, 0, 0);
+        }
+        static_for<slot * kUnits / kSlots, (slot + 1) * kUnits / kSlots>(unit);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
     return __any(bad);
-  };
-  // Instruction order of one iteration's MFMA + softmax block, for the
-  // scheduler: each MFMA (PV of the previous tile, then QK^T of the next)
-  // followed by an even share of the softmax's VALU work, every LDS operand
-  // read kDepth operands ahead of its MFMAs.  Masks: 0x100 LDS read, 0x008
-  // MFMA, 0x402 VALU including transcendentals.
-  auto interleave = [&]() VA_INLINE {
-    constexpr int kPVOps = 2 * C::VB, kOps = kPVOps + C::KC;
-    constexpr int kValu = SUM_BY_MFMA ? 5 : 7;
-    static_for<0, kDepth>([&](auto o) VA_INLINE {
-      __builtin_amdgcn_sched_group_barrier(0x100, decltype(o)::value < kPVOps ? 2 : 1, 0);
-    });
-    static_for<0, kOps>([&](auto o) VA_INLINE {
-      constexpr int i = decltype(o)::value;
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, kValu, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, kValu, 0);
-      if constexpr (i + kDepth < kOps) __builtin_amdgcn_sched_group_barrier(0x100, i + kDepth < kPVOps ? 2 : 1, 0);
-    });
   };
   // QK^T of one tile on its own (tile 0, and the slow path below).
   auto qk_only = [&](const lds_char* ks, f32x16 (&sn)[2]) VA_INLINE {
@@ -1277,14 +966,13 @@ __global__ __launch_bounds__(wide::kThreads, 1) void attn_fwd_wide(Params p) {
           if (active) {
             constexpr int cur = (U + 1) % 2;  // j % 2, j0 being odd
             mask(j, sbuf[cur]);
-            mfma_ops(vst(Int<U % kStages>{}), kst(Int<(U + 2) % kStages>{}), sbuf[cur ^ 1], BoolTag<true>{});
             float sum[2];
-            const bool slow = softmax_fast(sbuf[cur], sum);
+            const bool slow = fused_block(vst(Int<U % kStages>{}), kst(Int<(U + 2) % kStages>{}), sbuf[cur],
+                                          sbuf[cur ^ 1], sum);
             // The probabilities are only read in the next iteration; without
             // this use the compiler sinks their computation past the branch
-            // below, out of reach of the interleave.
+            // below, out of the interleave.
             asm volatile("" ::"v"(pf[0][0]), "v"(pf[0][1]), "v"(pf[1][0]), "v"(pf[1][1]));
-            interleave();
             // Commit the row sums on one path (the slow path restores them):
             // two paths merging into l_run cost the register allocator dearly.
             const float l_prev[2] = {l_run[0], l_run[1]};
@@ -1372,12 +1060,11 @@ __global__ __launch_bounds__(wide::kThreads, 1) void attn_fwd_wide(Params p) {
 // ============================================================================
 namespace va {
 
-// Kernel families.  Head dims <= 80 run the wide ping-pong kernel (64 rows
-// per wave, 512-row blocks) when some segment is longer than 256 queries,
-// else the dual kernel (256-row blocks, two workgroups per CU), which wastes
-// less on short segments.  Larger head dims run the ping-pong kernel (32 rows
-// per wave): 64 rows of a 128-wide accumulator would not fit two waves per
-// SIMD.
+// Kernel families.  The wide kernel (64 query rows per wave) runs 8 waves
+// and 512-row blocks for head dims <= 80, 4 waves and 256-row blocks for 128
+// and 192/128.  Head dims <= 80 with no segment longer than 256 queries run
+// the dual kernel instead (256-row blocks, two workgroups per CU), which
+// wastes less on short segments.
 struct Variant {
   const void* fn;
   int lds_bytes;
@@ -1394,13 +1081,9 @@ static Variant dual_variant() {
 }
 template <int DQK, int DV, bool SUM_BY_MFMA = false>
 static Variant wide_variant() {
-  return {(const void*)&attn_fwd_wide<DQK, DV, SUM_BY_MFMA>, wide::Cfg<DQK, DV>::LDS_BYTES, wide::kBM,
-          wide::kBN, wide::kThreads, "attn_fwd_wide"};
-}
-template <int DQK, int DV>
-static Variant pingpong_variant() {
-  return {(const void*)&attn_fwd_pingpong<DQK, DV>, pingpong::Cfg<DQK, DV>::LDS_BYTES, pingpong::kBM,
-          pingpong::kBN, pingpong::kThreads, "attn_fwd_pingpong"};
+  using C = wide::Cfg<DQK, DV>;
+  return {(const void*)&attn_fwd_wide<DQK, DV, SUM_BY_MFMA>, C::LDS_BYTES, C::BM, wide::kBN, C::THREADS,
+          "attn_fwd_wide"};
 }
 
 static bool supported_dims(int dqk, int dv) {
@@ -1421,8 +1104,8 @@ static Variant variant_for(int dqk, int dv, int max_seqlen_q, bool lse = true) {
     return !wide ? dual_variant<72, 72>() : lse ? wide_variant<72, 72>() : wide_variant<72, 72, true>();
   if (dqk == 80)
     return !wide ? dual_variant<80, 80>() : lse ? wide_variant<80, 80>() : wide_variant<80, 80, true>();
-  if (dqk == 128) return pingpong_variant<128, 128>();
-  return pingpong_variant<192, 128>();
+  if (dqk == 128) return wide_variant<128, 128>();
+  return wide_variant<192, 128>();
 }
 
 static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }

@@ -153,7 +153,7 @@ typedef struct va_plan {
   int32_t threads;       /* threads per workgroup */
   int32_t lds_bytes;     /* LDS per workgroup */
   int64_t grid;          /* workgroups launched (some exit at once on short segments) */
-  const char* kernel;    /* kernel family: "attn_fwd_wide" or, for head dims <= 80 with no segment over 256 queries, "attn_fwd_dual" */
+  const char* kernel;    /* kernel name ("attn_fwd_wide"); block_m and threads give its launch shape */
 } va_plan;
 
 int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch, int32_t num_heads,

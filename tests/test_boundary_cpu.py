@@ -151,10 +151,10 @@ def test_empty_work_returns_ok_without_launch():
 def test_plan():
     p = pkg.plan(80, 80, 8, 16, 4096, 4096)
     assert p["block_n"] in (32, 64) and p["threads"] in (256, 512)
-    assert p["kernel"] == "attn_fwd_wide" and p["block_m"] == 512
-    # segments of at most 256 queries take the 256-row kernel
+    assert p["kernel"] == "attn_fwd_wide" and p["block_m"] == 256 and p["threads"] == 256
+    # one launch shape for every head dim and segment length
     short = pkg.plan(80, 80, 36, 16, 256, 256)
-    assert short["kernel"] == "attn_fwd_dual" and short["block_m"] == 256
+    assert short["kernel"] == "attn_fwd_wide" and short["block_m"] == 256 and short["threads"] == 256
     assert pkg.plan(64, 64, 1, 16, 257, 257)["kernel"] == "attn_fwd_wide"
     assert pkg.plan(128, 128, 1, 16, 4096, 4096)["kernel"] == "attn_fwd_wide"
     # 8 x 16 (segment, head) groups, already a multiple of the 8 XCDs

@@ -72,9 +72,8 @@ struct Params {
   float scale_log2;  // softmax_scale * log2(e)
 };
 
-// Geometry of one K/V tile of BN keys staged in LDS, for a workgroup of
-// WAVES waves.
-template <int DQK, int DV, int BN, int WAVES>
+// Geometry of one K/V tile of BN keys staged in LDS.
+template <int DQK, int DV, int BN>
 struct TileGeom {
   static constexpr int DQKP = (DQK + 15) / 16 * 16;  // MFMA K granularity (72 -> 80)
   static constexpr int DVP = (DV + 31) / 32 * 32;    // 32-row V^T MFMA blocks (72, 80 -> 96)
@@ -96,8 +95,6 @@ struct TileGeom {
   static constexpr int V_WL = (V_SLOTS + 63) / 64;
   static constexpr int K_TILE = K_WL * 1024;         // bytes
   static constexpr int V_TILE = V_WL * 1024;
-  static constexpr int K_LOADS = (K_WL + WAVES - 1) / WAVES;  // most wave-loads one wave issues
-  static constexpr int V_LOADS = (V_WL + WAVES - 1) / WAVES;
   static_assert(CPR_V == 8 || CPR_V == 12 || CPR_V == 16, "V swizzle defined for 8/12/16 chunks");
 };
 
@@ -141,13 +138,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Value of lane l ^ 32 (the other half of the wave), without an LDS trip.
-__device__ __forceinline__ float other_half(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  // lanes 0-31 find the upper half's values in r[1], lanes 32-63 the lower
-  // half's in r[0]
-  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
-}
 
 // Workgroup barrier without __syncthreads()'s release/acquire fences.  With
 // LDS-DMA in flight the release fence turns into s_waitcnt vmcnt(0), making
@@ -171,312 +161,16 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const lds_char* base, int byte_off
 }
 
 // ============================================================================
-// Dual kernel (head dims <= 80): 4 waves x 64 query rows, 32-key tiles, and
-// two workgroups per CU.
-//
-// Each LDS operand read feeds two MFMAs (the wave's two 32-row query
-// blocks), halving LDS read traffic per MFMA against the ping-pong kernel;
-// the small accumulator (d_v <= 96 padded) keeps a wave within 256 VGPRs, so
-// two workgroups share each CU and the two waves on a SIMD overlap one's
-// softmax with the other's MFMAs.  Per 32-key tile a wave runs
-//   S^T = K Q^T -> mask (boundary tiles) + row max -> lazy rescale ->
-//   exp2 / row sum / bf16 pack -> O^T += V^T P^T,
-// while the tile two steps ahead streams into the third LDS stage.
-// ============================================================================
-namespace dual {
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerWave = 64;
-constexpr int kBM = kRowsPerWave * kWaves;  // query rows per workgroup
-constexpr int kBN = 32;                     // keys per tile
-constexpr int kStages = 3;
-template <int DQK, int DV>
-struct Cfg : TileGeom<DQK, DV, kBN, kWaves> {
-  static constexpr int LDS_BYTES = kStages * (Cfg::K_TILE + Cfg::V_TILE);
-};
-}  // namespace dual
-
-template <int DQK, int DV>
-__global__ __launch_bounds__(dual::kThreads, 2) void attn_fwd_dual(Params p) {
-  using namespace dual;
-  using C = Cfg<DQK, DV>;
-  __shared__ __attribute__((aligned(1024))) char lds_raw[C::LDS_BYTES];
-  lds_char* lds = (lds_char*)lds_raw;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int g = lane >> 5;
-
-  const WorkUnit wu = decode_block(blockIdx.x, p.batch, p.heads, p.n_qt, p.causal);
-  if (!wu.valid) return;
-  const int b = wu.b, h = wu.h, qt = wu.qt;
-  const int q0 = p.cu_q[b];
-  const int Lq = p.cu_q[b + 1] - q0;
-  const int k0 = p.cu_k[b];
-  const int Lk = p.cu_k[b + 1] - k0;
-  const int r0 = qt * kBM;
-  if (r0 >= Lq) return;
-  const int r1 = min(r0 + kBM, Lq);
-  const TileRange tr = tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN);
-  const int ntiles = tr.kt_end - tr.kt_begin;
-  // This lane's query rows: wrow0 + 32 qb + l32, qb = 0, 1.
-  const int wrow0 = r0 + wave * kRowsPerWave;
-
-  // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------
-  bf16x8 qf[2][C::KC];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = wrow0 + 32 * qb + l32;
-    const uint16_t* src = p.q + (int64_t)(q0 + row) * p.q_row + (int64_t)h * p.q_head;
-#pragma unroll
-    for (int c = 0; c < C::KC; ++c) {
-      const int d = c * 16 + 8 * g;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < r1 && d < DQK) x = *(const u32x4*)(src + d);
-      qf[qb][c] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
-
-  // ---- direct-to-LDS tile loads ---------------------------------------------
-  // Wave-load j of a tile covers LDS slots [64 j, 64 j + 64); lanes whose
-  // slot is past the tile, a pad chunk, or (72) chunk 9 read zeros.
-  const int64_t k_row_b = p.k_row * 2, v_row_b = p.v_row * 2;
-  uint32_t koff[C::K_LOADS], voff[C::V_LOADS];
-#pragma unroll
-  for (int i = 0; i < C::K_LOADS; ++i) {
-    const int s = (wave + kWaves * i) * 64 + lane;
-    const int row = s / C::KPITCH, c = s % C::KPITCH;
-    koff[i] = (s < C::K_SLOTS && c < C::K_REAL) ? (uint32_t)(row * k_row_b + c * 16) : kOOB;
-  }
-#pragma unroll
-  for (int i = 0; i < C::V_LOADS; ++i) {
-    const int s = (wave + kWaves * i) * 64 + lane;
-    const int row = s / C::CPR_V;
-    const int c = (s % C::CPR_V) ^ v_swizzle<C::CPR_V>(row);
-    voff[i] = (s < C::V_SLOTS && c < C::V_REAL) ? (uint32_t)(row * v_row_b + c * 16) : kOOB;
-  }
-  // Wave-loads this wave issues per tile (the last waves may issue fewer).
-  const int nk = (C::K_WL - wave + kWaves - 1) / kWaves;
-  const int nv = (C::V_WL - wave + kWaves - 1) / kWaves;
-  const char* kseg = (const char*)(p.k + (int64_t)k0 * p.k_row + (int64_t)h * p.k_head);
-  const char* vseg = (const char*)(p.v + (int64_t)k0 * p.v_row + (int64_t)h * p.v_head);
-  auto kbuf = [&](int j) VA_INLINE { return lds + (j % kStages) * (C::K_TILE + C::V_TILE); };
-  auto vbuf = [&](int j) VA_INLINE { return lds + (j % kStages) * (C::K_TILE + C::V_TILE) + C::K_TILE; };
-  auto load_tile = [&](int j) VA_INLINE {  // K and V of tile j into stage j % 3
-    const int key0 = (tr.kt_begin + j) * kBN;
-    const int rows = min(Lk - key0, kBN);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kseg + key0 * k_row_b), (short)0, (int)(rows * k_row_b), kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vseg + key0 * v_row_b), (short)0, (int)(rows * v_row_b), kBufferFlags);
-    lds_char* kd = kbuf(j);
-    lds_char* vd = vbuf(j);
-#pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i)
-      if (i < nk) dma16(rk, kd + (wave + kWaves * i) * 1024, koff[i]);
-#pragma unroll
-    for (int i = 0; i < C::V_LOADS; ++i)
-      if (i < nv) dma16(rv, vd + (wave + kWaves * i) * 1024, voff[i]);
-  };
-  // Wait until at most `pending` of this wave's wave-loads are in flight.
-  auto wait_loads_but = [&](int pending) VA_INLINE {
-    static_assert(C::K_LOADS + C::V_LOADS <= 8, "vmcnt cases");
-    switch (pending) {
-      case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-      case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
-      case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-      case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-      case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-      case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
-      case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-      default: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
-    }
-  };
-
-  // ---- LDS operand reads ----------------------------------------------------
-  const int k_rd = (l32 * C::KPITCH + g) * 16;  // K row l32, chunk 2c + g at + 32c
-  int v_rd[C::VB];
-  {
-    const int G = lane >> 4, i = lane & 15;
-    const int vrow = 4 * g + (i >> 2);
-    const int y = 2 * (G & 1) + ((i >> 1) & 1);
-#pragma unroll
-    for (int vb = 0; vb < C::VB; ++vb)
-      v_rd[vb] = (vrow * C::CPR_V + ((4 * vb + y) ^ v_swizzle<C::CPR_V>(vrow))) * 16 + 8 * (i & 1);
-  }
-
-  // ---- running state ----------------------------------------------------------
-  f32x16 acc[C::VB][2];
-#pragma unroll
-  for (int vb = 0; vb < C::VB; ++vb)
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[vb][qb][r] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
-  int row_lo[2], row_hi[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const RowBounds rb = row_bounds(wrow0 + 32 * qb + l32, Lq, Lk, p.causal, p.wl, p.wr);
-    row_lo[qb] = (int)imin64(rb.lo, (int64_t)Lk);
-    row_hi[qb] = (int)imax64(rb.hi, (int64_t)-1);
-  }
-
-  // One 32-key tile: the lane holds query block qb's column l32 and keys
-  // key0 + 8 (r / 4) + 4 g + r % 4 in s[qb][r].
-  auto tile = [&](int j, auto masked_tag) VA_INLINE {
-    constexpr bool kMasked = decltype(masked_tag)::value;
-    const lds_char* ks = kbuf(j);
-    const lds_char* vs = vbuf(j);
-    // S^T = K Q^T; each K operand feeds both query blocks.
-    f32x16 s[2];
-    const f32x16 zero = {};
-#pragma unroll
-    for (int c = 0; c < C::KC; ++c) {
-      const bf16x8 kf = lds_read_b128(ks, k_rd + 32 * c);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][c], c == 0 ? zero : s[qb], 0, 0, 0);
-    }
-    // mask (boundary tiles only) and row max
-    float m_new[2];
-    bool need = false;
-    const int key0 = (tr.kt_begin + j) * kBN;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      if constexpr (kMasked) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int jj = key0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          s[qb][r] = (jj >= row_lo[qb] && jj <= row_hi[qb]) ? s[qb][r] : -INFINITY;
-        }
-      }
-      float m = fmaxf(s[qb][0], s[qb][1]);
-#pragma unroll
-      for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(s[qb][r], s[qb][r + 1]));
-      m = fmaxf(m, other_half(m));
-      m_new[qb] = fmaxf(m_run[qb], m * p.scale_log2);
-      need |= m_new[qb] > m_run[qb] + kRescaleTau;
-    }
-    // lazy rescale: move the running max only when some row's max grew by
-    // more than kRescaleTau (log2 units); otherwise p <= 2^kRescaleTau
-    if (__any(need)) {
-      asm volatile("; lazy rescale" ::: "memory");  // keep the rare rescale a branch
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float alpha = (m_new[qb] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new[qb]);
-        m_run[qb] = m_new[qb];
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int vb = 0; vb < C::VB; ++vb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[vb][qb][r] *= alpha;
-      }
-    }
-    // p = exp2(s * scale * log2(e) - m), row sum, bf16 pack (PV B operand)
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-      float sum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 8 * t + 2 * e;
-          const float x0 = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, -m_use));
-          const float x1 = __builtin_amdgcn_exp2f(fmaf(s[qb][r + 1], p.scale_log2, -m_use));
-          sum += x0 + x1;
-          pk[e] = pack_bf16x2(x0, x1);
-        }
-        pf[qb][t] = __builtin_bit_cast(bf16x8, pk);
-      }
-      l_run[qb] += sum;
-    }
-    // O^T += V^T P^T; each V^T operand feeds both query blocks.
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int vb = 0; vb < C::VB; ++vb) {
-        const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
-        const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
-        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][t], acc[vb][qb], 0, 0, 0);
-      }
-  };
-
-  // ---- main loop ------------------------------------------------------------
-  // Tile j sits in stage j % 3.  Step j computes tile j while tiles j + 1
-  // (loaded during step j - 1) and j + 2 (issued now) are in flight; the
-  // stage of tile j + 2 last held tile j - 1, whose readers finished before
-  // the barrier that ended step j - 1.
-  if (ntiles > 0) {
-    load_tile(0);
-    if (ntiles > 1) load_tile(1);
-    wait_loads_but(0);
-    __syncthreads();
-    auto step = [&](int j, auto masked_tag) VA_INLINE {
-      const bool more = j + 2 < ntiles;
-      if (more) load_tile(j + 2);
-      tile(j, masked_tag);
-      // tile j + 1 must have landed; tile j + 2's loads may stay in flight
-      wait_loads_but(more ? nk + nv : 0);
-      __syncthreads();
-    };
-    // masked tiles sit at the two ends of the visited range
-    const int a = min(max(tr.full_begin - tr.kt_begin, 0), ntiles);
-    const int bnd = min(max(tr.full_end - tr.kt_begin, a), ntiles);
-    int j = 0;
-    for (; j < a; ++j) step(j, BoolTag<true>{});
-    for (; j < bnd; ++j) step(j, BoolTag<false>{});
-    for (; j < ntiles; ++j) step(j, BoolTag<true>{});
-  }
-
-  // ---- epilogue ---------------------------------------------------------------
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float l = l_run[qb] + other_half(l_run[qb]);
-    const int row = wrow0 + 32 * qb + l32;
-    if (row < r1) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      uint16_t* dst = p.o + (int64_t)(q0 + row) * p.o_row + (int64_t)h * p.o_head;
-#pragma unroll
-      for (int vb = 0; vb < C::VB; ++vb)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int dv = vb * 32 + 8 * jj + 4 * g;
-          if (dv < DV) {
-            u32x2 o2;
-            o2[0] = pack_bf16x2(acc[vb][qb][4 * jj] * inv, acc[vb][qb][4 * jj + 1] * inv);
-            o2[1] = pack_bf16x2(acc[vb][qb][4 * jj + 2] * inv, acc[vb][qb][4 * jj + 3] * inv);
-            *(u32x2*)(dst + dv) = o2;
-          }
-        }
-      if (p.lse != nullptr && g == 0) {
-        const float lse = l > 0.f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
-        p.lse[(int64_t)h * p.total_q + q0 + row] = lse;
-      }
-    }
-  }
-}
-
-// ============================================================================
-// Wide kernel (head dims <= 80, segments longer than 256 queries): 8 waves x
-// 64 query rows (BM = 512), 32-key tiles, six LDS stages.
+// The kernel: 4 waves x 64 query rows (BM = 256), 32-key tiles, six LDS
+// stages.
 //
 // Each LDS operand read feeds two MFMAs (the wave's two 32-row query
 // blocks), and each wave software-pipelines its own work: iteration j runs
 // the PV product of tile j - 1 and QK^T of tile j + 1 on the matrix cores
-// while the VALU computes the softmax of tile j.  Both waves on a SIMD run
-// the same pipeline, so MFMA and VALU overlap inside a wave and across the
-// two; a VALU-only phase per wave (the ping-pong kernel's) is issue-limited,
-// since a single wave issues VALU at roughly half the rate two waves do.
+// while the VALU computes the softmax of tile j.  Splitting the two among
+// waves instead (one wave's softmax against another's MFMAs, ping-pong
+// style) leaves the softmax to a single wave per SIMD, which issues VALU at
+// roughly half the rate of two.
 //
 // The rescale of the accumulator, when the running max moves, is applied at
 // the end of the iteration, after the PV MFMAs of tile j - 1 and before
@@ -494,14 +188,15 @@ constexpr int kBN = 32;              // keys per tile
 constexpr int kStages = 6;           // tile t lives in stage t % 6 (an even count: see the loop)
 constexpr int kAhead = kStages - 2;  // iteration j issues tile j + 4
 constexpr int kDepth = 3;            // LDS operands read ahead of their MFMA
-// Head dims <= 80 run 8 waves (two per SIMD, within 256 registers each);
-// 128 and 192 run 4 (one per SIMD), whose 64-row accumulators, Q fragments
-// and two score tiles need more than 256 registers.
-template <int DQK>
-constexpr int waves_for() { return DQK >= 128 ? 4 : 8; }
+// Four waves, 256-row blocks.  Head dims <= 80 fit a wave in 256 registers,
+// so two workgroups share a CU (two waves per SIMD); 128 and 192/128 (whose
+// 64-row accumulators, Q fragments and two score tiles need more) run one
+// wave per SIMD.  256-row blocks measured faster than 512-row ones for
+// every head dim: finer blocks balance ragged segment mixes better.
+constexpr int kWaves = 4;
 template <int DQK, int DV>
-struct Cfg : TileGeom<DQK, DV, kBN, waves_for<DQK>()> {
-  static constexpr int WAVES = waves_for<DQK>();
+struct Cfg : TileGeom<DQK, DV, kBN> {
+  static constexpr int WAVES = kWaves;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = kRowsPerWave * WAVES;  // query rows per workgroup
   // Every wave issues NK K and NV V wave-loads per tile (zeros into a dummy
@@ -541,7 +236,7 @@ __device__ __forceinline__ float from_lower_half(float x) {
 // probabilities the MFMA sees, which moves the LSE by up to ln(1 + 2^-9);
 // with an LSE requested the sum stays in fp32.
 template <int DQK, int DV, bool SUM_BY_MFMA>
-__global__ __launch_bounds__(64 * wide::waves_for<DQK>(), 1) void attn_fwd_wide(Params p) {
+__global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) {
   using namespace wide;
   using C = Cfg<DQK, DV>;
   static_assert(!SUM_BY_MFMA || C::V_PAD > 0, "the ones column needs a padded d_v");
@@ -1060,11 +755,8 @@ __global__ __launch_bounds__(64 * wide::waves_for<DQK>(), 1) void attn_fwd_wide(
 // ============================================================================
 namespace va {
 
-// Kernel families.  The wide kernel (64 query rows per wave) runs 8 waves
-// and 512-row blocks for head dims <= 80, 4 waves and 256-row blocks for 128
-// and 192/128.  Head dims <= 80 with no segment longer than 256 queries run
-// the dual kernel instead (256-row blocks, two workgroups per CU), which
-// wastes less on short segments.
+// One kernel, one instantiation per head-dim pair (and, for d_v 72/80, per
+// whether the LSE is returned): 4 waves x 64 query rows, 256-row blocks.
 struct Variant {
   const void* fn;
   int lds_bytes;
@@ -1074,11 +766,6 @@ struct Variant {
   const char* name;
 };
 
-template <int DQK, int DV>
-static Variant dual_variant() {
-  return {(const void*)&attn_fwd_dual<DQK, DV>, dual::Cfg<DQK, DV>::LDS_BYTES, dual::kBM, dual::kBN,
-          dual::kThreads, "attn_fwd_dual"};
-}
 template <int DQK, int DV, bool SUM_BY_MFMA = false>
 static Variant wide_variant() {
   using C = wide::Cfg<DQK, DV>;
@@ -1091,19 +778,14 @@ static bool supported_dims(int dqk, int dv) {
          (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128);
 }
 
-// Segments up to this many queries use 256-row blocks.
-static constexpr int kShortSegment = 256;
-
 // `lse`: whether the caller asked for the LSE (without it, d_v 72 and 80 take
 // the row sum from the PV product; the launch shape is the same either way).
 static Variant variant_for(int dqk, int dv, int max_seqlen_q, bool lse = true) {
   (void)dv;
-  const bool wide = max_seqlen_q > kShortSegment;
-  if (dqk == 64) return wide ? wide_variant<64, 64>() : dual_variant<64, 64>();
-  if (dqk == 72)
-    return !wide ? dual_variant<72, 72>() : lse ? wide_variant<72, 72>() : wide_variant<72, 72, true>();
-  if (dqk == 80)
-    return !wide ? dual_variant<80, 80>() : lse ? wide_variant<80, 80>() : wide_variant<80, 80, true>();
+  (void)max_seqlen_q;
+  if (dqk == 64) return wide_variant<64, 64>();
+  if (dqk == 72) return lse ? wide_variant<72, 72>() : wide_variant<72, 72, true>();
+  if (dqk == 80) return lse ? wide_variant<80, 80>() : wide_variant<80, 80, true>();
   if (dqk == 128) return wide_variant<128, 128>();
   return wide_variant<192, 128>();
 }

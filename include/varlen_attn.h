@@ -133,18 +133,21 @@ int varlen_attn_tile_range(int32_t seqlen_q, int32_t seqlen_k, int32_t row_begin
                            int32_t* full_begin, int32_t* full_end);
 
 /*
- * The kernel's workgroup-to-work mapping, computed on the host by the same
- * function the kernel runs (exported for tests).  For workgroup `block` of
- * the grid varlen_attn_fwd launches for (batch, num_heads, head dims,
- * max_seqlen_q, causal), returns the segment, head and q-tile (block_m query
- * rows, see varlen_attn_plan) it owns, or -1 in all three for a padding
- * workgroup that exits at once.  Returns VA_OK, VA_ERR_HEADDIM, or
- * VA_ERR_ARG for a block outside the grid / bad sizes.
+ * The kernel's workgroup-to-work mapping, computed on the host (exported for
+ * tests).  `seqlens_q` / `seqlens_k` are host arrays of `batch` per-segment
+ * lengths (the differences of cu_seqlens_q / cu_seqlens_k); max_seqlen_q is
+ * taken as their maximum.  For workgroup `block` of the grid varlen_attn_fwd
+ * launches for these sizes, returns the segment, head and q-tile (block_m
+ * query rows, see varlen_attn_plan) it owns, or -1 in all three for a
+ * workgroup that exits at once.  Segments of different lengths (at most 64
+ * of them) are dealt longest key length first; otherwise in packing order.
+ * Returns VA_OK, VA_ERR_NULL, VA_ERR_HEADDIM, or VA_ERR_ARG for a block
+ * outside the grid, a negative length or all-empty queries.
  * Host only; makes no HIP call.
  */
 int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_heads, int32_t head_dim_qk,
-                          int32_t head_dim_v, int32_t max_seqlen_q, int32_t causal,
-                          int32_t* segment, int32_t* head, int32_t* q_tile);
+                          int32_t head_dim_v, const int32_t* seqlens_q, const int32_t* seqlens_k,
+                          int32_t causal, int32_t* segment, int32_t* head, int32_t* q_tile);
 
 /* Launch shape varlen_attn_fwd would use (host only; makes no HIP call). */
 typedef struct va_plan {

@@ -13,9 +13,11 @@
 """
 import ctypes
 import os
+import random
 import re
 
 import numpy as np
+
 import pytest
 
 import varlen_attention_forward_amd as pkg
@@ -262,42 +264,77 @@ def test_tile_range_rejects_bad_arguments():
 # ---------------------------------------------------------------------------
 # workgroup -> (segment, head, q-tile) mapping
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("batch,heads,max_q,causal,dims", [
-    (8, 16, 4096, 0, (80, 80)), (36, 16, 256, 0, (80, 80)), (1, 16, 65536, 0, (128, 128)),
-    (4, 128, 4096, 1, (192, 128)), (3, 5, 700, 1, (64, 64)), (1, 1, 1, 0, (72, 72)), (3, 5, 700, 0, (128, 128)),
+def _ragged(seed, batch, lo, hi):
+    rng = random.Random(seed)
+    return [rng.randint(lo, hi) for _ in range(batch)]
+
+
+@pytest.mark.parametrize("lq,lk,heads,causal,dims", [
+    ([4096] * 8, [4096] * 8, 16, 0, (80, 80)),            # alike: packing order
+    ([256] * 36, [256] * 36, 16, 0, (80, 80)),
+    ([65536], [65536], 16, 0, (128, 128)),
+    ([1, 1], [1, 1], 1, 0, (72, 72)),
+    ([576, 1024, 2304, 4096, 1024, 576, 4096, 2304], None, 16, 0, (80, 80)),  # ragged: longest first
+    ([700, 0, 300, 1], [700, 5, 0, 1], 5, 1, (64, 64)),
+    ([3000, 100, 2000, 4096], None, 128, 1, (192, 128)),
+    (_ragged(1, 64, 0, 900), None, 3, 0, (128, 128)),     # 64 segments: still longest first
+    (_ragged(2, 65, 1, 900), None, 3, 1, (64, 64)),       # 65 segments: packing order
+    ([500, 500, 500], [500, 900, 500], 7, 1, (80, 80)),   # ties broken by packing order
 ])
-def test_work_unit_covers_every_tile_once(batch, heads, max_q, causal, dims):
-    p = pkg.plan(dims[0], dims[1], batch, heads, max_q, max_q, causal)
-    n_qt = -(-max_q // p["block_m"])
+def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
+    lk = lq if lk is None else lk
+    batch, max_q = len(lq), max(lq)
+    p = pkg.plan(dims[0], dims[1], batch, heads, max_q, max(lk), causal)
+    bm = p["block_m"]
+    n_qt = -(-max_q // bm)
+    longest_first = batch <= 64 and len(set(zip(lq, lk))) > 1
+    # tiles each segment must get: its own q-tiles when dealt longest first,
+    # else the same number for every segment (tiles past its end exit early)
+    want = {(b, h, qt) for b in range(batch) for h in range(heads)
+            for qt in range(-(-lq[b] // bm) if longest_first else n_qt)}
+    rank = sorted(range(batch), key=lambda i: (-lk[i], i))
+    rank = {b: r for r, b in enumerate(rank)}
     seen = {}
-    pad = 0
+    order = [[] for _ in range(8)]  # per XCD, owners in dispatch order
     for blk in range(p["grid"]):
-        b, h, qt = pkg.work_unit(blk, batch, heads, dims[0], dims[1], max_q, causal)
+        b, h, qt = pkg.work_unit(blk, heads, dims[0], dims[1], lq, lk, causal)
         if b < 0:
-            pad += 1
+            assert h == -1 and qt == -1
             continue
-        assert 0 <= b < batch and 0 <= h < heads and 0 <= qt < n_qt
         key = (b, h, qt)
+        assert key in want, key
         assert key not in seen, (blk, key, seen.get(key))
         seen[key] = blk
+        order[blk % 8].append(b)
         # groups are dealt round-robin over the 8 XCDs (block % 8)
-        assert (b * heads + h) % 8 == blk % 8
-    assert len(seen) == batch * heads * n_qt
-    assert pad == p["grid"] - batch * heads * n_qt and pad < 8 * n_qt
+        g = (rank[b] if longest_first else b) * heads + h
+        assert g % 8 == blk % 8
+    assert set(seen) == want
+    if longest_first:
+        # each XCD starts the segments in order of decreasing key length
+        for owners in order:
+            assert all(lk[a] >= lk[c] for a, c in zip(owners, owners[1:]))
+    else:
+        assert p["grid"] - len(want) < 8 * n_qt
     if causal:
         # within a group, the q-tile with the most keys is dispatched first
         first = {}
         for (b, h, qt), blk in seen.items():
             if (b, h) not in first or blk < first[(b, h)][0]:
                 first[(b, h)] = (blk, qt)
-        assert all(qt == n_qt - 1 for _, qt in first.values())
+        for (b, h), (_, qt) in first.items():
+            assert qt == (-(-lq[b] // bm) if longest_first else n_qt) - 1
 
 
 def test_work_unit_rejects_out_of_grid():
     p = pkg.plan(64, 64, 2, 3, 100, 100)
     with pytest.raises(ValueError):
-        pkg.work_unit(p["grid"], 2, 3, 64, 64, 100)
+        pkg.work_unit(p["grid"], 3, 64, 64, [100, 100], [100, 100])
     with pytest.raises(ValueError):
-        pkg.work_unit(-1, 2, 3, 64, 64, 100)
+        pkg.work_unit(-1, 3, 64, 64, [100, 100], [100, 100])
     with pytest.raises(ValueError):
-        pkg.work_unit(0, 2, 3, 96, 96, 100)
+        pkg.work_unit(0, 3, 96, 96, [100, 100], [100, 100])
+    with pytest.raises(ValueError):
+        pkg.work_unit(0, 3, 64, 64, [100, -1], [100, 100])
+    with pytest.raises(ValueError):
+        pkg.work_unit(0, 3, 64, 64, [0, 0], [100, 100])

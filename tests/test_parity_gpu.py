@@ -128,6 +128,23 @@ def test_multi_block_segments(dims, mode):
     assert_parity(out, lse, ref_o, ref_lse, what="multi/%s/%s" % (dims, mode))
 
 
+@pytest.mark.parametrize("batch", [2, 64, 90])
+@pytest.mark.parametrize("dims,causal", [((64, 64), False), ((128, 128), True), ((80, 80), False)],
+                         ids=lambda x: str(x))
+def test_many_ragged_segments(batch, dims, causal):
+    """Ragged batches dealt longest first (up to 64 segments, including empty
+    ones and equal lengths) and in packing order (more than 64)."""
+    d_qk, d_v = dims
+    rng = np.random.default_rng(batch * 7 + d_qk)
+    lq = [int(x) for x in rng.integers(0, 400, batch)]
+    lq[0], lq[-1] = 300, 300
+    lk = [x if i % 5 else int(rng.integers(0, 600)) for i, x in enumerate(lq)]
+    inp = workloads.make_inputs(lq, lk, 2, d_qk, d_v, seed=batch, causal=causal)
+    out, lse = run_gpu(inp)
+    ref_o, ref_lse = oracle_on(inp)
+    assert_parity(out, lse, ref_o, ref_lse, what="many/%d/%s/%s" % (batch, dims, causal))
+
+
 @pytest.mark.parametrize("dims,lens,causal", [
     ((128, 128), [300, 77], False),
     ((64, 64), [700, 77, 1100], False),   # several 256-row blocks

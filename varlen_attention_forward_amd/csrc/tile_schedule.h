@@ -123,4 +123,63 @@ VA_HD WorkUnit decode_block(int64_t w, int64_t batch, int64_t heads, int64_t n_q
   return u;
 }
 
+// Longest-first dealing.  On a batch of segments of different lengths,
+// dealing in packing order can leave a long segment's workgroups for last,
+// running alone at the end.  When the batch has at most kLptMaxBatch segments
+// and they are not all alike, the segments are instead ranked by key length,
+// longest first (ties in packing order), groups are dealt round-robin over
+// the XCDs in that order (group r * heads + h -> XCD (r * heads + h) % 8 for
+// the segment of rank r), and each group contributes only its real q-tiles
+// (ceil(Lq / block_m)), adjacent in its XCD's dispatch order.  The kernel
+// computes this from cu_seqlens (one lane per segment); decode_block_lpt is
+// the host reference.
+constexpr int kLptMaxBatch = 64;
+
+// The heads of the segment of rank r dealt to XCD x are h0, h0 + 8, ...
+VA_HD int32_t xcd_first_head(int32_t r, int32_t heads, int32_t x) {
+  return (x - (int32_t)(((int64_t)r * heads) % 8) + 8) % 8;
+}
+VA_HD int32_t xcd_head_count(int32_t h0, int32_t heads) { return h0 < heads ? (heads - 1 - h0) / 8 + 1 : 0; }
+
+// Whether longest-first dealing applies to segments with these lengths.
+inline bool lpt_applies(int32_t batch, const int32_t* lq, const int32_t* lk) {
+  if (batch > kLptMaxBatch) return false;
+  for (int32_t i = 1; i < batch; ++i)
+    if (lq[i] != lq[0] || lk[i] != lk[0]) return true;
+  return false;
+}
+
+// Host reference of the kernel's longest-first mapping (quadratic in batch).
+inline WorkUnit decode_block_lpt(int64_t w, int32_t batch, int32_t heads, int32_t block_m, int causal,
+                                 const int32_t* lq, const int32_t* lk) {
+  const int32_t x = (int32_t)(w & 7);
+  const int64_t k = w >> 3;
+  int64_t pre = 0;
+  for (int32_t r = 0; r < batch; ++r) {
+    int32_t i = 0;  // the segment of rank r
+    for (; i < batch; ++i) {
+      int32_t rank = 0;
+      for (int32_t j = 0; j < batch; ++j) rank += (lk[j] > lk[i] || (lk[j] == lk[i] && j < i)) ? 1 : 0;
+      if (rank == r) break;
+    }
+    const int32_t nqt = (lq[i] + block_m - 1) / block_m;
+    const int32_t h0 = xcd_first_head(r, heads, x);
+    const int64_t n = (int64_t)xcd_head_count(h0, heads) * nqt;
+    if (k < pre + n) {
+      const int64_t local = k - pre, qi = local % nqt;
+      WorkUnit u;
+      u.valid = 1;
+      u.b = i;
+      u.h = (int32_t)(h0 + 8 * (local / nqt));
+      u.qt = (int32_t)(causal ? nqt - 1 - qi : qi);
+      return u;
+    }
+    pre += n;
+  }
+  WorkUnit u;
+  u.valid = 0;
+  u.b = u.h = u.qt = -1;
+  return u;
+}
+
 }  // namespace va

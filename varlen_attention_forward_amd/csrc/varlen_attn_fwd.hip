@@ -152,6 +152,51 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// This workgroup's work unit (tile_schedule.h): longest-first dealing when
+// it applies, computed by every wave from cu_seqlens with one lane per
+// segment; else dealing in packing order.
+__device__ __forceinline__ WorkUnit decode_block_device(const Params& p, int lane, int block_m) {
+  const int64_t w = blockIdx.x;
+  if (p.batch <= kLptMaxBatch) {
+    int lq = 0, lk = -1;
+    if (lane < p.batch) {
+      lq = p.cu_q[lane + 1] - p.cu_q[lane];
+      lk = p.cu_k[lane + 1] - p.cu_k[lane];
+    }
+    const int lq0 = __builtin_amdgcn_readfirstlane(lq), lk0 = __builtin_amdgcn_readfirstlane(lk);
+    if (__ballot(lane < p.batch && (lq != lq0 || lk != lk0)) != 0) {
+      const int x = (int)(w & 7);
+      const int k = (int)(w >> 3);
+      int rank = 0;
+      for (int j = 0; j < p.batch; ++j) {
+        const int kj = __builtin_amdgcn_readlane(lk, j);
+        rank += (kj > lk || (kj == lk && j < lane)) ? 1 : 0;
+      }
+      const int nqt = lane < p.batch ? (lq + block_m - 1) / block_m : 0;
+      const int h0 = xcd_first_head(rank, p.heads, x);
+      const int n = xcd_head_count(h0, p.heads) * nqt;
+      int pre = 0;  // blocks of this XCD before this segment's
+      for (int j = 0; j < p.batch; ++j)
+        pre += __builtin_amdgcn_readlane(rank, j) < rank ? __builtin_amdgcn_readlane(n, j) : 0;
+      const uint64_t hit = __ballot(lane < p.batch && k >= pre && k < pre + n);
+      WorkUnit u;
+      u.valid = hit != 0;
+      u.b = u.h = u.qt = -1;
+      if (hit != 0) {
+        const int i = (int)__builtin_ctzll(hit);
+        const int local = k - __builtin_amdgcn_readlane(pre, i);
+        const int nq = __builtin_amdgcn_readlane(nqt, i);
+        const int qi = local % nq;
+        u.b = i;
+        u.h = __builtin_amdgcn_readlane(h0, i) + 8 * (local / nq);
+        u.qt = p.causal ? nq - 1 - qi : qi;
+      }
+      return u;
+    }
+  }
+  return decode_block(w, p.batch, p.heads, p.n_qt, p.causal);
+}
+
 __device__ __forceinline__ bf16x8 lds_read_b128(const lds_char* base, int byte_off) {
   return *(const __attribute__((address_space(3))) bf16x8*)(base + byte_off);
 }
@@ -278,7 +323,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  const WorkUnit wu = decode_block(blockIdx.x, p.batch, p.heads, p.n_qt, p.causal);
+  const WorkUnit wu = decode_block_device(p, lane, C::BM);
   if (!wu.valid) return;
   const int b = wu.b, h = wu.h, qt = wu.qt;
   const int q0 = p.cu_q[b];
@@ -838,16 +883,25 @@ extern "C" int varlen_attn_tile_range(int32_t seqlen_q, int32_t seqlen_k, int32_
 }
 
 extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_heads,
-                                     int32_t head_dim_qk, int32_t head_dim_v, int32_t max_seqlen_q,
-                                     int32_t causal, int32_t* segment, int32_t* head,
-                                     int32_t* q_tile) {
+                                     int32_t head_dim_qk, int32_t head_dim_v, const int32_t* seqlens_q,
+                                     const int32_t* seqlens_k, int32_t causal, int32_t* segment,
+                                     int32_t* head, int32_t* q_tile) {
   if (!segment || !head || !q_tile) return VA_ERR_NULL;
   if (!va::supported_dims(head_dim_qk, head_dim_v)) return VA_ERR_HEADDIM;
-  if (batch < 0 || num_heads <= 0 || max_seqlen_q <= 0 || (causal != 0 && causal != 1)) return VA_ERR_ARG;
-  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, max_seqlen_q);
-  const int64_t n_qt = ((int64_t)max_seqlen_q + var.block_m - 1) / var.block_m;
+  if (batch <= 0 || num_heads <= 0 || (causal != 0 && causal != 1)) return VA_ERR_ARG;
+  if (!seqlens_q || !seqlens_k) return VA_ERR_NULL;
+  int32_t max_q = 0;
+  for (int32_t i = 0; i < batch; ++i) {
+    if (seqlens_q[i] < 0 || seqlens_k[i] < 0) return VA_ERR_ARG;
+    max_q = seqlens_q[i] > max_q ? seqlens_q[i] : max_q;
+  }
+  if (max_q <= 0) return VA_ERR_ARG;
+  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, max_q);
+  const int64_t n_qt = ((int64_t)max_q + var.block_m - 1) / var.block_m;
   if (block < 0 || block >= va::grid_blocks(batch, num_heads, n_qt)) return VA_ERR_ARG;
-  const va::WorkUnit u = va::decode_block(block, batch, num_heads, n_qt, causal);
+  const va::WorkUnit u = va::lpt_applies(batch, seqlens_q, seqlens_k)
+                             ? va::decode_block_lpt(block, batch, num_heads, var.block_m, causal, seqlens_q, seqlens_k)
+                             : va::decode_block(block, batch, num_heads, n_qt, causal);
   *segment = u.valid ? u.b : -1;
   *head = u.valid ? u.h : -1;
   *q_tile = u.valid ? u.qt : -1;

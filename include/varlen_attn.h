@@ -140,7 +140,8 @@ int varlen_attn_tile_range(int32_t seqlen_q, int32_t seqlen_k, int32_t row_begin
  * launches for these sizes, returns the segment, head and q-tile (block_m
  * query rows, see varlen_attn_plan) it owns, or -1 in all three for a
  * workgroup that exits at once.  Segments of different lengths (at most 64
- * of them) are dealt longest key length first; otherwise in packing order.
+ * of them) are dealt longest key length first; otherwise in packing order;
+ * either way every odd quad of each XCD's dispatch order is reversed.
  * Returns VA_OK, VA_ERR_NULL, VA_ERR_HEADDIM, or VA_ERR_ARG for a block
  * outside the grid, a negative length or all-empty queries.
  * Host only; makes no HIP call.

@@ -305,25 +305,53 @@ def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
         assert key in want, key
         assert key not in seen, (blk, key, seen.get(key))
         seen[key] = blk
-        order[blk % 8].append(b)
+        order[blk % 8].append((blk >> 3, b))
         # groups are dealt round-robin over the 8 XCDs (block % 8)
         g = (rank[b] if longest_first else b) * heads + h
         assert g % 8 == blk % 8
     assert set(seen) == want
     if longest_first:
-        # each XCD starts the segments in order of decreasing key length
+        # each XCD starts the segments in order of decreasing key length, up
+        # to the order inside aligned quads of its dispatch index
         for owners in order:
-            assert all(lk[a] >= lk[c] for a, c in zip(owners, owners[1:]))
+            quads = {}
+            for k, b in owners:
+                quads.setdefault(k // 4, []).append(lk[b])
+            ks = sorted(quads)
+            assert all(min(quads[a]) >= max(quads[c]) for a, c in zip(ks, ks[1:]))
     else:
         assert p["grid"] - len(want) < 8 * n_qt
     if causal:
-        # within a group, the q-tile with the most keys is dispatched first
+        # within a group, one of the four q-tiles with the most keys is
+        # dispatched first
         first = {}
         for (b, h, qt), blk in seen.items():
             if (b, h) not in first or blk < first[(b, h)][0]:
                 first[(b, h)] = (blk, qt)
         for (b, h), (_, qt) in first.items():
-            assert qt == (-(-lq[b] // bm) if longest_first else n_qt) - 1
+            assert qt >= (-(-lq[b] // bm) if longest_first else n_qt) - 4
+
+
+@pytest.mark.parametrize("batch,heads,max_q,causal", [(4, 128, 4096, 1), (1, 16, 65536, 0), (3, 5, 700, 1)])
+def test_work_unit_snake_balances_engines(batch, heads, max_q, causal):
+    """The k-th workgroup of an XCD goes to shader engine (k + c) % 4; over
+    every aligned run of 8 dispatch slots the four engines get equal key
+    counts (each q-tile's keys, causal: (qt + 1) x 256)."""
+    p = pkg.plan(192, 128, batch, heads, max_q, max_q, causal)
+    cost = {}
+    for blk in range(p["grid"]):
+        b, h, qt = pkg.work_unit(blk, heads, 192, 128, [max_q] * batch, [max_q] * batch, causal)
+        if b >= 0:
+            cost[blk] = (qt + 1) if causal else 1
+    n_qt = -(-max_q // p["block_m"])
+    per_xcd = p["grid"] // 8
+    for x in range(8):
+        for k0 in range(0, per_xcd - per_xcd % 8, 8):
+            eng = [0] * 4
+            for k in range(k0, k0 + 8):
+                eng[k % 4] += cost.get(8 * k + x, 0)
+            if n_qt % 4 == 0 and all(8 * k + x in cost for k in range(k0, k0 + 8)):
+                assert len(set(eng)) == 1, (x, k0, eng)
 
 
 def test_work_unit_rejects_out_of_grid():

@@ -152,21 +152,31 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// This workgroup's work unit (tile_schedule.h): longest-first dealing when
-// it applies, computed by every wave from cu_seqlens with one lane per
-// segment; else dealing in packing order.
-__device__ __forceinline__ WorkUnit decode_block_device(const Params& p, int lane, int block_m) {
+// This workgroup's work unit (tile_schedule.h) and its segment's bounds:
+// longest-first dealing when it applies, computed by every wave from
+// cu_seqlens with one lane per segment (whose loads then also give the
+// bounds); else dealing in packing order.
+struct BlockWork {
+  WorkUnit u;
+  int q0, lq, k0, lk;  // the segment's first query / key row and lengths
+};
+
+__device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int block_m) {
   const int64_t w = blockIdx.x;
+  BlockWork r;
   if (p.batch <= kLptMaxBatch) {
-    int lq = 0, lk = -1;
+    int cq0 = 0, cq1 = 0, ck0 = 0, ck1 = -1;
     if (lane < p.batch) {
-      lq = p.cu_q[lane + 1] - p.cu_q[lane];
-      lk = p.cu_k[lane + 1] - p.cu_k[lane];
+      cq0 = p.cu_q[lane];
+      cq1 = p.cu_q[lane + 1];
+      ck0 = p.cu_k[lane];
+      ck1 = p.cu_k[lane + 1];
     }
+    const int lq = cq1 - cq0, lk = ck1 - ck0;  // lk = -1 on lanes past the batch
     const int lq0 = __builtin_amdgcn_readfirstlane(lq), lk0 = __builtin_amdgcn_readfirstlane(lk);
     if (__ballot(lane < p.batch && (lq != lq0 || lk != lk0)) != 0) {
       const int x = (int)(w & 7);
-      const int k = (int)(w >> 3);
+      const int k = (int)snake_quads(w >> 3, gridDim.x / 8);
       int rank = 0;
       for (int j = 0; j < p.batch; ++j) {
         const int kj = __builtin_amdgcn_readlane(lk, j);
@@ -179,22 +189,38 @@ __device__ __forceinline__ WorkUnit decode_block_device(const Params& p, int lan
       for (int j = 0; j < p.batch; ++j)
         pre += __builtin_amdgcn_readlane(rank, j) < rank ? __builtin_amdgcn_readlane(n, j) : 0;
       const uint64_t hit = __ballot(lane < p.batch && k >= pre && k < pre + n);
-      WorkUnit u;
-      u.valid = hit != 0;
-      u.b = u.h = u.qt = -1;
+      r.u.valid = hit != 0;
+      r.u.b = r.u.h = r.u.qt = -1;
       if (hit != 0) {
         const int i = (int)__builtin_ctzll(hit);
         const int local = k - __builtin_amdgcn_readlane(pre, i);
         const int nq = __builtin_amdgcn_readlane(nqt, i);
         const int qi = local % nq;
-        u.b = i;
-        u.h = __builtin_amdgcn_readlane(h0, i) + 8 * (local / nq);
-        u.qt = p.causal ? nq - 1 - qi : qi;
+        r.u.b = i;
+        r.u.h = __builtin_amdgcn_readlane(h0, i) + 8 * (local / nq);
+        r.u.qt = p.causal ? nq - 1 - qi : qi;
       }
-      return u;
+    } else {
+      r.u = decode_block(w, p.batch, p.heads, p.n_qt, p.causal);
     }
+    if (r.u.valid) {
+      const int b = __builtin_amdgcn_readfirstlane(r.u.b);
+      r.q0 = __builtin_amdgcn_readlane(cq0, b);
+      r.lq = __builtin_amdgcn_readlane(lq, b);
+      r.k0 = __builtin_amdgcn_readlane(ck0, b);
+      r.lk = __builtin_amdgcn_readlane(lk, b);
+    }
+    return r;
   }
-  return decode_block(w, p.batch, p.heads, p.n_qt, p.causal);
+  r.u = decode_block(w, p.batch, p.heads, p.n_qt, p.causal);
+  if (r.u.valid) {
+    const int b = __builtin_amdgcn_readfirstlane(r.u.b);
+    r.q0 = p.cu_q[b];
+    r.lq = p.cu_q[b + 1] - r.q0;
+    r.k0 = p.cu_k[b];
+    r.lk = p.cu_k[b + 1] - r.k0;
+  }
+  return r;
 }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const lds_char* base, int byte_off) {
@@ -323,13 +349,10 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  const WorkUnit wu = decode_block_device(p, lane, C::BM);
-  if (!wu.valid) return;
-  const int b = wu.b, h = wu.h, qt = wu.qt;
-  const int q0 = p.cu_q[b];
-  const int Lq = p.cu_q[b + 1] - q0;
-  const int k0 = p.cu_k[b];
-  const int Lk = p.cu_k[b + 1] - k0;
+  const BlockWork bw = block_work(p, lane, C::BM);
+  if (!bw.u.valid) return;
+  const int h = bw.u.h, qt = bw.u.qt;
+  const int q0 = bw.q0, Lq = bw.lq, k0 = bw.k0, Lk = bw.lk;
   const int r0 = qt * C::BM;
   if (r0 >= Lq) return;
   const int r1 = min(r0 + C::BM, Lq);
@@ -742,23 +765,23 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
     // The zero loads past the last tile must land before the workgroup's LDS
     // can be handed to the next workgroup.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (active) {  // PV of the last tile
+    if (active) {  // PV of the last tile, its stage picked at run time (all DMA has landed)
       const int last = (ntiles - 1) % kStages;
-      static_for<0, kStages>([&](auto st) VA_INLINE {
-        if (last == decltype(st)::value) {
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int vb = 0; vb < C::VB; ++vb) {
-              const bf16x4 lo = lds_read_tr(vst(st), v_rd[vb] + (16 * t) * C::CPR_V * 16);
-              const bf16x4 hi = lds_read_tr(vst(st), v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
-              const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-              for (int qb = 0; qb < 2; ++qb)
-                acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][t], acc[vb][qb], 0, 0, 0);
-            }
-        }
+      const lds_char* vs = vst(Int<0>{});
+      static_for<1, kStages>([&](auto st) VA_INLINE {
+        if (last == decltype(st)::value) vs = vst(st);
       });
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int vb = 0; vb < C::VB; ++vb) {
+          const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
+          const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
+          const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][t], acc[vb][qb], 0, 0, 0);
+        }
     }
   }
 
@@ -900,7 +923,8 @@ extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_h
   const int64_t n_qt = ((int64_t)max_q + var.block_m - 1) / var.block_m;
   if (block < 0 || block >= va::grid_blocks(batch, num_heads, n_qt)) return VA_ERR_ARG;
   const va::WorkUnit u = va::lpt_applies(batch, seqlens_q, seqlens_k)
-                             ? va::decode_block_lpt(block, batch, num_heads, var.block_m, causal, seqlens_q, seqlens_k)
+                             ? va::decode_block_lpt(block, batch, num_heads, var.block_m, (int32_t)n_qt, causal,
+                                                    seqlens_q, seqlens_k)
                              : va::decode_block(block, batch, num_heads, n_qt, causal);
   *segment = u.valid ? u.b : -1;
   *head = u.valid ? u.h : -1;

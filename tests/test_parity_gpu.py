@@ -333,34 +333,24 @@ def test_rows_outside_segments_untouched():
     assert_parity(out, lse, ref_o, ref_lse, rows=np.arange(150), what="partial cover")
 
 
-@pytest.mark.parametrize("dims,lens", [
-    ((64, 64), [300, 700]),
-    ((128, 128), [300, 700]),
-    ((192, 128), [200, 256]),
-])
-def test_no_lse_matches_with_lse(dims, lens):
-    """Where both calls run the same arithmetic (every head dim but 72/80,
-    whose no-LSE call sums the bf16 probabilities), O is bit-identical."""
-    inp = workloads.make_inputs(lens, lens, 2, dims[0], dims[1], seed=13)
-    o1, _ = run_gpu(inp, return_lse=False)
-    o2, _ = run_gpu(inp)
-    assert torch.equal(o1, o2)
-
-
-@pytest.mark.parametrize("dims", [(72, 72), (80, 80)], ids=lambda d: "d%d_%d" % d)
+@pytest.mark.parametrize("dims", DIMS, ids=lambda d: "d%d_%d" % d)
 @pytest.mark.parametrize("mode", ["full", "causal", "window"])
-def test_no_lse_row_sum_by_mfma(dims, mode):
-    """Without an LSE, d_v 72 and 80 take the row sum from a ones column in
-    the padded V tile (a sum of the bf16 probabilities): O must still match
-    the oracle, on multi-block segments with ragged tails and empty rows."""
+def test_no_lse_row_sum_over_bf16(dims, mode):
+    """Without an LSE the row sum is taken over the bf16 probabilities (a
+    ones column in the padded V tile for d_v 72/80, bf16 dot products for
+    d_v 64/128): O must still match the oracle, on multi-block segments with
+    ragged tails and rows that see no key, and stay within the tolerance of
+    the LSE call's O."""
     causal, window = MODES[mode]
-    lq = [1029, 700, 40, 513]
-    lk = [1029, 901, 0, 513]
+    lq = [1029, 700, 40, 513] if dims[0] < 192 else [600, 40, 257]
+    lk = [1029, 901, 0, 513] if dims[0] < 192 else [700, 0, 257]
     seed = zlib.crc32(repr(("nolse", dims, mode)).encode()) % 1000
     inp = workloads.make_inputs(lq, lk, 2, dims[0], dims[1], seed=seed, causal=causal, window=window)
     out, _ = run_gpu(inp, return_lse=False)
     ref_o, _ = oracle_on(inp)
     assert_parity(out, None, ref_o, None, what="nolse/%s/%s" % (dims, mode))
+    with_lse, _ = run_gpu(inp)
+    assert float((out.float() - with_lse.float()).abs().max()) <= TOL_O
 
 
 def test_empty_batch_and_zero_keys():

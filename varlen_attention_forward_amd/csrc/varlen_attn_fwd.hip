@@ -130,6 +130,13 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// acc + the two bf16 halves of x, in one dot-product op.
+__device__ __forceinline__ float bf16_pair_sum(uint32_t x, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), ones, acc, false);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 v;
@@ -301,29 +308,40 @@ __device__ __forceinline__ float from_lower_half(float x) {
   return __uint_as_float(r[0]);
 }
 
-// SUM_BY_MFMA (d_v 72 and 80, no LSE requested): column d_v of the padded V
-// tile holds ones, so the PV product accumulates each row's probability sum
-// alongside O and the softmax does no adds.  The sum is then over the bf16
-// probabilities the MFMA sees, which moves the LSE by up to ln(1 + 2^-9);
-// with an LSE requested the sum stays in fp32.
-template <int DQK, int DV, bool SUM_BY_MFMA>
+// How the row sum of the probabilities is formed.  With an LSE requested it
+// is an fp32 sum of the fp32 probabilities (kF32).  Without one, O only needs
+// the sum to normalise what the PV product accumulated, so it is taken over
+// the bf16 probabilities the MFMA sees: for d_v 72 and 80 by a column of ones
+// in the padded V tile, which makes the PV product accumulate it alongside O
+// with no VALU work (kMfma); for d_v 64 and 128 by bf16 dot products of the
+// packed probabilities with (1, 1), one op per pair instead of two adds
+// (kDot).  A bf16 sum can move the LSE by up to ln(1 + 2^-9), which is why an
+// LSE keeps the fp32 sum.
+enum class RowSum { kF32, kMfma, kDot };
+
+template <int DQK, int DV, RowSum SUM>
 __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) {
   using namespace wide;
   using C = Cfg<DQK, DV>;
+  constexpr bool SUM_BY_MFMA = SUM == RowSum::kMfma;
   static_assert(!SUM_BY_MFMA || C::V_PAD > 0, "the ones column needs a padded d_v");
   static_assert(kStages == 6, "stage objects below");
+  // The V stages are aligned more strictly than the K stages so the LDS
+  // allocator places them first, below 64 KB: there a transposing read folds
+  // its stage's address into the instruction's 16-bit offset instead of
+  // building it with a VALU op.
   __shared__ __attribute__((aligned(1024))) char ks0[C::K_TILE];
   __shared__ __attribute__((aligned(1024))) char ks1[C::K_TILE];
   __shared__ __attribute__((aligned(1024))) char ks2[C::K_TILE];
   __shared__ __attribute__((aligned(1024))) char ks3[C::K_TILE];
   __shared__ __attribute__((aligned(1024))) char ks4[C::K_TILE];
   __shared__ __attribute__((aligned(1024))) char ks5[C::K_TILE];
-  __shared__ __attribute__((aligned(1024))) char vs0[C::V_TILE];
-  __shared__ __attribute__((aligned(1024))) char vs1[C::V_TILE];
-  __shared__ __attribute__((aligned(1024))) char vs2[C::V_TILE];
-  __shared__ __attribute__((aligned(1024))) char vs3[C::V_TILE];
-  __shared__ __attribute__((aligned(1024))) char vs4[C::V_TILE];
-  __shared__ __attribute__((aligned(1024))) char vs5[C::V_TILE];
+  __shared__ __attribute__((aligned(4096))) char vs0[C::V_TILE];
+  __shared__ __attribute__((aligned(4096))) char vs1[C::V_TILE];
+  __shared__ __attribute__((aligned(4096))) char vs2[C::V_TILE];
+  __shared__ __attribute__((aligned(4096))) char vs3[C::V_TILE];
+  __shared__ __attribute__((aligned(4096))) char vs4[C::V_TILE];
+  __shared__ __attribute__((aligned(4096))) char vs5[C::V_TILE];
   auto kst = [&](auto st) VA_INLINE -> lds_char* {
     constexpr int i = decltype(st)::value % kStages;
     if constexpr (i == 0) return (lds_char*)ks0;
@@ -581,8 +599,9 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
           const int r = 8 * t + 2 * e;
           const float x0 = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, nm[qb]));
           const float x1 = __builtin_amdgcn_exp2f(fmaf(s[qb][r + 1], p.scale_log2, nm[qb]));
-          if constexpr (!SUM_BY_MFMA) sum += x0 + x1;
           pk[e] = pack_bf16x2(x0, x1);
+          if constexpr (SUM == RowSum::kF32) sum += x0 + x1;
+          if constexpr (SUM == RowSum::kDot) sum = bf16_pair_sum(pk[e], sum);
         }
         pf[qb][t] = __builtin_bit_cast(bf16x8, pk);
       }
@@ -632,8 +651,9 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
         s[qb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, nm[qb]));
       } else {  // bf16 pack (and fp32 row sum)
         constexpr int i = u - 48, qb = i / 8, t = (i / 4) % 2, e = i % 4, r = 8 * t + 2 * e;
-        if constexpr (!SUM_BY_MFMA) sum[qb] += s[qb][r] + s[qb][r + 1];
         pk[qb][t][e] = pack_bf16x2(s[qb][r], s[qb][r + 1]);
+        if constexpr (SUM == RowSum::kF32) sum[qb] += s[qb][r] + s[qb][r + 1];
+        if constexpr (SUM == RowSum::kDot) sum[qb] = bf16_pair_sum(pk[qb][t][e], sum[qb]);
         if constexpr (e == 3) pf[qb][t] = __builtin_bit_cast(bf16x8, pk[qb][t]);
       }
     };
@@ -834,10 +854,10 @@ struct Variant {
   const char* name;
 };
 
-template <int DQK, int DV, bool SUM_BY_MFMA = false>
+template <int DQK, int DV, RowSum SUM>
 static Variant wide_variant() {
   using C = wide::Cfg<DQK, DV>;
-  return {(const void*)&attn_fwd_wide<DQK, DV, SUM_BY_MFMA>, C::LDS_BYTES, C::BM, wide::kBN, C::THREADS,
+  return {(const void*)&attn_fwd_wide<DQK, DV, SUM>, C::LDS_BYTES, C::BM, wide::kBN, C::THREADS,
           "attn_fwd_wide"};
 }
 
@@ -846,16 +866,18 @@ static bool supported_dims(int dqk, int dv) {
          (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128);
 }
 
-// `lse`: whether the caller asked for the LSE (without it, d_v 72 and 80 take
-// the row sum from the PV product; the launch shape is the same either way).
+// `lse`: whether the caller asked for the LSE (without one the row sum is
+// taken over the bf16 probabilities, see RowSum; the launch shape is the same
+// either way).
 static Variant variant_for(int dqk, int dv, int max_seqlen_q, bool lse = true) {
   (void)dv;
   (void)max_seqlen_q;
-  if (dqk == 64) return wide_variant<64, 64>();
-  if (dqk == 72) return lse ? wide_variant<72, 72>() : wide_variant<72, 72, true>();
-  if (dqk == 80) return lse ? wide_variant<80, 80>() : wide_variant<80, 80, true>();
-  if (dqk == 128) return wide_variant<128, 128>();
-  return wide_variant<192, 128>();
+  constexpr RowSum F = RowSum::kF32, M = RowSum::kMfma, D = RowSum::kDot;
+  if (dqk == 64) return lse ? wide_variant<64, 64, F>() : wide_variant<64, 64, D>();
+  if (dqk == 72) return lse ? wide_variant<72, 72, F>() : wide_variant<72, 72, M>();
+  if (dqk == 80) return lse ? wide_variant<80, 80, F>() : wide_variant<80, 80, M>();
+  if (dqk == 128) return lse ? wide_variant<128, 128, F>() : wide_variant<128, 128, D>();
+  return lse ? wide_variant<192, 128, F>() : wide_variant<192, 128, D>();
 }
 
 static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }

@@ -809,25 +809,34 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
   // With SUM_BY_MFMA the row sum sits in column d_v of the accumulator:
   // dv block VB - 1, register 4 * ((d_v % 32) / 8), lanes 0-31.
   constexpr int kSumReg = 4 * ((DV % 32) / 8);
+  // Lane (row, g) holds d_v 8 jj + 4 g .. + 3 of its row for jj = 0..3 of
+  // each 32-wide block.  Swapping halves with lane row ^ 32 over a pair of
+  // chunks (jj, jj + 1) leaves lane g with the 8 contiguous values of chunk
+  // jj + g: one 16-byte store instead of two 8-byte ones per lane.
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l = SUM_BY_MFMA ? from_lower_half(acc[C::VB - 1][qb][kSumReg]) : xhalf_sum(l_run[qb]);
     const int row = wrow0 + 32 * qb + l32;
-    if (row < r1) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      uint16_t* dst = p.o + (int64_t)(q0 + row) * p.o_row + (int64_t)h * p.o_head;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* dst = p.o + (int64_t)(q0 + row) * p.o_row + (int64_t)h * p.o_head;
 #pragma unroll
-      for (int vb = 0; vb < C::VB; ++vb)
+    for (int vb = 0; vb < C::VB; ++vb)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int dv = vb * 32 + 8 * jj + 4 * g;
-          if (dv < DV) {
-            u32x2 o2;
-            o2[0] = pack_bf16x2(acc[vb][qb][4 * jj] * inv, acc[vb][qb][4 * jj + 1] * inv);
-            o2[1] = pack_bf16x2(acc[vb][qb][4 * jj + 2] * inv, acc[vb][qb][4 * jj + 3] * inv);
-            *(u32x2*)(dst + dv) = o2;
-          }
+      for (int jp = 0; jp < 4; jp += 2) {
+        const f32x16& a = acc[vb][qb];
+        const uint32_t x0 = pack_bf16x2(a[4 * jp] * inv, a[4 * jp + 1] * inv);
+        const uint32_t x1 = pack_bf16x2(a[4 * jp + 2] * inv, a[4 * jp + 3] * inv);
+        const uint32_t y0 = pack_bf16x2(a[4 * jp + 4] * inv, a[4 * jp + 5] * inv);
+        const uint32_t y1 = pack_bf16x2(a[4 * jp + 6] * inv, a[4 * jp + 7] * inv);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+        const int dv = vb * 32 + 8 * (jp + g);
+        if (row < r1 && dv < DV) {
+          const u32x4 o4 = {s0[0], s1[0], s0[1], s1[1]};
+          *(u32x4*)(dst + dv) = o4;
         }
+      }
+    if (row < r1) {
       if (p.lse != nullptr && g == 0) {
         const float lse = l > 0.f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
         p.lse[(int64_t)h * p.total_q + q0 + row] = lse;

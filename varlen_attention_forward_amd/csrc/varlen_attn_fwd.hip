@@ -377,9 +377,21 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
   const TileRange tr = tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN);
   const int ntiles = tr.kt_end - tr.kt_begin;
   const int wrow0 = r0 + wave * kRowsPerWave;
-  // Waves past the segment's last row still issue their share of the loads
-  // and meet every barrier, but skip the arithmetic.
-  const bool active = wrow0 < r1;
+  // Each wave's own key-tile range (its 64 rows see a sub-range of the
+  // workgroup's).  Iteration w_end, whose tile none of the wave's rows sees
+  // (masked to zero probabilities, so the running max and sum stay put and
+  // the slow path cannot trigger), still runs for the PV of tile w_end - 1;
+  // after it the wave only issues its share of the loads and meets the
+  // barriers.  Its own unmasked sub-range spares it the mask on tiles all its
+  // rows see.  Waves past the segment's last row compute nothing.
+  int w_end = 0, w_full_begin = 0, w_full_end = 0;  // relative to tr.kt_begin
+  if (wrow0 < r1) {
+    const TileRange wt = tile_range(Lq, Lk, wrow0, min(wrow0 + kRowsPerWave, r1), p.causal, p.wl, p.wr, kBN);
+    w_end = wt.kt_end - tr.kt_begin;
+    w_full_begin = wt.full_begin - tr.kt_begin;
+    w_full_end = wt.full_end - tr.kt_begin;
+  }
+  const bool active = w_end > 0;
 
   // ---- padded V chunks: zeros, or a one in column d_v ------------------------
   if constexpr (C::V_PAD > 0) {
@@ -551,7 +563,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
   // Boundary tiles only: scores of keys a row may not see become -inf.
   auto mask = [&](int j, f32x16 (&s)[2]) VA_INLINE {
     const int kt = tr.kt_begin + j;
-    if (kt < tr.full_begin || kt >= tr.full_end) {
+    if (j < w_full_begin || j >= w_full_end) {
       const int key0 = kt * kBN;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
@@ -720,6 +732,20 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
   //
   // Iteration j's softmax reads sbuf[j % 2] and QK^T writes sbuf[(j + 1) % 2];
   // the loop is unrolled by the (even) stage count so both are static.
+  // PV of one tile on its own (the workgroup's last tile).
+  auto pv_tile = [&](const lds_char* vs) VA_INLINE {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int vb = 0; vb < C::VB; ++vb) {
+        const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
+        const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
+        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][t], acc[vb][qb], 0, 0, 0);
+      }
+  };
   if (ntiles > 0) {
     static_for<0, kAhead>([&](auto t) VA_INLINE { issue(t); });  // tiles 0-3
     wait_landed(Int<kAhead - 1>{});                                // tile 0
@@ -746,7 +772,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
         const int j = j0 + U;
         if (U == 0 || j < ntiles) {
           issue(Int<(U + 1 + kAhead) % kStages>{});  // tile j + 4 (zeros past the last)
-          if (active) {
+          if (j <= w_end) {
             constexpr int cur = (U + 1) % 2;  // j % 2, j0 being odd
             mask(j, sbuf[cur]);
             float sum[2];
@@ -785,23 +811,13 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
     // The zero loads past the last tile must land before the workgroup's LDS
     // can be handed to the next workgroup.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (active) {  // PV of the last tile, its stage picked at run time (all DMA has landed)
+    if (w_end == ntiles) {  // PV of the last tile, its stage picked at run time (all DMA has landed)
       const int last = (ntiles - 1) % kStages;
       const lds_char* vs = vst(Int<0>{});
       static_for<1, kStages>([&](auto st) VA_INLINE {
         if (last == decltype(st)::value) vs = vst(st);
       });
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int vb = 0; vb < C::VB; ++vb) {
-          const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
-          const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
-          const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][t], acc[vb][qb], 0, 0, 0);
-        }
+      pv_tile(vs);
     }
   }
 

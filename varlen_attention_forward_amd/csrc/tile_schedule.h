@@ -121,21 +121,23 @@ VA_HD int64_t grid_blocks(int64_t batch, int64_t heads, int64_t n_qt) {
 
 // The quad snake over an XCD's dispatch index k (of k_count per XCD); a
 // trailing partial quad keeps its order.
-VA_HD int64_t snake_quads(int64_t k, int64_t k_count) {
-  return ((k >> 2) & 1) && (k | 3) < k_count ? k ^ 3 : k;
+VA_HD uint32_t snake_quads(uint32_t k, uint32_t k_count) {
+  return ((k >> 2) & 1u) && (k | 3u) < k_count ? k ^ 3u : k;
 }
 
-VA_HD WorkUnit decode_block(int64_t w, int64_t batch, int64_t heads, int64_t n_qt, int causal) {
-  const int64_t x = w & 7;
-  const int64_t k = snake_quads(w >> 3, grid_blocks(batch, heads, n_qt) / 8);
-  const int64_t gl = k / n_qt, qi = k % n_qt;
-  const int64_t g = gl * 8 + x;
+// 32-bit arithmetic: the launch checks that the grid fits in int32.
+VA_HD WorkUnit decode_block(uint32_t w, uint32_t batch, uint32_t heads, uint32_t n_qt, int causal) {
+  const uint32_t groups = batch * heads;
+  const uint32_t x = w & 7u;
+  const uint32_t k = snake_quads(w >> 3, (groups + 7u) / 8u * n_qt);
+  const uint32_t gl = k / n_qt, qi = k - gl * n_qt;
+  const uint32_t g = gl * 8u + x;
   WorkUnit u;
-  u.valid = g < batch * heads;
+  u.valid = g < groups;
   u.b = (int32_t)(g / heads);
-  u.h = (int32_t)(g % heads);
+  u.h = (int32_t)(g - (uint32_t)u.b * heads);
   // Causal: the last q-tiles of a segment see the most keys; start them first.
-  u.qt = (int32_t)(causal ? n_qt - 1 - qi : qi);
+  u.qt = (int32_t)(causal ? n_qt - 1u - qi : qi);
   return u;
 }
 
@@ -169,7 +171,7 @@ inline bool lpt_applies(int32_t batch, const int32_t* lq, const int32_t* lk) {
 inline WorkUnit decode_block_lpt(int64_t w, int32_t batch, int32_t heads, int32_t block_m, int32_t n_qt,
                                  int causal, const int32_t* lq, const int32_t* lk) {
   const int32_t x = (int32_t)(w & 7);
-  const int64_t k = snake_quads(w >> 3, grid_blocks(batch, heads, n_qt) / 8);
+  const int64_t k = snake_quads((uint32_t)(w >> 3), (uint32_t)(grid_blocks(batch, heads, n_qt) / 8));
   int64_t pre = 0;
   for (int32_t r = 0; r < batch; ++r) {
     int32_t i = 0;  // the segment of rank r

@@ -183,7 +183,7 @@ __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int b
     const int lq0 = __builtin_amdgcn_readfirstlane(lq), lk0 = __builtin_amdgcn_readfirstlane(lk);
     if (__ballot(lane < p.batch && (lq != lq0 || lk != lk0)) != 0) {
       const int x = (int)(w & 7);
-      const int k = (int)snake_quads(w >> 3, gridDim.x / 8);
+      const int k = (int)snake_quads((uint32_t)(w >> 3), gridDim.x / 8u);
       int rank = 0;
       for (int j = 0; j < p.batch; ++j) {
         const int kj = __builtin_amdgcn_readlane(lk, j);
@@ -208,7 +208,7 @@ __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int b
         r.u.qt = p.causal ? nq - 1 - qi : qi;
       }
     } else {
-      r.u = decode_block(w, p.batch, p.heads, p.n_qt, p.causal);
+      r.u = decode_block((uint32_t)w, (uint32_t)p.batch, (uint32_t)p.heads, (uint32_t)p.n_qt, p.causal);
     }
     if (r.u.valid) {
       const int b = __builtin_amdgcn_readfirstlane(r.u.b);
@@ -219,7 +219,7 @@ __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int b
     }
     return r;
   }
-  r.u = decode_block(w, p.batch, p.heads, p.n_qt, p.causal);
+  r.u = decode_block((uint32_t)w, (uint32_t)p.batch, (uint32_t)p.heads, (uint32_t)p.n_qt, p.causal);
   if (r.u.valid) {
     const int b = __builtin_amdgcn_readfirstlane(r.u.b);
     r.q0 = p.cu_q[b];
@@ -376,39 +376,11 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
   const int r1 = min(r0 + C::BM, Lq);
   const TileRange tr = tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN);
   const int ntiles = tr.kt_end - tr.kt_begin;
-  const int wrow0 = r0 + wave * kRowsPerWave;
-  // Each wave's own key-tile range (its 64 rows see a sub-range of the
-  // workgroup's).  Iteration w_end, whose tile none of the wave's rows sees
-  // (masked to zero probabilities, so the running max and sum stay put and
-  // the slow path cannot trigger), still runs for the PV of tile w_end - 1;
-  // after it the wave only issues its share of the loads and meets the
-  // barriers.  Its own unmasked sub-range spares it the mask on tiles all its
-  // rows see.  Waves past the segment's last row compute nothing.
-  int w_end = 0, w_full_begin = 0, w_full_end = 0;  // relative to tr.kt_begin
-  if (wrow0 < r1) {
-    const TileRange wt = tile_range(Lq, Lk, wrow0, min(wrow0 + kRowsPerWave, r1), p.causal, p.wl, p.wr, kBN);
-    w_end = wt.kt_end - tr.kt_begin;
-    w_full_begin = wt.full_begin - tr.kt_begin;
-    w_full_end = wt.full_end - tr.kt_begin;
-  }
-  const bool active = w_end > 0;
-
-  // ---- padded V chunks: zeros, or a one in column d_v ------------------------
-  if constexpr (C::V_PAD > 0) {
-    static_for<0, kStages>([&](auto st) VA_INLINE {
-      for (int i = tid; i < kBN * C::V_PAD; i += C::THREADS) {
-        const int row = i / C::V_PAD, c = C::V_REAL + i % C::V_PAD;
-        const u32x4 val = {(SUM_BY_MFMA && c == C::V_REAL) ? 0x3F80u : 0u, 0u, 0u, 0u};  // bf16 1.0
-        *(__attribute__((address_space(3))) u32x4*)(vst(st) + (row * C::CPR_V + c) * 16) = val;
-      }
-    });
-  }
-
   // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------
   bf16x8 qf[2][C::KC];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int row = wrow0 + 32 * qb + l32;
+    const int row = r0 + wave * kRowsPerWave + 32 * qb + l32;
     const uint16_t* src = p.q + (int64_t)(q0 + row) * p.q_row + (int64_t)h * p.q_head;
 #pragma unroll
     for (int c = 0; c < C::KC; ++c) {
@@ -485,6 +457,39 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
     static_assert(n < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
   };
+
+  // The Q and first tiles' loads go out before the rest of the set-up, which
+  // then runs under their latency.
+  if (ntiles > 0) static_for<0, kAhead>([&](auto t) VA_INLINE { issue(t); });  // tiles 0-3
+
+  const int wrow0 = r0 + wave * kRowsPerWave;
+  // Each wave's own key-tile range (its 64 rows see a sub-range of the
+  // workgroup's).  Iteration w_end, whose tile none of the wave's rows sees
+  // (masked to zero probabilities, so the running max and sum stay put and
+  // the slow path cannot trigger), still runs for the PV of tile w_end - 1;
+  // after it the wave only issues its share of the loads and meets the
+  // barriers.  Its own unmasked sub-range spares it the mask on tiles all its
+  // rows see.  Waves past the segment's last row compute nothing.
+  int w_end = 0, w_full_begin = 0, w_full_end = 0;  // relative to tr.kt_begin
+  if (wrow0 < r1) {
+    const TileRange wt = tile_range(Lq, Lk, wrow0, min(wrow0 + kRowsPerWave, r1), p.causal, p.wl, p.wr, kBN);
+    w_end = wt.kt_end - tr.kt_begin;
+    w_full_begin = wt.full_begin - tr.kt_begin;
+    w_full_end = wt.full_end - tr.kt_begin;
+  }
+  const bool active = w_end > 0;
+
+
+  // ---- padded V chunks: zeros, or a one in column d_v ------------------------
+  if constexpr (C::V_PAD > 0) {
+    static_for<0, kStages>([&](auto st) VA_INLINE {
+      for (int i = tid; i < kBN * C::V_PAD; i += C::THREADS) {
+        const int row = i / C::V_PAD, c = C::V_REAL + i % C::V_PAD;
+        const u32x4 val = {(SUM_BY_MFMA && c == C::V_REAL) ? 0x3F80u : 0u, 0u, 0u, 0u};  // bf16 1.0
+        *(__attribute__((address_space(3))) u32x4*)(vst(st) + (row * C::CPR_V + c) * 16) = val;
+      }
+    });
+  }
 
   // ---- LDS operand reads ----------------------------------------------------
   const int k_rd = (l32 * C::KPITCH + g) * 16;  // K row l32, chunk 2c + g at + 32c
@@ -747,8 +752,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
       }
   };
   if (ntiles > 0) {
-    static_for<0, kAhead>([&](auto t) VA_INLINE { issue(t); });  // tiles 0-3
-    wait_landed(Int<kAhead - 1>{});                                // tile 0
+    wait_landed(Int<kAhead - 1>{});  // tile 0 (tiles 0-3 were issued above)
     lds_barrier();
     if (active) mfma_ops(nullptr, kst(Int<0>{}), sbuf[0], BoolTag<false>{});  // QK^T(0)
     wait_landed(Int<kAhead - 2>{});  // tile 1
@@ -972,7 +976,8 @@ extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_h
   const va::WorkUnit u = va::lpt_applies(batch, seqlens_q, seqlens_k)
                              ? va::decode_block_lpt(block, batch, num_heads, var.block_m, (int32_t)n_qt, causal,
                                                     seqlens_q, seqlens_k)
-                             : va::decode_block(block, batch, num_heads, n_qt, causal);
+                             : va::decode_block((uint32_t)block, (uint32_t)batch, (uint32_t)num_heads,
+                                                (uint32_t)n_qt, causal);
   *segment = u.valid ? u.b : -1;
   *head = u.valid ? u.h : -1;
   *q_tile = u.valid ? u.qt : -1;

@@ -12,12 +12,19 @@ Prints one JSON line.  ``value`` is algorithmic TFLOP/s over the timed
 steps (FLOPs = heads * visible (query, key) pairs * 2 * (d_qk + d_v); no
 padding or skipped-tile work is counted).  ``roofline`` compares the kernel's
 average duration, measured with HIP events on the launch stream, against the
-MI355X dense bf16 MFMA peak (2.5 PFLOP/s).  ``cpu_baseline`` times the fp64
+MI355X dense bf16 MFMA peak (2.5 PFLOP/s) for workloads above the ridge
+(312.5 flop per algorithmic byte), else against the 8 TB/s HBM peak with
+achieved = algorithmic bytes / duration in GB/s.  ``cpu_baseline`` times the fp64
 numpy oracle on a bounded sample of the same workload on the host cores.
 
-Other modes (for the rocprofv3 summaries under profiles/):
+Other modes (for the summaries under profiles/):
     python bench.py --copy-calibration     a plain 1 GiB device copy, to scale
                                             FETCH_SIZE / WRITE_SIZE counters
+    python bench.py --report [--workload W]  every workload (or W): 10 rounds of
+                                            5 warm-up + 20 timed launches (best and
+                                            median), the same launches replayed from
+                                            a HIP graph, the host-inclusive eager rate
+                                            and the shader clock seen meanwhile
 """
 from __future__ import annotations
 
@@ -25,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -34,6 +42,8 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak, ViT d=80 and MLA 192/128"
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # 312.5
 DEFAULT_WORKLOAD = "vit_full_d80"
 KERNEL_SOURCES = [
     os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "varlen_attn_fwd.hip"),
@@ -142,6 +152,159 @@ def cpu_baseline(w, inp, budget_s: float = 12.0) -> dict:
     }
 
 
+def device_inputs(w, cpu_inp, rotate: int = 0):
+    """Input/output copies on cuda:0: three when the inputs fit the 256 MB
+    last-level cache (so the timed reads come from HBM), else one."""
+    import torch
+
+    rotate = rotate or (3 if algorithmic_bytes(w) < 256e6 else 1)
+    copies = []
+    for _ in range(rotate):
+        d = cpu_inp.to("cuda:0")
+        out = torch.empty((w.total_q, w.num_heads, w.head_dim_v), dtype=torch.bfloat16, device="cuda:0")
+        lse = torch.empty((w.num_heads, w.total_q), dtype=torch.float32, device="cuda:0") if w.return_lse else None
+        copies.append((d, out, lse))
+    return copies
+
+
+def launch(copies, i):
+    import varlen_attention_forward_amd as va
+
+    d, out, lse = copies[i % len(copies)]
+    va.varlen_attn_fwd(d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, d.max_seqlen_q, d.max_seqlen_k,
+                       softmax_scale=d.softmax_scale, causal=d.causal, window_size=d.window,
+                       out=out, return_lse=lse is not None, lse=lse)
+
+
+class ClockSampler:
+    """Samples the shader clock (MHz) with rocm-smi in a background thread."""
+
+    def __init__(self, period_s: float = 0.25):
+        import threading
+
+        self.samples = []
+        self.period_s = period_s
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        import re
+
+        try:
+            res = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=10)
+        except Exception:  # tool missing or stuck: no sample
+            return None
+        m = re.search(r"sclk clock level:\s*\d+:\s*\((\d+)\s*Mhz\)", res.stdout, re.IGNORECASE)
+        return int(m.group(1)) if m else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period_s)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=15)
+
+    def median(self):
+        return sorted(self.samples)[len(self.samples) // 2] if self.samples else None
+
+
+def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -> None:
+    """Per workload: best and median of `rounds` rounds of `timed` launches
+    (HIP events on the launch stream, `warmup` untimed launches before each),
+    the same `timed` launches captured once in a HIP graph and replayed
+    `rounds` times (every replay's outputs checked bit-equal to eager ones),
+    and the eager rate with host time included."""
+    import statistics
+
+    import torch
+    from varlen_attention_forward_amd import workloads
+
+    rows = []
+    for name in names:
+        w = workloads.WORKLOADS[name]
+        print("report: %s" % name, file=sys.stderr, flush=True)
+        copies = device_inputs(w, workloads.workload_inputs(w))
+        flops, nbytes = algorithmic_flops(w), algorithmic_bytes(w)
+        stream = torch.cuda.current_stream()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        eager_ms, wall_ms = [], []
+        with ClockSampler() as clk:
+            for _ in range(rounds):
+                for i in range(warmup):
+                    launch(copies, i)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                ev0.record(stream)
+                for i in range(timed):
+                    launch(copies, i)
+                ev1.record(stream)
+                torch.cuda.synchronize()
+                wall_ms.append((time.perf_counter() - t0) * 1e3 / timed)
+                eager_ms.append(ev0.elapsed_time(ev1) / timed)
+        # eager reference outputs of every copy
+        for i in range(len(copies)):
+            launch(copies, i)
+        torch.cuda.synchronize()
+        ref = [(o.clone(), None if l is None else l.clone()) for _, o, l in copies]
+        graph = torch.cuda.CUDAGraph()
+        for _, o, l in copies:  # replays must rewrite these
+            o.zero_()
+            if l is not None:
+                l.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            for i in range(timed):
+                launch(copies, i)
+        graph_ms = []
+        for _ in range(rounds):
+            for _, o, _l in copies:
+                o.zero_()
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            graph.replay()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            graph_ms.append(ev0.elapsed_time(ev1) / timed)
+            for (_, o, l), (ro, rl) in zip(copies, ref):
+                if not torch.equal(o, ro) or (l is not None and not torch.equal(l, rl)):
+                    raise RuntimeError("%s: graph replay differs from the eager result" % name)
+        del graph
+        best, med = min(eager_ms), statistics.median(eager_ms)
+        row = {
+            "workload": name,
+            "kernel_ms_best": round(best, 4),
+            "kernel_ms_median": round(med, 4),
+            "tflops_best": round(flops / best / 1e9, 2),
+            "tflops_median": round(flops / med / 1e9, 2),
+            "frac_of_bf16_peak_best": round(flops / best / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "gbs_best": round(nbytes / best / 1e6, 1),
+            "graph_ms_best": round(min(graph_ms), 4),
+            "graph_ms_median": round(statistics.median(graph_ms), 4),
+            "eager_wall_ms_median": round(statistics.median(wall_ms), 4),
+            "sclk_mhz_median": clk.median(),
+            "sclk_samples": len(clk.samples),
+            "input_copies": len(copies),
+        }
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+    print("| workload | kernel ms best / median | TFLOP/s best / median | % peak | GB/s | graph ms best / median "
+          "| eager wall ms | sclk MHz |", flush=True)
+    print("|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        print("| %s | %.4f / %.4f | %.1f / %.1f | %.1f%% | %.0f | %.4f / %.4f | %.4f | %s |" % (
+            r["workload"], r["kernel_ms_best"], r["kernel_ms_median"], r["tflops_best"], r["tflops_median"],
+            100 * r["frac_of_bf16_peak_best"], r["gbs_best"], r["graph_ms_best"], r["graph_ms_median"],
+            r["eager_wall_ms_median"], r["sclk_mhz_median"]), flush=True)
+
+
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5) -> None:
     import torch
 
@@ -163,6 +326,8 @@ def main() -> int:
                     help="input copies to cycle through (0 = 3 when the inputs fit the 256 MB MALL, else 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--report", action="store_true",
+                    help="timing protocol over every workload (or --workload if given explicitly)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -171,6 +336,12 @@ def main() -> int:
         return 2
     if args.copy_calibration:
         copy_calibration()
+        return 0
+    if args.report:
+        from varlen_attention_forward_amd import workloads
+
+        explicit = any(a == "--workload" or a.startswith("--workload=") for a in sys.argv[1:])
+        protocol_report([args.workload] if explicit else list(workloads.WORKLOADS))
         return 0
 
     import torch
@@ -216,7 +387,11 @@ def main() -> int:
     kernel_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
 
     flops = algorithmic_flops(w)
-    achieved = flops / kernel_s / 1e12
+    mfma_bound = flops / in_bytes >= RIDGE_FLOP_PER_BYTE
+    if mfma_bound:
+        achieved, peak, r_unit = flops / kernel_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, r_unit = in_bytes / kernel_s / 1e9, PEAK_HBM_GBS, "GB/s"
     plan = va.plan(w.head_dim_qk, w.head_dim_v, w.batch, w.num_heads, w.max_seqlen_q, w.max_seqlen_k, w.causal)
     result = {
         "metric": METRIC,
@@ -247,12 +422,13 @@ def main() -> int:
             "input_copies": rotate,
         },
         "roofline": {
-            "bound": "mfma",
+            "bound": "mfma" if mfma_bound else "hbm",
             "kernel": plan["kernel"],
             "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "peak": peak,
+            "unit": r_unit,
+            "frac": round(achieved / peak, 4),
+            "tflops_kernel": round(flops / kernel_s / 1e12, 2),
             "kernel_ms": round(kernel_s * 1e3, 4),
             "traffic": load_traffic(w.name),
             "algorithmic_bytes": in_bytes,

@@ -1,0 +1,61 @@
+"""Host-side logic of bench.py: FLOP and byte counts, the roofline choice and
+the single-GPU guard.  No GPU needed."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from varlen_attention_forward_amd import workloads  # noqa: E402
+
+
+def _brute_pairs(lq, lk, causal, wl, wr):
+    i = np.arange(lq)[:, None] + (lk - lq)
+    j = np.arange(lk)[None, :]
+    vis = np.ones((lq, lk), dtype=bool)
+    if causal:
+        vis &= j <= i
+    if wl >= 0:
+        vis &= j >= i - wl
+    if wr >= 0:
+        vis &= j <= i + wr
+    return int(vis.sum())
+
+
+@pytest.mark.parametrize("lq,lk", [(0, 5), (5, 0), (1, 1), (7, 7), (5, 9), (9, 5), (33, 64)])
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (False, (3, 0)),
+                                           (True, (4, -1)), (False, (0, 2))])
+def test_visible_pairs_brute_force(lq, lk, causal, window):
+    want = _brute_pairs(lq, lk, causal, *window)
+    assert bench.visible_pairs([lq], [lk], causal, window) == want
+
+
+@pytest.mark.parametrize("name,gflop", [
+    ("tiny_varlen_d64", 0.2852), ("vit_full_d80", 320.82), ("vit_window256_d80", 12.08),
+    ("vit_long65536_d128", 35184.4), ("mla_causal_192_128", 2749.45),
+])
+def test_algorithmic_flops(name, gflop):
+    """H x visible pairs x 2 (d_qk + d_v), against the figures worked out by hand
+    for each configuration (causal: L (L + 1) / 2 pairs per segment)."""
+    w = workloads.WORKLOADS[name]
+    assert bench.algorithmic_flops(w) / 1e9 == pytest.approx(gflop, rel=2e-4)
+
+
+def test_roofline_bound_follows_the_ridge():
+    """Workloads below 312.5 flop per algorithmic byte are reported against HBM."""
+    bounds = {n: bench.algorithmic_flops(w) / bench.algorithmic_bytes(w) >= bench.RIDGE_FLOP_PER_BYTE
+              for n, w in workloads.WORKLOADS.items()}
+    assert bounds == {"tiny_varlen_d64": False, "vit_full_d80": True, "vit_window256_d80": False,
+                      "vit_long65536_d128": True, "mla_causal_192_128": True}
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr

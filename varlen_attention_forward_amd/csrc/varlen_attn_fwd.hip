@@ -568,7 +568,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
   // Boundary tiles only: scores of keys a row may not see become -inf.
   auto mask = [&](int j, f32x16 (&s)[2]) VA_INLINE {
     const int kt = tr.kt_begin + j;
-    if (j < w_full_begin || j >= w_full_end) {
+    if ((unsigned)(j - w_full_begin) >= (unsigned)(w_full_end - w_full_begin)) {  // j outside [begin, end)
       const int key0 = kt * kBN;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)

@@ -24,7 +24,8 @@ Other modes (for the summaries under profiles/):
                                             5 warm-up + 20 timed launches (best and
                                             median), the same launches replayed from
                                             a HIP graph, the host-inclusive eager rate
-                                            and the shader clock seen meanwhile
+                                            and the shader clock seen meanwhile; then
+                                            the merge of two MLA-shaped partials (GB/s)
 """
 from __future__ import annotations
 
@@ -305,6 +306,52 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -
             r["eager_wall_ms_median"], r["sclk_mhz_median"]), flush=True)
 
 
+MERGE_SHAPE = (16384, 128, 128)  # rows, heads, d_v: the MLA prefill batch's output
+
+
+def merge_report(rounds: int = 10, warmup: int = 5, timed: int = 20) -> dict:
+    """varlen_attn_merge of two partial results shaped like the MLA batch's
+    output (three input/output copies cycled, so every read comes from HBM):
+    best and median kernel time over `rounds` rounds, and GB/s of its
+    algorithmic bytes (two bf16 outputs and two fp32 LSEs read, one of each
+    written) against the 8 TB/s HBM peak."""
+    import statistics
+
+    import torch
+    import varlen_attention_forward_amd as va
+
+    rows, heads, dim = MERGE_SHAPE
+    g = torch.Generator(device="cuda:0").manual_seed(7)
+    copies = []
+    for _ in range(3):
+        oa = torch.randn((rows, heads, dim), generator=g, device="cuda:0").to(torch.bfloat16)
+        ob = torch.randn((rows, heads, dim), generator=g, device="cuda:0").to(torch.bfloat16)
+        la = torch.randn((heads, rows), generator=g, device="cuda:0") * 4
+        lb = torch.randn((heads, rows), generator=g, device="cuda:0") * 4
+        copies.append((oa, la, ob, lb, torch.empty_like(oa), torch.empty_like(la)))
+    nbytes = 3 * rows * heads * dim * 2 + 3 * rows * heads * 4
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms = []
+    for _ in range(rounds):
+        for i in range(warmup):
+            oa, la, ob, lb, o, l = copies[i % 3]
+            va.varlen_attn_merge(oa, la, ob, lb, out=o, lse=l)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(timed):
+            oa, la, ob, lb, o, l = copies[i % 3]
+            va.varlen_attn_merge(oa, la, ob, lb, out=o, lse=l)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(ev0.elapsed_time(ev1) / timed)
+    best, med = min(ms), statistics.median(ms)
+    return {"kernel": "merge_states", "shape": "%d rows x %d heads x d %d" % MERGE_SHAPE,
+            "kernel_ms_best": round(best, 4), "kernel_ms_median": round(med, 4),
+            "gbs_best": round(nbytes / best / 1e6, 1), "gbs_median": round(nbytes / med / 1e6, 1),
+            "frac_of_hbm_peak_best": round(nbytes / best / 1e6 / PEAK_HBM_GBS, 4), "bytes": nbytes}
+
+
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5) -> None:
     import torch
 
@@ -342,6 +389,8 @@ def main() -> int:
 
         explicit = any(a == "--workload" or a.startswith("--workload=") for a in sys.argv[1:])
         protocol_report([args.workload] if explicit else list(workloads.WORKLOADS))
+        if not explicit:
+            print(json.dumps(merge_report()), flush=True)
         return 0
 
     import torch

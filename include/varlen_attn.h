@@ -112,6 +112,40 @@ int varlen_attn_fwd(const va_tensor* q, const va_tensor* k, const va_tensor* v,
                     int32_t causal, int32_t window_left, int32_t window_right,
                     const va_tensor* out, float* lse, void* stream);
 
+/*
+ * varlen_attn_merge -- merge two attention results over disjoint key sets of
+ * the same queries.  A prefill that reads its context in chunks merges the
+ * token-major partials of its per-chunk (non-causal) and new-token (causal)
+ * calls this way, and a split-KV forward ends with the same combine (vLLM
+ * docs page "vllm.v1.attention.backends.mla.prefill.flash_attn":
+ * FlashAttnPrefillBackend, `run_prefill_context_chunk` and the
+ * merge_attn_states remark in `_flash_attn_varlen_diff_headdims`;
+ * FA4SplitKVCombineKernel).
+ *
+ *   out_a, out_b   bf16 [rows, H, d] normalised partial outputs, as
+ *                  varlen_attn_fwd writes them
+ *   lse_a, lse_b   fp32 [H, rows] contiguous, their natural-log LSEs
+ *                  (-inf: the part saw no key for that row)
+ *   out            bf16 [rows, H, d]; may be the same buffer as out_a or out_b
+ *   lse            fp32 [H, rows] contiguous, or NULL; may be the same array
+ *                  as lse_a or lse_b
+ *   stream         hipStream_t
+ *
+ * For every row i and head h:  lse = ln(e^lse_a + e^lse_b) and
+ * out = e^(lse_a - lse) out_a + e^(lse_b - lse) out_b, in fp32, out rounded
+ * to bf16 (round to nearest even).  A part whose lse is -inf contributes
+ * nothing; both -inf give out = 0 and lse = -inf.  Every row of the
+ * descriptors is merged.  d: a multiple of 8 from 8 to 256, the same for the
+ * three tensors, as are rows and heads; strides in elements, positive,
+ * multiples of 8; data pointers 16-byte aligned, lse pointers 4-byte aligned.
+ * The caller owns every buffer.  Enqueues one kernel on `stream` and
+ * returns: no allocation, no synchronisation.  Returns VA_OK (rows == 0:
+ * nothing launched), VA_ERR_NULL, VA_ERR_SHAPE, VA_ERR_STRIDE, VA_ERR_ALIGN
+ * or VA_ERR_LAUNCH.
+ */
+int varlen_attn_merge(const va_tensor* out_a, const float* lse_a, const va_tensor* out_b,
+                      const float* lse_b, const va_tensor* out, float* lse, void* stream);
+
 /* Static, never-NULL description of a status code. */
 const char* varlen_attn_status_string(int status);
 

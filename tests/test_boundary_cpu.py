@@ -366,3 +366,39 @@ def test_work_unit_rejects_out_of_grid():
         pkg.work_unit(0, 3, 64, 64, [100, -1], [100, 100])
     with pytest.raises(ValueError):
         pkg.work_unit(0, 3, 64, 64, [0, 0], [100, 100])
+
+# ---------------------------------------------------------------------------
+# varlen_attn_merge validation (placeholder pointers; no call below launches)
+# ---------------------------------------------------------------------------
+def _merge(a=None, b=None, out=None, lse_a=FAKE, lse_b=FAKE, lse=FAKE):
+    a = a if a is not None else _t()
+    b = b if b is not None else _t()
+    out = out if out is not None else _t()
+    lib = pkg.library()
+    return lib.varlen_attn_merge(ctypes.byref(a), ctypes.c_void_p(lse_a), ctypes.byref(b), ctypes.c_void_p(lse_b),
+                                 ctypes.byref(out), ctypes.c_void_p(lse), ctypes.c_void_p(0))
+
+
+def test_merge_rejects_bad_arguments():
+    lib = pkg.library()
+    t = _t()
+    assert lib.varlen_attn_merge(None, FAKE, ctypes.byref(t), FAKE, ctypes.byref(t), FAKE, None) == B.VA_ERR_NULL
+    assert _merge(lse_a=0) == B.VA_ERR_NULL
+    assert _merge(lse_b=0) == B.VA_ERR_NULL
+    assert _merge(b=_t(rows=9)) == B.VA_ERR_SHAPE
+    assert _merge(out=_t(heads=3)) == B.VA_ERR_SHAPE
+    assert _merge(b=_t(dim=80)) == B.VA_ERR_SHAPE
+    assert _merge(a=_t(dim=4), b=_t(dim=4), out=_t(dim=4)) == B.VA_ERR_SHAPE     # below 8
+    assert _merge(a=_t(dim=12), b=_t(dim=12), out=_t(dim=12)) == B.VA_ERR_SHAPE  # not a multiple of 8
+    assert _merge(a=_t(dim=264), b=_t(dim=264), out=_t(dim=264)) == B.VA_ERR_SHAPE
+    assert _merge(a=_t(row_stride=0)) == B.VA_ERR_STRIDE
+    assert _merge(out=_t(head_stride=-64)) == B.VA_ERR_STRIDE
+    assert _merge(b=_t(row_stride=132)) == B.VA_ERR_ALIGN
+    assert _merge(out=_t(data=FAKE + 8)) == B.VA_ERR_ALIGN
+    assert _merge(a=_t(data=0)) == B.VA_ERR_NULL
+    assert _merge(lse=FAKE + 2) == B.VA_ERR_ALIGN
+
+
+def test_merge_of_no_rows_launches_nothing():
+    z = _t(rows=0, data=0)
+    assert _merge(a=z, b=z, out=z, lse_a=0, lse_b=0, lse=0) == B.VA_OK

@@ -15,11 +15,13 @@ from ._binding import (  # noqa: F401
     status_string,
     tile_range,
     varlen_attn_fwd,
+    varlen_attn_merge,
     work_unit,
 )
 
 __all__ = [
     "varlen_attn_fwd",
+    "varlen_attn_merge",
     "status_string",
     "tile_range",
     "work_unit",

@@ -39,6 +39,7 @@ EXPORTED_SYMBOLS = (
     "varlen_attn_tile_range",
     "varlen_attn_plan",
     "varlen_attn_work_unit",
+    "varlen_attn_merge",
 )
 
 
@@ -93,6 +94,9 @@ def library() -> ctypes.CDLL:
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         P(VaTensor), ctypes.c_void_p, ctypes.c_void_p,
     ]
+    lib.varlen_attn_merge.restype = ctypes.c_int
+    lib.varlen_attn_merge.argtypes = [P(VaTensor), ctypes.c_void_p, P(VaTensor), ctypes.c_void_p,
+                                      P(VaTensor), ctypes.c_void_p, ctypes.c_void_p]
     lib.varlen_attn_status_string.restype = ctypes.c_char_p
     lib.varlen_attn_status_string.argtypes = [ctypes.c_int]
     lib.varlen_attn_tile_range.restype = ctypes.c_int
@@ -251,3 +255,39 @@ def varlen_attn_fwd(
     if return_lse:
         return out, lse
     return out
+
+
+def _lse_ptr(t, name: str, heads: int, rows: int) -> int:
+    import torch
+
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda:
+        raise TypeError("%s must be a float32 GPU tensor" % name)
+    if not t.is_contiguous() or tuple(t.shape) != (heads, rows):
+        raise ValueError("%s must be contiguous of shape [H, rows] = %s" % (name, (heads, rows)))
+    return t.data_ptr()
+
+
+def varlen_attn_merge(out_a, lse_a, out_b, lse_b, out=None, lse=None, return_lse: bool = True):
+    """Merge two attention results over disjoint key sets of the same queries.
+
+    ``out_a``/``out_b`` bf16 [rows, H, d] and ``lse_a``/``lse_b`` fp32 [H, rows]
+    (what ``varlen_attn_fwd(..., return_lse=True)`` returns for each part).
+    Returns ``(out, lse)`` (``out`` alone when ``return_lse`` is False); ``out``
+    and ``lse`` may be given, also as one of the inputs (merge in place).
+    """
+    import torch
+
+    rows, heads, dim = out_a.shape
+    if out is None:
+        out = torch.empty_like(out_a)
+    if return_lse and lse is None:
+        lse = torch.empty((heads, rows), dtype=torch.float32, device=out_a.device)
+    st = library().varlen_attn_merge(
+        ctypes.byref(_desc(out_a, "out_a")), ctypes.c_void_p(_lse_ptr(lse_a, "lse_a", heads, rows)),
+        ctypes.byref(_desc(out_b, "out_b")), ctypes.c_void_p(_lse_ptr(lse_b, "lse_b", heads, rows)),
+        ctypes.byref(_desc(out, "out")),
+        ctypes.c_void_p(_lse_ptr(lse, "lse", heads, rows) if lse is not None else 0),
+        ctypes.c_void_p(torch.cuda.current_stream(out_a.device).cuda_stream),
+    )
+    _raise_for(st)
+    return (out, lse) if return_lse else out

@@ -1,0 +1,159 @@
+// Merge of two attention results over disjoint key sets of the same queries.
+//
+// A prefill that reads its context in chunks computes attention of the new
+// queries over each context chunk (non-causal) and over the new tokens
+// (causal), each call returning its normalised output and log-sum-exp, and
+// then merges those token-major partials (vLLM docs page
+// "vllm.v1.attention.backends.mla.prefill.flash_attn", FlashAttnPrefillBackend:
+// `run_prefill_context_chunk`, `run_prefill_new_tokens`, and the remark in
+// `_flash_attn_varlen_diff_headdims` that merge_attn_states needs token-major
+// partials).  A split-KV forward ends with the same combine over its splits
+// (same page, FA4SplitKVCombineKernel).
+//
+// For row i of head h, with parts (O_a, L_a) and (O_b, L_b) over key sets A
+// and B, the result over A u B is, exactly,
+//     L = ln(e^L_a + e^L_b),   O = e^(L_a - L) O_a + e^(L_b - L) O_b,
+// because O_x = sum_{j in x} e^{s_j} v_j / e^{L_x}.  A part whose LSE is -inf
+// saw no key and contributes nothing; both -inf gives O = 0, L = -inf, as the
+// forward writes for a row with no visible key.
+//
+// The kernel is an elementwise pass bound by HBM: per (row, head) it reads
+// two d_v-vectors of bf16 and two fp32 LSEs and writes one of each.  A group
+// of G lanes (G the power of two >= d_v / 8, so a group never straddles a
+// wave) owns one (row, head); lane c of the group moves the 16 bytes of
+// columns 8c .. 8c + 7, so consecutive lanes touch consecutive bytes of a
+// row.  Because a group's lanes read the LSEs in the same instruction before
+// lane 0 writes the result, the output LSE may be the same array as an
+// input's; the output O may be the same buffer as an input O.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "varlen_attn.h"
+
+namespace va_merge {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct Params {
+  const uint16_t* oa;
+  const uint16_t* ob;
+  uint16_t* o;
+  const float* la;
+  const float* lb;
+  float* l;
+  int64_t a_row, a_head, b_row, b_head, o_row, o_head;  // elements
+  int64_t rows;
+  int32_t heads;
+  int32_t chunks;      // d_v / 8
+  int32_t lane_shift;  // log2 of the lanes per (row, head)
+};
+
+__device__ __forceinline__ float lo_bf16(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
+
+// Two fp32 values rounded to bf16 (round to nearest even) in one word, a low.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__global__ __launch_bounds__(256) void merge_states(Params p) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t pair = t >> p.lane_shift;
+  const int c = (int)(t & ((1 << p.lane_shift) - 1));
+  if (pair >= p.rows * p.heads) return;
+  const int64_t i = pair / p.heads;
+  const int h = (int)(pair - i * p.heads);
+  const float la = p.la[(int64_t)h * p.rows + i];
+  const float lb = p.lb[(int64_t)h * p.rows + i];
+  const float m = fmaxf(la, lb);
+  float wa = 0.f, wb = 0.f, lse = -INFINITY;
+  if (m != -INFINITY) {
+    const float ea = expf(la - m), eb = expf(lb - m);  // the larger one is exactly 1
+    const float s = ea + eb;
+    wa = ea / s;
+    wb = eb / s;
+    lse = m + logf(s);
+  }
+  if (c < p.chunks) {
+    const u32x4 a = *(const u32x4*)(p.oa + i * p.a_row + h * p.a_head + 8 * c);
+    const u32x4 b = *(const u32x4*)(p.ob + i * p.b_row + h * p.b_head + 8 * c);
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // A part with weight 0 (no key, or negligible) is skipped, not scaled:
+      // its O is never read into the sum.
+      float x0 = 0.f, x1 = 0.f;
+      if (wa > 0.f) {
+        x0 += wa * lo_bf16(a[e]);
+        x1 += wa * hi_bf16(a[e]);
+      }
+      if (wb > 0.f) {
+        x0 += wb * lo_bf16(b[e]);
+        x1 += wb * hi_bf16(b[e]);
+      }
+      r[e] = pack_bf16x2(x0, x1);
+    }
+    *(u32x4*)(p.o + i * p.o_row + h * p.o_head + 8 * c) = r;
+  }
+  if (c == 0 && p.l != nullptr) p.l[(int64_t)h * p.rows + i] = lse;
+}
+
+static int check(const va_tensor* t, int64_t rows, int32_t heads, int32_t dim) {
+  if (t->rows != rows || t->heads != heads || t->dim != dim) return VA_ERR_SHAPE;
+  if (t->row_stride <= 0 || t->head_stride <= 0) return VA_ERR_STRIDE;
+  if ((t->row_stride & 7) != 0 || (t->head_stride & 7) != 0) return VA_ERR_ALIGN;
+  if (rows > 0 && t->data == nullptr) return VA_ERR_NULL;
+  if (((uintptr_t)t->data & 15u) != 0) return VA_ERR_ALIGN;
+  return VA_OK;
+}
+
+}  // namespace va_merge
+
+extern "C" int varlen_attn_merge(const va_tensor* out_a, const float* lse_a, const va_tensor* out_b,
+                                 const float* lse_b, const va_tensor* out, float* lse, void* stream) {
+  using namespace va_merge;
+  if (!out_a || !out_b || !out) return VA_ERR_NULL;
+  const int64_t rows = out_a->rows;
+  const int32_t heads = out_a->heads, dim = out_a->dim;
+  if (rows < 0 || rows > INT32_MAX || heads <= 0) return VA_ERR_SHAPE;
+  if (dim < 8 || dim > 256 || (dim & 7) != 0) return VA_ERR_SHAPE;
+  int st;
+  if ((st = check(out_a, rows, heads, dim)) != VA_OK) return st;
+  if ((st = check(out_b, rows, heads, dim)) != VA_OK) return st;
+  if ((st = check(out, rows, heads, dim)) != VA_OK) return st;
+  if (rows == 0) return VA_OK;
+  if (!lse_a || !lse_b) return VA_ERR_NULL;
+  if (((uintptr_t)lse_a & 3u) || ((uintptr_t)lse_b & 3u) || ((uintptr_t)lse & 3u)) return VA_ERR_ALIGN;
+
+  Params p;
+  p.oa = (const uint16_t*)out_a->data;
+  p.ob = (const uint16_t*)out_b->data;
+  p.o = (uint16_t*)out->data;
+  p.la = lse_a;
+  p.lb = lse_b;
+  p.l = lse;
+  p.a_row = out_a->row_stride;
+  p.a_head = out_a->head_stride;
+  p.b_row = out_b->row_stride;
+  p.b_head = out_b->head_stride;
+  p.o_row = out->row_stride;
+  p.o_head = out->head_stride;
+  p.rows = rows;
+  p.heads = heads;
+  p.chunks = dim / 8;
+  int shift = 0;
+  while ((1 << shift) < p.chunks) ++shift;
+  p.lane_shift = shift;
+  const int64_t threads = rows * heads << shift;
+  const int64_t grid = (threads + 255) / 256;
+  if (grid > INT32_MAX) return VA_ERR_SHAPE;
+  void* args[] = {&p};
+  const hipError_t err =
+      hipLaunchKernel((const void*)&merge_states, dim3((unsigned)grid), dim3(256), args, 0, (hipStream_t)stream);
+  return err == hipSuccess ? VA_OK : VA_ERR_LAUNCH;
+}

@@ -366,8 +366,10 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5) -> None:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The warm-up runs long enough (~70 ms on the default workload) for the
+    # shader clock to leave its idle state before the timed steps start.
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--rotate", type=int, default=0,
                     help="input copies to cycle through (0 = 3 when the inputs fit the 256 MB MALL, else 1)")

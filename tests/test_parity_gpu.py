@@ -336,11 +336,12 @@ def test_rows_outside_segments_untouched():
 @pytest.mark.parametrize("dims", DIMS, ids=lambda d: "d%d_%d" % d)
 @pytest.mark.parametrize("mode", ["full", "causal", "window"])
 def test_no_lse_row_sum_over_bf16(dims, mode):
-    """Without an LSE the row sum is taken over the bf16 probabilities (a
-    ones column in the padded V tile for d_v 72/80, bf16 dot products for
-    d_v 64/128): O must still match the oracle, on multi-block segments with
-    ragged tails and rows that see no key, and stay within the tolerance of
-    the LSE call's O."""
+    """Without an LSE, d_v 72/80 take the row sum over the bf16
+    probabilities (a ones column in the padded V tile): O must still match
+    the oracle, on multi-block segments with ragged tails and rows that see
+    no key, and stay within the tolerance of the LSE call's O.  The other
+    head dims run the same fp32 row sum with or without an LSE, so there the
+    two calls' O agree bit for bit."""
     causal, window = MODES[mode]
     lq = [1029, 700, 40, 513] if dims[0] < 192 else [600, 40, 257]
     lk = [1029, 901, 0, 513] if dims[0] < 192 else [700, 0, 257]
@@ -350,7 +351,10 @@ def test_no_lse_row_sum_over_bf16(dims, mode):
     ref_o, _ = oracle_on(inp)
     assert_parity(out, None, ref_o, None, what="nolse/%s/%s" % (dims, mode))
     with_lse, _ = run_gpu(inp)
-    assert float((out.float() - with_lse.float()).abs().max()) <= TOL_O
+    if dims[1] in (72, 80):
+        assert float((out.float() - with_lse.float()).abs().max()) <= TOL_O
+    else:
+        assert torch.equal(out, with_lse)
 
 
 def test_hip_graph_replay_matches_eager():

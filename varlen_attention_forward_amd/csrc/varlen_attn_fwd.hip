@@ -53,6 +53,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr float kRescaleTau = 8.0f;     // lazy rescale threshold, log2 units
+constexpr float kSumLimit = 256.0f;     // 2^kRescaleTau: a tile row sum this small bounds every p
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every range: reads 0
 constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
@@ -128,13 +129,6 @@ __device__ __forceinline__ void static_for(F&& f) {
     f(Int<I>{});
     static_for<I + 1, N>(f);
   }
-}
-
-// acc + the two bf16 halves of x, in one dot-product op.
-__device__ __forceinline__ float bf16_pair_sum(uint32_t x, float acc) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), ones, acc, false);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -308,19 +302,17 @@ __device__ __forceinline__ float from_lower_half(float x) {
   return __uint_as_float(r[0]);
 }
 
-// How the row sum of the probabilities is formed.  With an LSE requested it
-// is an fp32 sum of the fp32 probabilities (kF32).  Without one, O only needs
-// the sum to normalise what the PV product accumulated, so it is taken over
-// the bf16 probabilities the MFMA sees: for d_v 72 and 80 by a column of ones
-// in the padded V tile, which makes the PV product accumulate it alongside O
-// with no VALU work (kMfma); for d_v 64 and 128 by bf16 dot products of the
-// packed probabilities with (1, 1), one op per pair instead of two adds
-// (kDot).  A bf16 sum can move the LSE by up to ln(1 + 2^-9), which is why an
-// LSE keeps the fp32 sum.
-enum class RowSum { kF32, kMfma, kDot };
+// How the row sum of the probabilities is formed: an fp32 sum of the fp32
+// probabilities (kF32), or, for d_v 72 and 80 without an LSE, a column of
+// ones in the padded V tile, which makes the PV product accumulate the sum of
+// the bf16 probabilities it multiplies alongside O with no VALU work
+// (kMfma).  O only needs the sum to normalise what the PV product
+// accumulated, so the bf16 sum serves it; a bf16 sum can move the LSE by up
+// to ln(1 + 2^-9), which is why an LSE keeps the fp32 sum.
+enum class RowSum { kF32, kMfma };
 
 template <int DQK, int DV, RowSum SUM>
-__global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) {
+__global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd_wide(Params p) {
   using namespace wide;
   using C = Cfg<DQK, DV>;
   constexpr bool SUM_BY_MFMA = SUM == RowSum::kMfma;
@@ -522,6 +514,13 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
     row_lo[qb] = (int)imin64(rb.lo, (int64_t)Lk);
     row_hi[qb] = (int)imax64(rb.hi, (int64_t)-1);
   }
+  // Iteration (relative key tile) holding each row's first visible key, or
+  // -1 for a row that sees none: there the fast path cannot run (see
+  // fused_block).
+  int first_j[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+    first_j[qb] = row_lo[qb] <= row_hi[qb] ? row_lo[qb] / kBN - tr.kt_begin : -1;
   // Scores of two tiles (the one in the softmax and the next, which QK^T is
   // writing): sbuf[t % 2][qb][r] = key 8 (r / 4) + 4 g + r % 4, query l32.
   f32x16 sbuf[2][2];
@@ -618,7 +617,6 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
           const float x1 = __builtin_amdgcn_exp2f(fmaf(s[qb][r + 1], p.scale_log2, nm[qb]));
           pk[e] = pack_bf16x2(x0, x1);
           if constexpr (SUM == RowSum::kF32) sum += x0 + x1;
-          if constexpr (SUM == RowSum::kDot) sum = bf16_pair_sum(pk[e], sum);
         }
         pf[qb][t] = __builtin_bit_cast(bf16x8, pk);
       }
@@ -630,29 +628,36 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
   //
   // The fast path needs nothing of this tile's max: p = exp2(s * scale *
   // log2(e) - m_run) with the running max as it stands, in place, packed to
-  // bf16, and a check that this was valid: no row's tile max exceeds m_run +
-  // kRescaleTau (then p <= 2^kRescaleTau, exactly what the lazy rescale would
-  // produce) and no row saw its first visible key (lim = -FLT_MAX while m_run
-  // is -inf).  The row sums go to sum[], committed by the caller only if the
-  // check passed.
+  // bf16, and a check that this was valid: every p <= 2^kRescaleTau (the
+  // tile's max exceeds m_run by at most kRescaleTau, so the lazy rescale
+  // would not have moved the max either) and no row saw its first visible
+  // key (while m_run is -inf, p is not relative to any max yet).  With a
+  // row sum in registers (kF32) the first condition is read off the
+  // tile's row sum (sum <= 2^kRescaleTau bounds every term), so no row max
+  // is taken; with the ones-column sum (kMfma) the row max is taken on the
+  // raw scores as before.  The row sums go to sum[], committed by the caller
+  // only if the check passed.
   //
-  // Its VALU work is 64 units in dependency order: 16 row-max steps (8 per
-  // query block, on the raw scores), 32 in-place exps, 16 packs (+ sums).
-  // The MFMAs (PV of the previous tile, then QK^T of the next, two per LDS
-  // operand) each get an even share of the units, in source order pinned by
-  // scheduling barriers: the compiler's own schedule bunches the MFMAs, and
-  // an MFMA hides only a few VALU ops behind it.  The packs, which overwrite
-  // the probabilities PV reads, all fall after the last PV MFMA.
+  // Its VALU work is 48 or 64 units in dependency order: (16 row-max steps,
+  // 8 per query block, on the raw scores, kMfma only), 32 in-place exps, 16
+  // packs (+ sums).  The MFMAs (PV of the previous tile, then QK^T of the
+  // next, two per LDS operand) each get an even share of the units, in
+  // source order pinned by scheduling barriers: the compiler's own schedule
+  // bunches the MFMAs, and an MFMA hides only a few VALU ops behind it.  The
+  // packs, which overwrite the probabilities PV reads, all fall after the
+  // last PV MFMA.
   auto fused_block = [&](const lds_char* vs, const lds_char* ks, f32x16 (&s)[2], f32x16 (&sn)[2],
-                         float (&sum)[2]) VA_INLINE -> bool {
-    constexpr int kPVOps = 2 * C::VB, kOps = kPVOps + C::KC, kSlots = 2 * kOps, kUnits = 64;
-    static_assert(48 * kSlots / kUnits >= 2 * kPVOps, "packs must follow the PV MFMAs");
+                         float (&sum)[2], int j) VA_INLINE -> bool {
+    constexpr bool kMaxCheck = SUM_BY_MFMA;
+    constexpr int kPVOps = 2 * C::VB, kOps = kPVOps + C::KC, kSlots = 2 * kOps;
+    constexpr int kUnits = kMaxCheck ? 64 : 48;
+    static_assert((kUnits - 16) * kSlots / kUnits >= 2 * kPVOps, "packs must follow the PV MFMAs");
     float m[2];
     bool bad = false;
+    if constexpr (!kMaxCheck) bad = j == first_j[0] || j == first_j[1];
     u32x4 pk[2][2];
-    sum[0] = sum[1] = 0.f;
     auto unit = [&](auto uu) VA_INLINE {
-      constexpr int u = decltype(uu)::value;
+      constexpr int u = decltype(uu)::value + (kMaxCheck ? 0 : 16);
       if constexpr (u < 16) {  // row max, 8 steps per query block
         constexpr int qb = u / 8, st = u % 8;
         if constexpr (st == 0) {
@@ -666,12 +671,16 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
       } else if constexpr (u < 48) {  // p = exp2(s * scale - m_run), in place
         constexpr int qb = (u - 16) / 16, r = (u - 16) % 16;
         s[qb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, nm[qb]));
-      } else {  // bf16 pack (and fp32 row sum)
+      } else {  // bf16 pack (and row sum)
         constexpr int i = u - 48, qb = i / 8, t = (i / 4) % 2, e = i % 4, r = 8 * t + 2 * e;
+        constexpr bool first = t == 0 && e == 0;
         pk[qb][t][e] = pack_bf16x2(s[qb][r], s[qb][r + 1]);
-        if constexpr (SUM == RowSum::kF32) sum[qb] += s[qb][r] + s[qb][r + 1];
-        if constexpr (SUM == RowSum::kDot) sum[qb] = bf16_pair_sum(pk[qb][t][e], sum[qb]);
+        if constexpr (SUM == RowSum::kF32) {
+          const float pair = s[qb][r] + s[qb][r + 1];
+          sum[qb] = first ? pair : sum[qb] + pair;
+        }
         if constexpr (e == 3) pf[qb][t] = __builtin_bit_cast(bf16x8, pk[qb][t]);
+        if constexpr (!kMaxCheck && t == 1 && e == 3) bad |= !(sum[qb] <= kSumLimit);
       }
     };
     auto load_op = [&](int i, bf16x8& dst) VA_INLINE {
@@ -781,11 +790,13 @@ __global__ __launch_bounds__(64 * wide::kWaves, 1) void attn_fwd_wide(Params p) 
             mask(j, sbuf[cur]);
             float sum[2];
             const bool slow = fused_block(vst(Int<U % kStages>{}), kst(Int<(U + 2) % kStages>{}), sbuf[cur],
-                                          sbuf[cur ^ 1], sum);
-            // The probabilities are only read in the next iteration; without
-            // this use the compiler sinks their computation past the branch
-            // below, out of the interleave.
+                                          sbuf[cur ^ 1], sum, j);
+            // The probabilities are only read in the next iteration and the
+            // row sums only on the fast path; without these uses the compiler
+            // sinks their computation past the branch below, out of the
+            // interleave, where nothing hides it.
             asm volatile("" ::"v"(pf[0][0]), "v"(pf[0][1]), "v"(pf[1][0]), "v"(pf[1][1]));
+            if constexpr (!SUM_BY_MFMA) asm volatile("" ::"v"(sum[0]), "v"(sum[1]));
             // Commit the row sums on one path (the slow path restores them):
             // two paths merging into l_run cost the register allocator dearly.
             const float l_prev[2] = {l_run[0], l_run[1]};
@@ -901,12 +912,12 @@ static bool supported_dims(int dqk, int dv) {
 static Variant variant_for(int dqk, int dv, int max_seqlen_q, bool lse = true) {
   (void)dv;
   (void)max_seqlen_q;
-  constexpr RowSum F = RowSum::kF32, M = RowSum::kMfma, D = RowSum::kDot;
-  if (dqk == 64) return lse ? wide_variant<64, 64, F>() : wide_variant<64, 64, D>();
+  constexpr RowSum F = RowSum::kF32, M = RowSum::kMfma;
+  if (dqk == 64) return wide_variant<64, 64, F>();
   if (dqk == 72) return lse ? wide_variant<72, 72, F>() : wide_variant<72, 72, M>();
   if (dqk == 80) return lse ? wide_variant<80, 80, F>() : wide_variant<80, 80, M>();
-  if (dqk == 128) return lse ? wide_variant<128, 128, F>() : wide_variant<128, 128, D>();
-  return lse ? wide_variant<192, 128, F>() : wide_variant<192, 128, D>();
+  if (dqk == 128) return wide_variant<128, 128, F>();
+  return wide_variant<192, 128, F>();
 }
 
 static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }

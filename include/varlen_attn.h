@@ -77,7 +77,7 @@ typedef struct va_tensor {
 /*
  * varlen_attn_fwd -- fused varlen attention forward.
  *
- *   q, k, v        bf16 [total_q, H, d_qk], [total_k, H, d_qk], [total_k, H, d_v]
+ *   q, k, v        bf16 [total_q, H, d_qk], [total_k, H_kv, d_qk], [total_k, H_kv, d_v]
  *   cu_seqlens_q   device int32 [batch + 1]: segment b owns q rows
  *                  [cu_seqlens_q[b], cu_seqlens_q[b + 1]); same for _k
  *   batch          number of segments (>= 0)
@@ -95,7 +95,12 @@ typedef struct va_tensor {
  *   stream         hipStream_t (NULL = the default stream)
  *
  * Supported (d_qk, d_v): (64,64), (72,72), (80,80), (128,128), (192,128).
- * Heads: k->heads == v->heads == out->heads == q->heads (no grouped KV).
+ * Heads: out->heads == q->heads = H; k->heads == v->heads = H_kv, and H is a
+ * multiple of H_kv (grouped KV heads; SGLang PR #41344, "Accuracy Tests",
+ * lists GQA among the cases FA4 covers): query head h reads KV head
+ * h / (H / H_kv), so consecutive query heads share a KV head (a reading: the
+ * pages do not spell the grouping out; this is the usual one).  H_kv == H is
+ * plain multi-head attention.
  *
  * Preconditions that are documented but not checked (checking would need a
  * device-to-host copy): cu_seqlens are non-decreasing and start at 0; every
@@ -175,14 +180,17 @@ int varlen_attn_tile_range(int32_t seqlen_q, int32_t seqlen_k, int32_t row_begin
  * query rows, see varlen_attn_plan) it owns, or -1 in all three for a
  * workgroup that exits at once.  Segments of different lengths (at most 64
  * of them) are dealt longest key length first; otherwise in packing order;
- * either way every odd quad of each XCD's dispatch order is reversed.
+ * either way every odd quad of each XCD's dispatch order is reversed.  With
+ * num_heads_k KV heads (num_heads a multiple of it) the query heads of one
+ * KV head are dealt to the same XCD where the head counts allow.
  * Returns VA_OK, VA_ERR_NULL, VA_ERR_HEADDIM, or VA_ERR_ARG for a block
  * outside the grid, a negative length or all-empty queries.
  * Host only; makes no HIP call.
  */
-int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_heads, int32_t head_dim_qk,
-                          int32_t head_dim_v, const int32_t* seqlens_q, const int32_t* seqlens_k,
-                          int32_t causal, int32_t* segment, int32_t* head, int32_t* q_tile);
+int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_heads, int32_t num_heads_k,
+                          int32_t head_dim_qk, int32_t head_dim_v, const int32_t* seqlens_q,
+                          const int32_t* seqlens_k, int32_t causal, int32_t* segment, int32_t* head,
+                          int32_t* q_tile);
 
 /* Launch shape varlen_attn_fwd would use (host only; makes no HIP call). */
 typedef struct va_plan {

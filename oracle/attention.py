@@ -49,6 +49,11 @@ Readings where the pages are silent:
   ``_is_valid_warmup_shape_probe``, notes that sliding-window prefill is
   always causal, so the two combine).
 * Rows with no visible key give O = 0 and LSE = -inf.
+* Grouped KV heads (GQA): the SGLang PR #41344 "Accuracy Tests" section
+  lists GQA among the cases FA4 runs but does not spell the grouping out.
+  Read the usual way: with H query heads and H_kv KV heads (H a multiple of
+  H_kv), query head h attends with KV head h // (H // H_kv), so consecutive
+  query heads share a KV head.
 
 Rows of the output that belong to no segment are left as NaN here (the GPU
 leaves them untouched).  This module has pins in ``tests/test_oracle.py``.
@@ -126,7 +131,9 @@ def attention_fwd(
     """fp64 attention forward over packed segments.
 
     ``q``/``k``/``v`` are float arrays shaped [total, H, d] (bf16 inputs
-    upcast exactly).  ``softmax_scale`` is rounded to float32 first, since
+    upcast exactly); ``k`` and ``v`` may have fewer heads H_kv, H a multiple
+    of H_kv (grouped KV heads, see the module docstring).
+    ``softmax_scale`` is rounded to float32 first, since
     that is the value the GPU receives through its C interface.
     ``rows`` restricts the computation to the given global query rows and
     ``heads`` to the given heads; everything else stays NaN.
@@ -141,7 +148,9 @@ def attention_fwd(
     assert len(cu_q) == len(cu_k)
     total_q, H, _ = q.shape
     d_v = v.shape[2]
-    assert k.shape[1] == H and v.shape[1] == H, "one KV head per query head"
+    H_kv = k.shape[1]
+    assert v.shape[1] == H_kv and H_kv > 0 and H % H_kv == 0, "H must be a multiple of the KV heads"
+    group = H // H_kv
     scale = float(np.float32(softmax_scale))
     head_list = list(range(H)) if heads is None else [int(h) for h in heads]
 
@@ -168,8 +177,8 @@ def attention_fwd(
             for h in head_list:
                 o, l = _segment_head(
                     q[q0 + idx, h, :].astype(np.float64),
-                    k[k0:k1, h, :].astype(np.float64),
-                    v[k0:k1, h, :].astype(np.float64),
+                    k[k0:k1, h // group, :].astype(np.float64),
+                    v[k0:k1, h // group, :].astype(np.float64),
                     scale,
                     mask,
                 )

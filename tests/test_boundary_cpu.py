@@ -111,7 +111,11 @@ def test_unsupported_head_dims(dims):
 
 
 def test_shape_mismatches():
-    assert _call(k=_t(heads=1, dim=64)) == B.VA_ERR_SHAPE  # grouped KV heads are not supported
+    # grouped KV heads: q heads a multiple of the k/v heads, k and v alike
+    assert _call(q=_t(heads=3), out=_t(heads=3)) == B.VA_ERR_SHAPE  # 3 query heads over 2 KV heads
+    assert _call(k=_t(heads=1, dim=64)) == B.VA_ERR_SHAPE           # k and v head counts differ
+    assert _call(k=_t(heads=0), v=_t(heads=0)) == B.VA_ERR_SHAPE
+    assert _call(out=_t(heads=1)) == B.VA_ERR_SHAPE
     assert _call(v=_t(rows=11)) == B.VA_ERR_SHAPE
     assert _call(out=_t(rows=9)) == B.VA_ERR_SHAPE
     assert _call(k=_t(dim=80)) == B.VA_ERR_SHAPE
@@ -330,6 +334,33 @@ def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
                 first[(b, h)] = (blk, qt)
         for (b, h), (_, qt) in first.items():
             assert qt >= (-(-lq[b] // bm) if longest_first else n_qt) - 4
+
+
+@pytest.mark.parametrize("heads,heads_k,lq", [(64, 8, [4096, 4096]), (32, 4, [700, 900, 33]), (12, 1, [300]),
+                                              (16, 16, [1000, 2000]), (24, 8, [513] * 3)])
+def test_work_unit_grouped_kv_heads(heads, heads_k, lq):
+    """With grouped KV heads every (segment, query head, q-tile) is still owned
+    once, and when the KV heads are a multiple of 8 the query heads of one KV
+    head all run on one XCD (block % 8), sharing its L2."""
+    p = pkg.plan(128, 128, len(lq), heads, max(lq), max(lq), 0)
+    bm = p["block_m"]
+    longest_first = len(set(lq)) > 1
+    n_qt = -(-max(lq) // bm)
+    want = {(b, h, qt) for b in range(len(lq)) for h in range(heads)
+            for qt in range(-(-lq[b] // bm) if longest_first else n_qt)}
+    seen, xcd_of = set(), {}
+    for blk in range(p["grid"]):
+        b, h, qt = pkg.work_unit(blk, heads, 128, 128, lq, lq, False, num_heads_k=heads_k)
+        if b < 0:
+            continue
+        assert (b, h, qt) not in seen
+        seen.add((b, h, qt))
+        xcd_of.setdefault((b, h // (heads // heads_k)), set()).add(blk % 8)
+    assert seen == want
+    if heads_k % 8 == 0:
+        assert all(len(x) == 1 for x in xcd_of.values())
+    with pytest.raises(ValueError):
+        pkg.work_unit(0, heads, 128, 128, lq, lq, False, num_heads_k=heads_k + 1 if heads % (heads_k + 1) else 0)
 
 
 @pytest.mark.parametrize("batch,heads,max_q,causal", [(4, 128, 4096, 1), (1, 16, 65536, 0), (3, 5, 700, 1)])

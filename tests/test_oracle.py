@@ -263,6 +263,49 @@ def test_against_sdpa(dims, mode):
         assert np.all(lse[:, qs][:, ~rows] == -np.inf)
 
 
+@pytest.mark.parametrize("heads,heads_k", [(6, 1), (6, 2), (8, 4), (4, 4)])
+def test_grouped_kv_heads_against_sdpa(heads, heads_k):
+    """Grouped KV heads: query head h uses KV head h // (H // H_kv).  Pinned
+    to torch's scaled_dot_product_attention with enable_gqa (float64), which
+    repeats each KV head over consecutive query heads."""
+    seqlens_q, seqlens_k = [5, 33, 17], [9, 33, 40]
+    inp = workloads.make_inputs(seqlens_q, seqlens_k, heads, 64, 64, seed=31 + heads_k, causal=True,
+                                num_heads_k=heads_k)
+    q, k, v = f64(inp.q), f64(inp.k), f64(inp.v)
+    assert k.shape[1] == heads_k and v.shape[1] == heads_k
+    cu_q, cu_k = inp.cu_seqlens_q.tolist(), inp.cu_seqlens_k.tolist()
+    o, lse = _run(q, k, v, cu_q, cu_k, inp.softmax_scale, True)
+    scale = float(np.float32(inp.softmax_scale))
+    for b in range(len(seqlens_q)):
+        qs, ks = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        m = torch.from_numpy(_distance_mask(seqlens_q[b], seqlens_k[b], True, -1, -1))
+        tq = torch.from_numpy(q[qs]).transpose(0, 1)
+        tk = torch.from_numpy(k[ks]).transpose(0, 1)
+        tv = torch.from_numpy(v[ks]).transpose(0, 1)
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=m, scale=scale,
+                                                               enable_gqa=True)
+        rows = m.any(dim=1).numpy()
+        got = o[qs].transpose(1, 0, 2)
+        np.testing.assert_allclose(got[:, rows], ref.numpy()[:, rows], rtol=1e-10, atol=1e-12)
+
+
+def test_planted_interleaved_kv_grouping_is_caught(monkeypatch):
+    """Reading KV head h % H_kv (interleaved grouping) instead of
+    h // (H // H_kv) must fail the grouped-heads pin."""
+    orig = oracle_mod.attention_fwd
+
+    def interleaved(q, k, v, *a, **kw):
+        hk = k.shape[1]
+        if hk == q.shape[1]:
+            return orig(q, k, v, *a, **kw)
+        rep = q.shape[1] // hk
+        # tile (not repeat) the KV heads: query head h then reads h % H_kv
+        return orig(q, np.tile(k, (1, rep, 1)), np.tile(v, (1, rep, 1)), *a, **kw)
+
+    monkeypatch.setattr(oracle, "attention_fwd", interleaved)
+    assert _fails(lambda: test_grouped_kv_heads_against_sdpa(6, 2))
+
+
 def test_rows_subset_matches_full():
     inp = workloads.make_inputs([100, 37], [120, 37], 4, 64, 64, seed=9, causal=True)
     q, k, v = f64(inp.q), f64(inp.k), f64(inp.v)

@@ -357,6 +357,31 @@ def test_no_lse_row_sum_over_bf16(dims, mode):
         assert torch.equal(out, with_lse)
 
 
+@pytest.mark.parametrize("dims", [(64, 64), (80, 80), (128, 128), (192, 128)], ids=lambda d: "d%d_%d" % d)
+@pytest.mark.parametrize("heads,heads_k", [(8, 1), (8, 2), (6, 3), (16, 8)])
+@pytest.mark.parametrize("mode", ["full", "causal", "window"])
+def test_grouped_kv_heads(dims, heads, heads_k, mode):
+    """Grouped KV heads (query head h reads KV head h // (H / H_kv)) against
+    the oracle, on ragged multi-block segments with q < k and q > k, with
+    and without an LSE; and a call with each KV head repeated to H heads
+    (plain multi-head attention) gives the same O and LSE bit for bit."""
+    causal, window = MODES[mode]
+    lq, lk = [300, 1, 530, 64], [300, 90, 530, 40]
+    seed = zlib.crc32(repr(("gqa", dims, heads, heads_k, mode)).encode()) % 1000
+    inp = workloads.make_inputs(lq, lk, heads, dims[0], dims[1], seed=seed, causal=causal, window=window,
+                                num_heads_k=heads_k)
+    out, lse = run_gpu(inp)
+    ref_o, ref_lse = oracle_on(inp)
+    assert_parity(out, lse, ref_o, ref_lse, what="gqa/%s/%d/%d/%s" % (dims, heads, heads_k, mode))
+    rep = heads // heads_k
+    mha = workloads.Inputs(**{**inp.__dict__, "k": inp.k.repeat_interleave(rep, dim=1).contiguous(),
+                              "v": inp.v.repeat_interleave(rep, dim=1).contiguous()})
+    out2, lse2 = run_gpu(mha)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    out3, _ = run_gpu(inp, return_lse=False)
+    assert_parity(out3, None, ref_o, None, what="gqa-nolse")
+
+
 def test_hip_graph_replay_matches_eager():
     """The call enqueues one kernel and nothing else, so it can be captured in a
     HIP graph: three replays, with eager calls between them, reproduce the

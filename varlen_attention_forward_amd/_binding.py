@@ -102,7 +102,7 @@ def library() -> ctypes.CDLL:
     lib.varlen_attn_tile_range.restype = ctypes.c_int
     lib.varlen_attn_tile_range.argtypes = [ctypes.c_int32] * 8 + [P(ctypes.c_int32)] * 4
     lib.varlen_attn_work_unit.restype = ctypes.c_int
-    lib.varlen_attn_work_unit.argtypes = ([ctypes.c_int64] + [ctypes.c_int32] * 4 + [P(ctypes.c_int32)] * 2
+    lib.varlen_attn_work_unit.argtypes = ([ctypes.c_int64] + [ctypes.c_int32] * 5 + [P(ctypes.c_int32)] * 2
                                           + [ctypes.c_int32] + [P(ctypes.c_int32)] * 3)
     lib.varlen_attn_plan.restype = ctypes.c_int
     lib.varlen_attn_plan.argtypes = [ctypes.c_int32] * 7 + [P(VaPlan)]
@@ -135,17 +135,20 @@ def tile_range(seqlen_q, seqlen_k, row_begin, row_end, causal, window_left, wind
     return tuple(o.value for o in out)
 
 
-def work_unit(block, num_heads, head_dim_qk, head_dim_v, seqlens_q, seqlens_k, causal=False):
+def work_unit(block, num_heads, head_dim_qk, head_dim_v, seqlens_q, seqlens_k, causal=False, num_heads_k=None):
     """(segment, head, q_tile) the kernel's workgroup ``block`` owns; -1s for padding.
 
-    ``seqlens_q`` / ``seqlens_k`` are the per-segment lengths (host ints).
+    ``seqlens_q`` / ``seqlens_k`` are the per-segment lengths (host ints);
+    ``num_heads_k`` the KV heads (default ``num_heads``).
     """
+    num_heads_k = num_heads if num_heads_k is None else num_heads_k
     lq, lk = list(seqlens_q), list(seqlens_k)
     if len(lq) != len(lk):
         raise ValueError("seqlens_q and seqlens_k must have one entry per segment")
     arr = ctypes.c_int32 * max(1, len(lq))
     out = [ctypes.c_int32() for _ in range(3)]
-    st = library().varlen_attn_work_unit(block, len(lq), num_heads, head_dim_qk, head_dim_v, arr(*lq), arr(*lk),
+    st = library().varlen_attn_work_unit(block, len(lq), num_heads, num_heads_k, head_dim_qk, head_dim_v,
+                                         arr(*lq), arr(*lk),
                                          int(causal), *[ctypes.byref(o) for o in out])
     _raise_for(st)
     return tuple(o.value for o in out)

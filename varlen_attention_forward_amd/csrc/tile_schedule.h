@@ -153,6 +153,19 @@ VA_HD WorkUnit decode_block(uint32_t w, uint32_t batch, uint32_t heads, uint32_t
 // the host reference.
 constexpr int kLptMaxBatch = 64;
 
+// Grouped KV heads.  With heads_k KV heads shared by heads query heads
+// (heads a multiple of heads_k), query head h reads KV head h / (heads /
+// heads_k): consecutive query heads share a KV head.  The schedule deals
+// groups by a dealing index d, not by the query head directly: d runs over
+// the KV heads fastest, so the query heads of one KV head have dealing
+// indices congruent modulo heads_k and, when heads_k is a multiple of 8
+// (groups being dealt over the 8 XCDs by d), all run on one XCD and read
+// that KV head through its L2 (with heads_k = 4, on two).  Without grouping
+// (heads_k == heads) d is the query head.
+VA_HD int32_t query_head(int32_t d, int32_t heads, int32_t heads_k) {
+  return (d % heads_k) * (heads / heads_k) + d / heads_k;
+}
+
 // The heads of the segment of rank r dealt to XCD x are h0, h0 + 8, ...
 VA_HD int32_t xcd_first_head(int32_t r, int32_t heads, int32_t x) {
   return (x - (int32_t)(((int64_t)r * heads) % 8) + 8) % 8;

@@ -69,6 +69,7 @@ struct Params {
   int64_t q_row, q_head, k_row, k_head, v_row, v_head, o_row, o_head;  // elements
   int64_t total_q;
   int32_t batch, heads, n_qt;
+  int32_t heads_k;  // KV heads; heads is a multiple of it
   int32_t causal, wl, wr;
   float scale_log2;  // softmax_scale * log2(e)
 };
@@ -198,11 +199,12 @@ __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int b
         const int nq = __builtin_amdgcn_readlane(nqt, i);
         const int qi = local % nq;
         r.u.b = i;
-        r.u.h = __builtin_amdgcn_readlane(h0, i) + 8 * (local / nq);
+        r.u.h = query_head(__builtin_amdgcn_readlane(h0, i) + 8 * (local / nq), p.heads, p.heads_k);
         r.u.qt = p.causal ? nq - 1 - qi : qi;
       }
     } else {
       r.u = decode_block((uint32_t)w, (uint32_t)p.batch, (uint32_t)p.heads, (uint32_t)p.n_qt, p.causal);
+      r.u.h = query_head(r.u.h, p.heads, p.heads_k);
     }
     if (r.u.valid) {
       const int b = __builtin_amdgcn_readfirstlane(r.u.b);
@@ -214,6 +216,7 @@ __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int b
     return r;
   }
   r.u = decode_block((uint32_t)w, (uint32_t)p.batch, (uint32_t)p.heads, (uint32_t)p.n_qt, p.causal);
+  r.u.h = query_head(r.u.h, p.heads, p.heads_k);
   if (r.u.valid) {
     const int b = __builtin_amdgcn_readfirstlane(r.u.b);
     r.q0 = p.cu_q[b];
@@ -414,10 +417,11 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   }
   // K/V rows of the next tile to issue, advanced one tile per issue; tiles
   // past the last get an empty range (all reads zero).
+  const int hk = h / (p.heads / p.heads_k);  // the KV head query head h reads
   const char* k_next =
-      (const char*)(p.k + ((int64_t)k0 + (int64_t)tr.kt_begin * kBN) * p.k_row + (int64_t)h * p.k_head);
+      (const char*)(p.k + ((int64_t)k0 + (int64_t)tr.kt_begin * kBN) * p.k_row + (int64_t)hk * p.k_head);
   const char* v_next =
-      (const char*)(p.v + ((int64_t)k0 + (int64_t)tr.kt_begin * kBN) * p.v_row + (int64_t)h * p.v_head);
+      (const char*)(p.v + ((int64_t)k0 + (int64_t)tr.kt_begin * kBN) * p.v_row + (int64_t)hk * p.v_head);
   int keys_next = Lk - tr.kt_begin * kBN;
   auto issue = [&](auto st) VA_INLINE {  // this wave's loads of the next tile into stage st
     // (readfirstlane: the clamp compiles to a VALU med3, and a descriptor
@@ -940,7 +944,7 @@ extern "C" const char* varlen_attn_status_string(int status) {
   switch (status) {
     case VA_OK: return "ok";
     case VA_ERR_NULL: return "a required pointer is NULL";
-    case VA_ERR_SHAPE: return "tensor rows/heads/dims disagree or a size is out of range";
+    case VA_ERR_SHAPE: return "tensor rows/heads/dims disagree (q heads must be a multiple of k/v heads) or a size is out of range";
     case VA_ERR_HEADDIM: return "unsupported (head_dim_qk, head_dim_v); supported: (64,64) (72,72) (80,80) (128,128) (192,128)";
     case VA_ERR_STRIDE: return "a row or head stride is not positive";
     case VA_ERR_ALIGN: return "a data pointer or stride is not a multiple of 16 bytes (lse: 4 bytes)";
@@ -967,13 +971,14 @@ extern "C" int varlen_attn_tile_range(int32_t seqlen_q, int32_t seqlen_k, int32_
   return VA_OK;
 }
 
-extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_heads,
+extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_heads, int32_t num_heads_k,
                                      int32_t head_dim_qk, int32_t head_dim_v, const int32_t* seqlens_q,
                                      const int32_t* seqlens_k, int32_t causal, int32_t* segment,
                                      int32_t* head, int32_t* q_tile) {
   if (!segment || !head || !q_tile) return VA_ERR_NULL;
   if (!va::supported_dims(head_dim_qk, head_dim_v)) return VA_ERR_HEADDIM;
   if (batch <= 0 || num_heads <= 0 || (causal != 0 && causal != 1)) return VA_ERR_ARG;
+  if (num_heads_k <= 0 || num_heads % num_heads_k != 0) return VA_ERR_ARG;
   if (!seqlens_q || !seqlens_k) return VA_ERR_NULL;
   int32_t max_q = 0;
   for (int32_t i = 0; i < batch; ++i) {
@@ -990,7 +995,7 @@ extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_h
                              : va::decode_block((uint32_t)block, (uint32_t)batch, (uint32_t)num_heads,
                                                 (uint32_t)n_qt, causal);
   *segment = u.valid ? u.b : -1;
-  *head = u.valid ? u.h : -1;
+  *head = u.valid ? va::query_head(u.h, num_heads, num_heads_k) : -1;
   *q_tile = u.valid ? u.qt : -1;
   return VA_OK;
 }
@@ -1025,7 +1030,8 @@ extern "C" int varlen_attn_fwd(const va_tensor* q, const va_tensor* k, const va_
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return VA_ERR_ARG;
   if (causal != 0 && causal != 1) return VA_ERR_ARG;
   if (window_left < -1 || window_right < -1) return VA_ERR_ARG;
-  if (q->heads <= 0 || k->heads != q->heads || v->heads != q->heads || out->heads != q->heads)
+  if (q->heads <= 0 || k->heads <= 0 || v->heads != k->heads || out->heads != q->heads ||
+      q->heads % k->heads != 0)
     return VA_ERR_SHAPE;
   if (q->rows < 0 || k->rows < 0 || v->rows != k->rows || out->rows != q->rows) return VA_ERR_SHAPE;
   if (q->rows > INT32_MAX || k->rows > INT32_MAX) return VA_ERR_SHAPE;
@@ -1065,6 +1071,7 @@ extern "C" int varlen_attn_fwd(const va_tensor* q, const va_tensor* k, const va_
   p.total_q = q->rows;
   p.batch = batch;
   p.heads = q->heads;
+  p.heads_k = k->heads;
   p.n_qt = (int32_t)n_qt;
   p.causal = causal;
   p.wl = window_left;

@@ -207,15 +207,18 @@ def make_inputs(
     softmax_scale: Optional[float] = None,
     std: float = 1.0,
     v_std: float = 1.0,
+    num_heads_k: Optional[int] = None,
 ) -> Inputs:
     """Draw Q, K ~ N(0, std^2) and V ~ N(0, v_std^2) in float32 (in that order)
-    and round to bf16."""
+    and round to bf16.  K and V get ``num_heads_k`` heads (default
+    ``num_heads``)."""
     assert len(seqlens_q) == len(seqlens_k)
+    hk = num_heads if num_heads_k is None else int(num_heads_k)
     g = torch.Generator().manual_seed(seed)
     tq, tk = int(sum(seqlens_q)), int(sum(seqlens_k))
     q = torch.randn((tq, num_heads, head_dim_qk), generator=g, dtype=torch.float32)
-    k = torch.randn((tk, num_heads, head_dim_qk), generator=g, dtype=torch.float32)
-    v = torch.randn((tk, num_heads, head_dim_v), generator=g, dtype=torch.float32)
+    k = torch.randn((tk, hk, head_dim_qk), generator=g, dtype=torch.float32)
+    v = torch.randn((tk, hk, head_dim_v), generator=g, dtype=torch.float32)
     if std != 1.0:
         q, k = q * std, k * std
     if v_std != 1.0:

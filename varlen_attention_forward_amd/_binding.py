@@ -219,8 +219,9 @@ def varlen_attn_fwd(
 ):
     """Fused varlen attention forward on the current HIP stream.
 
-    ``q`` [total_q, H, d_qk], ``k`` [total_k, H, d_qk], ``v`` [total_k, H, d_v]
-    in bf16 on the GPU; ``cu_seqlens_q/k`` int32 [batch + 1] on the GPU.
+    ``q`` [total_q, H, d_qk], ``k`` [total_k, H_kv, d_qk], ``v`` [total_k, H_kv, d_v]
+    in bf16 on the GPU (H a multiple of H_kv: query head h reads KV head
+    h // (H // H_kv)); ``cu_seqlens_q/k`` int32 [batch + 1] on the GPU.
     Returns ``out`` [total_q, H, d_v] bf16, or ``(out, lse)`` with lse fp32
     [H, total_q] when ``return_lse``.  ``softmax_scale`` defaults to
     d_qk^-0.5.  ``window_size`` is ``(left, right)``, -1 for unbounded.

@@ -425,6 +425,32 @@ def test_empty_batch_and_zero_keys():
     assert va.varlen_attn_fwd(e, e, e, cu, cu, 0, 0).shape == (0, 2, 64)
 
 
+def test_tensors_beyond_2gib():
+    """64-bit addressing: 2100 segments of 1024 tokens, 8 heads, d 64, so Q,
+    K, V and O each span 2.2 GB and the last segments start past 2^31 bytes
+    (and past 2^31 elements of O in total).  Inputs are drawn on the GPU
+    from a seeded generator; sampled segments (first, middle and the last
+    three) are checked against the oracle run on just those segments."""
+    B, L, H, D = 2100, 1024, 8, 64
+    assert B * L * H * D * 2 > 2 ** 31
+    g = torch.Generator(device=DEV).manual_seed(2024)
+    q = torch.randn((B * L, H, D), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((B * L, H, D), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((B * L, H, D), generator=g, device=DEV).to(torch.bfloat16)
+    cu = torch.arange(0, (B + 1) * L, L, dtype=torch.int32, device=DEV)
+    out, lse = va.varlen_attn_fwd(q, k, v, cu, cu, L, L, causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    from oracle import attention_fwd
+
+    for b in (0, B // 2, B - 3, B - 2, B - 1):
+        sl = slice(b * L, (b + 1) * L)
+        ref_o, ref_lse = attention_fwd(f32(q[sl]), f32(k[sl]), f32(v[sl]), [0, L], [0, L], D ** -0.5,
+                                       causal=True)
+        assert_parity(out[sl], lse[:, sl].contiguous(), ref_o, ref_lse, what="segment %d" % b)
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------------------
 # the named workloads at full size (sampled rows where the oracle is slow)
 # ---------------------------------------------------------------------------

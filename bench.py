@@ -168,13 +168,13 @@ def device_inputs(w, cpu_inp, rotate: int = 0):
     return copies
 
 
-def launch(copies, i):
+def launch(copies, i, num_splits=1):
     import varlen_attention_forward_amd as va
 
     d, out, lse = copies[i % len(copies)]
     va.varlen_attn_fwd(d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, d.max_seqlen_q, d.max_seqlen_k,
                        softmax_scale=d.softmax_scale, causal=d.causal, window_size=d.window,
-                       out=out, return_lse=lse is not None, lse=lse)
+                       out=out, return_lse=lse is not None, lse=lse, num_splits=num_splits)
 
 
 class ClockSampler:
@@ -237,22 +237,23 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -
         stream = torch.cuda.current_stream()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         eager_ms, wall_ms = [], []
+        ns = w.num_splits
         with ClockSampler() as clk:
             for _ in range(rounds):
                 for i in range(warmup):
-                    launch(copies, i)
+                    launch(copies, i, ns)
                 torch.cuda.synchronize()
                 t0 = time.perf_counter()
                 ev0.record(stream)
                 for i in range(timed):
-                    launch(copies, i)
+                    launch(copies, i, ns)
                 ev1.record(stream)
                 torch.cuda.synchronize()
                 wall_ms.append((time.perf_counter() - t0) * 1e3 / timed)
                 eager_ms.append(ev0.elapsed_time(ev1) / timed)
         # eager reference outputs of every copy
         for i in range(len(copies)):
-            launch(copies, i)
+            launch(copies, i, ns)
         torch.cuda.synchronize()
         ref = [(o.clone(), None if l is None else l.clone()) for _, o, l in copies]
         graph = torch.cuda.CUDAGraph()
@@ -263,7 +264,7 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -
         torch.cuda.synchronize()
         with torch.cuda.graph(graph):
             for i in range(timed):
-                launch(copies, i)
+                launch(copies, i, ns)
         graph_ms = []
         for _ in range(rounds):
             for _, o, _l in copies:
@@ -278,6 +279,20 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -
                 if not torch.equal(o, ro) or (l is not None and not torch.equal(l, rl)):
                     raise RuntimeError("%s: graph replay differs from the eager result" % name)
         del graph
+        unsplit = None
+        if ns != 1:  # the same call without split-KV, for comparison
+            times = []
+            for _ in range(rounds):
+                for i in range(warmup):
+                    launch(copies, i, 1)
+                torch.cuda.synchronize()
+                ev0.record(stream)
+                for i in range(timed):
+                    launch(copies, i, 1)
+                ev1.record(stream)
+                torch.cuda.synchronize()
+                times.append(ev0.elapsed_time(ev1) / timed)
+            unsplit = min(times)
         best, med = min(eager_ms), statistics.median(eager_ms)
         row = {
             "workload": name,
@@ -294,6 +309,12 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -
             "sclk_samples": len(clk.samples),
             "input_copies": len(copies),
         }
+        if unsplit is not None:
+            va_mod = __import__("varlen_attention_forward_amd")
+            row["num_splits"] = va_mod.auto_num_splits(w.head_dim_qk, w.head_dim_v, w.batch, w.num_heads,
+                                                       w.max_seqlen_q, w.max_seqlen_k) if ns == 0 else ns
+            row["unsplit_kernel_ms_best"] = round(unsplit, 4)
+            row["unsplit_tflops_best"] = round(flops / unsplit / 1e9, 2)
         rows.append(row)
         print(json.dumps(row), flush=True)
     print("| workload | kernel ms best / median | TFLOP/s best / median | % peak | GB/s | graph ms best / median "
@@ -419,7 +440,7 @@ def main() -> int:
         d, out, lse = copies[i % rotate]
         va.varlen_attn_fwd(d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, d.max_seqlen_q, d.max_seqlen_k,
                            softmax_scale=d.softmax_scale, causal=d.causal, window_size=d.window,
-                           out=out, return_lse=lse is not None, lse=lse)
+                           out=out, return_lse=lse is not None, lse=lse, num_splits=w.num_splits)
 
     for i in range(args.warmup):
         step(i)

@@ -41,6 +41,7 @@
 #ifndef VARLEN_ATTN_H
 #define VARLEN_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -116,6 +117,55 @@ int varlen_attn_fwd(const va_tensor* q, const va_tensor* k, const va_tensor* v,
                     int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
                     int32_t causal, int32_t window_left, int32_t window_right,
                     const va_tensor* out, float* lse, void* stream);
+
+/*
+ * varlen_attn_fwd_splitkv -- varlen_attn_fwd with each work unit's key tiles
+ * split into num_splits runs computed by separate workgroups, then combined.
+ * Split-KV prefill as the vLLM MLA-prefill docs page describes it (FA4's
+ * `num_splits` argument in FA4MLAPrefillKernel.dispatch, and
+ * FA4SplitKVCombineKernel: per-split fp32 partial outputs [num_splits,
+ * total_q, H, d_v] and LSEs [num_splits, H, total_q] reduced by a combine
+ * kernel).  It fills the GPU when a call has few query tiles per head but
+ * long key ranges (a chunked prefill's context chunk, long K with short Q).
+ *
+ *   q .. lse, stream   as for varlen_attn_fwd (same checks, same results
+ *                      up to rounding: each split's partial is exact
+ *                      attention over its keys, and the combine is exact)
+ *   num_splits         1 .. 128; 1 is exactly varlen_attn_fwd (workspace
+ *                      unused, may be NULL)
+ *   workspace          device memory of at least
+ *                      varlen_attn_splitkv_workspace_bytes(total_q, H, d_v,
+ *                      num_splits) bytes, 256-byte aligned, owned by the
+ *                      caller; its contents on entry do not matter.  Calls
+ *                      that share a workspace must not overlap.
+ *
+ * Enqueues two kernels on `stream` (the split attention, then the combine)
+ * and returns; no allocation, no synchronisation, graph-capturable.
+ * Returns VA_OK, any varlen_attn_fwd error, VA_ERR_ARG for num_splits out of
+ * range or a workspace below the size, VA_ERR_NULL for a NULL workspace,
+ * VA_ERR_ALIGN for a misaligned one.
+ */
+int varlen_attn_fwd_splitkv(const va_tensor* q, const va_tensor* k, const va_tensor* v,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                            int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                            int32_t causal, int32_t window_left, int32_t window_right,
+                            const va_tensor* out, float* lse, int32_t num_splits, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Workspace bytes varlen_attn_fwd_splitkv needs (0 for num_splits <= 1). Host only. */
+size_t varlen_attn_splitkv_workspace_bytes(int64_t total_q, int32_t num_heads, int32_t head_dim_v,
+                                           int32_t num_splits);
+
+/*
+ * A split count for these sizes: the device's concurrent workgroups over
+ * the call's work units, at most 128 and at most one split per 16 key tiles
+ * (FA4's automatic choice on the vLLM page caps splits the same way, at
+ * num_SMs // total_m_blocks and 128); 1 when the units already fill the
+ * device.  Queries the current device's compute-unit count (a host call, no
+ * synchronisation).  Returns VA_OK, VA_ERR_NULL, VA_ERR_HEADDIM or VA_ERR_ARG.
+ */
+int varlen_attn_num_splits(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch, int32_t num_heads,
+                           int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t* num_splits);
 
 /*
  * varlen_attn_merge -- merge two attention results over disjoint key sets of

@@ -410,6 +410,40 @@ def _merge(a=None, b=None, out=None, lse_a=FAKE, lse_b=FAKE, lse=FAKE):
                                  ctypes.byref(out), ctypes.c_void_p(lse), ctypes.c_void_p(0))
 
 
+def test_splitkv_workspace_bytes():
+    f = pkg.splitkv_workspace_bytes
+    assert f(100, 3, 64, 1) == 0 and f(100, 3, 64, 0) == 0 and f(0, 3, 64, 4) == 0
+    o = 4 * 100 * 3 * 64 * 4
+    assert f(100, 3, 64, 4) == -(-o // 256) * 256 + 4 * 3 * 100 * 4
+    o = 7 * 33 * 5 * 80 * 4
+    assert f(33, 5, 80, 7) == -(-o // 256) * 256 + 7 * 5 * 33 * 4
+
+
+def _split_call(num_splits, ws=FAKE, nbytes=1 << 30):
+    t = _t()
+    return B.raw_fwd_splitkv(t, t, t, FAKE, FAKE, 1, 10, 10, 0.125, 0, -1, -1, t, 0, num_splits, ws, nbytes, 0)
+
+
+def test_splitkv_rejects_bad_arguments():
+    assert _split_call(0) == B.VA_ERR_ARG
+    assert _split_call(129) == B.VA_ERR_ARG
+    assert _split_call(4, ws=0) == B.VA_ERR_NULL
+    assert _split_call(4, ws=FAKE + 16) == B.VA_ERR_ALIGN
+    assert _split_call(4, nbytes=pkg.splitkv_workspace_bytes(10, 2, 64, 4) - 1) == B.VA_ERR_ARG
+    # the plain checks run first
+    t = _t()
+    assert B.raw_fwd_splitkv(t, _t(dim=80), t, FAKE, FAKE, 1, 10, 10, 0.125, 0, -1, -1, t, 0, 4, FAKE, 1 << 30,
+                             0) == B.VA_ERR_SHAPE
+
+
+def test_auto_num_splits():
+    n = pkg.auto_num_splits(128, 128, 1, 16, 512, 32768)
+    assert 1 <= n <= 128
+    assert pkg.auto_num_splits(128, 128, 0, 16, 512, 32768) == 1
+    with pytest.raises(ValueError):
+        pkg.auto_num_splits(96, 96, 1, 16, 512, 32768)
+
+
 def test_merge_rejects_bad_arguments():
     lib = pkg.library()
     t = _t()

@@ -382,6 +382,70 @@ def test_grouped_kv_heads(dims, heads, heads_k, mode):
     assert_parity(out3, None, ref_o, None, what="gqa-nolse")
 
 
+def run_gpu_split(inp, num_splits, out=None, lse_fill=None, return_lse=True):
+    q, k, v = guarded(inp.q), guarded(inp.k), guarded(inp.v)
+    cu_q, cu_k = inp.cu_seqlens_q.to(DEV), inp.cu_seqlens_k.to(DEV)
+    lse = None
+    if return_lse:
+        lse = torch.full((inp.q.shape[1], inp.q.shape[0]), float("nan") if lse_fill is None else lse_fill,
+                         dtype=torch.float32, device=DEV)
+    res = va.varlen_attn_fwd(q, k, v, cu_q, cu_k, inp.max_seqlen_q, inp.max_seqlen_k,
+                             softmax_scale=inp.softmax_scale, causal=inp.causal, window_size=inp.window,
+                             out=out, return_lse=return_lse, lse=lse, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return res if return_lse else (res, None)
+
+
+@pytest.mark.parametrize("dims", DIMS, ids=lambda d: "d%d_%d" % d)
+@pytest.mark.parametrize("mode", ["full", "causal", "window", "causal_window"])
+@pytest.mark.parametrize("splits", [2, 3, 8])
+def test_split_kv(dims, mode, splits):
+    """Split-KV: each unit's key tiles in `splits` runs, combined at the end,
+    against the oracle on ragged segments (q < k chunked-prefill shapes,
+    q > k, a segment with no keys, runs shorter than a tile and empty runs),
+    with and without an LSE; rows outside every segment stay untouched."""
+    causal, window = MODES[mode]
+    lq, lk = [1, 300, 77, 530, 9], [700, 300, 0, 900, 2]
+    seed = zlib.crc32(repr(("split", dims, mode, splits)).encode()) % 1000
+    inp = workloads.make_inputs(lq, lk, 2, dims[0], dims[1], seed=seed, causal=causal, window=window)
+    sentinel = torch.full((inp.q.shape[0] + 40, 2, dims[1]), 3.0, dtype=torch.bfloat16, device=DEV)
+    out, lse = run_gpu_split(inp, splits, out=sentinel[: inp.q.shape[0]])
+    assert torch.all(sentinel[inp.q.shape[0]:] == 3.0)
+    ref_o, ref_lse = oracle_on(inp)
+    assert_parity(out, lse, ref_o, ref_lse, what="split%d/%s/%s" % (splits, dims, mode))
+    out2, _ = run_gpu_split(inp, splits, return_lse=False)
+    assert_parity(out2, None, ref_o, None, what="split%d-nolse" % splits)
+
+
+def test_split_kv_one_split_is_the_plain_call():
+    inp = workloads.make_inputs([300, 77], [500, 77], 3, 128, 128, seed=40, causal=True)
+    a, la = run_gpu(inp)
+    b, lb = run_gpu_split(inp, 1)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_split_kv_rows_outside_segments_untouched():
+    inp = workloads.make_inputs([10, 140], [10, 140], 2, 64, 64, seed=13)
+    inp = workloads.Inputs(**{**inp.__dict__, "q": torch.cat([inp.q, inp.q[:60]]),
+                              "cu_seqlens_q": torch.tensor([0, 10, 150], dtype=torch.int32)})
+    sentinel = torch.full((210, 2, 64), 3.0, dtype=torch.bfloat16, device=DEV)
+    out, lse = run_gpu_split(inp, 4, out=sentinel, lse_fill=5.0)
+    assert torch.all(out[150:] == 3.0) and torch.all(lse[:, 150:] == 5.0)
+    ref_o, ref_lse = oracle_on(inp)
+    assert_parity(out, lse, ref_o, ref_lse, rows=np.arange(150), what="split partial cover")
+
+
+def test_split_kv_auto_count_and_grouped_heads():
+    """The library's split count on a short-query, long-key call (8 heads
+    over 2 KV heads) is > 1, and the result matches the oracle."""
+    inp = workloads.make_inputs([200, 64], [6000, 3000], 8, 128, 128, seed=41, causal=True, num_heads_k=2)
+    n = va.auto_num_splits(128, 128, 2, 8, 200, 6000)
+    assert 1 < n <= 128
+    out, lse = run_gpu_split(inp, 0)
+    ref_o, ref_lse = oracle_on(inp)
+    assert_parity(out, lse, ref_o, ref_lse, what="split auto (%d)" % n)
+
+
 def test_hip_graph_replay_matches_eager():
     """The call enqueues one kernel and nothing else, so it can be captured in a
     HIP graph: three replays, with eager calls between them, reproduce the
@@ -469,11 +533,14 @@ def _sample_rows(inp, n_random, seed=0):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name", ["tiny_varlen_d64", "vit_window256_d80"])
+@pytest.mark.parametrize("name", ["tiny_varlen_d64", "vit_window256_d80", "mla_context_chunk_tp8"])
 def test_workload_full_oracle(name):
     w = workloads.WORKLOADS[name]
     inp = workloads.workload_inputs(w)
-    out, lse = run_gpu(inp, return_lse=w.return_lse)
+    if w.num_splits != 1:
+        out, lse = run_gpu_split(inp, w.num_splits, return_lse=w.return_lse)
+    else:
+        out, lse = run_gpu(inp, return_lse=w.return_lse)
     ref_o, ref_lse = oracle_on(inp)
     e = assert_parity(out, lse, ref_o, ref_lse, what=name)
     print("%s: max|dO| %.3e max|dLSE| %s" % (name, e[0], e[1]))

@@ -9,9 +9,12 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     VaTensor,
     VarlenAttnError,
+    auto_num_splits,
     library,
     plan,
     raw_fwd,
+    raw_fwd_splitkv,
+    splitkv_workspace_bytes,
     status_string,
     tile_range,
     varlen_attn_fwd,
@@ -28,6 +31,9 @@ __all__ = [
     "plan",
     "library",
     "raw_fwd",
+    "raw_fwd_splitkv",
+    "splitkv_workspace_bytes",
+    "auto_num_splits",
     "VaTensor",
     "VarlenAttnError",
     "EXPORTED_SYMBOLS",

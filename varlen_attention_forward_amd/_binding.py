@@ -40,6 +40,9 @@ EXPORTED_SYMBOLS = (
     "varlen_attn_plan",
     "varlen_attn_work_unit",
     "varlen_attn_merge",
+    "varlen_attn_fwd_splitkv",
+    "varlen_attn_splitkv_workspace_bytes",
+    "varlen_attn_num_splits",
 )
 
 
@@ -94,6 +97,14 @@ def library() -> ctypes.CDLL:
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         P(VaTensor), ctypes.c_void_p, ctypes.c_void_p,
     ]
+    lib.varlen_attn_fwd_splitkv.restype = ctypes.c_int
+    lib.varlen_attn_fwd_splitkv.argtypes = lib.varlen_attn_fwd.argtypes[:-1] + [
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.varlen_attn_splitkv_workspace_bytes.restype = ctypes.c_size_t
+    lib.varlen_attn_splitkv_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                        ctypes.c_int32]
+    lib.varlen_attn_num_splits.restype = ctypes.c_int
+    lib.varlen_attn_num_splits.argtypes = [ctypes.c_int32] * 6 + [P(ctypes.c_int32)]
     lib.varlen_attn_merge.restype = ctypes.c_int
     lib.varlen_attn_merge.argtypes = [P(VaTensor), ctypes.c_void_p, P(VaTensor), ctypes.c_void_p,
                                       P(VaTensor), ctypes.c_void_p, ctypes.c_void_p]
@@ -184,6 +195,36 @@ def raw_fwd(q: VaTensor, k: VaTensor, v: VaTensor, cu_q_ptr: int, cu_k_ptr: int,
     )
 
 
+def raw_fwd_splitkv(q: VaTensor, k: VaTensor, v: VaTensor, cu_q_ptr: int, cu_k_ptr: int, batch: int,
+                    max_seqlen_q: int, max_seqlen_k: int, softmax_scale: float, causal: int,
+                    window_left: int, window_right: int, out: VaTensor, lse_ptr: int, num_splits: int,
+                    workspace_ptr: int, workspace_bytes: int, stream: int) -> int:
+    """The split-KV C entry point with plain descriptors; returns the status code."""
+    return library().varlen_attn_fwd_splitkv(
+        ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+        ctypes.c_void_p(cu_q_ptr), ctypes.c_void_p(cu_k_ptr), int(batch),
+        int(max_seqlen_q), int(max_seqlen_k), float(softmax_scale),
+        int(causal), int(window_left), int(window_right),
+        ctypes.byref(out), ctypes.c_void_p(lse_ptr), int(num_splits), ctypes.c_void_p(workspace_ptr),
+        int(workspace_bytes), ctypes.c_void_p(stream),
+    )
+
+
+def splitkv_workspace_bytes(total_q: int, num_heads: int, head_dim_v: int, num_splits: int) -> int:
+    """Workspace bytes ``varlen_attn_fwd(..., num_splits=S)`` needs (host call)."""
+    return int(library().varlen_attn_splitkv_workspace_bytes(total_q, num_heads, head_dim_v, num_splits))
+
+
+def auto_num_splits(head_dim_qk: int, head_dim_v: int, batch: int, num_heads: int, max_seqlen_q: int,
+                    max_seqlen_k: int) -> int:
+    """The library's split count for these sizes (1: the units already fill the GPU)."""
+    n = ctypes.c_int32()
+    st = library().varlen_attn_num_splits(head_dim_qk, head_dim_v, batch, num_heads, max_seqlen_q, max_seqlen_k,
+                                          ctypes.byref(n))
+    _raise_for(st)
+    return n.value
+
+
 def _desc(t, name: str) -> VaTensor:
     import torch
 
@@ -216,6 +257,7 @@ def varlen_attn_fwd(
     out=None,
     return_lse: bool = False,
     lse=None,
+    num_splits: int = 1,
 ):
     """Fused varlen attention forward on the current HIP stream.
 
@@ -225,6 +267,9 @@ def varlen_attn_fwd(
     Returns ``out`` [total_q, H, d_v] bf16, or ``(out, lse)`` with lse fp32
     [H, total_q] when ``return_lse``.  ``softmax_scale`` defaults to
     d_qk^-0.5.  ``window_size`` is ``(left, right)``, -1 for unbounded.
+    ``num_splits`` splits every work unit's keys into that many runs (split-KV,
+    combined at the end; the workspace is allocated here with torch); 0 lets
+    the library choose (1 when the call already fills the GPU).
     """
     import torch
 
@@ -249,12 +294,25 @@ def varlen_attn_fwd(
             raise ValueError("lse must be a contiguous float32 GPU tensor of shape [H, total_q]")
     wl, wr = window_size
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = raw_fwd(
-        _desc(q, "q"), _desc(k, "k"), _desc(v, "v"),
-        cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), batch,
-        max_seqlen_q, max_seqlen_k, softmax_scale, int(bool(causal)), wl, wr,
-        _desc(out, "out"), lse.data_ptr() if lse is not None else 0, stream,
-    )
+    if num_splits == 0:
+        num_splits = auto_num_splits(d_qk, d_v, batch, H, max_seqlen_q, max_seqlen_k)
+    if num_splits == 1:
+        st = raw_fwd(
+            _desc(q, "q"), _desc(k, "k"), _desc(v, "v"),
+            cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), batch,
+            max_seqlen_q, max_seqlen_k, softmax_scale, int(bool(causal)), wl, wr,
+            _desc(out, "out"), lse.data_ptr() if lse is not None else 0, stream,
+        )
+    else:
+        nbytes = splitkv_workspace_bytes(total_q, H, d_v, num_splits)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+        st = raw_fwd_splitkv(
+            _desc(q, "q"), _desc(k, "k"), _desc(v, "v"),
+            cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), batch,
+            max_seqlen_q, max_seqlen_k, softmax_scale, int(bool(causal)), wl, wr,
+            _desc(out, "out"), lse.data_ptr() if lse is not None else 0, num_splits,
+            ws.data_ptr(), nbytes, stream,
+        )
     _raise_for(st)
     if return_lse:
         return out, lse

@@ -105,6 +105,92 @@ __global__ __launch_bounds__(256) void merge_states(Params p) {
   if (c == 0 && p.l != nullptr) p.l[(int64_t)h * p.rows + i] = lse;
 }
 
+// Combine of split-KV partials (varlen_attn_fwd_splitkv).  The attention
+// kernel leaves, per split s, the normalised fp32 output O_s [S, rows, H, d]
+// and its natural-log LSE L_s [S, H, rows] over the split's keys (-inf where
+// a row saw none of them); the combine over the S disjoint key sets is the
+// merge above taken S ways: L = m + ln sum_s e^(L_s - m) with m = max_s L_s,
+// O = sum_s e^(L_s - L) O_s, out = bf16(O).  Only rows of some segment,
+// [cu_seqlens_q[0], cu_seqlens_q[batch]), are written: the others were not
+// computed and are left untouched, as the unsplit forward leaves them.  A
+// group of G lanes (G the power of two >= d / 4) owns one (row, head); lane
+// c reads the 16 bytes of columns 4c .. 4c + 3 of every split.
+struct CombineParams {
+  const float* part_o;
+  const float* part_lse;
+  uint16_t* o;
+  float* l;
+  const int32_t* cu_q;
+  int64_t o_row, o_head;  // elements
+  int64_t rows;
+  int32_t heads, dim, splits, batch;
+  int32_t lane_shift;
+};
+
+__global__ __launch_bounds__(256) void combine_splits(CombineParams p) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t pair = t >> p.lane_shift;
+  const int c = (int)(t & ((1 << p.lane_shift) - 1));
+  if (pair >= p.rows * p.heads) return;
+  const int64_t i = pair / p.heads;
+  const int h = (int)(pair - i * p.heads);
+  if (i < p.cu_q[0] || i >= p.cu_q[p.batch]) return;
+  const int64_t plane = p.rows * p.heads;  // (row, head) pairs per split
+  float m = -INFINITY;
+  for (int s = 0; s < p.splits; ++s) m = fmaxf(m, p.part_lse[(int64_t)s * plane + (int64_t)h * p.rows + i]);
+  float sum = 0.f;
+  if (m != -INFINITY)
+    for (int s = 0; s < p.splits; ++s) sum += expf(p.part_lse[(int64_t)s * plane + (int64_t)h * p.rows + i] - m);
+  if (4 * c < p.dim) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (m != -INFINITY) {
+      const float inv = 1.f / sum;
+      for (int s = 0; s < p.splits; ++s) {
+        const float w = expf(p.part_lse[(int64_t)s * plane + (int64_t)h * p.rows + i] - m) * inv;
+        // A split with weight 0 (no key, or negligible) is skipped, not
+        // scaled: its O is never read into the sum.
+        if (w > 0.f) {
+          const f32x4 x = __builtin_nontemporal_load(
+              (const f32x4*)(p.part_o + ((int64_t)s * plane + i * p.heads + h) * p.dim + 4 * c));
+          acc += w * x;
+        }
+      }
+    }
+    const u32x2 r = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    *(u32x2*)(p.o + i * p.o_row + h * p.o_head + 4 * c) = r;
+  }
+  if (c == 0 && p.l != nullptr) p.l[(int64_t)h * p.rows + i] = m != -INFINITY ? m + logf(sum) : -INFINITY;
+}
+
+int launch_combine(const float* part_o, const float* part_lse, int32_t num_splits, int64_t total_q, int32_t heads,
+                   int32_t dim, const int32_t* cu_seqlens_q, int32_t batch, const va_tensor* out, float* lse,
+                   void* stream) {
+  CombineParams p;
+  p.part_o = part_o;
+  p.part_lse = part_lse;
+  p.o = (uint16_t*)out->data;
+  p.l = lse;
+  p.cu_q = cu_seqlens_q;
+  p.o_row = out->row_stride;
+  p.o_head = out->head_stride;
+  p.rows = total_q;
+  p.heads = heads;
+  p.dim = dim;
+  p.splits = num_splits;
+  p.batch = batch;
+  int shift = 0;
+  while ((1 << shift) < (dim + 3) / 4) ++shift;
+  p.lane_shift = shift;
+  const int64_t grid = ((total_q * heads << shift) + 255) / 256;
+  if (grid > INT32_MAX) return VA_ERR_SHAPE;
+  void* args[] = {&p};
+  const hipError_t err =
+      hipLaunchKernel((const void*)&combine_splits, dim3((unsigned)grid), dim3(256), args, 0, (hipStream_t)stream);
+  return err == hipSuccess ? VA_OK : VA_ERR_LAUNCH;
+}
+
 static int check(const va_tensor* t, int64_t rows, int32_t heads, int32_t dim) {
   if (t->rows != rows || t->heads != heads || t->dim != dim) return VA_ERR_SHAPE;
   if (t->row_stride <= 0 || t->head_stride <= 0) return VA_ERR_STRIDE;

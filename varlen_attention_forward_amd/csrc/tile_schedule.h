@@ -90,6 +90,22 @@ VA_HD TileRange tile_range(int64_t Lq, int64_t Lk, int64_t r0, int64_t r1, int c
   return t;
 }
 
+// Split-KV: the split-th of num_splits runs of ceil(n / num_splits) tiles of
+// a visit range of n tiles (the last runs may be short or empty), with its
+// unmasked sub-range.  num_splits == 1 returns t unchanged.
+VA_HD TileRange split_range(TileRange t, int split, int num_splits) {
+  if (num_splits <= 1) return t;
+  const int32_t n = t.kt_end - t.kt_begin;
+  const int32_t per = (n + num_splits - 1) / num_splits;
+  TileRange r;
+  r.kt_begin = (int32_t)imin64(t.kt_begin + (int64_t)split * per, t.kt_end);
+  r.kt_end = (int32_t)imin64((int64_t)r.kt_begin + per, t.kt_end);
+  r.full_begin = (int32_t)imin64(imax64(t.full_begin, r.kt_begin), r.kt_end);
+  r.full_end = (int32_t)imin64(imax64(t.full_end, r.kt_begin), r.kt_end);
+  if (r.full_begin >= r.full_end) r.full_begin = r.full_end = r.kt_begin;
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Workgroup -> (segment, head, q-tile).
 //

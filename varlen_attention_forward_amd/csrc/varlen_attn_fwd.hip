@@ -70,6 +70,13 @@ struct Params {
   int64_t total_q;
   int32_t batch, heads, n_qt;
   int32_t heads_k;  // KV heads; heads is a multiple of it
+  // Split-KV: with num_splits > 1 the grid holds num_splits copies of the
+  // n_units work units; copy s takes the s-th of num_splits equal runs of
+  // each unit's key tiles and writes a normalised fp32 partial O and its
+  // LSE instead of out / lse (combined by combine_splits).
+  int32_t num_splits, n_units;
+  float* part_o;    // [num_splits, total_q, heads, d_v]
+  float* part_lse;  // [num_splits, heads, total_q]
   int32_t causal, wl, wr;
   float scale_log2;  // softmax_scale * log2(e)
 };
@@ -163,8 +170,7 @@ struct BlockWork {
   int q0, lq, k0, lk;  // the segment's first query / key row and lengths
 };
 
-__device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int block_m) {
-  const int64_t w = blockIdx.x;
+__device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int block_m, int64_t w) {
   BlockWork r;
   if (p.batch <= kLptMaxBatch) {
     int cq0 = 0, cq1 = 0, ck0 = 0, ck1 = -1;
@@ -178,7 +184,7 @@ __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int b
     const int lq0 = __builtin_amdgcn_readfirstlane(lq), lk0 = __builtin_amdgcn_readfirstlane(lk);
     if (__ballot(lane < p.batch && (lq != lq0 || lk != lk0)) != 0) {
       const int x = (int)(w & 7);
-      const int k = (int)snake_quads((uint32_t)(w >> 3), gridDim.x / 8u);
+      const int k = (int)snake_quads((uint32_t)(w >> 3), (uint32_t)p.n_units / 8u);
       int rank = 0;
       for (int j = 0; j < p.batch; ++j) {
         const int kj = __builtin_amdgcn_readlane(lk, j);
@@ -362,14 +368,18 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  const BlockWork bw = block_work(p, lane, C::BM);
+  // Split-KV copy of the work units this workgroup belongs to (0 without split).
+  const int split = (int)(blockIdx.x / (uint32_t)p.n_units);
+  const BlockWork bw = block_work(p, lane, C::BM, (int64_t)blockIdx.x - (int64_t)split * p.n_units);
   if (!bw.u.valid) return;
   const int h = bw.u.h, qt = bw.u.qt;
   const int q0 = bw.q0, Lq = bw.lq, k0 = bw.k0, Lk = bw.lk;
   const int r0 = qt * C::BM;
   if (r0 >= Lq) return;
   const int r1 = min(r0 + C::BM, Lq);
-  const TileRange tr = tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN);
+  // The key tiles this workgroup visits: all its rows see, or with split-KV
+  // the split-th of num_splits runs of them (possibly empty).
+  const TileRange tr = split_range(tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN), split, p.num_splits);
   const int ntiles = tr.kt_end - tr.kt_begin;
   // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------
   bf16x8 qf[2][C::KC];
@@ -469,9 +479,11 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   int w_end = 0, w_full_begin = 0, w_full_end = 0;  // relative to tr.kt_begin
   if (wrow0 < r1) {
     const TileRange wt = tile_range(Lq, Lk, wrow0, min(wrow0 + kRowsPerWave, r1), p.causal, p.wl, p.wr, kBN);
-    w_end = wt.kt_end - tr.kt_begin;
-    w_full_begin = wt.full_begin - tr.kt_begin;
-    w_full_end = wt.full_end - tr.kt_begin;
+    // (clamped to this workgroup's tiles, which with split-KV are a run of
+    // the rows' tiles)
+    w_end = min(max(wt.kt_end, tr.kt_begin), tr.kt_end) - tr.kt_begin;
+    w_full_begin = min(max(wt.full_begin, tr.kt_begin), tr.kt_end) - tr.kt_begin;
+    w_full_end = min(max(wt.full_end, tr.kt_begin), tr.kt_end) - tr.kt_begin;
   }
   const bool active = w_end > 0;
 
@@ -844,6 +856,34 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   // With SUM_BY_MFMA the row sum sits in column d_v of the accumulator:
   // dv block VB - 1, register 4 * ((d_v % 32) / 8), lanes 0-31.
   constexpr int kSumReg = 4 * ((DV % 32) / 8);
+  if (p.num_splits > 1) {
+    // Split-KV partial: O = acc / l in fp32 (lane (row, g) holds d_v 8 jj +
+    // 4 g .. + 3 of each 32-wide block: one 16-byte store each) and the LSE of
+    // this split's keys (-inf where a row saw none of them).
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float l = SUM_BY_MFMA ? from_lower_half(acc[C::VB - 1][qb][kSumReg]) : xhalf_sum(l_run[qb]);
+      const int row = wrow0 + 32 * qb + l32;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      float* dst = p.part_o + (((int64_t)split * p.total_q + q0 + row) * p.heads + h) * DV;
+#pragma unroll
+      for (int vb = 0; vb < C::VB; ++vb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int dv = vb * 32 + 8 * jj + 4 * g;
+          if (row < r1 && dv < DV) {
+            const f32x16& a = acc[vb][qb];
+            typedef float f32x4 __attribute__((ext_vector_type(4)));
+            const f32x4 o4 = {a[4 * jj] * inv, a[4 * jj + 1] * inv, a[4 * jj + 2] * inv, a[4 * jj + 3] * inv};
+            *(f32x4*)(dst + dv) = o4;
+          }
+        }
+      if (row < r1 && g == 0)
+        p.part_lse[((int64_t)split * p.heads + h) * p.total_q + q0 + row] =
+            l > 0.f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
   // Lane (row, g) holds d_v 8 jj + 4 g .. + 3 of its row for jj = 0..3 of
   // each 32-wide block.  Swapping halves with lane row ^ 32 over a pair of
   // chunks (jj, jj + 1) leaves lane g with the 8 contiguous values of chunk
@@ -1019,12 +1059,15 @@ extern "C" int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t
   return VA_OK;
 }
 
-extern "C" int varlen_attn_fwd(const va_tensor* q, const va_tensor* k, const va_tensor* v,
-                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
-                               int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
-                               int32_t causal, int32_t window_left, int32_t window_right,
-                               const va_tensor* out, float* lse, void* stream) {
-  using namespace va;
+namespace va {
+
+// Validation shared by the entry points; fills the launch parameters.
+// Returns VA_OK (and *launch = false when there is nothing to launch).
+static int prepare(const va_tensor* q, const va_tensor* k, const va_tensor* v, const int32_t* cu_seqlens_q,
+                   const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                   float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
+                   const va_tensor* out, float* lse, Params& p, bool& launch) {
+  launch = false;
   if (!q || !k || !v || !out) return VA_ERR_NULL;
   if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return VA_ERR_ARG;
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return VA_ERR_ARG;
@@ -1047,12 +1090,6 @@ extern "C" int varlen_attn_fwd(const va_tensor* q, const va_tensor* k, const va_
   if (batch == 0 || max_seqlen_q == 0 || q->rows == 0) return VA_OK;
   if (!cu_seqlens_q || !cu_seqlens_k) return VA_ERR_NULL;
 
-  const Variant var = variant_for(q->dim, v->dim, max_seqlen_q, lse != nullptr);
-  const int64_t n_qt = ((int64_t)max_seqlen_q + var.block_m - 1) / var.block_m;
-  const int64_t grid = grid_blocks(batch, q->heads, n_qt);
-  if (grid > INT32_MAX) return VA_ERR_SHAPE;
-
-  Params p;
   p.q = (const uint16_t*)q->data;
   p.k = (const uint16_t*)k->data;
   p.v = (const uint16_t*)v->data;
@@ -1072,14 +1109,117 @@ extern "C" int varlen_attn_fwd(const va_tensor* q, const va_tensor* k, const va_
   p.batch = batch;
   p.heads = q->heads;
   p.heads_k = k->heads;
-  p.n_qt = (int32_t)n_qt;
   p.causal = causal;
   p.wl = window_left;
   p.wr = window_right;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.num_splits = 1;
+  p.part_o = nullptr;
+  p.part_lse = nullptr;
+  (void)max_seqlen_k;
+  launch = true;
+  return VA_OK;
+}
 
+// One launch of the attention kernel over num_splits copies of the work units.
+static int launch_attention(Params& p, int32_t head_dim_qk, int32_t head_dim_v, int32_t max_seqlen_q,
+                            bool fp32_row_sum, void* stream) {
+  const Variant var = variant_for(head_dim_qk, head_dim_v, max_seqlen_q, fp32_row_sum);
+  const int64_t n_qt = ((int64_t)max_seqlen_q + var.block_m - 1) / var.block_m;
+  const int64_t units = grid_blocks(p.batch, p.heads, n_qt);
+  const int64_t grid = units * p.num_splits;
+  if (grid > INT32_MAX) return VA_ERR_SHAPE;
+  p.n_qt = (int32_t)n_qt;
+  p.n_units = (int32_t)units;
   void* args[] = {&p};
   const hipError_t err = hipLaunchKernel(var.fn, dim3((unsigned)grid), dim3(var.threads), args, 0,
                                          (hipStream_t)stream);
   return err == hipSuccess ? VA_OK : VA_ERR_LAUNCH;
+}
+
+}  // namespace va
+
+extern "C" int varlen_attn_fwd(const va_tensor* q, const va_tensor* k, const va_tensor* v,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                               int32_t causal, int32_t window_left, int32_t window_right,
+                               const va_tensor* out, float* lse, void* stream) {
+  va::Params p;
+  bool launch = false;
+  const int st = va::prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k, softmax_scale,
+                             causal, window_left, window_right, out, lse, p, launch);
+  if (st != VA_OK || !launch) return st;
+  return va::launch_attention(p, q->dim, v->dim, max_seqlen_q, lse != nullptr, stream);
+}
+
+namespace va {
+constexpr int kMaxSplits = 128;
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+}  // namespace va
+
+extern "C" size_t varlen_attn_splitkv_workspace_bytes(int64_t total_q, int32_t num_heads, int32_t head_dim_v,
+                                                      int32_t num_splits) {
+  if (total_q <= 0 || num_heads <= 0 || head_dim_v <= 0 || num_splits <= 1) return 0;
+  const size_t n = (size_t)num_splits * (size_t)total_q * (size_t)num_heads;
+  return va::align256(n * (size_t)head_dim_v * sizeof(float)) + n * sizeof(float);
+}
+
+extern "C" int varlen_attn_num_splits(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch, int32_t num_heads,
+                                      int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t* num_splits) {
+  if (!num_splits) return VA_ERR_NULL;
+  if (!va::supported_dims(head_dim_qk, head_dim_v)) return VA_ERR_HEADDIM;
+  if (batch < 0 || num_heads <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return VA_ERR_ARG;
+  *num_splits = 1;
+  if (batch == 0 || max_seqlen_q == 0 || max_seqlen_k == 0) return VA_OK;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return VA_OK;
+  // The work units a launch has (padding included) against the workgroups
+  // the device holds at once; each split keeps at least 16 key tiles.
+  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, max_seqlen_q, true);
+  const int64_t n_qt = ((int64_t)max_seqlen_q + var.block_m - 1) / var.block_m;
+  const int64_t units = va::grid_blocks(batch, num_heads, n_qt);
+  const int64_t slots = (int64_t)cus * (var.lds_bytes <= 80 * 1024 ? 2 : 1);
+  const int64_t by_tiles = ((int64_t)max_seqlen_k + 16 * var.block_n - 1) / (16 * var.block_n);
+  int64_t s = slots / units;
+  s = s < by_tiles ? s : by_tiles;
+  s = s < va::kMaxSplits ? s : va::kMaxSplits;
+  *num_splits = (int32_t)(s > 1 ? s : 1);
+  return VA_OK;
+}
+
+namespace va_merge {
+int launch_combine(const float* part_o, const float* part_lse, int32_t num_splits, int64_t total_q, int32_t heads,
+                   int32_t dim, const int32_t* cu_seqlens_q, int32_t batch, const va_tensor* out, float* lse,
+                   void* stream);
+}
+
+extern "C" int varlen_attn_fwd_splitkv(const va_tensor* q, const va_tensor* k, const va_tensor* v,
+                                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                                       int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                                       int32_t causal, int32_t window_left, int32_t window_right,
+                                       const va_tensor* out, float* lse, int32_t num_splits, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (num_splits < 1 || num_splits > va::kMaxSplits) return VA_ERR_ARG;
+  va::Params p;
+  bool launch = false;
+  int st = va::prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k, softmax_scale,
+                       causal, window_left, window_right, out, lse, p, launch);
+  if (st != VA_OK) return st;
+  if (num_splits == 1) return launch ? va::launch_attention(p, q->dim, v->dim, max_seqlen_q, lse != nullptr, stream)
+                                     : VA_OK;
+  const size_t need = varlen_attn_splitkv_workspace_bytes(q->rows, q->heads, v->dim, num_splits);
+  if (!launch) return VA_OK;
+  if (!workspace) return VA_ERR_NULL;
+  if (((uintptr_t)workspace & 255u) != 0) return VA_ERR_ALIGN;
+  if (workspace_bytes < need) return VA_ERR_ARG;
+  p.num_splits = num_splits;
+  p.part_o = (float*)workspace;
+  p.part_lse = (float*)((char*)workspace +
+                        va::align256((size_t)num_splits * (size_t)q->rows * (size_t)q->heads * (size_t)v->dim * 4));
+  // The partials' LSEs need the fp32 row sum, whether or not an LSE is returned.
+  if ((st = va::launch_attention(p, q->dim, v->dim, max_seqlen_q, true, stream)) != VA_OK) return st;
+  return va_merge::launch_combine(p.part_o, p.part_lse, num_splits, q->rows, q->heads, v->dim, cu_seqlens_q, batch,
+                                  out, lse, stream);
 }

@@ -51,6 +51,7 @@ class Workload:
     return_lse: bool = True
     softmax_scale: Optional[float] = None
     description: str = ""
+    num_splits: int = 1  # split-KV runs per work unit; 0: the library chooses
 
     @property
     def batch(self) -> int:
@@ -149,6 +150,20 @@ def _named_workloads() -> dict:
             description="MLA-style causal prefill, 4 x 4096 tokens, 128 heads, "
             "qk dim 192 (128 nope + 64 rope), v dim 128, LSE returned",
         ),
+        Workload(
+            name="mla_context_chunk_tp8",
+            seed=6,
+            seqlens_q=(512,),
+            seqlens_k=(16384,),
+            num_heads=16,
+            head_dim_qk=192,
+            head_dim_v=128,
+            causal=False,
+            num_splits=0,
+            description="MLA chunked-prefill context chunk at 16 heads per GPU (the MLA heads over 8 "
+            "GPUs): 512 new tokens over a 16384-token context chunk, non-causal, qk dim 192, v dim "
+            "128, LSE returned; split-KV with the library's split count",
+        ),
     ]
     return {w.name: w for w in ws}
 
@@ -160,6 +175,7 @@ WORKLOAD_ORDER = (
     "vit_window256_d80",
     "vit_long65536_d128",
     "mla_causal_192_128",
+    "mla_context_chunk_tp8",
 )
 
 

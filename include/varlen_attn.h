@@ -230,7 +230,10 @@ int varlen_attn_tile_range(int32_t seqlen_q, int32_t seqlen_k, int32_t row_begin
  * query rows, see varlen_attn_plan) it owns, or -1 in all three for a
  * workgroup that exits at once.  Segments of different lengths (at most 64
  * of them) are dealt longest key length first; otherwise in packing order;
- * either way every odd quad of each XCD's dispatch order is reversed.  With
+ * either way every odd quad of each XCD's dispatch order is reversed.  When
+ * short segments share workgroups (va_plan.segments_per_block P > 1, every
+ * segment at most 128 queries), workgroup `block` owns segments
+ * [segment, segment + P) (those that exist), their q-tile 0.  With
  * num_heads_k KV heads (num_heads a multiple of it) the query heads of one
  * KV head are dealt to the same XCD where the head counts allow.
  * Returns VA_OK, VA_ERR_NULL, VA_ERR_HEADDIM, or VA_ERR_ARG for a block
@@ -250,6 +253,8 @@ typedef struct va_plan {
   int32_t lds_bytes;     /* LDS per workgroup */
   int64_t grid;          /* workgroups launched (some exit at once on short segments) */
   const char* kernel;    /* kernel name ("attn_fwd_wide"); block_m and threads give its launch shape */
+  int32_t segments_per_block; /* 1, or 2 / 4 consecutive short segments per workgroup (max_seqlen_q
+                                 <= 128 / <= 64), one or two waves each */
 } va_plan;
 
 int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch, int32_t num_heads,

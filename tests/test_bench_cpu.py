@@ -38,6 +38,7 @@ def test_visible_pairs_brute_force(lq, lk, causal, window):
 @pytest.mark.parametrize("name,gflop", [
     ("tiny_varlen_d64", 0.2852), ("vit_full_d80", 320.82), ("vit_window256_d80", 12.08),
     ("vit_long65536_d128", 35184.4), ("mla_causal_192_128", 2749.45), ("mla_context_chunk_tp8", 85.899),
+    ("vit_window64_d80", 14.680),
 ])
 def test_algorithmic_flops(name, gflop):
     """H x visible pairs x 2 (d_qk + d_v), against the figures worked out by hand
@@ -51,6 +52,7 @@ def test_roofline_bound_follows_the_ridge():
     bounds = {n: bench.algorithmic_flops(w) / bench.algorithmic_bytes(w) >= bench.RIDGE_FLOP_PER_BYTE
               for n, w in workloads.WORKLOADS.items()}
     assert bounds == {"tiny_varlen_d64": False, "vit_full_d80": True, "vit_window256_d80": False,
+                      "vit_window64_d80": False,
                       "vit_long65536_d128": True, "mla_causal_192_128": True, "mla_context_chunk_tp8": True}
 
 

@@ -277,7 +277,9 @@ def _ragged(seed, batch, lo, hi):
     ([4096] * 8, [4096] * 8, 16, 0, (80, 80)),            # alike: packing order
     ([256] * 36, [256] * 36, 16, 0, (80, 80)),
     ([65536], [65536], 16, 0, (128, 128)),
-    ([1, 1], [1, 1], 1, 0, (72, 72)),
+    ([1, 1], [1, 1], 1, 0, (72, 72)),                     # short: four segments per workgroup
+    ([64] * 9, [80] * 9, 3, 1, (64, 64)),                 # four 64-query segments per workgroup
+    ([100, 3, 128, 0, 77], [500, 3, 9, 0, 77], 5, 0, (192, 128)),  # two per workgroup
     ([576, 1024, 2304, 4096, 1024, 576, 4096, 2304], None, 16, 0, (80, 80)),  # ragged: longest first
     ([700, 0, 300, 1], [700, 5, 0, 1], 5, 1, (64, 64)),
     ([3000, 100, 2000, 4096], None, 128, 1, (192, 128)),
@@ -290,6 +292,22 @@ def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
     batch, max_q = len(lq), max(lq)
     p = pkg.plan(dims[0], dims[1], batch, heads, max_q, max(lk), causal)
     bm = p["block_m"]
+    pack = p["segments_per_block"]
+    assert pack == (4 if max_q <= 64 else 2 if max_q <= 128 else 1)
+    if pack > 1:
+        # short segments: block owns segments [b, b + pack) of one head, q-tile 0
+        seen = {}
+        for blk in range(p["grid"]):
+            b, h, qt = pkg.work_unit(blk, heads, dims[0], dims[1], lq, lk, causal)
+            if b < 0:
+                continue
+            assert qt == 0 and b % pack == 0
+            for s_ in range(b, min(b + pack, batch)):
+                assert (s_, h) not in seen
+                seen[(s_, h)] = blk
+            assert (b // pack * heads + h) % 8 == blk % 8
+        assert set(seen) == {(b, h) for b in range(batch) for h in range(heads)}
+        return
     n_qt = -(-max_q // bm)
     longest_first = batch <= 64 and len(set(zip(lq, lk))) > 1
     # tiles each segment must get: its own q-tiles when dealt longest first,

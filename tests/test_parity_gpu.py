@@ -446,6 +446,45 @@ def test_split_kv_auto_count_and_grouped_heads():
     assert_parity(out, lse, ref_o, ref_lse, what="split auto (%d)" % n)
 
 
+@pytest.mark.parametrize("dims", DIMS, ids=lambda d: "d%d_%d" % d)
+@pytest.mark.parametrize("mode", ["full", "causal", "window", "left_only"])
+@pytest.mark.parametrize("lens", ["le64", "le128", "q_lt_k"])
+def test_packed_short_segments(dims, mode, lens):
+    """Short segments share workgroups (four per workgroup when every segment
+    has at most 64 queries, two when at most 128), each wave or pair of waves
+    on its own segment whose keys start anywhere inside the workgroup's key
+    tiles.  Against the oracle with ragged lengths, empty segments, a
+    partial last group and q < k, with and without an LSE; rows outside
+    every segment stay untouched."""
+    causal, window = MODES[mode]
+    lq, lk = {
+        "le64": ([1, 64, 0, 37, 64, 5, 63, 2, 50], None),
+        "le128": ([128, 1, 65, 100, 0, 127, 3], None),
+        "q_lt_k": ([40, 64, 1, 17, 64], [300, 64, 90, 0, 77]),
+    }[lens]
+    lk = lq if lk is None else lk
+    seed = zlib.crc32(repr(("packed", dims, mode, lens)).encode()) % 1000
+    inp = workloads.make_inputs(lq, lk, 3, dims[0], dims[1], seed=seed, causal=causal, window=window)
+    assert va.plan(dims[0], dims[1], len(lq), 3, max(lq), max(lk), causal)["segments_per_block"] == (
+        4 if max(lq) <= 64 else 2)
+    sentinel = torch.full((inp.q.shape[0] + 30, 3, dims[1]), 3.0, dtype=torch.bfloat16, device=DEV)
+    out, lse = run_gpu(inp, out=sentinel[: inp.q.shape[0]])
+    assert torch.all(sentinel[inp.q.shape[0]:] == 3.0)
+    ref_o, ref_lse = oracle_on(inp)
+    assert_parity(out, lse, ref_o, ref_lse, what="packed/%s/%s/%s" % (dims, mode, lens))
+    out2, _ = run_gpu(inp, return_lse=False)
+    assert_parity(out2, None, ref_o, None, what="packed-nolse")
+
+
+def test_packed_short_segments_with_split_kv_and_grouped_heads():
+    inp = workloads.make_inputs([64, 30, 64, 1, 64], [2000, 30, 700, 5, 64], 8, 128, 128, seed=42, causal=True,
+                                num_heads_k=2)
+    ref_o, ref_lse = oracle_on(inp)
+    for splits in (1, 4):
+        out, lse = run_gpu_split(inp, splits)
+        assert_parity(out, lse, ref_o, ref_lse, what="packed split %d" % splits)
+
+
 def test_hip_graph_replay_matches_eager():
     """The call enqueues one kernel and nothing else, so it can be captured in a
     HIP graph: three replays, with eager calls between them, reproduce the
@@ -533,7 +572,7 @@ def _sample_rows(inp, n_random, seed=0):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name", ["tiny_varlen_d64", "vit_window256_d80", "mla_context_chunk_tp8"])
+@pytest.mark.parametrize("name", ["tiny_varlen_d64", "vit_window256_d80", "vit_window64_d80", "mla_context_chunk_tp8"])
 def test_workload_full_oracle(name):
     w = workloads.WORKLOADS[name]
     inp = workloads.workload_inputs(w)

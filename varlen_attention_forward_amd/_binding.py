@@ -65,6 +65,7 @@ class VaPlan(ctypes.Structure):
         ("lds_bytes", ctypes.c_int32),
         ("grid", ctypes.c_int64),
         ("kernel", ctypes.c_char_p),
+        ("segments_per_block", ctypes.c_int32),
     ]
 
 
@@ -179,6 +180,7 @@ def plan(head_dim_qk, head_dim_v, batch, num_heads, max_seqlen_q, max_seqlen_k, 
         "lds_bytes": pl.lds_bytes,
         "grid": pl.grid,
         "kernel": pl.kernel.decode(),
+        "segments_per_block": pl.segments_per_block,
     }
 
 

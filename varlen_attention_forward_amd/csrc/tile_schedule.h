@@ -55,9 +55,11 @@ struct TileRange {
   int32_t full_begin, full_end;  // tiles that need no mask (subset of the above)
 };
 
-// Schedule for rows [r0, r1) (0 <= r0 < r1 <= Lq) and key tiles of bn keys.
+// Schedule for rows [r0, r1) (0 <= r0 < r1 <= Lq) and key tiles of bn keys,
+// the segment's keys starting at key key_off of the tiled range (0 unless
+// several short segments share one workgroup's keys).
 VA_HD TileRange tile_range(int64_t Lq, int64_t Lk, int64_t r0, int64_t r1, int causal, int wl,
-                           int wr, int bn) {
+                           int wr, int bn, int64_t key_off = 0) {
   TileRange t;
   t.kt_begin = t.kt_end = t.full_begin = t.full_end = 0;
   if (Lk <= 0 || r1 <= r0) return t;
@@ -69,15 +71,15 @@ VA_HD TileRange tile_range(int64_t Lq, int64_t Lk, int64_t r0, int64_t r1, int c
   if (right_bounded) first = imax64(first, -right_reach - off);
   if (wl >= 0) last = imin64(last, Lk - 1 + wl - off);
   if (first > last) return t;
-  const int64_t lo_first = row_bounds(first, Lq, Lk, causal, wl, wr).lo;
-  const int64_t hi_last = row_bounds(last, Lq, Lk, causal, wl, wr).hi;
+  const int64_t lo_first = key_off + row_bounds(first, Lq, Lk, causal, wl, wr).lo;
+  const int64_t hi_last = key_off + row_bounds(last, Lq, Lk, causal, wl, wr).hi;
   t.kt_begin = (int32_t)(lo_first / bn);
   t.kt_end = (int32_t)(hi_last / bn + 1);
   // A tile needs no mask when every row of the block sees all of it: the
   // largest lo (last row) is <= the tile start and the smallest hi (first
   // row) is >= the tile end.  Empty rows (hi < lo) make this impossible.
-  const int64_t lo_max = row_bounds(r1 - 1, Lq, Lk, causal, wl, wr).lo;
-  const int64_t hi_min = row_bounds(r0, Lq, Lk, causal, wl, wr).hi;
+  const int64_t lo_max = key_off + row_bounds(r1 - 1, Lq, Lk, causal, wl, wr).lo;
+  const int64_t hi_min = key_off + row_bounds(r0, Lq, Lk, causal, wl, wr).hi;
   int64_t fb = floor_div(lo_max + bn - 1, bn);
   int64_t fe = floor_div(hi_min + 1, bn);
   fb = imax64(fb, t.kt_begin);
@@ -129,6 +131,15 @@ struct WorkUnit {
   int32_t b, h, qt;
   int32_t valid;
 };
+
+// Short segments share a workgroup: with every segment at most 64 queries
+// long, four consecutive segments (one wave each); at most 128, two (two
+// waves each); otherwise one.  The group of P segments then takes the place
+// of a segment in the dealing below (segment index = group index, one
+// q-tile), and its keys, consecutive in memory, are the workgroup's keys.
+VA_HD int32_t segments_per_block(int64_t max_seqlen_q) {
+  return max_seqlen_q <= 64 ? 4 : (max_seqlen_q <= 128 ? 2 : 1);
+}
 
 VA_HD int64_t grid_blocks(int64_t batch, int64_t heads, int64_t n_qt) {
   const int64_t groups = batch * heads;

@@ -75,6 +75,7 @@ struct Params {
   // each unit's key tiles and writes a normalised fp32 partial O and its
   // LSE instead of out / lse (combined by combine_splits).
   int32_t num_splits, n_units;
+  int32_t pack;  // segments per workgroup (segments_per_block), 1, 2 or 4
   float* part_o;    // [num_splits, total_q, heads, d_v]
   float* part_lse;  // [num_splits, heads, total_q]
   int32_t causal, wl, wr;
@@ -172,6 +173,19 @@ struct BlockWork {
 
 __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int block_m, int64_t w) {
   BlockWork r;
+  if (p.pack > 1) {  // a group of pack short segments: one unit per (group, head), in packing order
+    const uint32_t groups = ((uint32_t)p.batch + (uint32_t)p.pack - 1u) / (uint32_t)p.pack;
+    r.u = decode_block((uint32_t)w, groups, (uint32_t)p.heads, 1u, p.causal);
+    r.u.h = query_head(r.u.h, p.heads, p.heads_k);
+    if (r.u.valid) {
+      const int first = r.u.b * p.pack, last = min(first + p.pack, p.batch);
+      r.q0 = p.cu_q[first];
+      r.lq = p.cu_q[last] - r.q0;
+      r.k0 = p.cu_k[first];
+      r.lk = p.cu_k[last] - r.k0;
+    }
+    return r;
+  }
   if (p.batch <= kLptMaxBatch) {
     int cq0 = 0, cq1 = 0, ck0 = 0, ck1 = -1;
     if (lane < p.batch) {
@@ -373,19 +387,47 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   const BlockWork bw = block_work(p, lane, C::BM, (int64_t)blockIdx.x - (int64_t)split * p.n_units);
   if (!bw.u.valid) return;
   const int h = bw.u.h, qt = bw.u.qt;
-  const int q0 = bw.q0, Lq = bw.lq, k0 = bw.k0, Lk = bw.lk;
+  const int k0 = bw.k0, Lk = bw.lk;  // the workgroup's keys
   const int r0 = qt * C::BM;
-  if (r0 >= Lq) return;
-  const int r1 = min(r0 + C::BM, Lq);
-  // The key tiles this workgroup visits: all its rows see, or with split-KV
-  // the split-th of num_splits runs of them (possibly empty).
-  const TileRange tr = split_range(tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN), split, p.num_splits);
+  if (r0 >= bw.lq) return;
+  const bool packed = p.pack > 1;
+  // This wave's rows: rows [wrow0, wr1) of a segment whose first query row is
+  // q0 and whose Lq queries see its Lk keys, found at key wkoff of the
+  // workgroup's keys.  One segment: rows r0 + 64 wave on, wkoff = 0.  Packed
+  // short segments: wave w takes segment pack * group + w / (4 / pack), rows
+  // 64 (w % (4 / pack)) on (a wave past the last segment has no rows).
+  int q0 = bw.q0, Lq = bw.lq, wLk = Lk, wkoff = 0, wrow0 = r0 + wave * kRowsPerWave;
+  int r1 = min(r0 + C::BM, Lq);
+  if (packed) {
+    const int per = C::WAVES / p.pack;
+    const int seg = bw.u.b * p.pack + wave / per;
+    wrow0 = (wave % per) * kRowsPerWave;
+    q0 = Lq = wLk = wkoff = r1 = 0;
+    if (seg < p.batch) {
+      q0 = p.cu_q[seg];
+      Lq = p.cu_q[seg + 1] - q0;
+      wkoff = p.cu_k[seg] - k0;
+      wLk = p.cu_k[seg + 1] - k0 - wkoff;
+      r1 = Lq;
+    }
+  }
+  // The key tiles this workgroup visits: all its rows see (packed: all of
+  // its keys, every tile masked), or with split-KV the split-th of
+  // num_splits runs of them (possibly empty).
+  TileRange tr0;
+  if (packed) {
+    tr0.kt_begin = tr0.full_begin = tr0.full_end = 0;
+    tr0.kt_end = (Lk + kBN - 1) / kBN;
+  } else {
+    tr0 = tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN);
+  }
+  const TileRange tr = split_range(tr0, split, p.num_splits);
   const int ntiles = tr.kt_end - tr.kt_begin;
   // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------
   bf16x8 qf[2][C::KC];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int row = r0 + wave * kRowsPerWave + 32 * qb + l32;
+    const int row = wrow0 + 32 * qb + l32;
     const uint16_t* src = p.q + (int64_t)(q0 + row) * p.q_row + (int64_t)h * p.q_head;
 #pragma unroll
     for (int c = 0; c < C::KC; ++c) {
@@ -468,7 +510,6 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   // then runs under their latency.
   if (ntiles > 0) static_for<0, kAhead>([&](auto t) VA_INLINE { issue(t); });  // tiles 0-3
 
-  const int wrow0 = r0 + wave * kRowsPerWave;
   // Each wave's own key-tile range (its 64 rows see a sub-range of the
   // workgroup's).  Iteration w_end, whose tile none of the wave's rows sees
   // (masked to zero probabilities, so the running max and sum stay put and
@@ -478,7 +519,8 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   // rows see.  Waves past the segment's last row compute nothing.
   int w_end = 0, w_full_begin = 0, w_full_end = 0;  // relative to tr.kt_begin
   if (wrow0 < r1) {
-    const TileRange wt = tile_range(Lq, Lk, wrow0, min(wrow0 + kRowsPerWave, r1), p.causal, p.wl, p.wr, kBN);
+    const TileRange wt =
+        tile_range(Lq, wLk, wrow0, min(wrow0 + kRowsPerWave, r1), p.causal, p.wl, p.wr, kBN, wkoff);
     // (clamped to this workgroup's tiles, which with split-KV are a run of
     // the rows' tiles)
     w_end = min(max(wt.kt_end, tr.kt_begin), tr.kt_end) - tr.kt_begin;
@@ -526,9 +568,9 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   int row_lo[2], row_hi[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const RowBounds rb = row_bounds(wrow0 + 32 * qb + l32, Lq, Lk, p.causal, p.wl, p.wr);
-    row_lo[qb] = (int)imin64(rb.lo, (int64_t)Lk);
-    row_hi[qb] = (int)imax64(rb.hi, (int64_t)-1);
+    const RowBounds rb = row_bounds(wrow0 + 32 * qb + l32, Lq, wLk, p.causal, p.wl, p.wr);
+    row_lo[qb] = wkoff + (int)imin64(rb.lo, (int64_t)wLk);
+    row_hi[qb] = wkoff + (int)imax64(rb.hi, (int64_t)-1);
   }
   // Iteration (relative key tile) holding each row's first visible key, or
   // -1 for a row that sees none: there the fast path cannot run (see
@@ -966,6 +1008,17 @@ static Variant variant_for(int dqk, int dv, int max_seqlen_q, bool lse = true) {
 
 static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
+// Work units of a launch (padding included): (segment, head, q-tile), or
+// with short segments packed (segments_per_block > 1) (group, head).
+static int64_t launch_units(int64_t batch, int64_t heads, int64_t max_seqlen_q, int block_m, int32_t* n_qt_out,
+                            int32_t* pack_out) {
+  const int32_t pack = segments_per_block(max_seqlen_q);
+  const int64_t n_qt = pack > 1 ? 1 : (max_seqlen_q + block_m - 1) / block_m;
+  if (n_qt_out) *n_qt_out = (int32_t)n_qt;
+  if (pack_out) *pack_out = pack;
+  return grid_blocks((batch + pack - 1) / pack, heads, n_qt);
+}
+
 // Row strides above 2^24 elements would overflow the 32-bit offsets of the
 // per-tile buffer loads (64 rows x stride x 2 bytes).
 static constexpr int64_t kMaxRowStride = (int64_t)1 << 24;
@@ -1027,14 +1080,15 @@ extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_h
   }
   if (max_q <= 0) return VA_ERR_ARG;
   const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, max_q);
-  const int64_t n_qt = ((int64_t)max_q + var.block_m - 1) / var.block_m;
-  if (block < 0 || block >= va::grid_blocks(batch, num_heads, n_qt)) return VA_ERR_ARG;
-  const va::WorkUnit u = va::lpt_applies(batch, seqlens_q, seqlens_k)
-                             ? va::decode_block_lpt(block, batch, num_heads, var.block_m, (int32_t)n_qt, causal,
+  int32_t n_qt = 0, pack = 1;
+  if (block < 0 || block >= va::launch_units(batch, num_heads, max_q, var.block_m, &n_qt, &pack)) return VA_ERR_ARG;
+  const int32_t groups = (batch + pack - 1) / pack;
+  const va::WorkUnit u = pack == 1 && va::lpt_applies(batch, seqlens_q, seqlens_k)
+                             ? va::decode_block_lpt(block, batch, num_heads, var.block_m, n_qt, causal,
                                                     seqlens_q, seqlens_k)
-                             : va::decode_block((uint32_t)block, (uint32_t)batch, (uint32_t)num_heads,
+                             : va::decode_block((uint32_t)block, (uint32_t)groups, (uint32_t)num_heads,
                                                 (uint32_t)n_qt, causal);
-  *segment = u.valid ? u.b : -1;
+  *segment = u.valid ? u.b * pack : -1;
   *head = u.valid ? va::query_head(u.h, num_heads, num_heads_k) : -1;
   *q_tile = u.valid ? u.qt : -1;
   return VA_OK;
@@ -1053,8 +1107,7 @@ extern "C" int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t
   plan->block_n = var.block_n;
   plan->threads = var.threads;
   plan->lds_bytes = var.lds_bytes;
-  const int64_t n_qt = ((int64_t)max_seqlen_q + var.block_m - 1) / var.block_m;
-  plan->grid = va::grid_blocks(batch, num_heads, n_qt);
+  plan->grid = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, nullptr, &plan->segments_per_block);
   plan->kernel = var.name;
   return VA_OK;
 }
@@ -1125,11 +1178,9 @@ static int prepare(const va_tensor* q, const va_tensor* k, const va_tensor* v, c
 static int launch_attention(Params& p, int32_t head_dim_qk, int32_t head_dim_v, int32_t max_seqlen_q,
                             bool fp32_row_sum, void* stream) {
   const Variant var = variant_for(head_dim_qk, head_dim_v, max_seqlen_q, fp32_row_sum);
-  const int64_t n_qt = ((int64_t)max_seqlen_q + var.block_m - 1) / var.block_m;
-  const int64_t units = grid_blocks(p.batch, p.heads, n_qt);
+  const int64_t units = launch_units(p.batch, p.heads, max_seqlen_q, var.block_m, &p.n_qt, &p.pack);
   const int64_t grid = units * p.num_splits;
   if (grid > INT32_MAX) return VA_ERR_SHAPE;
-  p.n_qt = (int32_t)n_qt;
   p.n_units = (int32_t)units;
   void* args[] = {&p};
   const hipError_t err = hipLaunchKernel(var.fn, dim3((unsigned)grid), dim3(var.threads), args, 0,
@@ -1178,8 +1229,7 @@ extern "C" int varlen_attn_num_splits(int32_t head_dim_qk, int32_t head_dim_v, i
   // The work units a launch has (padding included) against the workgroups
   // the device holds at once; each split keeps at least 16 key tiles.
   const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, max_seqlen_q, true);
-  const int64_t n_qt = ((int64_t)max_seqlen_q + var.block_m - 1) / var.block_m;
-  const int64_t units = va::grid_blocks(batch, num_heads, n_qt);
+  const int64_t units = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, nullptr, nullptr);
   const int64_t slots = (int64_t)cus * (var.lds_bytes <= 80 * 1024 ? 2 : 1);
   const int64_t by_tiles = ((int64_t)max_seqlen_k + 16 * var.block_n - 1) / (16 * var.block_n);
   int64_t s = slots / units;

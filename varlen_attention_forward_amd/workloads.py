@@ -127,6 +127,19 @@ def _named_workloads() -> dict:
             "256 tokens, 16 heads, d=80",
         ),
         Workload(
+            name="vit_window64_d80",
+            seed=7,
+            seqlens_q=(64,) * 700,
+            seqlens_k=(64,) * 700,
+            num_heads=16,
+            head_dim_qk=80,
+            head_dim_v=80,
+            causal=False,
+            return_lse=False,  # the ViT call takes no LSE
+            description="windowed ViT layer with 64-token windows (a 4K image's ~700 windows of 8 x 8 "
+            "merged patches), 16 heads, d=80, non-causal; four windows per workgroup",
+        ),
+        Workload(
             name="vit_long65536_d128",
             seed=4,
             seqlens_q=(65536,),
@@ -173,6 +186,7 @@ WORKLOAD_ORDER = (
     "tiny_varlen_d64",
     "vit_full_d80",
     "vit_window256_d80",
+    "vit_window64_d80",
     "vit_long65536_d128",
     "mla_causal_192_128",
     "mla_context_chunk_tp8",

@@ -25,6 +25,13 @@
 // softmax of tile j, whose exp does not wait for tile j's max (see
 // fused_block in attn_fwd_wide).
 //
+// Variations on the same workgroup: grouped KV heads (query head h reads KV
+// head h / (H / H_kv)); short segments packed four or two to a workgroup,
+// one or two waves each, sharing the workgroup's key tiles (segments of at
+// most 64 / 128 queries); and split-KV, where a workgroup visits one run of
+// its key tiles and writes an fp32 partial that combine_splits
+// (merge_states.hip) reduces.
+//
 // Where the pages describe FA4 on Blackwell (TMEM, tcgen05.ld.red row max,
 // 2-CTA MMA) that design is prior art only; what carries over is the online
 // softmax step with exp2 and a rescale threshold (SGLang PR #41344,
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   const int r0 = qt * C::BM;
   if (r0 >= bw.lq) return;
   const bool packed = p.pack > 1;
-  // This wave's rows: rows [wrow0, wr1) of a segment whose first query row is
+  // This wave's rows: rows [wrow0, r1) of a segment whose first query row is
   // q0 and whose Lq queries see its Lk keys, found at key wkoff of the
   // workgroup's keys.  One segment: rows r0 + 64 wave on, wkoff = 0.  Packed
   // short segments: wave w takes segment pack * group + w / (4 / pack), rows

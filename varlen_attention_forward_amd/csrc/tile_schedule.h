@@ -132,13 +132,14 @@ struct WorkUnit {
   int32_t valid;
 };
 
-// Short segments share a workgroup: with every segment at most 64 queries
-// long, four consecutive segments (one wave each); at most 128, two (two
-// waves each); otherwise one.  The group of P segments then takes the place
-// of a segment in the dealing below (segment index = group index, one
-// q-tile), and its keys, consecutive in memory, are the workgroup's keys.
-VA_HD int32_t segments_per_block(int64_t max_seqlen_q) {
-  return max_seqlen_q <= 64 ? 4 : (max_seqlen_q <= 128 ? 2 : 1);
+// Short segments share a workgroup of four waves of rows_per_wave query
+// rows: with every segment at most rows_per_wave queries long, four
+// consecutive segments (one wave each); at most twice that, two (two waves
+// each); otherwise one.  The group of P segments then takes the place of a
+// segment in the dealing below (segment index = group index, one q-tile),
+// and its keys, consecutive in memory, are the workgroup's keys.
+VA_HD int32_t segments_per_block(int64_t max_seqlen_q, int64_t rows_per_wave) {
+  return max_seqlen_q <= rows_per_wave ? 4 : (max_seqlen_q <= 2 * rows_per_wave ? 2 : 1);
 }
 
 VA_HD int64_t grid_blocks(int64_t batch, int64_t heads, int64_t n_qt) {

@@ -178,9 +178,10 @@ struct BlockWork {
   int q0, lq, k0, lk;  // the segment's first query / key row and lengths
 };
 
+template <bool PACKED>
 __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int block_m, int64_t w) {
   BlockWork r;
-  if (p.pack > 1) {  // a group of pack short segments: one unit per (group, head), in packing order
+  if constexpr (PACKED) {  // a group of pack short segments: one unit per (group, head), in packing order
     const uint32_t groups = ((uint32_t)p.batch + (uint32_t)p.pack - 1u) / (uint32_t)p.pack;
     r.u = decode_block((uint32_t)w, groups, (uint32_t)p.heads, 1u, p.causal);
     r.u.h = query_head(r.u.h, p.heads, p.heads_k);
@@ -285,7 +286,7 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const lds_char* base, int byte_off
 // every V read wait for all DMA in flight (s_waitcnt vmcnt(0)).
 // ============================================================================
 namespace wide {
-constexpr int kRowsPerWave = 64;
+constexpr int kRowsPerWave = 64;     // query rows per wave (Cfg::RPW)
 constexpr int kBN = 32;              // keys per tile
 constexpr int kStages = 6;           // tile t lives in stage t % 6 (an even count: see the loop)
 constexpr int kAhead = kStages - 2;  // iteration j issues tile j + 4
@@ -300,7 +301,15 @@ template <int DQK, int DV>
 struct Cfg : TileGeom<DQK, DV, kBN> {
   static constexpr int WAVES = kWaves;
   static constexpr int THREADS = 64 * WAVES;
-  static constexpr int BM = kRowsPerWave * WAVES;  // query rows per workgroup
+  // Query rows per wave: QB blocks of 32, each a separate MFMA N block that
+  // shares the wave's K and V operand reads.  Two for every head dim: head
+  // dims <= 80 run two waves per SIMD, which leaves 256 registers a wave, and
+  // a third block at 128 and 192/128 (one wave per SIMD) would need more
+  // than the 512 a wave can have (the compiler spills hundreds).
+  static constexpr int QB = 2;
+  static constexpr int RPW = 32 * QB;
+  static_assert(RPW == kRowsPerWave, "one row count per wave for every head dim");
+  static constexpr int BM = RPW * WAVES;  // query rows per workgroup
   // Every wave issues NK K and NV V wave-loads per tile (zeros into a dummy
   // area where the tile has fewer), so LOADS per tile and wave is constant.
   static constexpr int NK = (Cfg::K_WL + WAVES - 1) / WAVES;
@@ -341,7 +350,7 @@ __device__ __forceinline__ float from_lower_half(float x) {
 // to ln(1 + 2^-9), which is why an LSE keeps the fp32 sum.
 enum class RowSum { kF32, kMfma };
 
-template <int DQK, int DV, RowSum SUM>
+template <int DQK, int DV, RowSum SUM, bool PACKED>
 __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd_wide(Params p) {
   using namespace wide;
   using C = Cfg<DQK, DV>;
@@ -391,24 +400,24 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
 
   // Split-KV copy of the work units this workgroup belongs to (0 without split).
   const int split = (int)(blockIdx.x / (uint32_t)p.n_units);
-  const BlockWork bw = block_work(p, lane, C::BM, (int64_t)blockIdx.x - (int64_t)split * p.n_units);
+  const BlockWork bw = block_work<PACKED>(p, lane, C::BM, (int64_t)blockIdx.x - (int64_t)split * p.n_units);
   if (!bw.u.valid) return;
   const int h = bw.u.h, qt = bw.u.qt;
   const int k0 = bw.k0, Lk = bw.lk;  // the workgroup's keys
   const int r0 = qt * C::BM;
   if (r0 >= bw.lq) return;
-  const bool packed = p.pack > 1;
+  constexpr bool packed = PACKED;
   // This wave's rows: rows [wrow0, r1) of a segment whose first query row is
   // q0 and whose Lq queries see its Lk keys, found at key wkoff of the
   // workgroup's keys.  One segment: rows r0 + 64 wave on, wkoff = 0.  Packed
   // short segments: wave w takes segment pack * group + w / (4 / pack), rows
   // 64 (w % (4 / pack)) on (a wave past the last segment has no rows).
-  int q0 = bw.q0, Lq = bw.lq, wLk = Lk, wkoff = 0, wrow0 = r0 + wave * kRowsPerWave;
+  int q0 = bw.q0, Lq = bw.lq, wLk = Lk, wkoff = 0, wrow0 = r0 + wave * C::RPW;
   int r1 = min(r0 + C::BM, Lq);
-  if (packed) {
+  if constexpr (packed) {
     const int per = C::WAVES / p.pack;
     const int seg = bw.u.b * p.pack + wave / per;
-    wrow0 = (wave % per) * kRowsPerWave;
+    wrow0 = (wave % per) * C::RPW;
     q0 = Lq = wLk = wkoff = r1 = 0;
     if (seg < p.batch) {
       q0 = p.cu_q[seg];
@@ -422,7 +431,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   // its keys, every tile masked), or with split-KV the split-th of
   // num_splits runs of them (possibly empty).
   TileRange tr0;
-  if (packed) {
+  if constexpr (packed) {
     tr0.kt_begin = tr0.full_begin = tr0.full_end = 0;
     tr0.kt_end = (Lk + kBN - 1) / kBN;
   } else {
@@ -431,9 +440,9 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   const TileRange tr = split_range(tr0, split, p.num_splits);
   const int ntiles = tr.kt_end - tr.kt_begin;
   // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------
-  bf16x8 qf[2][C::KC];
+  bf16x8 qf[C::QB][C::KC];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < C::QB; ++qb) {
     const int row = wrow0 + 32 * qb + l32;
     const uint16_t* src = p.q + (int64_t)(q0 + row) * p.q_row + (int64_t)h * p.q_head;
 #pragma unroll
@@ -527,7 +536,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   int w_end = 0, w_full_begin = 0, w_full_end = 0;  // relative to tr.kt_begin
   if (wrow0 < r1) {
     const TileRange wt =
-        tile_range(Lq, wLk, wrow0, min(wrow0 + kRowsPerWave, r1), p.causal, p.wl, p.wr, kBN, wkoff);
+        tile_range(Lq, wLk, wrow0, min(wrow0 + C::RPW, r1), p.causal, p.wl, p.wr, kBN, wkoff);
     // (clamped to this workgroup's tiles, which with split-KV are a run of
     // the rows' tiles)
     w_end = min(max(wt.kt_end, tr.kt_begin), tr.kt_end) - tr.kt_begin;
@@ -561,20 +570,24 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   }
 
   // ---- running state ----------------------------------------------------------
-  f32x16 acc[C::VB][2];
+  f32x16 acc[C::VB][C::QB];
 #pragma unroll
   for (int vb = 0; vb < C::VB; ++vb)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[vb][qb][r] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY};  // running max of s * scale * log2(e)
-  float nm[2] = {0.f, 0.f};                 // -m_run, or 0 while m_run is -inf
-  float lim[2] = {-FLT_MAX, -FLT_MAX};      // m_run + kRescaleTau, or -FLT_MAX while m_run is -inf
-  float l_run[2] = {0.f, 0.f};              // fp32 row sum (unless SUM_BY_MFMA)
-  int row_lo[2], row_hi[2];
+  float m_run[C::QB], nm[C::QB], lim[C::QB], l_run[C::QB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < C::QB; ++qb) {
+    m_run[qb] = -INFINITY;  // running max of s * scale * log2(e)
+    nm[qb] = 0.f;           // -m_run, or 0 while m_run is -inf
+    lim[qb] = -FLT_MAX;     // m_run + kRescaleTau, or -FLT_MAX while m_run is -inf
+    l_run[qb] = 0.f;        // fp32 row sum (unless SUM_BY_MFMA)
+  }
+  int row_lo[C::QB], row_hi[C::QB];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
     const RowBounds rb = row_bounds(wrow0 + 32 * qb + l32, Lq, wLk, p.causal, p.wl, p.wr);
     row_lo[qb] = wkoff + (int)imin64(rb.lo, (int64_t)wLk);
     row_hi[qb] = wkoff + (int)imax64(rb.hi, (int64_t)-1);
@@ -582,19 +595,19 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   // Iteration (relative key tile) holding each row's first visible key, or
   // -1 for a row that sees none: there the fast path cannot run (see
   // fused_block).
-  int first_j[2];
+  int first_j[C::QB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < C::QB; ++qb)
     first_j[qb] = row_lo[qb] <= row_hi[qb] ? row_lo[qb] / kBN - tr.kt_begin : -1;
   // Scores of two tiles (the one in the softmax and the next, which QK^T is
   // writing): sbuf[t % 2][qb][r] = key 8 (r / 4) + 4 g + r % 4, query l32.
-  f32x16 sbuf[2][2];
-  bf16x8 pf[2][2];  // probabilities, PV B operand per (qb, 16-key half)
+  f32x16 sbuf[2][C::QB];
+  bf16x8 pf[C::QB][2];  // probabilities, PV B operand per (qb, 16-key half)
 
   // MFMAs of one iteration: PV of tile j - 1 (2 * VB operands, if kPV) then
   // QK^T of tile j + 1 (KC operands) into sn, each LDS operand feeding both
   // query blocks.  Operands are read kDepth ahead into a ring of registers.
-  auto mfma_ops = [&](const lds_char* vs, const lds_char* ks, f32x16 (&sn)[2], auto pv_tag) VA_INLINE {
+  auto mfma_ops = [&](const lds_char* vs, const lds_char* ks, f32x16 (&sn)[C::QB], auto pv_tag) VA_INLINE {
     constexpr bool kPV = decltype(pv_tag)::value;
     constexpr int kPVOps = kPV ? 2 * C::VB : 0;
     constexpr int kOps = kPVOps + C::KC;
@@ -619,23 +632,23 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
       if (i < kPVOps) {
         const int t = i / C::VB, vb = i % C::VB;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < C::QB; ++qb)
           acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, pf[qb][t], acc[vb][qb], 0, 0, 0);
       } else {
         const int c = i - kPVOps;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < C::QB; ++qb)
           sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qf[qb][c], c == 0 ? zero : sn[qb], 0, 0, 0);
       }
     }
   };
   // Boundary tiles only: scores of keys a row may not see become -inf.
-  auto mask = [&](int j, f32x16 (&s)[2]) VA_INLINE {
+  auto mask = [&](int j, f32x16 (&s)[C::QB]) VA_INLINE {
     const int kt = tr.kt_begin + j;
     if ((unsigned)(j - w_full_begin) >= (unsigned)(w_full_end - w_full_begin)) {  // j outside [begin, end)
       const int key0 = kt * kBN;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int jj = key0 + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -648,11 +661,11 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   // than kRescaleTau, in log2 units; then every row of the wave moves),
   // p = exp2(s * scale * log2(e) - m), row sum, bf16 pack into pf.  Returns
   // whether acc must be rescaled, with alpha per query block.
-  auto softmax = [&](f32x16 (&s)[2], float (&alpha)[2]) VA_INLINE -> bool {
-    float m_new[2];
+  auto softmax = [&](f32x16 (&s)[C::QB], float (&alpha)[C::QB]) VA_INLINE -> bool {
+    float m_new[C::QB];
     bool need = false;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < C::QB; ++qb) {
       float m = fmaxf(fmaxf(s[qb][0], s[qb][1]), s[qb][2]);
 #pragma unroll
       for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, s[qb][r]), s[qb][r + 1]);
@@ -662,7 +675,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
     }
     const bool move = __any(need);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < C::QB; ++qb) {
       const float m_next = move ? m_new[qb] : m_run[qb];
       alpha[qb] = (m_next == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_next);
       m_run[qb] = m_next;
@@ -670,7 +683,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
       lim[qb] = (m_next == -INFINITY) ? -FLT_MAX : m_next + kRescaleTau;
     }
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < C::QB; ++qb) {
       float sum = 0.f;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -711,19 +724,23 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   // bunches the MFMAs, and an MFMA hides only a few VALU ops behind it.  The
   // packs, which overwrite the probabilities PV reads, all fall after the
   // last PV MFMA.
-  auto fused_block = [&](const lds_char* vs, const lds_char* ks, f32x16 (&s)[2], f32x16 (&sn)[2],
-                         float (&sum)[2], int j) VA_INLINE -> bool {
+  auto fused_block = [&](const lds_char* vs, const lds_char* ks, f32x16 (&s)[C::QB], f32x16 (&sn)[C::QB],
+                         float (&sum)[C::QB], int j) VA_INLINE -> bool {
     constexpr bool kMaxCheck = SUM_BY_MFMA;
-    constexpr int kPVOps = 2 * C::VB, kOps = kPVOps + C::KC, kSlots = 2 * kOps;
-    constexpr int kUnits = kMaxCheck ? 64 : 48;
-    static_assert((kUnits - 16) * kSlots / kUnits >= 2 * kPVOps, "packs must follow the PV MFMAs");
-    float m[2];
+    constexpr int QB = C::QB;
+    constexpr int kPVOps = 2 * C::VB, kOps = kPVOps + C::KC, kSlots = QB * kOps;
+    constexpr int kMaxU = 8 * QB, kExpU = 16 * QB, kPackU = 8 * QB;  // units per kind
+    constexpr int kUnits = (kMaxCheck ? kMaxU : 0) + kExpU + kPackU;
+    static_assert((kUnits - kPackU) * kSlots / kUnits >= QB * kPVOps, "packs must follow the PV MFMAs");
+    float m[QB];
     bool bad = false;
-    if constexpr (!kMaxCheck) bad = j == first_j[0] || j == first_j[1];
-    u32x4 pk[2][2];
+    if constexpr (!kMaxCheck)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) bad |= j == first_j[qb];
+    u32x4 pk[QB][2];
     auto unit = [&](auto uu) VA_INLINE {
-      constexpr int u = decltype(uu)::value + (kMaxCheck ? 0 : 16);
-      if constexpr (u < 16) {  // row max, 8 steps per query block
+      constexpr int u = decltype(uu)::value + (kMaxCheck ? 0 : kMaxU);
+      if constexpr (u < kMaxU) {  // row max, 8 steps per query block
         constexpr int qb = u / 8, st = u % 8;
         if constexpr (st == 0) {
           m[qb] = fmaxf(fmaxf(s[qb][0], s[qb][1]), s[qb][2]);
@@ -733,11 +750,11 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
           m[qb] = fmaxf(m[qb], s[qb][15]);
           bad |= m[qb] * p.scale_log2 > lim[qb];
         }
-      } else if constexpr (u < 48) {  // p = exp2(s * scale - m_run), in place
-        constexpr int qb = (u - 16) / 16, r = (u - 16) % 16;
+      } else if constexpr (u < kMaxU + kExpU) {  // p = exp2(s * scale - m_run), in place
+        constexpr int qb = (u - kMaxU) / 16, r = (u - kMaxU) % 16;
         s[qb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, nm[qb]));
       } else {  // bf16 pack (and row sum)
-        constexpr int i = u - 48, qb = i / 8, t = (i / 4) % 2, e = i % 4, r = 8 * t + 2 * e;
+        constexpr int i = u - kMaxU - kExpU, qb = i / 8, t = (i / 4) % 2, e = i % 4, r = 8 * t + 2 * e;
         constexpr bool first = t == 0 && e == 0;
         pk[qb][t][e] = pack_bf16x2(s[qb][r], s[qb][r + 1]);
         if constexpr (SUM == RowSum::kF32) {
@@ -766,8 +783,8 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
       constexpr int i = decltype(oo)::value;
       const bf16x8 op = ring[i % kDepth];
       if constexpr (i + kDepth < kOps) load_op(i + kDepth, ring[i % kDepth]);
-      static_for<0, 2>([&](auto qq) VA_INLINE {
-        constexpr int qb = decltype(qq)::value, slot = 2 * i + qb;
+      static_for<0, QB>([&](auto qq) VA_INLINE {
+        constexpr int qb = decltype(qq)::value, slot = QB * i + qb;
         if constexpr (i < kPVOps) {
           constexpr int t = i / C::VB, vb = i % C::VB;
           acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, pf[qb][t], acc[vb][qb], 0, 0, 0);
@@ -782,15 +799,15 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
     return __any(bad);
   };
   // QK^T of one tile on its own (tile 0, and the slow path below).
-  auto qk_only = [&](const lds_char* ks, f32x16 (&sn)[2]) VA_INLINE {
+  auto qk_only = [&](const lds_char* ks, f32x16 (&sn)[C::QB]) VA_INLINE {
     mfma_ops(nullptr, ks, sn, BoolTag<false>{});
   };
   // acc *= alpha, after the PV MFMAs of the previous tile (rare).
-  auto rescale = [&](bool move, const float (&alpha)[2]) VA_INLINE {
+  auto rescale = [&](bool move, const float (&alpha)[C::QB]) VA_INLINE {
     if (move) {
       asm volatile("; lazy rescale" ::: "memory");  // keep the rare rescale a branch
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
         for (int vb = 0; vb < C::VB; ++vb)
 #pragma unroll
@@ -821,7 +838,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
         const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
         const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < C::QB; ++qb)
           acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][t], acc[vb][qb], 0, 0, 0);
       }
   };
@@ -837,7 +854,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
       if (active) {
         mask(0, sbuf[0]);
         mfma_ops(nullptr, kst(Int<1>{}), sbuf[1], BoolTag<false>{});
-        float alpha[2];
+        float alpha[C::QB];
         const bool move = softmax(sbuf[0], alpha);
         rescale(move, alpha);
       }
@@ -853,32 +870,36 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
           if (j <= w_end) {
             constexpr int cur = (U + 1) % 2;  // j % 2, j0 being odd
             mask(j, sbuf[cur]);
-            float sum[2];
+            float sum[C::QB];
             const bool slow = fused_block(vst(Int<U % kStages>{}), kst(Int<(U + 2) % kStages>{}), sbuf[cur],
                                           sbuf[cur ^ 1], sum, j);
             // The probabilities are only read in the next iteration and the
             // row sums only on the fast path; without these uses the compiler
             // sinks their computation past the branch below, out of the
             // interleave, where nothing hides it.
-            asm volatile("" ::"v"(pf[0][0]), "v"(pf[0][1]), "v"(pf[1][0]), "v"(pf[1][1]));
-            if constexpr (!SUM_BY_MFMA) asm volatile("" ::"v"(sum[0]), "v"(sum[1]));
+#pragma unroll
+            for (int qb = 0; qb < C::QB; ++qb) {
+              asm volatile("" ::"v"(pf[qb][0]), "v"(pf[qb][1]));
+              if constexpr (!SUM_BY_MFMA) asm volatile("" ::"v"(sum[qb]));
+            }
             // Commit the row sums on one path (the slow path restores them):
             // two paths merging into l_run cost the register allocator dearly.
-            const float l_prev[2] = {l_run[0], l_run[1]};
-            if constexpr (!SUM_BY_MFMA) {
-              l_run[0] += sum[0];
-              l_run[1] += sum[1];
+            float l_prev[C::QB];
+#pragma unroll
+            for (int qb = 0; qb < C::QB; ++qb) {
+              l_prev[qb] = l_run[qb];
+              if constexpr (!SUM_BY_MFMA) l_run[qb] += sum[qb];
             }
             if (slow) {
               // Some row's max moved past m_run + kRescaleTau (or a row saw
               // its first key): recompute this tile's scores from K, still
               // in its stage, and take the full softmax with the rescale.
               asm volatile("; softmax slow path" ::: "memory");
-              l_run[0] = l_prev[0];
-              l_run[1] = l_prev[1];
+#pragma unroll
+              for (int qb = 0; qb < C::QB; ++qb) l_run[qb] = l_prev[qb];
               qk_only(kst(Int<(U + 1) % kStages>{}), sbuf[cur]);
               mask(j, sbuf[cur]);
-              float alpha[2];
+              float alpha[C::QB];
               const bool move = softmax(sbuf[cur], alpha);
               rescale(move, alpha);
             }
@@ -910,7 +931,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
     // 4 g .. + 3 of each 32-wide block: one 16-byte store each) and the LSE of
     // this split's keys (-inf where a row saw none of them).
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < C::QB; ++qb) {
       const float l = SUM_BY_MFMA ? from_lower_half(acc[C::VB - 1][qb][kSumReg]) : xhalf_sum(l_run[qb]);
       const int row = wrow0 + 32 * qb + l32;
       const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -938,7 +959,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   // chunks (jj, jj + 1) leaves lane g with the 8 contiguous values of chunk
   // jj + g: one 16-byte store instead of two 8-byte ones per lane.
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < C::QB; ++qb) {
     const float l = SUM_BY_MFMA ? from_lower_half(acc[C::VB - 1][qb][kSumReg]) : xhalf_sum(l_run[qb]);
     const int row = wrow0 + 32 * qb + l32;
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -988,10 +1009,11 @@ struct Variant {
 };
 
 template <int DQK, int DV, RowSum SUM>
-static Variant wide_variant() {
+static Variant wide_variant(bool packed) {
   using C = wide::Cfg<DQK, DV>;
-  return {(const void*)&attn_fwd_wide<DQK, DV, SUM>, C::LDS_BYTES, C::BM, wide::kBN, C::THREADS,
-          "attn_fwd_wide"};
+  const void* fn = packed ? (const void*)&attn_fwd_wide<DQK, DV, SUM, true>
+                          : (const void*)&attn_fwd_wide<DQK, DV, SUM, false>;
+  return {fn, C::LDS_BYTES, C::BM, wide::kBN, C::THREADS, "attn_fwd_wide"};
 }
 
 static bool supported_dims(int dqk, int dv) {
@@ -1001,16 +1023,17 @@ static bool supported_dims(int dqk, int dv) {
 
 // `lse`: whether the caller asked for the LSE (without one the row sum is
 // taken over the bf16 probabilities, see RowSum; the launch shape is the same
-// either way).
+// either way).  Short segments (segments_per_block > 1) take the packed
+// instantiation; the other one carries none of its set-up.
 static Variant variant_for(int dqk, int dv, int max_seqlen_q, bool lse = true) {
   (void)dv;
-  (void)max_seqlen_q;
+  const bool pk = segments_per_block(max_seqlen_q, wide::kRowsPerWave) > 1;
   constexpr RowSum F = RowSum::kF32, M = RowSum::kMfma;
-  if (dqk == 64) return wide_variant<64, 64, F>();
-  if (dqk == 72) return lse ? wide_variant<72, 72, F>() : wide_variant<72, 72, M>();
-  if (dqk == 80) return lse ? wide_variant<80, 80, F>() : wide_variant<80, 80, M>();
-  if (dqk == 128) return wide_variant<128, 128, F>();
-  return wide_variant<192, 128, F>();
+  if (dqk == 64) return wide_variant<64, 64, F>(pk);
+  if (dqk == 72) return lse ? wide_variant<72, 72, F>(pk) : wide_variant<72, 72, M>(pk);
+  if (dqk == 80) return lse ? wide_variant<80, 80, F>(pk) : wide_variant<80, 80, M>(pk);
+  if (dqk == 128) return wide_variant<128, 128, F>(pk);
+  return wide_variant<192, 128, F>(pk);
 }
 
 static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
@@ -1019,7 +1042,7 @@ static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 // with short segments packed (segments_per_block > 1) (group, head).
 static int64_t launch_units(int64_t batch, int64_t heads, int64_t max_seqlen_q, int block_m, int32_t* n_qt_out,
                             int32_t* pack_out) {
-  const int32_t pack = segments_per_block(max_seqlen_q);
+  const int32_t pack = segments_per_block(max_seqlen_q, block_m / 4);
   const int64_t n_qt = pack > 1 ? 1 : (max_seqlen_q + block_m - 1) / block_m;
   if (n_qt_out) *n_qt_out = (int32_t)n_qt;
   if (pack_out) *pack_out = pack;

@@ -5,6 +5,18 @@ and the ``cpu_baseline`` leg of ``bench.py``.  The HIP library neither
 imports nor links anything here.
 """
 from .attention import attention_fwd, visible_interval, visible_mask, visible_pairs
+from .fp8 import attention_fwd_fp8, dequantize, e4m3_decode, e4m3_encode, quantize_output
 from .merge import merge_states
 
-__all__ = ["attention_fwd", "merge_states", "visible_interval", "visible_mask", "visible_pairs"]
+__all__ = [
+    "attention_fwd",
+    "attention_fwd_fp8",
+    "dequantize",
+    "e4m3_decode",
+    "e4m3_encode",
+    "merge_states",
+    "quantize_output",
+    "visible_interval",
+    "visible_mask",
+    "visible_pairs",
+]

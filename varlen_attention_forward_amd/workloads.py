@@ -268,6 +268,88 @@ def make_inputs(
     )
 
 
+@dataclasses.dataclass
+class Fp8Inputs:
+    """e4m3 codes (``torch.float8_e4m3fn``) with per-(segment, KV head) fp32
+    descales [batch, H_kv]: decoded code * descale approximates the drawn
+    value."""
+
+    q: torch.Tensor  # [total_q, H, d_qk] e4m3
+    k: torch.Tensor  # [total_k, H_kv, d_qk] e4m3
+    v: torch.Tensor  # [total_k, H_kv, d_v] e4m3
+    q_descale: torch.Tensor  # [batch, H_kv] fp32
+    k_descale: torch.Tensor
+    v_descale: torch.Tensor
+    cu_seqlens_q: torch.Tensor
+    cu_seqlens_k: torch.Tensor
+    max_seqlen_q: int
+    max_seqlen_k: int
+    softmax_scale: float
+    causal: bool
+    window: tuple
+
+    def to(self, device) -> "Fp8Inputs":
+        mv = {f: getattr(self, f).to(device) for f in ("q", "k", "v", "q_descale", "k_descale", "v_descale",
+                                                        "cu_seqlens_q", "cu_seqlens_k")}
+        return dataclasses.replace(self, **mv)
+
+
+def _quantize_blocks(x: torch.Tensor, cu: Sequence[int], heads_k: int):
+    """Per (segment, KV head) block of ``x`` [rows, H, d]: descale = amax / 448
+    (1 for an all-zero block), codes = e4m3(x / descale).  A query head's
+    block is its KV head's group of query heads."""
+    rows, H, d = x.shape
+    grp = H // heads_k
+    batch = len(cu) - 1
+    desc = torch.ones((batch, heads_k), dtype=torch.float32)
+    codes = torch.zeros((rows, H, d), dtype=torch.float8_e4m3fn)
+    for b in range(batch):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        for hk in range(heads_k):
+            blk = x[r0:r1, hk * grp:(hk + 1) * grp, :]
+            amax = float(blk.abs().max()) if blk.numel() else 0.0
+            ds = amax / 448.0 if amax > 0 else 1.0
+            desc[b, hk] = ds
+            codes[r0:r1, hk * grp:(hk + 1) * grp, :] = (blk / desc[b, hk]).clamp(-448, 448).to(torch.float8_e4m3fn)
+    return codes, desc
+
+
+def make_fp8_inputs(
+    seqlens_q: Sequence[int],
+    seqlens_k: Sequence[int],
+    num_heads: int,
+    head_dim_qk: int,
+    head_dim_v: int,
+    seed: int,
+    causal: bool = False,
+    window: tuple = (-1, -1),
+    softmax_scale: Optional[float] = None,
+    std: float = 1.0,
+    num_heads_k: Optional[int] = None,
+) -> Fp8Inputs:
+    """The draws of ``make_inputs`` (same seed, same order, before the bf16
+    rounding), quantised to e4m3 per (segment, KV head) block."""
+    assert len(seqlens_q) == len(seqlens_k)
+    hk = num_heads if num_heads_k is None else int(num_heads_k)
+    g = torch.Generator().manual_seed(seed)
+    tq, tk = int(sum(seqlens_q)), int(sum(seqlens_k))
+    q = torch.randn((tq, num_heads, head_dim_qk), generator=g, dtype=torch.float32) * std
+    k = torch.randn((tk, hk, head_dim_qk), generator=g, dtype=torch.float32) * std
+    v = torch.randn((tk, hk, head_dim_v), generator=g, dtype=torch.float32)
+    cq, ck = cu_seqlens(seqlens_q), cu_seqlens(seqlens_k)
+    q8, qd = _quantize_blocks(q, cq.tolist(), hk)
+    k8, kd = _quantize_blocks(k, ck.tolist(), hk)
+    v8, vd = _quantize_blocks(v, ck.tolist(), hk)
+    scale = head_dim_qk ** -0.5 if softmax_scale is None else float(softmax_scale)
+    return Fp8Inputs(
+        q=q8, k=k8, v=v8, q_descale=qd, k_descale=kd, v_descale=vd,
+        cu_seqlens_q=cq, cu_seqlens_k=ck,
+        max_seqlen_q=int(max(seqlens_q)) if len(seqlens_q) else 0,
+        max_seqlen_k=int(max(seqlens_k)) if len(seqlens_k) else 0,
+        softmax_scale=scale, causal=causal, window=tuple(window),
+    )
+
+
 def workload_inputs(w: Workload) -> Inputs:
     """The seeded tensors of a named workload (the seed is part of ``w``)."""
     if w.name == "vit_full_d80":

@@ -152,6 +152,50 @@ int varlen_attn_fwd_splitkv(const va_tensor* q, const va_tensor* k, const va_ten
                             const va_tensor* out, float* lse, int32_t num_splits, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/*
+ * varlen_attn_fwd_fp8 -- the forward on fp8 e4m3 inputs with descales, and
+ * optionally an e4m3 output.  SGLang PR #41344 ("Accuracy Tests") lists fp8
+ * e4m3 with descales among the FA4 configurations; the vLLM MLA-prefill docs
+ * page has the fp8 static per-tensor symmetric output quantisation
+ * (supports_quant_output with kFp8StaticTensorSym, the output_scale
+ * argument).  What is computed (readings; the pages give no formula):
+ *
+ *     Q~ = Q * q_descale[b, hk], K~ = K * k_descale[b, hk],
+ *     V~ = V * v_descale[b, hk]          (hk = the KV head of query head h)
+ *     O, LSE = the forward above on Q~, K~, V~ (same masks and scale)
+ *     out = O in bf16, or, with out_scale, e4m3(clamp(O / *out_scale,
+ *           -448, 448)) rounded to nearest even
+ *
+ *   q, k, v        e4m3 bytes (OCP E4M3: bias 7, no infinities, 0x7F/0xFF
+ *                  NaN, largest 448), [total, heads, dim] as va_tensor with
+ *                  strides in bytes; rows and heads 16-byte aligned
+ *   q_descale, k_descale, v_descale
+ *                  device fp32 [batch, H_kv] contiguous (entry b * H_kv +
+ *                  hk), or NULL for all ones; a per-tensor scale is the case
+ *                  of equal entries
+ *   out            bf16 [total_q, H, d_v], or e4m3 when out_scale is given
+ *   out_scale      NULL, or a device fp32 scalar > 0 (not checked)
+ *   num_splits, workspace, workspace_bytes
+ *                  as for varlen_attn_fwd_splitkv (1 = no split); a split
+ *                  call's output is bf16, so out_scale must be NULL there
+ *   other arguments as for varlen_attn_fwd
+ *
+ * Supported (d_qk, d_v): (64,64), (128,128), (192,128).  The kernel rounds
+ * the softmax probabilities to e4m3 for the PV product (each p <= 256, so
+ * none saturates) and normalises by the fp32 sum of the unrounded ones: O
+ * carries a relative rounding of up to 2^-4 per term, the LSE is as exact
+ * as for bf16 inputs.  Returns VA_OK or a VA_ERR_* code as
+ * varlen_attn_fwd_splitkv; VA_ERR_ARG also for out_scale with num_splits >
+ * 1, VA_ERR_ALIGN for a descale or out_scale pointer not 4-byte aligned.
+ */
+int varlen_attn_fwd_fp8(const va_tensor* q, const va_tensor* k, const va_tensor* v,
+                        const float* q_descale, const float* k_descale, const float* v_descale,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                        int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale, int32_t causal,
+                        int32_t window_left, int32_t window_right, const va_tensor* out,
+                        const float* out_scale, float* lse, int32_t num_splits, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 /* Workspace bytes varlen_attn_fwd_splitkv needs (0 for num_splits <= 1). Host only. */
 size_t varlen_attn_splitkv_workspace_bytes(int64_t total_q, int32_t num_heads, int32_t head_dim_v,
                                            int32_t num_splits);

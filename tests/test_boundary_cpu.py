@@ -485,3 +485,46 @@ def test_merge_rejects_bad_arguments():
 def test_merge_of_no_rows_launches_nothing():
     z = _t(rows=0, data=0)
     assert _merge(a=z, b=z, out=z, lse_a=0, lse_b=0, lse=0) == B.VA_OK
+
+
+# ---------------------------------------------------------------------------
+# fp8 entry point: validation only (every call fails or returns before launching)
+# ---------------------------------------------------------------------------
+def _call_fp8(q=None, k=None, v=None, out=None, dq=0, dk=0, dv=0, out_scale=0, batch=1, mq=10, mk=10,
+              splits=1, ws=0, ws_bytes=0, lse=0):
+    q = q if q is not None else _t(dim=128, row_stride=256, head_stride=128)
+    k = k if k is not None else _t(dim=128, row_stride=256, head_stride=128)
+    v = v if v is not None else _t(dim=128, row_stride=256, head_stride=128)
+    out = out if out is not None else _t(dim=128, row_stride=256, head_stride=128)
+    return B.raw_fwd_fp8(q, k, v, dq, dk, dv, FAKE, FAKE, batch, mq, mk, 0.1, 0, -1, -1, out, out_scale, lse,
+                         splits, ws, ws_bytes, 0)
+
+
+def test_fp8_head_dims():
+    # (64,64), (128,128), (192,128) only: the fp8 MFMA takes 64 head dims at a time
+    for d in (72, 80):
+        t = _t(dim=d, row_stride=2 * d, head_stride=d)
+        assert _call_fp8(q=t, k=t, v=t, out=t) == B.VA_ERR_HEADDIM
+
+
+def test_fp8_alignment_is_in_bytes():
+    # one byte per element: strides must be multiples of 16 elements (bf16 output: 8)
+    assert _call_fp8(q=_t(dim=128, row_stride=264, head_stride=128)) == B.VA_ERR_ALIGN
+    assert _call_fp8(k=_t(dim=128, row_stride=256, head_stride=136)) == B.VA_ERR_ALIGN
+    assert _call_fp8(dq=FAKE + 2) == B.VA_ERR_ALIGN
+    assert _call_fp8(dv=FAKE + 1) == B.VA_ERR_ALIGN
+    assert _call_fp8(out_scale=FAKE + 3) == B.VA_ERR_ALIGN
+
+
+def test_fp8_scalar_arguments():
+    assert _call_fp8(splits=0) == B.VA_ERR_ARG
+    assert _call_fp8(splits=129) == B.VA_ERR_ARG
+    assert _call_fp8(out_scale=FAKE, splits=2) == B.VA_ERR_ARG  # a split call's output is bf16
+    assert _call_fp8(splits=2, ws=0) == B.VA_ERR_NULL
+    assert _call_fp8(splits=2, ws=FAKE + 16, ws_bytes=1 << 30) == B.VA_ERR_ALIGN
+    assert _call_fp8(splits=2, ws=FAKE, ws_bytes=16) == B.VA_ERR_ARG
+
+
+def test_fp8_empty_work_returns_ok_without_launch():
+    assert _call_fp8(batch=0) == B.VA_OK
+    assert _call_fp8(mq=0) == B.VA_OK

@@ -1,0 +1,269 @@
+"""GPU parity of the fp8 e4m3 path (``varlen_attn_fwd_fp8``) against the fp64
+oracle on the dequantised inputs (marked ``gpu``).
+
+Tolerance, derived from the kernel's arithmetic.  The scores come from exact
+e4m3 products accumulated in fp32 and the LSE from the fp32 sum of the
+unrounded probabilities, so |dLSE| <= 1e-3 as for bf16 inputs.  O differs
+from the exact result by the e4m3 rounding of each probability before the
+PV product: a normal p is off by at most 2^-4 p (half an ulp of a 3-bit
+mantissa), a subnormal one by at most 2^-10, both measured against the row's
+true maximum (the running max a tile was scaled by never exceeds it).  So,
+per output element d of a row with probabilities p_j = exp(s_j - max) over
+its visible keys, l = sum p_j and dequantised values v_jd:
+
+    |dO_d| <= (2^-4 sum_j p_j |v_jd| + 2^-10 sum_j |v_jd|) / l
+              + 2^-8 |O_d|           (bf16 rounding of O, with margin)
+              + 1e-3 sum_j p_j |v_jd| / l + 1e-5   (fp32 arithmetic)
+
+checked element by element.  With an e4m3 output the decoded code times
+out_scale may in addition be off by half an e4m3 ulp of O / out_scale.
+
+Integer-exact checks: descales None equal descales of ones bit for bit, and
+halving softmax_scale while doubling every q descale gives the same bits (an
+exact power-of-two change of the fp32 score scale).
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import varlen_attention_forward_amd as va
+from varlen_attention_forward_amd import workloads
+from helpers import f64
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL_LSE = 1e-3
+DIMS = [(64, 64), (128, 128), (192, 128)]
+LEN_SETS = {
+    "ragged": ([1, 63, 64, 65, 127, 128, 129, 255, 256, 257], None),
+    "q_lt_k": ([1, 40, 64, 100, 129], [70, 64, 200, 100, 300]),
+    "empty_segments": ([0, 37, 0, 190, 5], [0, 0, 50, 190, 0]),
+}
+MODES = {
+    "full": (False, (-1, -1)),
+    "causal": (True, (-1, -1)),
+    "window": (False, (40, 17)),
+    "causal_window": (True, (70, -1)),
+}
+
+
+def u8(t):
+    return t.detach().cpu().view(torch.uint8).numpy()
+
+
+def make(lens_q, lens_k, dims, seed, mode="full", heads=4, heads_k=None, std=1.0):
+    causal, window = MODES[mode]
+    return workloads.make_fp8_inputs(lens_q, lens_k if lens_k is not None else lens_q, heads, dims[0], dims[1],
+                                     seed, causal=causal, window=window, num_heads_k=heads_k, std=std)
+
+
+def run_fp8(inp, out_scale=None, num_splits=1, return_lse=True, descales=True, scale=None, q_descale=None):
+    d = inp.to(DEV)
+    lse = None
+    if return_lse:
+        lse = torch.full((inp.q.shape[1], inp.q.shape[0]), float("nan"), dtype=torch.float32, device=DEV)
+    os_t = None if out_scale is None else torch.tensor([out_scale], dtype=torch.float32, device=DEV)
+    qd = d.q_descale if q_descale is None else q_descale.to(DEV)
+    res = va.varlen_attn_fwd_fp8(
+        d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, inp.max_seqlen_q, inp.max_seqlen_k,
+        softmax_scale=inp.softmax_scale if scale is None else scale, causal=inp.causal, window_size=inp.window,
+        q_descale=qd if descales else None, k_descale=d.k_descale if descales else None,
+        v_descale=d.v_descale if descales else None, out_scale=os_t, return_lse=return_lse, lse=lse,
+        num_splits=num_splits,
+    )
+    torch.cuda.synchronize()
+    return res if return_lse else (res, None)
+
+
+def oracle_fp8(inp, rows=None, heads=None):
+    wl, wr = inp.window
+    return oracle.attention_fwd_fp8(
+        u8(inp.q), u8(inp.k), u8(inp.v), inp.cu_seqlens_q.tolist(), inp.cu_seqlens_k.tolist(), inp.softmax_scale,
+        causal=inp.causal, window_left=wl, window_right=wr, q_descale=inp.q_descale.numpy(),
+        k_descale=inp.k_descale.numpy(), v_descale=inp.v_descale.numpy(), rows=rows, heads=heads,
+    )
+
+
+def o_tolerance(inp, rows=None, heads=None):
+    """The per-element bound of the module docstring, NaN off the requested rows."""
+    H, H_kv = inp.q.shape[1], inp.k.shape[1]
+    grp = H // H_kv
+    cq, ck = inp.cu_seqlens_q.tolist(), inp.cu_seqlens_k.tolist()
+    qd = oracle.dequantize(u8(inp.q), cq, np.repeat(inp.q_descale.numpy(), grp, axis=1))
+    kd = oracle.dequantize(u8(inp.k), ck, inp.k_descale.numpy())
+    vd = oracle.dequantize(u8(inp.v), ck, inp.v_descale.numpy())
+    scale = float(np.float32(inp.softmax_scale))
+    wl, wr = inp.window
+    tol = np.full((inp.q.shape[0], H, inp.v.shape[2]), np.nan)
+    want = None
+    if rows is not None:
+        want = np.zeros(inp.q.shape[0], dtype=bool)
+        want[np.asarray(rows)] = True
+    for b in range(len(cq) - 1):
+        Lq, Lk = cq[b + 1] - cq[b], ck[b + 1] - ck[b]
+        idx = np.arange(Lq)
+        if want is not None:
+            idx = idx[want[cq[b]:cq[b + 1]]]
+        if len(idx) == 0:
+            continue
+        lo, hi = oracle.visible_interval(idx, Lq, Lk, inp.causal, wl, wr)
+        j = np.arange(Lk)[None, :]
+        vis = (j >= lo[:, None]) & (j <= hi[:, None])
+        for h in (range(H) if heads is None else heads):
+            hk = h // grp
+            s = scale * (qd[cq[b] + idx, h, :] @ kd[ck[b]:ck[b + 1], hk, :].T)
+            s = np.where(vis, s, -np.inf)
+            m = s.max(axis=1) if Lk else np.full(len(idx), -np.inf)
+            ok = np.isfinite(m)
+            p = np.exp(s - np.where(ok, m, 0.0)[:, None])
+            l = np.where(ok, p.sum(axis=1), 1.0)[:, None]
+            av = np.abs(vd[ck[b]:ck[b + 1], hk, :])
+            a = (p @ av) / l
+            o = np.abs(p @ vd[ck[b]:ck[b + 1], hk, :]) / l
+            c = (vis.astype(np.float64) @ av) / l
+            tol[cq[b] + idx, h, :] = 2.0 ** -4 * a + 2.0 ** -10 * c + 2.0 ** -8 * o + 1e-3 * a + 1e-5
+    return tol
+
+
+def assert_fp8_parity(inp, out, lse, rows=None, heads=None, what=""):
+    ref_o, ref_lse = oracle_fp8(inp, rows=rows, heads=heads)
+    tol = o_tolerance(inp, rows=rows, heads=heads)
+    o = f64(out)
+    sel = ~np.isnan(ref_o)
+    assert np.all(np.isfinite(o[sel])), "%s: non-finite output" % what
+    err = np.abs(o - ref_o)
+    bad = sel & (err > tol)
+    assert not bad.any(), "%s: %d elements over the bound, worst excess %.3e (err %.3e)" % (
+        what, int(bad.sum()), float(np.max((err - tol)[bad])), float(np.max(err[bad])))
+    worst = float(np.max(err[sel])) if sel.any() else 0.0
+    if lse is not None:
+        l = f64(lse)
+        lsel = ~np.isnan(ref_lse)
+        neg = lsel & (ref_lse == -np.inf)
+        assert np.array_equal(l[lsel] == -np.inf, neg[lsel]), "%s: -inf LSE rows differ" % what
+        fin = lsel & ~neg
+        err_l = float(np.max(np.abs(l[fin] - ref_lse[fin]))) if fin.any() else 0.0
+        assert err_l <= TOL_LSE, "%s: max|dLSE| = %.3e" % (what, err_l)
+    return worst
+
+
+@pytest.mark.parametrize("dims", DIMS, ids=lambda d: "d%d_%d" % d)
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("lens", list(LEN_SETS))
+def test_fp8_small_parity(dims, mode, lens):
+    lq, lk = LEN_SETS[lens]
+    inp = make(lq, lk, dims, seed=zlib.crc32(("%s %s %s" % (dims, mode, lens)).encode()) % 10000, mode=mode)
+    out, lse = run_fp8(inp)
+    assert out.dtype == torch.bfloat16
+    assert_fp8_parity(inp, out, lse, what="%s %s %s" % (dims, mode, lens))
+
+
+@pytest.mark.parametrize("dims", [(128, 128), (192, 128)], ids=lambda d: "d%d_%d" % d)
+@pytest.mark.parametrize("heads,heads_k", [(8, 1), (8, 2), (6, 3)])
+@pytest.mark.parametrize("mode", ["full", "causal"])
+def test_fp8_grouped_kv_heads(dims, heads, heads_k, mode):
+    inp = make([100, 300, 17], [260, 300, 80], dims, seed=heads * 7 + heads_k, mode=mode, heads=heads,
+               heads_k=heads_k)
+    out, lse = run_fp8(inp)
+    assert_fp8_parity(inp, out, lse, what="gqa %s %d/%d %s" % (dims, heads, heads_k, mode))
+
+
+@pytest.mark.parametrize("dims", DIMS, ids=lambda d: "d%d_%d" % d)
+@pytest.mark.parametrize("lens", ["le64", "le128"])
+@pytest.mark.parametrize("mode", ["full", "causal"])
+def test_fp8_packed_short_segments(dims, lens, mode):
+    g = np.random.default_rng(len(lens) + dims[0])
+    hi = 64 if lens == "le64" else 128
+    lq = g.integers(0, hi + 1, 23).tolist()
+    if mode == "causal":
+        lk = [x + int(g.integers(0, 30)) for x in lq]
+    else:
+        lk = [int(g.integers(0, 200)) for _ in lq]
+    inp = make(lq, lk, dims, seed=hi + dims[0], mode=mode, heads=4)
+    assert va.plan(dims[0], dims[1], len(lq), 4, max(lq), max(lk))["segments_per_block"] > 1
+    out, lse = run_fp8(inp)
+    assert_fp8_parity(inp, out, lse, what="packed %s %s %s" % (dims, lens, mode))
+
+
+@pytest.mark.parametrize("dims", DIMS, ids=lambda d: "d%d_%d" % d)
+@pytest.mark.parametrize("splits", [2, 5])
+@pytest.mark.parametrize("mode", ["full", "causal"])
+def test_fp8_split_kv(dims, splits, mode):
+    inp = make([64, 300, 1], [2000, 900, 700], dims, seed=splits * 13 + dims[0], mode=mode, heads=4)
+    out, lse = run_fp8(inp, num_splits=splits)
+    assert_fp8_parity(inp, out, lse, what="split %s %d %s" % (dims, splits, mode))
+
+
+@pytest.mark.parametrize("dims", DIMS, ids=lambda d: "d%d_%d" % d)
+@pytest.mark.parametrize("mode", ["full", "causal"])
+def test_fp8_output_quantisation(dims, mode):
+    inp = make([64, 129, 255], None, dims, seed=dims[0] + 3, mode=mode, heads=4)
+    ref_o, _ = oracle_fp8(inp)
+    s = float(np.float32(np.nanmax(np.abs(ref_o)) / 200.0))
+    out, lse = run_fp8(inp, out_scale=s)
+    assert out.dtype == torch.float8_e4m3fn
+    got = oracle.e4m3_decode(u8(out)) * s
+    tol = o_tolerance(inp)
+    y = np.abs(ref_o) / s + tol / s
+    half_ulp = s * np.maximum(2.0 ** -4 * y, 2.0 ** -10)
+    sel = ~np.isnan(ref_o)
+    err = np.abs(got - ref_o)
+    assert not (sel & (err > tol + half_ulp)).any(), "max excess %.3e" % float(np.max((err - tol - half_ulp)[sel]))
+    # the LSE does not depend on the output format
+    _, lse2 = run_fp8(inp)
+    assert torch.equal(lse, lse2)
+
+
+def test_fp8_output_scale_with_splits_is_rejected():
+    inp = make([64], None, (128, 128), seed=1)
+    with pytest.raises(ValueError, match="VA_ERR_ARG"):
+        run_fp8(inp, out_scale=0.5, num_splits=2)
+
+
+def test_fp8_descales_none_are_ones_bit_exact():
+    inp = make([100, 257], [300, 257], (128, 128), seed=21, mode="causal")
+    ones = dataclass_with_unit_descales(inp)
+    a, la = run_fp8(inp, descales=False)
+    b, lb = run_fp8(ones)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def dataclass_with_unit_descales(inp):
+    import dataclasses
+
+    one = torch.ones_like(inp.q_descale)
+    return dataclasses.replace(inp, q_descale=one, k_descale=one.clone(), v_descale=one.clone())
+
+
+@pytest.mark.parametrize("dims", [(128, 128), (192, 128)], ids=lambda d: "d%d_%d" % d)
+def test_fp8_power_of_two_rescale_is_bit_exact(dims):
+    inp = make([77, 300], [200, 300], dims, seed=22, mode="causal")
+    a, la = run_fp8(inp)
+    b, lb = run_fp8(inp, scale=inp.softmax_scale / 2, q_descale=inp.q_descale * 2)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_fp8_rows_outside_segments_untouched():
+    inp = make([0, 50, 0, 70], [10, 50, 0, 90], (128, 128), seed=23)
+    d = inp.to(DEV)
+    total = inp.q.shape[0]
+    out = torch.full((total + 5, 4, 128), 7.0, dtype=torch.bfloat16, device=DEV)
+    cu_q = torch.tensor([2, 2, 52, 52, 122], dtype=torch.int32, device=DEV)  # rows 0, 1 belong to no segment
+    q = torch.zeros((total + 5, 4, 128), dtype=torch.float8_e4m3fn, device=DEV)
+    q[2:2 + total] = d.q
+    va.varlen_attn_fwd_fp8(q, d.k, d.v, cu_q, d.cu_seqlens_k, inp.max_seqlen_q, inp.max_seqlen_k,
+                           q_descale=d.q_descale, k_descale=d.k_descale, v_descale=d.v_descale, out=out)
+    torch.cuda.synchronize()
+    assert bool((out[:2] == 7.0).all()) and bool((out[2 + total:] == 7.0).all())
+
+
+def test_fp8_empty_and_zero_key_segments():
+    inp = make([0, 5, 3], [0, 0, 9], (64, 64), seed=24)
+    out, lse = run_fp8(inp)
+    assert bool((out[:5] == 0).all())
+    assert bool(torch.isinf(lse[:, :5]).all())
+    assert_fp8_parity(inp, out, lse, what="zero keys")

@@ -13,17 +13,21 @@ from ._binding import (  # noqa: F401
     library,
     plan,
     raw_fwd,
+    raw_fwd_fp8,
     raw_fwd_splitkv,
     splitkv_workspace_bytes,
     status_string,
     tile_range,
     varlen_attn_fwd,
+    varlen_attn_fwd_fp8,
     varlen_attn_merge,
     work_unit,
 )
 
 __all__ = [
     "varlen_attn_fwd",
+    "varlen_attn_fwd_fp8",
+    "raw_fwd_fp8",
     "varlen_attn_merge",
     "status_string",
     "tile_range",

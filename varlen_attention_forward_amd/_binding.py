@@ -43,6 +43,7 @@ EXPORTED_SYMBOLS = (
     "varlen_attn_fwd_splitkv",
     "varlen_attn_splitkv_workspace_bytes",
     "varlen_attn_num_splits",
+    "varlen_attn_fwd_fp8",
 )
 
 
@@ -101,6 +102,16 @@ def library() -> ctypes.CDLL:
     lib.varlen_attn_fwd_splitkv.restype = ctypes.c_int
     lib.varlen_attn_fwd_splitkv.argtypes = lib.varlen_attn_fwd.argtypes[:-1] + [
         ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.varlen_attn_fwd_fp8.restype = ctypes.c_int
+    lib.varlen_attn_fwd_fp8.argtypes = [
+        P(VaTensor), P(VaTensor), P(VaTensor),
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, P(VaTensor),
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+        ctypes.c_size_t, ctypes.c_void_p,
+    ]
     lib.varlen_attn_splitkv_workspace_bytes.restype = ctypes.c_size_t
     lib.varlen_attn_splitkv_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                         ctypes.c_int32]
@@ -212,6 +223,23 @@ def raw_fwd_splitkv(q: VaTensor, k: VaTensor, v: VaTensor, cu_q_ptr: int, cu_k_p
     )
 
 
+def raw_fwd_fp8(q: VaTensor, k: VaTensor, v: VaTensor, q_descale_ptr: int, k_descale_ptr: int,
+                v_descale_ptr: int, cu_q_ptr: int, cu_k_ptr: int, batch: int, max_seqlen_q: int,
+                max_seqlen_k: int, softmax_scale: float, causal: int, window_left: int, window_right: int,
+                out: VaTensor, out_scale_ptr: int, lse_ptr: int, num_splits: int, workspace_ptr: int,
+                workspace_bytes: int, stream: int) -> int:
+    """The fp8 C entry point with plain descriptors; returns the status code."""
+    return library().varlen_attn_fwd_fp8(
+        ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+        ctypes.c_void_p(q_descale_ptr), ctypes.c_void_p(k_descale_ptr), ctypes.c_void_p(v_descale_ptr),
+        ctypes.c_void_p(cu_q_ptr), ctypes.c_void_p(cu_k_ptr), int(batch),
+        int(max_seqlen_q), int(max_seqlen_k), float(softmax_scale),
+        int(causal), int(window_left), int(window_right),
+        ctypes.byref(out), ctypes.c_void_p(out_scale_ptr), ctypes.c_void_p(lse_ptr), int(num_splits),
+        ctypes.c_void_p(workspace_ptr), int(workspace_bytes), ctypes.c_void_p(stream),
+    )
+
+
 def splitkv_workspace_bytes(total_q: int, num_heads: int, head_dim_v: int, num_splits: int) -> int:
     """Workspace bytes ``varlen_attn_fwd(..., num_splits=S)`` needs (host call)."""
     return int(library().varlen_attn_splitkv_workspace_bytes(total_q, num_heads, head_dim_v, num_splits))
@@ -227,13 +255,14 @@ def auto_num_splits(head_dim_qk: int, head_dim_v: int, batch: int, num_heads: in
     return n.value
 
 
-def _desc(t, name: str) -> VaTensor:
+def _desc(t, name: str, dtype=None) -> VaTensor:
     import torch
 
+    dtype = torch.bfloat16 if dtype is None else dtype
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if t.dtype != torch.bfloat16:
-        raise TypeError("%s must be bfloat16, got %s" % (name, t.dtype))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if not t.is_cuda:
         raise ValueError("%s must be on a GPU device" % name)
     if t.dim() != 3:
@@ -315,6 +344,100 @@ def varlen_attn_fwd(
             _desc(out, "out"), lse.data_ptr() if lse is not None else 0, num_splits,
             ws.data_ptr(), nbytes, stream,
         )
+    _raise_for(st)
+    if return_lse:
+        return out, lse
+    return out
+
+
+def _check_cu(cu_seqlens_q, cu_seqlens_k) -> int:
+    import torch
+
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if not isinstance(cu, torch.Tensor) or cu.dtype != torch.int32 or not cu.is_cuda:
+            raise TypeError("%s must be an int32 GPU tensor" % name)
+        if cu.dim() != 1 or not cu.is_contiguous():
+            raise ValueError("%s must be a contiguous 1-D tensor" % name)
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have batch + 1 entries")
+    return cu_seqlens_q.numel() - 1
+
+
+def _f32_ptr(t, name: str, numel: int) -> int:
+    import torch
+
+    if t is None:
+        return 0
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+        raise TypeError("%s must be a contiguous float32 GPU tensor" % name)
+    if t.numel() != numel:
+        raise ValueError("%s must have %d elements, got %d" % (name, numel, t.numel()))
+    return t.data_ptr()
+
+
+def varlen_attn_fwd_fp8(
+    q,
+    k,
+    v,
+    cu_seqlens_q,
+    cu_seqlens_k,
+    max_seqlen_q: int,
+    max_seqlen_k: int,
+    softmax_scale: Optional[float] = None,
+    causal: bool = False,
+    window_size: Tuple[int, int] = (-1, -1),
+    q_descale=None,
+    k_descale=None,
+    v_descale=None,
+    out_scale=None,
+    out=None,
+    return_lse: bool = False,
+    lse=None,
+    num_splits: int = 1,
+):
+    """Varlen attention forward on fp8 e4m3 inputs, on the current HIP stream.
+
+    ``q``/``k``/``v`` are ``torch.float8_e4m3fn`` tensors shaped as for
+    ``varlen_attn_fwd``; ``q_descale``/``k_descale``/``v_descale`` fp32
+    [batch, H_kv] GPU tensors (None: ones) multiply the decoded values of
+    segment b and KV head hk.  ``out_scale`` (a one-element fp32 GPU tensor)
+    makes ``out`` e4m3 codes of O / out_scale; else ``out`` is bf16.
+    ``num_splits`` as for ``varlen_attn_fwd`` (bf16 output only).
+    """
+    import torch
+
+    batch = _check_cu(cu_seqlens_q, cu_seqlens_k)
+    total_q, H, d_qk = q.shape
+    H_kv, d_v = v.shape[1], v.shape[2]
+    if softmax_scale is None:
+        softmax_scale = d_qk ** -0.5
+    out_dtype = torch.float8_e4m3fn if out_scale is not None else torch.bfloat16
+    if out is None:
+        out = torch.empty((total_q, H, d_v), dtype=out_dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous() or tuple(lse.shape) != (H, total_q):
+            raise ValueError("lse must be a contiguous float32 GPU tensor of shape [H, total_q]")
+    wl, wr = window_size
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    if num_splits == 0:
+        num_splits = auto_num_splits(d_qk, d_v, batch, H, max_seqlen_q, max_seqlen_k)
+    nbytes, ws_ptr = 0, 0
+    if num_splits > 1:
+        nbytes = splitkv_workspace_bytes(total_q, H, d_v, num_splits)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+        ws_ptr = ws.data_ptr()
+    f8 = torch.float8_e4m3fn
+    st = raw_fwd_fp8(
+        _desc(q, "q", f8), _desc(k, "k", f8), _desc(v, "v", f8),
+        _f32_ptr(q_descale, "q_descale", batch * H_kv), _f32_ptr(k_descale, "k_descale", batch * H_kv),
+        _f32_ptr(v_descale, "v_descale", batch * H_kv),
+        cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), batch,
+        max_seqlen_q, max_seqlen_k, softmax_scale, int(bool(causal)), wl, wr,
+        _desc(out, "out", out_dtype), _f32_ptr(out_scale, "out_scale", 1),
+        lse.data_ptr() if lse is not None else 0, num_splits, ws_ptr, nbytes, stream,
+    )
     _raise_for(st)
     if return_lse:
         return out, lse

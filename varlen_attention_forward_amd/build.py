@@ -1,7 +1,8 @@
 """Ahead-of-time build of the HIP library for gfx950.
 
 ``python -m varlen_attention_forward_amd.build`` compiles
-``csrc/varlen_attn_fwd.hip`` and ``csrc/merge_states.hip`` into
+``csrc/varlen_attn_fwd.hip``, ``csrc/varlen_attn_fwd_fp8.hip`` and
+``csrc/merge_states.hip`` into
 ``libvarlen_attn.so`` next to this file.
 hipcc cross-compiles for gfx950 without a GPU present.
 """
@@ -18,7 +19,11 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(REPO_DIR, "include")
 LIB_NAME = "libvarlen_attn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = [os.path.join(CSRC, "varlen_attn_fwd.hip"), os.path.join(CSRC, "merge_states.hip")]
+SOURCES = [
+    os.path.join(CSRC, "varlen_attn_fwd.hip"),
+    os.path.join(CSRC, "varlen_attn_fwd_fp8.hip"),
+    os.path.join(CSRC, "merge_states.hip"),
+]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

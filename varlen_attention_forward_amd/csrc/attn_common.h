@@ -1,0 +1,235 @@
+// Device-side pieces shared by the attention kernels (bf16 and fp8 e4m3
+// inputs): kernel parameters, the direct-to-LDS load, the workgroup barrier,
+// the work-unit decode and cross-half lane reductions; plus the host-side
+// description of a kernel instantiation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "tile_schedule.h"
+#include "varlen_attn.h"
+
+// Kernel-local lambdas must inline: out-of-line copies would pass the
+// register arrays they capture through scratch memory.
+#define VA_INLINE __attribute__((always_inline))
+
+namespace va {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr float kRescaleTau = 8.0f;     // lazy rescale threshold, log2 units
+constexpr float kSumLimit = 256.0f;     // 2^kRescaleTau: a tile row sum this small bounds every p
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every range: reads 0
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
+
+struct Params {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int64_t q_row, q_head, k_row, k_head, v_row, v_head, o_row, o_head;  // elements
+  int64_t total_q;
+  int32_t batch, heads, n_qt;
+  int32_t heads_k;  // KV heads; heads is a multiple of it
+  // Split-KV: with num_splits > 1 the grid holds num_splits copies of the
+  // n_units work units; copy s takes the s-th of num_splits equal runs of
+  // each unit's key tiles and writes a normalised fp32 partial O and its
+  // LSE instead of out / lse (combined by combine_splits).
+  int32_t num_splits, n_units;
+  int32_t pack;  // segments per workgroup (segments_per_block), 1, 2 or 4
+  float* part_o;    // [num_splits, total_q, heads, d_v]
+  float* part_lse;  // [num_splits, heads, total_q]
+  int32_t causal, wl, wr;
+  float scale_log2;  // softmax_scale * log2(e)
+  // fp8 e4m3 inputs only: descales per (segment, KV head), [batch, heads_k]
+  // fp32 each, null meaning 1; out_scale (one fp32) non-null when out holds
+  // e4m3 codes of O / *out_scale instead of bf16.
+  const float* q_descale;
+  const float* k_descale;
+  const float* v_descale;
+  const float* out_scale;
+};
+
+// 16-byte-per-lane load from a buffer straight into LDS: lane i's bytes land
+// at dst + 16 i; offsets past the buffer's range read as zero.  (A plain
+// device function: inside the kernel template the builtin trips the host pass.)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, lds_char* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+}
+
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
+template <int N>
+struct Int {
+  static constexpr int value = N;
+};
+
+// f(Int<I>{}), ..., f(Int<N - 1>{}) in order, unrolled.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Int<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)a;  // round to nearest even
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+
+// Workgroup barrier without __syncthreads()'s release/acquire fences.  With
+// LDS-DMA in flight the release fence turns into s_waitcnt vmcnt(0), making
+// every wave wait for the prefetch it has just issued; the kernels that use
+// this wait for the loads a barrier must cover themselves.  LDS reads are
+// drained first so no stage is overwritten under a read still in flight,
+// and the empty asm statements keep the compiler from moving memory
+// accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// This workgroup's work unit (tile_schedule.h) and its segment's bounds:
+// longest-first dealing when it applies, computed by every wave from
+// cu_seqlens with one lane per segment (whose loads then also give the
+// bounds); else dealing in packing order.
+struct BlockWork {
+  WorkUnit u;
+  int q0, lq, k0, lk;  // the segment's first query / key row and lengths
+};
+
+template <bool PACKED>
+__device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int block_m, int64_t w) {
+  BlockWork r;
+  if constexpr (PACKED) {  // a group of pack short segments: one unit per (group, head), in packing order
+    const uint32_t groups = ((uint32_t)p.batch + (uint32_t)p.pack - 1u) / (uint32_t)p.pack;
+    r.u = decode_block((uint32_t)w, groups, (uint32_t)p.heads, 1u, p.causal);
+    r.u.h = query_head(r.u.h, p.heads, p.heads_k);
+    if (r.u.valid) {
+      const int first = r.u.b * p.pack, last = min(first + p.pack, p.batch);
+      r.q0 = p.cu_q[first];
+      r.lq = p.cu_q[last] - r.q0;
+      r.k0 = p.cu_k[first];
+      r.lk = p.cu_k[last] - r.k0;
+    }
+    return r;
+  }
+  if (p.batch <= kLptMaxBatch) {
+    int cq0 = 0, cq1 = 0, ck0 = 0, ck1 = -1;
+    if (lane < p.batch) {
+      cq0 = p.cu_q[lane];
+      cq1 = p.cu_q[lane + 1];
+      ck0 = p.cu_k[lane];
+      ck1 = p.cu_k[lane + 1];
+    }
+    const int lq = cq1 - cq0, lk = ck1 - ck0;  // lk = -1 on lanes past the batch
+    const int lq0 = __builtin_amdgcn_readfirstlane(lq), lk0 = __builtin_amdgcn_readfirstlane(lk);
+    if (__ballot(lane < p.batch && (lq != lq0 || lk != lk0)) != 0) {
+      const int x = (int)(w & 7);
+      const int k = (int)snake_quads((uint32_t)(w >> 3), (uint32_t)p.n_units / 8u);
+      int rank = 0;
+      for (int j = 0; j < p.batch; ++j) {
+        const int kj = __builtin_amdgcn_readlane(lk, j);
+        rank += (kj > lk || (kj == lk && j < lane)) ? 1 : 0;
+      }
+      const int nqt = lane < p.batch ? (lq + block_m - 1) / block_m : 0;
+      const int h0 = xcd_first_head(rank, p.heads, x);
+      const int n = xcd_head_count(h0, p.heads) * nqt;
+      int pre = 0;  // blocks of this XCD before this segment's
+      for (int j = 0; j < p.batch; ++j)
+        pre += __builtin_amdgcn_readlane(rank, j) < rank ? __builtin_amdgcn_readlane(n, j) : 0;
+      const uint64_t hit = __ballot(lane < p.batch && k >= pre && k < pre + n);
+      r.u.valid = hit != 0;
+      r.u.b = r.u.h = r.u.qt = -1;
+      if (hit != 0) {
+        const int i = (int)__builtin_ctzll(hit);
+        const int local = k - __builtin_amdgcn_readlane(pre, i);
+        const int nq = __builtin_amdgcn_readlane(nqt, i);
+        const int qi = local % nq;
+        r.u.b = i;
+        r.u.h = query_head(__builtin_amdgcn_readlane(h0, i) + 8 * (local / nq), p.heads, p.heads_k);
+        r.u.qt = p.causal ? nq - 1 - qi : qi;
+      }
+    } else {
+      r.u = decode_block((uint32_t)w, (uint32_t)p.batch, (uint32_t)p.heads, (uint32_t)p.n_qt, p.causal);
+      r.u.h = query_head(r.u.h, p.heads, p.heads_k);
+    }
+    if (r.u.valid) {
+      const int b = __builtin_amdgcn_readfirstlane(r.u.b);
+      r.q0 = __builtin_amdgcn_readlane(cq0, b);
+      r.lq = __builtin_amdgcn_readlane(lq, b);
+      r.k0 = __builtin_amdgcn_readlane(ck0, b);
+      r.lk = __builtin_amdgcn_readlane(lk, b);
+    }
+    return r;
+  }
+  r.u = decode_block((uint32_t)w, (uint32_t)p.batch, (uint32_t)p.heads, (uint32_t)p.n_qt, p.causal);
+  r.u.h = query_head(r.u.h, p.heads, p.heads_k);
+  if (r.u.valid) {
+    const int b = __builtin_amdgcn_readfirstlane(r.u.b);
+    r.q0 = p.cu_q[b];
+    r.lq = p.cu_q[b + 1] - r.q0;
+    r.k0 = p.cu_k[b];
+    r.lk = p.cu_k[b + 1] - r.k0;
+  }
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const lds_char* base, int byte_off) {
+  return *(const __attribute__((address_space(3))) bf16x8*)(base + byte_off);
+}
+
+// Cross-half (lane l and lane l ^ 32) max and sum: v_permlane32_swap
+// leaves lane l's and lane l ^ 32's values in the two results.
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Lane l ^ 32's value for lanes 32-63, the lane's own for lanes 0-31:
+// broadcasts what lanes 0-31 hold to the whole wave.
+__device__ __forceinline__ float from_lower_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]);
+}
+
+// One kernel instantiation and its launch shape.
+struct Variant {
+  const void* fn;
+  int lds_bytes;
+  int block_m;
+  int block_n;
+  int threads;
+  const char* name;
+};
+
+// The fp8 e4m3 kernel (varlen_attn_fwd_fp8.hip): whether it has an
+// instantiation for (dqk, dv), and that instantiation.
+bool fp8_supported_dims(int dqk, int dv);
+Variant fp8_variant(int dqk, int dv, bool packed);
+
+}  // namespace va

@@ -38,56 +38,9 @@
 // "Modifications": softmax.py update_row_max, "fast exp2, rescale
 // threshold") and masking only on the tiles that need it (same section: only
 // unmasked steady-state tiles take the fast path).
-#include <hip/hip_runtime.h>
-#include <float.h>
-#include <math.h>
-#include <stdint.h>
-
-#include "tile_schedule.h"
-#include "varlen_attn.h"
-
-// Kernel-local lambdas must inline: out-of-line copies would pass the
-// register arrays they capture through scratch memory.
-#define VA_INLINE __attribute__((always_inline))
+#include "attn_common.h"
 
 namespace va {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) char lds_char;
-
-constexpr float kRescaleTau = 8.0f;     // lazy rescale threshold, log2 units
-constexpr float kSumLimit = 256.0f;     // 2^kRescaleTau: a tile row sum this small bounds every p
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every range: reads 0
-constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
-
-struct Params {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  uint16_t* o;
-  float* lse;
-  const int32_t* cu_q;
-  const int32_t* cu_k;
-  int64_t q_row, q_head, k_row, k_head, v_row, v_head, o_row, o_head;  // elements
-  int64_t total_q;
-  int32_t batch, heads, n_qt;
-  int32_t heads_k;  // KV heads; heads is a multiple of it
-  // Split-KV: with num_splits > 1 the grid holds num_splits copies of the
-  // n_units work units; copy s takes the s-th of num_splits equal runs of
-  // each unit's key tiles and writes a normalised fp32 partial O and its
-  // LSE instead of out / lse (combined by combine_splits).
-  int32_t num_splits, n_units;
-  int32_t pack;  // segments per workgroup (segments_per_block), 1, 2 or 4
-  float* part_o;    // [num_splits, total_q, heads, d_v]
-  float* part_lse;  // [num_splits, heads, total_q]
-  int32_t causal, wl, wr;
-  float scale_log2;  // softmax_scale * log2(e)
-};
 
 // Geometry of one K/V tile of BN keys staged in LDS.
 template <int DQK, int DV, int BN>
@@ -119,144 +72,6 @@ struct TileGeom {
 template <int CPR_V>
 __host__ __device__ constexpr int v_swizzle(int row) {
   return CPR_V == 16 ? 4 * (row & 3) : (CPR_V == 8 ? 4 * ((row >> 1) & 1) : 0);
-}
-
-// 16-byte-per-lane load from a buffer straight into LDS: lane i's bytes land
-// at dst + 16 i; offsets past the buffer's range read as zero.  (A plain
-// device function: inside the kernel template the builtin trips the host pass.)
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, lds_char* dst, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
-}
-
-template <bool B>
-struct BoolTag {
-  static constexpr bool value = B;
-};
-
-template <int N>
-struct Int {
-  static constexpr int value = N;
-};
-
-// f(Int<I>{}), ..., f(Int<N - 1>{}) in order, unrolled.
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(Int<I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x2 v;
-  v[0] = (__bf16)a;  // round to nearest even
-  v[1] = (__bf16)b;
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-
-// Workgroup barrier without __syncthreads()'s release/acquire fences.  With
-// LDS-DMA in flight the release fence turns into s_waitcnt vmcnt(0), making
-// every wave wait for the prefetch it has just issued; the kernels that use
-// this wait for the loads a barrier must cover themselves.  LDS reads are
-// drained first so no stage is overwritten under a read still in flight,
-// and the empty asm statements keep the compiler from moving memory
-// accesses across.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// This workgroup's work unit (tile_schedule.h) and its segment's bounds:
-// longest-first dealing when it applies, computed by every wave from
-// cu_seqlens with one lane per segment (whose loads then also give the
-// bounds); else dealing in packing order.
-struct BlockWork {
-  WorkUnit u;
-  int q0, lq, k0, lk;  // the segment's first query / key row and lengths
-};
-
-template <bool PACKED>
-__device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int block_m, int64_t w) {
-  BlockWork r;
-  if constexpr (PACKED) {  // a group of pack short segments: one unit per (group, head), in packing order
-    const uint32_t groups = ((uint32_t)p.batch + (uint32_t)p.pack - 1u) / (uint32_t)p.pack;
-    r.u = decode_block((uint32_t)w, groups, (uint32_t)p.heads, 1u, p.causal);
-    r.u.h = query_head(r.u.h, p.heads, p.heads_k);
-    if (r.u.valid) {
-      const int first = r.u.b * p.pack, last = min(first + p.pack, p.batch);
-      r.q0 = p.cu_q[first];
-      r.lq = p.cu_q[last] - r.q0;
-      r.k0 = p.cu_k[first];
-      r.lk = p.cu_k[last] - r.k0;
-    }
-    return r;
-  }
-  if (p.batch <= kLptMaxBatch) {
-    int cq0 = 0, cq1 = 0, ck0 = 0, ck1 = -1;
-    if (lane < p.batch) {
-      cq0 = p.cu_q[lane];
-      cq1 = p.cu_q[lane + 1];
-      ck0 = p.cu_k[lane];
-      ck1 = p.cu_k[lane + 1];
-    }
-    const int lq = cq1 - cq0, lk = ck1 - ck0;  // lk = -1 on lanes past the batch
-    const int lq0 = __builtin_amdgcn_readfirstlane(lq), lk0 = __builtin_amdgcn_readfirstlane(lk);
-    if (__ballot(lane < p.batch && (lq != lq0 || lk != lk0)) != 0) {
-      const int x = (int)(w & 7);
-      const int k = (int)snake_quads((uint32_t)(w >> 3), (uint32_t)p.n_units / 8u);
-      int rank = 0;
-      for (int j = 0; j < p.batch; ++j) {
-        const int kj = __builtin_amdgcn_readlane(lk, j);
-        rank += (kj > lk || (kj == lk && j < lane)) ? 1 : 0;
-      }
-      const int nqt = lane < p.batch ? (lq + block_m - 1) / block_m : 0;
-      const int h0 = xcd_first_head(rank, p.heads, x);
-      const int n = xcd_head_count(h0, p.heads) * nqt;
-      int pre = 0;  // blocks of this XCD before this segment's
-      for (int j = 0; j < p.batch; ++j)
-        pre += __builtin_amdgcn_readlane(rank, j) < rank ? __builtin_amdgcn_readlane(n, j) : 0;
-      const uint64_t hit = __ballot(lane < p.batch && k >= pre && k < pre + n);
-      r.u.valid = hit != 0;
-      r.u.b = r.u.h = r.u.qt = -1;
-      if (hit != 0) {
-        const int i = (int)__builtin_ctzll(hit);
-        const int local = k - __builtin_amdgcn_readlane(pre, i);
-        const int nq = __builtin_amdgcn_readlane(nqt, i);
-        const int qi = local % nq;
-        r.u.b = i;
-        r.u.h = query_head(__builtin_amdgcn_readlane(h0, i) + 8 * (local / nq), p.heads, p.heads_k);
-        r.u.qt = p.causal ? nq - 1 - qi : qi;
-      }
-    } else {
-      r.u = decode_block((uint32_t)w, (uint32_t)p.batch, (uint32_t)p.heads, (uint32_t)p.n_qt, p.causal);
-      r.u.h = query_head(r.u.h, p.heads, p.heads_k);
-    }
-    if (r.u.valid) {
-      const int b = __builtin_amdgcn_readfirstlane(r.u.b);
-      r.q0 = __builtin_amdgcn_readlane(cq0, b);
-      r.lq = __builtin_amdgcn_readlane(lq, b);
-      r.k0 = __builtin_amdgcn_readlane(ck0, b);
-      r.lk = __builtin_amdgcn_readlane(lk, b);
-    }
-    return r;
-  }
-  r.u = decode_block((uint32_t)w, (uint32_t)p.batch, (uint32_t)p.heads, (uint32_t)p.n_qt, p.causal);
-  r.u.h = query_head(r.u.h, p.heads, p.heads_k);
-  if (r.u.valid) {
-    const int b = __builtin_amdgcn_readfirstlane(r.u.b);
-    r.q0 = p.cu_q[b];
-    r.lq = p.cu_q[b + 1] - r.q0;
-    r.k0 = p.cu_k[b];
-    r.lk = p.cu_k[b + 1] - r.k0;
-  }
-  return r;
-}
-
-__device__ __forceinline__ bf16x8 lds_read_b128(const lds_char* base, int byte_off) {
-  return *(const __attribute__((address_space(3))) bf16x8*)(base + byte_off);
 }
 
 __device__ __forceinline__ bf16x4 lds_read_tr(const lds_char* base, int byte_off) {
@@ -324,22 +139,6 @@ struct Cfg : TileGeom<DQK, DV, kBN> {
 }  // namespace wide
 
 
-// Cross-half (lane l and lane l ^ 32) max and sum: v_permlane32_swap
-// leaves lane l's and lane l ^ 32's values in the two results.
-__device__ __forceinline__ float xhalf_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xhalf_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-// Lane l ^ 32's value for lanes 32-63, the lane's own for lanes 0-31:
-// broadcasts what lanes 0-31 hold to the whole wave.
-__device__ __forceinline__ float from_lower_half(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]);
-}
 
 // How the row sum of the probabilities is formed: an fp32 sum of the fp32
 // probabilities (kF32), or, for d_v 72 and 80 without an LSE, a column of
@@ -999,15 +798,6 @@ namespace va {
 
 // One kernel, one instantiation per head-dim pair (and, for d_v 72/80, per
 // whether the LSE is returned): 4 waves x 64 query rows, 256-row blocks.
-struct Variant {
-  const void* fn;
-  int lds_bytes;
-  int block_m;
-  int block_n;
-  int threads;
-  const char* name;
-};
-
 template <int DQK, int DV, RowSum SUM>
 static Variant wide_variant(bool packed) {
   using C = wide::Cfg<DQK, DV>;
@@ -1053,9 +843,11 @@ static int64_t launch_units(int64_t batch, int64_t heads, int64_t max_seqlen_q, 
 // per-tile buffer loads (64 rows x stride x 2 bytes).
 static constexpr int64_t kMaxRowStride = (int64_t)1 << 24;
 
-static int check_tensor(const va_tensor* t, bool need_data) {
+// Strides are in elements of elem_bytes bytes; rows and heads must start on
+// 16-byte boundaries.
+static int check_tensor(const va_tensor* t, bool need_data, int elem_bytes = 2) {
   if (t->row_stride <= 0 || t->head_stride <= 0 || t->row_stride > kMaxRowStride) return VA_ERR_STRIDE;
-  if ((t->row_stride & 7) != 0 || (t->head_stride & 7) != 0) return VA_ERR_ALIGN;
+  if (((t->row_stride * elem_bytes) & 15) != 0 || ((t->head_stride * elem_bytes) & 15) != 0) return VA_ERR_ALIGN;
   if (need_data && t->data == nullptr) return VA_ERR_NULL;
   if (!aligned16(t->data)) return VA_ERR_ALIGN;
   return VA_OK;
@@ -1146,10 +938,12 @@ namespace va {
 
 // Validation shared by the entry points; fills the launch parameters.
 // Returns VA_OK (and *launch = false when there is nothing to launch).
+// fp8: Q, K, V hold e4m3 bytes (and out too when out_fp8).
 static int prepare(const va_tensor* q, const va_tensor* k, const va_tensor* v, const int32_t* cu_seqlens_q,
                    const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
                    float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
-                   const va_tensor* out, float* lse, Params& p, bool& launch) {
+                   const va_tensor* out, float* lse, Params& p, bool& launch, bool fp8 = false,
+                   bool out_fp8 = false) {
   launch = false;
   if (!q || !k || !v || !out) return VA_ERR_NULL;
   if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return VA_ERR_ARG;
@@ -1162,13 +956,14 @@ static int prepare(const va_tensor* q, const va_tensor* k, const va_tensor* v, c
   if (q->rows < 0 || k->rows < 0 || v->rows != k->rows || out->rows != q->rows) return VA_ERR_SHAPE;
   if (q->rows > INT32_MAX || k->rows > INT32_MAX) return VA_ERR_SHAPE;
   if (k->dim != q->dim || out->dim != v->dim) return VA_ERR_SHAPE;
-  if (!supported_dims(q->dim, v->dim)) return VA_ERR_HEADDIM;
+  if (!(fp8 ? fp8_supported_dims(q->dim, v->dim) : supported_dims(q->dim, v->dim))) return VA_ERR_HEADDIM;
   const bool has_q = q->rows > 0, has_k = k->rows > 0;
+  const int in_bytes = fp8 ? 1 : 2, out_bytes = out_fp8 ? 1 : 2;
   int st;
-  if ((st = check_tensor(q, has_q)) != VA_OK) return st;
-  if ((st = check_tensor(k, has_k)) != VA_OK) return st;
-  if ((st = check_tensor(v, has_k)) != VA_OK) return st;
-  if ((st = check_tensor(out, has_q)) != VA_OK) return st;
+  if ((st = check_tensor(q, has_q, in_bytes)) != VA_OK) return st;
+  if ((st = check_tensor(k, has_k, in_bytes)) != VA_OK) return st;
+  if ((st = check_tensor(v, has_k, in_bytes)) != VA_OK) return st;
+  if ((st = check_tensor(out, has_q, out_bytes)) != VA_OK) return st;
   if (lse != nullptr && ((uintptr_t)lse & 3u) != 0) return VA_ERR_ALIGN;
   if (batch == 0 || max_seqlen_q == 0 || q->rows == 0) return VA_OK;
   if (!cu_seqlens_q || !cu_seqlens_k) return VA_ERR_NULL;
@@ -1199,6 +994,7 @@ static int prepare(const va_tensor* q, const va_tensor* k, const va_tensor* v, c
   p.num_splits = 1;
   p.part_o = nullptr;
   p.part_lse = nullptr;
+  p.q_descale = p.k_descale = p.v_descale = p.out_scale = nullptr;
   (void)max_seqlen_k;
   launch = true;
   return VA_OK;
@@ -1206,8 +1002,10 @@ static int prepare(const va_tensor* q, const va_tensor* k, const va_tensor* v, c
 
 // One launch of the attention kernel over num_splits copies of the work units.
 static int launch_attention(Params& p, int32_t head_dim_qk, int32_t head_dim_v, int32_t max_seqlen_q,
-                            bool fp32_row_sum, void* stream) {
-  const Variant var = variant_for(head_dim_qk, head_dim_v, max_seqlen_q, fp32_row_sum);
+                            bool fp32_row_sum, void* stream, bool fp8 = false) {
+  const Variant var =
+      fp8 ? fp8_variant(head_dim_qk, head_dim_v, segments_per_block(max_seqlen_q, wide::kRowsPerWave) > 1)
+          : variant_for(head_dim_qk, head_dim_v, max_seqlen_q, fp32_row_sum);
   const int64_t units = launch_units(p.batch, p.heads, max_seqlen_q, var.block_m, &p.n_qt, &p.pack);
   const int64_t grid = units * p.num_splits;
   if (grid > INT32_MAX) return VA_ERR_SHAPE;
@@ -1300,6 +1098,40 @@ extern "C" int varlen_attn_fwd_splitkv(const va_tensor* q, const va_tensor* k, c
                         va::align256((size_t)num_splits * (size_t)q->rows * (size_t)q->heads * (size_t)v->dim * 4));
   // The partials' LSEs need the fp32 row sum, whether or not an LSE is returned.
   if ((st = va::launch_attention(p, q->dim, v->dim, max_seqlen_q, true, stream)) != VA_OK) return st;
+  return va_merge::launch_combine(p.part_o, p.part_lse, num_splits, q->rows, q->heads, v->dim, cu_seqlens_q, batch,
+                                  out, lse, stream);
+}
+
+extern "C" int varlen_attn_fwd_fp8(const va_tensor* q, const va_tensor* k, const va_tensor* v,
+                                   const float* q_descale, const float* k_descale, const float* v_descale,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                                   int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale, int32_t causal,
+                                   int32_t window_left, int32_t window_right, const va_tensor* out,
+                                   const float* out_scale, float* lse, int32_t num_splits, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (num_splits < 1 || num_splits > va::kMaxSplits) return VA_ERR_ARG;
+  if (out_scale != nullptr && num_splits > 1) return VA_ERR_ARG;  // the combine writes bf16
+  for (const float* d : {q_descale, k_descale, v_descale, out_scale})
+    if (((uintptr_t)d & 3u) != 0) return VA_ERR_ALIGN;
+  va::Params p;
+  bool launch = false;
+  int st = va::prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k, softmax_scale,
+                       causal, window_left, window_right, out, lse, p, launch, true, out_scale != nullptr);
+  if (st != VA_OK || !launch) return st;
+  p.q_descale = q_descale;
+  p.k_descale = k_descale;
+  p.v_descale = v_descale;
+  p.out_scale = out_scale;
+  if (num_splits == 1) return va::launch_attention(p, q->dim, v->dim, max_seqlen_q, true, stream, true);
+  const size_t need = varlen_attn_splitkv_workspace_bytes(q->rows, q->heads, v->dim, num_splits);
+  if (!workspace) return VA_ERR_NULL;
+  if (((uintptr_t)workspace & 255u) != 0) return VA_ERR_ALIGN;
+  if (workspace_bytes < need) return VA_ERR_ARG;
+  p.num_splits = num_splits;
+  p.part_o = (float*)workspace;
+  p.part_lse = (float*)((char*)workspace +
+                        va::align256((size_t)num_splits * (size_t)q->rows * (size_t)q->heads * (size_t)v->dim * 4));
+  if ((st = va::launch_attention(p, q->dim, v->dim, max_seqlen_q, true, stream, true)) != VA_OK) return st;
   return va_merge::launch_combine(p.part_o, p.part_lse, num_splits, q->rows, q->heads, v->dim, cu_seqlens_q, batch,
                                   out, lse, stream);
 }

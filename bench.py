@@ -43,6 +43,7 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak, ViT d=80 and MLA 192/128"
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0  # dense e4m3 MFMA, the roofline of the fp8 workloads
 PEAK_HBM_GBS = 8000.0
 RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # 312.5
 DEFAULT_WORKLOAD = "vit_full_d80"
@@ -89,9 +90,12 @@ def algorithmic_flops(w) -> float:
 
 
 def algorithmic_bytes(w) -> float:
-    """Read Q, K, V once; write O (bf16) and LSE (fp32, when returned)."""
+    """Read Q, K, V once (2 bytes an element, 1 for e4m3); write O (bf16) and
+    LSE (fp32, when returned)."""
     h = w.num_heads
-    b = 2.0 * h * (w.total_q * w.head_dim_qk + w.total_k * (w.head_dim_qk + w.head_dim_v) + w.total_q * w.head_dim_v)
+    eb = 1.0 if w.dtype == "e4m3" else 2.0
+    b = eb * h * (w.total_q * w.head_dim_qk + w.total_k * (w.head_dim_qk + w.head_dim_v))
+    b += 2.0 * h * w.total_q * w.head_dim_v
     if w.return_lse:
         b += 4.0 * h * w.total_q
     return b
@@ -122,27 +126,39 @@ def cpu_baseline(w, inp, budget_s: float = 12.0) -> dict:
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - threadpoolctl is optional
         threads = os.cpu_count() or 1
-    q = inp.q.to(torch.float32).numpy()
-    k = inp.k.to(torch.float32).numpy()
-    v = inp.v.to(torch.float32).numpy()
+    from oracle import attention_fwd_fp8
+
+    fp8 = w.dtype == "e4m3"
+    if fp8:
+        u8 = lambda t: t.view(torch.uint8).numpy()
+        q, k, v = u8(inp.q), u8(inp.k), u8(inp.v)
+        desc = dict(q_descale=inp.q_descale.numpy(), k_descale=inp.k_descale.numpy(),
+                    v_descale=inp.v_descale.numpy())
+    else:
+        q = inp.q.to(torch.float32).numpy()
+        k = inp.k.to(torch.float32).numpy()
+        v = inp.v.to(torch.float32).numpy()
     cu_q, cu_k = inp.cu_seqlens_q.tolist(), inp.cu_seqlens_k.tolist()
     wl, wr = w.window
     per_head = algorithmic_flops(w) / w.num_heads
     t0 = time.perf_counter()
     done = 0
     rows = None
-    if w.name == "vit_long65536_d128":
+    if w.name.startswith("vit_long65536_d128"):
         rows = np.arange(0, w.total_q, 64)  # 1/64 of the rows: every row costs the same
     for h in range(w.num_heads):
-        attention_fwd(q, k, v, cu_q, cu_k, w.scale, w.causal, wl, wr, rows=rows, heads=[h])
+        if fp8:
+            attention_fwd_fp8(q, k, v, cu_q, cu_k, w.scale, w.causal, wl, wr, rows=rows, heads=[h], **desc)
+        else:
+            attention_fwd(q, k, v, cu_q, cu_k, w.scale, w.causal, wl, wr, rows=rows, heads=[h])
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
     frac_rows = 1.0 if rows is None else len(rows) / w.total_q
     flops = per_head * done * frac_rows
-    sample = "%d of %d heads, %s rows, fp64 numpy oracle" % (
-        done, w.num_heads, "all" if rows is None else "every 64th of the")
+    sample = "%d of %d heads, %s rows, fp64 numpy oracle%s" % (
+        done, w.num_heads, "all" if rows is None else "every 64th of the", " on dequantised e4m3" if fp8 else "")
     return {
         "value": flops / el / 1e12,
         "unit": "TFLOP/s",
@@ -170,11 +186,22 @@ def device_inputs(w, cpu_inp, rotate: int = 0):
 
 def launch(copies, i, num_splits=1):
     import varlen_attention_forward_amd as va
+    from varlen_attention_forward_amd import workloads
 
     d, out, lse = copies[i % len(copies)]
-    va.varlen_attn_fwd(d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, d.max_seqlen_q, d.max_seqlen_k,
-                       softmax_scale=d.softmax_scale, causal=d.causal, window_size=d.window,
-                       out=out, return_lse=lse is not None, lse=lse, num_splits=num_splits)
+    if isinstance(d, workloads.Fp8Inputs):
+        va.varlen_attn_fwd_fp8(d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, d.max_seqlen_q, d.max_seqlen_k,
+                               softmax_scale=d.softmax_scale, causal=d.causal, window_size=d.window,
+                               q_descale=d.q_descale, k_descale=d.k_descale, v_descale=d.v_descale,
+                               out=out, return_lse=lse is not None, lse=lse, num_splits=num_splits)
+    else:
+        va.varlen_attn_fwd(d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, d.max_seqlen_q, d.max_seqlen_k,
+                           softmax_scale=d.softmax_scale, causal=d.causal, window_size=d.window,
+                           out=out, return_lse=lse is not None, lse=lse, num_splits=num_splits)
+
+
+def peak_tflops(w) -> float:
+    return PEAK_FP8_TFLOPS if w.dtype == "e4m3" else PEAK_BF16_TFLOPS
 
 
 class ClockSampler:
@@ -301,6 +328,8 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -
             "tflops_best": round(flops / best / 1e9, 2),
             "tflops_median": round(flops / med / 1e9, 2),
             "frac_of_bf16_peak_best": round(flops / best / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "dtype": w.dtype,
+            "frac_of_own_peak_best": round(flops / best / 1e9 / peak_tflops(w), 4),
             "gbs_best": round(nbytes / best / 1e6, 1),
             "graph_ms_best": round(min(graph_ms), 4),
             "graph_ms_median": round(statistics.median(graph_ms), 4),
@@ -317,13 +346,13 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -
             row["unsplit_tflops_best"] = round(flops / unsplit / 1e9, 2)
         rows.append(row)
         print(json.dumps(row), flush=True)
-    print("| workload | kernel ms best / median | TFLOP/s best / median | % peak | GB/s | graph ms best / median "
-          "| eager wall ms | sclk MHz |", flush=True)
+    print("| workload | kernel ms best / median | TFLOP/s best / median | % of its dtype's peak | GB/s "
+          "| graph ms best / median | eager wall ms | sclk MHz |", flush=True)
     print("|---|---|---|---|---|---|---|---|")
     for r in rows:
-        print("| %s | %.4f / %.4f | %.1f / %.1f | %.1f%% | %.0f | %.4f / %.4f | %.4f | %s |" % (
+        print("| %s | %.4f / %.4f | %.1f / %.1f | %.1f%% (%s) | %.0f | %.4f / %.4f | %.4f | %s |" % (
             r["workload"], r["kernel_ms_best"], r["kernel_ms_median"], r["tflops_best"], r["tflops_median"],
-            100 * r["frac_of_bf16_peak_best"], r["gbs_best"], r["graph_ms_best"], r["graph_ms_median"],
+            100 * r["frac_of_own_peak_best"], r["dtype"], r["gbs_best"], r["graph_ms_best"], r["graph_ms_median"],
             r["eager_wall_ms_median"], r["sclk_mhz_median"]), flush=True)
 
 
@@ -437,10 +466,7 @@ def main() -> int:
         copies.append((d, out, lse))
 
     def step(i):
-        d, out, lse = copies[i % rotate]
-        va.varlen_attn_fwd(d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, d.max_seqlen_q, d.max_seqlen_k,
-                           softmax_scale=d.softmax_scale, causal=d.causal, window_size=d.window,
-                           out=out, return_lse=lse is not None, lse=lse, num_splits=w.num_splits)
+        launch(copies, i, w.num_splits)
 
     for i in range(args.warmup):
         step(i)
@@ -461,10 +487,11 @@ def main() -> int:
     flops = algorithmic_flops(w)
     mfma_bound = flops / in_bytes >= RIDGE_FLOP_PER_BYTE
     if mfma_bound:
-        achieved, peak, r_unit = flops / kernel_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        achieved, peak, r_unit = flops / kernel_s / 1e12, peak_tflops(w), "TFLOP/s"
     else:
         achieved, peak, r_unit = in_bytes / kernel_s / 1e9, PEAK_HBM_GBS, "GB/s"
-    plan = va.plan(w.head_dim_qk, w.head_dim_v, w.batch, w.num_heads, w.max_seqlen_q, w.max_seqlen_k, w.causal)
+    plan = va.plan(w.head_dim_qk, w.head_dim_v, w.batch, w.num_heads, w.max_seqlen_q, w.max_seqlen_k, w.causal,
+                   fp8=w.dtype == "e4m3")
     result = {
         "metric": METRIC,
         "value": round(flops / wall_s / 1e12, 2),
@@ -476,8 +503,9 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16)",
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) %s)" % ("bf16" if w.dtype == "bf16" else
+                                                  "quantised to e4m3 with per-(segment, head) descales"),
         "config": {
             "workload": w.name,
             "description": w.description,

@@ -304,6 +304,11 @@ typedef struct va_plan {
 int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch, int32_t num_heads,
                      int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t causal, va_plan* plan);
 
+/* varlen_attn_plan for varlen_attn_fwd_fp8's kernel (supported pairs (64,64),
+ * (128,128), (192,128); 64-key tiles).  Host only; same returns. */
+int varlen_attn_plan_fp8(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch, int32_t num_heads,
+                         int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t causal, va_plan* plan);
+
 #ifdef __cplusplus
 }
 #endif

@@ -38,7 +38,7 @@ def test_visible_pairs_brute_force(lq, lk, causal, window):
 @pytest.mark.parametrize("name,gflop", [
     ("tiny_varlen_d64", 0.2852), ("vit_full_d80", 320.82), ("vit_window256_d80", 12.08),
     ("vit_long65536_d128", 35184.4), ("mla_causal_192_128", 2749.45), ("mla_context_chunk_tp8", 85.899),
-    ("vit_window64_d80", 14.680),
+    ("vit_window64_d80", 14.680), ("vit_long65536_d128_fp8", 35184.4), ("mla_causal_192_128_fp8", 2749.45),
 ])
 def test_algorithmic_flops(name, gflop):
     """H x visible pairs x 2 (d_qk + d_v), against the figures worked out by hand
@@ -53,7 +53,19 @@ def test_roofline_bound_follows_the_ridge():
               for n, w in workloads.WORKLOADS.items()}
     assert bounds == {"tiny_varlen_d64": False, "vit_full_d80": True, "vit_window256_d80": False,
                       "vit_window64_d80": False,
-                      "vit_long65536_d128": True, "mla_causal_192_128": True, "mla_context_chunk_tp8": True}
+                      "vit_long65536_d128": True, "mla_causal_192_128": True, "mla_context_chunk_tp8": True,
+                      "vit_long65536_d128_fp8": True, "mla_causal_192_128_fp8": True}
+
+
+def test_fp8_workloads_read_one_byte_per_input_element():
+    """The e4m3 twins of the long-image and MLA workloads read half the input
+    bytes (O is bf16 in both) and are priced against the 5 PFLOP/s fp8 peak."""
+    for name in ("vit_long65536_d128", "mla_causal_192_128"):
+        w, w8 = workloads.WORKLOADS[name], workloads.WORKLOADS[name + "_fp8"]
+        h = w.num_heads
+        inputs = h * (w.total_q * w.head_dim_qk + w.total_k * (w.head_dim_qk + w.head_dim_v))
+        assert bench.algorithmic_bytes(w) - bench.algorithmic_bytes(w8) == pytest.approx(inputs)
+        assert bench.peak_tflops(w8) == 5000.0 and bench.peak_tflops(w) == 2500.0
 
 
 def test_more_than_one_gpu_is_refused():

@@ -93,9 +93,14 @@ def o_tolerance(inp, rows=None, heads=None):
     H, H_kv = inp.q.shape[1], inp.k.shape[1]
     grp = H // H_kv
     cq, ck = inp.cu_seqlens_q.tolist(), inp.cu_seqlens_k.tolist()
-    qd = oracle.dequantize(u8(inp.q), cq, np.repeat(inp.q_descale.numpy(), grp, axis=1))
-    kd = oracle.dequantize(u8(inp.k), ck, inp.k_descale.numpy())
-    vd = oracle.dequantize(u8(inp.v), ck, inp.v_descale.numpy())
+    qc, kc, vc = u8(inp.q), u8(inp.k), u8(inp.v)
+    qdesc = np.repeat(inp.q_descale.numpy(), grp, axis=1)
+    head_list = list(range(H)) if heads is None else list(heads)
+    # dequantised per head (whole-tensor float64 copies would not fit at full sizes)
+    qd = {h: oracle.dequantize(qc, cq, qdesc, heads=[h])[:, 0, :] for h in head_list}
+    kd = {hk: oracle.dequantize(kc, ck, inp.k_descale.numpy(), heads=[hk])[:, 0, :]
+          for hk in {h // grp for h in head_list}}
+    vd = {hk: oracle.dequantize(vc, ck, inp.v_descale.numpy(), heads=[hk])[:, 0, :] for hk in kd}
     scale = float(np.float32(inp.softmax_scale))
     wl, wr = inp.window
     tol = np.full((inp.q.shape[0], H, inp.v.shape[2]), np.nan)
@@ -113,17 +118,17 @@ def o_tolerance(inp, rows=None, heads=None):
         lo, hi = oracle.visible_interval(idx, Lq, Lk, inp.causal, wl, wr)
         j = np.arange(Lk)[None, :]
         vis = (j >= lo[:, None]) & (j <= hi[:, None])
-        for h in (range(H) if heads is None else heads):
+        for h in head_list:
             hk = h // grp
-            s = scale * (qd[cq[b] + idx, h, :] @ kd[ck[b]:ck[b + 1], hk, :].T)
+            s = scale * (qd[h][cq[b] + idx, :] @ kd[hk][ck[b]:ck[b + 1], :].T)
             s = np.where(vis, s, -np.inf)
             m = s.max(axis=1) if Lk else np.full(len(idx), -np.inf)
             ok = np.isfinite(m)
             p = np.exp(s - np.where(ok, m, 0.0)[:, None])
             l = np.where(ok, p.sum(axis=1), 1.0)[:, None]
-            av = np.abs(vd[ck[b]:ck[b + 1], hk, :])
+            av = np.abs(vd[hk][ck[b]:ck[b + 1], :])
             a = (p @ av) / l
-            o = np.abs(p @ vd[ck[b]:ck[b + 1], hk, :]) / l
+            o = np.abs(p @ vd[hk][ck[b]:ck[b + 1], :]) / l
             c = (vis.astype(np.float64) @ av) / l
             tol[cq[b] + idx, h, :] = 2.0 ** -4 * a + 2.0 ** -10 * c + 2.0 ** -8 * o + 1e-3 * a + 1e-5
     return tol
@@ -267,3 +272,22 @@ def test_fp8_empty_and_zero_key_segments():
     assert bool((out[:5] == 0).all())
     assert bool(torch.isinf(lse[:, :5]).all())
     assert_fp8_parity(inp, out, lse, what="zero keys")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["vit_long65536_d128_fp8", "mla_causal_192_128_fp8"])
+def test_fp8_workload_sampled(name):
+    """Full-size fp8 workloads in the launch bench.py times, checked on sampled
+    rows (each segment's first and last rows and random ones) of three heads."""
+    w = workloads.WORKLOADS[name]
+    inp = workloads.workload_inputs(w)
+    out, lse = run_fp8(inp, return_lse=w.return_lse)
+    cq = inp.cu_seqlens_q.tolist()
+    g = np.random.default_rng(7)
+    rows = set(g.integers(0, w.total_q, 40).tolist())
+    for b in range(len(cq) - 1):
+        if cq[b + 1] > cq[b]:
+            rows |= {cq[b], cq[b + 1] - 1, (cq[b] + cq[b + 1]) // 2}
+    rows = np.array(sorted(rows))
+    heads = [0, w.num_heads // 2 + 1, w.num_heads - 1]
+    assert_fp8_parity(inp, out, lse, rows=rows, heads=heads, what=name)

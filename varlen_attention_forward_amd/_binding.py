@@ -44,6 +44,7 @@ EXPORTED_SYMBOLS = (
     "varlen_attn_splitkv_workspace_bytes",
     "varlen_attn_num_splits",
     "varlen_attn_fwd_fp8",
+    "varlen_attn_plan_fp8",
 )
 
 
@@ -129,6 +130,8 @@ def library() -> ctypes.CDLL:
                                           + [ctypes.c_int32] + [P(ctypes.c_int32)] * 3)
     lib.varlen_attn_plan.restype = ctypes.c_int
     lib.varlen_attn_plan.argtypes = [ctypes.c_int32] * 7 + [P(VaPlan)]
+    lib.varlen_attn_plan_fp8.restype = ctypes.c_int
+    lib.varlen_attn_plan_fp8.argtypes = [ctypes.c_int32] * 7 + [P(VaPlan)]
     _lib = lib
     return lib
 
@@ -177,12 +180,13 @@ def work_unit(block, num_heads, head_dim_qk, head_dim_v, seqlens_q, seqlens_k, c
     return tuple(o.value for o in out)
 
 
-def plan(head_dim_qk, head_dim_v, batch, num_heads, max_seqlen_q, max_seqlen_k, causal=False) -> dict:
-    """Launch shape the library would use (host call, no GPU needed)."""
+def plan(head_dim_qk, head_dim_v, batch, num_heads, max_seqlen_q, max_seqlen_k, causal=False,
+         fp8: bool = False) -> dict:
+    """Launch shape the library would use (host call, no GPU needed); ``fp8``
+    for ``varlen_attn_fwd_fp8``'s kernel."""
     pl = VaPlan()
-    st = library().varlen_attn_plan(
-        head_dim_qk, head_dim_v, batch, num_heads, max_seqlen_q, max_seqlen_k, int(causal), ctypes.byref(pl)
-    )
+    fn = library().varlen_attn_plan_fp8 if fp8 else library().varlen_attn_plan
+    st = fn(head_dim_qk, head_dim_v, batch, num_heads, max_seqlen_q, max_seqlen_k, int(causal), ctypes.byref(pl))
     _raise_for(st)
     return {
         "block_m": pl.block_m,

@@ -934,6 +934,25 @@ extern "C" int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t
   return VA_OK;
 }
 
+extern "C" int varlen_attn_plan_fp8(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch,
+                                    int32_t num_heads, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    int32_t causal, va_plan* plan) {
+  (void)max_seqlen_k;
+  (void)causal;
+  if (!plan) return VA_ERR_NULL;
+  if (!va::fp8_supported_dims(head_dim_qk, head_dim_v)) return VA_ERR_HEADDIM;
+  if (batch < 0 || num_heads <= 0 || max_seqlen_q < 0) return VA_ERR_ARG;
+  const va::Variant var = va::fp8_variant(head_dim_qk, head_dim_v,
+                                          va::segments_per_block(max_seqlen_q, va::wide::kRowsPerWave) > 1);
+  plan->block_m = var.block_m;
+  plan->block_n = var.block_n;
+  plan->threads = var.threads;
+  plan->lds_bytes = var.lds_bytes;
+  plan->grid = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, nullptr, &plan->segments_per_block);
+  plan->kernel = var.name;
+  return VA_OK;
+}
+
 namespace va {
 
 // Validation shared by the entry points; fills the launch parameters.

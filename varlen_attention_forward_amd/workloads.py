@@ -52,6 +52,7 @@ class Workload:
     softmax_scale: Optional[float] = None
     description: str = ""
     num_splits: int = 1  # split-KV runs per work unit; 0: the library chooses
+    dtype: str = "bf16"  # input element type: "bf16", or "e4m3" (fp8 with descales)
 
     @property
     def batch(self) -> int:
@@ -177,6 +178,33 @@ def _named_workloads() -> dict:
             "GPUs): 512 new tokens over a 16384-token context chunk, non-causal, qk dim 192, v dim "
             "128, LSE returned; split-KV with the library's split count",
         ),
+        Workload(
+            name="vit_long65536_d128_fp8",
+            seed=4,
+            seqlens_q=(65536,),
+            seqlens_k=(65536,),
+            num_heads=16,
+            head_dim_qk=128,
+            head_dim_v=128,
+            causal=False,
+            return_lse=False,
+            dtype="e4m3",
+            description="one 65536-token image, 16 heads, d=128, non-causal, fp8 e4m3 Q/K/V with "
+            "per-(image, head) descales, bf16 out",
+        ),
+        Workload(
+            name="mla_causal_192_128_fp8",
+            seed=5,
+            seqlens_q=(4096,) * 4,
+            seqlens_k=(4096,) * 4,
+            num_heads=128,
+            head_dim_qk=192,
+            head_dim_v=128,
+            causal=True,
+            dtype="e4m3",
+            description="MLA-style causal prefill, 4 x 4096 tokens, 128 heads, qk dim 192, v dim 128, fp8 "
+            "e4m3 Q/K/V with per-(segment, head) descales, bf16 out, LSE returned",
+        ),
     ]
     return {w.name: w for w in ws}
 
@@ -190,6 +218,8 @@ WORKLOAD_ORDER = (
     "vit_long65536_d128",
     "mla_causal_192_128",
     "mla_context_chunk_tp8",
+    "vit_long65536_d128_fp8",
+    "mla_causal_192_128_fp8",
 )
 
 
@@ -350,8 +380,12 @@ def make_fp8_inputs(
     )
 
 
-def workload_inputs(w: Workload) -> Inputs:
-    """The seeded tensors of a named workload (the seed is part of ``w``)."""
+def workload_inputs(w: Workload):
+    """The seeded tensors of a named workload (the seed is part of ``w``):
+    ``Inputs``, or ``Fp8Inputs`` for an e4m3 workload."""
+    if w.dtype == "e4m3":
+        return make_fp8_inputs(w.seqlens_q, w.seqlens_k, w.num_heads, w.head_dim_qk, w.head_dim_v, w.seed,
+                               causal=w.causal, window=w.window, softmax_scale=w.softmax_scale)
     if w.name == "vit_full_d80":
         # Keep the generator stream identical to drawing the lengths first and
         # then Q, K, V from the same generator.

@@ -49,6 +49,8 @@ RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # 312.5
 DEFAULT_WORKLOAD = "vit_full_d80"
 KERNEL_SOURCES = [
     os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "varlen_attn_fwd.hip"),
+    os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "varlen_attn_fwd_fp8.hip"),
+    os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "attn_common.h"),
     os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "tile_schedule.h"),
 ]
 

@@ -94,9 +94,9 @@ def algorithmic_flops(w) -> float:
 def algorithmic_bytes(w) -> float:
     """Read Q, K, V once (2 bytes an element, 1 for e4m3); write O (bf16) and
     LSE (fp32, when returned)."""
-    h = w.num_heads
+    h, hk = w.num_heads, w.heads_k
     eb = 1.0 if w.dtype == "e4m3" else 2.0
-    b = eb * h * (w.total_q * w.head_dim_qk + w.total_k * (w.head_dim_qk + w.head_dim_v))
+    b = eb * (h * w.total_q * w.head_dim_qk + hk * w.total_k * (w.head_dim_qk + w.head_dim_v))
     b += 2.0 * h * w.total_q * w.head_dim_v
     if w.return_lse:
         b += 4.0 * h * w.total_q
@@ -186,11 +186,17 @@ def device_inputs(w, cpu_inp, rotate: int = 0):
     return copies
 
 
-def launch(copies, i, num_splits=1):
+def launch(copies, i, num_splits=1, max_seqlen_q=None):
+    """One call on input copy i; ``max_seqlen_q`` overrides the bound (a
+    looser one selects the unpacked launch, for comparison)."""
+    import dataclasses
+
     import varlen_attention_forward_amd as va
     from varlen_attention_forward_amd import workloads
 
     d, out, lse = copies[i % len(copies)]
+    if max_seqlen_q is not None:
+        d = dataclasses.replace(d, max_seqlen_q=max_seqlen_q)
     if isinstance(d, workloads.Fp8Inputs):
         va.varlen_attn_fwd_fp8(d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, d.max_seqlen_q, d.max_seqlen_k,
                                softmax_scale=d.softmax_scale, causal=d.causal, window_size=d.window,
@@ -308,6 +314,23 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -
                 if not torch.equal(o, ro) or (l is not None and not torch.equal(l, rl)):
                     raise RuntimeError("%s: graph replay differs from the eager result" % name)
         del graph
+        unpacked = None
+        pl = __import__("varlen_attention_forward_amd").plan(
+            w.head_dim_qk, w.head_dim_v, w.batch, w.num_heads, w.max_seqlen_q, w.max_seqlen_k, w.causal,
+            fp8=w.dtype == "e4m3", num_heads_k=w.heads_k)
+        if pl["pack_mode"] != 0:  # the same call with max_seqlen_q = 257: unpacked, for comparison
+            times = []
+            for _ in range(rounds):
+                for i in range(warmup):
+                    launch(copies, i, ns, 257)
+                torch.cuda.synchronize()
+                ev0.record(stream)
+                for i in range(timed):
+                    launch(copies, i, ns, 257)
+                ev1.record(stream)
+                torch.cuda.synchronize()
+                times.append(ev0.elapsed_time(ev1) / timed)
+            unpacked = min(times)
         unsplit = None
         if ns != 1:  # the same call without split-KV, for comparison
             times = []
@@ -340,6 +363,10 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -
             "sclk_samples": len(clk.samples),
             "input_copies": len(copies),
         }
+        if unpacked is not None:
+            row["pack_mode"] = pl["pack_mode"]
+            row["unpacked_kernel_ms_best"] = round(unpacked, 4)
+            row["unpacked_tflops_best"] = round(flops / unpacked / 1e9, 2)
         if unsplit is not None:
             va_mod = __import__("varlen_attention_forward_amd")
             row["num_splits"] = va_mod.auto_num_splits(w.head_dim_qk, w.head_dim_v, w.batch, w.num_heads,
@@ -493,7 +520,7 @@ def main() -> int:
     else:
         achieved, peak, r_unit = in_bytes / kernel_s / 1e9, PEAK_HBM_GBS, "GB/s"
     plan = va.plan(w.head_dim_qk, w.head_dim_v, w.batch, w.num_heads, w.max_seqlen_q, w.max_seqlen_k, w.causal,
-                   fp8=w.dtype == "e4m3")
+                   fp8=w.dtype == "e4m3", num_heads_k=w.heads_k)
     result = {
         "metric": METRIC,
         "value": round(flops / wall_s / 1e12, 2),

@@ -277,9 +277,11 @@ int varlen_attn_tile_range(int32_t seqlen_q, int32_t seqlen_k, int32_t row_begin
  * either way every odd quad of each XCD's dispatch order is reversed.  When
  * short segments share workgroups (va_plan.segments_per_block P > 1, every
  * segment at most 128 queries), workgroup `block` owns segments
- * [segment, segment + P) (those that exist), their q-tile 0.  With
- * num_heads_k KV heads (num_heads a multiple of it) the query heads of one
- * KV head are dealt to the same XCD where the head counts allow.
+ * [segment, segment + P) (those that exist), their q-tile 0 (pack_mode 1),
+ * or, when the KV-head group size num_heads / num_heads_k is a multiple of
+ * P, query heads [head, head + P) of one segment, q-tile 0 (pack_mode 2).
+ * With num_heads_k KV heads (num_heads a multiple of it) the query heads of
+ * one KV head are dealt to the same XCD where the head counts allow.
  * Returns VA_OK, VA_ERR_NULL, VA_ERR_HEADDIM, or VA_ERR_ARG for a block
  * outside the grid, a negative length or all-empty queries.
  * Host only; makes no HIP call.
@@ -297,17 +299,23 @@ typedef struct va_plan {
   int32_t lds_bytes;     /* LDS per workgroup */
   int64_t grid;          /* workgroups launched (some exit at once on short segments) */
   const char* kernel;    /* kernel name ("attn_fwd_wide"); block_m and threads give its launch shape */
-  int32_t segments_per_block; /* 1, or 2 / 4 consecutive short segments per workgroup (max_seqlen_q
-                                 <= 128 / <= 64), one or two waves each */
+  int32_t segments_per_block; /* 1, or 2 / 4 slots per workgroup for short segments (max_seqlen_q
+                                 <= 128 / <= 64), one or two waves each; see pack_mode */
+  int32_t pack_mode;          /* 0: unpacked; 1: the slots take consecutive segments of one head;
+                                 2: they take query heads of one KV head over one segment (grouped
+                                 KV heads with a group size that is a multiple of the slot count:
+                                 FA4's pack_gqa, SGLang PR #41344 "Accuracy Tests") */
 } va_plan;
 
 int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch, int32_t num_heads,
-                     int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t causal, va_plan* plan);
+                     int32_t num_heads_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t causal,
+                     va_plan* plan);
 
 /* varlen_attn_plan for varlen_attn_fwd_fp8's kernel (supported pairs (64,64),
  * (128,128), (192,128); 64-key tiles).  Host only; same returns. */
 int varlen_attn_plan_fp8(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch, int32_t num_heads,
-                         int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t causal, va_plan* plan);
+                         int32_t num_heads_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t causal,
+                         va_plan* plan);
 
 #ifdef __cplusplus
 }

@@ -39,6 +39,7 @@ def test_visible_pairs_brute_force(lq, lk, causal, window):
     ("tiny_varlen_d64", 0.2852), ("vit_full_d80", 320.82), ("vit_window256_d80", 12.08),
     ("vit_long65536_d128", 35184.4), ("mla_causal_192_128", 2749.45), ("mla_context_chunk_tp8", 85.899),
     ("vit_window64_d80", 14.680), ("vit_long65536_d128_fp8", 35184.4), ("mla_causal_192_128_fp8", 2749.45),
+    ("gqa_chunk64_d128", 135.325),
 ])
 def test_algorithmic_flops(name, gflop):
     """H x visible pairs x 2 (d_qk + d_v), against the figures worked out by hand
@@ -54,7 +55,7 @@ def test_roofline_bound_follows_the_ridge():
     assert bounds == {"tiny_varlen_d64": False, "vit_full_d80": True, "vit_window256_d80": False,
                       "vit_window64_d80": False,
                       "vit_long65536_d128": True, "mla_causal_192_128": True, "mla_context_chunk_tp8": True,
-                      "vit_long65536_d128_fp8": True, "mla_causal_192_128_fp8": True}
+                      "vit_long65536_d128_fp8": True, "mla_causal_192_128_fp8": True, "gqa_chunk64_d128": True}
 
 
 def test_fp8_workloads_read_one_byte_per_input_element():
@@ -73,3 +74,11 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_grouped_kv_workload_counts_kv_heads_once():
+    """K and V are read once per KV head (4 here), Q and O once per query head."""
+    w = workloads.WORKLOADS["gqa_chunk64_d128"]
+    q_o = 2 * 32 * 4096 * (128 + 128)
+    kv = 2 * 4 * (64 * 2048) * (128 + 128)
+    assert bench.algorithmic_bytes(w) == pytest.approx(q_o + kv + 4 * 32 * 4096)

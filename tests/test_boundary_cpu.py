@@ -528,3 +528,40 @@ def test_fp8_scalar_arguments():
 def test_fp8_empty_work_returns_ok_without_launch():
     assert _call_fp8(batch=0) == B.VA_OK
     assert _call_fp8(mq=0) == B.VA_OK
+
+
+@pytest.mark.parametrize("heads,heads_k,lq,pack", [
+    (32, 4, [64, 1, 0, 50, 64], 4),      # group 8, <= 64 queries: four query heads a workgroup
+    (16, 4, [33, 64], 4),                # group 4
+    (12, 3, [100, 128, 65], 2),          # group 4, <= 128 queries: two query heads, two waves each
+    (16, 8, [128, 7], 2),                # group 2
+])
+def test_work_unit_head_packing(heads, heads_k, lq, pack):
+    """Grouped KV heads with short segments: a workgroup takes `pack` query
+    heads of one KV head over one segment (FA4's pack_gqa), every (segment,
+    query head) owned once, and a KV head's groups stay on one XCD when the
+    KV heads are a multiple of 8 (here: by construction of the dealing)."""
+    p = pkg.plan(128, 128, len(lq), heads, max(lq), max(lq), 0, num_heads_k=heads_k)
+    assert p["segments_per_block"] == pack and p["pack_mode"] == 2
+    grp = heads // heads_k
+    seen = set()
+    for blk in range(p["grid"]):
+        b, h, qt = pkg.work_unit(blk, heads, 128, 128, lq, lq, False, num_heads_k=heads_k)
+        if b < 0:
+            continue
+        assert qt == 0 and h % pack == 0 and h // grp == (h + pack - 1) // grp
+        for x in range(h, h + pack):
+            assert (b, x) not in seen
+            seen.add((b, x))
+    assert seen == {(b, h) for b in range(len(lq)) for h in range(heads)}
+
+
+@pytest.mark.parametrize("heads,heads_k,max_q,mode", [
+    (32, 4, 64, 2), (32, 4, 65, 2), (32, 4, 129, 0),   # head packing up to 128 queries, then none
+    (6, 3, 64, 1),                                     # group 2 is not a multiple of 4: segments
+    (6, 3, 100, 2),                                    # but of 2
+    (8, 8, 64, 1), (9, 3, 64, 1),                      # no grouping / group 3: segments
+])
+def test_pack_mode_choice(heads, heads_k, max_q, mode):
+    assert pkg.plan(64, 64, 5, heads, max_q, max_q, 0, num_heads_k=heads_k)["pack_mode"] == mode
+    assert pkg.plan(64, 64, 5, heads, max_q, max_q, 0, fp8=True, num_heads_k=heads_k)["pack_mode"] == mode

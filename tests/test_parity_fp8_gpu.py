@@ -291,3 +291,21 @@ def test_fp8_workload_sampled(name):
     rows = np.array(sorted(rows))
     heads = [0, w.num_heads // 2 + 1, w.num_heads - 1]
     assert_fp8_parity(inp, out, lse, rows=rows, heads=heads, what=name)
+
+
+@pytest.mark.parametrize("dims", DIMS, ids=lambda d: "d%d_%d" % d)
+@pytest.mark.parametrize("heads,heads_k,hi", [(32, 4, 64), (12, 3, 128)])
+@pytest.mark.parametrize("mode", ["full", "causal"])
+def test_fp8_packed_query_heads(dims, heads, heads_k, hi, mode):
+    import dataclasses
+
+    g = np.random.default_rng(heads + hi + dims[0])
+    lq = g.integers(0, hi + 1, 9).tolist()
+    lq[0] = hi
+    lk = [x + int(g.integers(0, 300)) for x in lq]
+    inp = make(lq, lk, dims, seed=heads * 3 + hi, mode=mode, heads=heads, heads_k=heads_k)
+    assert va.plan(dims[0], dims[1], len(lq), heads, hi, max(lk), fp8=True, num_heads_k=heads_k)["pack_mode"] == 2
+    out, lse = run_fp8(inp)
+    assert_fp8_parity(inp, out, lse, what="fp8 packed heads %s %d/%d %d %s" % (dims, heads, heads_k, hi, mode))
+    out2, lse2 = run_fp8(dataclasses.replace(inp, max_seqlen_q=257))
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)

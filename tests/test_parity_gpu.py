@@ -589,6 +589,7 @@ def test_workload_full_oracle(name):
     ("vit_full_d80", 384, None),
     ("vit_long65536_d128", 24, None),
     ("mla_causal_192_128", 128, None),
+    ("gqa_chunk64_d128", 256, None),
 ])
 def test_workload_sampled(name, n_random, heads):
     w = workloads.WORKLOADS[name]
@@ -598,3 +599,31 @@ def test_workload_sampled(name, n_random, heads):
     ref_o, ref_lse = oracle_on(inp, rows=rows, heads=heads)
     e = assert_parity(out, lse, ref_o, ref_lse, rows=rows, what=name)
     print("%s: %d rows, max|dO| %.3e max|dLSE| %s" % (name, len(rows), e[0], e[1]))
+
+
+# ---------------------------------------------------------------------------
+# grouped KV heads with short segments: a workgroup takes several query heads
+# of one KV head (pack_mode 2)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dims", DIMS, ids=lambda d: "d%d_%d" % d)
+@pytest.mark.parametrize("heads,heads_k,lens", [
+    (16, 4, "le64"), (32, 4, "le64"), (12, 3, "le128"), (16, 8, "le128"),
+])
+@pytest.mark.parametrize("mode", ["full", "causal", "window"])
+def test_packed_query_heads(dims, heads, heads_k, lens, mode):
+    g = np.random.default_rng(heads * 31 + heads_k + dims[0])
+    hi = 64 if lens == "le64" else 128
+    lq = g.integers(0, hi + 1, 11).tolist()
+    lq[0] = hi
+    lk = [x + int(g.integers(0, 300)) for x in lq]
+    causal, window = MODES[mode]
+    inp = workloads.make_inputs(lq, lk, heads, dims[0], dims[1], seed=hi + heads, causal=causal, window=window,
+                                num_heads_k=heads_k)
+    assert va.plan(dims[0], dims[1], len(lq), heads, hi, max(lk), causal, num_heads_k=heads_k)["pack_mode"] == 2
+    out, lse = run_gpu(inp)
+    ref_o, ref_lse = oracle_on(inp)
+    assert_parity(out, lse, ref_o, ref_lse, what="packed heads %s %d/%d %s %s" % (dims, heads, heads_k, lens, mode))
+    # the same call with a looser max_seqlen_q runs unpacked: same rows, same tiles, same bits
+    import dataclasses
+    out2, lse2 = run_gpu(dataclasses.replace(inp, max_seqlen_q=129 if hi == 128 else 257))
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)

@@ -68,6 +68,7 @@ class VaPlan(ctypes.Structure):
         ("grid", ctypes.c_int64),
         ("kernel", ctypes.c_char_p),
         ("segments_per_block", ctypes.c_int32),
+        ("pack_mode", ctypes.c_int32),
     ]
 
 
@@ -129,9 +130,9 @@ def library() -> ctypes.CDLL:
     lib.varlen_attn_work_unit.argtypes = ([ctypes.c_int64] + [ctypes.c_int32] * 5 + [P(ctypes.c_int32)] * 2
                                           + [ctypes.c_int32] + [P(ctypes.c_int32)] * 3)
     lib.varlen_attn_plan.restype = ctypes.c_int
-    lib.varlen_attn_plan.argtypes = [ctypes.c_int32] * 7 + [P(VaPlan)]
+    lib.varlen_attn_plan.argtypes = [ctypes.c_int32] * 8 + [P(VaPlan)]
     lib.varlen_attn_plan_fp8.restype = ctypes.c_int
-    lib.varlen_attn_plan_fp8.argtypes = [ctypes.c_int32] * 7 + [P(VaPlan)]
+    lib.varlen_attn_plan_fp8.argtypes = [ctypes.c_int32] * 8 + [P(VaPlan)]
     _lib = lib
     return lib
 
@@ -181,12 +182,14 @@ def work_unit(block, num_heads, head_dim_qk, head_dim_v, seqlens_q, seqlens_k, c
 
 
 def plan(head_dim_qk, head_dim_v, batch, num_heads, max_seqlen_q, max_seqlen_k, causal=False,
-         fp8: bool = False) -> dict:
+         fp8: bool = False, num_heads_k=None) -> dict:
     """Launch shape the library would use (host call, no GPU needed); ``fp8``
-    for ``varlen_attn_fwd_fp8``'s kernel."""
+    for ``varlen_attn_fwd_fp8``'s kernel; ``num_heads_k`` defaults to
+    ``num_heads``."""
     pl = VaPlan()
     fn = library().varlen_attn_plan_fp8 if fp8 else library().varlen_attn_plan
-    st = fn(head_dim_qk, head_dim_v, batch, num_heads, max_seqlen_q, max_seqlen_k, int(causal), ctypes.byref(pl))
+    hk = num_heads if num_heads_k is None else num_heads_k
+    st = fn(head_dim_qk, head_dim_v, batch, num_heads, hk, max_seqlen_q, max_seqlen_k, int(causal), ctypes.byref(pl))
     _raise_for(st)
     return {
         "block_m": pl.block_m,
@@ -196,6 +199,7 @@ def plan(head_dim_qk, head_dim_v, batch, num_heads, max_seqlen_q, max_seqlen_k, 
         "grid": pl.grid,
         "kernel": pl.kernel.decode(),
         "segments_per_block": pl.segments_per_block,
+        "pack_mode": pl.pack_mode,
     }
 
 

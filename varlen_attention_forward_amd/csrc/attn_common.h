@@ -48,7 +48,7 @@ struct Params {
   // each unit's key tiles and writes a normalised fp32 partial O and its
   // LSE instead of out / lse (combined by combine_splits).
   int32_t num_splits, n_units;
-  int32_t pack;  // segments per workgroup (segments_per_block), 1, 2 or 4
+  int32_t pack;  // segments, or query heads, per workgroup (segments_per_block): 1, 2 or 4
   float* part_o;    // [num_splits, total_q, heads, d_v]
   float* part_lse;  // [num_splits, heads, total_q]
   int32_t causal, wl, wr;
@@ -119,10 +119,25 @@ struct BlockWork {
   int q0, lq, k0, lk;  // the segment's first query / key row and lengths
 };
 
-template <bool PACKED>
+template <int PK>
 __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int block_m, int64_t w) {
   BlockWork r;
-  if constexpr (PACKED) {  // a group of pack short segments: one unit per (group, head), in packing order
+  if constexpr (PK == kPackHeads) {
+    // (segment, group of pack query heads of one KV head): the group index
+    // takes the place of the head in the dealing, and query_head keeps a KV
+    // head's groups on one XCD; r.u.h is the group's first query head.
+    const uint32_t vheads = (uint32_t)(p.heads / p.pack);
+    r.u = decode_block((uint32_t)w, (uint32_t)p.batch, vheads, 1u, p.causal);
+    r.u.h = query_head(r.u.h, (int)vheads, p.heads_k) * p.pack;
+    if (r.u.valid) {
+      r.q0 = p.cu_q[r.u.b];
+      r.lq = p.cu_q[r.u.b + 1] - r.q0;
+      r.k0 = p.cu_k[r.u.b];
+      r.lk = p.cu_k[r.u.b + 1] - r.k0;
+    }
+    return r;
+  }
+  if constexpr (PK == kPackSegments) {  // a group of pack short segments: one unit per (group, head), in packing order
     const uint32_t groups = ((uint32_t)p.batch + (uint32_t)p.pack - 1u) / (uint32_t)p.pack;
     r.u = decode_block((uint32_t)w, groups, (uint32_t)p.heads, 1u, p.causal);
     r.u.h = query_head(r.u.h, p.heads, p.heads_k);
@@ -230,6 +245,6 @@ struct Variant {
 // The fp8 e4m3 kernel (varlen_attn_fwd_fp8.hip): whether it has an
 // instantiation for (dqk, dv), and that instantiation.
 bool fp8_supported_dims(int dqk, int dv);
-Variant fp8_variant(int dqk, int dv, bool packed);
+Variant fp8_variant(int dqk, int dv, int pack_mode);
 
 }  // namespace va

@@ -142,6 +142,21 @@ VA_HD int32_t segments_per_block(int64_t max_seqlen_q, int64_t rows_per_wave) {
   return max_seqlen_q <= rows_per_wave ? 4 : (max_seqlen_q <= 2 * rows_per_wave ? 2 : 1);
 }
 
+// How a workgroup's four waves are filled when segments are that short:
+// with grouped KV heads whose group size is a multiple of P, the P slots take
+// P query heads of one KV head over the same segment (kPackHeads: every K/V
+// tile staged feeds all of them, and the segment's rows and tiles are those
+// of an unpacked unit); otherwise P consecutive segments of one head
+// (kPackSegments).  The workgroup's unit is then (segment, group of P query
+// heads) or (group of P segments, head), one q-tile.
+enum PackMode : int32_t { kPackNone = 0, kPackSegments = 1, kPackHeads = 2 };
+
+VA_HD int32_t pack_mode(int64_t max_seqlen_q, int64_t rows_per_wave, int64_t heads, int64_t heads_k) {
+  const int32_t pk = segments_per_block(max_seqlen_q, rows_per_wave);
+  if (pk == 1) return kPackNone;
+  return (heads_k > 0 && heads % heads_k == 0 && (heads / heads_k) % pk == 0) ? kPackHeads : kPackSegments;
+}
+
 VA_HD int64_t grid_blocks(int64_t batch, int64_t heads, int64_t n_qt) {
   const int64_t groups = batch * heads;
   return 8 * ((groups + 7) / 8) * n_qt;

@@ -149,7 +149,7 @@ struct Cfg : TileGeom<DQK, DV, kBN> {
 // to ln(1 + 2^-9), which is why an LSE keeps the fp32 sum.
 enum class RowSum { kF32, kMfma };
 
-template <int DQK, int DV, RowSum SUM, bool PACKED>
+template <int DQK, int DV, RowSum SUM, int PK>
 __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd_wide(Params p) {
   using namespace wide;
   using C = Cfg<DQK, DV>;
@@ -199,13 +199,14 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
 
   // Split-KV copy of the work units this workgroup belongs to (0 without split).
   const int split = (int)(blockIdx.x / (uint32_t)p.n_units);
-  const BlockWork bw = block_work<PACKED>(p, lane, C::BM, (int64_t)blockIdx.x - (int64_t)split * p.n_units);
+  const BlockWork bw = block_work<PK>(p, lane, C::BM, (int64_t)blockIdx.x - (int64_t)split * p.n_units);
   if (!bw.u.valid) return;
-  const int h = bw.u.h, qt = bw.u.qt;
+  int h = bw.u.h;
+  const int qt = bw.u.qt;
   const int k0 = bw.k0, Lk = bw.lk;  // the workgroup's keys
   const int r0 = qt * C::BM;
   if (r0 >= bw.lq) return;
-  constexpr bool packed = PACKED;
+  constexpr bool packed = PK == kPackSegments;
   // This wave's rows: rows [wrow0, r1) of a segment whose first query row is
   // q0 and whose Lq queries see its Lk keys, found at key wkoff of the
   // workgroup's keys.  One segment: rows r0 + 64 wave on, wkoff = 0.  Packed
@@ -229,6 +230,13 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   // The key tiles this workgroup visits: all its rows see (packed: all of
   // its keys, every tile masked), or with split-KV the split-th of
   // num_splits runs of them (possibly empty).
+  if constexpr (PK == kPackHeads) {
+    // Query head h + wave / (4 / pack), rows 64 (wave % (4 / pack)) on, of the
+    // one segment (r0 = 0): the workgroup's tiles are an unpacked unit's.
+    const int per = C::WAVES / p.pack;
+    h += wave / per;
+    wrow0 = (wave % per) * C::RPW;
+  }
   TileRange tr0;
   if constexpr (packed) {
     tr0.kt_begin = tr0.full_begin = tr0.full_end = 0;
@@ -799,10 +807,11 @@ namespace va {
 // One kernel, one instantiation per head-dim pair (and, for d_v 72/80, per
 // whether the LSE is returned): 4 waves x 64 query rows, 256-row blocks.
 template <int DQK, int DV, RowSum SUM>
-static Variant wide_variant(bool packed) {
+static Variant wide_variant(int mode) {
   using C = wide::Cfg<DQK, DV>;
-  const void* fn = packed ? (const void*)&attn_fwd_wide<DQK, DV, SUM, true>
-                          : (const void*)&attn_fwd_wide<DQK, DV, SUM, false>;
+  const void* fn = mode == kPackHeads      ? (const void*)&attn_fwd_wide<DQK, DV, SUM, kPackHeads>
+                   : mode == kPackSegments ? (const void*)&attn_fwd_wide<DQK, DV, SUM, kPackSegments>
+                                           : (const void*)&attn_fwd_wide<DQK, DV, SUM, kPackNone>;
   return {fn, C::LDS_BYTES, C::BM, wide::kBN, C::THREADS, "attn_fwd_wide"};
 }
 
@@ -813,11 +822,11 @@ static bool supported_dims(int dqk, int dv) {
 
 // `lse`: whether the caller asked for the LSE (without one the row sum is
 // taken over the bf16 probabilities, see RowSum; the launch shape is the same
-// either way).  Short segments (segments_per_block > 1) take the packed
-// instantiation; the other one carries none of its set-up.
-static Variant variant_for(int dqk, int dv, int max_seqlen_q, bool lse = true) {
+// either way).  Short segments take a packed instantiation (pack_mode); the
+// unpacked one carries none of its set-up.
+static Variant variant_for(int dqk, int dv, int max_seqlen_q, int heads, int heads_k, bool lse = true) {
   (void)dv;
-  const bool pk = segments_per_block(max_seqlen_q, wide::kRowsPerWave) > 1;
+  const int pk = pack_mode(max_seqlen_q, wide::kRowsPerWave, heads, heads_k);
   constexpr RowSum F = RowSum::kF32, M = RowSum::kMfma;
   if (dqk == 64) return wide_variant<64, 64, F>(pk);
   if (dqk == 72) return lse ? wide_variant<72, 72, F>(pk) : wide_variant<72, 72, M>(pk);
@@ -828,14 +837,18 @@ static Variant variant_for(int dqk, int dv, int max_seqlen_q, bool lse = true) {
 
 static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
-// Work units of a launch (padding included): (segment, head, q-tile), or
-// with short segments packed (segments_per_block > 1) (group, head).
-static int64_t launch_units(int64_t batch, int64_t heads, int64_t max_seqlen_q, int block_m, int32_t* n_qt_out,
-                            int32_t* pack_out) {
+// Work units of a launch (padding included): (segment, head, q-tile); with
+// short segments packed (pack_mode) (group of segments, head) or (segment,
+// group of query heads).
+static int64_t launch_units(int64_t batch, int64_t heads, int64_t heads_k, int64_t max_seqlen_q, int block_m,
+                            int32_t* n_qt_out, int32_t* pack_out, int32_t* mode_out = nullptr) {
+  const int32_t mode = pack_mode(max_seqlen_q, block_m / 4, heads, heads_k);
   const int32_t pack = segments_per_block(max_seqlen_q, block_m / 4);
   const int64_t n_qt = pack > 1 ? 1 : (max_seqlen_q + block_m - 1) / block_m;
   if (n_qt_out) *n_qt_out = (int32_t)n_qt;
   if (pack_out) *pack_out = pack;
+  if (mode_out) *mode_out = mode;
+  if (mode == kPackHeads) return grid_blocks(batch, heads / pack, 1);
   return grid_blocks((batch + pack - 1) / pack, heads, n_qt);
 }
 
@@ -901,9 +914,18 @@ extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_h
     max_q = seqlens_q[i] > max_q ? seqlens_q[i] : max_q;
   }
   if (max_q <= 0) return VA_ERR_ARG;
-  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, max_q);
-  int32_t n_qt = 0, pack = 1;
-  if (block < 0 || block >= va::launch_units(batch, num_heads, max_q, var.block_m, &n_qt, &pack)) return VA_ERR_ARG;
+  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, max_q, num_heads, num_heads_k);
+  int32_t n_qt = 0, pack = 1, mode = va::kPackNone;
+  if (block < 0 || block >= va::launch_units(batch, num_heads, num_heads_k, max_q, var.block_m, &n_qt, &pack, &mode))
+    return VA_ERR_ARG;
+  if (mode == va::kPackHeads) {  // (segment, first query head of the group)
+    const int32_t vheads = num_heads / pack;
+    const va::WorkUnit u = va::decode_block((uint32_t)block, (uint32_t)batch, (uint32_t)vheads, 1u, causal);
+    *segment = u.valid ? u.b : -1;
+    *head = u.valid ? va::query_head(u.h, vheads, num_heads_k) * pack : -1;
+    *q_tile = u.valid ? 0 : -1;
+    return VA_OK;
+  }
   const int32_t groups = (batch + pack - 1) / pack;
   const va::WorkUnit u = pack == 1 && va::lpt_applies(batch, seqlens_q, seqlens_k)
                              ? va::decode_block_lpt(block, batch, num_heads, var.block_m, n_qt, causal,
@@ -917,38 +939,42 @@ extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_h
 }
 
 extern "C" int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch,
-                                int32_t num_heads, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                                int32_t causal, va_plan* plan) {
+                                int32_t num_heads, int32_t num_heads_k, int32_t max_seqlen_q,
+                                int32_t max_seqlen_k, int32_t causal, va_plan* plan) {
   (void)max_seqlen_k;
   (void)causal;
   if (!plan) return VA_ERR_NULL;
   if (!va::supported_dims(head_dim_qk, head_dim_v)) return VA_ERR_HEADDIM;
   if (batch < 0 || num_heads <= 0 || max_seqlen_q < 0) return VA_ERR_ARG;
-  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, max_seqlen_q);
+  if (num_heads_k <= 0 || num_heads % num_heads_k != 0) return VA_ERR_ARG;
+  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, max_seqlen_q, num_heads, num_heads_k);
   plan->block_m = var.block_m;
   plan->block_n = var.block_n;
   plan->threads = var.threads;
   plan->lds_bytes = var.lds_bytes;
-  plan->grid = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, nullptr, &plan->segments_per_block);
+  plan->grid = va::launch_units(batch, num_heads, num_heads_k, max_seqlen_q, var.block_m, nullptr,
+                                &plan->segments_per_block, &plan->pack_mode);
   plan->kernel = var.name;
   return VA_OK;
 }
 
 extern "C" int varlen_attn_plan_fp8(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch,
-                                    int32_t num_heads, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                                    int32_t causal, va_plan* plan) {
+                                    int32_t num_heads, int32_t num_heads_k, int32_t max_seqlen_q,
+                                    int32_t max_seqlen_k, int32_t causal, va_plan* plan) {
   (void)max_seqlen_k;
   (void)causal;
   if (!plan) return VA_ERR_NULL;
   if (!va::fp8_supported_dims(head_dim_qk, head_dim_v)) return VA_ERR_HEADDIM;
   if (batch < 0 || num_heads <= 0 || max_seqlen_q < 0) return VA_ERR_ARG;
-  const va::Variant var = va::fp8_variant(head_dim_qk, head_dim_v,
-                                          va::segments_per_block(max_seqlen_q, va::wide::kRowsPerWave) > 1);
+  if (num_heads_k <= 0 || num_heads % num_heads_k != 0) return VA_ERR_ARG;
+  const va::Variant var = va::fp8_variant(
+      head_dim_qk, head_dim_v, va::pack_mode(max_seqlen_q, va::wide::kRowsPerWave, num_heads, num_heads_k));
   plan->block_m = var.block_m;
   plan->block_n = var.block_n;
   plan->threads = var.threads;
   plan->lds_bytes = var.lds_bytes;
-  plan->grid = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, nullptr, &plan->segments_per_block);
+  plan->grid = va::launch_units(batch, num_heads, num_heads_k, max_seqlen_q, var.block_m, nullptr,
+                                &plan->segments_per_block, &plan->pack_mode);
   plan->kernel = var.name;
   return VA_OK;
 }
@@ -1023,9 +1049,9 @@ static int prepare(const va_tensor* q, const va_tensor* k, const va_tensor* v, c
 static int launch_attention(Params& p, int32_t head_dim_qk, int32_t head_dim_v, int32_t max_seqlen_q,
                             bool fp32_row_sum, void* stream, bool fp8 = false) {
   const Variant var =
-      fp8 ? fp8_variant(head_dim_qk, head_dim_v, segments_per_block(max_seqlen_q, wide::kRowsPerWave) > 1)
-          : variant_for(head_dim_qk, head_dim_v, max_seqlen_q, fp32_row_sum);
-  const int64_t units = launch_units(p.batch, p.heads, max_seqlen_q, var.block_m, &p.n_qt, &p.pack);
+      fp8 ? fp8_variant(head_dim_qk, head_dim_v, pack_mode(max_seqlen_q, wide::kRowsPerWave, p.heads, p.heads_k))
+          : variant_for(head_dim_qk, head_dim_v, max_seqlen_q, p.heads, p.heads_k, fp32_row_sum);
+  const int64_t units = launch_units(p.batch, p.heads, p.heads_k, max_seqlen_q, var.block_m, &p.n_qt, &p.pack);
   const int64_t grid = units * p.num_splits;
   if (grid > INT32_MAX) return VA_ERR_SHAPE;
   p.n_units = (int32_t)units;
@@ -1075,8 +1101,8 @@ extern "C" int varlen_attn_num_splits(int32_t head_dim_qk, int32_t head_dim_v, i
     return VA_OK;
   // The work units a launch has (padding included) against the workgroups
   // the device holds at once; each split keeps at least 16 key tiles.
-  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, max_seqlen_q, true);
-  const int64_t units = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, nullptr, nullptr);
+  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, max_seqlen_q, num_heads, num_heads, true);
+  const int64_t units = va::launch_units(batch, num_heads, num_heads, max_seqlen_q, var.block_m, nullptr, nullptr);
   const int64_t slots = (int64_t)cus * (var.lds_bytes <= 80 * 1024 ? 2 : 1);
   const int64_t by_tiles = ((int64_t)max_seqlen_k + 16 * var.block_n - 1) / (16 * var.block_n);
   int64_t s = slots / units;

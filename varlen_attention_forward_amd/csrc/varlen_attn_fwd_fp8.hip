@@ -128,7 +128,7 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
 // t of lane (d, g) covers bytes 8t..8t+7, i.e. keys 16 t + 8 (i / 4) + 4 g +
 // i % 4 for rows i = 0..7.
 // ============================================================================
-template <int DQK, int DV, bool PACKED>
+template <int DQK, int DV, int PK>
 __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
   using namespace fp8k;
   using C = Cfg<DQK, DV>;
@@ -171,13 +171,14 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
   const int g = lane >> 5;
 
   const int split = (int)(blockIdx.x / (uint32_t)p.n_units);
-  const BlockWork bw = block_work<PACKED>(p, lane, C::BM, (int64_t)blockIdx.x - (int64_t)split * p.n_units);
+  const BlockWork bw = block_work<PK>(p, lane, C::BM, (int64_t)blockIdx.x - (int64_t)split * p.n_units);
   if (!bw.u.valid) return;
-  const int h = bw.u.h, qt = bw.u.qt;
+  int h = bw.u.h;
+  const int qt = bw.u.qt;
   const int k0 = bw.k0, Lk = bw.lk;
   const int r0 = qt * C::BM;
   if (r0 >= bw.lq) return;
-  constexpr bool packed = PACKED;
+  constexpr bool packed = PK == kPackSegments;
   // This wave's rows and segment (as in attn_fwd_wide).
   int q0 = bw.q0, Lq = bw.lq, wLk = Lk, wkoff = 0, wrow0 = r0 + wave * C::RPW;
   int r1 = min(r0 + C::BM, Lq);
@@ -195,6 +196,13 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
       wLk = p.cu_k[seg + 1] - k0 - wkoff;
       r1 = Lq;
     }
+  }
+  if constexpr (PK == kPackHeads) {
+    // Query head h + wave / (4 / pack), rows 64 (wave % (4 / pack)) on, of the
+    // one segment (r0 = 0): the workgroup's tiles are an unpacked unit's.
+    const int per = C::WAVES / p.pack;
+    h += wave / per;
+    wrow0 = (wave % per) * C::RPW;
   }
   TileRange tr0;
   if constexpr (packed) {
@@ -453,7 +461,6 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
     bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) bad |= j == first_j[qb];
-    uint32_t pk[QB][4 * kSB];
     auto unit = [&](auto uu) VA_INLINE {
       constexpr int u = decltype(uu)::value;
       if constexpr (u < kExpU) {  // p = exp2(s * scale - m_run), in place
@@ -463,16 +470,11 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
         constexpr int i = u - kExpU, qb = i / (8 * kSB), sb = (i / 8) % kSB, pr = i % 8, r = 2 * pr;
         constexpr int w = 4 * sb + pr / 2;
         constexpr bool hi = pr % 2 == 1, first = sb == 0 && pr == 0, last = sb == kSB - 1 && pr == 7;
-        pk[qb][w] = pack_e4m3x2<hi>(s[qb][sb][r], s[qb][sb][r + 1], hi ? pk[qb][w] : 0u);
+        // (straight into the PV operand: every PV MFMA reading it has issued)
+        pf[qb][w] = (int)pack_e4m3x2<hi>(s[qb][sb][r], s[qb][sb][r + 1], hi ? (uint32_t)pf[qb][w] : 0u);
         const float pair = s[qb][sb][r] + s[qb][sb][r + 1];
         sum[qb] = first ? pair : sum[qb] + pair;
-        if constexpr (last) {
-          i32x8 v;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (int)pk[qb][e];
-          pf[qb] = v;
-          bad |= !(sum[qb] <= kSumLimit);
-        }
+        if constexpr (last) bad |= !(sum[qb] <= kSumLimit);
       }
     };
     const f32x16 zero = {};
@@ -680,17 +682,19 @@ bool fp8_supported_dims(int dqk, int dv) {
 }
 
 template <int DQK, int DV>
-static Variant fp8_variant_t(bool packed) {
+static Variant fp8_variant_t(int mode) {
   using C = fp8k::Cfg<DQK, DV>;
-  const void* fn = packed ? (const void*)&attn_fwd_fp8<DQK, DV, true> : (const void*)&attn_fwd_fp8<DQK, DV, false>;
+  const void* fn = mode == kPackHeads      ? (const void*)&attn_fwd_fp8<DQK, DV, kPackHeads>
+                   : mode == kPackSegments ? (const void*)&attn_fwd_fp8<DQK, DV, kPackSegments>
+                                           : (const void*)&attn_fwd_fp8<DQK, DV, kPackNone>;
   return {fn, C::LDS_BYTES, C::BM, fp8k::kBN, C::THREADS, "attn_fwd_fp8"};
 }
 
-Variant fp8_variant(int dqk, int dv, bool packed) {
+Variant fp8_variant(int dqk, int dv, int pack_mode) {
   (void)dv;
-  if (dqk == 64) return fp8_variant_t<64, 64>(packed);
-  if (dqk == 128) return fp8_variant_t<128, 128>(packed);
-  return fp8_variant_t<192, 128>(packed);
+  if (dqk == 64) return fp8_variant_t<64, 64>(pack_mode);
+  if (dqk == 128) return fp8_variant_t<128, 128>(pack_mode);
+  return fp8_variant_t<192, 128>(pack_mode);
 }
 
 }  // namespace va

@@ -53,6 +53,11 @@ class Workload:
     description: str = ""
     num_splits: int = 1  # split-KV runs per work unit; 0: the library chooses
     dtype: str = "bf16"  # input element type: "bf16", or "e4m3" (fp8 with descales)
+    num_heads_k: Optional[int] = None  # KV heads (grouped KV heads); None: num_heads
+
+    @property
+    def heads_k(self) -> int:
+        return self.num_heads if self.num_heads_k is None else int(self.num_heads_k)
 
     @property
     def batch(self) -> int:
@@ -179,6 +184,20 @@ def _named_workloads() -> dict:
             "128, LSE returned; split-KV with the library's split count",
         ),
         Workload(
+            name="gqa_chunk64_d128",
+            seed=8,
+            seqlens_q=(64,) * 64,
+            seqlens_k=(2048,) * 64,
+            num_heads=32,
+            head_dim_qk=128,
+            head_dim_v=128,
+            causal=True,
+            num_heads_k=4,
+            description="grouped KV heads with short queries: 64 segments of 64 new queries over 2048 keys "
+            "each (causal, bottom-right), 32 query heads over 4 KV heads, d=128, LSE returned; four query "
+            "heads of a KV head per workgroup",
+        ),
+        Workload(
             name="vit_long65536_d128_fp8",
             seed=4,
             seqlens_q=(65536,),
@@ -218,6 +237,7 @@ WORKLOAD_ORDER = (
     "vit_long65536_d128",
     "mla_causal_192_128",
     "mla_context_chunk_tp8",
+    "gqa_chunk64_d128",
     "vit_long65536_d128_fp8",
     "mla_causal_192_128_fp8",
 )
@@ -385,7 +405,8 @@ def workload_inputs(w: Workload):
     ``Inputs``, or ``Fp8Inputs`` for an e4m3 workload."""
     if w.dtype == "e4m3":
         return make_fp8_inputs(w.seqlens_q, w.seqlens_k, w.num_heads, w.head_dim_qk, w.head_dim_v, w.seed,
-                               causal=w.causal, window=w.window, softmax_scale=w.softmax_scale)
+                               causal=w.causal, window=w.window, softmax_scale=w.softmax_scale,
+                               num_heads_k=w.num_heads_k)
     if w.name == "vit_full_d80":
         # Keep the generator stream identical to drawing the lengths first and
         # then Q, K, V from the same generator.
@@ -399,9 +420,9 @@ def workload_inputs(w: Workload):
 def _draw_with(g: torch.Generator, w: Workload) -> Inputs:
     q = torch.randn((w.total_q, w.num_heads, w.head_dim_qk), generator=g, dtype=torch.float32)
     q = q.to(torch.bfloat16)
-    k = torch.randn((w.total_k, w.num_heads, w.head_dim_qk), generator=g, dtype=torch.float32)
+    k = torch.randn((w.total_k, w.heads_k, w.head_dim_qk), generator=g, dtype=torch.float32)
     k = k.to(torch.bfloat16)
-    v = torch.randn((w.total_k, w.num_heads, w.head_dim_v), generator=g, dtype=torch.float32)
+    v = torch.randn((w.total_k, w.heads_k, w.head_dim_v), generator=g, dtype=torch.float32)
     v = v.to(torch.bfloat16)
     return Inputs(
         q=q,

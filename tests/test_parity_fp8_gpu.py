@@ -309,3 +309,44 @@ def test_fp8_packed_query_heads(dims, heads, heads_k, hi, mode):
     assert_fp8_parity(inp, out, lse, what="fp8 packed heads %s %d/%d %d %s" % (dims, heads, heads_k, hi, mode))
     out2, lse2 = run_fp8(dataclasses.replace(inp, max_seqlen_q=257))
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_fp8_hip_graph_replay_matches_eager(splits):
+    """The fp8 call (with split-KV: two kernels, workspace allocated before
+    capture) replays from a HIP graph bit-equal to the eager call, three times
+    with eager work in between."""
+    inp = make([300, 77, 1029], [300, 500, 1029], (128, 128), seed=25, mode="causal", heads=2)
+    d = inp.to(DEV)
+    nbytes = va.splitkv_workspace_bytes(inp.q.shape[0], 2, 128, splits)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+
+    def call(out, lse):
+        st = va.raw_fwd_fp8(
+            va._binding._desc(d.q, "q", torch.float8_e4m3fn), va._binding._desc(d.k, "k", torch.float8_e4m3fn),
+            va._binding._desc(d.v, "v", torch.float8_e4m3fn), d.q_descale.data_ptr(), d.k_descale.data_ptr(),
+            d.v_descale.data_ptr(), d.cu_seqlens_q.data_ptr(), d.cu_seqlens_k.data_ptr(), 3, d.max_seqlen_q,
+            d.max_seqlen_k, d.softmax_scale, 1, -1, -1, va._binding._desc(out, "out"), 0, lse.data_ptr(), splits,
+            ws.data_ptr() if splits > 1 else 0, nbytes, torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+
+    shape_o, shape_l = (d.q.shape[0], 2, 128), (2, d.q.shape[0])
+    out_e = torch.empty(shape_o, dtype=torch.bfloat16, device=DEV)
+    lse_e = torch.empty(shape_l, dtype=torch.float32, device=DEV)
+    call(out_e, lse_e)
+    out_g = torch.zeros(shape_o, dtype=torch.bfloat16, device=DEV)
+    lse_g = torch.zeros(shape_l, dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(out_g, lse_g)
+    for _ in range(3):
+        out_g.zero_()
+        lse_g.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e) and torch.equal(lse_g, lse_e)
+        call(torch.empty_like(out_e), torch.empty_like(lse_e))
+        torch.cuda.synchronize()
+    assert_fp8_parity(inp, out_g, lse_g, what="fp8 graph replay")

@@ -111,9 +111,11 @@ template <bool HI>
 __device__ __forceinline__ uint32_t pack_e4m3x2(float a, float b, uint32_t old) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
 }
-// Four fp32 values to e4m3 bytes 0-3.
-__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
-  return pack_e4m3x2<true>(c, d, pack_e4m3x2<false>(a, b, 0u));
+// Four fp32 values to e4m3 bytes 0-3.  The second pack replaces the two
+// bytes the first one keeps, so `reg` (the destination's old value) only
+// spares the compiler a zeroing move.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d, uint32_t reg = 0u) {
+  return pack_e4m3x2<true>(c, d, pack_e4m3x2<false>(a, b, reg));
 }
 
 // ============================================================================
@@ -429,7 +431,6 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) {
       float sum = 0.f;
-      i32x8 pk;
 #pragma unroll
       for (int sb = 0; sb < kSB; ++sb)
 #pragma unroll
@@ -440,9 +441,8 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
             x[e] = __builtin_amdgcn_exp2f(fmaf(s[qb][sb][4 * w + e], sl2, nm[qb]));
             sum += x[e];
           }
-          pk[4 * sb + w] = (int)pack_e4m3x4(x[0], x[1], x[2], x[3]);
+          pf[qb][4 * sb + w] = (int)pack_e4m3x4(x[0], x[1], x[2], x[3], (uint32_t)pf[qb][4 * sb + w]);
         }
-      pf[qb] = pk;
       l_run[qb] = l_run[qb] * alpha[qb] + sum;
     }
     return move;
@@ -471,7 +471,8 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
         constexpr int w = 4 * sb + pr / 2;
         constexpr bool hi = pr % 2 == 1, first = sb == 0 && pr == 0, last = sb == kSB - 1 && pr == 7;
         // (straight into the PV operand: every PV MFMA reading it has issued)
-        pf[qb][w] = (int)pack_e4m3x2<hi>(s[qb][sb][r], s[qb][sb][r + 1], hi ? (uint32_t)pf[qb][w] : 0u);
+        // (the low half's pack keeps the old high bytes, which the high half's replaces)
+        pf[qb][w] = (int)pack_e4m3x2<hi>(s[qb][sb][r], s[qb][sb][r + 1], (uint32_t)pf[qb][w]);
         const float pair = s[qb][sb][r] + s[qb][sb][r + 1];
         sum[qb] = first ? pair : sum[qb] + pair;
         if constexpr (last) bad |= !(sum[qb] <= kSumLimit);

@@ -119,6 +119,27 @@ int varlen_attn_fwd(const va_tensor* q, const va_tensor* k, const va_tensor* v,
                     const va_tensor* out, float* lse, void* stream);
 
 /*
+ * varlen_attn_fwd_quant_out -- varlen_attn_fwd with the output quantised to
+ * fp8 e4m3 under one static per-tensor scale: out = RNE(clamp(O / *out_scale,
+ * -448, 448)) (the vLLM MLA-prefill docs page: supports_quant_output with
+ * kFp8StaticTensorSym, the output_scale argument of
+ * _flash_attn_varlen_diff_headdims; bf16 inputs as there).
+ *
+ *   out        e4m3 [total_q, H, d_v] (va_tensor with strides in bytes; rows
+ *              and heads 16-byte aligned)
+ *   out_scale  device fp32 scalar > 0 (not checked), 4-byte aligned
+ *   the rest   as for varlen_attn_fwd; the LSE is the same as there
+ *
+ * Returns what varlen_attn_fwd returns, and VA_ERR_NULL for a NULL
+ * out_scale, VA_ERR_ALIGN for a misaligned one.
+ */
+int varlen_attn_fwd_quant_out(const va_tensor* q, const va_tensor* k, const va_tensor* v,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                              int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale, int32_t causal,
+                              int32_t window_left, int32_t window_right, const va_tensor* out,
+                              const float* out_scale, float* lse, void* stream);
+
+/*
  * varlen_attn_fwd_splitkv -- varlen_attn_fwd with each work unit's key tiles
  * split into num_splits runs computed by separate workgroups, then combined.
  * Split-KV prefill as the vLLM MLA-prefill docs page describes it (FA4's

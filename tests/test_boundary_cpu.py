@@ -565,3 +565,20 @@ def test_work_unit_head_packing(heads, heads_k, lq, pack):
 def test_pack_mode_choice(heads, heads_k, max_q, mode):
     assert pkg.plan(64, 64, 5, heads, max_q, max_q, 0, num_heads_k=heads_k)["pack_mode"] == mode
     assert pkg.plan(64, 64, 5, heads, max_q, max_q, 0, fp8=True, num_heads_k=heads_k)["pack_mode"] == mode
+
+
+def _call_quant(out=None, out_scale=FAKE, lse=0):
+    lib = pkg.library()
+    t = _t()
+    out = out if out is not None else _t(row_stride=128, head_stride=64)
+    return lib.varlen_attn_fwd_quant_out(ctypes.byref(t), ctypes.byref(t), ctypes.byref(t), ctypes.c_void_p(FAKE),
+                                         ctypes.c_void_p(FAKE), 1, 10, 10, ctypes.c_float(0.125), 0, -1, -1,
+                                         ctypes.byref(out), ctypes.c_void_p(out_scale), ctypes.c_void_p(lse), None)
+
+
+def test_quant_out_validation():
+    assert _call_quant(out_scale=0) == B.VA_ERR_NULL
+    assert _call_quant(out_scale=FAKE + 2) == B.VA_ERR_ALIGN
+    # the e4m3 output's strides count bytes: a multiple of 16 elements
+    assert _call_quant(out=_t(row_stride=136, head_stride=64)) == B.VA_ERR_ALIGN
+    assert _call_quant(out=_t(row_stride=128, head_stride=72)) == B.VA_ERR_ALIGN

@@ -627,3 +627,46 @@ def test_packed_query_heads(dims, heads, heads_k, lens, mode):
     import dataclasses
     out2, lse2 = run_gpu(dataclasses.replace(inp, max_seqlen_q=129 if hi == 128 else 257))
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+# ---------------------------------------------------------------------------
+# bf16 inputs, e4m3 output under a static per-tensor scale
+# (varlen_attn_fwd_quant_out)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dims", DIMS, ids=lambda d: "d%d_%d" % d)
+@pytest.mark.parametrize("mode", ["full", "causal", "window"])
+@pytest.mark.parametrize("with_lse", [True, False])
+def test_quantised_output(dims, mode, with_lse):
+    """O before rounding is within the bf16 path's 2e-2 of the oracle; the
+    e4m3 rounding adds at most half an ulp of O / s (2^-4 relative, 2^-10
+    absolute below the normal range): |decode(code) s - O_ref| <= 2e-2 +
+    s max(2^-4 (|O_ref| + 2e-2) / s, 2^-10).  The LSE is the bf16 call's."""
+    lq, lk = LEN_SETS["ragged"]
+    causal, window = MODES[mode]
+    inp = workloads.make_inputs(lq, lq, 4, dims[0], dims[1], seed=dims[0] + len(mode), causal=causal, window=window)
+    ref_o, ref_lse = oracle_on(inp)
+    s = float(np.float32(np.nanmax(np.abs(ref_o)) / 100.0))
+    d = inp.to(DEV)
+    sc = torch.tensor([s], dtype=torch.float32, device=DEV)
+    # one byte an element: d_v 72 needs heads padded to 80 bytes (16-byte strides)
+    dvp = -(-dims[1] // 16) * 16
+    out_buf = torch.empty((inp.q.shape[0], 4, dvp), dtype=torch.float8_e4m3fn, device=DEV)
+    res = va.varlen_attn_fwd(d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, inp.max_seqlen_q, inp.max_seqlen_k,
+                             softmax_scale=inp.softmax_scale, causal=causal, window_size=window,
+                             return_lse=with_lse, out_scale=sc, out=out_buf[:, :, :dims[1]])
+    out, lse = res if with_lse else (res, None)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float8_e4m3fn
+    got = oracle.e4m3_decode(out.cpu().contiguous().view(torch.uint8).numpy()) * s
+    tol = 2e-2 + s * np.maximum(2.0 ** -4 * (np.abs(ref_o) + 2e-2) / s, 2.0 ** -10)
+    err = np.abs(got - ref_o)
+    assert np.all(err <= tol), "max excess %.3e" % float(np.max(err - tol))
+    ref_out, ref_l = run_gpu(inp, return_lse=with_lse)
+    if with_lse:
+        assert torch.equal(lse, ref_l)
+    # the codes are the RNE e4m3 codes of the bf16 call's O / s wherever that
+    # O (bf16-rounded) is not within a bf16 ulp of a rounding boundary: check
+    # the decoded values agree within one e4m3 ulp everywhere
+    y = f64(ref_out) / s
+    ulp = np.maximum(np.exp2(np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -6))) - 3), 2.0 ** -9)
+    assert np.all(np.abs(got / s - np.clip(y, -448, 448)) <= ulp)

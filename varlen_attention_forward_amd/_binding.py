@@ -45,6 +45,7 @@ EXPORTED_SYMBOLS = (
     "varlen_attn_num_splits",
     "varlen_attn_fwd_fp8",
     "varlen_attn_plan_fp8",
+    "varlen_attn_fwd_quant_out",
 )
 
 
@@ -114,6 +115,9 @@ def library() -> ctypes.CDLL:
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
         ctypes.c_size_t, ctypes.c_void_p,
     ]
+    lib.varlen_attn_fwd_quant_out.restype = ctypes.c_int
+    lib.varlen_attn_fwd_quant_out.argtypes = lib.varlen_attn_fwd.argtypes[:13] + [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.varlen_attn_splitkv_workspace_bytes.restype = ctypes.c_size_t
     lib.varlen_attn_splitkv_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                         ctypes.c_int32]
@@ -297,6 +301,7 @@ def varlen_attn_fwd(
     return_lse: bool = False,
     lse=None,
     num_splits: int = 1,
+    out_scale=None,
 ):
     """Fused varlen attention forward on the current HIP stream.
 
@@ -309,6 +314,8 @@ def varlen_attn_fwd(
     ``num_splits`` splits every work unit's keys into that many runs (split-KV,
     combined at the end; the workspace is allocated here with torch); 0 lets
     the library choose (1 when the call already fills the GPU).
+    ``out_scale`` (a one-element fp32 GPU tensor) makes ``out`` e4m3 codes
+    of O / out_scale (``torch.float8_e4m3fn``; no split-KV).
     """
     import torch
 
@@ -324,8 +331,9 @@ def varlen_attn_fwd(
     d_v = v.shape[2]
     if softmax_scale is None:
         softmax_scale = d_qk ** -0.5
+    out_dtype = torch.bfloat16 if out_scale is None else torch.float8_e4m3fn
     if out is None:
-        out = torch.empty((total_q, H, d_v), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((total_q, H, d_v), dtype=out_dtype, device=q.device)
     if return_lse and lse is None:
         lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
     if lse is not None:
@@ -333,6 +341,18 @@ def varlen_attn_fwd(
             raise ValueError("lse must be a contiguous float32 GPU tensor of shape [H, total_q]")
     wl, wr = window_size
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    if out_scale is not None:
+        if num_splits != 1:
+            raise ValueError("an e4m3 output (out_scale) takes no split-KV")
+        st = library().varlen_attn_fwd_quant_out(
+            ctypes.byref(_desc(q, "q")), ctypes.byref(_desc(k, "k")), ctypes.byref(_desc(v, "v")),
+            ctypes.c_void_p(cu_seqlens_q.data_ptr()), ctypes.c_void_p(cu_seqlens_k.data_ptr()), batch,
+            int(max_seqlen_q), int(max_seqlen_k), float(softmax_scale), int(bool(causal)), int(wl), int(wr),
+            ctypes.byref(_desc(out, "out", torch.float8_e4m3fn)), ctypes.c_void_p(_f32_ptr(out_scale, "out_scale", 1)),
+            ctypes.c_void_p(lse.data_ptr() if lse is not None else 0), ctypes.c_void_p(stream),
+        )
+        _raise_for(st)
+        return (out, lse) if return_lse else out
     if num_splits == 0:
         num_splits = auto_num_splits(d_qk, d_v, batch, H, max_seqlen_q, max_seqlen_k)
     if num_splits == 1:

@@ -215,6 +215,29 @@ __device__ __forceinline__ bf16x8 lds_read_b128(const lds_char* base, int byte_o
   return *(const __attribute__((address_space(3))) bf16x8*)(base + byte_off);
 }
 
+constexpr float kE4M3Max = 448.f;  // largest finite e4m3 value
+
+// Two fp32 values to e4m3 (round to nearest even) in bytes 2 HI, 2 HI + 1 of
+// `old`, the other two bytes kept.
+template <bool HI>
+__device__ __forceinline__ uint32_t pack_e4m3x2(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+// Four fp32 values to e4m3 bytes 0-3.  The second pack replaces the two
+// bytes the first one keeps, so `reg` (the destination's old value) only
+// spares the compiler a zeroing move.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d, uint32_t reg = 0u) {
+  return pack_e4m3x2<true>(c, d, pack_e4m3x2<false>(a, b, reg));
+}
+
+
+// e4m3 codes of four values times `scale`, clamped to +-448 first (the
+// static per-tensor output quantisation).
+__device__ __forceinline__ uint32_t quant_e4m3x4(float a, float b, float c, float d, float scale) {
+  auto q = [scale](float x) { return fminf(fmaxf(x * scale, -kE4M3Max), kE4M3Max); };
+  return pack_e4m3x4(q(a), q(b), q(c), q(d));
+}
+
 // Cross-half (lane l and lane l ^ 32) max and sum: v_permlane32_swap
 // leaves lane l's and lane l ^ 32's values in the two results.
 __device__ __forceinline__ float xhalf_max(float x) {

@@ -765,6 +765,35 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   // each 32-wide block.  Swapping halves with lane row ^ 32 over a pair of
   // chunks (jj, jj + 1) leaves lane g with the 8 contiguous values of chunk
   // jj + g: one 16-byte store instead of two 8-byte ones per lane.
+  // With an output scale (varlen_attn_fwd_quant_out) the same values leave as
+  // e4m3 codes of O / out_scale, 8 bytes a lane.
+  if (p.out_scale != nullptr) {
+    const float os = 1.f / *p.out_scale;
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      const float l = SUM_BY_MFMA ? from_lower_half(acc[C::VB - 1][qb][kSumReg]) : xhalf_sum(l_run[qb]);
+      const int row = wrow0 + 32 * qb + l32;
+      const float inv = l > 0.f ? os / l : 0.f;
+      uint8_t* dst = (uint8_t*)p.o + (int64_t)(q0 + row) * p.o_row + (int64_t)h * p.o_head;
+#pragma unroll
+      for (int vb = 0; vb < C::VB; ++vb)
+#pragma unroll
+        for (int jp = 0; jp < 4; jp += 2) {
+          const f32x16& a = acc[vb][qb];
+          const uint32_t x = quant_e4m3x4(a[4 * jp], a[4 * jp + 1], a[4 * jp + 2], a[4 * jp + 3], inv);
+          const uint32_t y = quant_e4m3x4(a[4 * jp + 4], a[4 * jp + 5], a[4 * jp + 6], a[4 * jp + 7], inv);
+          const auto sw = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+          const int dv = vb * 32 + 8 * (jp + g);
+          if (row < r1 && dv < DV) {
+            const u32x2 o2 = {sw[0], sw[1]};
+            *(u32x2*)(dst + dv) = o2;
+          }
+        }
+      if (row < r1 && p.lse != nullptr && g == 0)
+        p.lse[(int64_t)h * p.total_q + q0 + row] = l > 0.f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
     const float l = SUM_BY_MFMA ? from_lower_half(acc[C::VB - 1][qb][kSumReg]) : xhalf_sum(l_run[qb]);
@@ -1073,6 +1102,22 @@ extern "C" int varlen_attn_fwd(const va_tensor* q, const va_tensor* k, const va_
   const int st = va::prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k, softmax_scale,
                              causal, window_left, window_right, out, lse, p, launch);
   if (st != VA_OK || !launch) return st;
+  return va::launch_attention(p, q->dim, v->dim, max_seqlen_q, lse != nullptr, stream);
+}
+
+extern "C" int varlen_attn_fwd_quant_out(const va_tensor* q, const va_tensor* k, const va_tensor* v,
+                                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                                         int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                                         int32_t causal, int32_t window_left, int32_t window_right,
+                                         const va_tensor* out, const float* out_scale, float* lse, void* stream) {
+  if (!out_scale) return VA_ERR_NULL;
+  if (((uintptr_t)out_scale & 3u) != 0) return VA_ERR_ALIGN;
+  va::Params p;
+  bool launch = false;
+  const int st = va::prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k, softmax_scale,
+                             causal, window_left, window_right, out, lse, p, launch, false, true);
+  if (st != VA_OK || !launch) return st;
+  p.out_scale = out_scale;
   return va::launch_attention(p, q->dim, v->dim, max_seqlen_q, lse != nullptr, stream);
 }
 

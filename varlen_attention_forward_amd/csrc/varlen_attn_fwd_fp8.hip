@@ -48,7 +48,6 @@ constexpr int kStages = 6;           // tile t lives in stage t % 6 (an even cou
 constexpr int kAhead = kStages - 2;  // iteration j issues tile j + 4
 constexpr int kDepth = 3;            // LDS operands read ahead of their MFMA
 constexpr int kWaves = 4;
-constexpr float kE4M3Max = 448.f;
 
 template <int DQK, int DV>
 struct Cfg {
@@ -103,19 +102,6 @@ __device__ __forceinline__ i32x8 lds_read_2xb128(const lds_char* base, int byte_
 
 __device__ __forceinline__ i32x2 lds_read_tr8(const lds_char* base, int byte_off) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(base + byte_off));
-}
-
-// Two fp32 values to e4m3 (round to nearest even) in bytes 2 HI, 2 HI + 1 of
-// `old`, the other two bytes kept.
-template <bool HI>
-__device__ __forceinline__ uint32_t pack_e4m3x2(float a, float b, uint32_t old) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
-}
-// Four fp32 values to e4m3 bytes 0-3.  The second pack replaces the two
-// bytes the first one keeps, so `reg` (the destination's old value) only
-// spares the compiler a zeroing move.
-__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d, uint32_t reg = 0u) {
-  return pack_e4m3x2<true>(c, d, pack_e4m3x2<false>(a, b, reg));
 }
 
 // ============================================================================
@@ -635,10 +621,7 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
     if (out_e4m3) {
       uint8_t* dst = (uint8_t*)p.o + (int64_t)(q0 + row) * p.o_row + (int64_t)h * p.o_head;
       auto q4 = [&](const f32x16& a, int r) VA_INLINE -> uint32_t {
-        float x[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = fminf(fmaxf(a[r + e] * inv, -kE4M3Max), kE4M3Max);
-        return pack_e4m3x4(x[0], x[1], x[2], x[3]);
+        return quant_e4m3x4(a[r], a[r + 1], a[r + 2], a[r + 3], inv);
       };
 #pragma unroll
       for (int vb = 0; vb < C::VB; ++vb)

@@ -197,8 +197,8 @@ int varlen_attn_fwd_splitkv(const va_tensor* q, const va_tensor* k, const va_ten
  *   out            bf16 [total_q, H, d_v], or e4m3 when out_scale is given
  *   out_scale      NULL, or a device fp32 scalar > 0 (not checked)
  *   num_splits, workspace, workspace_bytes
- *                  as for varlen_attn_fwd_splitkv (1 = no split); a split
- *                  call's output is bf16, so out_scale must be NULL there
+ *                  as for varlen_attn_fwd_splitkv (1 = no split; with
+ *                  splits the combine kernel writes the e4m3 output)
  *   other arguments as for varlen_attn_fwd
  *
  * Supported (d_qk, d_v): (64,64), (128,128), (192,128).  The kernel rounds
@@ -206,8 +206,8 @@ int varlen_attn_fwd_splitkv(const va_tensor* q, const va_tensor* k, const va_ten
  * none saturates) and normalises by the fp32 sum of the unrounded ones: O
  * carries a relative rounding of up to 2^-4 per term, the LSE is as exact
  * as for bf16 inputs.  Returns VA_OK or a VA_ERR_* code as
- * varlen_attn_fwd_splitkv; VA_ERR_ARG also for out_scale with num_splits >
- * 1, VA_ERR_ALIGN for a descale or out_scale pointer not 4-byte aligned.
+ * varlen_attn_fwd_splitkv, and VA_ERR_ALIGN for a descale or out_scale
+ * pointer not 4-byte aligned.
  */
 int varlen_attn_fwd_fp8(const va_tensor* q, const va_tensor* k, const va_tensor* v,
                         const float* q_descale, const float* k_descale, const float* v_descale,

@@ -519,7 +519,7 @@ def test_fp8_alignment_is_in_bytes():
 def test_fp8_scalar_arguments():
     assert _call_fp8(splits=0) == B.VA_ERR_ARG
     assert _call_fp8(splits=129) == B.VA_ERR_ARG
-    assert _call_fp8(out_scale=FAKE, splits=2) == B.VA_ERR_ARG  # a split call's output is bf16
+    assert _call_fp8(out_scale=FAKE, splits=2) == B.VA_ERR_NULL  # e4m3 output with splits: needs a workspace
     assert _call_fp8(splits=2, ws=0) == B.VA_ERR_NULL
     assert _call_fp8(splits=2, ws=FAKE + 16, ws_bytes=1 << 30) == B.VA_ERR_ALIGN
     assert _call_fp8(splits=2, ws=FAKE, ws_bytes=16) == B.VA_ERR_ARG

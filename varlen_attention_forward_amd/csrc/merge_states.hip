@@ -31,6 +31,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "attn_common.h"  // quant_e4m3x4
 #include "varlen_attn.h"
 
 namespace va_merge {
@@ -110,7 +111,9 @@ __global__ __launch_bounds__(256) void merge_states(Params p) {
 // and its natural-log LSE L_s [S, H, rows] over the split's keys (-inf where
 // a row saw none of them); the combine over the S disjoint key sets is the
 // merge above taken S ways: L = m + ln sum_s e^(L_s - m) with m = max_s L_s,
-// O = sum_s e^(L_s - L) O_s, out = bf16(O).  Only rows of some segment,
+// O = sum_s e^(L_s - L) O_s, out = bf16(O), or with an output scale the
+// e4m3 codes of clamp(O / scale, +-448) (the fp8 call's static per-tensor
+// output quantisation).  Only rows of some segment,
 // [cu_seqlens_q[0], cu_seqlens_q[batch]), are written: the others were not
 // computed and are left untouched, as the unsplit forward leaves them.  A
 // group of G lanes (G the power of two >= d / 4) owns one (row, head); lane
@@ -125,6 +128,7 @@ struct CombineParams {
   int64_t rows;
   int32_t heads, dim, splits, batch;
   int32_t lane_shift;
+  const float* out_scale;  // null: bf16 out; else e4m3 out (o holds bytes)
 };
 
 __global__ __launch_bounds__(256) void combine_splits(CombineParams p) {
@@ -158,16 +162,22 @@ __global__ __launch_bounds__(256) void combine_splits(CombineParams p) {
         }
       }
     }
-    const u32x2 r = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-    *(u32x2*)(p.o + i * p.o_row + h * p.o_head + 4 * c) = r;
+    if (p.out_scale != nullptr) {
+      const uint32_t code = va::quant_e4m3x4(acc[0], acc[1], acc[2], acc[3], 1.f / *p.out_scale);
+      *(uint32_t*)((uint8_t*)p.o + i * p.o_row + h * p.o_head + 4 * c) = code;
+    } else {
+      const u32x2 r = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+      *(u32x2*)(p.o + i * p.o_row + h * p.o_head + 4 * c) = r;
+    }
   }
   if (c == 0 && p.l != nullptr) p.l[(int64_t)h * p.rows + i] = m != -INFINITY ? m + logf(sum) : -INFINITY;
 }
 
 int launch_combine(const float* part_o, const float* part_lse, int32_t num_splits, int64_t total_q, int32_t heads,
                    int32_t dim, const int32_t* cu_seqlens_q, int32_t batch, const va_tensor* out, float* lse,
-                   void* stream) {
+                   void* stream, const float* out_scale) {
   CombineParams p;
+  p.out_scale = out_scale;
   p.part_o = part_o;
   p.part_lse = part_lse;
   p.o = (uint16_t*)out->data;

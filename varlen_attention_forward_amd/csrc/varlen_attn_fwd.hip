@@ -1160,7 +1160,7 @@ extern "C" int varlen_attn_num_splits(int32_t head_dim_qk, int32_t head_dim_v, i
 namespace va_merge {
 int launch_combine(const float* part_o, const float* part_lse, int32_t num_splits, int64_t total_q, int32_t heads,
                    int32_t dim, const int32_t* cu_seqlens_q, int32_t batch, const va_tensor* out, float* lse,
-                   void* stream);
+                   void* stream, const float* out_scale = nullptr);
 }
 
 extern "C" int varlen_attn_fwd_splitkv(const va_tensor* q, const va_tensor* k, const va_tensor* v,
@@ -1200,7 +1200,6 @@ extern "C" int varlen_attn_fwd_fp8(const va_tensor* q, const va_tensor* k, const
                                    const float* out_scale, float* lse, int32_t num_splits, void* workspace,
                                    size_t workspace_bytes, void* stream) {
   if (num_splits < 1 || num_splits > va::kMaxSplits) return VA_ERR_ARG;
-  if (out_scale != nullptr && num_splits > 1) return VA_ERR_ARG;  // the combine writes bf16
   for (const float* d : {q_descale, k_descale, v_descale, out_scale})
     if (((uintptr_t)d & 3u) != 0) return VA_ERR_ALIGN;
   va::Params p;
@@ -1223,5 +1222,5 @@ extern "C" int varlen_attn_fwd_fp8(const va_tensor* q, const va_tensor* k, const
                         va::align256((size_t)num_splits * (size_t)q->rows * (size_t)q->heads * (size_t)v->dim * 4));
   if ((st = va::launch_attention(p, q->dim, v->dim, max_seqlen_q, true, stream, true)) != VA_OK) return st;
   return va_merge::launch_combine(p.part_o, p.part_lse, num_splits, q->rows, q->heads, v->dim, cu_seqlens_q, batch,
-                                  out, lse, stream);
+                                  out, lse, stream, out_scale);
 }

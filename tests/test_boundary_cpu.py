@@ -582,3 +582,17 @@ def test_quant_out_validation():
     # the e4m3 output's strides count bytes: a multiple of 16 elements
     assert _call_quant(out=_t(row_stride=136, head_stride=64)) == B.VA_ERR_ALIGN
     assert _call_quant(out=_t(row_stride=128, head_stride=72)) == B.VA_ERR_ALIGN
+
+
+@pytest.mark.parametrize("dims,lds_kib", [((64, 64), 55), ((128, 128), 103), ((192, 128), 127)])
+def test_plan_fp8(dims, lds_kib):
+    """The fp8 kernel: 256-row workgroups of 4 waves, 64-key tiles (one fp8
+    PV MFMA takes 64 keys), six LDS stages of K (plus a pad chunk a row) and
+    V bytes; the grid is the bf16 kernel's (same work units)."""
+    p8 = pkg.plan(dims[0], dims[1], 3, 16, 4096, 4096, 1, fp8=True)
+    p16 = pkg.plan(dims[0], dims[1], 3, 16, 4096, 4096, 1)
+    assert p8["kernel"] == "attn_fwd_fp8" and p8["block_n"] == 64 and p8["block_m"] == 256
+    assert p8["threads"] == 256 and p8["grid"] == p16["grid"]
+    assert p8["lds_bytes"] // 1024 == lds_kib and p8["lds_bytes"] <= 160 * 1024
+    with pytest.raises(ValueError):
+        pkg.plan(80, 80, 1, 16, 64, 64, 0, fp8=True)  # d 80 has no fp8 instantiation

@@ -153,6 +153,7 @@ def assert_fp8_parity(inp, out, lse, rows=None, heads=None, what=""):
     tol, dsr = o_tolerance(inp, rows=rows, heads=heads, want_ds=True)
     o = f64(out)
     sel = ~np.isnan(ref_o)
+    assert np.all(np.isfinite(tol[sel])), "%s: the bound is not finite where it is checked" % what
     assert np.all(np.isfinite(o[sel])), "%s: non-finite output" % what
     err = np.abs(o - ref_o)
     bad = sel & (err > tol)
@@ -165,7 +166,9 @@ def assert_fp8_parity(inp, out, lse, rows=None, heads=None, what=""):
         neg = lsel & (ref_lse == -np.inf)
         assert np.array_equal(l[lsel] == -np.inf, neg[lsel]), "%s: -inf LSE rows differ" % what
         fin = lsel & ~neg
-        excess = (np.abs(l - ref_lse) - (TOL_LSE + dsr))[fin]
+        assert np.all(np.isfinite(dsr[fin])), "%s: score-error bound not finite" % what
+        with np.errstate(invalid="ignore"):  # -inf - -inf off the checked rows
+            excess = (np.abs(l - ref_lse) - (TOL_LSE + dsr))[fin]
         assert not (excess > 0).any(), "%s: LSE over 1e-3 + ds by up to %.3e" % (what, float(np.max(excess)))
     return worst
 

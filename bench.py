@@ -116,59 +116,155 @@ def load_traffic(workload: str):
     return float(t["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(w, inp, budget_s: float = 12.0) -> dict:
-    """Time the fp64 oracle on whole heads of the workload until ``budget_s``."""
+def host_info() -> dict:
+    """The host's core counts and CPU model, as the oracle baseline reports them."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - not Linux
+        affinity = os.cpu_count() or 1
+    return {"cpu_count": os.cpu_count(), "affinity": affinity, "cpu_model": model}
+
+
+# Oracle tasks run in forked worker processes that inherit these arrays.
+_ORACLE_ARGS = {}
+
+
+def _limit_blas_threads():
+    try:
+        from threadpoolctl import threadpool_limits
+
+        threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        pass
+
+
+def _oracle_task(task):
+    """One (segment, head, block of query rows) of the workload through the
+    oracle, on that segment and head alone."""
+    import numpy as np
+
+    a = _ORACLE_ARGS
+    b, h, r0, r1, _ = task
+    cu_q, cu_k, group = a["cu_q"], a["cu_k"], a["group"]
+    q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+    hk = h // group
+    sl_q, sl_k = slice(q0, q1), slice(k0, k1)
+    rows = np.arange(r0, r1)
+    if a["fp8"]:
+        from oracle import attention_fwd_fp8
+
+        one = lambda x: x[b:b + 1, hk:hk + 1]
+        attention_fwd_fp8(a["q"][sl_q, h:h + 1], a["k"][sl_k, hk:hk + 1], a["v"][sl_k, hk:hk + 1], [0, q1 - q0],
+                          [0, k1 - k0], a["scale"], a["causal"], a["wl"], a["wr"], rows=rows,
+                          q_descale=one(a["q_descale"]), k_descale=one(a["k_descale"]),
+                          v_descale=one(a["v_descale"]))
+    else:
+        from oracle import attention_fwd
+
+        attention_fwd(a["q"][sl_q, h:h + 1], a["k"][sl_k, hk:hk + 1], a["v"][sl_k, hk:hk + 1], [0, q1 - q0],
+                      [0, k1 - k0], a["scale"], a["causal"], a["wl"], a["wr"], rows=rows)
+    return task
+
+
+def cpu_baseline(w, inp, budget_s: float = 12.0, row_block: int = 512) -> dict:
+    """The fp64 oracle timed on the host cores: one task per (segment, head,
+    block of ``row_block`` query rows), in a seeded random order, on a pool
+    of forked worker processes (one per core of this process's affinity,
+    at most 16), each with one BLAS thread.  Tasks run until ``budget_s`` of
+    wall time has passed; the rate is the algorithmic FLOPs of the completed
+    tasks over that time.  Must run before the GPU is initialised (the
+    workers are forks of this process)."""
+    import multiprocessing
+
     import numpy as np
     import torch
-    from oracle import attention_fwd
-
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = os.cpu_count() or 1
-    from oracle import attention_fwd_fp8
 
     fp8 = w.dtype == "e4m3"
     if fp8:
         u8 = lambda t: t.view(torch.uint8).numpy()
-        q, k, v = u8(inp.q), u8(inp.k), u8(inp.v)
-        desc = dict(q_descale=inp.q_descale.numpy(), k_descale=inp.k_descale.numpy(),
-                    v_descale=inp.v_descale.numpy())
+        arrays = dict(q=u8(inp.q), k=u8(inp.k), v=u8(inp.v), q_descale=inp.q_descale.numpy(),
+                      k_descale=inp.k_descale.numpy(), v_descale=inp.v_descale.numpy())
     else:
-        q = inp.q.to(torch.float32).numpy()
-        k = inp.k.to(torch.float32).numpy()
-        v = inp.v.to(torch.float32).numpy()
+        f = lambda t: t.to(torch.float32).numpy()
+        arrays = dict(q=f(inp.q), k=f(inp.k), v=f(inp.v))
     cu_q, cu_k = inp.cu_seqlens_q.tolist(), inp.cu_seqlens_k.tolist()
     wl, wr = w.window
-    per_head = algorithmic_flops(w) / w.num_heads
-    t0 = time.perf_counter()
-    done = 0
-    rows = None
-    if w.name.startswith("vit_long65536_d128"):
-        rows = np.arange(0, w.total_q, 64)  # 1/64 of the rows: every row costs the same
-    for h in range(w.num_heads):
-        if fp8:
-            attention_fwd_fp8(q, k, v, cu_q, cu_k, w.scale, w.causal, wl, wr, rows=rows, heads=[h], **desc)
-        else:
-            attention_fwd(q, k, v, cu_q, cu_k, w.scale, w.causal, wl, wr, rows=rows, heads=[h])
-        done += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    el = time.perf_counter() - t0
-    frac_rows = 1.0 if rows is None else len(rows) / w.total_q
-    flops = per_head * done * frac_rows
-    sample = "%d of %d heads, %s rows, fp64 numpy oracle%s" % (
-        done, w.num_heads, "all" if rows is None else "every 64th of the", " on dequantised e4m3" if fp8 else "")
+    _ORACLE_ARGS.clear()
+    _ORACLE_ARGS.update(arrays, cu_q=cu_q, cu_k=cu_k, group=w.num_heads // w.heads_k, scale=w.scale,
+                        causal=w.causal, wl=wl, wr=wr, fp8=fp8)
+    flop_per_pair = 2.0 * (w.head_dim_qk + w.head_dim_v)
+    tasks = []
+    for b in range(w.batch):
+        lq, lk = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        for r0 in range(0, lq, row_block):
+            r1 = min(r0 + row_block, lq)
+            pairs = _pairs_in_rows(lq, lk, r0, r1, w.causal, w.window)
+            for h in range(w.num_heads):
+                tasks.append((b, h, r0, r1, pairs * flop_per_pair))
+    order = np.random.default_rng(0).permutation(len(tasks))
+    tasks = [tasks[i] for i in order]
+    info = host_info()
+    workers = max(1, min(info["affinity"], 16))
+    ctx = multiprocessing.get_context("fork")
+    done_flops, done = 0.0, 0
+    pool = ctx.Pool(workers, initializer=_limit_blas_threads)
+    try:
+        t0 = time.perf_counter()
+        for task in pool.imap_unordered(_oracle_task, tasks, chunksize=1):
+            done_flops += task[4]
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        el = time.perf_counter() - t0
+    finally:
+        pool.terminate()
+        pool.join()
+        _ORACLE_ARGS.clear()
+    total = sum(t[4] for t in tasks)
     return {
-        "value": flops / el / 1e12,
+        "value": done_flops / el / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": workers,
         "kind": "oracle",
-        "sample": sample,
+        "sample": "%d of %d (segment, head, %d-row block) tasks in seeded random order, %.1f%% of the "
+                  "workload's FLOPs, fp64 numpy oracle%s, %d worker processes x 1 BLAS thread" % (
+                      done, len(tasks), row_block, 100.0 * done_flops / total,
+                      " on dequantised e4m3" if fp8 else "", workers),
         "seconds": round(el, 3),
+        "cpu_count": info["cpu_count"],
+        "affinity": info["affinity"],
+        "cpu_model": info["cpu_model"],
     }
+
+
+def _pairs_in_rows(lq, lk, r0, r1, causal, window) -> int:
+    """Visible (query, key) pairs of query rows [r0, r1) of one segment."""
+    if lq <= 0 or lk <= 0:
+        return 0
+    wl, wr = window
+    if not causal and wl < 0 and wr < 0:
+        return (r1 - r0) * lk
+    total = 0
+    off = lk - lq
+    for i in range(r0, r1):
+        p = i + off
+        lo = max(0, p - wl) if wl >= 0 else 0
+        hi = lk - 1
+        if causal:
+            hi = min(hi, p)
+        elif wr >= 0:
+            hi = min(hi, p + wr)
+        total += max(0, hi - lo + 1)
+    return total
 
 
 def device_inputs(w, cpu_inp, rotate: int = 0):
@@ -370,7 +466,8 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -
         if unsplit is not None:
             va_mod = __import__("varlen_attention_forward_amd")
             row["num_splits"] = va_mod.auto_num_splits(w.head_dim_qk, w.head_dim_v, w.batch, w.num_heads,
-                                                       w.max_seqlen_q, w.max_seqlen_k) if ns == 0 else ns
+                                                       w.max_seqlen_q, w.max_seqlen_k, num_heads_k=w.heads_k,
+                                                       fp8=w.dtype == "e4m3") if ns == 0 else ns
             row["unsplit_kernel_ms_best"] = round(unsplit, 4)
             row["unsplit_tflops_best"] = round(flops / unsplit / 1e9, 2)
         rows.append(row)
@@ -442,78 +539,50 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5) -> None:
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    # The warm-up runs long enough (~70 ms on the default workload) for the
-    # shader clock to leave its idle state before the timed steps start.
-    ap.add_argument("--steps", type=int, default=300)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--rotate", type=int, default=0,
-                    help="input copies to cycle through (0 = 3 when the inputs fit the 256 MB MALL, else 1)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--report", action="store_true",
-                    help="timing protocol over every workload (or --workload if given explicitly)")
-    args = ap.parse_args()
+# The secondary configuration the metric names (MLA prefill); timed in the
+# default run beside the ViT batch, which gives ``value``.
+SECONDARY_WORKLOADS = ("mla_causal_192_128",)
+# Warm-up continues past --warmup launches until this much wall time has
+# passed: from idle the shader clock takes tens of milliseconds to ramp up.
+MIN_WARMUP_S = 0.3
 
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr, flush=True)
-        return 2
-    if args.copy_calibration:
-        copy_calibration()
-        return 0
-    if args.report:
-        from varlen_attention_forward_amd import workloads
 
-        explicit = any(a == "--workload" or a.startswith("--workload=") for a in sys.argv[1:])
-        protocol_report([args.workload] if explicit else list(workloads.WORKLOADS))
-        if not explicit:
-            print(json.dumps(merge_report()), flush=True)
-        return 0
-
+def time_workload(w, copies, steps: int, warmup: int, min_warmup_s: float = MIN_WARMUP_S) -> dict:
+    """``warmup`` untimed launches (more until ``min_warmup_s`` of wall time
+    has passed), then exactly ``steps`` launches between HIP events on the
+    launch stream, the shader clock sampled meanwhile."""
     import torch
-    import varlen_attention_forward_amd as va
-    from varlen_attention_forward_amd import workloads
 
-    if args.workload not in workloads.WORKLOADS:
-        print("unknown workload %r; choose from %s" % (args.workload, list(workloads.WORKLOADS)), file=sys.stderr)
-        return 2
-    w = workloads.WORKLOADS[args.workload]
-    print("bench: workload %s, building inputs" % w.name, file=sys.stderr, flush=True)
-    cpu_inp = workloads.workload_inputs(w)
-    in_bytes = algorithmic_bytes(w)
-    rotate = args.rotate or (3 if in_bytes < 256e6 else 1)
-    dev = "cuda:0"
-    copies = []
-    for _ in range(rotate):
-        d = cpu_inp.to(dev)
-        out = torch.empty((w.total_q, w.num_heads, w.head_dim_v), dtype=torch.bfloat16, device=dev)
-        lse = torch.empty((w.num_heads, w.total_q), dtype=torch.float32, device=dev) if w.return_lse else None
-        copies.append((d, out, lse))
-
-    def step(i):
-        launch(copies, i, w.num_splits)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall_s = (t1 - t0) / args.steps
-    kernel_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
+    with ClockSampler(period_s=0.05) as clk:
+        t0 = time.perf_counter()
+        n_warm = 0
+        while n_warm < warmup or time.perf_counter() - t0 < min_warmup_s:
+            launch(copies, n_warm, w.num_splits)
+            n_warm += 1
+            if n_warm % 8 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        warm_s = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(steps):
+            launch(copies, i, w.num_splits)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    return {"wall_s": (t1 - t0) / steps, "kernel_s": ev0.elapsed_time(ev1) / 1e3 / steps,
+            "warmup_launches": n_warm, "warmup_s": warm_s, "sclk_mhz_median": clk.median(),
+            "sclk_samples": len(clk.samples)}
 
-    flops = algorithmic_flops(w)
+
+def result_fields(w, t: dict, steps: int, warmup: int, rotate: int) -> dict:
+    """The bench-contract fields of one workload from its timing."""
+    import varlen_attention_forward_amd as va
+
+    flops, in_bytes = algorithmic_flops(w), algorithmic_bytes(w)
+    wall_s, kernel_s = t["wall_s"], t["kernel_s"]
     mfma_bound = flops / in_bytes >= RIDGE_FLOP_PER_BYTE
     if mfma_bound:
         achieved, peak, r_unit = flops / kernel_s / 1e12, peak_tflops(w), "TFLOP/s"
@@ -521,17 +590,12 @@ def main() -> int:
         achieved, peak, r_unit = in_bytes / kernel_s / 1e9, PEAK_HBM_GBS, "GB/s"
     plan = va.plan(w.head_dim_qk, w.head_dim_v, w.batch, w.num_heads, w.max_seqlen_q, w.max_seqlen_k, w.causal,
                    fp8=w.dtype == "e4m3", num_heads_k=w.heads_k)
-    result = {
-        "metric": METRIC,
+    return {
         "value": round(flops / wall_s / 1e12, 2),
         "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(wall_s * 1e3, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) %s)" % ("bf16" if w.dtype == "bf16" else
                                                   "quantised to e4m3 with per-(segment, head) descales"),
@@ -562,10 +626,104 @@ def main() -> int:
             "traffic": load_traffic(w.name),
             "algorithmic_bytes": in_bytes,
         },
+        "clock": {
+            "sclk_mhz_median": t["sclk_mhz_median"],
+            "sclk_samples": t["sclk_samples"],
+            "warmup_launches": t["warmup_launches"],
+            "warmup_ms": round(t["warmup_s"] * 1e3, 1),
+        },
     }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input copies to cycle through (0 = 3 when the inputs fit the 256 MB MALL, else 1)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="time only --workload (by default the MLA prefill is timed beside the ViT batch)")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--report", action="store_true",
+                    help="timing protocol over every workload (or --workload if given explicitly)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr, flush=True)
+        return 2
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+    if args.report:
+        from varlen_attention_forward_amd import workloads
+
+        explicit = any(a == "--workload" or a.startswith("--workload=") for a in sys.argv[1:])
+        protocol_report([args.workload] if explicit else list(workloads.WORKLOADS))
+        if not explicit:
+            print(json.dumps(merge_report()), flush=True)
+        return 0
+
+    from varlen_attention_forward_amd import workloads
+
+    if args.workload not in workloads.WORKLOADS:
+        print("unknown workload %r; choose from %s" % (args.workload, list(workloads.WORKLOADS)), file=sys.stderr)
+        return 2
+    names = [args.workload]
+    if args.workload == DEFAULT_WORKLOAD and not args.no_secondary:
+        names += list(SECONDARY_WORKLOADS)
+
+    # Inputs on the host, then the oracle baselines, all before the GPU is
+    # touched (the oracle's worker processes are forks of this one).
+    cpu_inputs, baselines = {}, {}
+    for name in names:
+        print("bench: workload %s, building inputs" % name, file=sys.stderr, flush=True)
+        cpu_inputs[name] = workloads.workload_inputs(workloads.WORKLOADS[name])
     if not args.no_cpu_baseline:
-        print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, cpu_inp)
+        for name in names:
+            print("bench: timing the oracle on the host (%s)" % name, file=sys.stderr, flush=True)
+            baselines[name] = cpu_baseline(workloads.WORKLOADS[name], cpu_inputs[name])
+
+    import torch
+
+    results = {}
+    for name in names:
+        w = workloads.WORKLOADS[name]
+        copies = device_inputs(w, cpu_inputs.pop(name), args.rotate)
+        print("bench: timing %d steps of %s" % (args.steps, name), file=sys.stderr, flush=True)
+        t = time_workload(w, copies, args.steps, args.warmup)
+        results[name] = result_fields(w, t, args.steps, args.warmup, len(copies))
+        if name in baselines:
+            results[name]["cpu_baseline"] = baselines[name]
+        del copies
+        torch.cuda.empty_cache()
+
+    main_r = results[names[0]]
+    result = {
+        "metric": METRIC,
+        "value": main_r["value"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": main_r["dtype"],
+        "data": main_r["data"],
+        "config": main_r["config"],
+        "roofline": main_r["roofline"],
+        "clock": main_r["clock"],
+    }
+    if "cpu_baseline" in main_r:
+        result["cpu_baseline"] = main_r["cpu_baseline"]
+    others = [dict(results[n], vs_baseline=None) for n in names[1:]]
+    if others:
+        result["other_configs"] = others
     print(json.dumps(result), flush=True)
     return 0
 

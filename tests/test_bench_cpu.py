@@ -82,3 +82,19 @@ def test_grouped_kv_workload_counts_kv_heads_once():
     q_o = 2 * 32 * 4096 * (128 + 128)
     kv = 2 * 4 * (64 * 2048) * (128 + 128)
     assert bench.algorithmic_bytes(w) == pytest.approx(q_o + kv + 4 * 32 * 4096)
+
+
+@pytest.mark.parametrize("lq,lk", [(1, 1), (7, 7), (600, 600), (300, 1000), (1000, 300)])
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (False, (100, 30)),
+                                           (True, (64, -1))])
+def test_oracle_task_pairs_add_up(lq, lk, causal, window):
+    """The oracle baseline prices each (segment, head, row block) task by the
+    visible pairs of its rows; over the blocks of a segment they add up to
+    the segment's pairs."""
+    total = sum(bench._pairs_in_rows(lq, lk, r0, min(r0 + 256, lq), causal, window) for r0 in range(0, lq, 256))
+    assert total == bench.visible_pairs([lq], [lk], causal, window) == _brute_pairs(lq, lk, causal, *window)
+
+
+def test_host_info_reports_core_counts():
+    info = bench.host_info()
+    assert info["cpu_count"] >= 1 and 1 <= info["affinity"] <= info["cpu_count"]

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings():
     for code in range(-7, 1):
         s = pkg.status_string(code)
-        assert isinstance(s, str) and s
+        assert isinstance(s, str) and s != "unknown status"
     assert pkg.status_string(12345) == "unknown status"
     assert pkg.status_string(B.VA_ERR_HEADDIM).startswith("unsupported")
 
@@ -458,8 +458,14 @@ def test_auto_num_splits():
     n = pkg.auto_num_splits(128, 128, 1, 16, 512, 32768)
     assert 1 <= n <= 128
     assert pkg.auto_num_splits(128, 128, 0, 16, 512, 32768) == 1
+    assert 1 <= pkg.auto_num_splits(128, 128, 1, 32, 64, 32768, num_heads_k=4) <= 128
+    assert 1 <= pkg.auto_num_splits(192, 128, 1, 16, 512, 32768, fp8=True) <= 128
     with pytest.raises(ValueError):
         pkg.auto_num_splits(96, 96, 1, 16, 512, 32768)
+    with pytest.raises(ValueError):
+        pkg.auto_num_splits(80, 80, 1, 16, 512, 32768, fp8=True)  # no fp8 kernel at d 80
+    with pytest.raises(ValueError):
+        pkg.auto_num_splits(128, 128, 1, 16, 512, 32768, num_heads_k=3)  # 16 heads over 3 KV heads
 
 
 def test_merge_rejects_bad_arguments():
@@ -567,21 +573,26 @@ def test_pack_mode_choice(heads, heads_k, max_q, mode):
     assert pkg.plan(64, 64, 5, heads, max_q, max_q, 0, fp8=True, num_heads_k=heads_k)["pack_mode"] == mode
 
 
-def _call_quant(out=None, out_scale=FAKE, lse=0):
+def _call_quant(out=None, out_scale=FAKE, lse=0, batch=1):
     lib = pkg.library()
     t = _t()
     out = out if out is not None else _t(row_stride=128, head_stride=64)
     return lib.varlen_attn_fwd_quant_out(ctypes.byref(t), ctypes.byref(t), ctypes.byref(t), ctypes.c_void_p(FAKE),
-                                         ctypes.c_void_p(FAKE), 1, 10, 10, ctypes.c_float(0.125), 0, -1, -1,
+                                         ctypes.c_void_p(FAKE), batch, 10, 10, ctypes.c_float(0.125), 0, -1, -1,
                                          ctypes.byref(out), ctypes.c_void_p(out_scale), ctypes.c_void_p(lse), None)
 
 
 def test_quant_out_validation():
     assert _call_quant(out_scale=0) == B.VA_ERR_NULL
     assert _call_quant(out_scale=FAKE + 2) == B.VA_ERR_ALIGN
-    # the e4m3 output's strides count bytes: a multiple of 16 elements
-    assert _call_quant(out=_t(row_stride=136, head_stride=64)) == B.VA_ERR_ALIGN
-    assert _call_quant(out=_t(row_stride=128, head_stride=72)) == B.VA_ERR_ALIGN
+    # the e4m3 output's strides count bytes and are written 8 bytes at a
+    # time: multiples of 8 pass (a contiguous d_v 72 head), others do not
+    assert _call_quant(out=_t(row_stride=132, head_stride=64)) == B.VA_ERR_ALIGN
+    assert _call_quant(out=_t(row_stride=128, head_stride=68)) == B.VA_ERR_ALIGN
+    assert _call_quant(out=_t(data=FAKE + 4)) == B.VA_ERR_ALIGN
+    # (batch 0: every check runs, nothing is launched)
+    assert _call_quant(out=_t(row_stride=144, head_stride=72, data=FAKE + 8), batch=0) == B.VA_OK
+    assert _call_quant(out=_t(row_stride=144, head_stride=72, data=FAKE + 4), batch=0) == B.VA_ERR_ALIGN
 
 
 @pytest.mark.parametrize("dims,lds_kib", [((64, 64), 55), ((128, 128), 103), ((192, 128), 127)])

@@ -558,15 +558,19 @@ def test_tensors_beyond_2gib():
 # the named workloads at full size (sampled rows where the oracle is slow)
 # ---------------------------------------------------------------------------
 def _sample_rows(inp, n_random, seed=0):
+    """Rows 0, 1, L - 2, L - 1 of every segment, the rows on both sides of
+    every query-block boundary (b * block_m - 1, b * block_m,
+    b * block_m + 1 for every block b), and ``n_random`` seeded random rows."""
     bm = va.plan(inp.q.shape[2], inp.v.shape[2], len(inp.cu_seqlens_q) - 1, inp.q.shape[1],
                  inp.max_seqlen_q, inp.max_seqlen_k, inp.causal)["block_m"]
     cu = inp.cu_seqlens_q.tolist()
     rows = set()
     for b in range(len(cu) - 1):
         L = cu[b + 1] - cu[b]
-        for r in (0, 1, bm - 1, bm, bm + 1, L - 2, L - 1):
-            if 0 <= r < L:
-                rows.add(cu[b] + r)
+        cand = [0, 1, L - 2, L - 1]
+        for t in range(1, (L + bm - 1) // bm):
+            cand += [t * bm - 1, t * bm, t * bm + 1]
+        rows.update(cu[b] + r for r in cand if 0 <= r < L)
     rng = np.random.default_rng(seed)
     rows.update(rng.integers(0, cu[-1], n_random).tolist())
     return np.array(sorted(rows))
@@ -587,7 +591,7 @@ def test_workload_full_oracle(name):
 
 @pytest.mark.parametrize("name,n_random,heads", [
     ("vit_full_d80", 384, None),
-    ("vit_long65536_d128", 24, None),
+    ("vit_long65536_d128", 1024, None),
     ("mla_causal_192_128", 128, None),
     ("gqa_chunk64_d128", 256, None),
 ])
@@ -670,3 +674,24 @@ def test_quantised_output(dims, mode, with_lse):
     y = f64(ref_out) / s
     ulp = np.maximum(np.exp2(np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -6))) - 3), 2.0 ** -9)
     assert np.all(np.abs(got / s - np.clip(y, -448, 448)) <= ulp)
+
+
+def test_quantised_output_default_allocation_d72():
+    """d_v 72 with out=None: the binding allocates a contiguous [T, H, 72]
+    e4m3 tensor (72-byte heads, which the 8-byte rule for e4m3 outputs
+    accepts); its codes equal those written into a head-padded buffer."""
+    lq = [300, 77, 129]
+    inp = workloads.make_inputs(lq, lq, 4, 72, 72, seed=72, causal=True)
+    d = inp.to(DEV)
+    sc = torch.tensor([0.01], dtype=torch.float32, device=DEV)
+    args = (d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, inp.max_seqlen_q, inp.max_seqlen_k)
+    out = va.varlen_attn_fwd(*args, causal=True, out_scale=sc)
+    buf = torch.empty((inp.q.shape[0], 4, 80), dtype=torch.float8_e4m3fn, device=DEV)
+    out2 = va.varlen_attn_fwd(*args, causal=True, out_scale=sc, out=buf[:, :, :72])
+    torch.cuda.synchronize()
+    assert out.shape == (inp.q.shape[0], 4, 72) and out.is_contiguous()
+    assert torch.equal(out.view(torch.uint8), out2.view(torch.uint8))
+    ref_o, _ = oracle_on(inp)
+    got = oracle.e4m3_decode(out.cpu().view(torch.uint8).numpy()) * 0.01
+    tol = 2e-2 + 0.01 * np.maximum(2.0 ** -4 * (np.abs(ref_o) + 2e-2) / 0.01, 2.0 ** -10)
+    assert np.all(np.abs(got - ref_o) <= tol)

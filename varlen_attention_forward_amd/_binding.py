@@ -122,7 +122,7 @@ def library() -> ctypes.CDLL:
     lib.varlen_attn_splitkv_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                         ctypes.c_int32]
     lib.varlen_attn_num_splits.restype = ctypes.c_int
-    lib.varlen_attn_num_splits.argtypes = [ctypes.c_int32] * 6 + [P(ctypes.c_int32)]
+    lib.varlen_attn_num_splits.argtypes = [ctypes.c_int32] * 8 + [P(ctypes.c_int32)]
     lib.varlen_attn_merge.restype = ctypes.c_int
     lib.varlen_attn_merge.argtypes = [P(VaTensor), ctypes.c_void_p, P(VaTensor), ctypes.c_void_p,
                                       P(VaTensor), ctypes.c_void_p, ctypes.c_void_p]
@@ -258,11 +258,14 @@ def splitkv_workspace_bytes(total_q: int, num_heads: int, head_dim_v: int, num_s
 
 
 def auto_num_splits(head_dim_qk: int, head_dim_v: int, batch: int, num_heads: int, max_seqlen_q: int,
-                    max_seqlen_k: int) -> int:
-    """The library's split count for these sizes (1: the units already fill the GPU)."""
+                    max_seqlen_k: int, num_heads_k: int = None, fp8: bool = False) -> int:
+    """The library's split count for these sizes (1: the units already fill
+    the GPU), for the launch of ``varlen_attn_fwd`` (``fp8``: of
+    ``varlen_attn_fwd_fp8``) with ``num_heads_k`` KV heads (None: num_heads)."""
     n = ctypes.c_int32()
-    st = library().varlen_attn_num_splits(head_dim_qk, head_dim_v, batch, num_heads, max_seqlen_q, max_seqlen_k,
-                                          ctypes.byref(n))
+    hk = num_heads if num_heads_k is None else num_heads_k
+    st = library().varlen_attn_num_splits(head_dim_qk, head_dim_v, batch, num_heads, hk, max_seqlen_q,
+                                          max_seqlen_k, int(bool(fp8)), ctypes.byref(n))
     _raise_for(st)
     return n.value
 
@@ -354,7 +357,7 @@ def varlen_attn_fwd(
         _raise_for(st)
         return (out, lse) if return_lse else out
     if num_splits == 0:
-        num_splits = auto_num_splits(d_qk, d_v, batch, H, max_seqlen_q, max_seqlen_k)
+        num_splits = auto_num_splits(d_qk, d_v, batch, H, max_seqlen_q, max_seqlen_k, num_heads_k=k.shape[1])
     if num_splits == 1:
         st = raw_fwd(
             _desc(q, "q"), _desc(k, "k"), _desc(v, "v"),
@@ -450,7 +453,7 @@ def varlen_attn_fwd_fp8(
     wl, wr = window_size
     stream = torch.cuda.current_stream(q.device).cuda_stream
     if num_splits == 0:
-        num_splits = auto_num_splits(d_qk, d_v, batch, H, max_seqlen_q, max_seqlen_k)
+        num_splits = auto_num_splits(d_qk, d_v, batch, H, max_seqlen_q, max_seqlen_k, num_heads_k=H_kv, fp8=True)
     nbytes, ws_ptr = 0, 0
     if num_splits > 1:
         nbytes = splitkv_workspace_bytes(total_q, H, d_v, num_splits)

@@ -29,7 +29,6 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
-    "-shared",
     "-fPIC",
     # Inputs are finite and masked scores are -inf, never NaN: lets fmaxf map
     # to v_max3_f32 without NaN-quieting copies.
@@ -54,21 +53,45 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library in place and return its path."""
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-o", tmp] + SOURCES
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        if os.path.exists(tmp):
-            os.remove(tmp)
-        raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, err))
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    return res.returncode, "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library in place and return its path.
+
+    Each source is compiled to its own object in parallel (each carries its
+    own gfx950 code object), then the objects are linked into one library."""
+    from concurrent.futures import ThreadPoolExecutor
+    import tempfile
+
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    with tempfile.TemporaryDirectory(prefix="va_build_") as objdir:
+        objs, cmds = [], []
+        for src in SOURCES:
+            obj = os.path.join(objdir, os.path.basename(src) + ".o")
+            objs.append(obj)
+            cmds.append([hipcc()] + HIPCC_FLAGS + ["-c", "-I", INCLUDE, "-I", CSRC, "-o", obj, src])
+        if verbose:
+            for c in cmds:
+                print(" ".join(c), flush=True)
+        with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+            results = list(ex.map(_run, cmds))
+        link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+        for rc, err in results:
+            if rc != 0:
+                raise RuntimeError("hipcc failed (%d):\n%s" % (rc, err))
+            if verbose and err.strip():
+                print(err, file=sys.stderr)
+        if verbose:
+            print(" ".join(link), flush=True)
+        rc, err = _run(link)
+        if rc != 0:
+            if os.path.exists(tmp):
+                os.remove(tmp)
+            raise RuntimeError("hipcc link failed (%d):\n%s" % (rc, err))
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -263,6 +263,7 @@ struct Variant {
   int block_n;
   int threads;
   const char* name;
+  int per_cu;  // workgroups a compute unit holds at once (the launch bounds' minimum)
 };
 
 // The fp8 e4m3 kernel (varlen_attn_fwd_fp8.hip): whether it has an

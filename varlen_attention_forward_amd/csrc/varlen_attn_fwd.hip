@@ -841,7 +841,7 @@ static Variant wide_variant(int mode) {
   const void* fn = mode == kPackHeads      ? (const void*)&attn_fwd_wide<DQK, DV, SUM, kPackHeads>
                    : mode == kPackSegments ? (const void*)&attn_fwd_wide<DQK, DV, SUM, kPackSegments>
                                            : (const void*)&attn_fwd_wide<DQK, DV, SUM, kPackNone>;
-  return {fn, C::LDS_BYTES, C::BM, wide::kBN, C::THREADS, "attn_fwd_wide"};
+  return {fn, C::LDS_BYTES, C::BM, wide::kBN, C::THREADS, "attn_fwd_wide", DQK <= 80 ? 2 : 1};
 }
 
 static bool supported_dims(int dqk, int dv) {
@@ -864,7 +864,6 @@ static Variant variant_for(int dqk, int dv, int max_seqlen_q, int heads, int hea
   return wide_variant<192, 128, F>(pk);
 }
 
-static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 // Work units of a launch (padding included): (segment, head, q-tile); with
 // short segments packed (pack_mode) (group of segments, head) or (segment,
@@ -886,12 +885,15 @@ static int64_t launch_units(int64_t batch, int64_t heads, int64_t heads_k, int64
 static constexpr int64_t kMaxRowStride = (int64_t)1 << 24;
 
 // Strides are in elements of elem_bytes bytes; rows and heads must start on
-// 16-byte boundaries.
-static int check_tensor(const va_tensor* t, bool need_data, int elem_bytes = 2) {
+// `align`-byte boundaries: 16 for every tensor the kernels read or write
+// with 16-byte accesses, 8 for e4m3 outputs (written 8 bytes at a time, so
+// a head of d_v 72 packed contiguously qualifies).
+static int check_tensor(const va_tensor* t, bool need_data, int elem_bytes = 2, int align = 16) {
   if (t->row_stride <= 0 || t->head_stride <= 0 || t->row_stride > kMaxRowStride) return VA_ERR_STRIDE;
-  if (((t->row_stride * elem_bytes) & 15) != 0 || ((t->head_stride * elem_bytes) & 15) != 0) return VA_ERR_ALIGN;
+  const int64_t m = align - 1;
+  if (((t->row_stride * elem_bytes) & m) != 0 || ((t->head_stride * elem_bytes) & m) != 0) return VA_ERR_ALIGN;
   if (need_data && t->data == nullptr) return VA_ERR_NULL;
-  if (!aligned16(t->data)) return VA_ERR_ALIGN;
+  if (((uintptr_t)t->data & (uintptr_t)m) != 0) return VA_ERR_ALIGN;
   return VA_OK;
 }
 
@@ -1037,7 +1039,7 @@ static int prepare(const va_tensor* q, const va_tensor* k, const va_tensor* v, c
   if ((st = check_tensor(q, has_q, in_bytes)) != VA_OK) return st;
   if ((st = check_tensor(k, has_k, in_bytes)) != VA_OK) return st;
   if ((st = check_tensor(v, has_k, in_bytes)) != VA_OK) return st;
-  if ((st = check_tensor(out, has_q, out_bytes)) != VA_OK) return st;
+  if ((st = check_tensor(out, has_q, out_bytes, out_fp8 ? 8 : 16)) != VA_OK) return st;
   if (lse != nullptr && ((uintptr_t)lse & 3u) != 0) return VA_ERR_ALIGN;
   if (batch == 0 || max_seqlen_q == 0 || q->rows == 0) return VA_OK;
   if (!cu_seqlens_q || !cu_seqlens_k) return VA_ERR_NULL;
@@ -1134,21 +1136,30 @@ extern "C" size_t varlen_attn_splitkv_workspace_bytes(int64_t total_q, int32_t n
 }
 
 extern "C" int varlen_attn_num_splits(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch, int32_t num_heads,
-                                      int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t* num_splits) {
+                                      int32_t num_heads_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t fp8,
+                                      int32_t* num_splits) {
   if (!num_splits) return VA_ERR_NULL;
-  if (!va::supported_dims(head_dim_qk, head_dim_v)) return VA_ERR_HEADDIM;
-  if (batch < 0 || num_heads <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return VA_ERR_ARG;
+  if (!(fp8 ? va::fp8_supported_dims(head_dim_qk, head_dim_v) : va::supported_dims(head_dim_qk, head_dim_v)))
+    return VA_ERR_HEADDIM;
+  if (batch < 0 || num_heads <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || (fp8 != 0 && fp8 != 1))
+    return VA_ERR_ARG;
+  if (num_heads_k <= 0 || num_heads % num_heads_k != 0) return VA_ERR_ARG;
   *num_splits = 1;
   if (batch == 0 || max_seqlen_q == 0 || max_seqlen_k == 0) return VA_OK;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return VA_OK;
-  // The work units a launch has (padding included) against the workgroups
-  // the device holds at once; each split keeps at least 16 key tiles.
-  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, max_seqlen_q, num_heads, num_heads, true);
-  const int64_t units = va::launch_units(batch, num_heads, num_heads, max_seqlen_q, var.block_m, nullptr, nullptr);
-  const int64_t slots = (int64_t)cus * (var.lds_bytes <= 80 * 1024 ? 2 : 1);
+  // The work units the launch has (padding included; packing and grouped
+  // heads as the launch takes them) against the workgroups the device holds
+  // at once; each split keeps at least 16 key tiles of the kernel's width.
+  const va::Variant var =
+      fp8 ? va::fp8_variant(head_dim_qk, head_dim_v,
+                            va::pack_mode(max_seqlen_q, va::wide::kRowsPerWave, num_heads, num_heads_k))
+          : va::variant_for(head_dim_qk, head_dim_v, max_seqlen_q, num_heads, num_heads_k, true);
+  const int64_t units =
+      va::launch_units(batch, num_heads, num_heads_k, max_seqlen_q, var.block_m, nullptr, nullptr);
+  const int64_t slots = (int64_t)cus * var.per_cu;
   const int64_t by_tiles = ((int64_t)max_seqlen_k + 16 * var.block_n - 1) / (16 * var.block_n);
   int64_t s = slots / units;
   s = s < by_tiles ? s : by_tiles;

@@ -56,6 +56,7 @@ extern "C" {
 #define VA_ERR_ALIGN (-5)   /* a pointer or stride breaks the 16-byte alignment rule */
 #define VA_ERR_ARG (-6)     /* a scalar argument is out of range */
 #define VA_ERR_LAUNCH (-7)  /* the HIP kernel launch failed */
+#define VA_ERR_SCRATCH (-8) /* more scratch than varlen_attn_fwd_splitkv_noalloc holds */
 
 /*
  * A packed bf16 tensor [rows, heads, dim] in device memory.  Element (t, h, c)
@@ -173,6 +174,42 @@ int varlen_attn_fwd_splitkv(const va_tensor* q, const va_tensor* k, const va_ten
                             int32_t causal, int32_t window_left, int32_t window_right,
                             const va_tensor* out, float* lse, int32_t num_splits, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* Bytes of the per-GPU scratch array of varlen_attn_fwd_splitkv_noalloc. */
+#define VA_SCRATCH_BYTES (64u << 20)
+
+/*
+ * varlen_attn_fwd_splitkv_noalloc -- varlen_attn_fwd_splitkv for callers
+ * that cannot allocate device memory or pass a workspace (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * The split partials live in a fixed array of VA_SCRATCH_BYTES (64 MiB) in
+ * device memory that the library holds on each GPU it runs on until the
+ * process ends; the call itself allocates nothing.
+ *
+ *   arguments   as for varlen_attn_fwd_splitkv, without the workspace; the
+ *               caller passes inputs and outputs as there
+ *   num_splits  1 .. 128; 1 is exactly varlen_attn_fwd (no scratch used)
+ *
+ * The partials need varlen_attn_splitkv_workspace_bytes(total_q, H, d_v,
+ * num_splits) bytes; a call needing more than VA_SCRATCH_BYTES returns
+ * VA_ERR_SCRATCH and launches nothing.  All calls on one GPU share that
+ * GPU's array: calls that overlap on one GPU (several streams or host
+ * threads at once) race and give undefined results; calls in order on one
+ * stream do not.  The array keeps the last call's contents; nothing needs
+ * clearing (every partial the combine reads is written by the same call).
+ * The first call on a device looks the array up there (a host call that
+ * makes no allocation and no synchronisation).  Returns what
+ * varlen_attn_fwd_splitkv returns, VA_ERR_SCRATCH, or VA_ERR_LAUNCH when no
+ * device is current or the lookup fails.
+ */
+int varlen_attn_fwd_splitkv_noalloc(const va_tensor* q, const va_tensor* k, const va_tensor* v,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                                    int32_t causal, int32_t window_left, int32_t window_right,
+                                    const va_tensor* out, float* lse, int32_t num_splits, void* stream);
+
+/* VA_SCRATCH_BYTES, as the library was built with it.  Host only. */
+size_t varlen_attn_scratch_bytes(void);
 
 /*
  * varlen_attn_fwd_fp8 -- the forward on fp8 e4m3 inputs with descales, and

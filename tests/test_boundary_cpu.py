@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         s = pkg.status_string(code)
         assert isinstance(s, str) and s != "unknown status"
     assert pkg.status_string(12345) == "unknown status"
@@ -452,6 +452,24 @@ def test_splitkv_rejects_bad_arguments():
     t = _t()
     assert B.raw_fwd_splitkv(t, _t(dim=80), t, FAKE, FAKE, 1, 10, 10, 0.125, 0, -1, -1, t, 0, 4, FAKE, 1 << 30,
                              0) == B.VA_ERR_SHAPE
+
+
+def test_noalloc_validation_before_any_device_call():
+    """The allocation-free split-KV entry point runs the plain checks, then
+    rejects partials larger than its scratch array (VA_ERR_SCRATCH), all
+    before any HIP call; one split needs no scratch."""
+    assert pkg.scratch_bytes() == 64 << 20
+    t = _t()
+    call = lambda q, out, splits, batch=1: B.raw_fwd_splitkv_noalloc(
+        q, t, t, FAKE, FAKE, batch, 10, 10, 0.125, 0, -1, -1, out, 0, splits, 0)
+    assert call(t, t, 0) == B.VA_ERR_ARG
+    assert call(t, t, 129) == B.VA_ERR_ARG
+    assert call(_t(dim=80), t, 4) == B.VA_ERR_SHAPE
+    big_q = _t(rows=1 << 16, heads=2, dim=64)
+    big_o = _t(rows=1 << 16, heads=2, dim=64)
+    assert pkg.splitkv_workspace_bytes(1 << 16, 2, 64, 2) > pkg.scratch_bytes()
+    assert call(big_q, big_o, 2) == B.VA_ERR_SCRATCH
+    assert call(big_q, big_o, 2, batch=0) == B.VA_OK  # nothing to launch
 
 
 def test_auto_num_splits():

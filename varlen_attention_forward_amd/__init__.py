@@ -15,11 +15,14 @@ from ._binding import (  # noqa: F401
     raw_fwd,
     raw_fwd_fp8,
     raw_fwd_splitkv,
+    raw_fwd_splitkv_noalloc,
+    scratch_bytes,
     splitkv_workspace_bytes,
     status_string,
     tile_range,
     varlen_attn_fwd,
     varlen_attn_fwd_fp8,
+    varlen_attn_fwd_noalloc,
     varlen_attn_merge,
     work_unit,
 )
@@ -36,6 +39,9 @@ __all__ = [
     "library",
     "raw_fwd",
     "raw_fwd_splitkv",
+    "raw_fwd_splitkv_noalloc",
+    "varlen_attn_fwd_noalloc",
+    "scratch_bytes",
     "splitkv_workspace_bytes",
     "auto_num_splits",
     "VaTensor",

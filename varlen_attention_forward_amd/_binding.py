@@ -18,6 +18,7 @@ VA_ERR_STRIDE = -4
 VA_ERR_ALIGN = -5
 VA_ERR_ARG = -6
 VA_ERR_LAUNCH = -7
+VA_ERR_SCRATCH = -8
 
 STATUS_NAMES = {
     VA_OK: "VA_OK",
@@ -28,6 +29,7 @@ STATUS_NAMES = {
     VA_ERR_ALIGN: "VA_ERR_ALIGN",
     VA_ERR_ARG: "VA_ERR_ARG",
     VA_ERR_LAUNCH: "VA_ERR_LAUNCH",
+    VA_ERR_SCRATCH: "VA_ERR_SCRATCH",
 }
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvarlen_attn.so")
@@ -46,6 +48,8 @@ EXPORTED_SYMBOLS = (
     "varlen_attn_fwd_fp8",
     "varlen_attn_plan_fp8",
     "varlen_attn_fwd_quant_out",
+    "varlen_attn_fwd_splitkv_noalloc",
+    "varlen_attn_scratch_bytes",
 )
 
 
@@ -105,6 +109,11 @@ def library() -> ctypes.CDLL:
     lib.varlen_attn_fwd_splitkv.restype = ctypes.c_int
     lib.varlen_attn_fwd_splitkv.argtypes = lib.varlen_attn_fwd.argtypes[:-1] + [
         ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.varlen_attn_fwd_splitkv_noalloc.restype = ctypes.c_int
+    lib.varlen_attn_fwd_splitkv_noalloc.argtypes = lib.varlen_attn_fwd.argtypes[:-1] + [
+        ctypes.c_int32, ctypes.c_void_p]
+    lib.varlen_attn_scratch_bytes.restype = ctypes.c_size_t
+    lib.varlen_attn_scratch_bytes.argtypes = []
     lib.varlen_attn_fwd_fp8.restype = ctypes.c_int
     lib.varlen_attn_fwd_fp8.argtypes = [
         P(VaTensor), P(VaTensor), P(VaTensor),
@@ -233,6 +242,22 @@ def raw_fwd_splitkv(q: VaTensor, k: VaTensor, v: VaTensor, cu_q_ptr: int, cu_k_p
         ctypes.byref(out), ctypes.c_void_p(lse_ptr), int(num_splits), ctypes.c_void_p(workspace_ptr),
         int(workspace_bytes), ctypes.c_void_p(stream),
     )
+
+
+def raw_fwd_splitkv_noalloc(q: VaTensor, k: VaTensor, v: VaTensor, cu_q_ptr: int, cu_k_ptr: int, batch: int,
+                            max_q: int, max_k: int, scale: float, causal: int, window_left: int,
+                            window_right: int, out: VaTensor, lse_ptr: int, num_splits: int,
+                            stream: int) -> int:
+    return library().varlen_attn_fwd_splitkv_noalloc(
+        ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+        ctypes.c_void_p(cu_q_ptr), ctypes.c_void_p(cu_k_ptr), int(batch),
+        int(max_q), int(max_k), ctypes.c_float(scale), int(causal), int(window_left), int(window_right),
+        ctypes.byref(out), ctypes.c_void_p(lse_ptr), int(num_splits), ctypes.c_void_p(stream))
+
+
+def scratch_bytes() -> int:
+    """Size of the per-GPU scratch array of the allocation-free entry point."""
+    return int(library().varlen_attn_scratch_bytes())
 
 
 def raw_fwd_fp8(q: VaTensor, k: VaTensor, v: VaTensor, q_descale_ptr: int, k_descale_ptr: int,
@@ -379,6 +404,46 @@ def varlen_attn_fwd(
     if return_lse:
         return out, lse
     return out
+
+
+def varlen_attn_fwd_noalloc(
+    q,
+    k,
+    v,
+    cu_seqlens_q,
+    cu_seqlens_k,
+    max_seqlen_q: int,
+    max_seqlen_k: int,
+    out,
+    num_splits: int,
+    lse=None,
+    softmax_scale: Optional[float] = None,
+    causal: bool = False,
+    window_size: Tuple[int, int] = (-1, -1),
+):
+    """Split-KV forward that allocates nothing: the caller passes ``out``
+    (bf16 [total_q, H, d_v]) and, to get the LSE, ``lse`` (fp32 [H,
+    total_q]); the split partials live in the library's fixed per-GPU
+    scratch array (``scratch_bytes()``), which calls that overlap on one GPU
+    share.  ``num_splits`` as for ``varlen_attn_fwd`` but explicit (1 to
+    128).  Returns ``out``, or ``(out, lse)`` when ``lse`` is given."""
+    import torch
+
+    batch = _check_cu(cu_seqlens_q, cu_seqlens_k)
+    H, total_q, d_qk = q.shape[1], q.shape[0], q.shape[2]
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous() or tuple(lse.shape) != (H, total_q):
+            raise ValueError("lse must be a contiguous float32 GPU tensor of shape [H, total_q]")
+    if softmax_scale is None:
+        softmax_scale = d_qk ** -0.5
+    wl, wr = window_size
+    st = raw_fwd_splitkv_noalloc(
+        _desc(q, "q"), _desc(k, "k"), _desc(v, "v"), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), batch,
+        max_seqlen_q, max_seqlen_k, softmax_scale, int(bool(causal)), wl, wr, _desc(out, "out"),
+        lse.data_ptr() if lse is not None else 0, num_splits, torch.cuda.current_stream(q.device).cuda_stream,
+    )
+    _raise_for(st)
+    return out if lse is None else (out, lse)
 
 
 def _check_cu(cu_seqlens_q, cu_seqlens_k) -> int:

@@ -38,6 +38,8 @@
 // "Modifications": softmax.py update_row_max, "fast exp2, rescale
 // threshold") and masking only on the tiles that need it (same section: only
 // unmasked steady-state tiles take the fast path).
+#include <mutex>
+
 #include "attn_common.h"
 
 namespace va {
@@ -909,6 +911,7 @@ extern "C" const char* varlen_attn_status_string(int status) {
     case VA_ERR_ALIGN: return "a data pointer or stride is not a multiple of 16 bytes (lse: 4 bytes)";
     case VA_ERR_ARG: return "a scalar argument is out of range";
     case VA_ERR_LAUNCH: return "the HIP kernel launch failed";
+    case VA_ERR_SCRATCH: return "the split-KV partials need more than the allocation-free entry point's scratch (varlen_attn_scratch_bytes)";
     default: return "unknown status";
   }
 }
@@ -1201,6 +1204,65 @@ extern "C" int varlen_attn_fwd_splitkv(const va_tensor* q, const va_tensor* k, c
   if ((st = va::launch_attention(p, q->dim, v->dim, max_seqlen_q, true, stream)) != VA_OK) return st;
   return va_merge::launch_combine(p.part_o, p.part_lse, num_splits, q->rows, q->heads, v->dim, cu_seqlens_q, batch,
                                   out, lse, stream);
+}
+
+// ----------------------------------------------------------------------------
+// Split-KV without a caller workspace: the fp32 partials live in one
+// file-scope device array per GPU, found once per device with
+// hipGetSymbolAddress (in host code the array's name is only a stand-in for
+// that address).  Calls on one GPU share the array, so calls that overlap on
+// one GPU (concurrent streams, host threads) race; consecutive calls on one
+// stream do not.  The kernels write every partial the combine reads, so
+// nothing is cleared between calls.
+// ----------------------------------------------------------------------------
+namespace va {
+static __device__ __align__(256) char scratch[VA_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mutex;
+static void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once found
+
+// The current device's copy of `scratch` (nullptr: no device, or the lookup
+// failed).
+static void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace va
+
+extern "C" size_t varlen_attn_scratch_bytes(void) { return (size_t)VA_SCRATCH_BYTES; }
+
+extern "C" int varlen_attn_fwd_splitkv_noalloc(const va_tensor* q, const va_tensor* k, const va_tensor* v,
+                                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                               int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                               float softmax_scale, int32_t causal, int32_t window_left,
+                                               int32_t window_right, const va_tensor* out, float* lse,
+                                               int32_t num_splits, void* stream) {
+  if (num_splits < 1 || num_splits > va::kMaxSplits) return VA_ERR_ARG;
+  if (num_splits == 1)
+    return varlen_attn_fwd_splitkv(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k,
+                                   softmax_scale, causal, window_left, window_right, out, lse, 1, nullptr, 0,
+                                   stream);
+  // The argument checks first (they make no HIP call); then the size limit.
+  va::Params p;
+  bool launch = false;
+  const int st = va::prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k,
+                             softmax_scale, causal, window_left, window_right, out, lse, p, launch);
+  if (st != VA_OK || !launch) return st;
+  const size_t need = varlen_attn_splitkv_workspace_bytes(q->rows, q->heads, v->dim, num_splits);
+  if (need > (size_t)VA_SCRATCH_BYTES) return VA_ERR_SCRATCH;
+  void* ws = va::scratch_address();
+  if (ws == nullptr) return VA_ERR_LAUNCH;
+  return varlen_attn_fwd_splitkv(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k,
+                                 softmax_scale, causal, window_left, window_right, out, lse, num_splits, ws,
+                                 (size_t)VA_SCRATCH_BYTES, stream);
 }
 
 extern "C" int varlen_attn_fwd_fp8(const va_tensor* q, const va_tensor* k, const va_tensor* v,

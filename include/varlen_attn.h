@@ -156,6 +156,17 @@ int varlen_attn_fwd_quant_out(const va_tensor* q, const va_tensor* k, const va_t
  *                      attention over its keys, and the combine is exact)
  *   num_splits         1 .. 128; 1 is exactly varlen_attn_fwd (workspace
  *                      unused, may be NULL)
+ *   num_splits_dynamic NULL, or device int32 [batch], 4-byte aligned:
+ *                      per-segment split counts, as FA4's scheduler
+ *                      supplies its combine a num_splits_dynamic_ptr (vLLM
+ *                      docs page, FA4SplitKVCombineKernel).  Segment b's
+ *                      keys are then split into min(max(count_b, 1),
+ *                      num_splits) runs and the combine reads that many
+ *                      partials for its rows; num_splits only bounds them
+ *                      (and sizes the grid and workspace).  The counts are
+ *                      read on the device; varlen_attn_splitkv_counts fills
+ *                      them from cu_seqlens_k.  With counts, short segments
+ *                      are not packed several to a workgroup.
  *   workspace          device memory of at least
  *                      varlen_attn_splitkv_workspace_bytes(total_q, H, d_v,
  *                      num_splits) bytes, 256-byte aligned, owned by the
@@ -166,14 +177,15 @@ int varlen_attn_fwd_quant_out(const va_tensor* q, const va_tensor* k, const va_t
  * and returns; no allocation, no synchronisation, graph-capturable.
  * Returns VA_OK, any varlen_attn_fwd error, VA_ERR_ARG for num_splits out of
  * range or a workspace below the size, VA_ERR_NULL for a NULL workspace,
- * VA_ERR_ALIGN for a misaligned one.
+ * VA_ERR_ALIGN for a misaligned workspace or num_splits_dynamic.
  */
 int varlen_attn_fwd_splitkv(const va_tensor* q, const va_tensor* k, const va_tensor* v,
                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
                             int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
                             int32_t causal, int32_t window_left, int32_t window_right,
-                            const va_tensor* out, float* lse, int32_t num_splits, void* workspace,
-                            size_t workspace_bytes, void* stream);
+                            const va_tensor* out, float* lse, int32_t num_splits,
+                            const int32_t* num_splits_dynamic, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* Bytes of the per-GPU scratch array of varlen_attn_fwd_splitkv_noalloc. */
 #define VA_SCRATCH_BYTES (64u << 20)
@@ -235,7 +247,7 @@ size_t varlen_attn_scratch_bytes(void);
  *   out            bf16 [total_q, H, d_v], or e4m3 when out_scale is given
  *                  (then data and strides multiples of 8 bytes)
  *   out_scale      NULL, or a device fp32 scalar > 0 (not checked)
- *   num_splits, workspace, workspace_bytes
+ *   num_splits, num_splits_dynamic, workspace, workspace_bytes
  *                  as for varlen_attn_fwd_splitkv (1 = no split; with
  *                  splits the combine kernel writes the e4m3 output)
  *   other arguments as for varlen_attn_fwd
@@ -261,8 +273,9 @@ int varlen_attn_fwd_fp8(const va_tensor* q, const va_tensor* k, const va_tensor*
                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
                         int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale, int32_t causal,
                         int32_t window_left, int32_t window_right, const va_tensor* out,
-                        const float* out_scale, float* lse, int32_t num_splits, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                        const float* out_scale, float* lse, int32_t num_splits,
+                        const int32_t* num_splits_dynamic, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* Workspace bytes varlen_attn_fwd_splitkv needs (0 for num_splits <= 1). Host only. */
 size_t varlen_attn_splitkv_workspace_bytes(int64_t total_q, int32_t num_heads, int32_t head_dim_v,
@@ -283,6 +296,21 @@ size_t varlen_attn_splitkv_workspace_bytes(int64_t total_q, int32_t num_heads, i
 int varlen_attn_num_splits(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch, int32_t num_heads,
                            int32_t num_heads_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t fp8,
                            int32_t* num_splits);
+
+/*
+ * varlen_attn_splitkv_counts -- per-segment split counts on the device, for
+ * varlen_attn_fwd_splitkv's num_splits_dynamic: count_b = min(max(ceil(Lk_b
+ * / keys_per_split), 1), max_splits) with Lk_b = cu_seqlens_k[b + 1] -
+ * cu_seqlens_k[b], so each split gets at least keys_per_split keys where
+ * the segment has them (FA4's automatic choice keeps splits similarly
+ * long).  Enqueues one small kernel on `stream` (no host read of
+ * cu_seqlens, no allocation); `num_splits_dynamic` is device int32 [batch],
+ * owned by the caller.  Returns VA_OK (batch == 0: nothing launched),
+ * VA_ERR_ARG for batch < 0, max_splits outside 1 .. 128 or keys_per_split
+ * < 1, VA_ERR_NULL, VA_ERR_ALIGN (pointers 4-byte aligned) or VA_ERR_LAUNCH.
+ */
+int varlen_attn_splitkv_counts(const int32_t* cu_seqlens_k, int32_t batch, int32_t max_splits,
+                               int32_t keys_per_split, int32_t* num_splits_dynamic, void* stream);
 
 /*
  * varlen_attn_merge -- merge two attention results over disjoint key sets of

@@ -625,3 +625,56 @@ def test_plan_fp8(dims, lds_kib):
     assert p8["lds_bytes"] // 1024 == lds_kib and p8["lds_bytes"] <= 160 * 1024
     with pytest.raises(ValueError):
         pkg.plan(80, 80, 1, 16, 64, 64, 0, fp8=True)  # d 80 has no fp8 instantiation
+
+
+def _fastdiv(d):
+    """The multiplier and shift the kernel's FastDiv uses (tile_schedule.h)."""
+    s = 0
+    while (1 << s) < d:
+        s += 1
+    m = ((1 << (32 + s)) + d - 1) // d
+    return m - (1 << 32), s
+
+
+@pytest.mark.parametrize("d", list(range(1, 300)) + [511, 512, 513, 1000, 4095, 4096, 65535, 65536, 65537,
+                                                         (1 << 20) + 3, (1 << 30) + 1, (1 << 31) - 1])
+def test_fastdiv_is_exact(d):
+    """floor(n / d) = (umulhi(n, mul) + n) >> shift for every numerator the
+    kernel divides (0 <= n < 2^31): checked at the divisor's multiples and
+    their neighbours, the top of the range and random numerators."""
+    mul, s = _fastdiv(d)
+    assert 0 <= mul < (1 << 32)
+    rng = random.Random(d)
+    ns = {0, 1, (1 << 31) - 1, (1 << 31) - 2}
+    for q in list(range(0, 70)) + [((1 << 31) - 1) // d - i for i in range(3)] + [rng.randrange(0, (1 << 31) // d)
+                                                                                  for _ in range(50)]:
+        for r in (-1, 0, 1, d - 1):
+            n = q * d + r
+            if 0 <= n < (1 << 31):
+                ns.add(n)
+    ns.update(rng.randrange(0, 1 << 31) for _ in range(200))
+    for n in ns:
+        t = (n * mul) >> 32
+        assert t + n < (1 << 32)
+        assert (t + n) >> s == n // d, (n, d)
+
+
+def test_dynamic_split_counts_validation():
+    """Per-segment split counts: a misaligned counts pointer is refused by
+    the split-KV entry points, and the device count helper checks its
+    arguments before launching anything (batch 0 launches nothing)."""
+    t = _t()
+    assert B.raw_fwd_splitkv(t, t, t, FAKE, FAKE, 1, 10, 10, 0.125, 0, -1, -1, t, 0, 4, FAKE, 1 << 30, 0,
+                             splits_dyn_ptr=FAKE + 2) == B.VA_ERR_ALIGN
+    lib = pkg.library()
+    counts = lambda cu, batch, mx, kps, out: lib.varlen_attn_splitkv_counts(
+        ctypes.c_void_p(cu), batch, mx, kps, ctypes.c_void_p(out), None)
+    assert counts(FAKE, -1, 4, 512, FAKE) == B.VA_ERR_ARG
+    assert counts(FAKE, 3, 0, 512, FAKE) == B.VA_ERR_ARG
+    assert counts(FAKE, 3, 129, 512, FAKE) == B.VA_ERR_ARG
+    assert counts(FAKE, 3, 4, 0, FAKE) == B.VA_ERR_ARG
+    assert counts(0, 3, 4, 512, FAKE) == B.VA_ERR_NULL
+    assert counts(FAKE, 3, 4, 512, 0) == B.VA_ERR_NULL
+    assert counts(FAKE + 2, 3, 4, 512, FAKE) == B.VA_ERR_ALIGN
+    assert counts(FAKE, 3, 4, 512, FAKE + 1) == B.VA_ERR_ALIGN
+    assert counts(0, 0, 4, 512, 0) == B.VA_OK

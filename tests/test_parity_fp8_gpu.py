@@ -431,3 +431,19 @@ def test_fp8_score_error_single_key(dims, std):
     print("fp8 %s std %g: max |dLSE| %.3e, max (|dLSE| - fp32 rounding) / (scale sum|q k|) %.3e (2^-15 = %.3e)" % (
         dims, std, float(err.max()), ratio, 2.0 ** -15))
     assert np.all(err <= bound), "score error above 2^-15 scale sum|q k| by up to %.3e" % float(np.max(err - bound))
+
+
+@pytest.mark.parametrize("dims", DIMS, ids=lambda d: "d%d_%d" % d)
+def test_fp8_split_kv_dynamic_counts(dims):
+    """fp8 inputs with per-segment split counts (explicit and the library's)
+    against the oracle, within the element-wise bound."""
+    inp = make([1, 64, 300, 17], [3000, 64, 1200, 900], dims, seed=dims[0] + 77, mode="causal")
+    d = inp.to(DEV)
+    for counts in ([3, 1, 0, 9], "auto"):
+        dyn = counts if isinstance(counts, str) else torch.tensor(counts, dtype=torch.int32, device=DEV)
+        out, lse = va.varlen_attn_fwd_fp8(
+            d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, inp.max_seqlen_q, inp.max_seqlen_k, causal=True,
+            q_descale=d.q_descale, k_descale=d.k_descale, v_descale=d.v_descale, return_lse=True, num_splits=6,
+            num_splits_dynamic=dyn)
+        torch.cuda.synchronize()
+        assert_fp8_parity(inp, out, lse, what="fp8 dyn %s %s" % (dims, counts))

@@ -695,3 +695,62 @@ def test_quantised_output_default_allocation_d72():
     got = oracle.e4m3_decode(out.cpu().view(torch.uint8).numpy()) * 0.01
     tol = 2e-2 + 0.01 * np.maximum(2.0 ** -4 * (np.abs(ref_o) + 2e-2) / 0.01, 2.0 ** -10)
     assert np.all(np.abs(got - ref_o) <= tol)
+
+
+def _host_counts(lk, max_splits, keys_per_split):
+    return [min(max(-(-x // keys_per_split), 1), max_splits) for x in lk]
+
+
+def test_splitkv_counts_kernel():
+    """varlen_attn_splitkv_counts against the formula it documents."""
+    lk = [0, 1, 511, 512, 513, 4096, 70000, 33, 100000]
+    cu = workloads.cu_seqlens(lk).to(DEV)
+    for mx, kps in ((8, 512), (128, 512), (3, 1000), (1, 512)):
+        got = va.splitkv_counts(cu, mx, kps).cpu().tolist()
+        assert got == _host_counts(lk, mx, kps), (mx, kps, got)
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (80, 80), (192, 128)], ids=lambda d: "d%d_%d" % d)
+@pytest.mark.parametrize("mode", ["full", "causal", "window"])
+def test_split_kv_dynamic_counts(dims, mode):
+    """Per-segment split counts (num_splits_dynamic): explicit counts with
+    zero, one, more than num_splits and in between, and the library's own
+    ("auto"), on segments of very different key lengths (short queries
+    that the plain launch would pack several to a workgroup, and long
+    ones), against the oracle; counts all equal to num_splits give the
+    static split call bit for bit."""
+    causal, window = MODES[mode]
+    lq, lk = [1, 64, 17, 300, 40], [3000, 64, 900, 1200, 0]
+    S = 6
+    seed = zlib.crc32(repr(("dyn", dims, mode)).encode()) % 1000
+    inp = workloads.make_inputs(lq, lk, 3, dims[0], dims[1], seed=seed, causal=causal, window=window)
+    ref_o, ref_lse = oracle_on(inp)
+    d = inp.to(DEV)
+    args = (d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, inp.max_seqlen_q, inp.max_seqlen_k)
+    kw = dict(softmax_scale=inp.softmax_scale, causal=causal, window_size=window, return_lse=True, num_splits=S)
+    for counts in ([0, 1, 9, 3, 2], [S] * 5, "auto"):
+        dyn = counts if isinstance(counts, str) else torch.tensor(counts, dtype=torch.int32, device=DEV)
+        out, lse = va.varlen_attn_fwd(*args, num_splits_dynamic=dyn, **kw)
+        torch.cuda.synchronize()
+        assert_parity(out, lse, ref_o, ref_lse, what="dyn %s %s %s" % (dims, mode, counts))
+        if counts == [S] * 5:
+            o2, l2 = va.varlen_attn_fwd(*args, **kw)
+            torch.cuda.synchronize()
+            assert torch.equal(out, o2) and torch.equal(lse, l2)
+
+
+@pytest.mark.parametrize("dims", [(80, 80), (128, 128)], ids=lambda d: "d%d_%d" % d)
+def test_split_kv_dynamic_counts_short_queries(dims):
+    """Every segment at most 64 queries, so the plain launch would pack four
+    segments to a workgroup; with per-segment counts each workgroup holds one
+    segment.  Against the oracle, causal (bottom-right, q < k)."""
+    lq, lk = [64, 1, 30, 64, 7, 64], [2000, 64, 700, 5000, 7, 64]
+    inp = workloads.make_inputs(lq, lk, 4, dims[0], dims[1], seed=dims[0] + 5, causal=True)
+    ref_o, ref_lse = oracle_on(inp)
+    d = inp.to(DEV)
+    for counts in ([4, 1, 2, 8, 1, 1], "auto"):
+        dyn = counts if isinstance(counts, str) else torch.tensor(counts, dtype=torch.int32, device=DEV)
+        out, lse = va.varlen_attn_fwd(d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, 64, 5000, causal=True,
+                                      return_lse=True, num_splits=8, num_splits_dynamic=dyn)
+        torch.cuda.synchronize()
+        assert_parity(out, lse, ref_o, ref_lse, what="dyn short %s %s" % (dims, counts))

@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     raw_fwd_splitkv,
     raw_fwd_splitkv_noalloc,
     scratch_bytes,
+    splitkv_counts,
     splitkv_workspace_bytes,
     status_string,
     tile_range,
@@ -43,6 +44,7 @@ __all__ = [
     "varlen_attn_fwd_noalloc",
     "scratch_bytes",
     "splitkv_workspace_bytes",
+    "splitkv_counts",
     "auto_num_splits",
     "VaTensor",
     "VarlenAttnError",

@@ -50,6 +50,7 @@ EXPORTED_SYMBOLS = (
     "varlen_attn_fwd_quant_out",
     "varlen_attn_fwd_splitkv_noalloc",
     "varlen_attn_scratch_bytes",
+    "varlen_attn_splitkv_counts",
 )
 
 
@@ -108,7 +109,10 @@ def library() -> ctypes.CDLL:
     ]
     lib.varlen_attn_fwd_splitkv.restype = ctypes.c_int
     lib.varlen_attn_fwd_splitkv.argtypes = lib.varlen_attn_fwd.argtypes[:-1] + [
-        ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.varlen_attn_splitkv_counts.restype = ctypes.c_int
+    lib.varlen_attn_splitkv_counts.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_void_p, ctypes.c_void_p]
     lib.varlen_attn_fwd_splitkv_noalloc.restype = ctypes.c_int
     lib.varlen_attn_fwd_splitkv_noalloc.argtypes = lib.varlen_attn_fwd.argtypes[:-1] + [
         ctypes.c_int32, ctypes.c_void_p]
@@ -121,7 +125,7 @@ def library() -> ctypes.CDLL:
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, P(VaTensor),
-        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_size_t, ctypes.c_void_p,
     ]
     lib.varlen_attn_fwd_quant_out.restype = ctypes.c_int
@@ -232,16 +236,32 @@ def raw_fwd(q: VaTensor, k: VaTensor, v: VaTensor, cu_q_ptr: int, cu_k_ptr: int,
 def raw_fwd_splitkv(q: VaTensor, k: VaTensor, v: VaTensor, cu_q_ptr: int, cu_k_ptr: int, batch: int,
                     max_seqlen_q: int, max_seqlen_k: int, softmax_scale: float, causal: int,
                     window_left: int, window_right: int, out: VaTensor, lse_ptr: int, num_splits: int,
-                    workspace_ptr: int, workspace_bytes: int, stream: int) -> int:
+                    workspace_ptr: int, workspace_bytes: int, stream: int, splits_dyn_ptr: int = 0) -> int:
     """The split-KV C entry point with plain descriptors; returns the status code."""
     return library().varlen_attn_fwd_splitkv(
         ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
         ctypes.c_void_p(cu_q_ptr), ctypes.c_void_p(cu_k_ptr), int(batch),
         int(max_seqlen_q), int(max_seqlen_k), float(softmax_scale),
         int(causal), int(window_left), int(window_right),
-        ctypes.byref(out), ctypes.c_void_p(lse_ptr), int(num_splits), ctypes.c_void_p(workspace_ptr),
-        int(workspace_bytes), ctypes.c_void_p(stream),
+        ctypes.byref(out), ctypes.c_void_p(lse_ptr), int(num_splits), ctypes.c_void_p(splits_dyn_ptr),
+        ctypes.c_void_p(workspace_ptr), int(workspace_bytes), ctypes.c_void_p(stream),
     )
+
+
+def splitkv_counts(cu_seqlens_k, max_splits: int, keys_per_split: int, out=None):
+    """Per-segment split counts computed on the device from ``cu_seqlens_k``
+    (varlen_attn_splitkv_counts): an int32 GPU tensor [batch]."""
+    import torch
+
+    batch = cu_seqlens_k.numel() - 1
+    if out is None:
+        out = torch.empty(max(batch, 0), dtype=torch.int32, device=cu_seqlens_k.device)
+    st = library().varlen_attn_splitkv_counts(
+        ctypes.c_void_p(cu_seqlens_k.data_ptr()), int(batch), int(max_splits), int(keys_per_split),
+        ctypes.c_void_p(out.data_ptr() if batch > 0 else 0),
+        ctypes.c_void_p(torch.cuda.current_stream(cu_seqlens_k.device).cuda_stream))
+    _raise_for(st)
+    return out
 
 
 def raw_fwd_splitkv_noalloc(q: VaTensor, k: VaTensor, v: VaTensor, cu_q_ptr: int, cu_k_ptr: int, batch: int,
@@ -264,7 +284,7 @@ def raw_fwd_fp8(q: VaTensor, k: VaTensor, v: VaTensor, q_descale_ptr: int, k_des
                 v_descale_ptr: int, cu_q_ptr: int, cu_k_ptr: int, batch: int, max_seqlen_q: int,
                 max_seqlen_k: int, softmax_scale: float, causal: int, window_left: int, window_right: int,
                 out: VaTensor, out_scale_ptr: int, lse_ptr: int, num_splits: int, workspace_ptr: int,
-                workspace_bytes: int, stream: int) -> int:
+                workspace_bytes: int, stream: int, splits_dyn_ptr: int = 0) -> int:
     """The fp8 C entry point with plain descriptors; returns the status code."""
     return library().varlen_attn_fwd_fp8(
         ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
@@ -273,7 +293,7 @@ def raw_fwd_fp8(q: VaTensor, k: VaTensor, v: VaTensor, q_descale_ptr: int, k_des
         int(max_seqlen_q), int(max_seqlen_k), float(softmax_scale),
         int(causal), int(window_left), int(window_right),
         ctypes.byref(out), ctypes.c_void_p(out_scale_ptr), ctypes.c_void_p(lse_ptr), int(num_splits),
-        ctypes.c_void_p(workspace_ptr), int(workspace_bytes), ctypes.c_void_p(stream),
+        ctypes.c_void_p(splits_dyn_ptr), ctypes.c_void_p(workspace_ptr), int(workspace_bytes), ctypes.c_void_p(stream),
     )
 
 
@@ -330,6 +350,7 @@ def varlen_attn_fwd(
     lse=None,
     num_splits: int = 1,
     out_scale=None,
+    num_splits_dynamic=None,
 ):
     """Fused varlen attention forward on the current HIP stream.
 
@@ -342,6 +363,11 @@ def varlen_attn_fwd(
     ``num_splits`` splits every work unit's keys into that many runs (split-KV,
     combined at the end; the workspace is allocated here with torch); 0 lets
     the library choose (1 when the call already fills the GPU).
+    ``num_splits_dynamic`` (with num_splits > 1): per-segment split counts,
+    an int32 GPU tensor [batch], or ``"auto"`` to have the library compute
+    them on the device from ``cu_seqlens_k`` (one split per 16 key tiles, at
+    most num_splits); segment b's keys then take min(count_b, num_splits)
+    runs.
     ``out_scale`` (a one-element fp32 GPU tensor) makes ``out`` e4m3 codes
     of O / out_scale (``torch.float8_e4m3fn``; no split-KV).
     """
@@ -393,12 +419,15 @@ def varlen_attn_fwd(
     else:
         nbytes = splitkv_workspace_bytes(total_q, H, d_v, num_splits)
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+        dyn = _split_counts(num_splits_dynamic, cu_seqlens_k, batch, num_splits,
+                            plan(d_qk, d_v, batch, H, max_seqlen_q, max_seqlen_k, causal,
+                                 num_heads_k=k.shape[1])["block_n"])
         st = raw_fwd_splitkv(
             _desc(q, "q"), _desc(k, "k"), _desc(v, "v"),
             cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), batch,
             max_seqlen_q, max_seqlen_k, softmax_scale, int(bool(causal)), wl, wr,
             _desc(out, "out"), lse.data_ptr() if lse is not None else 0, num_splits,
-            ws.data_ptr(), nbytes, stream,
+            ws.data_ptr(), nbytes, stream, splits_dyn_ptr=0 if dyn is None else dyn.data_ptr(),
         )
     _raise_for(st)
     if return_lse:
@@ -446,6 +475,24 @@ def varlen_attn_fwd_noalloc(
     return out if lse is None else (out, lse)
 
 
+def _split_counts(spec, cu_seqlens_k, batch: int, num_splits: int, block_n: int):
+    """The per-segment split counts tensor for ``num_splits_dynamic``: None,
+    the caller's int32 GPU tensor [batch] (checked), or ``"auto"``: computed
+    on the device, one split per 16 key tiles of block_n keys."""
+    import torch
+
+    if spec is None:
+        return None
+    if isinstance(spec, str):
+        if spec != "auto":
+            raise ValueError("num_splits_dynamic must be None, 'auto' or an int32 GPU tensor")
+        return splitkv_counts(cu_seqlens_k, num_splits, 16 * block_n)
+    if (not isinstance(spec, torch.Tensor) or spec.dtype != torch.int32 or not spec.is_cuda
+            or not spec.is_contiguous() or spec.numel() != batch):
+        raise ValueError("num_splits_dynamic must be a contiguous int32 GPU tensor of batch entries")
+    return spec
+
+
 def _check_cu(cu_seqlens_q, cu_seqlens_k) -> int:
     import torch
 
@@ -490,6 +537,7 @@ def varlen_attn_fwd_fp8(
     return_lse: bool = False,
     lse=None,
     num_splits: int = 1,
+    num_splits_dynamic=None,
 ):
     """Varlen attention forward on fp8 e4m3 inputs, on the current HIP stream.
 
@@ -498,7 +546,7 @@ def varlen_attn_fwd_fp8(
     [batch, H_kv] GPU tensors (None: ones) multiply the decoded values of
     segment b and KV head hk.  ``out_scale`` (a one-element fp32 GPU tensor)
     makes ``out`` e4m3 codes of O / out_scale; else ``out`` is bf16.
-    ``num_splits`` as for ``varlen_attn_fwd`` (bf16 output only).
+    ``num_splits`` and ``num_splits_dynamic`` as for ``varlen_attn_fwd``.
     """
     import torch
 
@@ -519,11 +567,14 @@ def varlen_attn_fwd_fp8(
     stream = torch.cuda.current_stream(q.device).cuda_stream
     if num_splits == 0:
         num_splits = auto_num_splits(d_qk, d_v, batch, H, max_seqlen_q, max_seqlen_k, num_heads_k=H_kv, fp8=True)
-    nbytes, ws_ptr = 0, 0
+    nbytes, ws_ptr, dyn = 0, 0, None
     if num_splits > 1:
         nbytes = splitkv_workspace_bytes(total_q, H, d_v, num_splits)
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
         ws_ptr = ws.data_ptr()
+        dyn = _split_counts(num_splits_dynamic, cu_seqlens_k, batch, num_splits,
+                            plan(d_qk, d_v, batch, H, max_seqlen_q, max_seqlen_k, causal, fp8=True,
+                                 num_heads_k=H_kv)["block_n"])
     f8 = torch.float8_e4m3fn
     st = raw_fwd_fp8(
         _desc(q, "q", f8), _desc(k, "k", f8), _desc(v, "v", f8),
@@ -533,6 +584,7 @@ def varlen_attn_fwd_fp8(
         max_seqlen_q, max_seqlen_k, softmax_scale, int(bool(causal)), wl, wr,
         _desc(out, "out", out_dtype), _f32_ptr(out_scale, "out_scale", 1),
         lse.data_ptr() if lse is not None else 0, num_splits, ws_ptr, nbytes, stream,
+        splits_dyn_ptr=0 if dyn is None else dyn.data_ptr(),
     )
     _raise_for(st)
     if return_lse:

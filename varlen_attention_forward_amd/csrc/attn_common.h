@@ -48,7 +48,18 @@ struct Params {
   // each unit's key tiles and writes a normalised fp32 partial O and its
   // LSE instead of out / lse (combined by combine_splits).
   int32_t num_splits, n_units;
+  // Optional per-segment split counts [batch] (device; null: num_splits for
+  // every segment).  Only with launches of one segment per workgroup.
+  const int32_t* splits_dyn;
   int32_t pack;  // segments, or query heads, per workgroup (segments_per_block): 1, 2 or 4
+  int32_t pack_shift;  // log2(pack)
+  // Work-unit decode, set up on the host: the head count the dealing runs
+  // over (query heads, or groups of pack query heads of one KV head), the
+  // q-tiles per (segment, head) group, the KV heads, and the query heads
+  // per KV head, as FastDivs; the segment count the dealing runs over
+  // (groups of pack segments when packed); the group size query_head takes.
+  FastDiv fd_heads, fd_nqt, fd_heads_k, fd_group;
+  int32_t n_dealt, qh_group;
   float* part_o;    // [num_splits, total_q, heads, d_v]
   float* part_lse;  // [num_splits, heads, total_q]
   int32_t causal, wl, wr;
@@ -126,9 +137,8 @@ __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int b
     // (segment, group of pack query heads of one KV head): the group index
     // takes the place of the head in the dealing, and query_head keeps a KV
     // head's groups on one XCD; r.u.h is the group's first query head.
-    const uint32_t vheads = (uint32_t)(p.heads / p.pack);
-    r.u = decode_block((uint32_t)w, (uint32_t)p.batch, vheads, 1u, p.causal);
-    r.u.h = query_head(r.u.h, (int)vheads, p.heads_k) * p.pack;
+    r.u = decode_block((uint32_t)w, (uint32_t)p.n_dealt, p.fd_heads, p.fd_nqt, p.causal);
+    r.u.h = query_head(r.u.h, p.fd_heads_k, p.qh_group) << p.pack_shift;
     if (r.u.valid) {
       r.q0 = p.cu_q[r.u.b];
       r.lq = p.cu_q[r.u.b + 1] - r.q0;
@@ -138,11 +148,10 @@ __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int b
     return r;
   }
   if constexpr (PK == kPackSegments) {  // a group of pack short segments: one unit per (group, head), in packing order
-    const uint32_t groups = ((uint32_t)p.batch + (uint32_t)p.pack - 1u) / (uint32_t)p.pack;
-    r.u = decode_block((uint32_t)w, groups, (uint32_t)p.heads, 1u, p.causal);
-    r.u.h = query_head(r.u.h, p.heads, p.heads_k);
+    r.u = decode_block((uint32_t)w, (uint32_t)p.n_dealt, p.fd_heads, p.fd_nqt, p.causal);
+    r.u.h = query_head(r.u.h, p.fd_heads_k, p.qh_group);
     if (r.u.valid) {
-      const int first = r.u.b * p.pack, last = min(first + p.pack, p.batch);
+      const int first = r.u.b << p.pack_shift, last = min(first + p.pack, p.batch);
       r.q0 = p.cu_q[first];
       r.lq = p.cu_q[last] - r.q0;
       r.k0 = p.cu_k[first];
@@ -183,12 +192,12 @@ __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int b
         const int nq = __builtin_amdgcn_readlane(nqt, i);
         const int qi = local % nq;
         r.u.b = i;
-        r.u.h = query_head(__builtin_amdgcn_readlane(h0, i) + 8 * (local / nq), p.heads, p.heads_k);
+        r.u.h = query_head(__builtin_amdgcn_readlane(h0, i) + 8 * (local / nq), p.fd_heads_k, p.qh_group);
         r.u.qt = p.causal ? nq - 1 - qi : qi;
       }
     } else {
-      r.u = decode_block((uint32_t)w, (uint32_t)p.batch, (uint32_t)p.heads, (uint32_t)p.n_qt, p.causal);
-      r.u.h = query_head(r.u.h, p.heads, p.heads_k);
+      r.u = decode_block((uint32_t)w, (uint32_t)p.n_dealt, p.fd_heads, p.fd_nqt, p.causal);
+      r.u.h = query_head(r.u.h, p.fd_heads_k, p.qh_group);
     }
     if (r.u.valid) {
       const int b = __builtin_amdgcn_readfirstlane(r.u.b);
@@ -199,8 +208,8 @@ __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int b
     }
     return r;
   }
-  r.u = decode_block((uint32_t)w, (uint32_t)p.batch, (uint32_t)p.heads, (uint32_t)p.n_qt, p.causal);
-  r.u.h = query_head(r.u.h, p.heads, p.heads_k);
+  r.u = decode_block((uint32_t)w, (uint32_t)p.n_dealt, p.fd_heads, p.fd_nqt, p.causal);
+  r.u.h = query_head(r.u.h, p.fd_heads_k, p.qh_group);
   if (r.u.valid) {
     const int b = __builtin_amdgcn_readfirstlane(r.u.b);
     r.q0 = p.cu_q[b];

@@ -129,6 +129,9 @@ struct CombineParams {
   int32_t heads, dim, splits, batch;
   int32_t lane_shift;
   const float* out_scale;  // null: bf16 out; else e4m3 out (o holds bytes)
+  // Per-segment split counts [batch] (null: `splits` for every row): the
+  // rows of segment b combine the first min(max(count, 1), splits) partials.
+  const int32_t* splits_dyn;
 };
 
 __global__ __launch_bounds__(256) void combine_splits(CombineParams p) {
@@ -141,17 +144,27 @@ __global__ __launch_bounds__(256) void combine_splits(CombineParams p) {
   const int64_t i = pair / p.heads;
   const int h = (int)(pair - i * p.heads);
   if (i < p.cu_q[0] || i >= p.cu_q[p.batch]) return;
+  int splits = p.splits;
+  if (p.splits_dyn != nullptr) {
+    // the row's segment: the last b with cu_q[b] <= i (binary search)
+    int lo = 0, hi = p.batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.cu_q[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    splits = min(max(p.splits_dyn[lo], 1), p.splits);
+  }
   const int64_t plane = p.rows * p.heads;  // (row, head) pairs per split
   float m = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) m = fmaxf(m, p.part_lse[(int64_t)s * plane + (int64_t)h * p.rows + i]);
+  for (int s = 0; s < splits; ++s) m = fmaxf(m, p.part_lse[(int64_t)s * plane + (int64_t)h * p.rows + i]);
   float sum = 0.f;
   if (m != -INFINITY)
-    for (int s = 0; s < p.splits; ++s) sum += expf(p.part_lse[(int64_t)s * plane + (int64_t)h * p.rows + i] - m);
+    for (int s = 0; s < splits; ++s) sum += expf(p.part_lse[(int64_t)s * plane + (int64_t)h * p.rows + i] - m);
   if (4 * c < p.dim) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (m != -INFINITY) {
       const float inv = 1.f / sum;
-      for (int s = 0; s < p.splits; ++s) {
+      for (int s = 0; s < splits; ++s) {
         const float w = expf(p.part_lse[(int64_t)s * plane + (int64_t)h * p.rows + i] - m) * inv;
         // A split with weight 0 (no key, or negligible) is skipped, not
         // scaled: its O is never read into the sum.
@@ -175,9 +188,10 @@ __global__ __launch_bounds__(256) void combine_splits(CombineParams p) {
 
 int launch_combine(const float* part_o, const float* part_lse, int32_t num_splits, int64_t total_q, int32_t heads,
                    int32_t dim, const int32_t* cu_seqlens_q, int32_t batch, const va_tensor* out, float* lse,
-                   void* stream, const float* out_scale) {
+                   void* stream, const float* out_scale, const int32_t* splits_dyn) {
   CombineParams p;
   p.out_scale = out_scale;
+  p.splits_dyn = splits_dyn;
   p.part_o = part_o;
   p.part_lse = part_lse;
   p.o = (uint16_t*)out->data;
@@ -199,6 +213,18 @@ int launch_combine(const float* part_o, const float* part_lse, int32_t num_split
   const hipError_t err =
       hipLaunchKernel((const void*)&combine_splits, dim3((unsigned)grid), dim3(256), args, 0, (hipStream_t)stream);
   return err == hipSuccess ? VA_OK : VA_ERR_LAUNCH;
+}
+
+// Per-segment split counts for split-KV, on the device from cu_seqlens_k:
+// count_b = min(max(ceil(Lk_b / keys_per_split), 1), max_splits), so a
+// segment gets one split per keys_per_split keys (short segments one).
+__global__ __launch_bounds__(256) void splitkv_counts(const int32_t* cu_k, int32_t batch, int32_t max_splits,
+                                                      int32_t keys_per_split, int32_t* counts) {
+  const int b = (int)(blockIdx.x * 256 + threadIdx.x);
+  if (b >= batch) return;
+  const int64_t lk = (int64_t)cu_k[b + 1] - cu_k[b];
+  const int64_t n = (lk + keys_per_split - 1) / keys_per_split;
+  counts[b] = (int32_t)(n < 1 ? 1 : (n > max_splits ? max_splits : n));
 }
 
 static int check(const va_tensor* t, int64_t rows, int32_t heads, int32_t dim) {
@@ -253,5 +279,17 @@ extern "C" int varlen_attn_merge(const va_tensor* out_a, const float* lse_a, con
   void* args[] = {&p};
   const hipError_t err =
       hipLaunchKernel((const void*)&merge_states, dim3((unsigned)grid), dim3(256), args, 0, (hipStream_t)stream);
+  return err == hipSuccess ? VA_OK : VA_ERR_LAUNCH;
+}
+
+extern "C" int varlen_attn_splitkv_counts(const int32_t* cu_seqlens_k, int32_t batch, int32_t max_splits,
+                                          int32_t keys_per_split, int32_t* num_splits_dynamic, void* stream) {
+  if (batch < 0 || max_splits < 1 || max_splits > 128 || keys_per_split < 1) return VA_ERR_ARG;
+  if (batch == 0) return VA_OK;
+  if (!cu_seqlens_k || !num_splits_dynamic) return VA_ERR_NULL;
+  if (((uintptr_t)cu_seqlens_k & 3u) != 0 || ((uintptr_t)num_splits_dynamic & 3u) != 0) return VA_ERR_ALIGN;
+  void* args[] = {(void*)&cu_seqlens_k, &batch, &max_splits, &keys_per_split, &num_splits_dynamic};
+  const hipError_t err = hipLaunchKernel((const void*)&va_merge::splitkv_counts, dim3((unsigned)((batch + 255) / 256)),
+                                         dim3(256), args, 0, (hipStream_t)stream);
   return err == hipSuccess ? VA_OK : VA_ERR_LAUNCH;
 }

@@ -24,6 +24,35 @@
 
 namespace va {
 
+// Division by a run-time constant without a divide: q = floor(n / d) for
+// 0 <= n < 2^31 as (umulhi(n, mul) + n) >> shift, with 2^shift >= d and
+// 2^32 + mul = ceil(2^(32 + shift) / d).  (Exact: writing
+// (2^32 + mul) d = 2^(32 + shift) + e with 0 <= e < d <= 2^shift, the
+// product n (2^32 + mul) / 2^(32 + shift) exceeds n / d by n e / (d 2^(32 +
+// shift)) < 1 / d, too little to reach the next integer; n < 2^31 keeps
+// umulhi(n, mul) + n below 2^32.)  The host computes the multipliers once
+// per launch; the kernel's work-unit decode then costs a multiply and a
+// shift per division instead of a division routine.
+struct FastDiv {
+  uint32_t d, mul, shift;
+};
+
+VA_HD FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  uint32_t s = 0;
+  while (((uint64_t)1 << s) < (uint64_t)d) ++s;
+  const uint64_t m = (((uint64_t)1 << (32 + s)) + d - 1) / d;
+  f.d = d;
+  f.mul = (uint32_t)(m - ((uint64_t)1 << 32));
+  f.shift = s;
+  return f;
+}
+
+VA_HD uint32_t fdiv(uint32_t n, FastDiv f) {
+  const uint32_t t = (uint32_t)(((uint64_t)n * f.mul) >> 32);
+  return (t + n) >> f.shift;
+}
+
 struct RowBounds {
   int64_t lo;
   int64_t hi;
@@ -168,19 +197,20 @@ VA_HD uint32_t snake_quads(uint32_t k, uint32_t k_count) {
   return ((k >> 2) & 1u) && (k | 3u) < k_count ? k ^ 3u : k;
 }
 
-// 32-bit arithmetic: the launch checks that the grid fits in int32.
-VA_HD WorkUnit decode_block(uint32_t w, uint32_t batch, uint32_t heads, uint32_t n_qt, int causal) {
-  const uint32_t groups = batch * heads;
+// 32-bit arithmetic: the launch checks that the grid fits in int32.  `heads`
+// and `n_qt` are the dealt head count and q-tiles per group as FastDivs.
+VA_HD WorkUnit decode_block(uint32_t w, uint32_t batch, FastDiv heads, FastDiv n_qt, int causal) {
+  const uint32_t groups = batch * heads.d;
   const uint32_t x = w & 7u;
-  const uint32_t k = snake_quads(w >> 3, (groups + 7u) / 8u * n_qt);
-  const uint32_t gl = k / n_qt, qi = k - gl * n_qt;
+  const uint32_t k = snake_quads(w >> 3, (groups + 7u) / 8u * n_qt.d);
+  const uint32_t gl = fdiv(k, n_qt), qi = k - gl * n_qt.d;
   const uint32_t g = gl * 8u + x;
   WorkUnit u;
   u.valid = g < groups;
-  u.b = (int32_t)(g / heads);
-  u.h = (int32_t)(g - (uint32_t)u.b * heads);
+  u.b = (int32_t)fdiv(g, heads);
+  u.h = (int32_t)(g - (uint32_t)u.b * heads.d);
   // Causal: the last q-tiles of a segment see the most keys; start them first.
-  u.qt = (int32_t)(causal ? n_qt - 1u - qi : qi);
+  u.qt = (int32_t)(causal ? n_qt.d - 1u - qi : qi);
   return u;
 }
 
@@ -205,8 +235,10 @@ constexpr int kLptMaxBatch = 64;
 // (groups being dealt over the 8 XCDs by d), all run on one XCD and read
 // that KV head through its L2 (with heads_k = 4, on two).  Without grouping
 // (heads_k == heads) d is the query head.
-VA_HD int32_t query_head(int32_t d, int32_t heads, int32_t heads_k) {
-  return (d % heads_k) * (heads / heads_k) + d / heads_k;
+// heads_k as a FastDiv, group = heads / heads_k.
+VA_HD int32_t query_head(int32_t d, FastDiv heads_k, int32_t group) {
+  const int32_t dq = (int32_t)fdiv((uint32_t)d, heads_k);
+  return (d - dq * (int32_t)heads_k.d) * group + dq;
 }
 
 // The heads of the segment of rank r dealt to XCD x are h0, h0 + 8, ...

@@ -114,6 +114,7 @@ constexpr int kDepth = 3;            // LDS operands read ahead of their MFMA
 // wave per SIMD.  256-row blocks measured faster than 512-row ones for
 // every head dim: finer blocks balance ragged segment mixes better.
 constexpr int kWaves = 4;
+static_assert(kWaves == 4, "the packed set-up shifts wave indices by log2(4 / pack)");
 template <int DQK, int DV>
 struct Cfg : TileGeom<DQK, DV, kBN> {
   static constexpr int WAVES = kWaves;
@@ -200,8 +201,8 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   const int g = lane >> 5;
 
   // Split-KV copy of the work units this workgroup belongs to (0 without split).
-  const int split = (int)(blockIdx.x / (uint32_t)p.n_units);
-  const BlockWork bw = block_work<PK>(p, lane, C::BM, (int64_t)blockIdx.x - (int64_t)split * p.n_units);
+  const int split = (int)blockIdx.y;  // split-KV copy (0 without split)
+  const BlockWork bw = block_work<PK>(p, lane, C::BM, (int64_t)blockIdx.x);
   if (!bw.u.valid) return;
   int h = bw.u.h;
   const int qt = bw.u.qt;
@@ -217,9 +218,9 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   int q0 = bw.q0, Lq = bw.lq, wLk = Lk, wkoff = 0, wrow0 = r0 + wave * C::RPW;
   int r1 = min(r0 + C::BM, Lq);
   if constexpr (packed) {
-    const int per = C::WAVES / p.pack;
-    const int seg = bw.u.b * p.pack + wave / per;
-    wrow0 = (wave % per) * C::RPW;
+    const int per = C::WAVES >> p.pack_shift;
+    const int seg = (bw.u.b << p.pack_shift) + (wave >> (2 - p.pack_shift));
+    wrow0 = (wave & (per - 1)) * C::RPW;
     q0 = Lq = wLk = wkoff = r1 = 0;
     if (seg < p.batch) {
       q0 = p.cu_q[seg];
@@ -235,9 +236,9 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   if constexpr (PK == kPackHeads) {
     // Query head h + wave / (4 / pack), rows 64 (wave % (4 / pack)) on, of the
     // one segment (r0 = 0): the workgroup's tiles are an unpacked unit's.
-    const int per = C::WAVES / p.pack;
-    h += wave / per;
-    wrow0 = (wave % per) * C::RPW;
+    const int per = C::WAVES >> p.pack_shift;
+    h += wave >> (2 - p.pack_shift);
+    wrow0 = (wave & (per - 1)) * C::RPW;
   }
   TileRange tr0;
   if constexpr (packed) {
@@ -246,20 +247,52 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   } else {
     tr0 = tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN);
   }
-  const TileRange tr = split_range(tr0, split, p.num_splits);
+  // Split-KV with per-segment split counts: this segment's units take
+  // min(max(count, 1), num_splits) runs; copies past that have no work.
+  int n_splits = p.num_splits;
+  if constexpr (PK != kPackSegments) {  // (a unit holds one segment; the host never packs segments then)
+    if (p.splits_dyn != nullptr) {
+      n_splits = min(max(p.splits_dyn[bw.u.b], 1), p.num_splits);
+      if (split >= n_splits) return;
+    }
+  }
+  const TileRange tr = split_range(tr0, split, n_splits);
   const int ntiles = tr.kt_end - tr.kt_begin;
   // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------
+  // For head dims <= 80, buffer loads over this wave's rows [wrow0, r1):
+  // rows past r1 (and the head-dim padding of d 72) read as zero, with no
+  // branch per load.  (At 128 and 192 the compiler then allocates the main
+  // loop's registers worse, measured 7% slower on MLA; those keep plain
+  // loads under a row check.)
   bf16x8 qf[C::QB][C::KC];
+  if constexpr (DQK > 80) {
 #pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    const int row = wrow0 + 32 * qb + l32;
-    const uint16_t* src = p.q + (int64_t)(q0 + row) * p.q_row + (int64_t)h * p.q_head;
+    for (int qb = 0; qb < C::QB; ++qb) {
+      const int row = wrow0 + 32 * qb + l32;
+      const uint16_t* src = p.q + (int64_t)(q0 + row) * p.q_row + (int64_t)h * p.q_head;
 #pragma unroll
-    for (int c = 0; c < C::KC; ++c) {
-      const int d = c * 16 + 8 * g;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < r1 && d < DQK) x = *(const u32x4*)(src + d);
-      qf[qb][c] = __builtin_bit_cast(bf16x8, x);
+      for (int c = 0; c < C::KC; ++c) {
+        const int d = c * 16 + 8 * g;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (row < r1) x = *(const u32x4*)(src + d);
+        qf[qb][c] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
+  } else {
+    const int64_t q_row_b = p.q_row * 2;
+    const int vrows = __builtin_amdgcn_readfirstlane(max(min(r1 - wrow0, C::RPW), 0));
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.q + (int64_t)(q0 + wrow0) * p.q_row + (int64_t)h * p.q_head), (short)0,
+        (int)(uint32_t)(vrows * q_row_b), kBufferFlags);
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      const uint32_t row_off = (uint32_t)((32 * qb + l32) * q_row_b);
+#pragma unroll
+      for (int c = 0; c < C::KC; ++c) {
+        const int d = c * 16 + 8 * g;
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, d < DQK ? row_off + 2 * d : kOOB, 0, 0);
+        qf[qb][c] = __builtin_bit_cast(bf16x8, x);
+      }
     }
   }
 
@@ -294,7 +327,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   }
   // K/V rows of the next tile to issue, advanced one tile per issue; tiles
   // past the last get an empty range (all reads zero).
-  const int hk = h / (p.heads / p.heads_k);  // the KV head query head h reads
+  const int hk = (int)fdiv((uint32_t)h, p.fd_group);  // the KV head query head h reads
   const char* k_next =
       (const char*)(p.k + ((int64_t)k0 + (int64_t)tr.kt_begin * kBN) * p.k_row + (int64_t)hk * p.k_head);
   const char* v_next =
@@ -342,17 +375,25 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   // after it the wave only issues its share of the loads and meets the
   // barriers.  Its own unmasked sub-range spares it the mask on tiles all its
   // rows see.  Waves past the segment's last row compute nothing.
-  int w_end = 0, w_full_begin = 0, w_full_end = 0;  // relative to tr.kt_begin
+  int w_beg = 0, w_end = 0, w_full_begin = 0, w_full_end = 0;  // relative to tr.kt_begin
   if (wrow0 < r1) {
     const TileRange wt =
         tile_range(Lq, wLk, wrow0, min(wrow0 + C::RPW, r1), p.causal, p.wl, p.wr, kBN, wkoff);
     // (clamped to this workgroup's tiles, which with split-KV are a run of
     // the rows' tiles)
+    w_beg = min(max(wt.kt_begin, tr.kt_begin), tr.kt_end) - tr.kt_begin;
     w_end = min(max(wt.kt_end, tr.kt_begin), tr.kt_end) - tr.kt_begin;
     w_full_begin = min(max(wt.full_begin, tr.kt_begin), tr.kt_end) - tr.kt_begin;
     w_full_end = min(max(wt.full_end, tr.kt_begin), tr.kt_end) - tr.kt_begin;
   }
-  const bool active = w_end > 0;
+  const bool active = w_end > w_beg;
+  // A wave computes iterations w_beg - 1 .. w_end: before its first tile it
+  // only issues its share of the loads and meets the barriers (with short
+  // segments packed into one workgroup, or a left window, the later waves'
+  // keys start later).  Iteration w_beg - 1 computes QK^T of tile w_beg
+  // (with the PV of tile w_beg - 2 on the zero probabilities below, and
+  // the softmax of the fully masked tile w_beg - 1, which changes nothing).
+  const int w_first = w_beg > 0 ? w_beg - 1 : 0;
 
 
   // ---- padded V chunks: zeros, or a one in column d_v ------------------------
@@ -411,44 +452,28 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   // Scores of two tiles (the one in the softmax and the next, which QK^T is
   // writing): sbuf[t % 2][qb][r] = key 8 (r / 4) + 4 g + r % 4, query l32.
   f32x16 sbuf[2][C::QB];
-  bf16x8 pf[C::QB][2];  // probabilities, PV B operand per (qb, 16-key half)
+  // Probabilities, the PV B operand per (qb, 16-key half); zero until a
+  // wave's first computed tile, whose PV of the previous tile then adds
+  // nothing.
+  bf16x8 pf[C::QB][2];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) pf[qb][0] = pf[qb][1] = bf16x8{};
 
-  // MFMAs of one iteration: PV of tile j - 1 (2 * VB operands, if kPV) then
-  // QK^T of tile j + 1 (KC operands) into sn, each LDS operand feeding both
-  // query blocks.  Operands are read kDepth ahead into a ring of registers.
-  auto mfma_ops = [&](const lds_char* vs, const lds_char* ks, f32x16 (&sn)[C::QB], auto pv_tag) VA_INLINE {
-    constexpr bool kPV = decltype(pv_tag)::value;
-    constexpr int kPVOps = kPV ? 2 * C::VB : 0;
-    constexpr int kOps = kPVOps + C::KC;
-    auto load_op = [&](int i, bf16x8& dst) VA_INLINE {
-      if (i < kPVOps) {  // V^T operand (t, vb) of PV
-        const int t = i / C::VB, vb = i % C::VB;
-        const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
-        const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
-        dst = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      } else {  // K operand c of QK^T
-        dst = lds_read_b128(ks, k_rd + 32 * (i - kPVOps));
-      }
-    };
+  // QK^T of one tile on its own (tile 0 and the next, and the slow path):
+  // KC K operands into sn, each LDS operand feeding both query blocks,
+  // operands read kDepth ahead into a ring of registers.
+  auto qk_only = [&](const lds_char* ks, f32x16 (&sn)[C::QB]) VA_INLINE {
     const f32x16 zero = {};
     bf16x8 ring[kDepth];
 #pragma unroll
-    for (int i = 0; i < kDepth && i < kOps; ++i) load_op(i, ring[i]);
+    for (int i = 0; i < kDepth && i < C::KC; ++i) ring[i] = lds_read_b128(ks, k_rd + 32 * i);
 #pragma unroll
-    for (int i = 0; i < kOps; ++i) {
-      const bf16x8 op = ring[i % kDepth];
-      if (i + kDepth < kOps) load_op(i + kDepth, ring[i % kDepth]);
-      if (i < kPVOps) {
-        const int t = i / C::VB, vb = i % C::VB;
+    for (int c = 0; c < C::KC; ++c) {
+      const bf16x8 op = ring[c % kDepth];
+      if (c + kDepth < C::KC) ring[c % kDepth] = lds_read_b128(ks, k_rd + 32 * (c + kDepth));
 #pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb)
-          acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, pf[qb][t], acc[vb][qb], 0, 0, 0);
-      } else {
-        const int c = i - kPVOps;
-#pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb)
-          sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qf[qb][c], c == 0 ? zero : sn[qb], 0, 0, 0);
-      }
+      for (int qb = 0; qb < C::QB; ++qb)
+        sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qf[qb][c], c == 0 ? zero : sn[qb], 0, 0, 0);
     }
   };
   // Boundary tiles only: scores of keys a row may not see become -inf.
@@ -574,24 +599,24 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
         if constexpr (!kMaxCheck && t == 1 && e == 3) bad |= !(sum[qb] <= kSumLimit);
       }
     };
-    auto load_op = [&](int i, bf16x8& dst) VA_INLINE {
-      if (i < kPVOps) {  // V^T operand (t, vb) of PV
-        const int t = i / C::VB, vb = i % C::VB;
+    auto load_op = [&](auto ii, bf16x8& dst) VA_INLINE {
+      constexpr int i = decltype(ii)::value;
+      if constexpr (i < kPVOps) {  // V^T operand (t, vb) of PV
+        constexpr int t = i / C::VB, vb = i % C::VB;
         const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
         const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
         dst = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      } else {  // K operand c of QK^T
+      } else {  // K operand i - kPVOps of QK^T
         dst = lds_read_b128(ks, k_rd + 32 * (i - kPVOps));
       }
     };
     const f32x16 zero = {};
     bf16x8 ring[kDepth];
-#pragma unroll
-    for (int i = 0; i < kDepth; ++i) load_op(i, ring[i]);
+    static_for<0, kDepth>([&](auto ii) VA_INLINE { load_op(ii, ring[decltype(ii)::value]); });
     static_for<0, kOps>([&](auto oo) VA_INLINE {
       constexpr int i = decltype(oo)::value;
       const bf16x8 op = ring[i % kDepth];
-      if constexpr (i + kDepth < kOps) load_op(i + kDepth, ring[i % kDepth]);
+      if constexpr (i + kDepth < kOps) load_op(Int<i + kDepth>{}, ring[i % kDepth]);
       static_for<0, QB>([&](auto qq) VA_INLINE {
         constexpr int qb = decltype(qq)::value, slot = QB * i + qb;
         if constexpr (i < kPVOps) {
@@ -606,10 +631,6 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
       });
     });
     return __any(bad);
-  };
-  // QK^T of one tile on its own (tile 0, and the slow path below).
-  auto qk_only = [&](const lds_char* ks, f32x16 (&sn)[C::QB]) VA_INLINE {
-    mfma_ops(nullptr, ks, sn, BoolTag<false>{});
   };
   // acc *= alpha, after the PV MFMAs of the previous tile (rare).
   auto rescale = [&](bool move, const float (&alpha)[C::QB]) VA_INLINE {
@@ -654,15 +675,15 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   if (ntiles > 0) {
     wait_landed(Int<kAhead - 1>{});  // tile 0 (tiles 0-3 were issued above)
     lds_barrier();
-    if (active) mfma_ops(nullptr, kst(Int<0>{}), sbuf[0], BoolTag<false>{});  // QK^T(0)
+    if (active && w_beg == 0) qk_only(kst(Int<0>{}), sbuf[0]);  // QK^T(0)
     wait_landed(Int<kAhead - 2>{});  // tile 1
     lds_barrier();
     // iteration 0 (no PV before it)
     {
       issue(Int<kAhead % kStages>{});
-      if (active) {
+      if (active && w_first == 0) {
         mask(0, sbuf[0]);
-        mfma_ops(nullptr, kst(Int<1>{}), sbuf[1], BoolTag<false>{});
+        qk_only(kst(Int<1>{}), sbuf[1]);
         float alpha[C::QB];
         const bool move = softmax(sbuf[0], alpha);
         rescale(move, alpha);
@@ -676,7 +697,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
         const int j = j0 + U;
         if (U == 0 || j < ntiles) {
           issue(Int<(U + 1 + kAhead) % kStages>{});  // tile j + 4 (zeros past the last)
-          if (j <= w_end) {
+          if (active && j <= w_end && j >= w_first) {
             constexpr int cur = (U + 1) % 2;  // j % 2, j0 being odd
             mask(j, sbuf[cur]);
             float sum[C::QB];
@@ -721,7 +742,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
     // The zero loads past the last tile must land before the workgroup's LDS
     // can be handed to the next workgroup.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (w_end == ntiles) {  // PV of the last tile, its stage picked at run time (all DMA has landed)
+    if (active && w_end == ntiles) {  // PV of the last tile, its stage picked at run time (all DMA has landed)
       const int last = (ntiles - 1) % kStages;
       const lds_char* vs = vst(Int<0>{});
       static_for<1, kStages>([&](auto st) VA_INLINE {
@@ -851,13 +872,20 @@ static bool supported_dims(int dqk, int dv) {
          (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128);
 }
 
+// How a launch fills its workgroups (tile_schedule.h, pack_mode); with
+// per-segment split counts (split-KV with num_splits_dynamic) a workgroup
+// must hold one segment, so short segments are not packed together then.
+static int32_t launch_mode(int64_t max_seqlen_q, int64_t heads, int64_t heads_k, bool segment_packing = true) {
+  const int32_t mode = pack_mode(max_seqlen_q, wide::kRowsPerWave, heads, heads_k);
+  return (mode == kPackSegments && !segment_packing) ? (int32_t)kPackNone : mode;
+}
+
 // `lse`: whether the caller asked for the LSE (without one the row sum is
 // taken over the bf16 probabilities, see RowSum; the launch shape is the same
-// either way).  Short segments take a packed instantiation (pack_mode); the
+// either way).  Short segments take a packed instantiation (launch_mode); the
 // unpacked one carries none of its set-up.
-static Variant variant_for(int dqk, int dv, int max_seqlen_q, int heads, int heads_k, bool lse = true) {
+static Variant variant_for(int dqk, int dv, int32_t pk, bool lse = true) {
   (void)dv;
-  const int pk = pack_mode(max_seqlen_q, wide::kRowsPerWave, heads, heads_k);
   constexpr RowSum F = RowSum::kF32, M = RowSum::kMfma;
   if (dqk == 64) return wide_variant<64, 64, F>(pk);
   if (dqk == 72) return lse ? wide_variant<72, 72, F>(pk) : wide_variant<72, 72, M>(pk);
@@ -870,14 +898,12 @@ static Variant variant_for(int dqk, int dv, int max_seqlen_q, int heads, int hea
 // Work units of a launch (padding included): (segment, head, q-tile); with
 // short segments packed (pack_mode) (group of segments, head) or (segment,
 // group of query heads).
-static int64_t launch_units(int64_t batch, int64_t heads, int64_t heads_k, int64_t max_seqlen_q, int block_m,
-                            int32_t* n_qt_out, int32_t* pack_out, int32_t* mode_out = nullptr) {
-  const int32_t mode = pack_mode(max_seqlen_q, block_m / 4, heads, heads_k);
-  const int32_t pack = segments_per_block(max_seqlen_q, block_m / 4);
+static int64_t launch_units(int64_t batch, int64_t heads, int64_t max_seqlen_q, int block_m, int32_t mode,
+                            int32_t* n_qt_out, int32_t* pack_out) {
+  const int32_t pack = mode == kPackNone ? 1 : segments_per_block(max_seqlen_q, block_m / 4);
   const int64_t n_qt = pack > 1 ? 1 : (max_seqlen_q + block_m - 1) / block_m;
   if (n_qt_out) *n_qt_out = (int32_t)n_qt;
   if (pack_out) *pack_out = pack;
-  if (mode_out) *mode_out = mode;
   if (mode == kPackHeads) return grid_blocks(batch, heads / pack, 1);
   return grid_blocks((batch + pack - 1) / pack, heads, n_qt);
 }
@@ -948,15 +974,17 @@ extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_h
     max_q = seqlens_q[i] > max_q ? seqlens_q[i] : max_q;
   }
   if (max_q <= 0) return VA_ERR_ARG;
-  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, max_q, num_heads, num_heads_k);
-  int32_t n_qt = 0, pack = 1, mode = va::kPackNone;
-  if (block < 0 || block >= va::launch_units(batch, num_heads, num_heads_k, max_q, var.block_m, &n_qt, &pack, &mode))
+  const int32_t mode = va::launch_mode(max_q, num_heads, num_heads_k);
+  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, mode);
+  int32_t n_qt = 0, pack = 1;
+  if (block < 0 || block >= va::launch_units(batch, num_heads, max_q, var.block_m, mode, &n_qt, &pack))
     return VA_ERR_ARG;
   if (mode == va::kPackHeads) {  // (segment, first query head of the group)
     const int32_t vheads = num_heads / pack;
-    const va::WorkUnit u = va::decode_block((uint32_t)block, (uint32_t)batch, (uint32_t)vheads, 1u, causal);
+    const va::WorkUnit u = va::decode_block((uint32_t)block, (uint32_t)batch, va::make_fastdiv((uint32_t)vheads),
+                                            va::make_fastdiv(1u), causal);
     *segment = u.valid ? u.b : -1;
-    *head = u.valid ? va::query_head(u.h, vheads, num_heads_k) * pack : -1;
+    *head = u.valid ? va::query_head(u.h, va::make_fastdiv((uint32_t)num_heads_k), vheads / num_heads_k) * pack : -1;
     *q_tile = u.valid ? 0 : -1;
     return VA_OK;
   }
@@ -964,10 +992,10 @@ extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_h
   const va::WorkUnit u = pack == 1 && va::lpt_applies(batch, seqlens_q, seqlens_k)
                              ? va::decode_block_lpt(block, batch, num_heads, var.block_m, n_qt, causal,
                                                     seqlens_q, seqlens_k)
-                             : va::decode_block((uint32_t)block, (uint32_t)groups, (uint32_t)num_heads,
-                                                (uint32_t)n_qt, causal);
+                             : va::decode_block((uint32_t)block, (uint32_t)groups, va::make_fastdiv((uint32_t)num_heads),
+                                                va::make_fastdiv((uint32_t)n_qt), causal);
   *segment = u.valid ? u.b * pack : -1;
-  *head = u.valid ? va::query_head(u.h, num_heads, num_heads_k) : -1;
+  *head = u.valid ? va::query_head(u.h, va::make_fastdiv((uint32_t)num_heads_k), num_heads / num_heads_k) : -1;
   *q_tile = u.valid ? u.qt : -1;
   return VA_OK;
 }
@@ -981,13 +1009,14 @@ extern "C" int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t
   if (!va::supported_dims(head_dim_qk, head_dim_v)) return VA_ERR_HEADDIM;
   if (batch < 0 || num_heads <= 0 || max_seqlen_q < 0) return VA_ERR_ARG;
   if (num_heads_k <= 0 || num_heads % num_heads_k != 0) return VA_ERR_ARG;
-  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, max_seqlen_q, num_heads, num_heads_k);
+  const int32_t mode = va::launch_mode(max_seqlen_q, num_heads, num_heads_k);
+  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, mode);
   plan->block_m = var.block_m;
   plan->block_n = var.block_n;
   plan->threads = var.threads;
   plan->lds_bytes = var.lds_bytes;
-  plan->grid = va::launch_units(batch, num_heads, num_heads_k, max_seqlen_q, var.block_m, nullptr,
-                                &plan->segments_per_block, &plan->pack_mode);
+  plan->grid = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, mode, nullptr, &plan->segments_per_block);
+  plan->pack_mode = mode;
   plan->kernel = var.name;
   return VA_OK;
 }
@@ -1001,14 +1030,14 @@ extern "C" int varlen_attn_plan_fp8(int32_t head_dim_qk, int32_t head_dim_v, int
   if (!va::fp8_supported_dims(head_dim_qk, head_dim_v)) return VA_ERR_HEADDIM;
   if (batch < 0 || num_heads <= 0 || max_seqlen_q < 0) return VA_ERR_ARG;
   if (num_heads_k <= 0 || num_heads % num_heads_k != 0) return VA_ERR_ARG;
-  const va::Variant var = va::fp8_variant(
-      head_dim_qk, head_dim_v, va::pack_mode(max_seqlen_q, va::wide::kRowsPerWave, num_heads, num_heads_k));
+  const int32_t mode = va::launch_mode(max_seqlen_q, num_heads, num_heads_k);
+  const va::Variant var = va::fp8_variant(head_dim_qk, head_dim_v, mode);
   plan->block_m = var.block_m;
   plan->block_n = var.block_n;
   plan->threads = var.threads;
   plan->lds_bytes = var.lds_bytes;
-  plan->grid = va::launch_units(batch, num_heads, num_heads_k, max_seqlen_q, var.block_m, nullptr,
-                                &plan->segments_per_block, &plan->pack_mode);
+  plan->grid = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, mode, nullptr, &plan->segments_per_block);
+  plan->pack_mode = mode;
   plan->kernel = var.name;
   return VA_OK;
 }
@@ -1071,6 +1100,7 @@ static int prepare(const va_tensor* q, const va_tensor* k, const va_tensor* v, c
   p.wr = window_right;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   p.num_splits = 1;
+  p.splits_dyn = nullptr;
   p.part_o = nullptr;
   p.part_lse = nullptr;
   p.q_descale = p.k_descale = p.v_descale = p.out_scale = nullptr;
@@ -1082,16 +1112,25 @@ static int prepare(const va_tensor* q, const va_tensor* k, const va_tensor* v, c
 // One launch of the attention kernel over num_splits copies of the work units.
 static int launch_attention(Params& p, int32_t head_dim_qk, int32_t head_dim_v, int32_t max_seqlen_q,
                             bool fp32_row_sum, void* stream, bool fp8 = false) {
-  const Variant var =
-      fp8 ? fp8_variant(head_dim_qk, head_dim_v, pack_mode(max_seqlen_q, wide::kRowsPerWave, p.heads, p.heads_k))
-          : variant_for(head_dim_qk, head_dim_v, max_seqlen_q, p.heads, p.heads_k, fp32_row_sum);
-  const int64_t units = launch_units(p.batch, p.heads, p.heads_k, max_seqlen_q, var.block_m, &p.n_qt, &p.pack);
-  const int64_t grid = units * p.num_splits;
-  if (grid > INT32_MAX) return VA_ERR_SHAPE;
+  const int32_t mode = launch_mode(max_seqlen_q, p.heads, p.heads_k, p.splits_dyn == nullptr);
+  const Variant var = fp8 ? fp8_variant(head_dim_qk, head_dim_v, mode)
+                          : variant_for(head_dim_qk, head_dim_v, mode, fp32_row_sum);
+  const int64_t units = launch_units(p.batch, p.heads, max_seqlen_q, var.block_m, mode, &p.n_qt, &p.pack);
+  if (units > INT32_MAX) return VA_ERR_SHAPE;
   p.n_units = (int32_t)units;
+  // The work-unit decode's divisors (the kernel divides by multiplying).
+  const int32_t dealt_heads = mode == kPackHeads ? p.heads / p.pack : p.heads;
+  p.fd_heads = make_fastdiv((uint32_t)dealt_heads);
+  p.fd_nqt = make_fastdiv((uint32_t)p.n_qt);
+  p.fd_heads_k = make_fastdiv((uint32_t)p.heads_k);
+  p.fd_group = make_fastdiv((uint32_t)(p.heads / p.heads_k));
+  p.qh_group = dealt_heads / p.heads_k;
+  p.n_dealt = mode == kPackSegments ? (p.batch + p.pack - 1) / p.pack : p.batch;
+  p.pack_shift = p.pack == 4 ? 2 : (p.pack == 2 ? 1 : 0);
+  // Work units along x, split-KV copies along y.
   void* args[] = {&p};
-  const hipError_t err = hipLaunchKernel(var.fn, dim3((unsigned)grid), dim3(var.threads), args, 0,
-                                         (hipStream_t)stream);
+  const hipError_t err = hipLaunchKernel(var.fn, dim3((unsigned)units, (unsigned)p.num_splits), dim3(var.threads),
+                                         args, 0, (hipStream_t)stream);
   return err == hipSuccess ? VA_OK : VA_ERR_LAUNCH;
 }
 
@@ -1156,12 +1195,10 @@ extern "C" int varlen_attn_num_splits(int32_t head_dim_qk, int32_t head_dim_v, i
   // The work units the launch has (padding included; packing and grouped
   // heads as the launch takes them) against the workgroups the device holds
   // at once; each split keeps at least 16 key tiles of the kernel's width.
-  const va::Variant var =
-      fp8 ? va::fp8_variant(head_dim_qk, head_dim_v,
-                            va::pack_mode(max_seqlen_q, va::wide::kRowsPerWave, num_heads, num_heads_k))
-          : va::variant_for(head_dim_qk, head_dim_v, max_seqlen_q, num_heads, num_heads_k, true);
-  const int64_t units =
-      va::launch_units(batch, num_heads, num_heads_k, max_seqlen_q, var.block_m, nullptr, nullptr);
+  const int32_t mode = va::launch_mode(max_seqlen_q, num_heads, num_heads_k);
+  const va::Variant var = fp8 ? va::fp8_variant(head_dim_qk, head_dim_v, mode)
+                              : va::variant_for(head_dim_qk, head_dim_v, mode, true);
+  const int64_t units = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, mode, nullptr, nullptr);
   const int64_t slots = (int64_t)cus * var.per_cu;
   const int64_t by_tiles = ((int64_t)max_seqlen_k + 16 * var.block_n - 1) / (16 * var.block_n);
   int64_t s = slots / units;
@@ -1174,16 +1211,18 @@ extern "C" int varlen_attn_num_splits(int32_t head_dim_qk, int32_t head_dim_v, i
 namespace va_merge {
 int launch_combine(const float* part_o, const float* part_lse, int32_t num_splits, int64_t total_q, int32_t heads,
                    int32_t dim, const int32_t* cu_seqlens_q, int32_t batch, const va_tensor* out, float* lse,
-                   void* stream, const float* out_scale = nullptr);
+                   void* stream, const float* out_scale, const int32_t* splits_dyn);
 }
 
 extern "C" int varlen_attn_fwd_splitkv(const va_tensor* q, const va_tensor* k, const va_tensor* v,
                                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
                                        int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
                                        int32_t causal, int32_t window_left, int32_t window_right,
-                                       const va_tensor* out, float* lse, int32_t num_splits, void* workspace,
-                                       size_t workspace_bytes, void* stream) {
+                                       const va_tensor* out, float* lse, int32_t num_splits,
+                                       const int32_t* num_splits_dynamic, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
   if (num_splits < 1 || num_splits > va::kMaxSplits) return VA_ERR_ARG;
+  if (((uintptr_t)num_splits_dynamic & 3u) != 0) return VA_ERR_ALIGN;
   va::Params p;
   bool launch = false;
   int st = va::prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k, softmax_scale,
@@ -1197,13 +1236,14 @@ extern "C" int varlen_attn_fwd_splitkv(const va_tensor* q, const va_tensor* k, c
   if (((uintptr_t)workspace & 255u) != 0) return VA_ERR_ALIGN;
   if (workspace_bytes < need) return VA_ERR_ARG;
   p.num_splits = num_splits;
+  p.splits_dyn = num_splits_dynamic;
   p.part_o = (float*)workspace;
   p.part_lse = (float*)((char*)workspace +
                         va::align256((size_t)num_splits * (size_t)q->rows * (size_t)q->heads * (size_t)v->dim * 4));
   // The partials' LSEs need the fp32 row sum, whether or not an LSE is returned.
   if ((st = va::launch_attention(p, q->dim, v->dim, max_seqlen_q, true, stream)) != VA_OK) return st;
   return va_merge::launch_combine(p.part_o, p.part_lse, num_splits, q->rows, q->heads, v->dim, cu_seqlens_q, batch,
-                                  out, lse, stream);
+                                  out, lse, stream, nullptr, num_splits_dynamic);
 }
 
 // ----------------------------------------------------------------------------
@@ -1248,8 +1288,8 @@ extern "C" int varlen_attn_fwd_splitkv_noalloc(const va_tensor* q, const va_tens
   if (num_splits < 1 || num_splits > va::kMaxSplits) return VA_ERR_ARG;
   if (num_splits == 1)
     return varlen_attn_fwd_splitkv(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k,
-                                   softmax_scale, causal, window_left, window_right, out, lse, 1, nullptr, 0,
-                                   stream);
+                                   softmax_scale, causal, window_left, window_right, out, lse, 1, nullptr, nullptr,
+                                   0, stream);
   // The argument checks first (they make no HIP call); then the size limit.
   va::Params p;
   bool launch = false;
@@ -1261,7 +1301,7 @@ extern "C" int varlen_attn_fwd_splitkv_noalloc(const va_tensor* q, const va_tens
   void* ws = va::scratch_address();
   if (ws == nullptr) return VA_ERR_LAUNCH;
   return varlen_attn_fwd_splitkv(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k,
-                                 softmax_scale, causal, window_left, window_right, out, lse, num_splits, ws,
+                                 softmax_scale, causal, window_left, window_right, out, lse, num_splits, nullptr, ws,
                                  (size_t)VA_SCRATCH_BYTES, stream);
 }
 
@@ -1270,11 +1310,13 @@ extern "C" int varlen_attn_fwd_fp8(const va_tensor* q, const va_tensor* k, const
                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
                                    int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale, int32_t causal,
                                    int32_t window_left, int32_t window_right, const va_tensor* out,
-                                   const float* out_scale, float* lse, int32_t num_splits, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
+                                   const float* out_scale, float* lse, int32_t num_splits,
+                                   const int32_t* num_splits_dynamic, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
   if (num_splits < 1 || num_splits > va::kMaxSplits) return VA_ERR_ARG;
   for (const float* d : {q_descale, k_descale, v_descale, out_scale})
     if (((uintptr_t)d & 3u) != 0) return VA_ERR_ALIGN;
+  if (((uintptr_t)num_splits_dynamic & 3u) != 0) return VA_ERR_ALIGN;
   va::Params p;
   bool launch = false;
   int st = va::prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k, softmax_scale,
@@ -1290,10 +1332,11 @@ extern "C" int varlen_attn_fwd_fp8(const va_tensor* q, const va_tensor* k, const
   if (((uintptr_t)workspace & 255u) != 0) return VA_ERR_ALIGN;
   if (workspace_bytes < need) return VA_ERR_ARG;
   p.num_splits = num_splits;
+  p.splits_dyn = num_splits_dynamic;
   p.part_o = (float*)workspace;
   p.part_lse = (float*)((char*)workspace +
                         va::align256((size_t)num_splits * (size_t)q->rows * (size_t)q->heads * (size_t)v->dim * 4));
   if ((st = va::launch_attention(p, q->dim, v->dim, max_seqlen_q, true, stream, true)) != VA_OK) return st;
   return va_merge::launch_combine(p.part_o, p.part_lse, num_splits, q->rows, q->heads, v->dim, cu_seqlens_q, batch,
-                                  out, lse, stream, out_scale);
+                                  out, lse, stream, out_scale, num_splits_dynamic);
 }

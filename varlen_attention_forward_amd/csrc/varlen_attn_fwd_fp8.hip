@@ -50,6 +50,7 @@ constexpr int kStages = 6;           // tile t lives in stage t % 6 (an even cou
 constexpr int kAhead = kStages - 2;  // iteration j issues tile j + 4
 constexpr int kDepth = 3;            // LDS operands read ahead of their MFMA
 constexpr int kWaves = 4;
+static_assert(kWaves == 4, "the packed set-up shifts wave indices by log2(4 / pack)");
 
 template <int DQK, int DV>
 struct Cfg {
@@ -160,8 +161,8 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  const int split = (int)(blockIdx.x / (uint32_t)p.n_units);
-  const BlockWork bw = block_work<PK>(p, lane, C::BM, (int64_t)blockIdx.x - (int64_t)split * p.n_units);
+  const int split = (int)blockIdx.y;  // split-KV copy (0 without split)
+  const BlockWork bw = block_work<PK>(p, lane, C::BM, (int64_t)blockIdx.x);
   if (!bw.u.valid) return;
   int h = bw.u.h;
   const int qt = bw.u.qt;
@@ -174,9 +175,9 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
   int r1 = min(r0 + C::BM, Lq);
   int wseg = bw.u.b;
   if constexpr (packed) {
-    const int per = C::WAVES / p.pack;
-    const int seg = bw.u.b * p.pack + wave / per;
-    wrow0 = (wave % per) * C::RPW;
+    const int per = C::WAVES >> p.pack_shift;
+    const int seg = (bw.u.b << p.pack_shift) + (wave >> (2 - p.pack_shift));
+    wrow0 = (wave & (per - 1)) * C::RPW;
     q0 = Lq = wLk = wkoff = r1 = 0;
     wseg = seg;
     if (seg < p.batch) {
@@ -190,9 +191,9 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
   if constexpr (PK == kPackHeads) {
     // Query head h + wave / (4 / pack), rows 64 (wave % (4 / pack)) on, of the
     // one segment (r0 = 0): the workgroup's tiles are an unpacked unit's.
-    const int per = C::WAVES / p.pack;
-    h += wave / per;
-    wrow0 = (wave % per) * C::RPW;
+    const int per = C::WAVES >> p.pack_shift;
+    h += wave >> (2 - p.pack_shift);
+    wrow0 = (wave & (per - 1)) * C::RPW;
   }
   TileRange tr0;
   if constexpr (packed) {
@@ -201,26 +202,39 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
   } else {
     tr0 = tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN);
   }
-  const TileRange tr = split_range(tr0, split, p.num_splits);
+  // Per-segment split counts, as in attn_fwd_wide.
+  int n_splits = p.num_splits;
+  if constexpr (PK != kPackSegments) {  // (a unit holds one segment; the host never packs segments then)
+    if (p.splits_dyn != nullptr) {
+      n_splits = min(max(p.splits_dyn[bw.u.b], 1), p.num_splits);
+      if (split >= n_splits) return;
+    }
+  }
+  const TileRange tr = split_range(tr0, split, n_splits);
   const int ntiles = tr.kt_end - tr.kt_begin;
-  const int hk = h / (p.heads / p.heads_k);  // the KV head query head h reads
+  const int hk = (int)fdiv((uint32_t)h, p.fd_group);  // the KV head query head h reads
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane (query, g) holds head
   // dims 64 c + 32 g .. + 31 of chunk c.
+  // Buffer loads over this wave's rows [wrow0, r1): rows past r1 read as
+  // zero, with no branch per load.
   i32x8 qf[C::QB][C::KC];
+  {
+    const int64_t q_row_b = p.q_row;  // one byte per element
+    const int vrows = __builtin_amdgcn_readfirstlane(max(min(r1 - wrow0, C::RPW), 0));
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)p.q + (int64_t)(q0 + wrow0) * p.q_row + (int64_t)h * p.q_head), (short)0,
+        (int)(uint32_t)(vrows * q_row_b), kBufferFlags);
 #pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    const int row = wrow0 + 32 * qb + l32;
-    const uint8_t* src = (const uint8_t*)p.q + (int64_t)(q0 + row) * p.q_row + (int64_t)h * p.q_head;
+    for (int qb = 0; qb < C::QB; ++qb) {
+      const uint32_t row_off = (uint32_t)((32 * qb + l32) * q_row_b);
 #pragma unroll
-    for (int c = 0; c < C::KC; ++c) {
-      const int d = 64 * c + 32 * g;
-      u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-      if (row < r1) {
-        lo = *(const u32x4*)(src + d);
-        hi = *(const u32x4*)(src + d + 16);
+      for (int c = 0; c < C::KC; ++c) {
+        const uint32_t off = row_off + 64 * c + 32 * g;
+        const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+        const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0);
+        qf[qb][c] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-      qf[qb][c] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   }
 
@@ -287,15 +301,18 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
     if (p.v_descale != nullptr) vsc = p.v_descale[di];
   }
 
-  int w_end = 0, w_full_begin = 0, w_full_end = 0;  // relative to tr.kt_begin
+  int w_beg = 0, w_end = 0, w_full_begin = 0, w_full_end = 0;  // relative to tr.kt_begin
   if (wrow0 < r1) {
     const TileRange wt =
         tile_range(Lq, wLk, wrow0, min(wrow0 + C::RPW, r1), p.causal, p.wl, p.wr, kBN, wkoff);
+    w_beg = min(max(wt.kt_begin, tr.kt_begin), tr.kt_end) - tr.kt_begin;
     w_end = min(max(wt.kt_end, tr.kt_begin), tr.kt_end) - tr.kt_begin;
     w_full_begin = min(max(wt.full_begin, tr.kt_begin), tr.kt_end) - tr.kt_begin;
     w_full_end = min(max(wt.full_end, tr.kt_begin), tr.kt_end) - tr.kt_begin;
   }
-  const bool active = w_end > 0;
+  const bool active = w_end > w_beg;
+  // As in attn_fwd_wide: a wave computes iterations w_beg - 1 .. w_end only.
+  const int w_first = w_beg > 0 ? w_beg - 1 : 0;
 
   // ---- LDS operand reads ----------------------------------------------------
   // K operand (sb, c): row 32 sb + l32, chunks 4 c + 2 g and 4 c + 2 g + 1.
@@ -339,7 +356,9 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
   // Scores of two tiles: sbuf[t % 2][qb][sb][r] = key 32 sb + 8 (r / 4) +
   // 4 g + r % 4, query l32.
   f32x16 sbuf[2][C::QB][kSB];
-  i32x8 pf[C::QB];  // probabilities, PV B operand
+  i32x8 pf[C::QB];  // probabilities, PV B operand; zero until a wave's first computed tile
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) pf[qb] = i32x8{};
 
   auto load_op = [&](int i, int pv_ops, const lds_char* vs, const lds_char* ks, i32x8& dst) VA_INLINE {
     if (i < pv_ops) {  // V^T operand vb = i
@@ -516,12 +535,12 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
   if (ntiles > 0) {
     wait_landed(Int<kAhead - 1>{});  // tile 0
     lds_barrier();
-    if (active) mfma_ops(nullptr, kst(Int<0>{}), sbuf[0], BoolTag<false>{});  // QK^T(0)
+    if (active && w_beg == 0) mfma_ops(nullptr, kst(Int<0>{}), sbuf[0], BoolTag<false>{});  // QK^T(0)
     wait_landed(Int<kAhead - 2>{});  // tile 1
     lds_barrier();
     {
       issue(Int<kAhead % kStages>{});
-      if (active) {
+      if (active && w_first == 0) {
         mask(0, sbuf[0]);
         mfma_ops(nullptr, kst(Int<1>{}), sbuf[1], BoolTag<false>{});
         float alpha[C::QB];
@@ -537,7 +556,7 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
         const int j = j0 + U;
         if (U == 0 || j < ntiles) {
           issue(Int<(U + 1 + kAhead) % kStages>{});  // tile j + 4 (zeros past the last)
-          if (j <= w_end) {
+          if (active && j <= w_end && j >= w_first) {
             constexpr int cur = (U + 1) % 2;
             mask(j, sbuf[cur]);
             float sum[C::QB];
@@ -574,7 +593,7 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
       });
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (w_end == ntiles) {  // PV of the last tile, its stage picked at run time
+    if (active && w_end == ntiles) {  // PV of the last tile, its stage picked at run time
       const int last = (ntiles - 1) % kStages;
       const lds_char* vs = vst(Int<0>{});
       static_for<1, kStages>([&](auto st) VA_INLINE {

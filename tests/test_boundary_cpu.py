@@ -273,6 +273,20 @@ def _ragged(seed, batch, lo, hi):
     return [rng.randint(lo, hi) for _ in range(batch)]
 
 
+def _head_group_shift(d_qk, d_v, heads, heads_k=None, in_bytes=2):
+    """Adjacent heads dealt together: the fewest 2^s heads whose rows of Q,
+    K, V (in_bytes per element) and O (bf16) fill whole 128-byte lines."""
+    if heads_k is not None and heads_k != heads:
+        return 0
+    for s_ in range(4):
+        hg = 1 << s_
+        if heads % hg:
+            break
+        if (hg * d_qk * in_bytes) % 128 == 0 and (hg * d_v * in_bytes) % 128 == 0 and (hg * d_v * 2) % 128 == 0:
+            return s_
+    return 0
+
+
 @pytest.mark.parametrize("lq,lk,heads,causal,dims", [
     ([4096] * 8, [4096] * 8, 16, 0, (80, 80)),            # alike: packing order
     ([256] * 36, [256] * 36, 16, 0, (80, 80)),
@@ -291,6 +305,8 @@ def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
     lk = lq if lk is None else lk
     batch, max_q = len(lq), max(lq)
     p = pkg.plan(dims[0], dims[1], batch, heads, max_q, max(lk), causal)
+    # head groups only where every segment is one q-tile (or packed)
+    hs = _head_group_shift(dims[0], dims[1], heads) if max_q <= p["block_m"] else 0
     bm = p["block_m"]
     pack = p["segments_per_block"]
     assert pack == (4 if max_q <= 64 else 2 if max_q <= 128 else 1)
@@ -305,7 +321,7 @@ def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
             for s_ in range(b, min(b + pack, batch)):
                 assert (s_, h) not in seen
                 seen[(s_, h)] = blk
-            assert (b // pack * heads + h) % 8 == blk % 8
+            assert (b // pack * (heads >> hs) + (h >> hs)) % 8 == blk % 8
         assert set(seen) == {(b, h) for b in range(batch) for h in range(heads)}
         return
     n_qt = -(-max_q // bm)
@@ -328,8 +344,9 @@ def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
         assert key not in seen, (blk, key, seen.get(key))
         seen[key] = blk
         order[blk % 8].append((blk >> 3, b))
-        # groups are dealt round-robin over the 8 XCDs (block % 8)
-        g = (rank[b] if longest_first else b) * heads + h
+        # (segment, head group) groups are dealt round-robin over the 8 XCDs
+        # (block % 8); a group's 2^hs heads run on one XCD
+        g = (rank[b] if longest_first else b) * (heads >> hs) + (h >> hs)
         assert g % 8 == blk % 8
     assert set(seen) == want
     if longest_first:
@@ -342,7 +359,7 @@ def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
             ks = sorted(quads)
             assert all(min(quads[a]) >= max(quads[c]) for a, c in zip(ks, ks[1:]))
     else:
-        assert p["grid"] - len(want) < 8 * n_qt
+        assert p["grid"] - len(want) < (8 * n_qt) << hs
     if causal:
         # within a group, one of the four q-tiles with the most keys is
         # dispatched first

@@ -60,6 +60,8 @@ struct Params {
   // (groups of pack segments when packed); the group size query_head takes.
   FastDiv fd_heads, fd_nqt, fd_heads_k, fd_group;
   int32_t n_dealt, qh_group;
+  int32_t hg_shift;  // log2 of the heads dealt together (head_group_shift); fd_heads
+                     // then counts head groups and fd_nqt workgroups per group
   float* part_o;    // [num_splits, total_q, heads, d_v]
   float* part_lse;  // [num_splits, heads, total_q]
   int32_t causal, wl, wr;
@@ -137,7 +139,7 @@ __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int b
     // (segment, group of pack query heads of one KV head): the group index
     // takes the place of the head in the dealing, and query_head keeps a KV
     // head's groups on one XCD; r.u.h is the group's first query head.
-    r.u = decode_block((uint32_t)w, (uint32_t)p.n_dealt, p.fd_heads, p.fd_nqt, p.causal);
+    r.u = decode_block((uint32_t)w, (uint32_t)p.n_dealt, p.fd_heads, p.fd_nqt, 0u, p.causal);
     r.u.h = query_head(r.u.h, p.fd_heads_k, p.qh_group) << p.pack_shift;
     if (r.u.valid) {
       r.q0 = p.cu_q[r.u.b];
@@ -148,7 +150,7 @@ __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int b
     return r;
   }
   if constexpr (PK == kPackSegments) {  // a group of pack short segments: one unit per (group, head), in packing order
-    r.u = decode_block((uint32_t)w, (uint32_t)p.n_dealt, p.fd_heads, p.fd_nqt, p.causal);
+    r.u = decode_block((uint32_t)w, (uint32_t)p.n_dealt, p.fd_heads, p.fd_nqt, (uint32_t)p.hg_shift, p.causal);
     r.u.h = query_head(r.u.h, p.fd_heads_k, p.qh_group);
     if (r.u.valid) {
       const int first = r.u.b << p.pack_shift, last = min(first + p.pack, p.batch);
@@ -178,8 +180,9 @@ __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int b
         rank += (kj > lk || (kj == lk && j < lane)) ? 1 : 0;
       }
       const int nqt = lane < p.batch ? (lq + block_m - 1) / block_m : 0;
-      const int h0 = xcd_first_head(rank, p.heads, x);
-      const int n = xcd_head_count(h0, p.heads) * nqt;
+      const int hgroups = p.heads >> p.hg_shift;
+      const int h0 = xcd_first_head(rank, hgroups, x);
+      const int n = xcd_head_count(h0, hgroups) * (nqt << p.hg_shift);
       int pre = 0;  // blocks of this XCD before this segment's
       for (int j = 0; j < p.batch; ++j)
         pre += __builtin_amdgcn_readlane(rank, j) < rank ? __builtin_amdgcn_readlane(n, j) : 0;
@@ -190,13 +193,15 @@ __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int b
         const int i = (int)__builtin_ctzll(hit);
         const int local = k - __builtin_amdgcn_readlane(pre, i);
         const int nq = __builtin_amdgcn_readlane(nqt, i);
-        const int qi = local % nq;
+        const int per = nq << p.hg_shift;
+        const int grp = local / per, rem = local - grp * per, qi = rem >> p.hg_shift;
         r.u.b = i;
-        r.u.h = query_head(__builtin_amdgcn_readlane(h0, i) + 8 * (local / nq), p.fd_heads_k, p.qh_group);
+        r.u.h = query_head(((__builtin_amdgcn_readlane(h0, i) + 8 * grp) << p.hg_shift) + (rem & ((1 << p.hg_shift) - 1)),
+                           p.fd_heads_k, p.qh_group);
         r.u.qt = p.causal ? nq - 1 - qi : qi;
       }
     } else {
-      r.u = decode_block((uint32_t)w, (uint32_t)p.n_dealt, p.fd_heads, p.fd_nqt, p.causal);
+      r.u = decode_block((uint32_t)w, (uint32_t)p.n_dealt, p.fd_heads, p.fd_nqt, (uint32_t)p.hg_shift, p.causal);
       r.u.h = query_head(r.u.h, p.fd_heads_k, p.qh_group);
     }
     if (r.u.valid) {
@@ -208,7 +213,7 @@ __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int b
     }
     return r;
   }
-  r.u = decode_block((uint32_t)w, (uint32_t)p.n_dealt, p.fd_heads, p.fd_nqt, p.causal);
+  r.u = decode_block((uint32_t)w, (uint32_t)p.n_dealt, p.fd_heads, p.fd_nqt, (uint32_t)p.hg_shift, p.causal);
   r.u.h = query_head(r.u.h, p.fd_heads_k, p.qh_group);
   if (r.u.valid) {
     const int b = __builtin_amdgcn_readfirstlane(r.u.b);

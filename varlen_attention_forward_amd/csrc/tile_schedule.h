@@ -186,9 +186,32 @@ VA_HD int32_t pack_mode(int64_t max_seqlen_q, int64_t rows_per_wave, int64_t hea
   return (heads_k > 0 && heads % heads_k == 0 && (heads / heads_k) % pk == 0) ? kPackHeads : kPackSegments;
 }
 
-VA_HD int64_t grid_blocks(int64_t batch, int64_t heads, int64_t n_qt) {
-  const int64_t groups = batch * heads;
-  return 8 * ((groups + 7) / 8) * n_qt;
+// Workgroups of a launch: (segment, head group) groups dealt over the 8
+// XCDs, each holding n_per workgroups (its heads' q-tiles).
+VA_HD int64_t grid_blocks(int64_t batch, int64_t hgroups, int64_t n_per) {
+  const int64_t groups = batch * hgroups;
+  return 8 * ((groups + 7) / 8) * n_per;
+}
+
+// Head groups.  With head dims of 72 or 80 a head's row of Q, K, V or O
+// (144 / 160 bytes) shares 128-byte lines with its neighbours, so heads
+// dealt to different XCDs make every XCD's L2 fetch those lines again
+// (measured: 1.6x the algorithmic bytes fetched on the 256- and 64-token
+// ViT windows).  The dealing below therefore keeps 2^hs adjacent heads of a
+// segment together, 2^hs x (row bytes) being a whole number of lines: their
+// workgroups go to one XCD, one q-tile of each head after the other, so they
+// run together and share those lines in its L2.  hs = 0 for grouped KV
+// heads (whose own dealing keeps a KV head's query heads together) and
+// where the rows are line-aligned already.
+VA_HD int32_t head_group_shift(int32_t d_qk, int32_t d_v, int32_t heads, int32_t heads_k, int32_t in_bytes) {
+  if (heads_k != heads) return 0;
+  for (int32_t s = 0; s <= 3; ++s) {
+    const int32_t hg = 1 << s;
+    if (heads % hg != 0) break;
+    if ((hg * d_qk * in_bytes) % 128 == 0 && (hg * d_v * in_bytes) % 128 == 0 && (hg * d_v * 2) % 128 == 0)
+      return s;
+  }
+  return 0;
 }
 
 // The quad snake over an XCD's dispatch index k (of k_count per XCD); a
@@ -197,20 +220,24 @@ VA_HD uint32_t snake_quads(uint32_t k, uint32_t k_count) {
   return ((k >> 2) & 1u) && (k | 3u) < k_count ? k ^ 3u : k;
 }
 
-// 32-bit arithmetic: the launch checks that the grid fits in int32.  `heads`
-// and `n_qt` are the dealt head count and q-tiles per group as FastDivs.
-VA_HD WorkUnit decode_block(uint32_t w, uint32_t batch, FastDiv heads, FastDiv n_qt, int causal) {
-  const uint32_t groups = batch * heads.d;
+// 32-bit arithmetic: the launch checks that the grid fits in int32.
+// `hgroups` is the dealt head count over 2^hs (head groups, see
+// head_group_shift) and `n_per` the workgroups per group (q-tiles per
+// segment times 2^hs), both as FastDivs.  Within a group the order is
+// q-tile major: q-tile 0 of its 2^hs heads, then q-tile 1, ...
+VA_HD WorkUnit decode_block(uint32_t w, uint32_t batch, FastDiv hgroups, FastDiv n_per, uint32_t hs, int causal) {
+  const uint32_t groups = batch * hgroups.d;
   const uint32_t x = w & 7u;
-  const uint32_t k = snake_quads(w >> 3, (groups + 7u) / 8u * n_qt.d);
-  const uint32_t gl = fdiv(k, n_qt), qi = k - gl * n_qt.d;
+  const uint32_t k = snake_quads(w >> 3, (groups + 7u) / 8u * n_per.d);
+  const uint32_t gl = fdiv(k, n_per), local = k - gl * n_per.d;
   const uint32_t g = gl * 8u + x;
+  const uint32_t qi = local >> hs, n_qt = n_per.d >> hs;
   WorkUnit u;
   u.valid = g < groups;
-  u.b = (int32_t)fdiv(g, heads);
-  u.h = (int32_t)(g - (uint32_t)u.b * heads.d);
+  u.b = (int32_t)fdiv(g, hgroups);
+  u.h = (int32_t)(((g - (uint32_t)u.b * hgroups.d) << hs) + (local & ((1u << hs) - 1u)));
   // Causal: the last q-tiles of a segment see the most keys; start them first.
-  u.qt = (int32_t)(causal ? n_qt.d - 1u - qi : qi);
+  u.qt = (int32_t)(causal ? n_qt - 1u - qi : qi);
   return u;
 }
 
@@ -241,7 +268,8 @@ VA_HD int32_t query_head(int32_t d, FastDiv heads_k, int32_t group) {
   return (d - dq * (int32_t)heads_k.d) * group + dq;
 }
 
-// The heads of the segment of rank r dealt to XCD x are h0, h0 + 8, ...
+// The heads (or head groups) of the segment of rank r dealt to XCD x are
+// h0, h0 + 8, ...
 VA_HD int32_t xcd_first_head(int32_t r, int32_t heads, int32_t x) {
   return (x - (int32_t)(((int64_t)r * heads) % 8) + 8) % 8;
 }
@@ -257,9 +285,10 @@ inline bool lpt_applies(int32_t batch, const int32_t* lq, const int32_t* lk) {
 
 // Host reference of the kernel's longest-first mapping (quadratic in batch).
 inline WorkUnit decode_block_lpt(int64_t w, int32_t batch, int32_t heads, int32_t block_m, int32_t n_qt,
-                                 int causal, const int32_t* lq, const int32_t* lk) {
+                                 int causal, const int32_t* lq, const int32_t* lk, int32_t hs = 0) {
   const int32_t x = (int32_t)(w & 7);
-  const int64_t k = snake_quads((uint32_t)(w >> 3), (uint32_t)(grid_blocks(batch, heads, n_qt) / 8));
+  const int32_t hgroups = heads >> hs;
+  const int64_t k = snake_quads((uint32_t)(w >> 3), (uint32_t)(grid_blocks(batch, hgroups, (int64_t)n_qt << hs) / 8));
   int64_t pre = 0;
   for (int32_t r = 0; r < batch; ++r) {
     int32_t i = 0;  // the segment of rank r
@@ -269,14 +298,15 @@ inline WorkUnit decode_block_lpt(int64_t w, int32_t batch, int32_t heads, int32_
       if (rank == r) break;
     }
     const int32_t nqt = (lq[i] + block_m - 1) / block_m;
-    const int32_t h0 = xcd_first_head(r, heads, x);
-    const int64_t n = (int64_t)xcd_head_count(h0, heads) * nqt;
+    const int64_t per = (int64_t)nqt << hs;  // workgroups of one head group of this segment
+    const int32_t h0 = xcd_first_head(r, hgroups, x);
+    const int64_t n = (int64_t)xcd_head_count(h0, hgroups) * per;
     if (k < pre + n) {
-      const int64_t local = k - pre, qi = local % nqt;
+      const int64_t local = k - pre, grp = local / per, rem = local - grp * per, qi = rem >> hs;
       WorkUnit u;
       u.valid = 1;
       u.b = i;
-      u.h = (int32_t)(h0 + 8 * (local / nqt));
+      u.h = (int32_t)(((h0 + 8 * grp) << hs) + (rem & ((1 << hs) - 1)));
       u.qt = (int32_t)(causal ? nqt - 1 - qi : qi);
       return u;
     }

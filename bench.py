@@ -33,7 +33,6 @@ import argparse
 import hashlib
 import json
 import os
-import subprocess
 import sys
 import time
 
@@ -309,24 +308,47 @@ def peak_tflops(w) -> float:
 
 
 class ClockSampler:
-    """Samples the shader clock (MHz) with rocm-smi in a background thread."""
+    """Samples the shader clock (MHz) of cuda:0 in a background thread: the
+    starred (current) level of the amdgpu driver's pp_dpm_sclk for the PCI
+    device that backs cuda:0.  (Read from sysfs, not through rocm-smi: no
+    child process, so nothing is exec'd from a process that holds the GPU.)"""
 
     def __init__(self, period_s: float = 0.25):
         import threading
 
         self.samples = []
         self.period_s = period_s
+        self._path = self._find()
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _find():
+        import glob
+
+        import torch
+
+        try:
+            pr = torch.cuda.get_device_properties(0)
+            want = "%04x:%02x:%02x." % (pr.pci_domain_id, pr.pci_bus_id, pr.pci_device_id)
+        except Exception:
+            return None
+        for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            if os.path.basename(os.path.realpath(os.path.dirname(f))).lower().startswith(want):
+                return f
+        return None
 
     def _read(self):
         import re
 
-        try:
-            res = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=10)
-        except Exception:  # tool missing or stuck: no sample
+        if self._path is None:
             return None
-        m = re.search(r"sclk clock level:\s*\d+:\s*\((\d+)\s*Mhz\)", res.stdout, re.IGNORECASE)
+        try:
+            with open(self._path) as fh:
+                txt = fh.read()
+        except OSError:
+            return None
+        m = re.search(r"(\d+)\s*mhz\s*\*", txt, re.IGNORECASE)
         return int(m.group(1)) if m else None
 
     def _run(self):
@@ -414,7 +436,8 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -
         pl = __import__("varlen_attention_forward_amd").plan(
             w.head_dim_qk, w.head_dim_v, w.batch, w.num_heads, w.max_seqlen_q, w.max_seqlen_k, w.causal,
             fp8=w.dtype == "e4m3", num_heads_k=w.heads_k)
-        if pl["pack_mode"] != 0:  # the same call with max_seqlen_q = 257: unpacked, for comparison
+        # the same call with max_seqlen_q = 257: unpacked on the four-wave kernel, for comparison
+        if pl["pack_mode"] != 0 or pl["kernel"] == "attn_fwd_short":
             times = []
             for _ in range(rounds):
                 for i in range(warmup):
@@ -461,6 +484,7 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -
         }
         if unpacked is not None:
             row["pack_mode"] = pl["pack_mode"]
+            row["kernel"] = pl["kernel"]
             row["unpacked_kernel_ms_best"] = round(unpacked, 4)
             row["unpacked_tflops_best"] = round(flops / unpacked / 1e9, 2)
         if unsplit is not None:

@@ -375,7 +375,11 @@ int varlen_attn_tile_range(int32_t seqlen_q, int32_t seqlen_k, int32_t row_begin
  * query rows, see varlen_attn_plan) it owns, or -1 in all three for a
  * workgroup that exits at once.  Segments of different lengths (at most 64
  * of them) are dealt longest key length first; otherwise in packing order;
- * either way every odd quad of each XCD's dispatch order is reversed.  When
+ * either way every odd quad of each XCD's dispatch order is reversed.
+ * Segments of at most 64 queries with head dims <= 80 (and no grouped query
+ * heads to pack instead) run one wave per (segment, head) on the
+ * short-segment kernel (va_plan.kernel "attn_fwd_short", block_m 64): q-tile
+ * 0 of each, a segment's heads dealt to one XCD in groups of up to 16.  When
  * short segments share workgroups (va_plan.segments_per_block P > 1, every
  * segment at most 128 queries), workgroup `block` owns segments
  * [segment, segment + P) (those that exist), their q-tile 0 (pack_mode 1),
@@ -399,7 +403,9 @@ typedef struct va_plan {
   int32_t threads;       /* threads per workgroup */
   int32_t lds_bytes;     /* LDS per workgroup */
   int64_t grid;          /* workgroups launched (some exit at once on short segments) */
-  const char* kernel;    /* kernel name ("attn_fwd_wide"); block_m and threads give its launch shape */
+  const char* kernel;    /* kernel name ("attn_fwd_wide", or "attn_fwd_short": one wave per (segment,
+                            head) for segments of at most 64 queries, head dims <= 80); block_m and
+                            threads give its launch shape */
   int32_t segments_per_block; /* 1, or 2 / 4 slots per workgroup for short segments (max_seqlen_q
                                  <= 128 / <= 64), one or two waves each; see pack_mode */
   int32_t pack_mode;          /* 0: unpacked; 1: the slots take consecutive segments of one head;

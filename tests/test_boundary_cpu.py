@@ -287,12 +287,25 @@ def _head_group_shift(d_qk, d_v, heads, heads_k=None, in_bytes=2):
     return 0
 
 
+def _short_head_group_shift(d_qk, d_v, heads, batch):
+    """The one-wave short-segment kernel deals more heads together: all of a
+    segment's heads (up to 16) while every XCD still gets at least 8 (segment,
+    head group) groups, and never fewer than _head_group_shift."""
+    s_ = _head_group_shift(d_qk, d_v, heads)
+    while s_ < 4 and heads % (2 << s_) == 0 and batch * (heads >> (s_ + 1)) >= 64:
+        s_ += 1
+    return s_
+
+
 @pytest.mark.parametrize("lq,lk,heads,causal,dims", [
     ([4096] * 8, [4096] * 8, 16, 0, (80, 80)),            # alike: packing order
     ([256] * 36, [256] * 36, 16, 0, (80, 80)),
     ([65536], [65536], 16, 0, (128, 128)),
-    ([1, 1], [1, 1], 1, 0, (72, 72)),                     # short: four segments per workgroup
-    ([64] * 9, [80] * 9, 3, 1, (64, 64)),                 # four 64-query segments per workgroup
+    ([1, 1], [1, 1], 1, 0, (72, 72)),                     # short: one wave per segment and head
+    ([64] * 9, [80] * 9, 3, 1, (64, 64)),
+    ([64] * 700, None, 16, 0, (80, 80)),                  # 64-token windows: all 16 heads together
+    ([64] * 20, None, 16, 0, (80, 80)),                   # 20 windows: heads stay in fours (eights: < 8 groups an XCD)
+    ([64] * 9, [80] * 9, 3, 1, (128, 128)),               # four 64-query segments per workgroup
     ([100, 3, 128, 0, 77], [500, 3, 9, 0, 77], 5, 0, (192, 128)),  # two per workgroup
     ([576, 1024, 2304, 4096, 1024, 576, 4096, 2304], None, 16, 0, (80, 80)),  # ragged: longest first
     ([700, 0, 300, 1], [700, 5, 0, 1], 5, 1, (64, 64)),
@@ -305,11 +318,15 @@ def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
     lk = lq if lk is None else lk
     batch, max_q = len(lq), max(lq)
     p = pkg.plan(dims[0], dims[1], batch, heads, max_q, max(lk), causal)
+    short = p["kernel"] == "attn_fwd_short"  # one wave per (segment, head, 64 rows)
     # head groups only where every segment is one q-tile (or packed)
-    hs = _head_group_shift(dims[0], dims[1], heads) if max_q <= p["block_m"] else 0
+    hs = ((_short_head_group_shift(dims[0], dims[1], heads, batch) if short
+           else _head_group_shift(dims[0], dims[1], heads)) if max_q <= p["block_m"] else 0)
     bm = p["block_m"]
     pack = p["segments_per_block"]
-    assert pack == (4 if max_q <= 64 else 2 if max_q <= 128 else 1)
+    assert short == (max_q <= 64 and dims[0] <= 80)
+    assert pack == (1 if short else 4 if max_q <= 64 else 2 if max_q <= 128 else 1)
+    assert (bm, p["threads"]) == ((64, 64) if short else (256, 256))
     if pack > 1:
         # short segments: block owns segments [b, b + pack) of one head, q-tile 0
         seen = {}
@@ -604,7 +621,14 @@ def test_work_unit_head_packing(heads, heads_k, lq, pack):
     (8, 8, 64, 1), (9, 3, 64, 1),                      # no grouping / group 3: segments
 ])
 def test_pack_mode_choice(heads, heads_k, max_q, mode):
-    assert pkg.plan(64, 64, 5, heads, max_q, max_q, 0, num_heads_k=heads_k)["pack_mode"] == mode
+    """bf16 segments of at most 64 queries that would be packed by segment
+    take the one-wave short-segment kernel instead (no packing, pack_mode 0)
+    where the head dims have it (<= 80); fp8 and d 128 keep the packing."""
+    short = mode == 1 and max_q <= 64
+    p = pkg.plan(64, 64, 5, heads, max_q, max_q, 0, num_heads_k=heads_k)
+    assert p["pack_mode"] == (0 if short else mode)
+    assert p["kernel"] == ("attn_fwd_short" if short else "attn_fwd_wide")
+    assert pkg.plan(128, 128, 5, heads, max_q, max_q, 0, num_heads_k=heads_k)["pack_mode"] == mode
     assert pkg.plan(64, 64, 5, heads, max_q, max_q, 0, fp8=True, num_heads_k=heads_k)["pack_mode"] == mode
 
 

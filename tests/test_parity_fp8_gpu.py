@@ -207,7 +207,7 @@ def test_fp8_packed_short_segments(dims, lens, mode):
     else:
         lk = [int(g.integers(0, 200)) for _ in lq]
     inp = make(lq, lk, dims, seed=hi + dims[0], mode=mode, heads=4)
-    assert va.plan(dims[0], dims[1], len(lq), 4, max(lq), max(lk))["segments_per_block"] > 1
+    assert va.plan(dims[0], dims[1], len(lq), 4, max(lq), max(lk), fp8=True)["segments_per_block"] > 1
     out, lse = run_fp8(inp)
     assert_fp8_parity(inp, out, lse, what="packed %s %s %s" % (dims, lens, mode))
 

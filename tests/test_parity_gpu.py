@@ -453,9 +453,10 @@ def test_packed_short_segments(dims, mode, lens):
     """Short segments share workgroups (four per workgroup when every segment
     has at most 64 queries, two when at most 128), each wave or pair of waves
     on its own segment whose keys start anywhere inside the workgroup's key
-    tiles.  Against the oracle with ragged lengths, empty segments, a
-    partial last group and q < k, with and without an LSE; rows outside
-    every segment stay untouched."""
+    tiles; at most 64 queries with head dims <= 80 take the one-wave
+    short-segment kernel instead.  Against the oracle with ragged lengths,
+    empty segments, a partial last group and q < k, with and without an
+    LSE; rows outside every segment stay untouched."""
     causal, window = MODES[mode]
     lq, lk = {
         "le64": ([1, 64, 0, 37, 64, 5, 63, 2, 50], None),
@@ -465,8 +466,10 @@ def test_packed_short_segments(dims, mode, lens):
     lk = lq if lk is None else lk
     seed = zlib.crc32(repr(("packed", dims, mode, lens)).encode()) % 1000
     inp = workloads.make_inputs(lq, lk, 3, dims[0], dims[1], seed=seed, causal=causal, window=window)
-    assert va.plan(dims[0], dims[1], len(lq), 3, max(lq), max(lk), causal)["segments_per_block"] == (
-        4 if max(lq) <= 64 else 2)
+    pl = va.plan(dims[0], dims[1], len(lq), 3, max(lq), max(lk), causal)
+    short = max(lq) <= 64 and dims[0] <= 80
+    assert pl["kernel"] == ("attn_fwd_short" if short else "attn_fwd_wide")
+    assert pl["segments_per_block"] == (1 if short else 4 if max(lq) <= 64 else 2)
     sentinel = torch.full((inp.q.shape[0] + 30, 3, dims[1]), 3.0, dtype=torch.bfloat16, device=DEV)
     out, lse = run_gpu(inp, out=sentinel[: inp.q.shape[0]])
     assert torch.all(sentinel[inp.q.shape[0]:] == 3.0)
@@ -474,6 +477,57 @@ def test_packed_short_segments(dims, mode, lens):
     assert_parity(out, lse, ref_o, ref_lse, what="packed/%s/%s/%s" % (dims, mode, lens))
     out2, _ = run_gpu(inp, return_lse=False)
     assert_parity(out2, None, ref_o, None, what="packed-nolse")
+
+
+SHORT_LENS = {
+    "le64": ([1, 64, 0, 37, 64, 5, 63, 2, 50], None),
+    "q_lt_k": ([40, 64, 1, 17, 64], [300, 64, 90, 0, 77]),
+    "q_gt_k": ([64, 33, 50], [10, 1, 49]),
+    "windows": ([64] * 24, None),
+}
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (72, 72), (80, 80)], ids=lambda d: "d%d_%d" % d)
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("lens", list(SHORT_LENS))
+def test_short_kernel_bit_equal_to_unpacked(dims, mode, lens):
+    """Segments of at most 64 queries (head dims <= 80) run one wave per
+    (segment, head) on the short-segment kernel, whose arithmetic per key
+    tile is the four-wave kernel's: O and LSE are bit-identical to the
+    four-wave kernel's unpacked launch of the same call (max_seqlen_q passed
+    as 300), with the fp32 row sum (LSE returned) and the ones-column sum (no
+    LSE), and with e4m3 output; and within the oracle's tolerance.  Eight
+    heads, so d 72 and 80 deal heads in groups (8 and 4)."""
+    causal, window = MODES[mode]
+    lq, lk = SHORT_LENS[lens]
+    lk = lq if lk is None else lk
+    heads = 8
+    seed = zlib.crc32(repr(("short", dims, mode, lens)).encode()) % 1000
+    inp = workloads.make_inputs(lq, lk, heads, dims[0], dims[1], seed=seed, causal=causal, window=window)
+    assert va.plan(dims[0], dims[1], len(lq), heads, max(lq), max(lk), causal)["kernel"] == "attn_fwd_short"
+    assert va.plan(dims[0], dims[1], len(lq), heads, 300, max(lk), causal)["kernel"] == "attn_fwd_wide"
+    d = inp.to(DEV)
+
+    def call(max_q, return_lse, out_scale=None):
+        res = va.varlen_attn_fwd(d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, max_q, inp.max_seqlen_k,
+                                 softmax_scale=inp.softmax_scale, causal=causal, window_size=window,
+                                 return_lse=return_lse, out_scale=out_scale)
+        torch.cuda.synchronize()
+        return res if return_lse else (res, None)
+
+    out, lse = call(inp.max_seqlen_q, True)
+    out_w, lse_w = call(300, True)
+    assert torch.equal(out, out_w) and torch.equal(lse, lse_w)
+    ref_o, ref_lse = oracle_on(inp)
+    assert_parity(out, lse, ref_o, ref_lse, what="short/%s/%s/%s" % (dims, mode, lens))
+    out, _ = call(inp.max_seqlen_q, False)
+    out_w, _ = call(300, False)
+    assert torch.equal(out, out_w)
+    assert_parity(out, None, ref_o, None, what="short-nolse")
+    sc = torch.tensor([0.01], dtype=torch.float32, device=DEV)
+    out, _ = call(inp.max_seqlen_q, False, sc)
+    out_w, _ = call(300, False, sc)
+    assert torch.equal(out.view(torch.uint8), out_w.view(torch.uint8))
 
 
 def test_packed_short_segments_with_split_kv_and_grouped_heads():

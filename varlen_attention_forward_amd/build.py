@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = [
     os.path.join(CSRC, "varlen_attn_fwd.hip"),
     os.path.join(CSRC, "varlen_attn_fwd_fp8.hip"),
+    os.path.join(CSRC, "varlen_attn_short.hip"),
     os.path.join(CSRC, "merge_states.hip"),
 ]
 

@@ -284,5 +284,9 @@ struct Variant {
 // instantiation for (dqk, dv), and that instantiation.
 bool fp8_supported_dims(int dqk, int dv);
 Variant fp8_variant(int dqk, int dv, int pack_mode);
+// The one-wave short-segment kernel (varlen_attn_short.hip): head dims it
+// has, and its variant (lse: whether the call returns the LSE).
+bool short_supported(int dqk, int dv);
+Variant short_variant(int dqk, int dv, bool lse);
 
 }  // namespace va

@@ -41,44 +41,9 @@
 #include <mutex>
 
 #include "attn_common.h"
+#include "wide_tile.h"
 
 namespace va {
-
-// Geometry of one K/V tile of BN keys staged in LDS.
-template <int DQK, int DV, int BN>
-struct TileGeom {
-  static constexpr int DQKP = (DQK + 15) / 16 * 16;  // MFMA K granularity (72 -> 80)
-  static constexpr int DVP = (DV + 31) / 32 * 32;    // 32-row V^T MFMA blocks (72, 80 -> 96)
-  static constexpr int KC = DQKP / 16;               // k-chunks of the QK^T product
-  static constexpr int VB = DVP / 32;                // dv blocks of the PV product
-  // K tile: BN rows of DQKP bf16 = CPR_K 16-byte chunks, plus one pad chunk
-  // per row so the 32 rows an MFMA operand read touches hit distinct banks.
-  static constexpr int CPR_K = DQKP / 8;
-  static constexpr int KPITCH = CPR_K + 1;           // chunks per K row in LDS
-  static constexpr int K_REAL = DQK / 8;             // chunks holding data
-  // V tile: BN rows of DVP bf16, chunk index XOR-swizzled per row so the
-  // four rows a transposing read touches hit distinct banks.
-  static constexpr int CPR_V = DVP / 8;
-  static constexpr int V_REAL = DV / 8;
-  // Tiles are filled by 64-lane x 16-byte LDS-DMA wave-loads (1 KB each).
-  static constexpr int K_SLOTS = BN * KPITCH;
-  static constexpr int V_SLOTS = BN * CPR_V;
-  static constexpr int K_WL = (K_SLOTS + 63) / 64;   // wave-loads per tile
-  static constexpr int V_WL = (V_SLOTS + 63) / 64;
-  static constexpr int K_TILE = K_WL * 1024;         // bytes
-  static constexpr int V_TILE = V_WL * 1024;
-  static_assert(CPR_V == 8 || CPR_V == 12 || CPR_V == 16, "V swizzle defined for 8/12/16 chunks");
-};
-
-// XOR applied to the chunk index of V row `row` (see TileGeom).
-template <int CPR_V>
-__host__ __device__ constexpr int v_swizzle(int row) {
-  return CPR_V == 16 ? 4 * (row & 3) : (CPR_V == 8 ? 4 * ((row >> 1) & 1) : 0);
-}
-
-__device__ __forceinline__ bf16x4 lds_read_tr(const lds_char* base, int byte_off) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(base + byte_off));
-}
 
 // ============================================================================
 // The kernel: 4 waves x 64 query rows (BM = 256), 32-key tiles, six LDS
@@ -143,14 +108,6 @@ struct Cfg : TileGeom<DQK, DV, kBN> {
 
 
 
-// How the row sum of the probabilities is formed: an fp32 sum of the fp32
-// probabilities (kF32), or, for d_v 72 and 80 without an LSE, a column of
-// ones in the padded V tile, which makes the PV product accumulate the sum of
-// the bf16 probabilities it multiplies alongside O with no VALU work
-// (kMfma).  O only needs the sum to normalise what the PV product
-// accumulated, so the bf16 sum serves it; a bf16 sum can move the LSE by up
-// to ln(1 + 2^-9), which is why an LSE keeps the fp32 sum.
-enum class RowSum { kF32, kMfma };
 
 template <int DQK, int DV, RowSum SUM, int PK>
 __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd_wide(Params p) {
@@ -894,6 +851,22 @@ static Variant variant_for(int dqk, int dv, int32_t pk, bool lse = true) {
   return wide_variant<192, 128, F>(pk);
 }
 
+// The kernel and fill mode of a bf16 launch.  Segments of at most 64
+// queries that would be packed four to a workgroup (no grouped query heads
+// to pack instead) take the one-wave short-segment kernel, one workgroup per
+// (segment, head), when the head dims have it and the call is not split.
+struct LaunchChoice {
+  Variant var;
+  int32_t mode;
+};
+static LaunchChoice choose_launch(int dqk, int dv, int64_t max_seqlen_q, int64_t heads, int64_t heads_k, bool lse,
+                                  bool split, bool segment_packing = true) {
+  const int32_t mode = launch_mode(max_seqlen_q, heads, heads_k, segment_packing);
+  if (!split && mode == kPackSegments && max_seqlen_q <= wide::kRowsPerWave && short_supported(dqk, dv))
+    return {short_variant(dqk, dv, lse), (int32_t)kPackNone};
+  return {variant_for(dqk, dv, mode, lse), mode};
+}
+
 
 // Work units of a launch (padding included): (segment, head, q-tile); with
 // short segments packed (pack_mode) (group of segments, head) or (segment,
@@ -906,8 +879,9 @@ static Variant variant_for(int dqk, int dv, int32_t pk, bool lse = true) {
 // loaded on ragged batches (ViT batch: 0.317 -> 0.387 ms); and none when
 // query heads of a KV head share workgroups.
 static int32_t launch_hs(int32_t dqk, int32_t dv, int32_t heads, int32_t heads_k, int32_t mode, bool fp8,
-                         int64_t max_seqlen_q, int32_t block_m) {
-  if (mode == kPackHeads || (mode == kPackNone && max_seqlen_q > block_m)) return 0;
+                         int64_t max_seqlen_q, const Variant& var, int64_t batch) {
+  if (mode == kPackHeads || (mode == kPackNone && max_seqlen_q > var.block_m)) return 0;
+  if (var.threads == 64) return short_head_group_shift(dqk, dv, heads, heads_k, batch, 2);  // one-wave kernel
   return head_group_shift(dqk, dv, heads, heads_k, fp8 ? 1 : 2);
 }
 
@@ -987,9 +961,10 @@ extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_h
     max_q = seqlens_q[i] > max_q ? seqlens_q[i] : max_q;
   }
   if (max_q <= 0) return VA_ERR_ARG;
-  const int32_t mode = va::launch_mode(max_q, num_heads, num_heads_k);
-  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, mode);
-  const int32_t hs = va::launch_hs(head_dim_qk, head_dim_v, num_heads, num_heads_k, mode, false, max_q, var.block_m);
+  const va::LaunchChoice lc = va::choose_launch(head_dim_qk, head_dim_v, max_q, num_heads, num_heads_k, true, false);
+  const int32_t mode = lc.mode;
+  const va::Variant var = lc.var;
+  const int32_t hs = va::launch_hs(head_dim_qk, head_dim_v, num_heads, num_heads_k, mode, false, max_q, var, batch);
   int32_t n_qt = 0, pack = 1;
   if (block < 0 || block >= va::launch_units(batch, num_heads, max_q, var.block_m, mode, hs, &n_qt, &pack))
     return VA_ERR_ARG;
@@ -1024,15 +999,17 @@ extern "C" int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t
   if (!va::supported_dims(head_dim_qk, head_dim_v)) return VA_ERR_HEADDIM;
   if (batch < 0 || num_heads <= 0 || max_seqlen_q < 0) return VA_ERR_ARG;
   if (num_heads_k <= 0 || num_heads % num_heads_k != 0) return VA_ERR_ARG;
-  const int32_t mode = va::launch_mode(max_seqlen_q, num_heads, num_heads_k);
-  const va::Variant var = va::variant_for(head_dim_qk, head_dim_v, mode);
+  const va::LaunchChoice lc =
+      va::choose_launch(head_dim_qk, head_dim_v, max_seqlen_q, num_heads, num_heads_k, true, false);
+  const int32_t mode = lc.mode;
+  const va::Variant var = lc.var;
   plan->block_m = var.block_m;
   plan->block_n = var.block_n;
   plan->threads = var.threads;
   plan->lds_bytes = var.lds_bytes;
   plan->grid = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, mode,
                                 va::launch_hs(head_dim_qk, head_dim_v, num_heads, num_heads_k, mode, false,
-                                              max_seqlen_q, var.block_m),
+                                              max_seqlen_q, var, batch),
                                 nullptr,
                                 &plan->segments_per_block);
   plan->pack_mode = mode;
@@ -1057,7 +1034,7 @@ extern "C" int varlen_attn_plan_fp8(int32_t head_dim_qk, int32_t head_dim_v, int
   plan->lds_bytes = var.lds_bytes;
   plan->grid = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, mode,
                                 va::launch_hs(head_dim_qk, head_dim_v, num_heads, num_heads_k, mode, true,
-                                              max_seqlen_q, var.block_m),
+                                              max_seqlen_q, var, batch),
                                 nullptr,
                                 &plan->segments_per_block);
   plan->pack_mode = mode;
@@ -1135,10 +1112,17 @@ static int prepare(const va_tensor* q, const va_tensor* k, const va_tensor* v, c
 // One launch of the attention kernel over num_splits copies of the work units.
 static int launch_attention(Params& p, int32_t head_dim_qk, int32_t head_dim_v, int32_t max_seqlen_q,
                             bool fp32_row_sum, void* stream, bool fp8 = false) {
-  const int32_t mode = launch_mode(max_seqlen_q, p.heads, p.heads_k, p.splits_dyn == nullptr);
-  const Variant var = fp8 ? fp8_variant(head_dim_qk, head_dim_v, mode)
-                          : variant_for(head_dim_qk, head_dim_v, mode, fp32_row_sum);
-  const int32_t hs = launch_hs(head_dim_qk, head_dim_v, p.heads, p.heads_k, mode, fp8, max_seqlen_q, var.block_m);
+  int32_t mode = launch_mode(max_seqlen_q, p.heads, p.heads_k, p.splits_dyn == nullptr);
+  Variant var;
+  if (fp8) {
+    var = fp8_variant(head_dim_qk, head_dim_v, mode);
+  } else {
+    const LaunchChoice lc = choose_launch(head_dim_qk, head_dim_v, max_seqlen_q, p.heads, p.heads_k, fp32_row_sum,
+                                          p.num_splits > 1, p.splits_dyn == nullptr);
+    var = lc.var;
+    mode = lc.mode;
+  }
+  const int32_t hs = launch_hs(head_dim_qk, head_dim_v, p.heads, p.heads_k, mode, fp8, max_seqlen_q, var, p.batch);
   const int64_t units = launch_units(p.batch, p.heads, max_seqlen_q, var.block_m, mode, hs, &p.n_qt, &p.pack);
   if (units > INT32_MAX) return VA_ERR_SHAPE;
   p.n_units = (int32_t)units;
@@ -1226,7 +1210,7 @@ extern "C" int varlen_attn_num_splits(int32_t head_dim_qk, int32_t head_dim_v, i
   const int64_t units =
       va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, mode,
                        va::launch_hs(head_dim_qk, head_dim_v, num_heads, num_heads_k, mode, fp8 != 0, max_seqlen_q,
-                                     var.block_m),
+                                     var, batch),
                        nullptr, nullptr);
   const int64_t slots = (int64_t)cus * var.per_cu;
   const int64_t by_tiles = ((int64_t)max_seqlen_k + 16 * var.block_n - 1) / (16 * var.block_n);

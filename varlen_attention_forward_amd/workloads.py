@@ -143,7 +143,7 @@ def _named_workloads() -> dict:
             causal=False,
             return_lse=False,  # the ViT call takes no LSE
             description="windowed ViT layer with 64-token windows (a 4K image's ~700 windows of 8 x 8 "
-            "merged patches), 16 heads, d=80, non-causal; four windows per workgroup",
+            "merged patches), 16 heads, d=80, non-causal; one wave per window and head",
         ),
         Workload(
             name="vit_long65536_d128",

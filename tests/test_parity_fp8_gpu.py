@@ -26,6 +26,9 @@ factor within e^(+-ds).  For the same reason |dLSE| <= 1e-3 + ds per row
 (the LSE moves by at most the largest score error).  With an e4m3 output the decoded code times
 out_scale may in addition be off by half an e4m3 ulp of O / out_scale.
 
+A call without an LSE runs the same arithmetic (the fp32 row sum is kept):
+its O is bit-identical to the call that returns one.
+
 Integer-exact checks: descales None equal descales of ones bit for bit, and
 halving softmax_scale while doubling every q descale gives the same bits (an
 exact power-of-two change of the fp32 score scale).
@@ -183,6 +186,8 @@ def test_fp8_small_parity(dims, mode, lens):
     out, lse = run_fp8(inp)
     assert out.dtype == torch.bfloat16
     assert_fp8_parity(inp, out, lse, what="%s %s %s" % (dims, mode, lens))
+    out2, _ = run_fp8(inp, return_lse=False)
+    assert torch.equal(out, out2)
 
 
 @pytest.mark.parametrize("dims", [(128, 128), (192, 128)], ids=lambda d: "d%d_%d" % d)
@@ -210,6 +215,8 @@ def test_fp8_packed_short_segments(dims, lens, mode):
     assert va.plan(dims[0], dims[1], len(lq), 4, max(lq), max(lk), fp8=True)["segments_per_block"] > 1
     out, lse = run_fp8(inp)
     assert_fp8_parity(inp, out, lse, what="packed %s %s %s" % (dims, lens, mode))
+    out2, _ = run_fp8(inp, return_lse=False)
+    assert torch.equal(out, out2)
 
 
 @pytest.mark.parametrize("dims", DIMS, ids=lambda d: "d%d_%d" % d)
@@ -393,7 +400,8 @@ def test_fp8_peaked_scores(dims, mode, std):
     more than the rescale threshold on many tiles, so the slow path runs
     repeatedly, and many probabilities fall into the e4m3 subnormal range or
     to zero; O stays within the element-wise bound and the LSE within
-    1e-3 + ds of the module docstring (ds reaches the 1e-3 range here)."""
+    1e-3 + ds of the module docstring (ds reaches the 1e-3 range here); the
+    call without an LSE gives the same O bit for bit."""
     inp = make([700, 129, 1000], [900, 129, 1000], dims, seed=int(std) * 11 + dims[0], mode=mode, std=std)
     out, lse = run_fp8(inp)
     assert_fp8_parity(inp, out, lse, what="peaked %s %s std %g" % (dims, mode, std))

@@ -75,6 +75,15 @@ struct Params {
   const float* out_scale;
 };
 
+// How the bf16 kernels form the row sum of the probabilities: an fp32 sum of
+// the fp32 probabilities (kF32), or, for d_v 72 and 80 without an LSE, a
+// column of ones in the padded V tile, which makes the PV product accumulate
+// the sum of the bf16 probabilities it multiplies alongside O with no VALU
+// work (kMfma).  O only needs the sum to normalise what the PV product
+// accumulated, so the bf16 sum serves it; a bf16 sum can move the LSE by up
+// to ln(1 + 2^-9), which is why an LSE keeps the fp32 sum.
+enum class RowSum { kF32, kMfma };
+
 // 16-byte-per-lane load from a buffer straight into LDS: lane i's bytes land
 // at dst + 16 i; offsets past the buffer's range read as zero.  (A plain
 // device function: inside the kernel template the builtin trips the host pass.)

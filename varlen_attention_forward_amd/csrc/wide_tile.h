@@ -44,13 +44,5 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const lds_char* base, int byte_off
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(base + byte_off));
 }
 
-// How the row sum of the probabilities is formed: an fp32 sum of the fp32
-// probabilities (kF32), or, for d_v 72 and 80 without an LSE, a column of
-// ones in the padded V tile, which makes the PV product accumulate the sum of
-// the bf16 probabilities it multiplies alongside O with no VALU work
-// (kMfma).  O only needs the sum to normalise what the PV product
-// accumulated, so the bf16 sum serves it; a bf16 sum can move the LSE by up
-// to ln(1 + 2^-9), which is why an LSE keeps the fp32 sum.
-enum class RowSum { kF32, kMfma };
 
 }  // namespace va

@@ -308,17 +308,22 @@ def peak_tflops(w) -> float:
 
 
 class ClockSampler:
-    """Samples the shader clock (MHz) of cuda:0 in a background thread: the
-    starred (current) level of the amdgpu driver's pp_dpm_sclk for the PCI
-    device that backs cuda:0.  (Read from sysfs, not through rocm-smi: no
-    child process, so nothing is exec'd from a process that holds the GPU.)"""
+    """Samples the shader clock (MHz) and board power (W) of cuda:0 in a
+    background thread: the starred (current) level of the amdgpu driver's
+    pp_dpm_sclk and its hwmon power1_input, for the PCI device that backs
+    cuda:0 (power1_cap gives the board's power limit).  Read from sysfs, not
+    through rocm-smi: no child process, so nothing is exec'd from a process
+    that holds the GPU."""
 
     def __init__(self, period_s: float = 0.25):
         import threading
 
         self.samples = []
+        self.power = []
         self.period_s = period_s
-        self._path = self._find()
+        dev = self._find()
+        self._path = None if dev is None else os.path.join(dev, "pp_dpm_sclk")
+        self._power_path, self.power_cap_w = self._hwmon(dev)
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
 
@@ -333,29 +338,51 @@ class ClockSampler:
             want = "%04x:%02x:%02x." % (pr.pci_domain_id, pr.pci_bus_id, pr.pci_device_id)
         except Exception:
             return None
-        for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
-            if os.path.basename(os.path.realpath(os.path.dirname(f))).lower().startswith(want):
-                return f
+        for d in sorted(glob.glob("/sys/class/drm/card*/device")):
+            if os.path.basename(os.path.realpath(d)).lower().startswith(want):
+                return d
         return None
+
+    @staticmethod
+    def _hwmon(dev):
+        import glob
+
+        if dev is None:
+            return None, None
+        for h in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*"))):
+            inp = os.path.join(h, "power1_input")
+            if os.path.exists(inp):
+                try:
+                    with open(os.path.join(h, "power1_cap")) as fh:
+                        cap = round(int(fh.read().strip()) / 1e6, 1)
+                except (OSError, ValueError):
+                    cap = None
+                return inp, cap
+        return None, None
 
     def _read(self):
         import re
 
-        if self._path is None:
-            return None
+        clk = pw = None
         try:
-            with open(self._path) as fh:
-                txt = fh.read()
-        except OSError:
-            return None
-        m = re.search(r"(\d+)\s*mhz\s*\*", txt, re.IGNORECASE)
-        return int(m.group(1)) if m else None
+            if self._path is not None:
+                with open(self._path) as fh:
+                    m = re.search(r"(\d+)\s*mhz\s*\*", fh.read(), re.IGNORECASE)
+                    clk = int(m.group(1)) if m else None
+            if self._power_path is not None:
+                with open(self._power_path) as fh:
+                    pw = int(fh.read().strip()) / 1e6
+        except (OSError, ValueError):
+            pass
+        return clk, pw
 
     def _run(self):
         while not self._stop.is_set():
-            v = self._read()
-            if v is not None:
-                self.samples.append(v)
+            clk, pw = self._read()
+            if clk is not None:
+                self.samples.append(clk)
+            if pw is not None:
+                self.power.append(pw)
             self._stop.wait(self.period_s)
 
     def __enter__(self):
@@ -368,6 +395,9 @@ class ClockSampler:
 
     def median(self):
         return sorted(self.samples)[len(self.samples) // 2] if self.samples else None
+
+    def power_median(self):
+        return round(sorted(self.power)[len(self.power) // 2], 1) if self.power else None
 
 
 def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -> None:
@@ -480,6 +510,7 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -
             "eager_wall_ms_median": round(statistics.median(wall_ms), 4),
             "sclk_mhz_median": clk.median(),
             "sclk_samples": len(clk.samples),
+            "board_power_w_median": clk.power_median(),
             "input_copies": len(copies),
         }
         if unpacked is not None:
@@ -598,7 +629,8 @@ def time_workload(w, copies, steps: int, warmup: int, min_warmup_s: float = MIN_
         t1 = time.perf_counter()
     return {"wall_s": (t1 - t0) / steps, "kernel_s": ev0.elapsed_time(ev1) / 1e3 / steps,
             "warmup_launches": n_warm, "warmup_s": warm_s, "sclk_mhz_median": clk.median(),
-            "sclk_samples": len(clk.samples)}
+            "sclk_samples": len(clk.samples), "board_power_w_median": clk.power_median(),
+            "power_cap_w": clk.power_cap_w}
 
 
 def result_fields(w, t: dict, steps: int, warmup: int, rotate: int) -> dict:
@@ -653,6 +685,8 @@ def result_fields(w, t: dict, steps: int, warmup: int, rotate: int) -> dict:
         "clock": {
             "sclk_mhz_median": t["sclk_mhz_median"],
             "sclk_samples": t["sclk_samples"],
+            "board_power_w_median": t["board_power_w_median"],
+            "power_cap_w": t["power_cap_w"],
             "warmup_launches": t["warmup_launches"],
             "warmup_ms": round(t["warmup_s"] * 1e3, 1),
         },

@@ -318,8 +318,8 @@ class ClockSampler:
     def __init__(self, period_s: float = 0.25):
         import threading
 
-        self.samples = []
-        self.power = []
+        self.samples, self.times = [], []  # shader clock (MHz) and when it was read
+        self.power, self.power_times = [], []
         self.period_s = period_s
         dev = self._find()
         self._path = None if dev is None else os.path.join(dev, "pp_dpm_sclk")
@@ -379,10 +379,13 @@ class ClockSampler:
     def _run(self):
         while not self._stop.is_set():
             clk, pw = self._read()
+            now = time.perf_counter()
             if clk is not None:
                 self.samples.append(clk)
+                self.times.append(now)
             if pw is not None:
                 self.power.append(pw)
+                self.power_times.append(now)
             self._stop.wait(self.period_s)
 
     def __enter__(self):
@@ -393,11 +396,17 @@ class ClockSampler:
         self._stop.set()
         self._thread.join(timeout=15)
 
-    def median(self):
-        return sorted(self.samples)[len(self.samples) // 2] if self.samples else None
+    def median(self, since=None):
+        """Median of the samples read at or after perf_counter time `since`."""
+        v = sorted(x for x, t in zip(self.samples, self.times) if since is None or t >= since)
+        return v[len(v) // 2] if v else None
 
-    def power_median(self):
-        return round(sorted(self.power)[len(self.power) // 2], 1) if self.power else None
+    def power_median(self, since=None):
+        v = sorted(x for x, t in zip(self.power, self.power_times) if since is None or t >= since)
+        return round(v[len(v) // 2], 1) if v else None
+
+    def count(self, since=None):
+        return sum(1 for t in self.times if since is None or t >= since)
 
 
 def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -> None:
@@ -610,7 +619,7 @@ def time_workload(w, copies, steps: int, warmup: int, min_warmup_s: float = MIN_
 
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with ClockSampler(period_s=0.05) as clk:
+    with ClockSampler(period_s=0.02) as clk:
         t0 = time.perf_counter()
         n_warm = 0
         while n_warm < warmup or time.perf_counter() - t0 < min_warmup_s:
@@ -621,6 +630,7 @@ def time_workload(w, copies, steps: int, warmup: int, min_warmup_s: float = MIN_
         torch.cuda.synchronize()
         warm_s = time.perf_counter() - t0
         t0 = time.perf_counter()
+        since = t0 - 0.15  # the clock and power of the last 150 ms of warm-up and the timed steps
         ev0.record(stream)
         for i in range(steps):
             launch(copies, i, w.num_splits)
@@ -628,8 +638,8 @@ def time_workload(w, copies, steps: int, warmup: int, min_warmup_s: float = MIN_
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     return {"wall_s": (t1 - t0) / steps, "kernel_s": ev0.elapsed_time(ev1) / 1e3 / steps,
-            "warmup_launches": n_warm, "warmup_s": warm_s, "sclk_mhz_median": clk.median(),
-            "sclk_samples": len(clk.samples), "board_power_w_median": clk.power_median(),
+            "warmup_launches": n_warm, "warmup_s": warm_s, "sclk_mhz_median": clk.median(since),
+            "sclk_samples": clk.count(since), "board_power_w_median": clk.power_median(since),
             "power_cap_w": clk.power_cap_w}
 
 

@@ -530,6 +530,60 @@ def test_short_kernel_bit_equal_to_unpacked(dims, mode, lens):
     assert torch.equal(out.view(torch.uint8), out_w.view(torch.uint8))
 
 
+def test_short_kernel_strided_views():
+    """The short-segment kernel on views: Q and K with a padded head stride,
+    V inside an interleaved [T, H, 2 x d] buffer, O written into a strided
+    view whose padding stays untouched; bit-identical to the contiguous
+    call."""
+    lq = [64, 17, 0, 64, 1, 50, 64, 33]
+    inp = workloads.make_inputs(lq, lq, 4, 80, 80, seed=77, causal=False, window=(20, 5))
+    assert va.plan(80, 80, len(lq), 4, 64, 64, False)["kernel"] == "attn_fwd_short"
+    o_ref, l_ref = run_gpu(inp)
+    T = inp.q.shape[0]
+
+    def padded(t, width):
+        buf = torch.full((T, 4, width), float("nan"), dtype=torch.bfloat16, device=DEV)
+        buf[:, :, width - 80:] = t.to(DEV)
+        return buf[:, :, width - 80:]
+
+    q_view, k_view, v_view = padded(inp.q, 96), padded(inp.k, 128), padded(inp.v, 160)
+    assert q_view.stride() == (4 * 96, 96, 1) and v_view.stride() == (4 * 160, 160, 1)
+    big = torch.full((T, 4, 112), 7.0, dtype=torch.bfloat16, device=DEV)
+    out_view = big[:, :, 16:96]
+    lse = torch.full((4, T), float("nan"), dtype=torch.float32, device=DEV)
+    va.varlen_attn_fwd(q_view, k_view, v_view, inp.cu_seqlens_q.to(DEV), inp.cu_seqlens_k.to(DEV),
+                       inp.max_seqlen_q, inp.max_seqlen_k, softmax_scale=inp.softmax_scale,
+                       window_size=inp.window, out=out_view, return_lse=True, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out_view, o_ref) and torch.equal(lse, l_ref)
+    assert torch.all(big[:, :, :16] == 7.0) and torch.all(big[:, :, 96:] == 7.0)
+
+
+def test_short_kernel_beyond_2gib():
+    """64-bit addressing in the short-segment kernel: 36000 windows of 64
+    tokens, 8 heads, d 64, so Q, K, V and O each span 2.36 GB and the last
+    windows start past 2^31 bytes.  Sampled windows (first, middle, last
+    three) against the oracle run on just those windows."""
+    B, L, H, D = 36000, 64, 8, 64
+    assert B * L * H * D * 2 > 2 ** 31
+    g = torch.Generator(device=DEV).manual_seed(2025)
+    q = torch.randn((B * L, H, D), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((B * L, H, D), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((B * L, H, D), generator=g, device=DEV).to(torch.bfloat16)
+    cu = torch.arange(0, (B + 1) * L, L, dtype=torch.int32, device=DEV)
+    assert va.plan(D, D, B, H, L, L, False)["kernel"] == "attn_fwd_short"
+    out, lse = va.varlen_attn_fwd(q, k, v, cu, cu, L, L, return_lse=True)
+    torch.cuda.synchronize()
+    from oracle import attention_fwd
+
+    for b in (0, B // 2, B - 3, B - 2, B - 1):
+        sl = slice(b * L, (b + 1) * L)
+        ref_o, ref_lse = attention_fwd(f32(q[sl]), f32(k[sl]), f32(v[sl]), [0, L], [0, L], D ** -0.5)
+        assert_parity(out[sl], lse[:, sl].contiguous(), ref_o, ref_lse, what="window %d" % b)
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+
+
 def test_packed_short_segments_with_split_kv_and_grouped_heads():
     inp = workloads.make_inputs([64, 30, 64, 1, 64], [2000, 30, 700, 5, 64], 8, 128, 128, seed=42, causal=True,
                                 num_heads_k=2)

@@ -49,7 +49,10 @@ DEFAULT_WORKLOAD = "vit_full_d80"
 KERNEL_SOURCES = [
     os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "varlen_attn_fwd.hip"),
     os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "varlen_attn_fwd_fp8.hip"),
+    os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "varlen_attn_short.hip"),
+    os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "merge_states.hip"),
     os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "attn_common.h"),
+    os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "wide_tile.h"),
     os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "tile_schedule.h"),
 ]
 

@@ -508,8 +508,8 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   // only if the check passed.
   //
   // Its VALU work is 48 or 64 units in dependency order: (16 row-max steps,
-  // 8 per query block, on the raw scores, kMfma only), 32 in-place exps, 16
-  // packs (+ sums).  The MFMAs (PV of the previous tile, then QK^T of the
+  // 8 per query block, on the raw scores, kMfma only), (32 scale-and-shift
+  // FMAs, head dims <= 80,) 32 in-place exps, 16 packs (+ sums).  The MFMAs (PV of the previous tile, then QK^T of the
   // next, two per LDS operand) each get an even share of the units, in
   // source order pinned by scheduling barriers: the compiler's own schedule
   // bunches the MFMAs, and an MFMA hides only a few VALU ops behind it.  The
@@ -520,8 +520,12 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
     constexpr bool kMaxCheck = SUM_BY_MFMA;
     constexpr int QB = C::QB;
     constexpr int kPVOps = 2 * C::VB, kOps = kPVOps + C::KC, kSlots = QB * kOps;
-    constexpr int kMaxU = 8 * QB, kExpU = 16 * QB, kPackU = 8 * QB;  // units per kind
-    constexpr int kUnits = (kMaxCheck ? kMaxU : 0) + kExpU + kPackU;
+    // With two waves per SIMD (head dims <= 80) the scale-and-shift FMAs run
+    // as units of their own, all before the exps (measured +1% on the ViT
+    // batch, bit-identical); one wave per SIMD keeps each FMA with its exp.
+    constexpr bool kSplitExp = DQK <= 80;
+    constexpr int kMaxU = 8 * QB, kFmaU = kSplitExp ? 16 * QB : 0, kExpU = 16 * QB, kPackU = 8 * QB;  // units per kind
+    constexpr int kUnits = (kMaxCheck ? kMaxU : 0) + kFmaU + kExpU + kPackU;
     static_assert((kUnits - kPackU) * kSlots / kUnits >= QB * kPVOps, "packs must follow the PV MFMAs");
     float m[QB];
     bool bad = false;
@@ -541,11 +545,15 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
           m[qb] = fmaxf(m[qb], s[qb][15]);
           bad |= m[qb] * p.scale_log2 > lim[qb];
         }
-      } else if constexpr (u < kMaxU + kExpU) {  // p = exp2(s * scale - m_run), in place
+      } else if constexpr (u < kMaxU + kFmaU) {  // s * scale - m_run, in place
         constexpr int qb = (u - kMaxU) / 16, r = (u - kMaxU) % 16;
-        s[qb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, nm[qb]));
+        s[qb][r] = fmaf(s[qb][r], p.scale_log2, nm[qb]);
+      } else if constexpr (u < kMaxU + kFmaU + kExpU) {  // p = exp2(s * scale - m_run), in place
+        constexpr int qb = (u - kMaxU - kFmaU) / 16, r = (u - kMaxU - kFmaU) % 16;
+        s[qb][r] = kSplitExp ? __builtin_amdgcn_exp2f(s[qb][r])
+                             : __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, nm[qb]));
       } else {  // bf16 pack (and row sum)
-        constexpr int i = u - kMaxU - kExpU, qb = i / 8, t = (i / 4) % 2, e = i % 4, r = 8 * t + 2 * e;
+        constexpr int i = u - kMaxU - kFmaU - kExpU, qb = i / 8, t = (i / 4) % 2, e = i % 4, r = 8 * t + 2 * e;
         constexpr bool first = t == 0 && e == 0;
         pk[qb][t][e] = pack_bf16x2(s[qb][r], s[qb][r + 1]);
         if constexpr (SUM == RowSum::kF32) {

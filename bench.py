@@ -433,7 +433,7 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         eager_ms, wall_ms = [], []
         ns = w.num_splits
-        with ClockSampler() as clk:
+        with ClockSampler(period_s=0.02) as clk:
             for _ in range(rounds):
                 for i in range(warmup):
                     launch(copies, i, ns)
@@ -540,13 +540,13 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -
         rows.append(row)
         print(json.dumps(row), flush=True)
     print("| workload | kernel ms best / median | TFLOP/s best / median | % of its dtype's peak | GB/s "
-          "| graph ms best / median | eager wall ms | sclk MHz |", flush=True)
-    print("|---|---|---|---|---|---|---|---|")
+          "| graph ms best / median | eager wall ms | sclk MHz | board W |", flush=True)
+    print("|---|---|---|---|---|---|---|---|---|")
     for r in rows:
-        print("| %s | %.4f / %.4f | %.1f / %.1f | %.1f%% (%s) | %.0f | %.4f / %.4f | %.4f | %s |" % (
+        print("| %s | %.4f / %.4f | %.1f / %.1f | %.1f%% (%s) | %.0f | %.4f / %.4f | %.4f | %s | %s |" % (
             r["workload"], r["kernel_ms_best"], r["kernel_ms_median"], r["tflops_best"], r["tflops_median"],
             100 * r["frac_of_own_peak_best"], r["dtype"], r["gbs_best"], r["graph_ms_best"], r["graph_ms_median"],
-            r["eager_wall_ms_median"], r["sclk_mhz_median"]), flush=True)
+            r["eager_wall_ms_median"], r["sclk_mhz_median"], r["board_power_w_median"]), flush=True)
 
 
 MERGE_SHAPE = (16384, 128, 128)  # rows, heads, d_v: the MLA prefill batch's output

@@ -265,11 +265,31 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_short(Params p) {
   // key: tested on the raw row max with the ones-column sum, on the row sums
   // and first tiles with the fp32 sum), else the slow path with the rescale;
   // then O^T += V^T P^T.
-  auto tile = [&](auto st, int j) VA_INLINE {
+  // The full softmax step with its rescale (the slow path).
+  auto slow = [&](f32x16 (&s)[QB]) VA_INLINE {
+    float alpha[QB];
+    const bool move = softmax(s, alpha);
+    if (move) {
+      asm volatile("; lazy rescale" ::: "memory");
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int vb = 0; vb < C::VB; ++vb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[vb][qb][r] *= alpha[qb];
+    }
+  };
+  // The wave's first tile holds some row's first visible key, so the fast
+  // path cannot hold there: it takes the full softmax at once (FIRST), with
+  // no fast-path work to discard and no scores to recompute.
+  auto tile = [&](auto st, int j, auto first) VA_INLINE {
     constexpr int S = decltype(st)::value;
     f32x16 s[QB];
     qk(kf[S], s);
     mask(j, s);
+    if constexpr (decltype(first)::value) {
+      slow(s);
+    } else {
     // The fast path: p = exp2(s * scale * log2(e) - m_run) in place, packed
     // to bf16 (and summed in pairs with the fp32 sum), valid when every p <=
     // 2^kRescaleTau and no row meets its first visible key: tested on the
@@ -326,17 +346,8 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_short(Params p) {
       for (int qb = 0; qb < QB; ++qb) l_run[qb] = l_prev[qb];
       qk(kf[S], s);
       mask(j, s);
-      float alpha[QB];
-      const bool move = softmax(s, alpha);
-      if (move) {
-        asm volatile("; lazy rescale" ::: "memory");
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int vb = 0; vb < C::VB; ++vb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[vb][qb][r] *= alpha[qb];
-      }
+      slow(s);
+    }
     }
     // K of tile j + 2 into this register set, then V of this tile landed:
     // only K j + 1, V j + 1 and K j + 2 (those that exist) may be in flight.
@@ -363,18 +374,26 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_short(Params p) {
       }
   };
 
-  // ---- main loop: tile j in set / stage j % 2 (the loop unrolled by the
-  // stage count so each is named statically); V of tile j + 2 is issued into
-  // the stage once PV j has read it.  (K j's registers are waited for by the
-  // compiler at their first use.)
-  for (int j0 = 0; j0 < ntiles; j0 += kStages) {
+  // ---- main loop: tile j in set / stage j % 2 (tile 0 on its own, then
+  // the loop unrolled by the stage count so each is named statically); V of
+  // tile j + 2 is issued into the stage once PV j has read it.  (K j's
+  // registers are waited for by the compiler at their first use.)
+  if (ntiles > 0) {
+    tile(Int<0>{}, 0, BoolTag<true>{});
+    if (kStages < ntiles) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage 0's V^T reads are done
+      issue_v(Int<0>{}, kStages);
+    }
+  }
+  for (int j0 = 1; j0 < ntiles; j0 += kStages) {
     static_for<0, kStages>([&](auto u) VA_INLINE {
+      constexpr int S = (decltype(u)::value + 1) % kStages;
       const int j = j0 + decltype(u)::value;
       if (j < ntiles) {
-        tile(u, j);
+        tile(Int<S>{}, j, BoolTag<false>{});
         if (j + kStages < ntiles) {
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this stage's V^T reads are done
-          issue_v(u, j + kStages);
+          issue_v(Int<S>{}, j + kStages);
         }
       }
     });

@@ -373,7 +373,8 @@ int varlen_attn_tile_range(int32_t seqlen_q, int32_t seqlen_k, int32_t row_begin
  * taken as their maximum.  For workgroup `block` of the grid varlen_attn_fwd
  * launches for these sizes, returns the segment, head and q-tile (block_m
  * query rows, see varlen_attn_plan) it owns, or -1 in all three for a
- * workgroup that exits at once.  Segments of different lengths (at most 64
+ * workgroup that exits at once.  For attn_fwd_short `block` is a one-wave
+ * work unit (va_plan.units of them, four to a workgroup).  Segments of different lengths (at most 64
  * of them) are dealt longest key length first; otherwise in packing order;
  * either way every odd quad of each XCD's dispatch order is reversed.
  * Segments of at most 64 queries with head dims <= 80 (and no grouped query
@@ -398,20 +399,23 @@ int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_heads, int32
 
 /* Launch shape varlen_attn_fwd would use (host only; makes no HIP call). */
 typedef struct va_plan {
-  int32_t block_m;       /* query rows per workgroup */
+  int32_t block_m;       /* query rows per work unit (per workgroup, but for attn_fwd_short) */
   int32_t block_n;       /* keys per K/V tile */
   int32_t threads;       /* threads per workgroup */
   int32_t lds_bytes;     /* LDS per workgroup */
   int64_t grid;          /* workgroups launched (some exit at once on short segments) */
-  const char* kernel;    /* kernel name ("attn_fwd_wide", or "attn_fwd_short": one wave per (segment,
-                            head) for segments of at most 64 queries, head dims <= 80); block_m and
-                            threads give its launch shape */
+  const char* kernel;    /* kernel name: "attn_fwd_wide", or "attn_fwd_short" for segments of at most
+                            64 queries with head dims <= 80, whose workgroups hold four independent
+                            one-wave units (block_m 64 rows each): workgroup w's wave v takes unit
+                            ((w >> 3) * 4 + v) * 8 + (w & 7) */
   int32_t segments_per_block; /* 1, or 2 / 4 slots per workgroup for short segments (max_seqlen_q
                                  <= 128 / <= 64), one or two waves each; see pack_mode */
   int32_t pack_mode;          /* 0: unpacked; 1: the slots take consecutive segments of one head;
                                  2: they take query heads of one KV head over one segment (grouped
                                  KV heads with a group size that is a multiple of the slot count:
                                  FA4's pack_gqa, SGLang PR #41344 "Accuracy Tests") */
+  int64_t units;              /* work units (varlen_attn_work_unit's blocks), padding included:
+                                 grid, or 4 per workgroup for attn_fwd_short */
 } va_plan;
 
 int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch, int32_t num_heads,

@@ -287,6 +287,26 @@ def _head_group_shift(d_qk, d_v, heads, heads_k=None, in_bytes=2):
     return 0
 
 
+@pytest.mark.parametrize("batch,heads", [(700, 16), (5, 3), (33, 8), (1, 1)])
+def test_short_kernel_workgroups_cover_units(batch, heads):
+    """The short-segment kernel's workgroups hold four one-wave units:
+    workgroup w's wave v takes unit ((w >> 3) * 4 + v) * 8 + (w & 7).  Over
+    the plan's grid every unit below va_plan.units is taken exactly once, on
+    the XCD (w % 8) its dealing intends (unit % 8), and no workgroup is
+    launched whose waves all fall past the units."""
+    p = pkg.plan(80, 80, batch, heads, 64, 64)
+    assert p["kernel"] == "attn_fwd_short" and p["threads"] == 256
+    taken = {}
+    for w in range(p["grid"]):
+        us = [((w >> 3) * 4 + v) * 8 + (w & 7) for v in range(4)]
+        assert any(u < p["units"] for u in us)
+        for u in us:
+            if u < p["units"]:
+                assert u not in taken and u % 8 == w % 8
+                taken[u] = w
+    assert sorted(taken) == list(range(p["units"]))
+
+
 def _short_head_group_shift(d_qk, d_v, heads, batch):
     """The one-wave short-segment kernel deals more heads together: all of a
     segment's heads (up to 16) while every XCD still gets at least 8 (segment,
@@ -326,11 +346,14 @@ def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
     pack = p["segments_per_block"]
     assert short == (max_q <= 64 and dims[0] <= 80)
     assert pack == (1 if short else 4 if max_q <= 64 else 2 if max_q <= 128 else 1)
-    assert (bm, p["threads"]) == ((64, 64) if short else (256, 256))
+    assert (bm, p["threads"]) == (64, 256) if short else (256, 256)
+    # one-wave units, four to a workgroup, for the short-segment kernel
+    assert p["units"] % 8 == 0
+    assert p["grid"] == ((p["units"] // 8 + 3) // 4 * 8 if short else p["units"])
     if pack > 1:
         # short segments: block owns segments [b, b + pack) of one head, q-tile 0
         seen = {}
-        for blk in range(p["grid"]):
+        for blk in range(p["units"]):
             b, h, qt = pkg.work_unit(blk, heads, dims[0], dims[1], lq, lk, causal)
             if b < 0:
                 continue
@@ -351,7 +374,7 @@ def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
     rank = {b: r for r, b in enumerate(rank)}
     seen = {}
     order = [[] for _ in range(8)]  # per XCD, owners in dispatch order
-    for blk in range(p["grid"]):
+    for blk in range(p["units"]):
         b, h, qt = pkg.work_unit(blk, heads, dims[0], dims[1], lq, lk, causal)
         if b < 0:
             assert h == -1 and qt == -1
@@ -376,7 +399,7 @@ def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
             ks = sorted(quads)
             assert all(min(quads[a]) >= max(quads[c]) for a, c in zip(ks, ks[1:]))
     else:
-        assert p["grid"] - len(want) < (8 * n_qt) << hs
+        assert p["units"] - len(want) < (8 * n_qt) << hs
     if causal:
         # within a group, one of the four q-tiles with the most keys is
         # dispatched first

@@ -75,6 +75,7 @@ class VaPlan(ctypes.Structure):
         ("kernel", ctypes.c_char_p),
         ("segments_per_block", ctypes.c_int32),
         ("pack_mode", ctypes.c_int32),
+        ("units", ctypes.c_int64),
     ]
 
 
@@ -217,6 +218,7 @@ def plan(head_dim_qk, head_dim_v, batch, num_heads, max_seqlen_q, max_seqlen_k, 
         "kernel": pl.kernel.decode(),
         "segments_per_block": pl.segments_per_block,
         "pack_mode": pl.pack_mode,
+        "units": pl.units,
     }
 
 

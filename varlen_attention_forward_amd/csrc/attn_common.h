@@ -287,6 +287,7 @@ struct Variant {
   int threads;
   const char* name;
   int per_cu;  // workgroups a compute unit holds at once (the launch bounds' minimum)
+  int units_per_wg;  // work units a workgroup holds (its waves' own units; 1 but for attn_fwd_short)
 };
 
 // The fp8 e4m3 kernel (varlen_attn_fwd_fp8.hip): whether it has an

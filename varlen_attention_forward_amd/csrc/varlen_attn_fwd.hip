@@ -829,7 +829,7 @@ static Variant wide_variant(int mode) {
   const void* fn = mode == kPackHeads      ? (const void*)&attn_fwd_wide<DQK, DV, SUM, kPackHeads>
                    : mode == kPackSegments ? (const void*)&attn_fwd_wide<DQK, DV, SUM, kPackSegments>
                                            : (const void*)&attn_fwd_wide<DQK, DV, SUM, kPackNone>;
-  return {fn, C::LDS_BYTES, C::BM, wide::kBN, C::THREADS, "attn_fwd_wide", DQK <= 80 ? 2 : 1};
+  return {fn, C::LDS_BYTES, C::BM, wide::kBN, C::THREADS, "attn_fwd_wide", DQK <= 80 ? 2 : 1, 1};
 }
 
 static bool supported_dims(int dqk, int dv) {
@@ -889,8 +889,18 @@ static LaunchChoice choose_launch(int dqk, int dv, int64_t max_seqlen_q, int64_t
 static int32_t launch_hs(int32_t dqk, int32_t dv, int32_t heads, int32_t heads_k, int32_t mode, bool fp8,
                          int64_t max_seqlen_q, const Variant& var, int64_t batch) {
   if (mode == kPackHeads || (mode == kPackNone && max_seqlen_q > var.block_m)) return 0;
-  if (var.threads == 64) return short_head_group_shift(dqk, dv, heads, heads_k, batch, 2);  // one-wave kernel
+  if (var.units_per_wg > 1) return short_head_group_shift(dqk, dv, heads, heads_k, batch, 2);  // one-wave units
   return head_group_shift(dqk, dv, heads, heads_k, fp8 ? 1 : 2);
+}
+
+// Workgroups launched for `units` work units (a multiple of 8): one each, or
+// for a kernel whose workgroup holds u > 1 units (attn_fwd_short: one per
+// wave), ceil(units / 8u) x 8 of them, workgroup w's wave v taking unit
+// ((w >> 3) u + v) x 8 + (w & 7), so that every unit keeps its XCD (w % 8 =
+// unit % 8) and each XCD's units stay in dispatch order.
+static int64_t launch_workgroups(int64_t units, const Variant& var) {
+  const int64_t u = var.units_per_wg;
+  return u == 1 ? units : (units / 8 + u - 1) / u * 8;
 }
 
 static int64_t launch_units(int64_t batch, int64_t heads, int64_t max_seqlen_q, int block_m, int32_t mode,
@@ -1015,11 +1025,12 @@ extern "C" int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t
   plan->block_n = var.block_n;
   plan->threads = var.threads;
   plan->lds_bytes = var.lds_bytes;
-  plan->grid = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, mode,
-                                va::launch_hs(head_dim_qk, head_dim_v, num_heads, num_heads_k, mode, false,
-                                              max_seqlen_q, var, batch),
-                                nullptr,
-                                &plan->segments_per_block);
+  plan->units = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, mode,
+                                 va::launch_hs(head_dim_qk, head_dim_v, num_heads, num_heads_k, mode, false,
+                                               max_seqlen_q, var, batch),
+                                 nullptr,
+                                 &plan->segments_per_block);
+  plan->grid = va::launch_workgroups(plan->units, var);
   plan->pack_mode = mode;
   plan->kernel = var.name;
   return VA_OK;
@@ -1040,11 +1051,12 @@ extern "C" int varlen_attn_plan_fp8(int32_t head_dim_qk, int32_t head_dim_v, int
   plan->block_n = var.block_n;
   plan->threads = var.threads;
   plan->lds_bytes = var.lds_bytes;
-  plan->grid = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, mode,
-                                va::launch_hs(head_dim_qk, head_dim_v, num_heads, num_heads_k, mode, true,
-                                              max_seqlen_q, var, batch),
-                                nullptr,
-                                &plan->segments_per_block);
+  plan->units = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, mode,
+                                 va::launch_hs(head_dim_qk, head_dim_v, num_heads, num_heads_k, mode, true,
+                                               max_seqlen_q, var, batch),
+                                 nullptr,
+                                 &plan->segments_per_block);
+  plan->grid = va::launch_workgroups(plan->units, var);
   plan->pack_mode = mode;
   plan->kernel = var.name;
   return VA_OK;
@@ -1144,10 +1156,10 @@ static int launch_attention(Params& p, int32_t head_dim_qk, int32_t head_dim_v, 
   p.qh_group = dealt_heads / p.heads_k;
   p.n_dealt = mode == kPackSegments ? (p.batch + p.pack - 1) / p.pack : p.batch;
   p.pack_shift = p.pack == 4 ? 2 : (p.pack == 2 ? 1 : 0);
-  // Work units along x, split-KV copies along y.
+  // Workgroups along x, split-KV copies along y.
   void* args[] = {&p};
-  const hipError_t err = hipLaunchKernel(var.fn, dim3((unsigned)units, (unsigned)p.num_splits), dim3(var.threads),
-                                         args, 0, (hipStream_t)stream);
+  const hipError_t err = hipLaunchKernel(var.fn, dim3((unsigned)launch_workgroups(units, var), (unsigned)p.num_splits),
+                                         dim3(var.threads), args, 0, (hipStream_t)stream);
   return err == hipSuccess ? VA_OK : VA_ERR_LAUNCH;
 }
 

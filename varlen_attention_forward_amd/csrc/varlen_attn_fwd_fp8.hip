@@ -692,7 +692,7 @@ static Variant fp8_variant_t(int mode) {
   const void* fn = mode == kPackHeads      ? (const void*)&attn_fwd_fp8<DQK, DV, kPackHeads>
                    : mode == kPackSegments ? (const void*)&attn_fwd_fp8<DQK, DV, kPackSegments>
                                            : (const void*)&attn_fwd_fp8<DQK, DV, kPackNone>;
-  return {fn, C::LDS_BYTES, C::BM, fp8k::kBN, C::THREADS, "attn_fwd_fp8", 1};
+  return {fn, C::LDS_BYTES, C::BM, fp8k::kBN, C::THREADS, "attn_fwd_fp8", 1, 1};
 }
 
 Variant fp8_variant(int dqk, int dv, int pack_mode) {

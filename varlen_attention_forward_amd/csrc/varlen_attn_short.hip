@@ -15,8 +15,10 @@
 //   V tile: HBM -> one of two private LDS stages by direct-to-LDS loads, for
 //       the transposing reads (ds_read_b64_tr_b16) that form the V^T operand.
 //
-// Eight such workgroups share a CU (256 registers a wave, 12 KB of LDS at
-// d_v 80).  SGLang PR #41344, "Speed Tests and Profiling" ("Where fa4
+// A workgroup holds four such waves, each on its own unit, sharing nothing
+// but the launch (one-wave workgroups left the dispatcher the bottleneck:
+// 64-token windows ran 11% slower); two workgroups share a CU (256
+// registers a wave, 2 x 6 KB of LDS a wave at d_v 80).  SGLang PR #41344, "Speed Tests and Profiling" ("Where fa4
 // loses" (b)), asks for a smaller query tile for short segments; this is it.
 //
 // The arithmetic on each 32-key tile is the four-wave kernel's per wave,
@@ -31,6 +33,7 @@ namespace va {
 namespace narrow {
 constexpr int kBN = 32;      // keys per tile
 constexpr int kStages = 2;   // tile t: K in register set t % 2, V in LDS stage t % 2
+constexpr int kWaves = 4;    // waves (independent work units) per workgroup
 template <int DQK, int DV>
 struct Cfg : TileGeom<DQK, DV, kBN> {
   static constexpr int QB = 2;         // 32-row query blocks of the wave
@@ -42,23 +45,27 @@ struct Cfg : TileGeom<DQK, DV, kBN> {
 }  // namespace narrow
 
 template <int DQK, int DV, RowSum SUM>
-__global__ __launch_bounds__(64, 2) void attn_fwd_short(Params p) {
+__global__ __launch_bounds__(64 * narrow::kWaves, 2) void attn_fwd_short(Params p) {
   using namespace narrow;
   using C = Cfg<DQK, DV>;
   constexpr int QB = C::QB;
   constexpr bool SUM_BY_MFMA = SUM == RowSum::kMfma;
   static_assert(!SUM_BY_MFMA || C::V_PAD > 0, "the ones column needs a padded d_v");
-  __shared__ __attribute__((aligned(4096))) char vs0[C::V_TILE];
-  __shared__ __attribute__((aligned(4096))) char vs1[C::V_TILE];
-  auto vst = [&](auto st) VA_INLINE -> lds_char* {
-    if constexpr (decltype(st)::value % 2 == 0) return (lds_char*)vs0;
-    else return (lds_char*)vs1;
+  __shared__ __attribute__((aligned(4096))) char vs0[kWaves * C::V_TILE];
+  __shared__ __attribute__((aligned(4096))) char vs1[kWaves * C::V_TILE];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  auto vst = [&](auto st) VA_INLINE -> lds_char* {  // this wave's stage st
+    if constexpr (decltype(st)::value % 2 == 0) return (lds_char*)vs0 + wave * C::V_TILE;
+    else return (lds_char*)vs1 + wave * C::V_TILE;
   };
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
-  const BlockWork bw = block_work<kPackNone>(p, lane, C::RPW, (int64_t)blockIdx.x);
+  // This wave's work unit: workgroup w's wave v takes unit ((w >> 3) kWaves
+  // + v) x 8 + (w & 7), on the XCD (w % 8) the unit's dealing intends.
+  const int64_t unit = ((int64_t)(blockIdx.x >> 3) * kWaves + wave) * 8 + (blockIdx.x & 7);
+  const BlockWork bw = block_work<kPackNone>(p, lane, C::RPW, unit);
   if (!bw.u.valid) return;
   const int h = bw.u.h;
   const int q0 = bw.q0, Lq = bw.lq, k0 = bw.k0, Lk = bw.lk;
@@ -465,8 +472,8 @@ bool short_supported(int dqk, int dv) {
 template <int DQK, int DV, RowSum SUM>
 static Variant short_variant_of() {
   using C = narrow::Cfg<DQK, DV>;
-  return {(const void*)&attn_fwd_short<DQK, DV, SUM>, narrow::kStages * C::V_TILE, C::RPW, narrow::kBN, 64,
-          "attn_fwd_short", 8};
+  return {(const void*)&attn_fwd_short<DQK, DV, SUM>, narrow::kStages * narrow::kWaves * C::V_TILE, C::RPW,
+          narrow::kBN, 64 * narrow::kWaves, "attn_fwd_short", 2, narrow::kWaves};
 }
 
 // `lse`: whether the caller asked for the LSE (d_v 72 / 80 without one sum

@@ -507,10 +507,11 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   // raw scores as before.  The row sums go to sum[], committed by the caller
   // only if the check passed.
   //
-  // Its VALU work is 48 or 64 units in dependency order: (16 row-max steps,
-  // 8 per query block, on the raw scores, kMfma only), (32 scale-and-shift
-  // FMAs, head dims <= 80,) 32 in-place exps, 16 packs (+ sums).  The MFMAs (PV of the previous tile, then QK^T of the
-  // next, two per LDS operand) each get an even share of the units, in
+  // Its VALU work is 80 or 96 units in dependency order: (16 row-max steps,
+  // 8 per query block, on the raw scores, kMfma only), 32 scale-and-shift
+  // FMAs, 32 in-place exps, 16 packs (+ sums).  The MFMAs (PV of the
+  // previous tile, then QK^T of the next, two per LDS operand) each get an
+  // even share of the units, in
   // source order pinned by scheduling barriers: the compiler's own schedule
   // bunches the MFMAs, and an MFMA hides only a few VALU ops behind it.  The
   // packs, which overwrite the probabilities PV reads, all fall after the
@@ -520,11 +521,10 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
     constexpr bool kMaxCheck = SUM_BY_MFMA;
     constexpr int QB = C::QB;
     constexpr int kPVOps = 2 * C::VB, kOps = kPVOps + C::KC, kSlots = QB * kOps;
-    // With two waves per SIMD (head dims <= 80) the scale-and-shift FMAs run
-    // as units of their own, all before the exps (measured +1% on the ViT
-    // batch, bit-identical); one wave per SIMD keeps each FMA with its exp.
-    constexpr bool kSplitExp = DQK <= 80;
-    constexpr int kMaxU = 8 * QB, kFmaU = kSplitExp ? 16 * QB : 0, kExpU = 16 * QB, kPackU = 8 * QB;  // units per kind
+    // The scale-and-shift FMAs run as units of their own, all before the
+    // exps, rather than each with its exp (measured +1% on the ViT batch and
+    // the MLA prefill, +0.4% on d 128, bit-identical).
+    constexpr int kMaxU = 8 * QB, kFmaU = 16 * QB, kExpU = 16 * QB, kPackU = 8 * QB;  // units per kind
     constexpr int kUnits = (kMaxCheck ? kMaxU : 0) + kFmaU + kExpU + kPackU;
     static_assert((kUnits - kPackU) * kSlots / kUnits >= QB * kPVOps, "packs must follow the PV MFMAs");
     float m[QB];
@@ -550,8 +550,7 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
         s[qb][r] = fmaf(s[qb][r], p.scale_log2, nm[qb]);
       } else if constexpr (u < kMaxU + kFmaU + kExpU) {  // p = exp2(s * scale - m_run), in place
         constexpr int qb = (u - kMaxU - kFmaU) / 16, r = (u - kMaxU - kFmaU) % 16;
-        s[qb][r] = kSplitExp ? __builtin_amdgcn_exp2f(s[qb][r])
-                             : __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, nm[qb]));
+        s[qb][r] = __builtin_amdgcn_exp2f(s[qb][r]);
       } else {  // bf16 pack (and row sum)
         constexpr int i = u - kMaxU - kFmaU - kExpU, qb = i / 8, t = (i / 4) % 2, e = i % 4, r = 8 * t + 2 * e;
         constexpr bool first = t == 0 && e == 0;

@@ -31,6 +31,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import struct
 import json
 import os
 import sys
@@ -46,22 +47,54 @@ PEAK_FP8_TFLOPS = 5000.0  # dense e4m3 MFMA, the roofline of the fp8 workloads
 PEAK_HBM_GBS = 8000.0
 RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # 312.5
 DEFAULT_WORKLOAD = "vit_full_d80"
-KERNEL_SOURCES = [
-    os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "varlen_attn_fwd.hip"),
-    os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "varlen_attn_fwd_fp8.hip"),
-    os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "varlen_attn_short.hip"),
-    os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "merge_states.hip"),
-    os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "attn_common.h"),
-    os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "wide_tile.h"),
-    os.path.join(ROOT, "varlen_attention_forward_amd", "csrc", "tile_schedule.h"),
-]
+def _elf_sections(data: bytes, base: int = 0) -> dict:
+    """Section name -> (file offset, size) of the little-endian ELF64 image at data[base:]."""
+    if data[base:base + 4] != b"\x7fELF" or data[base + 4] != 2 or data[base + 5] != 1:
+        raise ValueError("not a little-endian ELF64 image")
+    shoff, = struct.unpack_from("<Q", data, base + 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, base + 0x3A)
+    hdrs = [struct.unpack_from("<IIQQQQ", data, base + shoff + i * shentsize) for i in range(shnum)]
+    strtab = base + hdrs[shstrndx][4]
+    out = {}
+    for name_off, _typ, _flags, _addr, off, size in hdrs:
+        end = data.index(b"\0", strtab + name_off)
+        out[data[strtab + name_off:end].decode()] = (base + off, size)
+    return out
 
 
-def kernel_source_hash() -> str:
+def kernel_code_hash(lib_path: str = None) -> str:
+    """First 16 hex digits of the sha256 of the library's gfx950 machine code: the
+    .text and .rodata sections of every gfx950 code object in the clang offload
+    bundles of its .hip_fatbin section, in order.  Comments, host code and
+    symbol tables do not enter it, so a traffic record stays valid exactly as
+    long as the kernels it was taken on are the ones that run."""
+    if lib_path is None:
+        from varlen_attention_forward_amd import _binding
+        lib_path = _binding.LIB_PATH
+    with open(lib_path, "rb") as f:
+        data = f.read()
+    off, size = _elf_sections(data)[".hip_fatbin"]
+    fat = data[off:off + size]
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+    n_code = 0
+    pos = fat.find(magic)
+    while pos >= 0:
+        entries, = struct.unpack_from("<Q", fat, pos + len(magic))
+        q = pos + len(magic) + 8
+        for _ in range(entries):
+            eoff, esize, tlen = struct.unpack_from("<QQQ", fat, q)
+            triple = fat[q + 24:q + 24 + tlen].decode()
+            q += 24 + tlen
+            if triple.endswith("gfx950") and esize > 0:
+                secs = _elf_sections(fat, pos + eoff)
+                for name in (".text", ".rodata"):
+                    so, sz = secs[name]
+                    h.update(fat[so:so + sz])
+                n_code += 1
+        pos = fat.find(magic, pos + 1)
+    if n_code == 0:
+        raise ValueError("no gfx950 code object in %s" % lib_path)
     return h.hexdigest()[:16]
 
 
@@ -107,13 +140,13 @@ def algorithmic_bytes(w) -> float:
 
 def load_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the kernel source changed since the counters were taken."""
+    None when the kernels' machine code changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha") != kernel_source_hash():
+    if t.get("kernel_code_sha") != kernel_code_hash():
         return None
     return float(t["hbm_bytes_per_launch"])
 

@@ -1,6 +1,8 @@
 """Host-side logic of bench.py: FLOP and byte counts, the roofline choice and
 the single-GPU guard.  No GPU needed."""
+import json
 import os
+import struct
 import subprocess
 import sys
 
@@ -98,3 +100,44 @@ def test_oracle_task_pairs_add_up(lq, lk, causal, window):
 def test_host_info_reports_core_counts():
     info = bench.host_info()
     assert info["cpu_count"] >= 1 and 1 <= info["affinity"] <= info["cpu_count"]
+
+
+def test_kernel_code_hash_reads_the_built_machine_code(tmp_path):
+    """Traffic records are keyed by a hash of the library's gfx950 machine
+    code (.text and .rodata of each code object in the offload bundles): the
+    built library yields one, the same on every read, and a record carrying
+    another hash is treated as stale."""
+    from varlen_attention_forward_amd import _binding
+    h = bench.kernel_code_hash(_binding.LIB_PATH)
+    assert len(h) == 16 and int(h, 16) >= 0
+    assert bench.kernel_code_hash(_binding.LIB_PATH) == h
+    # a copy whose machine code differs in one byte of .text hashes differently
+    data = bytearray(open(_binding.LIB_PATH, "rb").read())
+    off, size = bench._elf_sections(bytes(data))[".hip_fatbin"]
+    fat = bytes(data[off:off + size])
+    pos = fat.find(b"__CLANG_OFFLOAD_BUNDLE__")
+    n, = struct.unpack_from("<Q", fat, pos + 24)
+    q = pos + 32
+    for _ in range(n):
+        eoff, esize, tlen = struct.unpack_from("<QQQ", fat, q)
+        triple = fat[q + 24:q + 24 + tlen].decode()
+        q += 24 + tlen
+        if triple.endswith("gfx950") and esize > 0:
+            text_off, _ = bench._elf_sections(fat, pos + eoff)[".text"]
+            data[off + text_off] ^= 0xFF
+            break
+    mod = tmp_path / "mod.so"
+    mod.write_bytes(bytes(data))
+    assert bench.kernel_code_hash(str(mod)) != h
+
+
+def test_stale_traffic_record_reads_as_null(tmp_path, monkeypatch):
+    """load_traffic returns the record's bytes only while its hash matches."""
+    rec = {"kernel_code_sha": "0" * 16, "hbm_bytes_per_launch": 123}
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "traffic_x.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_code_hash", lambda lib_path=None: "0" * 16)
+    assert bench.load_traffic("x") == 123.0
+    monkeypatch.setattr(bench, "kernel_code_hash", lambda lib_path=None: "1" * 16)
+    assert bench.load_traffic("x") is None

@@ -5,8 +5,8 @@
 // The four-wave kernel can only give such a segment one wave of a shared
 // workgroup: the workgroup then streams four segments' keys behind common
 // barriers, and in each tile step only the wave whose segment owns the tile
-// computes.  Here a workgroup is one wave, which streams its own segment's
-// keys and meets no barrier:
+// computes.  Here each wave is a work unit of its own, which streams its
+// segment's keys and meets no barrier:
 //
 //   K tile: HBM -> registers directly.  The A operand of S^T = K Q^T on
 //       v_mfma_f32_32x32x16_bf16 is, per lane, 16 contiguous bytes of one key
@@ -18,8 +18,9 @@
 // A workgroup holds four such waves, each on its own unit, sharing nothing
 // but the launch (one-wave workgroups left the dispatcher the bottleneck:
 // 64-token windows ran 11% slower); two workgroups share a CU (256
-// registers a wave, 2 x 6 KB of LDS a wave at d_v 80).  SGLang PR #41344, "Speed Tests and Profiling" ("Where fa4
-// loses" (b)), asks for a smaller query tile for short segments; this is it.
+// registers a wave, 2 x 6 KB of LDS a wave at d_v 80).  SGLang PR #41344,
+// "Speed Tests and Profiling" ("Where fa4 loses" (b)), asks for a smaller
+// query tile for short segments; this is it.
 //
 // The arithmetic on each 32-key tile is the four-wave kernel's per wave,
 // step for step: the same tiles (they start at the segment's first key), the
@@ -37,7 +38,7 @@ constexpr int kWaves = 4;    // waves (independent work units) per workgroup
 template <int DQK, int DV>
 struct Cfg : TileGeom<DQK, DV, kBN> {
   static constexpr int QB = 2;         // 32-row query blocks of the wave
-  static constexpr int RPW = 32 * QB;  // query rows per workgroup
+  static constexpr int RPW = 32 * QB;  // query rows per wave (one work unit)
   static constexpr int V_PAD = Cfg::CPR_V - Cfg::V_REAL;
   static_assert(2 * Cfg::KC + Cfg::V_WL < 64, "vmcnt range");
   static_assert(Cfg::CPR_V != 12 || v_swizzle<12>(1) == 0, "pad chunks sit at fixed positions");
@@ -267,11 +268,6 @@ __global__ __launch_bounds__(64 * narrow::kWaves, 2) void attn_fwd_short(Params 
     }
     return move;
   };
-  // One tile: scores, mask, the fast path (p against the running max as it
-  // stands, valid when every p <= 2^kRescaleTau and no row meets its first
-  // key: tested on the raw row max with the ones-column sum, on the row sums
-  // and first tiles with the fp32 sum), else the slow path with the rescale;
-  // then O^T += V^T P^T.
   // The full softmax step with its rescale (the slow path).
   auto slow = [&](f32x16 (&s)[QB]) VA_INLINE {
     float alpha[QB];
@@ -286,9 +282,11 @@ __global__ __launch_bounds__(64 * narrow::kWaves, 2) void attn_fwd_short(Params 
           for (int r = 0; r < 16; ++r) acc[vb][qb][r] *= alpha[qb];
     }
   };
-  // The wave's first tile holds some row's first visible key, so the fast
-  // path cannot hold there: it takes the full softmax at once (FIRST), with
-  // no fast-path work to discard and no scores to recompute.
+  // One tile: scores, mask, the fast path or the slow path, then
+  // O^T += V^T P^T.  The wave's first tile holds some row's first visible
+  // key, so the fast path cannot hold there: it takes the full softmax at
+  // once (FIRST), with no fast-path work to discard and no scores to
+  // recompute.
   auto tile = [&](auto st, int j, auto first) VA_INLINE {
     constexpr int S = decltype(st)::value;
     f32x16 s[QB];
@@ -297,64 +295,64 @@ __global__ __launch_bounds__(64 * narrow::kWaves, 2) void attn_fwd_short(Params 
     if constexpr (decltype(first)::value) {
       slow(s);
     } else {
-    // The fast path: p = exp2(s * scale * log2(e) - m_run) in place, packed
-    // to bf16 (and summed in pairs with the fp32 sum), valid when every p <=
-    // 2^kRescaleTau and no row meets its first visible key: tested on the
-    // raw row maxima with the ones-column sum, on the tile's row sums and the
-    // rows' first tiles with the fp32 sum.
-    bool bad = false;
-    if constexpr (SUM_BY_MFMA) {
+      // The fast path: p = exp2(s * scale * log2(e) - m_run) in place, packed
+      // to bf16 (and summed in pairs with the fp32 sum), valid when every p <=
+      // 2^kRescaleTau and no row meets its first visible key: tested on the
+      // raw row maxima with the ones-column sum, on the tile's row sums and the
+      // rows' first tiles with the fp32 sum.
+      bool bad = false;
+      if constexpr (SUM_BY_MFMA) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          float m = fmaxf(fmaxf(s[qb][0], s[qb][1]), s[qb][2]);
+#pragma unroll
+          for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, s[qb][r]), s[qb][r + 1]);
+          m = fmaxf(m, s[qb][15]);
+          bad |= m * p.scale_log2 > lim[qb];
+        }
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) bad |= j == first_j[qb];
+      }
+      float sum[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        float m = fmaxf(fmaxf(s[qb][0], s[qb][1]), s[qb][2]);
 #pragma unroll
-        for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, s[qb][r]), s[qb][r + 1]);
-        m = fmaxf(m, s[qb][15]);
-        bad |= m * p.scale_log2 > lim[qb];
-      }
-    } else {
+        for (int t = 0; t < 2; ++t) {
+          u32x4 pk;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) bad |= j == first_j[qb];
-    }
-    float sum[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 8 * t + 2 * e;
-          s[qb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, nm[qb]));
-          s[qb][r + 1] = __builtin_amdgcn_exp2f(fmaf(s[qb][r + 1], p.scale_log2, nm[qb]));
-          pk[e] = pack_bf16x2(s[qb][r], s[qb][r + 1]);
-          if constexpr (!SUM_BY_MFMA) {
-            const float pair = s[qb][r] + s[qb][r + 1];
-            sum[qb] = (t == 0 && e == 0) ? pair : sum[qb] + pair;
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * t + 2 * e;
+            s[qb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, nm[qb]));
+            s[qb][r + 1] = __builtin_amdgcn_exp2f(fmaf(s[qb][r + 1], p.scale_log2, nm[qb]));
+            pk[e] = pack_bf16x2(s[qb][r], s[qb][r + 1]);
+            if constexpr (!SUM_BY_MFMA) {
+              const float pair = s[qb][r] + s[qb][r + 1];
+              sum[qb] = (t == 0 && e == 0) ? pair : sum[qb] + pair;
+            }
           }
+          pf[qb][t] = __builtin_bit_cast(bf16x8, pk);
         }
-        pf[qb][t] = __builtin_bit_cast(bf16x8, pk);
+        if constexpr (!SUM_BY_MFMA) bad |= !(sum[qb] <= kSumLimit);
       }
-      if constexpr (!SUM_BY_MFMA) bad |= !(sum[qb] <= kSumLimit);
-    }
-    // Commit the row sums on one path; the slow path restores them.
-    float l_prev[QB];
+      // Commit the row sums on one path; the slow path restores them.
+      float l_prev[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      l_prev[qb] = l_run[qb];
-      if constexpr (!SUM_BY_MFMA) l_run[qb] += sum[qb];
-    }
-    if (__any(bad)) {
-      // Some row's max moved past m_run + kRescaleTau (or a row met its
-      // first key): recompute the scores from K, still in registers, and take
-      // the full softmax with the rescale.
-      asm volatile("; softmax slow path" ::: "memory");
+      for (int qb = 0; qb < QB; ++qb) {
+        l_prev[qb] = l_run[qb];
+        if constexpr (!SUM_BY_MFMA) l_run[qb] += sum[qb];
+      }
+      if (__any(bad)) {
+        // Some row's max moved past m_run + kRescaleTau (or a row met its
+        // first key): recompute the scores from K, still in registers, and take
+        // the full softmax with the rescale.
+        asm volatile("; softmax slow path" ::: "memory");
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) l_run[qb] = l_prev[qb];
-      qk(kf[S], s);
-      mask(j, s);
-      slow(s);
-    }
+        for (int qb = 0; qb < QB; ++qb) l_run[qb] = l_prev[qb];
+        qk(kf[S], s);
+        mask(j, s);
+        slow(s);
+      }
     }
     // K of tile j + 2 into this register set, then V of this tile landed:
     // only K j + 1, V j + 1 and K j + 2 (those that exist) may be in flight.

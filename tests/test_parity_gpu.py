@@ -862,3 +862,58 @@ def test_split_kv_dynamic_counts_short_queries(dims):
                                       return_lse=True, num_splits=8, num_splits_dynamic=dyn)
         torch.cuda.synchronize()
         assert_parity(out, lse, ref_o, ref_lse, what="dyn short %s %s" % (dims, counts))
+
+
+def test_concurrent_streams_bit_equal():
+    """Calls on different HIP streams at once share nothing: a short-segment
+    (one-wave kernel) call, a causal d 128 call, a split-KV 192/128 call
+    with its own workspace and a merge, each launched three times on its own
+    stream (default priority) and interleaved, give outputs bit-equal to the
+    same calls run one after another on the default stream."""
+    short = [64, 17, 64, 40] * 6
+    cases = [
+        workloads.make_inputs(short, short, 8, 80, 80, seed=501),
+        workloads.make_inputs([700, 300, 1029], [700, 300, 1029], 4, 128, 128, seed=502, causal=True),
+        workloads.make_inputs([256, 64], [5000, 3000], 4, 192, 128, seed=503, causal=True),
+    ]
+    dev = [c.to(DEV) for c in cases]
+    splits = [1, 1, 4]
+
+    def call(i, out, lse):
+        d = dev[i]
+        return va.varlen_attn_fwd(d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, d.max_seqlen_q, d.max_seqlen_k,
+                                  softmax_scale=d.softmax_scale, causal=d.causal, window_size=d.window,
+                                  out=out, return_lse=True, lse=lse, num_splits=splits[i])
+
+    def buffers(i):
+        d = dev[i]
+        out = torch.full((d.q.shape[0], d.q.shape[1], d.v.shape[2]), 7.0, dtype=torch.bfloat16, device=DEV)
+        lse = torch.full((d.q.shape[1], d.q.shape[0]), 7.0, dtype=torch.float32, device=DEV)
+        return out, lse
+
+    ref = []
+    for i in range(len(cases)):
+        out, lse = buffers(i)
+        call(i, out, lse)
+        ref.append((out, lse))
+    # the merge of case 2 with itself: O unchanged, LSE + ln 2
+    m_ref = va.varlen_attn_merge(ref[2][0], ref[2][1], ref[2][0], ref[2][1])
+    torch.cuda.synchronize()
+
+    streams = [torch.cuda.Stream() for _ in range(len(cases) + 1)]
+    bufs = [[buffers(i) for _ in range(3)] for i in range(len(cases))]
+    merged = []
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, s in enumerate(streams[:-1]):
+            with torch.cuda.stream(s):
+                call(i, *bufs[i][rep])
+        with torch.cuda.stream(streams[-1]):
+            merged.append(va.varlen_attn_merge(ref[2][0], ref[2][1], ref[2][0], ref[2][1]))
+    torch.cuda.synchronize()
+    for i in range(len(cases)):
+        for rep in range(3):
+            out, lse = bufs[i][rep]
+            assert torch.equal(out, ref[i][0]) and torch.equal(lse, ref[i][1]), (i, rep)
+    for o, l in merged:
+        assert torch.equal(o, m_ref[0]) and torch.equal(l, m_ref[1])

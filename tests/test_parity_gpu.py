@@ -593,18 +593,32 @@ def test_packed_short_segments_with_split_kv_and_grouped_heads():
         assert_parity(out, lse, ref_o, ref_lse, what="packed split %d" % splits)
 
 
-def test_hip_graph_replay_matches_eager():
-    """The call enqueues one kernel and nothing else, so it can be captured in a
-    HIP graph: three replays, with eager calls between them, reproduce the
-    eager O and LSE bit for bit (outputs cleared outside the graph first)."""
-    inp = workloads.make_inputs([300, 77, 1029], [300, 500, 1029], 2, 128, 128, seed=21, causal=True)
+GRAPH_CASES = {
+    "wide_d128_causal": (([300, 77, 1029], [300, 500, 1029], 2, 128, 128), dict(seed=21, causal=True), 1),
+    "short_d80_windows": (([64, 17, 64, 40, 0, 64] * 4, [64, 17, 64, 40, 0, 64] * 4, 4, 80, 80), dict(seed=22), 1),
+    "split4_192_128": (([256, 64], [5000, 3000], 2, 192, 128), dict(seed=23, causal=True), 4),
+}
+
+
+@pytest.mark.parametrize("case", list(GRAPH_CASES))
+def test_hip_graph_replay_matches_eager(case):
+    """The call enqueues its kernel launches and nothing else (one kernel, or
+    with split-KV the kernel and the combine, the workspace taken from the
+    graph's memory pool), so it can be captured in a HIP graph: three
+    replays, with eager calls between them, reproduce the eager O and LSE bit
+    for bit (outputs cleared outside the graph first), for the four-wave
+    kernel, the one-wave short-segment kernel and a split-KV call."""
+    args, kw, splits = GRAPH_CASES[case]
+    inp = workloads.make_inputs(*args, **kw)
     d = inp.to(DEV)
+    heads, dv = args[2], args[4]
 
     def call(out, lse):
         va.varlen_attn_fwd(d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, d.max_seqlen_q, d.max_seqlen_k,
-                           softmax_scale=d.softmax_scale, causal=d.causal, out=out, return_lse=True, lse=lse)
+                           softmax_scale=d.softmax_scale, causal=d.causal, out=out, return_lse=True, lse=lse,
+                           num_splits=splits)
 
-    shape_o, shape_l = (d.q.shape[0], 2, 128), (2, d.q.shape[0])
+    shape_o, shape_l = (d.q.shape[0], heads, dv), (heads, d.q.shape[0])
     out_e = torch.empty(shape_o, dtype=torch.bfloat16, device=DEV)
     lse_e = torch.empty(shape_l, dtype=torch.float32, device=DEV)
     call(out_e, lse_e)

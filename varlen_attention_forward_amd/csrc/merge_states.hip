@@ -155,26 +155,67 @@ __global__ __launch_bounds__(256) void combine_splits(CombineParams p) {
     splits = min(max(p.splits_dyn[lo], 1), p.splits);
   }
   const int64_t plane = p.rows * p.heads;  // (row, head) pairs per split
+  // Lane c of the group reads the LSE of split s0 + c, and the group's
+  // lanes pass them round (__shfl within the group), so each LSE is loaded
+  // once rather than by every lane in every pass.  The arithmetic is the
+  // same in every lane and in split order: the max, then the sum of
+  // exp(lse - max), then the weighted O; a split past the row's count
+  // contributes an LSE of -inf, whose exp(-inf - max) = 0 leaves the sum as
+  // it was.  The loops run to the launch's split count, the same for every
+  // lane of the wave.  The partial O loads of eight splits are issued
+  // before any is used.
+  const int G = 1 << p.lane_shift;
+  const float* lse_row = p.part_lse + (int64_t)h * p.rows + i;
+  auto lse_chunk = [&](int s0) {  // this lane's LSE of split s0 + c
+    return s0 + c < splits ? lse_row[(int64_t)(s0 + c) * plane] : -INFINITY;
+  };
   float m = -INFINITY;
-  for (int s = 0; s < splits; ++s) m = fmaxf(m, p.part_lse[(int64_t)s * plane + (int64_t)h * p.rows + i]);
+  for (int s0 = 0; s0 < p.splits; s0 += G) {
+    const float mine = lse_chunk(s0);
+    const int n = min(G, p.splits - s0);
+    for (int k = 0; k < n; ++k) m = fmaxf(m, __shfl(mine, k, G));
+  }
   float sum = 0.f;
-  if (m != -INFINITY)
-    for (int s = 0; s < splits; ++s) sum += expf(p.part_lse[(int64_t)s * plane + (int64_t)h * p.rows + i] - m);
-  if (4 * c < p.dim) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (m != -INFINITY) {
-      const float inv = 1.f / sum;
-      for (int s = 0; s < splits; ++s) {
-        const float w = expf(p.part_lse[(int64_t)s * plane + (int64_t)h * p.rows + i] - m) * inv;
-        // A split with weight 0 (no key, or negligible) is skipped, not
-        // scaled: its O is never read into the sum.
-        if (w > 0.f) {
-          const f32x4 x = __builtin_nontemporal_load(
-              (const f32x4*)(p.part_o + ((int64_t)s * plane + i * p.heads + h) * p.dim + 4 * c));
-          acc += w * x;
-        }
-      }
+  for (int s0 = 0; s0 < p.splits; s0 += G) {
+    const float mine = lse_chunk(s0);
+    const int n = min(G, p.splits - s0);
+    for (int k = 0; k < n; ++k) {
+      const float l = __shfl(mine, k, G);
+      if (m != -INFINITY && s0 + k < splits) sum += expf(l - m);
     }
+  }
+  // (Every lane runs the loops, so each __shfl reads lanes that take part;
+  // lanes past the head dim only skip the loads.)
+  const bool cols = 4 * c < p.dim;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const float inv = m != -INFINITY ? 1.f / sum : 0.f;
+  constexpr int kC = 8;
+  for (int s0 = 0; s0 < p.splits; s0 += G) {
+    const float mine = lse_chunk(s0);
+    const int n = min(G, p.splits - s0);
+    for (int k0 = 0; k0 < n; k0 += kC) {
+      float w[kC];
+      f32x4 x[kC];
+#pragma unroll
+      for (int k = 0; k < kC; ++k) {
+        const float l = __shfl(mine, min(k0 + k, G - 1), G);
+        w[k] = (m != -INFINITY && k0 + k < n && s0 + k0 + k < splits) ? expf(l - m) * inv : 0.f;
+      }
+      // A split with weight 0 (no key, or negligible) is skipped, not
+      // scaled: its O is never read into the sum.
+#pragma unroll
+      for (int k = 0; k < kC; ++k) {
+        x[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (cols && w[k] > 0.f)
+          x[k] = __builtin_nontemporal_load(
+              (const f32x4*)(p.part_o + ((int64_t)(s0 + k0 + k) * plane + i * p.heads + h) * p.dim + 4 * c));
+      }
+#pragma unroll
+      for (int k = 0; k < kC; ++k)
+        if (w[k] > 0.f) acc += w[k] * x[k];
+    }
+  }
+  if (cols) {
     if (p.out_scale != nullptr) {
       const uint32_t code = va::quant_e4m3x4(acc[0], acc[1], acc[2], acc[3], 1.f / *p.out_scale);
       *(uint32_t*)((uint8_t*)p.o + i * p.o_row + h * p.o_head + 4 * c) = code;

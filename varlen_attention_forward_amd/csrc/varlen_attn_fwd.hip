@@ -28,9 +28,10 @@
 // Variations on the same workgroup: grouped KV heads (query head h reads KV
 // head h / (H / H_kv)); short segments packed four or two to a workgroup,
 // one or two waves each, sharing the workgroup's key tiles (segments of at
-// most 64 / 128 queries); and split-KV, where a workgroup visits one run of
-// its key tiles and writes an fp32 partial that combine_splits
-// (merge_states.hip) reduces.
+// most 64 / 128 queries; at most 64 with head dims <= 80 go to the
+// short-segment kernel of varlen_attn_short.hip instead); and split-KV,
+// where a workgroup visits one run of its key tiles and writes an fp32
+// partial that combine_splits (merge_states.hip) reduces.
 //
 // Where the pages describe FA4 on Blackwell (TMEM, tcgen05.ld.red row max,
 // 2-CTA MMA) that design is prior art only; what carries over is the online
@@ -860,8 +861,9 @@ static Variant variant_for(int dqk, int dv, int32_t pk, bool lse = true) {
 
 // The kernel and fill mode of a bf16 launch.  Segments of at most 64
 // queries that would be packed four to a workgroup (no grouped query heads
-// to pack instead) take the one-wave short-segment kernel, one workgroup per
-// (segment, head), when the head dims have it and the call is not split.
+// to pack instead) take the short-segment kernel, one wave per (segment,
+// head), four such units a workgroup, when the head dims have it and the
+// call is not split.
 struct LaunchChoice {
   Variant var;
   int32_t mode;

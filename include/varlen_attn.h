@@ -377,7 +377,10 @@ int varlen_attn_tile_range(int32_t seqlen_q, int32_t seqlen_k, int32_t row_begin
  * work unit (va_plan.units of them, four to a workgroup).  Segments of different lengths (at most 64
  * of them) are dealt longest key length first; otherwise in packing order;
  * either way every odd quad of each XCD's dispatch order is reversed.
- * Segments of at most 64 queries with head dims <= 80 (and no grouped query
+ * When va_plan.pair_q_tiles is 1, the workgroup runs q-tile `q_tile` and
+ * then q-tile n_b - 1 - q_tile of the same (segment, head) if that is
+ * another one (n_b = ceil(seqlen_q / block_m)); q_tile is the later, longer
+ * one.  Segments of at most 64 queries with head dims <= 80 (and no grouped query
  * heads to pack instead) run one wave per (segment, head) on the
  * short-segment kernel (va_plan.kernel "attn_fwd_short", block_m 64): q-tile
  * 0 of each, a segment's heads dealt to one XCD in groups of up to 16.  When
@@ -416,6 +419,10 @@ typedef struct va_plan {
                                  FA4's pack_gqa, SGLang PR #41344 "Accuracy Tests") */
   int64_t units;              /* work units (varlen_attn_work_unit's blocks), padding included:
                                  grid, or 4 per workgroup for attn_fwd_short */
+  int32_t pair_q_tiles;       /* 1 when each work unit runs two q-tiles of one segment, n_b - 1 - t
+                                 and then t (n_b = ceil(seqlen_q / block_m)), so that every unit
+                                 of a causal launch sees the same number of key tiles: causal,
+                                 max_seqlen_q > block_m, unpacked, attn_fwd_wide, unsplit */
 } va_plan;
 
 int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch, int32_t num_heads,

@@ -366,6 +366,11 @@ def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
         return
     n_qt = -(-max_q // bm)
     longest_first = batch <= 64 and len(set(zip(lq, lk))) > 1
+    # causal launches of the one-workgroup-per-CU head dims: a unit runs
+    # q-tile qt and then n_b - 1 - qt, so every unit has n_b + 1 key tiles
+    pair = p["pair_q_tiles"] == 1
+    assert pair == (bool(causal) and dims[0] > 80 and max_q > bm and pack == 1)
+    n_units_qt = (n_qt + 1) // 2 if pair else n_qt
     # tiles each segment must get: its own q-tiles when dealt longest first,
     # else the same number for every segment (tiles past its end exit early)
     want = {(b, h, qt) for b in range(batch) for h in range(heads)
@@ -374,15 +379,23 @@ def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
     rank = {b: r for r, b in enumerate(rank)}
     seen = {}
     order = [[] for _ in range(8)]  # per XCD, owners in dispatch order
+    valid = 0
     for blk in range(p["units"]):
         b, h, qt = pkg.work_unit(blk, heads, dims[0], dims[1], lq, lk, causal)
         if b < 0:
             assert h == -1 and qt == -1
             continue
-        key = (b, h, qt)
-        assert key in want, key
-        assert key not in seen, (blk, key, seen.get(key))
-        seen[key] = blk
+        valid += 1
+        tiles = [qt]
+        if pair:
+            nb = -(-lq[b] // bm)
+            assert 2 * qt >= nb - 1  # the later tile of the two is reported
+            tiles += [nb - 1 - qt] if nb - 1 - qt != qt else []
+        for t in tiles:
+            key = (b, h, t)
+            assert key in want, key
+            assert key not in seen, (blk, key, seen.get(key))
+            seen[key] = blk
         order[blk % 8].append((blk >> 3, b))
         # (segment, head group) groups are dealt round-robin over the 8 XCDs
         # (block % 8); a group's 2^hs heads run on one XCD
@@ -399,8 +412,8 @@ def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
             ks = sorted(quads)
             assert all(min(quads[a]) >= max(quads[c]) for a, c in zip(ks, ks[1:]))
     else:
-        assert p["units"] - len(want) < (8 * n_qt) << hs
-    if causal:
+        assert p["units"] - valid < (8 * n_units_qt) << hs
+    if causal and not pair:
         # within a group, one of the four q-tiles with the most keys is
         # dispatched first
         first = {}
@@ -442,14 +455,22 @@ def test_work_unit_grouped_kv_heads(heads, heads_k, lq):
 def test_work_unit_snake_balances_engines(batch, heads, max_q, causal):
     """The k-th workgroup of an XCD goes to shader engine (k + c) % 4; over
     every aligned run of 8 dispatch slots the four engines get equal key
-    counts (each q-tile's keys, causal: (qt + 1) x 256)."""
+    counts (each q-tile's keys, causal: (qt + 1) x 256, a pair of q-tiles
+    qt and n_b - 1 - qt together: (n_b + 1) x 256)."""
     p = pkg.plan(192, 128, batch, heads, max_q, max_q, causal)
+    n_b = -(-max_q // p["block_m"])
     cost = {}
     for blk in range(p["grid"]):
         b, h, qt = pkg.work_unit(blk, heads, 192, 128, [max_q] * batch, [max_q] * batch, causal)
         if b >= 0:
             cost[blk] = (qt + 1) if causal else 1
+            if p["pair_q_tiles"] and 2 * qt > n_b - 1:  # and then q-tile n_b - 1 - qt
+                cost[blk] += n_b - qt
     n_qt = -(-max_q // p["block_m"])
+    if p["pair_q_tiles"]:
+        # pairs of q-tiles: every unit but a middle one has n_b + 1 key tiles
+        assert causal and all(c == n_b + 1 for c in cost.values() if c != (n_b + 1) // 2)
+        n_qt = (n_qt + 1) // 2
     per_xcd = p["grid"] // 8
     for x in range(8):
         for k0 in range(0, per_xcd - per_xcd % 8, 8):
@@ -681,11 +702,14 @@ def test_quant_out_validation():
 def test_plan_fp8(dims, lds_kib):
     """The fp8 kernel: 256-row workgroups of 4 waves, 64-key tiles (one fp8
     PV MFMA takes 64 keys), six LDS stages of K (plus a pad chunk a row) and
-    V bytes; the grid is the bf16 kernel's (same work units)."""
+    V bytes; the grid is the bf16 kernel's (same work units), save that the
+    bf16 kernel pairs the 16 causal q-tiles of a d_qk > 80 segment in 8
+    workgroups and the fp8 kernel does not."""
     p8 = pkg.plan(dims[0], dims[1], 3, 16, 4096, 4096, 1, fp8=True)
     p16 = pkg.plan(dims[0], dims[1], 3, 16, 4096, 4096, 1)
     assert p8["kernel"] == "attn_fwd_fp8" and p8["block_n"] == 64 and p8["block_m"] == 256
-    assert p8["threads"] == 256 and p8["grid"] == p16["grid"]
+    assert p16["pair_q_tiles"] == (dims[0] > 80) and p8["pair_q_tiles"] == 0
+    assert p8["threads"] == 256 and p8["grid"] == p16["grid"] * (2 if p16["pair_q_tiles"] else 1)
     assert p8["lds_bytes"] // 1024 == lds_kib and p8["lds_bytes"] <= 160 * 1024
     with pytest.raises(ValueError):
         pkg.plan(80, 80, 1, 16, 64, 64, 0, fp8=True)  # d 80 has no fp8 instantiation

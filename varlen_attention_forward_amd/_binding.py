@@ -76,6 +76,7 @@ class VaPlan(ctypes.Structure):
         ("segments_per_block", ctypes.c_int32),
         ("pack_mode", ctypes.c_int32),
         ("units", ctypes.c_int64),
+        ("pair_q_tiles", ctypes.c_int32),
     ]
 
 
@@ -219,6 +220,7 @@ def plan(head_dim_qk, head_dim_v, batch, num_heads, max_seqlen_q, max_seqlen_k, 
         "segments_per_block": pl.segments_per_block,
         "pack_mode": pl.pack_mode,
         "units": pl.units,
+        "pair_q_tiles": pl.pair_q_tiles,
     }
 
 

@@ -62,6 +62,11 @@ struct Params {
   int32_t n_dealt, qh_group;
   int32_t hg_shift;  // log2 of the heads dealt together (head_group_shift); fd_heads
                      // then counts head groups and fd_nqt workgroups per group
+  // Causal q-tile pairing (attn_fwd_wide, unsplit, unpacked): a work unit's
+  // q-tile index t stands for the pair of q-tiles n_b - 1 - t and t of its
+  // segment (n_b = ceil(Lq / block_m)), so that every workgroup of a causal
+  // launch has the same number of key tiles; n_qt then counts pairs.
+  int32_t pair_qt;
   float* part_o;    // [num_splits, total_q, heads, d_v]
   float* part_lse;  // [num_splits, heads, total_q]
   int32_t causal, wl, wr;
@@ -188,7 +193,8 @@ __device__ __forceinline__ BlockWork block_work(const Params& p, int lane, int b
         const int kj = __builtin_amdgcn_readlane(lk, j);
         rank += (kj > lk || (kj == lk && j < lane)) ? 1 : 0;
       }
-      const int nqt = lane < p.batch ? (lq + block_m - 1) / block_m : 0;
+      const int nqt1 = lane < p.batch ? (lq + block_m - 1) / block_m : 0;
+      const int nqt = p.pair_qt ? (nqt1 + 1) >> 1 : nqt1;  // q-tiles, or pairs of them
       const int hgroups = p.heads >> p.hg_shift;
       const int h0 = xcd_first_head(rank, hgroups, x);
       const int n = xcd_head_count(h0, hgroups) * (nqt << p.hg_shift);

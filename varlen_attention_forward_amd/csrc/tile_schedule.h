@@ -300,7 +300,8 @@ inline bool lpt_applies(int32_t batch, const int32_t* lq, const int32_t* lk) {
 
 // Host reference of the kernel's longest-first mapping (quadratic in batch).
 inline WorkUnit decode_block_lpt(int64_t w, int32_t batch, int32_t heads, int32_t block_m, int32_t n_qt,
-                                 int causal, const int32_t* lq, const int32_t* lk, int32_t hs = 0) {
+                                 int causal, const int32_t* lq, const int32_t* lk, int32_t hs = 0,
+                                 bool pair = false) {
   const int32_t x = (int32_t)(w & 7);
   const int32_t hgroups = heads >> hs;
   const int64_t k = snake_quads((uint32_t)(w >> 3), (uint32_t)(grid_blocks(batch, hgroups, (int64_t)n_qt << hs) / 8));
@@ -312,7 +313,8 @@ inline WorkUnit decode_block_lpt(int64_t w, int32_t batch, int32_t heads, int32_
       for (int32_t j = 0; j < batch; ++j) rank += (lk[j] > lk[i] || (lk[j] == lk[i] && j < i)) ? 1 : 0;
       if (rank == r) break;
     }
-    const int32_t nqt = (lq[i] + block_m - 1) / block_m;
+    const int32_t nqt1 = (lq[i] + block_m - 1) / block_m;
+    const int32_t nqt = pair ? (nqt1 + 1) / 2 : nqt1;  // q-tiles, or pairs of them
     const int64_t per = (int64_t)nqt << hs;  // workgroups of one head group of this segment
     const int32_t h0 = xcd_first_head(r, hgroups, x);
     const int64_t n = (int64_t)xcd_head_count(h0, hgroups) * per;

@@ -162,653 +162,674 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
   const int split = (int)blockIdx.y;  // split-KV copy (0 without split)
   const BlockWork bw = block_work<PK>(p, lane, C::BM, (int64_t)blockIdx.x);
   if (!bw.u.valid) return;
-  int h = bw.u.h;
-  const int qt = bw.u.qt;
-  const int k0 = bw.k0, Lk = bw.lk;  // the workgroup's keys
-  const int r0 = qt * C::BM;
-  if (r0 >= bw.lq) return;
-  constexpr bool packed = PK == kPackSegments;
-  // This wave's rows: rows [wrow0, r1) of a segment whose first query row is
-  // q0 and whose Lq queries see its Lk keys, found at key wkoff of the
-  // workgroup's keys.  One segment: rows r0 + 64 wave on, wkoff = 0.  Packed
-  // short segments: wave w takes segment pack * group + w / (4 / pack), rows
-  // 64 (w % (4 / pack)) on (a wave past the last segment has no rows).
-  int q0 = bw.q0, Lq = bw.lq, wLk = Lk, wkoff = 0, wrow0 = r0 + wave * C::RPW;
-  int r1 = min(r0 + C::BM, Lq);
-  if constexpr (packed) {
-    const int per = C::WAVES >> p.pack_shift;
-    const int seg = (bw.u.b << p.pack_shift) + (wave >> (2 - p.pack_shift));
-    wrow0 = (wave & (per - 1)) * C::RPW;
-    q0 = Lq = wLk = wkoff = r1 = 0;
-    if (seg < p.batch) {
-      q0 = p.cu_q[seg];
-      Lq = p.cu_q[seg + 1] - q0;
-      wkoff = p.cu_k[seg] - k0;
-      wLk = p.cu_k[seg + 1] - k0 - wkoff;
-      r1 = Lq;
-    }
+  // Causal launches of the one-workgroup-per-CU head dims pair a segment's
+  // q-tiles n_b - 1 - t and t in one workgroup (Params::pair_qt), so that
+  // every workgroup runs as many key tiles: dispatched in order to the shader
+  // engines in turn, workgroups of unequal length otherwise leave compute
+  // units idle behind one headed for an engine whose units are all busy.
+  // The longer q-tile runs first.  (Head dims <= 80 share a CU between two
+  // workgroups, which absorbs that, and have no registers to spare for the
+  // loop.)
+  constexpr bool kPairs = DQK > 80 && PK == kPackNone;
+  int qt_first = bw.u.qt, qt_second = -1;
+  if (kPairs && p.pair_qt) {
+    const int nb = (bw.lq + C::BM - 1) / C::BM, t = bw.u.qt;
+    if (nb - 1 - t < t) return;
+    qt_first = nb - 1 - t;
+    qt_second = nb - 1 - t > t ? t : -1;
   }
-  // The key tiles this workgroup visits: all its rows see (packed: all of
-  // its keys, every tile masked), or with split-KV the split-th of
-  // num_splits runs of them (possibly empty).
-  if constexpr (PK == kPackHeads) {
-    // Query head h + wave / (4 / pack), rows 64 (wave % (4 / pack)) on, of the
-    // one segment (r0 = 0): the workgroup's tiles are an unpacked unit's.
-    const int per = C::WAVES >> p.pack_shift;
-    h += wave >> (2 - p.pack_shift);
-    wrow0 = (wave & (per - 1)) * C::RPW;
-  }
-  TileRange tr0;
-  if constexpr (packed) {
-    tr0.kt_begin = tr0.full_begin = tr0.full_end = 0;
-    tr0.kt_end = (Lk + kBN - 1) / kBN;
-  } else {
-    tr0 = tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN);
-  }
-  // Split-KV with per-segment split counts: this segment's units take
-  // min(max(count, 1), num_splits) runs; copies past that have no work.
-  int n_splits = p.num_splits;
-  if constexpr (PK != kPackSegments) {  // (a unit holds one segment; the host never packs segments then)
-    if (p.splits_dyn != nullptr) {
-      n_splits = min(max(p.splits_dyn[bw.u.b], 1), p.num_splits);
-      if (split >= n_splits) return;
-    }
-  }
-  const TileRange tr = split_range(tr0, split, n_splits);
-  const int ntiles = tr.kt_end - tr.kt_begin;
-  // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------
-  // For head dims <= 80, buffer loads over this wave's rows [wrow0, r1):
-  // rows past r1 (and the head-dim padding of d 72) read as zero, with no
-  // branch per load.  (At 128 and 192 the compiler then allocates the main
-  // loop's registers worse, measured 7% slower on MLA; those keep plain
-  // loads under a row check.)
-  bf16x8 qf[C::QB][C::KC];
-  if constexpr (DQK > 80) {
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      const int row = wrow0 + 32 * qb + l32;
-      const uint16_t* src = p.q + (int64_t)(q0 + row) * p.q_row + (int64_t)h * p.q_head;
-#pragma unroll
-      for (int c = 0; c < C::KC; ++c) {
-        const int d = c * 16 + 8 * g;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (row < r1) x = *(const u32x4*)(src + d);
-        qf[qb][c] = __builtin_bit_cast(bf16x8, x);
+  const int n_runs = kPairs && qt_second >= 0 ? 2 : 1;
+#pragma clang loop unroll(disable)
+  for (int rep = 0; rep < n_runs; ++rep) {
+    if (rep > 0) lds_barrier();  // every wave is done reading the previous q-tile's stages
+    int h = bw.u.h;
+    const int qt = rep == 0 ? qt_first : qt_second;
+    const int k0 = bw.k0, Lk = bw.lk;  // the workgroup's keys
+    const int r0 = qt * C::BM;
+    if (r0 >= bw.lq) continue;
+    constexpr bool packed = PK == kPackSegments;
+    // This wave's rows: rows [wrow0, r1) of a segment whose first query row is
+    // q0 and whose Lq queries see its Lk keys, found at key wkoff of the
+    // workgroup's keys.  One segment: rows r0 + 64 wave on, wkoff = 0.  Packed
+    // short segments: wave w takes segment pack * group + w / (4 / pack), rows
+    // 64 (w % (4 / pack)) on (a wave past the last segment has no rows).
+    int q0 = bw.q0, Lq = bw.lq, wLk = Lk, wkoff = 0, wrow0 = r0 + wave * C::RPW;
+    int r1 = min(r0 + C::BM, Lq);
+    if constexpr (packed) {
+      const int per = C::WAVES >> p.pack_shift;
+      const int seg = (bw.u.b << p.pack_shift) + (wave >> (2 - p.pack_shift));
+      wrow0 = (wave & (per - 1)) * C::RPW;
+      q0 = Lq = wLk = wkoff = r1 = 0;
+      if (seg < p.batch) {
+        q0 = p.cu_q[seg];
+        Lq = p.cu_q[seg + 1] - q0;
+        wkoff = p.cu_k[seg] - k0;
+        wLk = p.cu_k[seg + 1] - k0 - wkoff;
+        r1 = Lq;
       }
     }
-  } else {
-    const int64_t q_row_b = p.q_row * 2;
-    const int vrows = __builtin_amdgcn_readfirstlane(max(min(r1 - wrow0, C::RPW), 0));
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.q + (int64_t)(q0 + wrow0) * p.q_row + (int64_t)h * p.q_head), (short)0,
-        (int)(uint32_t)(vrows * q_row_b), kBufferFlags);
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      const uint32_t row_off = (uint32_t)((32 * qb + l32) * q_row_b);
-#pragma unroll
-      for (int c = 0; c < C::KC; ++c) {
-        const int d = c * 16 + 8 * g;
-        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, d < DQK ? row_off + 2 * d : kOOB, 0, 0);
-        qf[qb][c] = __builtin_bit_cast(bf16x8, x);
+    // The key tiles this workgroup visits: all its rows see (packed: all of
+    // its keys, every tile masked), or with split-KV the split-th of
+    // num_splits runs of them (possibly empty).
+    if constexpr (PK == kPackHeads) {
+      // Query head h + wave / (4 / pack), rows 64 (wave % (4 / pack)) on, of the
+      // one segment (r0 = 0): the workgroup's tiles are an unpacked unit's.
+      const int per = C::WAVES >> p.pack_shift;
+      h += wave >> (2 - p.pack_shift);
+      wrow0 = (wave & (per - 1)) * C::RPW;
+    }
+    TileRange tr0;
+    if constexpr (packed) {
+      tr0.kt_begin = tr0.full_begin = tr0.full_end = 0;
+      tr0.kt_end = (Lk + kBN - 1) / kBN;
+    } else {
+      tr0 = tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN);
+    }
+    // Split-KV with per-segment split counts: this segment's units take
+    // min(max(count, 1), num_splits) runs; copies past that have no work.
+    int n_splits = p.num_splits;
+    if constexpr (PK != kPackSegments) {  // (a unit holds one segment; the host never packs segments then)
+      if (p.splits_dyn != nullptr) {
+        n_splits = min(max(p.splits_dyn[bw.u.b], 1), p.num_splits);
+        if (split >= n_splits) continue;
       }
     }
-  }
+    const TileRange tr = split_range(tr0, split, n_splits);
+    const int ntiles = tr.kt_end - tr.kt_begin;
+    // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------
+    // For head dims <= 80, buffer loads over this wave's rows [wrow0, r1):
+    // rows past r1 (and the head-dim padding of d 72) read as zero, with no
+    // branch per load.  (At 128 and 192 the compiler then allocates the main
+    // loop's registers worse, measured 7% slower on MLA; those keep plain
+    // loads under a row check.)
+    bf16x8 qf[C::QB][C::KC];
+    if constexpr (DQK > 80) {
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+        const int row = wrow0 + 32 * qb + l32;
+        const uint16_t* src = p.q + (int64_t)(q0 + row) * p.q_row + (int64_t)h * p.q_head;
+#pragma unroll
+        for (int c = 0; c < C::KC; ++c) {
+          const int d = c * 16 + 8 * g;
+          u32x4 x = {0u, 0u, 0u, 0u};
+          if (row < r1) x = *(const u32x4*)(src + d);
+          qf[qb][c] = __builtin_bit_cast(bf16x8, x);
+        }
+      }
+    } else {
+      const int64_t q_row_b = p.q_row * 2;
+      const int vrows = __builtin_amdgcn_readfirstlane(max(min(r1 - wrow0, C::RPW), 0));
+      const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.q + (int64_t)(q0 + wrow0) * p.q_row + (int64_t)h * p.q_head), (short)0,
+          (int)(uint32_t)(vrows * q_row_b), kBufferFlags);
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+        const uint32_t row_off = (uint32_t)((32 * qb + l32) * q_row_b);
+#pragma unroll
+        for (int c = 0; c < C::KC; ++c) {
+          const int d = c * 16 + 8 * g;
+          const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, d < DQK ? row_off + 2 * d : kOOB, 0, 0);
+          qf[qb][c] = __builtin_bit_cast(bf16x8, x);
+        }
+      }
+    }
 
-  // ---- direct-to-LDS tile loads ---------------------------------------------
-  // A tile is K_WL K wave-loads then V_WL V wave-loads, each 64 lanes x 16
-  // bytes: K wave-load i covers K slots [64 i, 64 i + 64), likewise for V.
-  // Wave w issues K wave-loads w + WAVES x (x < NK) and V wave-loads
-  // w + WAVES x (x < NV) every tile; where such a wave-load does not exist
-  // it reads zeros into a dummy area instead, so every wave issues LOADS
-  // loads per tile and every wait below is a constant.  K pad chunks, chunk
-  // 9 of a 72-wide row and slots past the tile read zeros; lanes on padded V
-  // chunks load nothing.
-  __shared__ __attribute__((aligned(1024))) char dummy[1024];
-  const int64_t k_row_b = p.k_row * 2, v_row_b = p.v_row * 2;
-  uint32_t k_off[C::NK], v_off[C::NV];
-  bool v_on[C::NV];
-#pragma unroll
-  for (int x = 0; x < C::NK; ++x) {
-    const int i = wave + C::WAVES * x;
-    const int sl = i * 64 + lane;
-    const int row = sl / C::KPITCH, c = sl % C::KPITCH;
-    k_off[x] = (i < C::K_WL && sl < C::K_SLOTS && c < C::K_REAL) ? (uint32_t)(row * k_row_b + c * 16) : kOOB;
-  }
-#pragma unroll
-  for (int x = 0; x < C::NV; ++x) {
-    const int i = wave + C::WAVES * x;
-    const int sl = i * 64 + lane;
-    const int row = sl / C::CPR_V;
-    const int c = (sl % C::CPR_V) ^ v_swizzle<C::CPR_V>(row);
-    v_on[x] = i >= C::V_WL || sl >= C::V_SLOTS || c < C::V_REAL;
-    v_off[x] = (i < C::V_WL && sl < C::V_SLOTS && c < C::V_REAL) ? (uint32_t)(row * v_row_b + c * 16) : kOOB;
-  }
-  // K/V rows of the next tile to issue, advanced one tile per issue; tiles
-  // past the last get an empty range (all reads zero).
-  const int hk = (int)fdiv((uint32_t)h, p.fd_group);  // the KV head query head h reads
-  const char* k_next =
-      (const char*)(p.k + ((int64_t)k0 + (int64_t)tr.kt_begin * kBN) * p.k_row + (int64_t)hk * p.k_head);
-  const char* v_next =
-      (const char*)(p.v + ((int64_t)k0 + (int64_t)tr.kt_begin * kBN) * p.v_row + (int64_t)hk * p.v_head);
-  int keys_next = Lk - tr.kt_begin * kBN;
-  auto issue = [&](auto st) VA_INLINE {  // this wave's loads of the next tile into stage st
-    // (readfirstlane: the clamp compiles to a VALU med3, and a descriptor
-    // the compiler cannot prove uniform costs a waterfall loop per load)
-    const int rows = __builtin_amdgcn_readfirstlane(max(min(keys_next, kBN), 0));
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)k_next, (short)0, (int)(rows * k_row_b), kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)v_next, (short)0, (int)(rows * v_row_b), kBufferFlags);
+    // ---- direct-to-LDS tile loads ---------------------------------------------
+    // A tile is K_WL K wave-loads then V_WL V wave-loads, each 64 lanes x 16
+    // bytes: K wave-load i covers K slots [64 i, 64 i + 64), likewise for V.
+    // Wave w issues K wave-loads w + WAVES x (x < NK) and V wave-loads
+    // w + WAVES x (x < NV) every tile; where such a wave-load does not exist
+    // it reads zeros into a dummy area instead, so every wave issues LOADS
+    // loads per tile and every wait below is a constant.  K pad chunks, chunk
+    // 9 of a 72-wide row and slots past the tile read zeros; lanes on padded V
+    // chunks load nothing.
+    __shared__ __attribute__((aligned(1024))) char dummy[1024];
+    const int64_t k_row_b = p.k_row * 2, v_row_b = p.v_row * 2;
+    uint32_t k_off[C::NK], v_off[C::NV];
+    bool v_on[C::NV];
 #pragma unroll
     for (int x = 0; x < C::NK; ++x) {
       const int i = wave + C::WAVES * x;
-      dma16(rk, i < C::K_WL ? kst(st) + i * 1024 : (lds_char*)dummy, k_off[x]);
+      const int sl = i * 64 + lane;
+      const int row = sl / C::KPITCH, c = sl % C::KPITCH;
+      k_off[x] = (i < C::K_WL && sl < C::K_SLOTS && c < C::K_REAL) ? (uint32_t)(row * k_row_b + c * 16) : kOOB;
     }
 #pragma unroll
     for (int x = 0; x < C::NV; ++x) {
       const int i = wave + C::WAVES * x;
-      if (v_on[x]) dma16(rv, i < C::V_WL ? vst(st) + i * 1024 : (lds_char*)dummy, v_off[x]);
+      const int sl = i * 64 + lane;
+      const int row = sl / C::CPR_V;
+      const int c = (sl % C::CPR_V) ^ v_swizzle<C::CPR_V>(row);
+      v_on[x] = i >= C::V_WL || sl >= C::V_SLOTS || c < C::V_REAL;
+      v_off[x] = (i < C::V_WL && sl < C::V_SLOTS && c < C::V_REAL) ? (uint32_t)(row * v_row_b + c * 16) : kOOB;
     }
-    k_next += kBN * k_row_b;
-    v_next += kBN * v_row_b;
-    keys_next -= kBN;
-  };
-  // Every iteration issues LOADS loads per wave, and loads complete in issue
-  // order: "tile t landed" with the loads of n later tiles in flight is
-  // s_waitcnt vmcnt(n LOADS).
-  auto wait_landed = [&](auto later_tiles) VA_INLINE {
-    constexpr int n = C::LOADS * decltype(later_tiles)::value;
-    static_assert(n < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
-  };
-
-  // The Q and first tiles' loads go out before the rest of the set-up, which
-  // then runs under their latency.
-  if (ntiles > 0) static_for<0, kAhead>([&](auto t) VA_INLINE { issue(t); });  // tiles 0-3
-
-  // Each wave's own key-tile range (its 64 rows see a sub-range of the
-  // workgroup's).  Iteration w_end, whose tile none of the wave's rows sees
-  // (masked to zero probabilities, so the running max and sum stay put and
-  // the slow path cannot trigger), still runs for the PV of tile w_end - 1;
-  // after it the wave only issues its share of the loads and meets the
-  // barriers.  Its own unmasked sub-range spares it the mask on tiles all its
-  // rows see.  Waves past the segment's last row compute nothing.
-  int w_beg = 0, w_end = 0, w_full_begin = 0, w_full_end = 0;  // relative to tr.kt_begin
-  if (wrow0 < r1) {
-    const TileRange wt =
-        tile_range(Lq, wLk, wrow0, min(wrow0 + C::RPW, r1), p.causal, p.wl, p.wr, kBN, wkoff);
-    // (clamped to this workgroup's tiles, which with split-KV are a run of
-    // the rows' tiles)
-    w_beg = min(max(wt.kt_begin, tr.kt_begin), tr.kt_end) - tr.kt_begin;
-    w_end = min(max(wt.kt_end, tr.kt_begin), tr.kt_end) - tr.kt_begin;
-    w_full_begin = min(max(wt.full_begin, tr.kt_begin), tr.kt_end) - tr.kt_begin;
-    w_full_end = min(max(wt.full_end, tr.kt_begin), tr.kt_end) - tr.kt_begin;
-  }
-  const bool active = w_end > w_beg;
-  // A wave computes iterations w_beg - 1 .. w_end: before its first tile it
-  // only issues its share of the loads and meets the barriers (with short
-  // segments packed into one workgroup, or a left window, the later waves'
-  // keys start later).  Iteration w_beg - 1 computes QK^T of tile w_beg
-  // (with the PV of tile w_beg - 2 on the zero probabilities below, and
-  // the softmax of the fully masked tile w_beg - 1, which changes nothing).
-  const int w_first = w_beg > 0 ? w_beg - 1 : 0;
-
-
-  // ---- padded V chunks: zeros, or a one in column d_v ------------------------
-  if constexpr (C::V_PAD > 0) {
-    static_for<0, kStages>([&](auto st) VA_INLINE {
-      for (int i = tid; i < kBN * C::V_PAD; i += C::THREADS) {
-        const int row = i / C::V_PAD, c = C::V_REAL + i % C::V_PAD;
-        const u32x4 val = {(SUM_BY_MFMA && c == C::V_REAL) ? 0x3F80u : 0u, 0u, 0u, 0u};  // bf16 1.0
-        *(__attribute__((address_space(3))) u32x4*)(vst(st) + (row * C::CPR_V + c) * 16) = val;
+    // K/V rows of the next tile to issue, advanced one tile per issue; tiles
+    // past the last get an empty range (all reads zero).
+    const int hk = (int)fdiv((uint32_t)h, p.fd_group);  // the KV head query head h reads
+    const char* k_next =
+        (const char*)(p.k + ((int64_t)k0 + (int64_t)tr.kt_begin * kBN) * p.k_row + (int64_t)hk * p.k_head);
+    const char* v_next =
+        (const char*)(p.v + ((int64_t)k0 + (int64_t)tr.kt_begin * kBN) * p.v_row + (int64_t)hk * p.v_head);
+    int keys_next = Lk - tr.kt_begin * kBN;
+    auto issue = [&](auto st) VA_INLINE {  // this wave's loads of the next tile into stage st
+      // (readfirstlane: the clamp compiles to a VALU med3, and a descriptor
+      // the compiler cannot prove uniform costs a waterfall loop per load)
+      const int rows = __builtin_amdgcn_readfirstlane(max(min(keys_next, kBN), 0));
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)k_next, (short)0, (int)(rows * k_row_b), kBufferFlags);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc((void*)v_next, (short)0, (int)(rows * v_row_b), kBufferFlags);
+#pragma unroll
+      for (int x = 0; x < C::NK; ++x) {
+        const int i = wave + C::WAVES * x;
+        dma16(rk, i < C::K_WL ? kst(st) + i * 1024 : (lds_char*)dummy, k_off[x]);
       }
-    });
-  }
+#pragma unroll
+      for (int x = 0; x < C::NV; ++x) {
+        const int i = wave + C::WAVES * x;
+        if (v_on[x]) dma16(rv, i < C::V_WL ? vst(st) + i * 1024 : (lds_char*)dummy, v_off[x]);
+      }
+      k_next += kBN * k_row_b;
+      v_next += kBN * v_row_b;
+      keys_next -= kBN;
+    };
+    // Every iteration issues LOADS loads per wave, and loads complete in issue
+    // order: "tile t landed" with the loads of n later tiles in flight is
+    // s_waitcnt vmcnt(n LOADS).
+    auto wait_landed = [&](auto later_tiles) VA_INLINE {
+      constexpr int n = C::LOADS * decltype(later_tiles)::value;
+      static_assert(n < 64, "vmcnt range");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
+    };
 
-  // ---- LDS operand reads ----------------------------------------------------
-  const int k_rd = (l32 * C::KPITCH + g) * 16;  // K row l32, chunk 2c + g at + 32c
-  int v_rd[C::VB];
-  {
-    const int G = lane >> 4, i = lane & 15;
-    const int vrow = 4 * g + (i >> 2);
-    const int y = 2 * (G & 1) + ((i >> 1) & 1);
+    // The Q and first tiles' loads go out before the rest of the set-up, which
+    // then runs under their latency.
+    if (ntiles > 0) static_for<0, kAhead>([&](auto t) VA_INLINE { issue(t); });  // tiles 0-3
+
+    // Each wave's own key-tile range (its 64 rows see a sub-range of the
+    // workgroup's).  Iteration w_end, whose tile none of the wave's rows sees
+    // (masked to zero probabilities, so the running max and sum stay put and
+    // the slow path cannot trigger), still runs for the PV of tile w_end - 1;
+    // after it the wave only issues its share of the loads and meets the
+    // barriers.  Its own unmasked sub-range spares it the mask on tiles all its
+    // rows see.  Waves past the segment's last row compute nothing.
+    int w_beg = 0, w_end = 0, w_full_begin = 0, w_full_end = 0;  // relative to tr.kt_begin
+    if (wrow0 < r1) {
+      const TileRange wt =
+          tile_range(Lq, wLk, wrow0, min(wrow0 + C::RPW, r1), p.causal, p.wl, p.wr, kBN, wkoff);
+      // (clamped to this workgroup's tiles, which with split-KV are a run of
+      // the rows' tiles)
+      w_beg = min(max(wt.kt_begin, tr.kt_begin), tr.kt_end) - tr.kt_begin;
+      w_end = min(max(wt.kt_end, tr.kt_begin), tr.kt_end) - tr.kt_begin;
+      w_full_begin = min(max(wt.full_begin, tr.kt_begin), tr.kt_end) - tr.kt_begin;
+      w_full_end = min(max(wt.full_end, tr.kt_begin), tr.kt_end) - tr.kt_begin;
+    }
+    const bool active = w_end > w_beg;
+    // A wave computes iterations w_beg - 1 .. w_end: before its first tile it
+    // only issues its share of the loads and meets the barriers (with short
+    // segments packed into one workgroup, or a left window, the later waves'
+    // keys start later).  Iteration w_beg - 1 computes QK^T of tile w_beg
+    // (with the PV of tile w_beg - 2 on the zero probabilities below, and
+    // the softmax of the fully masked tile w_beg - 1, which changes nothing).
+    const int w_first = w_beg > 0 ? w_beg - 1 : 0;
+
+
+    // ---- padded V chunks: zeros, or a one in column d_v ------------------------
+    if constexpr (C::V_PAD > 0) {
+      static_for<0, kStages>([&](auto st) VA_INLINE {
+        for (int i = tid; i < kBN * C::V_PAD; i += C::THREADS) {
+          const int row = i / C::V_PAD, c = C::V_REAL + i % C::V_PAD;
+          const u32x4 val = {(SUM_BY_MFMA && c == C::V_REAL) ? 0x3F80u : 0u, 0u, 0u, 0u};  // bf16 1.0
+          *(__attribute__((address_space(3))) u32x4*)(vst(st) + (row * C::CPR_V + c) * 16) = val;
+        }
+      });
+    }
+
+    // ---- LDS operand reads ----------------------------------------------------
+    const int k_rd = (l32 * C::KPITCH + g) * 16;  // K row l32, chunk 2c + g at + 32c
+    int v_rd[C::VB];
+    {
+      const int G = lane >> 4, i = lane & 15;
+      const int vrow = 4 * g + (i >> 2);
+      const int y = 2 * (G & 1) + ((i >> 1) & 1);
+#pragma unroll
+      for (int vb = 0; vb < C::VB; ++vb)
+        v_rd[vb] = (vrow * C::CPR_V + ((4 * vb + y) ^ v_swizzle<C::CPR_V>(vrow))) * 16 + 8 * (i & 1);
+    }
+
+    // ---- running state ----------------------------------------------------------
+    f32x16 acc[C::VB][C::QB];
 #pragma unroll
     for (int vb = 0; vb < C::VB; ++vb)
-      v_rd[vb] = (vrow * C::CPR_V + ((4 * vb + y) ^ v_swizzle<C::CPR_V>(vrow))) * 16 + 8 * (i & 1);
-  }
-
-  // ---- running state ----------------------------------------------------------
-  f32x16 acc[C::VB][C::QB];
 #pragma unroll
-  for (int vb = 0; vb < C::VB; ++vb)
+      for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[vb][qb][r] = 0.f;
+    float m_run[C::QB], nm[C::QB], lim[C::QB], l_run[C::QB];
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      m_run[qb] = -INFINITY;  // running max of s * scale * log2(e)
+      nm[qb] = 0.f;           // -m_run, or 0 while m_run is -inf
+      lim[qb] = -FLT_MAX;     // m_run + kRescaleTau, or -FLT_MAX while m_run is -inf
+      l_run[qb] = 0.f;        // fp32 row sum (unless SUM_BY_MFMA)
+    }
+    int row_lo[C::QB], row_hi[C::QB];
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      const RowBounds rb = row_bounds(wrow0 + 32 * qb + l32, Lq, wLk, p.causal, p.wl, p.wr);
+      row_lo[qb] = wkoff + (int)imin64(rb.lo, (int64_t)wLk);
+      row_hi[qb] = wkoff + (int)imax64(rb.hi, (int64_t)-1);
+    }
+    // Iteration (relative key tile) holding each row's first visible key, or
+    // -1 for a row that sees none: there the fast path cannot run (see
+    // fused_block).
+    int first_j[C::QB];
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb)
+      first_j[qb] = row_lo[qb] <= row_hi[qb] ? row_lo[qb] / kBN - tr.kt_begin : -1;
+    // Scores of two tiles (the one in the softmax and the next, which QK^T is
+    // writing): sbuf[t % 2][qb][r] = key 8 (r / 4) + 4 g + r % 4, query l32.
+    f32x16 sbuf[2][C::QB];
+    // Probabilities, the PV B operand per (qb, 16-key half); zero until a
+    // wave's first computed tile, whose PV of the previous tile then adds
+    // nothing.
+    bf16x8 pf[C::QB][2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[vb][qb][r] = 0.f;
-  float m_run[C::QB], nm[C::QB], lim[C::QB], l_run[C::QB];
-#pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    m_run[qb] = -INFINITY;  // running max of s * scale * log2(e)
-    nm[qb] = 0.f;           // -m_run, or 0 while m_run is -inf
-    lim[qb] = -FLT_MAX;     // m_run + kRescaleTau, or -FLT_MAX while m_run is -inf
-    l_run[qb] = 0.f;        // fp32 row sum (unless SUM_BY_MFMA)
-  }
-  int row_lo[C::QB], row_hi[C::QB];
-#pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    const RowBounds rb = row_bounds(wrow0 + 32 * qb + l32, Lq, wLk, p.causal, p.wl, p.wr);
-    row_lo[qb] = wkoff + (int)imin64(rb.lo, (int64_t)wLk);
-    row_hi[qb] = wkoff + (int)imax64(rb.hi, (int64_t)-1);
-  }
-  // Iteration (relative key tile) holding each row's first visible key, or
-  // -1 for a row that sees none: there the fast path cannot run (see
-  // fused_block).
-  int first_j[C::QB];
-#pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb)
-    first_j[qb] = row_lo[qb] <= row_hi[qb] ? row_lo[qb] / kBN - tr.kt_begin : -1;
-  // Scores of two tiles (the one in the softmax and the next, which QK^T is
-  // writing): sbuf[t % 2][qb][r] = key 8 (r / 4) + 4 g + r % 4, query l32.
-  f32x16 sbuf[2][C::QB];
-  // Probabilities, the PV B operand per (qb, 16-key half); zero until a
-  // wave's first computed tile, whose PV of the previous tile then adds
-  // nothing.
-  bf16x8 pf[C::QB][2];
-#pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) pf[qb][0] = pf[qb][1] = bf16x8{};
+    for (int qb = 0; qb < C::QB; ++qb) pf[qb][0] = pf[qb][1] = bf16x8{};
 
-  // QK^T of one tile on its own (tile 0 and the next, and the slow path):
-  // KC K operands into sn, each LDS operand feeding both query blocks,
-  // operands read kDepth ahead into a ring of registers.
-  auto qk_only = [&](const lds_char* ks, f32x16 (&sn)[C::QB]) VA_INLINE {
-    const f32x16 zero = {};
-    bf16x8 ring[kDepth];
+    // QK^T of one tile on its own (tile 0 and the next, and the slow path):
+    // KC K operands into sn, each LDS operand feeding both query blocks,
+    // operands read kDepth ahead into a ring of registers.
+    auto qk_only = [&](const lds_char* ks, f32x16 (&sn)[C::QB]) VA_INLINE {
+      const f32x16 zero = {};
+      bf16x8 ring[kDepth];
 #pragma unroll
-    for (int i = 0; i < kDepth && i < C::KC; ++i) ring[i] = lds_read_b128(ks, k_rd + 32 * i);
+      for (int i = 0; i < kDepth && i < C::KC; ++i) ring[i] = lds_read_b128(ks, k_rd + 32 * i);
 #pragma unroll
-    for (int c = 0; c < C::KC; ++c) {
-      const bf16x8 op = ring[c % kDepth];
-      if (c + kDepth < C::KC) ring[c % kDepth] = lds_read_b128(ks, k_rd + 32 * (c + kDepth));
+      for (int c = 0; c < C::KC; ++c) {
+        const bf16x8 op = ring[c % kDepth];
+        if (c + kDepth < C::KC) ring[c % kDepth] = lds_read_b128(ks, k_rd + 32 * (c + kDepth));
 #pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb)
-        sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qf[qb][c], c == 0 ? zero : sn[qb], 0, 0, 0);
-    }
-  };
-  // Boundary tiles only: scores of keys a row may not see become -inf.
-  auto mask = [&](int j, f32x16 (&s)[C::QB]) VA_INLINE {
-    const int kt = tr.kt_begin + j;
-    if ((unsigned)(j - w_full_begin) >= (unsigned)(w_full_end - w_full_begin)) {  // j outside [begin, end)
-      const int key0 = kt * kBN;
-#pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int jj = key0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          s[qb][r] = (jj >= row_lo[qb] && jj <= row_hi[qb]) ? s[qb][r] : -INFINITY;
-        }
-    }
-  };
-  // Online softmax of one tile, branch-free: row max, the lazy-rescale
-  // decision (the running max moves only when some row's max grew by more
-  // than kRescaleTau, in log2 units; then every row of the wave moves),
-  // p = exp2(s * scale * log2(e) - m), row sum, bf16 pack into pf.  Returns
-  // whether acc must be rescaled, with alpha per query block.
-  auto softmax = [&](f32x16 (&s)[C::QB], float (&alpha)[C::QB]) VA_INLINE -> bool {
-    float m_new[C::QB];
-    bool need = false;
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      float m = fmaxf(fmaxf(s[qb][0], s[qb][1]), s[qb][2]);
-#pragma unroll
-      for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, s[qb][r]), s[qb][r + 1]);
-      m = fmaxf(m, s[qb][15]);
-      m_new[qb] = fmaxf(m_run[qb], xhalf_max(m) * p.scale_log2);
-      need |= m_new[qb] > m_run[qb] + kRescaleTau;
-    }
-    const bool move = __any(need);
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      const float m_next = move ? m_new[qb] : m_run[qb];
-      alpha[qb] = (m_next == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_next);
-      m_run[qb] = m_next;
-      nm[qb] = (m_next == -INFINITY) ? 0.f : -m_next;
-      lim[qb] = (m_next == -INFINITY) ? -FLT_MAX : m_next + kRescaleTau;
-    }
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      float sum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 8 * t + 2 * e;
-          const float x0 = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, nm[qb]));
-          const float x1 = __builtin_amdgcn_exp2f(fmaf(s[qb][r + 1], p.scale_log2, nm[qb]));
-          pk[e] = pack_bf16x2(x0, x1);
-          if constexpr (SUM == RowSum::kF32) sum += x0 + x1;
-        }
-        pf[qb][t] = __builtin_bit_cast(bf16x8, pk);
-      }
-      if constexpr (!SUM_BY_MFMA) l_run[qb] = l_run[qb] * alpha[qb] + sum;
-    }
-    return move;
-  };
-  // One iteration's MFMAs and fast-path softmax, interleaved by hand.
-  //
-  // The fast path needs nothing of this tile's max: p = exp2(s * scale *
-  // log2(e) - m_run) with the running max as it stands, in place, packed to
-  // bf16, and a check that this was valid: every p <= 2^kRescaleTau (the
-  // tile's max exceeds m_run by at most kRescaleTau, so the lazy rescale
-  // would not have moved the max either) and no row saw its first visible
-  // key (while m_run is -inf, p is not relative to any max yet).  With a
-  // row sum in registers (kF32) the first condition is read off the
-  // tile's row sum (sum <= 2^kRescaleTau bounds every term), so no row max
-  // is taken; with the ones-column sum (kMfma) the row max is taken on the
-  // raw scores as before.  The row sums go to sum[], committed by the caller
-  // only if the check passed.
-  //
-  // Its VALU work is 80 or 96 units in dependency order: (16 row-max steps,
-  // 8 per query block, on the raw scores, kMfma only), 32 scale-and-shift
-  // FMAs, 32 in-place exps, 16 packs (+ sums).  The MFMAs (PV of the
-  // previous tile, then QK^T of the next, two per LDS operand) each get an
-  // even share of the units, in
-  // source order pinned by scheduling barriers: the compiler's own schedule
-  // bunches the MFMAs, and an MFMA hides only a few VALU ops behind it.  The
-  // packs, which overwrite the probabilities PV reads, all fall after the
-  // last PV MFMA.
-  auto fused_block = [&](const lds_char* vs, const lds_char* ks, f32x16 (&s)[C::QB], f32x16 (&sn)[C::QB],
-                         float (&sum)[C::QB], int j) VA_INLINE -> bool {
-    constexpr bool kMaxCheck = SUM_BY_MFMA;
-    constexpr int QB = C::QB;
-    constexpr int kPVOps = 2 * C::VB, kOps = kPVOps + C::KC, kSlots = QB * kOps;
-    // The scale-and-shift FMAs run as units of their own, all before the
-    // exps, rather than each with its exp (measured +1% on the ViT batch and
-    // the MLA prefill, +0.4% on d 128, bit-identical).
-    constexpr int kMaxU = 8 * QB, kFmaU = 16 * QB, kExpU = 16 * QB, kPackU = 8 * QB;  // units per kind
-    constexpr int kUnits = (kMaxCheck ? kMaxU : 0) + kFmaU + kExpU + kPackU;
-    static_assert((kUnits - kPackU) * kSlots / kUnits >= QB * kPVOps, "packs must follow the PV MFMAs");
-    float m[QB];
-    bool bad = false;
-    if constexpr (!kMaxCheck)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) bad |= j == first_j[qb];
-    u32x4 pk[QB][2];
-    auto unit = [&](auto uu) VA_INLINE {
-      constexpr int u = decltype(uu)::value + (kMaxCheck ? 0 : kMaxU);
-      if constexpr (u < kMaxU) {  // row max, 8 steps per query block
-        constexpr int qb = u / 8, st = u % 8;
-        if constexpr (st == 0) {
-          m[qb] = fmaxf(fmaxf(s[qb][0], s[qb][1]), s[qb][2]);
-        } else if constexpr (st < 7) {
-          m[qb] = fmaxf(fmaxf(m[qb], s[qb][2 * st + 1]), s[qb][2 * st + 2]);
-        } else {
-          m[qb] = fmaxf(m[qb], s[qb][15]);
-          bad |= m[qb] * p.scale_log2 > lim[qb];
-        }
-      } else if constexpr (u < kMaxU + kFmaU) {  // s * scale - m_run, in place
-        constexpr int qb = (u - kMaxU) / 16, r = (u - kMaxU) % 16;
-        s[qb][r] = fmaf(s[qb][r], p.scale_log2, nm[qb]);
-      } else if constexpr (u < kMaxU + kFmaU + kExpU) {  // p = exp2(s * scale - m_run), in place
-        constexpr int qb = (u - kMaxU - kFmaU) / 16, r = (u - kMaxU - kFmaU) % 16;
-        s[qb][r] = __builtin_amdgcn_exp2f(s[qb][r]);
-      } else {  // bf16 pack (and row sum)
-        constexpr int i = u - kMaxU - kFmaU - kExpU, qb = i / 8, t = (i / 4) % 2, e = i % 4, r = 8 * t + 2 * e;
-        constexpr bool first = t == 0 && e == 0;
-        pk[qb][t][e] = pack_bf16x2(s[qb][r], s[qb][r + 1]);
-        if constexpr (SUM == RowSum::kF32) {
-          const float pair = s[qb][r] + s[qb][r + 1];
-          sum[qb] = first ? pair : sum[qb] + pair;
-        }
-        if constexpr (e == 3) pf[qb][t] = __builtin_bit_cast(bf16x8, pk[qb][t]);
-        if constexpr (!kMaxCheck && t == 1 && e == 3) bad |= !(sum[qb] <= kSumLimit);
-      }
-    };
-    auto load_op = [&](auto ii, bf16x8& dst) VA_INLINE {
-      constexpr int i = decltype(ii)::value;
-      if constexpr (i < kPVOps) {  // V^T operand (t, vb) of PV
-        constexpr int t = i / C::VB, vb = i % C::VB;
-        const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
-        const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
-        dst = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      } else {  // K operand i - kPVOps of QK^T
-        dst = lds_read_b128(ks, k_rd + 32 * (i - kPVOps));
-      }
-    };
-    const f32x16 zero = {};
-    bf16x8 ring[kDepth];
-    static_for<0, kDepth>([&](auto ii) VA_INLINE { load_op(ii, ring[decltype(ii)::value]); });
-    static_for<0, kOps>([&](auto oo) VA_INLINE {
-      constexpr int i = decltype(oo)::value;
-      const bf16x8 op = ring[i % kDepth];
-      if constexpr (i + kDepth < kOps) load_op(Int<i + kDepth>{}, ring[i % kDepth]);
-      static_for<0, QB>([&](auto qq) VA_INLINE {
-        constexpr int qb = decltype(qq)::value, slot = QB * i + qb;
-        if constexpr (i < kPVOps) {
-          constexpr int t = i / C::VB, vb = i % C::VB;
-          acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, pf[qb][t], acc[vb][qb], 0, 0, 0);
-        } else {
-          constexpr int c = i - kPVOps;
+        for (int qb = 0; qb < C::QB; ++qb)
           sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qf[qb][c], c == 0 ? zero : sn[qb], 0, 0, 0);
-        }
-        static_for<slot * kUnits / kSlots, (slot + 1) * kUnits / kSlots>(unit);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-    });
-    return __any(bad);
-  };
-  // acc *= alpha, after the PV MFMAs of the previous tile (rare).
-  auto rescale = [&](bool move, const float (&alpha)[C::QB]) VA_INLINE {
-    if (move) {
-      asm volatile("; lazy rescale" ::: "memory");  // keep the rare rescale a branch
+      }
+    };
+    // Boundary tiles only: scores of keys a row may not see become -inf.
+    auto mask = [&](int j, f32x16 (&s)[C::QB]) VA_INLINE {
+      const int kt = tr.kt_begin + j;
+      if ((unsigned)(j - w_full_begin) >= (unsigned)(w_full_end - w_full_begin)) {  // j outside [begin, end)
+        const int key0 = kt * kBN;
 #pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb)
+        for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int jj = key0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            s[qb][r] = (jj >= row_lo[qb] && jj <= row_hi[qb]) ? s[qb][r] : -INFINITY;
+          }
+      }
+    };
+    // Online softmax of one tile, branch-free: row max, the lazy-rescale
+    // decision (the running max moves only when some row's max grew by more
+    // than kRescaleTau, in log2 units; then every row of the wave moves),
+    // p = exp2(s * scale * log2(e) - m), row sum, bf16 pack into pf.  Returns
+    // whether acc must be rescaled, with alpha per query block.
+    auto softmax = [&](f32x16 (&s)[C::QB], float (&alpha)[C::QB]) VA_INLINE -> bool {
+      float m_new[C::QB];
+      bool need = false;
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+        float m = fmaxf(fmaxf(s[qb][0], s[qb][1]), s[qb][2]);
+#pragma unroll
+        for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, s[qb][r]), s[qb][r + 1]);
+        m = fmaxf(m, s[qb][15]);
+        m_new[qb] = fmaxf(m_run[qb], xhalf_max(m) * p.scale_log2);
+        need |= m_new[qb] > m_run[qb] + kRescaleTau;
+      }
+      const bool move = __any(need);
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+        const float m_next = move ? m_new[qb] : m_run[qb];
+        alpha[qb] = (m_next == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_next);
+        m_run[qb] = m_next;
+        nm[qb] = (m_next == -INFINITY) ? 0.f : -m_next;
+        lim[qb] = (m_next == -INFINITY) ? -FLT_MAX : m_next + kRescaleTau;
+      }
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+        float sum = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          u32x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * t + 2 * e;
+            const float x0 = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, nm[qb]));
+            const float x1 = __builtin_amdgcn_exp2f(fmaf(s[qb][r + 1], p.scale_log2, nm[qb]));
+            pk[e] = pack_bf16x2(x0, x1);
+            if constexpr (SUM == RowSum::kF32) sum += x0 + x1;
+          }
+          pf[qb][t] = __builtin_bit_cast(bf16x8, pk);
+        }
+        if constexpr (!SUM_BY_MFMA) l_run[qb] = l_run[qb] * alpha[qb] + sum;
+      }
+      return move;
+    };
+    // One iteration's MFMAs and fast-path softmax, interleaved by hand.
+    //
+    // The fast path needs nothing of this tile's max: p = exp2(s * scale *
+    // log2(e) - m_run) with the running max as it stands, in place, packed to
+    // bf16, and a check that this was valid: every p <= 2^kRescaleTau (the
+    // tile's max exceeds m_run by at most kRescaleTau, so the lazy rescale
+    // would not have moved the max either) and no row saw its first visible
+    // key (while m_run is -inf, p is not relative to any max yet).  With a
+    // row sum in registers (kF32) the first condition is read off the
+    // tile's row sum (sum <= 2^kRescaleTau bounds every term), so no row max
+    // is taken; with the ones-column sum (kMfma) the row max is taken on the
+    // raw scores as before.  The row sums go to sum[], committed by the caller
+    // only if the check passed.
+    //
+    // Its VALU work is 80 or 96 units in dependency order: (16 row-max steps,
+    // 8 per query block, on the raw scores, kMfma only), 32 scale-and-shift
+    // FMAs, 32 in-place exps, 16 packs (+ sums).  The MFMAs (PV of the
+    // previous tile, then QK^T of the next, two per LDS operand) each get an
+    // even share of the units, in
+    // source order pinned by scheduling barriers: the compiler's own schedule
+    // bunches the MFMAs, and an MFMA hides only a few VALU ops behind it.  The
+    // packs, which overwrite the probabilities PV reads, all fall after the
+    // last PV MFMA.
+    auto fused_block = [&](const lds_char* vs, const lds_char* ks, f32x16 (&s)[C::QB], f32x16 (&sn)[C::QB],
+                           float (&sum)[C::QB], int j) VA_INLINE -> bool {
+      constexpr bool kMaxCheck = SUM_BY_MFMA;
+      constexpr int QB = C::QB;
+      constexpr int kPVOps = 2 * C::VB, kOps = kPVOps + C::KC, kSlots = QB * kOps;
+      // The scale-and-shift FMAs run as units of their own, all before the
+      // exps, rather than each with its exp (measured +1% on the ViT batch and
+      // the MLA prefill, +0.4% on d 128, bit-identical).
+      constexpr int kMaxU = 8 * QB, kFmaU = 16 * QB, kExpU = 16 * QB, kPackU = 8 * QB;  // units per kind
+      constexpr int kUnits = (kMaxCheck ? kMaxU : 0) + kFmaU + kExpU + kPackU;
+      static_assert((kUnits - kPackU) * kSlots / kUnits >= QB * kPVOps, "packs must follow the PV MFMAs");
+      float m[QB];
+      bool bad = false;
+      if constexpr (!kMaxCheck)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) bad |= j == first_j[qb];
+      u32x4 pk[QB][2];
+      auto unit = [&](auto uu) VA_INLINE {
+        constexpr int u = decltype(uu)::value + (kMaxCheck ? 0 : kMaxU);
+        if constexpr (u < kMaxU) {  // row max, 8 steps per query block
+          constexpr int qb = u / 8, st = u % 8;
+          if constexpr (st == 0) {
+            m[qb] = fmaxf(fmaxf(s[qb][0], s[qb][1]), s[qb][2]);
+          } else if constexpr (st < 7) {
+            m[qb] = fmaxf(fmaxf(m[qb], s[qb][2 * st + 1]), s[qb][2 * st + 2]);
+          } else {
+            m[qb] = fmaxf(m[qb], s[qb][15]);
+            bad |= m[qb] * p.scale_log2 > lim[qb];
+          }
+        } else if constexpr (u < kMaxU + kFmaU) {  // s * scale - m_run, in place
+          constexpr int qb = (u - kMaxU) / 16, r = (u - kMaxU) % 16;
+          s[qb][r] = fmaf(s[qb][r], p.scale_log2, nm[qb]);
+        } else if constexpr (u < kMaxU + kFmaU + kExpU) {  // p = exp2(s * scale - m_run), in place
+          constexpr int qb = (u - kMaxU - kFmaU) / 16, r = (u - kMaxU - kFmaU) % 16;
+          s[qb][r] = __builtin_amdgcn_exp2f(s[qb][r]);
+        } else {  // bf16 pack (and row sum)
+          constexpr int i = u - kMaxU - kFmaU - kExpU, qb = i / 8, t = (i / 4) % 2, e = i % 4, r = 8 * t + 2 * e;
+          constexpr bool first = t == 0 && e == 0;
+          pk[qb][t][e] = pack_bf16x2(s[qb][r], s[qb][r + 1]);
+          if constexpr (SUM == RowSum::kF32) {
+            const float pair = s[qb][r] + s[qb][r + 1];
+            sum[qb] = first ? pair : sum[qb] + pair;
+          }
+          if constexpr (e == 3) pf[qb][t] = __builtin_bit_cast(bf16x8, pk[qb][t]);
+          if constexpr (!kMaxCheck && t == 1 && e == 3) bad |= !(sum[qb] <= kSumLimit);
+        }
+      };
+      auto load_op = [&](auto ii, bf16x8& dst) VA_INLINE {
+        constexpr int i = decltype(ii)::value;
+        if constexpr (i < kPVOps) {  // V^T operand (t, vb) of PV
+          constexpr int t = i / C::VB, vb = i % C::VB;
+          const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
+          const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
+          dst = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {  // K operand i - kPVOps of QK^T
+          dst = lds_read_b128(ks, k_rd + 32 * (i - kPVOps));
+        }
+      };
+      const f32x16 zero = {};
+      bf16x8 ring[kDepth];
+      static_for<0, kDepth>([&](auto ii) VA_INLINE { load_op(ii, ring[decltype(ii)::value]); });
+      static_for<0, kOps>([&](auto oo) VA_INLINE {
+        constexpr int i = decltype(oo)::value;
+        const bf16x8 op = ring[i % kDepth];
+        if constexpr (i + kDepth < kOps) load_op(Int<i + kDepth>{}, ring[i % kDepth]);
+        static_for<0, QB>([&](auto qq) VA_INLINE {
+          constexpr int qb = decltype(qq)::value, slot = QB * i + qb;
+          if constexpr (i < kPVOps) {
+            constexpr int t = i / C::VB, vb = i % C::VB;
+            acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, pf[qb][t], acc[vb][qb], 0, 0, 0);
+          } else {
+            constexpr int c = i - kPVOps;
+            sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qf[qb][c], c == 0 ? zero : sn[qb], 0, 0, 0);
+          }
+          static_for<slot * kUnits / kSlots, (slot + 1) * kUnits / kSlots>(unit);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      });
+      return __any(bad);
+    };
+    // acc *= alpha, after the PV MFMAs of the previous tile (rare).
+    auto rescale = [&](bool move, const float (&alpha)[C::QB]) VA_INLINE {
+      if (move) {
+        asm volatile("; lazy rescale" ::: "memory");  // keep the rare rescale a branch
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+          for (int vb = 0; vb < C::VB; ++vb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[vb][qb][r] *= alpha[qb];
+      }
+    };
+
+    // ---- main loop ----------------------------------------------------------------
+    // Iteration j: issue tile j + 4; MFMAs of PV(j - 1) and QK^T(j + 1) with
+    // the softmax of tile j; rescale; wait for this wave's share of tile j + 2;
+    // barrier.  Tile t sits in stage t % 6, which last held tile t - 6: its K
+    // was last read in iteration t - 7, its V in iteration t - 5, both before
+    // iteration t - 4 issues tile t.  Tile j + 2 (read by iteration j + 1's
+    // QK^T) is waited for at the end of iteration j, three iterations after
+    // its issue.  Every iteration issues, past the last tile too (zeros), so
+    // the waits are constants; QK^T of tile ntiles in the last iteration reads
+    // such zeros, already landed, and its result is never used.
+    //
+    // Iteration j's softmax reads sbuf[j % 2] and QK^T writes sbuf[(j + 1) % 2];
+    // the loop is unrolled by the (even) stage count so both are static.
+    // PV of one tile on its own (the workgroup's last tile).
+    auto pv_tile = [&](const lds_char* vs) VA_INLINE {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int vb = 0; vb < C::VB; ++vb) {
+          const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
+          const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
+          const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int qb = 0; qb < C::QB; ++qb)
+            acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][t], acc[vb][qb], 0, 0, 0);
+        }
+    };
+    if (ntiles > 0) {
+      wait_landed(Int<kAhead - 1>{});  // tile 0 (tiles 0-3 were issued above)
+      lds_barrier();
+      if (active && w_beg == 0) qk_only(kst(Int<0>{}), sbuf[0]);  // QK^T(0)
+      wait_landed(Int<kAhead - 2>{});  // tile 1
+      lds_barrier();
+      // iteration 0 (no PV before it)
+      {
+        issue(Int<kAhead % kStages>{});
+        if (active && w_first == 0) {
+          mask(0, sbuf[0]);
+          qk_only(kst(Int<1>{}), sbuf[1]);
+          float alpha[C::QB];
+          const bool move = softmax(sbuf[0], alpha);
+          rescale(move, alpha);
+        }
+        wait_landed(Int<kAhead - 2>{});  // tile 2
+        lds_barrier();
+      }
+      for (int j0 = 1; j0 < ntiles; j0 += kStages) {  // tile j0 + u sits in stage (u + 1) % 6
+        static_for<0, kStages>([&](auto u) VA_INLINE {
+          constexpr int U = decltype(u)::value;
+          const int j = j0 + U;
+          if (U == 0 || j < ntiles) {
+            issue(Int<(U + 1 + kAhead) % kStages>{});  // tile j + 4 (zeros past the last)
+            if (active && j <= w_end && j >= w_first) {
+              constexpr int cur = (U + 1) % 2;  // j % 2, j0 being odd
+              mask(j, sbuf[cur]);
+              float sum[C::QB];
+              const bool slow = fused_block(vst(Int<U % kStages>{}), kst(Int<(U + 2) % kStages>{}), sbuf[cur],
+                                            sbuf[cur ^ 1], sum, j);
+              // The probabilities are only read in the next iteration and the
+              // row sums only on the fast path; without these uses the compiler
+              // sinks their computation past the branch below, out of the
+              // interleave, where nothing hides it.
+#pragma unroll
+              for (int qb = 0; qb < C::QB; ++qb) {
+                asm volatile("" ::"v"(pf[qb][0]), "v"(pf[qb][1]));
+                if constexpr (!SUM_BY_MFMA) asm volatile("" ::"v"(sum[qb]));
+              }
+              // Commit the row sums on one path (the slow path restores them):
+              // two paths merging into l_run cost the register allocator dearly.
+              float l_prev[C::QB];
+#pragma unroll
+              for (int qb = 0; qb < C::QB; ++qb) {
+                l_prev[qb] = l_run[qb];
+                if constexpr (!SUM_BY_MFMA) l_run[qb] += sum[qb];
+              }
+              if (slow) {
+                // Some row's max moved past m_run + kRescaleTau (or a row saw
+                // its first key): recompute this tile's scores from K, still
+                // in its stage, and take the full softmax with the rescale.
+                asm volatile("; softmax slow path" ::: "memory");
+#pragma unroll
+                for (int qb = 0; qb < C::QB; ++qb) l_run[qb] = l_prev[qb];
+                qk_only(kst(Int<(U + 1) % kStages>{}), sbuf[cur]);
+                mask(j, sbuf[cur]);
+                float alpha[C::QB];
+                const bool move = softmax(sbuf[cur], alpha);
+                rescale(move, alpha);
+              }
+            }
+            wait_landed(Int<kAhead - 2>{});  // tile j + 2
+            lds_barrier();
+          }
+        });
+      }
+      // The zero loads past the last tile must land before the workgroup's LDS
+      // can be handed to the next workgroup.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (active && w_end == ntiles) {  // PV of the last tile, its stage picked at run time (all DMA has landed)
+        const int last = (ntiles - 1) % kStages;
+        const lds_char* vs = vst(Int<0>{});
+        static_for<1, kStages>([&](auto st) VA_INLINE {
+          if (last == decltype(st)::value) vs = vst(st);
+        });
+        pv_tile(vs);
+      }
+    }
+
+    // ---- epilogue ---------------------------------------------------------------
+    // With SUM_BY_MFMA the row sum sits in column d_v of the accumulator:
+    // dv block VB - 1, register 4 * ((d_v % 32) / 8), lanes 0-31.
+    constexpr int kSumReg = 4 * ((DV % 32) / 8);
+    if (p.num_splits > 1) {
+      // Split-KV partial: O = acc / l in fp32 (lane (row, g) holds d_v 8 jj +
+      // 4 g .. + 3 of each 32-wide block: one 16-byte store each) and the LSE of
+      // this split's keys (-inf where a row saw none of them).
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+        const float l = SUM_BY_MFMA ? from_lower_half(acc[C::VB - 1][qb][kSumReg]) : xhalf_sum(l_run[qb]);
+        const int row = wrow0 + 32 * qb + l32;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        float* dst = p.part_o + (((int64_t)split * p.total_q + q0 + row) * p.heads + h) * DV;
 #pragma unroll
         for (int vb = 0; vb < C::VB; ++vb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[vb][qb][r] *= alpha[qb];
-    }
-  };
-
-  // ---- main loop ----------------------------------------------------------------
-  // Iteration j: issue tile j + 4; MFMAs of PV(j - 1) and QK^T(j + 1) with
-  // the softmax of tile j; rescale; wait for this wave's share of tile j + 2;
-  // barrier.  Tile t sits in stage t % 6, which last held tile t - 6: its K
-  // was last read in iteration t - 7, its V in iteration t - 5, both before
-  // iteration t - 4 issues tile t.  Tile j + 2 (read by iteration j + 1's
-  // QK^T) is waited for at the end of iteration j, three iterations after
-  // its issue.  Every iteration issues, past the last tile too (zeros), so
-  // the waits are constants; QK^T of tile ntiles in the last iteration reads
-  // such zeros, already landed, and its result is never used.
-  //
-  // Iteration j's softmax reads sbuf[j % 2] and QK^T writes sbuf[(j + 1) % 2];
-  // the loop is unrolled by the (even) stage count so both are static.
-  // PV of one tile on its own (the workgroup's last tile).
-  auto pv_tile = [&](const lds_char* vs) VA_INLINE {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int vb = 0; vb < C::VB; ++vb) {
-        const bf16x4 lo = lds_read_tr(vs, v_rd[vb] + (16 * t) * C::CPR_V * 16);
-        const bf16x4 hi = lds_read_tr(vs, v_rd[vb] + (16 * t + 8) * C::CPR_V * 16);
-        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb)
-          acc[vb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][t], acc[vb][qb], 0, 0, 0);
-      }
-  };
-  if (ntiles > 0) {
-    wait_landed(Int<kAhead - 1>{});  // tile 0 (tiles 0-3 were issued above)
-    lds_barrier();
-    if (active && w_beg == 0) qk_only(kst(Int<0>{}), sbuf[0]);  // QK^T(0)
-    wait_landed(Int<kAhead - 2>{});  // tile 1
-    lds_barrier();
-    // iteration 0 (no PV before it)
-    {
-      issue(Int<kAhead % kStages>{});
-      if (active && w_first == 0) {
-        mask(0, sbuf[0]);
-        qk_only(kst(Int<1>{}), sbuf[1]);
-        float alpha[C::QB];
-        const bool move = softmax(sbuf[0], alpha);
-        rescale(move, alpha);
-      }
-      wait_landed(Int<kAhead - 2>{});  // tile 2
-      lds_barrier();
-    }
-    for (int j0 = 1; j0 < ntiles; j0 += kStages) {  // tile j0 + u sits in stage (u + 1) % 6
-      static_for<0, kStages>([&](auto u) VA_INLINE {
-        constexpr int U = decltype(u)::value;
-        const int j = j0 + U;
-        if (U == 0 || j < ntiles) {
-          issue(Int<(U + 1 + kAhead) % kStages>{});  // tile j + 4 (zeros past the last)
-          if (active && j <= w_end && j >= w_first) {
-            constexpr int cur = (U + 1) % 2;  // j % 2, j0 being odd
-            mask(j, sbuf[cur]);
-            float sum[C::QB];
-            const bool slow = fused_block(vst(Int<U % kStages>{}), kst(Int<(U + 2) % kStages>{}), sbuf[cur],
-                                          sbuf[cur ^ 1], sum, j);
-            // The probabilities are only read in the next iteration and the
-            // row sums only on the fast path; without these uses the compiler
-            // sinks their computation past the branch below, out of the
-            // interleave, where nothing hides it.
-#pragma unroll
-            for (int qb = 0; qb < C::QB; ++qb) {
-              asm volatile("" ::"v"(pf[qb][0]), "v"(pf[qb][1]));
-              if constexpr (!SUM_BY_MFMA) asm volatile("" ::"v"(sum[qb]));
-            }
-            // Commit the row sums on one path (the slow path restores them):
-            // two paths merging into l_run cost the register allocator dearly.
-            float l_prev[C::QB];
-#pragma unroll
-            for (int qb = 0; qb < C::QB; ++qb) {
-              l_prev[qb] = l_run[qb];
-              if constexpr (!SUM_BY_MFMA) l_run[qb] += sum[qb];
-            }
-            if (slow) {
-              // Some row's max moved past m_run + kRescaleTau (or a row saw
-              // its first key): recompute this tile's scores from K, still
-              // in its stage, and take the full softmax with the rescale.
-              asm volatile("; softmax slow path" ::: "memory");
-#pragma unroll
-              for (int qb = 0; qb < C::QB; ++qb) l_run[qb] = l_prev[qb];
-              qk_only(kst(Int<(U + 1) % kStages>{}), sbuf[cur]);
-              mask(j, sbuf[cur]);
-              float alpha[C::QB];
-              const bool move = softmax(sbuf[cur], alpha);
-              rescale(move, alpha);
+          for (int jj = 0; jj < 4; ++jj) {
+            const int dv = vb * 32 + 8 * jj + 4 * g;
+            if (row < r1 && dv < DV) {
+              const f32x16& a = acc[vb][qb];
+              typedef float f32x4 __attribute__((ext_vector_type(4)));
+              const f32x4 o4 = {a[4 * jj] * inv, a[4 * jj + 1] * inv, a[4 * jj + 2] * inv, a[4 * jj + 3] * inv};
+              *(f32x4*)(dst + dv) = o4;
             }
           }
-          wait_landed(Int<kAhead - 2>{});  // tile j + 2
-          lds_barrier();
-        }
-      });
+        if (row < r1 && g == 0)
+          p.part_lse[((int64_t)split * p.heads + h) * p.total_q + q0 + row] =
+              l > 0.f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
+      }
+      continue;
     }
-    // The zero loads past the last tile must land before the workgroup's LDS
-    // can be handed to the next workgroup.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (active && w_end == ntiles) {  // PV of the last tile, its stage picked at run time (all DMA has landed)
-      const int last = (ntiles - 1) % kStages;
-      const lds_char* vs = vst(Int<0>{});
-      static_for<1, kStages>([&](auto st) VA_INLINE {
-        if (last == decltype(st)::value) vs = vst(st);
-      });
-      pv_tile(vs);
+    // Lane (row, g) holds d_v 8 jj + 4 g .. + 3 of its row for jj = 0..3 of
+    // each 32-wide block.  Swapping halves with lane row ^ 32 over a pair of
+    // chunks (jj, jj + 1) leaves lane g with the 8 contiguous values of chunk
+    // jj + g: one 16-byte store instead of two 8-byte ones per lane.
+    // With an output scale (varlen_attn_fwd_quant_out) the same values leave as
+    // e4m3 codes of O / out_scale, 8 bytes a lane.
+    if (p.out_scale != nullptr) {
+      const float os = 1.f / *p.out_scale;
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+        const float l = SUM_BY_MFMA ? from_lower_half(acc[C::VB - 1][qb][kSumReg]) : xhalf_sum(l_run[qb]);
+        const int row = wrow0 + 32 * qb + l32;
+        const float inv = l > 0.f ? os / l : 0.f;
+        uint8_t* dst = (uint8_t*)p.o + (int64_t)(q0 + row) * p.o_row + (int64_t)h * p.o_head;
+#pragma unroll
+        for (int vb = 0; vb < C::VB; ++vb)
+#pragma unroll
+          for (int jp = 0; jp < 4; jp += 2) {
+            const f32x16& a = acc[vb][qb];
+            const uint32_t x = quant_e4m3x4(a[4 * jp], a[4 * jp + 1], a[4 * jp + 2], a[4 * jp + 3], inv);
+            const uint32_t y = quant_e4m3x4(a[4 * jp + 4], a[4 * jp + 5], a[4 * jp + 6], a[4 * jp + 7], inv);
+            const auto sw = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+            const int dv = vb * 32 + 8 * (jp + g);
+            if (row < r1 && dv < DV) {
+              const u32x2 o2 = {sw[0], sw[1]};
+              *(u32x2*)(dst + dv) = o2;
+            }
+          }
+        if (row < r1 && p.lse != nullptr && g == 0)
+          p.lse[(int64_t)h * p.total_q + q0 + row] = l > 0.f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
+      }
+      continue;
     }
-  }
-
-  // ---- epilogue ---------------------------------------------------------------
-  // With SUM_BY_MFMA the row sum sits in column d_v of the accumulator:
-  // dv block VB - 1, register 4 * ((d_v % 32) / 8), lanes 0-31.
-  constexpr int kSumReg = 4 * ((DV % 32) / 8);
-  if (p.num_splits > 1) {
-    // Split-KV partial: O = acc / l in fp32 (lane (row, g) holds d_v 8 jj +
-    // 4 g .. + 3 of each 32-wide block: one 16-byte store each) and the LSE of
-    // this split's keys (-inf where a row saw none of them).
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) {
       const float l = SUM_BY_MFMA ? from_lower_half(acc[C::VB - 1][qb][kSumReg]) : xhalf_sum(l_run[qb]);
       const int row = wrow0 + 32 * qb + l32;
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      float* dst = p.part_o + (((int64_t)split * p.total_q + q0 + row) * p.heads + h) * DV;
-#pragma unroll
-      for (int vb = 0; vb < C::VB; ++vb)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int dv = vb * 32 + 8 * jj + 4 * g;
-          if (row < r1 && dv < DV) {
-            const f32x16& a = acc[vb][qb];
-            typedef float f32x4 __attribute__((ext_vector_type(4)));
-            const f32x4 o4 = {a[4 * jj] * inv, a[4 * jj + 1] * inv, a[4 * jj + 2] * inv, a[4 * jj + 3] * inv};
-            *(f32x4*)(dst + dv) = o4;
-          }
-        }
-      if (row < r1 && g == 0)
-        p.part_lse[((int64_t)split * p.heads + h) * p.total_q + q0 + row] =
-            l > 0.f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
-    }
-    return;
-  }
-  // Lane (row, g) holds d_v 8 jj + 4 g .. + 3 of its row for jj = 0..3 of
-  // each 32-wide block.  Swapping halves with lane row ^ 32 over a pair of
-  // chunks (jj, jj + 1) leaves lane g with the 8 contiguous values of chunk
-  // jj + g: one 16-byte store instead of two 8-byte ones per lane.
-  // With an output scale (varlen_attn_fwd_quant_out) the same values leave as
-  // e4m3 codes of O / out_scale, 8 bytes a lane.
-  if (p.out_scale != nullptr) {
-    const float os = 1.f / *p.out_scale;
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      const float l = SUM_BY_MFMA ? from_lower_half(acc[C::VB - 1][qb][kSumReg]) : xhalf_sum(l_run[qb]);
-      const int row = wrow0 + 32 * qb + l32;
-      const float inv = l > 0.f ? os / l : 0.f;
-      uint8_t* dst = (uint8_t*)p.o + (int64_t)(q0 + row) * p.o_row + (int64_t)h * p.o_head;
+      uint16_t* dst = p.o + (int64_t)(q0 + row) * p.o_row + (int64_t)h * p.o_head;
 #pragma unroll
       for (int vb = 0; vb < C::VB; ++vb)
 #pragma unroll
         for (int jp = 0; jp < 4; jp += 2) {
           const f32x16& a = acc[vb][qb];
-          const uint32_t x = quant_e4m3x4(a[4 * jp], a[4 * jp + 1], a[4 * jp + 2], a[4 * jp + 3], inv);
-          const uint32_t y = quant_e4m3x4(a[4 * jp + 4], a[4 * jp + 5], a[4 * jp + 6], a[4 * jp + 7], inv);
-          const auto sw = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+          const uint32_t x0 = pack_bf16x2(a[4 * jp] * inv, a[4 * jp + 1] * inv);
+          const uint32_t x1 = pack_bf16x2(a[4 * jp + 2] * inv, a[4 * jp + 3] * inv);
+          const uint32_t y0 = pack_bf16x2(a[4 * jp + 4] * inv, a[4 * jp + 5] * inv);
+          const uint32_t y1 = pack_bf16x2(a[4 * jp + 6] * inv, a[4 * jp + 7] * inv);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
           const int dv = vb * 32 + 8 * (jp + g);
           if (row < r1 && dv < DV) {
-            const u32x2 o2 = {sw[0], sw[1]};
-            *(u32x2*)(dst + dv) = o2;
+            const u32x4 o4 = {s0[0], s1[0], s0[1], s1[1]};
+            *(u32x4*)(dst + dv) = o4;
           }
         }
-      if (row < r1 && p.lse != nullptr && g == 0)
-        p.lse[(int64_t)h * p.total_q + q0 + row] = l > 0.f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
-    }
-    return;
-  }
-#pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    const float l = SUM_BY_MFMA ? from_lower_half(acc[C::VB - 1][qb][kSumReg]) : xhalf_sum(l_run[qb]);
-    const int row = wrow0 + 32 * qb + l32;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* dst = p.o + (int64_t)(q0 + row) * p.o_row + (int64_t)h * p.o_head;
-#pragma unroll
-    for (int vb = 0; vb < C::VB; ++vb)
-#pragma unroll
-      for (int jp = 0; jp < 4; jp += 2) {
-        const f32x16& a = acc[vb][qb];
-        const uint32_t x0 = pack_bf16x2(a[4 * jp] * inv, a[4 * jp + 1] * inv);
-        const uint32_t x1 = pack_bf16x2(a[4 * jp + 2] * inv, a[4 * jp + 3] * inv);
-        const uint32_t y0 = pack_bf16x2(a[4 * jp + 4] * inv, a[4 * jp + 5] * inv);
-        const uint32_t y1 = pack_bf16x2(a[4 * jp + 6] * inv, a[4 * jp + 7] * inv);
-        const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
-        const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
-        const int dv = vb * 32 + 8 * (jp + g);
-        if (row < r1 && dv < DV) {
-          const u32x4 o4 = {s0[0], s1[0], s0[1], s1[1]};
-          *(u32x4*)(dst + dv) = o4;
+      if (row < r1) {
+        if (p.lse != nullptr && g == 0) {
+          const float lse = l > 0.f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
+          p.lse[(int64_t)h * p.total_q + q0 + row] = lse;
         }
-      }
-    if (row < r1) {
-      if (p.lse != nullptr && g == 0) {
-        const float lse = l > 0.f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
-        p.lse[(int64_t)h * p.total_q + q0 + row] = lse;
       }
     }
   }
@@ -904,10 +925,21 @@ static int64_t launch_workgroups(int64_t units, const Variant& var) {
   return u == 1 ? units : (units / 8 + u - 1) / u * 8;
 }
 
+// Whether a launch pairs each segment's q-tiles n_b - 1 - t and t in one
+// workgroup (Params::pair_qt): causal, several q-tiles, one segment a
+// workgroup, unsplit, on the four-wave bf16 kernel at the head dims that run
+// one workgroup per CU (whose work units then all see the same number of key
+// tiles).
+static bool pair_q_tiles(bool causal, int32_t mode, const Variant& var, int64_t max_seqlen_q, bool split, bool fp8) {
+  return causal && !split && !fp8 && mode == kPackNone && var.units_per_wg == 1 && var.per_cu == 1 &&
+         max_seqlen_q > var.block_m;
+}
+
 static int64_t launch_units(int64_t batch, int64_t heads, int64_t max_seqlen_q, int block_m, int32_t mode,
-                            int32_t hs, int32_t* n_qt_out, int32_t* pack_out) {
+                            int32_t hs, int32_t* n_qt_out, int32_t* pack_out, bool pair = false) {
   const int32_t pack = mode == kPackNone ? 1 : segments_per_block(max_seqlen_q, block_m / 4);
-  const int64_t n_qt = pack > 1 ? 1 : (max_seqlen_q + block_m - 1) / block_m;
+  const int64_t n_qt1 = pack > 1 ? 1 : (max_seqlen_q + block_m - 1) / block_m;
+  const int64_t n_qt = pair ? (n_qt1 + 1) / 2 : n_qt1;  // q-tiles, or pairs of them
   if (n_qt_out) *n_qt_out = (int32_t)n_qt;
   if (pack_out) *pack_out = pack;
   if (mode == kPackHeads) return grid_blocks(batch, heads / pack, 1);
@@ -984,8 +1016,9 @@ extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_h
   const int32_t mode = lc.mode;
   const va::Variant var = lc.var;
   const int32_t hs = va::launch_hs(head_dim_qk, head_dim_v, num_heads, num_heads_k, mode, false, max_q, var, batch);
+  const bool pair = va::pair_q_tiles(causal != 0, mode, var, max_q, false, false);
   int32_t n_qt = 0, pack = 1;
-  if (block < 0 || block >= va::launch_units(batch, num_heads, max_q, var.block_m, mode, hs, &n_qt, &pack))
+  if (block < 0 || block >= va::launch_units(batch, num_heads, max_q, var.block_m, mode, hs, &n_qt, &pack, pair))
     return VA_ERR_ARG;
   if (mode == va::kPackHeads) {  // (segment, first query head of the group)
     const int32_t vheads = num_heads / pack;
@@ -999,13 +1032,20 @@ extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_h
   const int32_t groups = (batch + pack - 1) / pack;
   const va::WorkUnit u = pack == 1 && va::lpt_applies(batch, seqlens_q, seqlens_k)
                              ? va::decode_block_lpt(block, batch, num_heads, var.block_m, n_qt, causal,
-                                                    seqlens_q, seqlens_k, hs)
+                                                    seqlens_q, seqlens_k, hs, pair)
                              : va::decode_block((uint32_t)block, (uint32_t)groups,
                                                 va::make_fastdiv((uint32_t)(num_heads >> hs)),
                                                 va::make_fastdiv((uint32_t)(n_qt << hs)), (uint32_t)hs, causal);
-  *segment = u.valid ? u.b * pack : -1;
-  *head = u.valid ? va::query_head(u.h, va::make_fastdiv((uint32_t)num_heads_k), num_heads / num_heads_k) : -1;
-  *q_tile = u.valid ? u.qt : -1;
+  int32_t qt = u.qt;
+  bool valid = u.valid;
+  if (valid && pair) {  // pair t: q-tile n_b - 1 - t first (none past the segment's middle)
+    const int32_t nb = (seqlens_q[u.b] + var.block_m - 1) / var.block_m;
+    valid = nb - 1 - u.qt >= u.qt;
+    qt = nb - 1 - u.qt;
+  }
+  *segment = valid ? u.b * pack : -1;
+  *head = valid ? va::query_head(u.h, va::make_fastdiv((uint32_t)num_heads_k), num_heads / num_heads_k) : -1;
+  *q_tile = valid ? qt : -1;
   return VA_OK;
 }
 
@@ -1013,7 +1053,6 @@ extern "C" int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t
                                 int32_t num_heads, int32_t num_heads_k, int32_t max_seqlen_q,
                                 int32_t max_seqlen_k, int32_t causal, va_plan* plan) {
   (void)max_seqlen_k;
-  (void)causal;
   if (!plan) return VA_ERR_NULL;
   if (!va::supported_dims(head_dim_qk, head_dim_v)) return VA_ERR_HEADDIM;
   if (batch < 0 || num_heads <= 0 || max_seqlen_q < 0) return VA_ERR_ARG;
@@ -1026,14 +1065,16 @@ extern "C" int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t
   plan->block_n = var.block_n;
   plan->threads = var.threads;
   plan->lds_bytes = var.lds_bytes;
+  const bool pair = va::pair_q_tiles(causal != 0, mode, var, max_seqlen_q, false, false);
   plan->units = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, mode,
                                  va::launch_hs(head_dim_qk, head_dim_v, num_heads, num_heads_k, mode, false,
                                                max_seqlen_q, var, batch),
                                  nullptr,
-                                 &plan->segments_per_block);
+                                 &plan->segments_per_block, pair);
   plan->grid = va::launch_workgroups(plan->units, var);
   plan->pack_mode = mode;
   plan->kernel = var.name;
+  plan->pair_q_tiles = pair ? 1 : 0;
   return VA_OK;
 }
 
@@ -1060,6 +1101,7 @@ extern "C" int varlen_attn_plan_fp8(int32_t head_dim_qk, int32_t head_dim_v, int
   plan->grid = va::launch_workgroups(plan->units, var);
   plan->pack_mode = mode;
   plan->kernel = var.name;
+  plan->pair_q_tiles = 0;
   return VA_OK;
 }
 
@@ -1122,6 +1164,7 @@ static int prepare(const va_tensor* q, const va_tensor* k, const va_tensor* v, c
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   p.num_splits = 1;
   p.splits_dyn = nullptr;
+  p.pair_qt = 0;
   p.part_o = nullptr;
   p.part_lse = nullptr;
   p.q_descale = p.k_descale = p.v_descale = p.out_scale = nullptr;
@@ -1144,7 +1187,9 @@ static int launch_attention(Params& p, int32_t head_dim_qk, int32_t head_dim_v, 
     mode = lc.mode;
   }
   const int32_t hs = launch_hs(head_dim_qk, head_dim_v, p.heads, p.heads_k, mode, fp8, max_seqlen_q, var, p.batch);
-  const int64_t units = launch_units(p.batch, p.heads, max_seqlen_q, var.block_m, mode, hs, &p.n_qt, &p.pack);
+  const bool pair = pair_q_tiles(p.causal != 0, mode, var, max_seqlen_q, p.num_splits > 1 || p.splits_dyn != nullptr, fp8);
+  p.pair_qt = pair ? 1 : 0;
+  const int64_t units = launch_units(p.batch, p.heads, max_seqlen_q, var.block_m, mode, hs, &p.n_qt, &p.pack, pair);
   if (units > INT32_MAX) return VA_ERR_SHAPE;
   p.n_units = (int32_t)units;
   // The work-unit decode's divisors (the kernel divides by multiplying).

@@ -190,6 +190,28 @@ def test_fp8_small_parity(dims, mode, lens):
     assert torch.equal(out, out2)
 
 
+@pytest.mark.parametrize("dims", DIMS, ids=lambda d: "d%d_%d" % d)
+@pytest.mark.parametrize("mode", ["causal", "causal_window"])
+@pytest.mark.parametrize("order", ["longest_first", "packing_order"])
+def test_fp8_causal_multi_tile_segments(dims, mode, order):
+    """Causal segments of many q-tiles (odd and even counts, one-tile and
+    empty segments, a ragged last tile, Lq != Lk), dealt longest first and in
+    packing order; the e4m3 kernel runs one q-tile a workgroup."""
+    if order == "longest_first":
+        lq = [1029, 512, 40, 700, 513, 1280, 1, 0]
+        lk = [1029, 600, 333, 901, 513, 1280, 1, 0]
+    else:
+        rng = np.random.default_rng(dims[0] + 1)
+        lq = [int(x) for x in rng.integers(0, 1100, 70)]
+        lq[0], lq[1], lq[2] = 1100, 256, 257
+        lk = [x if i % 4 else x + int(rng.integers(0, 200)) for i, x in enumerate(lq)]
+    assert va.plan(dims[0], dims[1], len(lq), 2, max(lq), max(lk), 1, fp8=True)["pair_q_tiles"] == 0
+    inp = make(lq, lk, dims, seed=zlib.crc32(("multi %s %s %s" % (dims, mode, order)).encode()) % 10000,
+               mode=mode, heads=2)
+    out, lse = run_fp8(inp)
+    assert_fp8_parity(inp, out, lse, what="multi %s %s %s" % (dims, mode, order))
+
+
 @pytest.mark.parametrize("dims", [(128, 128), (192, 128)], ids=lambda d: "d%d_%d" % d)
 @pytest.mark.parametrize("heads,heads_k", [(8, 1), (8, 2), (6, 3)])
 @pytest.mark.parametrize("mode", ["full", "causal"])

@@ -304,13 +304,15 @@ __global__ __launch_bounds__(64 * wide::kWaves, DQK <= 80 ? 2 : 1) void attn_fwd
       v_off[x] = (i < C::V_WL && sl < C::V_SLOTS && c < C::V_REAL) ? (uint32_t)(row * v_row_b + c * 16) : kOOB;
     }
     // K/V rows of the next tile to issue, advanced one tile per issue; tiles
-    // past the last get an empty range (all reads zero).
+    // past the workgroup's last (tr.kt_end, which for a causal q-tile is its
+    // diagonal, not the segment's end) get an empty range, so the prefetches
+    // past it read zeros instead of keys no row sees.
     const int hk = (int)fdiv((uint32_t)h, p.fd_group);  // the KV head query head h reads
     const char* k_next =
         (const char*)(p.k + ((int64_t)k0 + (int64_t)tr.kt_begin * kBN) * p.k_row + (int64_t)hk * p.k_head);
     const char* v_next =
         (const char*)(p.v + ((int64_t)k0 + (int64_t)tr.kt_begin * kBN) * p.v_row + (int64_t)hk * p.v_head);
-    int keys_next = Lk - tr.kt_begin * kBN;
+    int keys_next = min(Lk, tr.kt_end * kBN) - tr.kt_begin * kBN;
     auto issue = [&](auto st) VA_INLINE {  // this wave's loads of the next tile into stage st
       // (readfirstlane: the clamp compiles to a VALU med3, and a descriptor
       // the compiler cannot prove uniform costs a waterfall loop per load)

@@ -262,7 +262,9 @@ __global__ __launch_bounds__(64 * fp8k::kWaves, 1) void attn_fwd_fp8(Params p) {
       (const char*)p.k + ((int64_t)k0 + (int64_t)tr.kt_begin * kBN) * p.k_row + (int64_t)hk * p.k_head;
   const char* v_next =
       (const char*)p.v + ((int64_t)k0 + (int64_t)tr.kt_begin * kBN) * p.v_row + (int64_t)hk * p.v_head;
-  int keys_next = Lk - tr.kt_begin * kBN;
+  // (prefetches past the workgroup's last tile, a causal q-tile's diagonal,
+  // read zeros: an empty range)
+  int keys_next = min(Lk, tr.kt_end * kBN) - tr.kt_begin * kBN;
   auto issue = [&](auto st) VA_INLINE {
     const int rows = __builtin_amdgcn_readfirstlane(max(min(keys_next, kBN), 0));
     const __amdgpu_buffer_rsrc_t rk =

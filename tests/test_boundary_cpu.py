@@ -424,25 +424,32 @@ def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
             assert qt >= (-(-lq[b] // bm) if longest_first else n_qt) - 4
 
 
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("heads,heads_k,lq", [(64, 8, [4096, 4096]), (32, 4, [700, 900, 33]), (12, 1, [300]),
                                               (16, 16, [1000, 2000]), (24, 8, [513] * 3)])
-def test_work_unit_grouped_kv_heads(heads, heads_k, lq):
+def test_work_unit_grouped_kv_heads(heads, heads_k, lq, causal):
     """With grouped KV heads every (segment, query head, q-tile) is still owned
-    once, and when the KV heads are a multiple of 8 the query heads of one KV
-    head all run on one XCD (block % 8), sharing its L2."""
-    p = pkg.plan(128, 128, len(lq), heads, max(lq), max(lq), 0)
+    once (causal: q-tiles in pairs qt, n_b - 1 - qt), and when the KV heads
+    are a multiple of 8 the query heads of one KV head all run on one XCD
+    (block % 8), sharing its L2."""
+    p = pkg.plan(128, 128, len(lq), heads, max(lq), max(lq), int(causal))
     bm = p["block_m"]
+    assert p["pair_q_tiles"] == int(causal and max(lq) > bm)
     longest_first = len(set(lq)) > 1
     n_qt = -(-max(lq) // bm)
     want = {(b, h, qt) for b in range(len(lq)) for h in range(heads)
             for qt in range(-(-lq[b] // bm) if longest_first else n_qt)}
     seen, xcd_of = set(), {}
     for blk in range(p["grid"]):
-        b, h, qt = pkg.work_unit(blk, heads, 128, 128, lq, lq, False, num_heads_k=heads_k)
+        b, h, qt = pkg.work_unit(blk, heads, 128, 128, lq, lq, causal, num_heads_k=heads_k)
         if b < 0:
             continue
-        assert (b, h, qt) not in seen
-        seen.add((b, h, qt))
+        tiles = [qt]
+        if p["pair_q_tiles"] and 2 * qt > -(-lq[b] // bm) - 1:
+            tiles.append(-(-lq[b] // bm) - 1 - qt)
+        for t in tiles:
+            assert (b, h, t) not in seen
+            seen.add((b, h, t))
         xcd_of.setdefault((b, h // (heads // heads_k)), set()).add(blk % 8)
     assert seen == want
     if heads_k % 8 == 0:

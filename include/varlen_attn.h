@@ -422,7 +422,9 @@ typedef struct va_plan {
   int32_t pair_q_tiles;       /* 1 when each work unit runs two q-tiles of one segment, n_b - 1 - t
                                  and then t (n_b = ceil(seqlen_q / block_m)), so that every unit
                                  of a causal launch sees the same number of key tiles: causal,
-                                 max_seqlen_q > block_m, unpacked, attn_fwd_wide, unsplit */
+                                 max_seqlen_q > block_m, unpacked, attn_fwd_wide at
+                                 head_dim_qk > 80, unsplit, and at least 512 units unpaired (two
+                                 rounds of one workgroup per CU) */
 } va_plan;
 
 int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch, int32_t num_heads,

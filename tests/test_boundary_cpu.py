@@ -317,6 +317,20 @@ def _short_head_group_shift(d_qk, d_v, heads, batch):
     return s_
 
 
+def _expect_pairs(dq, dv, batch, heads, max_q, max_k, heads_k=None):
+    """Whether a causal launch of the four-wave kernel pairs q-tiles: head dims
+    that run one workgroup per CU (d_qk > 80), several q-tiles, unpacked, at
+    least two rounds of unpaired units on each XCD (padded grid / 8 over its 32
+    CUs) and pairs that fill at least 15/16 of their last round."""
+    p0 = pkg.plan(dq, dv, batch, heads, max_q, max_k, 0, num_heads_k=heads_k or heads)
+    n_qt = -(-max_q // p0["block_m"])
+    if dq <= 80 or n_qt < 2 or p0["segments_per_block"] != 1 or p0["pack_mode"] != 0:
+        return False
+    solo = p0["units"] // 8
+    pairs = solo // n_qt * ((n_qt + 1) // 2)
+    return solo >= 64 and 16 * pairs >= 15 * 32 * -(-pairs // 32)
+
+
 @pytest.mark.parametrize("lq,lk,heads,causal,dims", [
     ([4096] * 8, [4096] * 8, 16, 0, (80, 80)),            # alike: packing order
     ([256] * 36, [256] * 36, 16, 0, (80, 80)),
@@ -369,7 +383,7 @@ def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
     # causal launches of the one-workgroup-per-CU head dims: a unit runs
     # q-tile qt and then n_b - 1 - qt, so every unit has n_b + 1 key tiles
     pair = p["pair_q_tiles"] == 1
-    assert pair == (bool(causal) and dims[0] > 80 and max_q > bm and pack == 1)
+    assert pair == (bool(causal) and _expect_pairs(dims[0], dims[1], batch, heads, max_q, max(lk)))
     n_units_qt = (n_qt + 1) // 2 if pair else n_qt
     # tiles each segment must get: its own q-tiles when dealt longest first,
     # else the same number for every segment (tiles past its end exit early)
@@ -434,9 +448,9 @@ def test_work_unit_grouped_kv_heads(heads, heads_k, lq, causal):
     (block % 8), sharing its L2."""
     p = pkg.plan(128, 128, len(lq), heads, max(lq), max(lq), int(causal))
     bm = p["block_m"]
-    assert p["pair_q_tiles"] == int(causal and max(lq) > bm)
     longest_first = len(set(lq)) > 1
     n_qt = -(-max(lq) // bm)
+    assert p["pair_q_tiles"] == int(causal and _expect_pairs(128, 128, len(lq), heads, max(lq), max(lq), heads_k))
     want = {(b, h, qt) for b in range(len(lq)) for h in range(heads)
             for qt in range(-(-lq[b] // bm) if longest_first else n_qt)}
     seen, xcd_of = set(), {}
@@ -709,13 +723,13 @@ def test_quant_out_validation():
 def test_plan_fp8(dims, lds_kib):
     """The fp8 kernel: 256-row workgroups of 4 waves, 64-key tiles (one fp8
     PV MFMA takes 64 keys), six LDS stages of K (plus a pad chunk a row) and
-    V bytes; the grid is the bf16 kernel's (same work units), save that the
-    bf16 kernel pairs the 16 causal q-tiles of a d_qk > 80 segment in 8
-    workgroups and the fp8 kernel does not."""
+    V bytes; the grid is the bf16 kernel's (same work units), save where the
+    bf16 kernel pairs causal q-tiles (not here: 48 pairs an XCD would fill
+    3/4 of their second round); the fp8 kernel never does."""
     p8 = pkg.plan(dims[0], dims[1], 3, 16, 4096, 4096, 1, fp8=True)
     p16 = pkg.plan(dims[0], dims[1], 3, 16, 4096, 4096, 1)
     assert p8["kernel"] == "attn_fwd_fp8" and p8["block_n"] == 64 and p8["block_m"] == 256
-    assert p16["pair_q_tiles"] == (dims[0] > 80) and p8["pair_q_tiles"] == 0
+    assert p16["pair_q_tiles"] == _expect_pairs(dims[0], dims[1], 3, 16, 4096, 4096) and p8["pair_q_tiles"] == 0
     assert p8["threads"] == 256 and p8["grid"] == p16["grid"] * (2 if p16["pair_q_tiles"] else 1)
     assert p8["lds_bytes"] // 1024 == lds_kib and p8["lds_bytes"] <= 160 * 1024
     with pytest.raises(ValueError):

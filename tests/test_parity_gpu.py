@@ -133,22 +133,26 @@ def test_multi_block_segments(dims, mode):
 @pytest.mark.parametrize("order", ["longest_first", "packing_order"])
 def test_causal_q_tile_pairs(dims, mode, order):
     """Causal launches at d_qk 128/192 run q-tiles n_b - 1 - t and t of a
-    segment in one workgroup: odd and even q-tile counts (the middle tile of
-    an odd count runs alone), one-tile segments, a ragged last tile, Lq != Lk,
-    dealt longest first (few segments) and in packing order (more than 64)."""
+    segment in one workgroup where the pairs fill their rounds: odd and even
+    q-tile counts (the middle tile of an odd count runs alone), one-tile
+    segments, a ragged last tile, Lq != Lk, dealt longest first (few segments)
+    and in packing order (more than 64)."""
     d_qk, d_v = dims
     causal, window = MODES[mode]
+    # shapes whose pairs fill their rounds: 8 x 8 groups of 4 pairs, 128 x 2 of 2
     if order == "longest_first":
-        lq = [1029, 512, 40, 700, 513, 1280, 1, 0]
-        lk = [1029, 600, 333, 901, 513, 1280, 1, 0]
+        lq = [1029, 512, 40, 700, 513, 2048, 1, 0]
+        lk = [1029, 600, 333, 901, 513, 2048, 1, 0]
+        heads = 8
     else:
         rng = np.random.default_rng(d_qk)
-        lq = [int(x) for x in rng.integers(0, 1100, 70)]
-        lq[0], lq[1], lq[2] = 1100, 256, 257
+        lq = [int(x) for x in rng.integers(0, 769, 128)]
+        lq[0], lq[1], lq[2] = 768, 256, 257
         lk = [x if i % 4 else x + int(rng.integers(0, 200)) for i, x in enumerate(lq)]
-    assert va.plan(d_qk, d_v, len(lq), 2, max(lq), max(lk), 1)["pair_q_tiles"] == 1
+        heads = 2
+    assert va.plan(d_qk, d_v, len(lq), heads, max(lq), max(lk), 1)["pair_q_tiles"] == 1
     seed = zlib.crc32(repr(("pairs", dims, mode, order)).encode()) % 1000
-    inp = workloads.make_inputs(lq, lk, 2, d_qk, d_v, seed=seed, causal=causal, window=window)
+    inp = workloads.make_inputs(lq, lk, heads, d_qk, d_v, seed=seed, causal=causal, window=window)
     out, lse = run_gpu(inp)
     ref_o, ref_lse = oracle_on(inp)
     assert_parity(out, lse, ref_o, ref_lse, what="pairs/%s/%s/%s" % (dims, mode, order))

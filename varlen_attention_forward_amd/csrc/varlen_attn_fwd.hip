@@ -927,16 +927,6 @@ static int64_t launch_workgroups(int64_t units, const Variant& var) {
   return u == 1 ? units : (units / 8 + u - 1) / u * 8;
 }
 
-// Whether a launch pairs each segment's q-tiles n_b - 1 - t and t in one
-// workgroup (Params::pair_qt): causal, several q-tiles, one segment a
-// workgroup, unsplit, on the four-wave bf16 kernel at the head dims that run
-// one workgroup per CU (whose work units then all see the same number of key
-// tiles).
-static bool pair_q_tiles(bool causal, int32_t mode, const Variant& var, int64_t max_seqlen_q, bool split, bool fp8) {
-  return causal && !split && !fp8 && mode == kPackNone && var.units_per_wg == 1 && var.per_cu == 1 &&
-         max_seqlen_q > var.block_m;
-}
-
 static int64_t launch_units(int64_t batch, int64_t heads, int64_t max_seqlen_q, int block_m, int32_t mode,
                             int32_t hs, int32_t* n_qt_out, int32_t* pack_out, bool pair = false) {
   const int32_t pack = mode == kPackNone ? 1 : segments_per_block(max_seqlen_q, block_m / 4);
@@ -946,6 +936,28 @@ static int64_t launch_units(int64_t batch, int64_t heads, int64_t max_seqlen_q, 
   if (pack_out) *pack_out = pack;
   if (mode == kPackHeads) return grid_blocks(batch, heads / pack, 1);
   return grid_blocks((batch + pack - 1) / pack, heads >> hs, n_qt << hs);
+}
+
+// Whether a launch pairs each segment's q-tiles n_b - 1 - t and t in one
+// workgroup (Params::pair_qt): causal, several q-tiles, one segment a
+// workgroup, unsplit, on the four-wave bf16 kernel at the head dims that run
+// one workgroup per CU, whose work units then all see the same number of key
+// tiles.  The dealing gives each XCD an equal share of the padded grid (its
+// units / 8) for its 32 CUs.  Pairs pay where the unpaired units take at
+// least two rounds of an XCD (in one round the longest q-tile sets the time
+// either way) and the pairs fill their last round (at least 15/16 of it):
+// otherwise half-empty rounds of double-length workgroups cost more than the
+// unequal q-tiles lose to in-order dispatch.
+static constexpr int64_t kCusPerXcd = 32;
+static bool pair_q_tiles(bool causal, int32_t mode, const Variant& var, int64_t batch, int64_t heads,
+                         int64_t max_seqlen_q, int32_t hs, bool split, bool fp8) {
+  if (!causal || split || fp8 || mode != kPackNone || var.units_per_wg != 1 || var.per_cu != 1 ||
+      max_seqlen_q <= var.block_m)
+    return false;
+  const int64_t solo = launch_units(batch, heads, max_seqlen_q, var.block_m, mode, hs, nullptr, nullptr) / 8;
+  const int64_t pairs = launch_units(batch, heads, max_seqlen_q, var.block_m, mode, hs, nullptr, nullptr, true) / 8;
+  const int64_t rounds = (pairs + kCusPerXcd - 1) / kCusPerXcd;
+  return solo >= 2 * kCusPerXcd && 16 * pairs >= 15 * kCusPerXcd * rounds;
 }
 
 // Row strides above 2^24 elements would overflow the 32-bit offsets of the
@@ -1018,7 +1030,7 @@ extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_h
   const int32_t mode = lc.mode;
   const va::Variant var = lc.var;
   const int32_t hs = va::launch_hs(head_dim_qk, head_dim_v, num_heads, num_heads_k, mode, false, max_q, var, batch);
-  const bool pair = va::pair_q_tiles(causal != 0, mode, var, max_q, false, false);
+  const bool pair = va::pair_q_tiles(causal != 0, mode, var, batch, num_heads, max_q, hs, false, false);
   int32_t n_qt = 0, pack = 1;
   if (block < 0 || block >= va::launch_units(batch, num_heads, max_q, var.block_m, mode, hs, &n_qt, &pack, pair))
     return VA_ERR_ARG;
@@ -1067,11 +1079,10 @@ extern "C" int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t
   plan->block_n = var.block_n;
   plan->threads = var.threads;
   plan->lds_bytes = var.lds_bytes;
-  const bool pair = va::pair_q_tiles(causal != 0, mode, var, max_seqlen_q, false, false);
-  plan->units = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, mode,
-                                 va::launch_hs(head_dim_qk, head_dim_v, num_heads, num_heads_k, mode, false,
-                                               max_seqlen_q, var, batch),
-                                 nullptr,
+  const int32_t hs = va::launch_hs(head_dim_qk, head_dim_v, num_heads, num_heads_k, mode, false, max_seqlen_q, var,
+                                   batch);
+  const bool pair = va::pair_q_tiles(causal != 0, mode, var, batch, num_heads, max_seqlen_q, hs, false, false);
+  plan->units = va::launch_units(batch, num_heads, max_seqlen_q, var.block_m, mode, hs, nullptr,
                                  &plan->segments_per_block, pair);
   plan->grid = va::launch_workgroups(plan->units, var);
   plan->pack_mode = mode;
@@ -1189,7 +1200,8 @@ static int launch_attention(Params& p, int32_t head_dim_qk, int32_t head_dim_v, 
     mode = lc.mode;
   }
   const int32_t hs = launch_hs(head_dim_qk, head_dim_v, p.heads, p.heads_k, mode, fp8, max_seqlen_q, var, p.batch);
-  const bool pair = pair_q_tiles(p.causal != 0, mode, var, max_seqlen_q, p.num_splits > 1 || p.splits_dyn != nullptr, fp8);
+  const bool pair = pair_q_tiles(p.causal != 0, mode, var, p.batch, p.heads, max_seqlen_q, hs,
+                                 p.num_splits > 1 || p.splits_dyn != nullptr, fp8);
   p.pair_qt = pair ? 1 : 0;
   const int64_t units = launch_units(p.batch, p.heads, max_seqlen_q, var.block_m, mode, hs, &p.n_qt, &p.pack, pair);
   if (units > INT32_MAX) return VA_ERR_SHAPE;

@@ -26,6 +26,9 @@ Other modes (for the summaries under profiles/):
                                             a HIP graph, the host-inclusive eager rate
                                             and the shader clock seen meanwhile; then
                                             the merge of two MLA-shaped partials (GB/s)
+    python bench.py --pages                the same protocol over the shapes of the
+                                            SGLang PR #41344 speed tables (16 heads,
+                                            d 64/72/80, non-causal, no LSE)
 """
 from __future__ import annotations
 
@@ -445,7 +448,7 @@ class ClockSampler:
         return sum(1 for t in self.times if since is None or t >= since)
 
 
-def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -> None:
+def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20, registry=None) -> None:
     """Per workload: best and median of `rounds` rounds of `timed` launches
     (HIP events on the launch stream, `warmup` untimed launches before each),
     the same `timed` launches captured once in a HIP graph and replayed
@@ -458,7 +461,7 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20) -
 
     rows = []
     for name in names:
-        w = workloads.WORKLOADS[name]
+        w = (registry or workloads.WORKLOADS)[name]
         print("report: %s" % name, file=sys.stderr, flush=True)
         copies = device_inputs(w, workloads.workload_inputs(w))
         flops, nbytes = algorithmic_flops(w), algorithmic_bytes(w)
@@ -753,6 +756,8 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--report", action="store_true",
                     help="timing protocol over every workload (or --workload if given explicitly)")
+    ap.add_argument("--pages", action="store_true",
+                    help="the same protocol over the shapes of the SGLang PR #41344 speed tables")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -761,6 +766,11 @@ def main() -> int:
         return 2
     if args.copy_calibration:
         copy_calibration()
+        return 0
+    if args.pages:
+        from varlen_attention_forward_amd import workloads
+
+        protocol_report(list(workloads.PAGE_SHAPES), registry=workloads.PAGE_SHAPES)
         return 0
     if args.report:
         from varlen_attention_forward_amd import workloads

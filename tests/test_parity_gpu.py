@@ -746,9 +746,11 @@ def test_workload_full_oracle(name):
     ("vit_long65536_d128", 1024, None),
     ("mla_causal_192_128", 128, None),
     ("gqa_chunk64_d128", 256, None),
+    ("page_1x32768_d72", 256, None),   # shapes of the pages' speed tables
+    ("page_64x1024_d64", 256, None),
 ])
 def test_workload_sampled(name, n_random, heads):
-    w = workloads.WORKLOADS[name]
+    w = workloads.WORKLOADS[name] if name in workloads.WORKLOADS else workloads.PAGE_SHAPES[name]
     inp = workloads.workload_inputs(w)
     out, lse = run_gpu(inp, return_lse=w.return_lse)
     rows = _sample_rows(inp, n_random)

@@ -229,6 +229,29 @@ def _named_workloads() -> dict:
 
 
 WORKLOADS = _named_workloads()
+
+
+def _page_shapes() -> dict:
+    """The shapes of the speed tables on the SGLang PR #41344 page ("Speed
+    Tests and Profiling": the tcgen05.ld.red on/off kernel times and the d=64
+    ViT call timings): images of equal length, 16 heads, non-causal, no LSE.
+    Timed by ``bench.py --pages`` beside the page's own figures (another GPU:
+    context, not a target); the two rows whose segment lengths the page does
+    not state (8 mixed-size images, a 32-frame video) are left out."""
+    shapes = [(8, 4096, 80), (8, 4096, 72), (8, 4096, 64), (64, 1024, 80), (64, 1024, 64),
+              (1, 32768, 80), (1, 32768, 72), (1, 32768, 64),
+              (1, 256, 64), (1, 1024, 64), (4, 1024, 64), (16, 1024, 64), (1, 4096, 64), (4, 4096, 64),
+              (1, 16384, 64)]
+    ws = {}
+    for n, L, d in shapes:
+        name = "page_%dx%d_d%d" % (n, L, d)
+        ws[name] = Workload(name=name, seed=7, seqlens_q=(L,) * n, seqlens_k=(L,) * n, num_heads=16,
+                            head_dim_qk=d, head_dim_v=d, causal=False, return_lse=False,
+                            description="%d image(s) x %d tokens, 16 heads, d=%d, non-causal, no LSE" % (n, L, d))
+    return ws
+
+
+PAGE_SHAPES = _page_shapes()
 WORKLOAD_ORDER = (
     "tiny_varlen_d64",
     "vit_full_d80",

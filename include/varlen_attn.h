@@ -383,7 +383,10 @@ int varlen_attn_tile_range(int32_t seqlen_q, int32_t seqlen_k, int32_t row_begin
  * one.  Segments of at most 64 queries with head dims <= 80 (and no grouped query
  * heads to pack instead) run one wave per (segment, head) on the
  * short-segment kernel (va_plan.kernel "attn_fwd_short", block_m 64): q-tile
- * 0 of each, a segment's heads dealt to one XCD in groups of up to 16.  When
+ * 0 of each, a segment's heads dealt to one XCD in groups of up to 16.  On
+ * small launches of longer segments (va_plan.key_split 4) the same kernel
+ * takes unit `block` per workgroup: q-tile `q_tile` of 64 rows, its key
+ * tiles split over the workgroup's four waves.  When
  * short segments share workgroups (va_plan.segments_per_block P > 1, every
  * segment at most 128 queries), workgroup `block` owns segments
  * [segment, segment + P) (those that exist), their q-tile 0 (pack_mode 1),
@@ -423,8 +426,16 @@ typedef struct va_plan {
                                  and then t (n_b = ceil(seqlen_q / block_m)), so that every unit
                                  of a causal launch sees the same number of key tiles: causal,
                                  max_seqlen_q > block_m, unpacked, attn_fwd_wide at
-                                 head_dim_qk > 80, unsplit, and at least 512 units unpaired (two
-                                 rounds of one workgroup per CU) */
+                                 head_dim_qk > 80, unsplit, where the unpaired units fill at least
+                                 two rounds of each XCD's 32 CUs (the padded grid / 8) and the
+                                 pairs at least 15/16 of their last round */
+  int32_t key_split;          /* waves of a workgroup that share one work unit and split its key
+                                 tiles: 4 for attn_fwd_short on launches of segments longer than
+                                 64 queries (head dims <= 80, unsplit) whose 64-row blocks fit one
+                                 round on every XCD: 8 x ceil(batch x num_heads / 8) x
+                                 ceil(max_seqlen_q / 64) <= 512 (an XCD's eighth: two workgroups
+                                 on each of its 32 CUs); one block a workgroup, the waves' partial
+                                 results merged in LDS; else 1 */
 } va_plan;
 
 int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t batch, int32_t num_heads,

@@ -161,12 +161,20 @@ def test_plan():
     # one launch shape for every head dim and segment length
     short = pkg.plan(80, 80, 36, 16, 256, 256)
     assert short["kernel"] == "attn_fwd_wide" and short["block_m"] == 256 and short["threads"] == 256
-    assert pkg.plan(64, 64, 1, 16, 257, 257)["kernel"] == "attn_fwd_wide"
+    assert pkg.plan(64, 64, 16, 16, 257, 257)["kernel"] == "attn_fwd_wide"
     assert pkg.plan(128, 128, 1, 16, 4096, 4096)["kernel"] == "attn_fwd_wide"
+    # 64-row blocks that fit one round of two workgroups a CU on each XCD
+    # (2 x 8 (segment, head) groups x 5 blocks = 80 <= 8 x 64):
+    # the short-segment kernel, a workgroup's four waves splitting each block's keys
+    ks = pkg.plan(64, 64, 1, 16, 257, 257)
+    assert (ks["kernel"], ks["block_m"], ks["threads"], ks["key_split"]) == ("attn_fwd_short", 64, 256, 4)
+    assert ks["grid"] == ks["units"] == 8 * 2 * 5  # 16 heads pad to 2 x 8 groups, 5 blocks of 64
+    assert pkg.plan(128, 128, 1, 16, 257, 257)["key_split"] == 1  # head dims > 80: four-wave kernel
+    assert p["key_split"] == 1 and short["key_split"] == 1
     # 8 x 16 (segment, head) groups, already a multiple of the 8 XCDs
     assert p["grid"] == 8 * 16 * -(-4096 // p["block_m"])
     # 3 x 5 = 15 groups pad to 16
-    assert pkg.plan(80, 80, 3, 5, 4096, 4096)["grid"] == 16 * -(-4096 // p["block_m"])
+    assert pkg.plan(128, 128, 3, 5, 4096, 4096)["grid"] == 16 * -(-4096 // p["block_m"])
     with pytest.raises(ValueError):
         pkg.plan(96, 96, 1, 1, 10, 10)
 
@@ -353,17 +361,20 @@ def test_work_unit_covers_every_tile_once(lq, lk, heads, causal, dims):
     batch, max_q = len(lq), max(lq)
     p = pkg.plan(dims[0], dims[1], batch, heads, max_q, max(lk), causal)
     short = p["kernel"] == "attn_fwd_short"  # one wave per (segment, head, 64 rows)
+    # small launches of longer segments: four waves on one 64-row block
+    ksplit = p["key_split"] == 4
+    assert ksplit == (dims[0] <= 80 and max_q > 64 and 8 * -(-batch * heads // 8) * -(-max_q // 64) <= 512)
     # head groups only where every segment is one q-tile (or packed)
     hs = ((_short_head_group_shift(dims[0], dims[1], heads, batch) if short
            else _head_group_shift(dims[0], dims[1], heads)) if max_q <= p["block_m"] else 0)
     bm = p["block_m"]
     pack = p["segments_per_block"]
-    assert short == (max_q <= 64 and dims[0] <= 80)
+    assert short == ((max_q <= 64 or ksplit) and dims[0] <= 80)
     assert pack == (1 if short else 4 if max_q <= 64 else 2 if max_q <= 128 else 1)
     assert (bm, p["threads"]) == (64, 256) if short else (256, 256)
     # one-wave units, four to a workgroup, for the short-segment kernel
     assert p["units"] % 8 == 0
-    assert p["grid"] == ((p["units"] // 8 + 3) // 4 * 8 if short else p["units"])
+    assert p["grid"] == ((p["units"] // 8 + 3) // 4 * 8 if short and not ksplit else p["units"])
     if pack > 1:
         # short segments: block owns segments [b, b + pack) of one head, q-tile 0
         seen = {}
@@ -690,9 +701,13 @@ def test_pack_mode_choice(heads, heads_k, max_q, mode):
     take the one-wave short-segment kernel instead (no packing, pack_mode 0)
     where the head dims have it (<= 80); fp8 and d 128 keep the packing."""
     short = mode == 1 and max_q <= 64
+    # unpacked and too small for the CUs (5 x heads units of 256 rows < 256):
+    # four waves split each 64-row block's keys on the short-segment kernel
+    ksplit = mode in (0, 1) and max_q > 64 and 8 * -(-5 * heads // 8) * -(-max_q // 64) <= 512
     p = pkg.plan(64, 64, 5, heads, max_q, max_q, 0, num_heads_k=heads_k)
     assert p["pack_mode"] == (0 if short else mode)
-    assert p["kernel"] == ("attn_fwd_short" if short else "attn_fwd_wide")
+    assert p["kernel"] == ("attn_fwd_short" if short or ksplit else "attn_fwd_wide")
+    assert p["key_split"] == (4 if ksplit else 1)
     assert pkg.plan(128, 128, 5, heads, max_q, max_q, 0, num_heads_k=heads_k)["pack_mode"] == mode
     assert pkg.plan(64, 64, 5, heads, max_q, max_q, 0, fp8=True, num_heads_k=heads_k)["pack_mode"] == mode
 

@@ -478,29 +478,34 @@ def test_split_kv_auto_count_and_grouped_heads():
 
 @pytest.mark.parametrize("dims", DIMS, ids=lambda d: "d%d_%d" % d)
 @pytest.mark.parametrize("mode", ["full", "causal", "window", "left_only"])
-@pytest.mark.parametrize("lens", ["le64", "le128", "q_lt_k"])
+@pytest.mark.parametrize("lens", ["le64", "le128", "le128_small", "q_lt_k"])
 def test_packed_short_segments(dims, mode, lens):
     """Short segments share workgroups (four per workgroup when every segment
     has at most 64 queries, two when at most 128), each wave or pair of waves
     on its own segment whose keys start anywhere inside the workgroup's key
     tiles; at most 64 queries with head dims <= 80 take the one-wave
-    short-segment kernel instead.  Against the oracle with ragged lengths,
-    empty segments, a partial last group and q < k, with and without an
-    LSE; rows outside every segment stay untouched."""
+    short-segment kernel instead, and at most 128 queries on a launch too
+    small for the CUs (3 heads) the same kernel with its waves splitting each
+    64-row block's keys.  Against the oracle with ragged lengths, empty
+    segments, a partial last group and q < k, with and without an LSE; rows
+    outside every segment stay untouched."""
     causal, window = MODES[mode]
-    lq, lk = {
-        "le64": ([1, 64, 0, 37, 64, 5, 63, 2, 50], None),
-        "le128": ([128, 1, 65, 100, 0, 127, 3], None),
-        "q_lt_k": ([40, 64, 1, 17, 64], [300, 64, 90, 0, 77]),
+    lq, lk, heads = {
+        "le64": ([1, 64, 0, 37, 64, 5, 63, 2, 50], None, 3),
+        "le128": ([128, 1, 65, 100, 0, 127, 3], None, 40),  # 7 x 40 units: packed two a workgroup
+        "le128_small": ([128, 1, 65, 100, 0, 127, 3], None, 3),
+        "q_lt_k": ([40, 64, 1, 17, 64], [300, 64, 90, 0, 77], 3),
     }[lens]
     lk = lq if lk is None else lk
     seed = zlib.crc32(repr(("packed", dims, mode, lens)).encode()) % 1000
-    inp = workloads.make_inputs(lq, lk, 3, dims[0], dims[1], seed=seed, causal=causal, window=window)
-    pl = va.plan(dims[0], dims[1], len(lq), 3, max(lq), max(lk), causal)
-    short = max(lq) <= 64 and dims[0] <= 80
+    inp = workloads.make_inputs(lq, lk, heads, dims[0], dims[1], seed=seed, causal=causal, window=window)
+    pl = va.plan(dims[0], dims[1], len(lq), heads, max(lq), max(lk), causal)
+    ksplit = dims[0] <= 80 and max(lq) > 64 and 8 * -(-len(lq) * heads // 8) * 2 <= 512
+    short = (max(lq) <= 64 or ksplit) and dims[0] <= 80
     assert pl["kernel"] == ("attn_fwd_short" if short else "attn_fwd_wide")
+    assert pl["key_split"] == (4 if ksplit else 1)
     assert pl["segments_per_block"] == (1 if short else 4 if max(lq) <= 64 else 2)
-    sentinel = torch.full((inp.q.shape[0] + 30, 3, dims[1]), 3.0, dtype=torch.bfloat16, device=DEV)
+    sentinel = torch.full((inp.q.shape[0] + 30, heads, dims[1]), 3.0, dtype=torch.bfloat16, device=DEV)
     out, lse = run_gpu(inp, out=sentinel[: inp.q.shape[0]])
     assert torch.all(sentinel[inp.q.shape[0]:] == 3.0)
     ref_o, ref_lse = oracle_on(inp)
@@ -525,9 +530,10 @@ def test_short_kernel_bit_equal_to_unpacked(dims, mode, lens):
     (segment, head) on the short-segment kernel, whose arithmetic per key
     tile is the four-wave kernel's: O and LSE are bit-identical to the
     four-wave kernel's unpacked launch of the same call (max_seqlen_q passed
-    as 300), with the fp32 row sum (LSE returned) and the ones-column sum (no
-    LSE), and with e4m3 output; and within the oracle's tolerance.  Eight
-    heads, so d 72 and 80 deal heads in groups (8 and 4)."""
+    as 4096: enough 256-row units that the launch is not split by keys), with
+    the fp32 row sum (LSE returned) and the ones-column sum (no LSE), and
+    with e4m3 output; and within the oracle's tolerance.  Eight heads, so
+    d 72 and 80 deal heads in groups (8 and 4)."""
     causal, window = MODES[mode]
     lq, lk = SHORT_LENS[lens]
     lk = lq if lk is None else lk
@@ -535,7 +541,7 @@ def test_short_kernel_bit_equal_to_unpacked(dims, mode, lens):
     seed = zlib.crc32(repr(("short", dims, mode, lens)).encode()) % 1000
     inp = workloads.make_inputs(lq, lk, heads, dims[0], dims[1], seed=seed, causal=causal, window=window)
     assert va.plan(dims[0], dims[1], len(lq), heads, max(lq), max(lk), causal)["kernel"] == "attn_fwd_short"
-    assert va.plan(dims[0], dims[1], len(lq), heads, 300, max(lk), causal)["kernel"] == "attn_fwd_wide"
+    assert va.plan(dims[0], dims[1], len(lq), heads, 4096, max(lk), causal)["kernel"] == "attn_fwd_wide"
     d = inp.to(DEV)
 
     def call(max_q, return_lse, out_scale=None):
@@ -546,18 +552,73 @@ def test_short_kernel_bit_equal_to_unpacked(dims, mode, lens):
         return res if return_lse else (res, None)
 
     out, lse = call(inp.max_seqlen_q, True)
-    out_w, lse_w = call(300, True)
+    out_w, lse_w = call(4096, True)
     assert torch.equal(out, out_w) and torch.equal(lse, lse_w)
     ref_o, ref_lse = oracle_on(inp)
     assert_parity(out, lse, ref_o, ref_lse, what="short/%s/%s/%s" % (dims, mode, lens))
     out, _ = call(inp.max_seqlen_q, False)
-    out_w, _ = call(300, False)
+    out_w, _ = call(4096, False)
     assert torch.equal(out, out_w)
     assert_parity(out, None, ref_o, None, what="short-nolse")
     sc = torch.tensor([0.01], dtype=torch.float32, device=DEV)
     out, _ = call(inp.max_seqlen_q, False, sc)
-    out_w, _ = call(300, False, sc)
+    out_w, _ = call(4096, False, sc)
     assert torch.equal(out.view(torch.uint8), out_w.view(torch.uint8))
+
+
+KEY_SPLIT_LENS = {
+    "one_257": ([257], None, 16),
+    "one_1024": ([1024], None, 16),
+    "tiny_64_256": ([64, 256], None, 16),
+    "ragged": ([300, 1, 700, 129, 0, 65], [300, 40, 900, 129, 7, 0], 3),
+    "q_lt_k": ([130, 200], [2000, 333], 16),
+}
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (72, 72), (80, 80)], ids=lambda d: "d%d_%d" % d)
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("lens", list(KEY_SPLIT_LENS))
+def test_key_split_small_launches(dims, mode, lens):
+    """Launches of segments longer than 64 queries with too few 256-row units
+    for the CUs run the short-segment kernel with a workgroup's four waves on
+    one 64-row block, each over a quarter of its key tiles, merged through
+    LDS: against the oracle with the LSE, without it (d 72 / 80: the
+    ones-column row sum) and with e4m3 output, and against the four-wave
+    kernel (max_seqlen_q passed as 4096) within the same tolerance.  Empty
+    segments, a segment without keys, key ranges shorter than four tiles
+    (waves with nothing to do) and masks that leave a wave's rows no key."""
+    causal, window = MODES[mode]
+    lq, lk, heads = KEY_SPLIT_LENS[lens]
+    lk = lq if lk is None else lk
+    p = va.plan(dims[0], dims[1], len(lq), heads, max(lq), max(lk), causal)
+    assert (p["kernel"], p["key_split"]) == ("attn_fwd_short", 4)
+    seed = zlib.crc32(repr(("ksplit", dims, mode, lens)).encode()) % 1000
+    inp = workloads.make_inputs(lq, lk, heads, dims[0], dims[1], seed=seed, causal=causal, window=window)
+    d = inp.to(DEV)
+
+    def call(max_q, return_lse, out_scale=None):
+        res = va.varlen_attn_fwd(d.q, d.k, d.v, d.cu_seqlens_q, d.cu_seqlens_k, max_q, inp.max_seqlen_k,
+                                 softmax_scale=inp.softmax_scale, causal=causal, window_size=window,
+                                 return_lse=return_lse, out_scale=out_scale)
+        torch.cuda.synchronize()
+        return res if return_lse else (res, None)
+
+    ref_o, ref_lse = oracle_on(inp)
+    out, lse = call(inp.max_seqlen_q, True)
+    assert_parity(out, lse, ref_o, ref_lse, what="ksplit/%s/%s/%s" % (dims, mode, lens))
+    assert va.plan(dims[0], dims[1], len(lq), heads, 4096, max(lk), causal)["key_split"] == 1
+    out_w, lse_w = call(4096, True)
+    assert_parity(out_w, lse_w, ref_o, ref_lse, what="wide/%s/%s/%s" % (dims, mode, lens))
+    out, _ = call(inp.max_seqlen_q, False)
+    assert_parity(out, None, ref_o, None, what="ksplit-nolse")
+    sc = torch.tensor([0.01], dtype=torch.float32, device=DEV)
+    out8, _ = call(inp.max_seqlen_q, False, sc)
+    out8w, _ = call(4096, False, sc)
+    # e4m3 codes of O / 0.01: the two kernels' O differ by rounding, so their
+    # decoded values agree to an e4m3 step of the larger (2^-3 relative)
+    a = out8.view(torch.float8_e4m3fn).float() * 0.01
+    b = out8w.view(torch.float8_e4m3fn).float() * 0.01
+    assert torch.all((a - b).abs() <= 0.125 * torch.maximum(a.abs(), b.abs()) + 2e-3)
 
 
 def test_short_kernel_strided_views():
@@ -781,9 +842,12 @@ def test_packed_query_heads(dims, heads, heads_k, lens, mode):
     out, lse = run_gpu(inp)
     ref_o, ref_lse = oracle_on(inp)
     assert_parity(out, lse, ref_o, ref_lse, what="packed heads %s %d/%d %s %s" % (dims, heads, heads_k, lens, mode))
-    # the same call with a looser max_seqlen_q runs unpacked: same rows, same tiles, same bits
+    # the same call with a looser max_seqlen_q runs unpacked on the four-wave
+    # kernel (4096: enough 256-row units that the launch is not split by
+    # keys): same rows, same tiles, same bits
     import dataclasses
-    out2, lse2 = run_gpu(dataclasses.replace(inp, max_seqlen_q=129 if hi == 128 else 257))
+    assert va.plan(dims[0], dims[1], len(lq), heads, 4096, max(lk), causal, num_heads_k=heads_k)["key_split"] == 1
+    out2, lse2 = run_gpu(dataclasses.replace(inp, max_seqlen_q=4096))
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 

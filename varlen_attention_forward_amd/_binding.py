@@ -77,6 +77,7 @@ class VaPlan(ctypes.Structure):
         ("pack_mode", ctypes.c_int32),
         ("units", ctypes.c_int64),
         ("pair_q_tiles", ctypes.c_int32),
+        ("key_split", ctypes.c_int32),
     ]
 
 
@@ -221,6 +222,7 @@ def plan(head_dim_qk, head_dim_v, batch, num_heads, max_seqlen_q, max_seqlen_k, 
         "pack_mode": pl.pack_mode,
         "units": pl.units,
         "pair_q_tiles": pl.pair_q_tiles,
+        "key_split": pl.key_split,
     }
 
 

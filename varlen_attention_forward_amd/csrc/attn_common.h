@@ -67,6 +67,9 @@ struct Params {
   // segment (n_b = ceil(Lq / block_m)), so that every workgroup of a causal
   // launch has the same number of key tiles; n_qt then counts pairs.
   int32_t pair_qt;
+  // attn_fwd_short on small launches: the waves of a workgroup that share one
+  // work unit (64 query rows) and split its key tiles (1: a unit per wave).
+  int32_t key_split;
   float* part_o;    // [num_splits, total_q, heads, d_v]
   float* part_lse;  // [num_splits, heads, total_q]
   int32_t causal, wl, wr;
@@ -294,6 +297,7 @@ struct Variant {
   const char* name;
   int per_cu;  // workgroups a compute unit holds at once (the launch bounds' minimum)
   int units_per_wg;  // work units a workgroup holds (its waves' own units; 1 but for attn_fwd_short)
+  int key_split = 1;  // waves that split one unit's key tiles (attn_fwd_short on small launches: 4)
 };
 
 // The fp8 e4m3 kernel (varlen_attn_fwd_fp8.hip): whether it has an
@@ -304,5 +308,8 @@ Variant fp8_variant(int dqk, int dv, int pack_mode);
 // has, and its variant (lse: whether the call returns the LSE).
 bool short_supported(int dqk, int dv);
 Variant short_variant(int dqk, int dv, bool lse);
+// The same kernel with a workgroup's four waves on one unit, each taking a
+// quarter of its key tiles (launches too small to fill the CUs otherwise).
+Variant short_key_split_variant(int dqk, int dv, bool lse);
 
 }  // namespace va

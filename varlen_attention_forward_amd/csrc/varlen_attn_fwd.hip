@@ -886,16 +886,30 @@ static Variant variant_for(int dqk, int dv, int32_t pk, bool lse = true) {
 // queries that would be packed four to a workgroup (no grouped query heads
 // to pack instead) take the short-segment kernel, one wave per (segment,
 // head), four such units a workgroup, when the head dims have it and the
-// call is not split.
+// call is not split.  Launches of longer segments (unpacked, or up to 128
+// queries packed two to a workgroup) whose 64-row blocks fit one round of
+// that kernel on every XCD (the padded grid, whose eighth is an XCD's share,
+// at most kKeySplitMaxUnits: two workgroups on each of an XCD's 32 CUs) take
+// the short-segment kernel with a workgroup's four waves on one 64-row block,
+// each walking a quarter of its key tiles (Params::key_split): a quarter of
+// the key loop on the path that sets the time.  Past one round the four-wave
+// kernel is faster (3 x 1024 queries x 16 heads: 25 against 30 us; 1 x 8192
+// x 4 heads, whose 4 (segment, head) groups fill only 4 XCDs: 182 against
+// 238 us).
 struct LaunchChoice {
   Variant var;
   int32_t mode;
 };
+static constexpr int64_t kKeySplitMaxUnits = 8 * 2 * 32;  // 8 XCDs x one round of two workgroups on 32 CUs
 static LaunchChoice choose_launch(int dqk, int dv, int64_t max_seqlen_q, int64_t heads, int64_t heads_k, bool lse,
-                                  bool split, bool segment_packing = true) {
+                                  bool split, int64_t batch, bool segment_packing = true) {
   const int32_t mode = launch_mode(max_seqlen_q, heads, heads_k, segment_packing);
   if (!split && mode == kPackSegments && max_seqlen_q <= wide::kRowsPerWave && short_supported(dqk, dv))
     return {short_variant(dqk, dv, lse), (int32_t)kPackNone};
+  const int64_t bm = wide::kRowsPerWave;  // the short kernel's rows a unit
+  if (!split && (mode == kPackNone || mode == kPackSegments) && max_seqlen_q > wide::kRowsPerWave &&
+      short_supported(dqk, dv) && grid_blocks(batch, heads, (max_seqlen_q + bm - 1) / bm) <= kKeySplitMaxUnits)
+    return {short_key_split_variant(dqk, dv, lse), (int32_t)kPackNone};
   return {variant_for(dqk, dv, mode, lse), mode};
 }
 
@@ -1026,7 +1040,8 @@ extern "C" int varlen_attn_work_unit(int64_t block, int32_t batch, int32_t num_h
     max_q = seqlens_q[i] > max_q ? seqlens_q[i] : max_q;
   }
   if (max_q <= 0) return VA_ERR_ARG;
-  const va::LaunchChoice lc = va::choose_launch(head_dim_qk, head_dim_v, max_q, num_heads, num_heads_k, true, false);
+  const va::LaunchChoice lc =
+      va::choose_launch(head_dim_qk, head_dim_v, max_q, num_heads, num_heads_k, true, false, batch);
   const int32_t mode = lc.mode;
   const va::Variant var = lc.var;
   const int32_t hs = va::launch_hs(head_dim_qk, head_dim_v, num_heads, num_heads_k, mode, false, max_q, var, batch);
@@ -1072,7 +1087,7 @@ extern "C" int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t
   if (batch < 0 || num_heads <= 0 || max_seqlen_q < 0) return VA_ERR_ARG;
   if (num_heads_k <= 0 || num_heads % num_heads_k != 0) return VA_ERR_ARG;
   const va::LaunchChoice lc =
-      va::choose_launch(head_dim_qk, head_dim_v, max_seqlen_q, num_heads, num_heads_k, true, false);
+      va::choose_launch(head_dim_qk, head_dim_v, max_seqlen_q, num_heads, num_heads_k, true, false, batch);
   const int32_t mode = lc.mode;
   const va::Variant var = lc.var;
   plan->block_m = var.block_m;
@@ -1088,6 +1103,7 @@ extern "C" int varlen_attn_plan(int32_t head_dim_qk, int32_t head_dim_v, int32_t
   plan->pack_mode = mode;
   plan->kernel = var.name;
   plan->pair_q_tiles = pair ? 1 : 0;
+  plan->key_split = var.key_split;
   return VA_OK;
 }
 
@@ -1115,6 +1131,7 @@ extern "C" int varlen_attn_plan_fp8(int32_t head_dim_qk, int32_t head_dim_v, int
   plan->pack_mode = mode;
   plan->kernel = var.name;
   plan->pair_q_tiles = 0;
+  plan->key_split = 1;
   return VA_OK;
 }
 
@@ -1178,6 +1195,7 @@ static int prepare(const va_tensor* q, const va_tensor* k, const va_tensor* v, c
   p.num_splits = 1;
   p.splits_dyn = nullptr;
   p.pair_qt = 0;
+  p.key_split = 1;
   p.part_o = nullptr;
   p.part_lse = nullptr;
   p.q_descale = p.k_descale = p.v_descale = p.out_scale = nullptr;
@@ -1195,7 +1213,7 @@ static int launch_attention(Params& p, int32_t head_dim_qk, int32_t head_dim_v, 
     var = fp8_variant(head_dim_qk, head_dim_v, mode);
   } else {
     const LaunchChoice lc = choose_launch(head_dim_qk, head_dim_v, max_seqlen_q, p.heads, p.heads_k, fp32_row_sum,
-                                          p.num_splits > 1, p.splits_dyn == nullptr);
+                                          p.num_splits > 1, p.batch, p.splits_dyn == nullptr);
     var = lc.var;
     mode = lc.mode;
   }
@@ -1203,6 +1221,7 @@ static int launch_attention(Params& p, int32_t head_dim_qk, int32_t head_dim_v, 
   const bool pair = pair_q_tiles(p.causal != 0, mode, var, p.batch, p.heads, max_seqlen_q, hs,
                                  p.num_splits > 1 || p.splits_dyn != nullptr, fp8);
   p.pair_qt = pair ? 1 : 0;
+  p.key_split = var.key_split;
   const int64_t units = launch_units(p.batch, p.heads, max_seqlen_q, var.block_m, mode, hs, &p.n_qt, &p.pack, pair);
   if (units > INT32_MAX) return VA_ERR_SHAPE;
   p.n_units = (int32_t)units;

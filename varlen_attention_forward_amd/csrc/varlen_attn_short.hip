@@ -64,8 +64,14 @@ __global__ __launch_bounds__(64 * narrow::kWaves, 2) void attn_fwd_short(Params 
   const int l32 = lane & 31;
   const int g = lane >> 5;
   // This wave's work unit: workgroup w's wave v takes unit ((w >> 3) kWaves
-  // + v) x 8 + (w & 7), on the XCD (w % 8) the unit's dealing intends.
-  const int64_t unit = ((int64_t)(blockIdx.x >> 3) * kWaves + wave) * 8 + (blockIdx.x & 7);
+  // + v) x 8 + (w & 7), on the XCD (w % 8) the unit's dealing intends.  On
+  // small launches (Params::key_split) the four waves share unit w instead,
+  // each with a quarter of its key tiles, and merge their partial results
+  // through LDS before wave 0 writes them out; the early exits below are then
+  // the whole workgroup's, so every wave meets the merge's barriers.
+  const bool ksplit = p.key_split > 1;
+  const int64_t unit =
+      ksplit ? (int64_t)blockIdx.x : ((int64_t)(blockIdx.x >> 3) * kWaves + wave) * 8 + (blockIdx.x & 7);
   const BlockWork bw = block_work<kPackNone>(p, lane, C::RPW, unit);
   if (!bw.u.valid) return;
   const int h = bw.u.h;
@@ -73,7 +79,8 @@ __global__ __launch_bounds__(64 * narrow::kWaves, 2) void attn_fwd_short(Params 
   const int r0 = bw.u.qt * C::RPW;
   if (r0 >= Lq) return;
   const int r1 = min(r0 + C::RPW, Lq);
-  const TileRange tr = tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN);
+  const TileRange tr_unit = tile_range(Lq, Lk, r0, r1, p.causal, p.wl, p.wr, kBN);
+  const TileRange tr = ksplit ? split_range(tr_unit, wave, kWaves) : tr_unit;  // this wave's tiles
   const int ntiles = tr.kt_end - tr.kt_begin;
 
   // ---- Q fragments (B operand of S^T = K Q^T): rows [r0, r1), zero past r1
@@ -404,10 +411,83 @@ __global__ __launch_bounds__(64 * narrow::kWaves, 2) void attn_fwd_short(Params 
     });
   }
 
-  // ---- epilogue (as the four-wave kernel's) -----------------------------------
   // With SUM_BY_MFMA the row sum sits in column d_v of the accumulator:
   // dv block VB - 1, register 4 * ((d_v % 32) / 8), lanes 0-31.
   constexpr int kSumReg = 4 * ((DV % 32) / 8);
+
+  // ---- merge of the key-split waves (small launches) --------------------------
+  // Wave w holds (m_w, l_w, acc_w) over its keys, with p = exp2(s c - m_w).
+  // With M = max_w m_w and f_w = exp2(m_w - M) (0 for a wave that saw no
+  // key), the unit's state is (M, sum_w f_w l_w, sum_w f_w acc_w).  The
+  // stages are free once every wave has left its loop: the m and l of all
+  // waves go through vs1 + 8 KB, then one d_v block of acc at a time through
+  // vs0 (waves 1, 2) and vs1 (wave 3), 8 KB a wave, summed by wave 0.
+  if (ksplit) {
+    static_assert(kWaves == 4 && kWaves * C::V_TILE >= 16384, "merge layout: 2 x 8 KB in vs0, 8 + 4 KB in vs1");
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) float lds_f32;
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    lds_f32* ml = (lds_f32*)((lds_char*)vs1 + 8192);  // [wave][qb][m, l][lane]
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      ml[((wave * QB + qb) * 2 + 0) * 64 + lane] = m_run[qb];
+      ml[((wave * QB + qb) * 2 + 1) * 64 + lane] = SUM_BY_MFMA ? 0.f : xhalf_sum(l_run[qb]);
+    }
+    lds_barrier();
+    float f[QB], m_all[QB], l_all[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mw[kWaves];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) mw[w] = ml[((w * QB + qb) * 2 + 0) * 64 + lane];
+      m_all[qb] = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+      l_all[qb] = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        if (mw[w] != -INFINITY)
+          l_all[qb] += ml[((w * QB + qb) * 2 + 1) * 64 + lane] * __builtin_amdgcn_exp2f(mw[w] - m_all[qb]);
+      f[qb] = m_run[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m_all[qb]);
+    }
+    lds_f32x4* slot = (lds_f32x4*)(wave == 3 ? (lds_char*)vs1 : (lds_char*)vs0 + (wave == 2 ? 8192 : 0));
+#pragma unroll
+    for (int vb = 0; vb < C::VB; ++vb) {
+      if (wave > 0) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x16& a = acc[vb][qb];
+            const f32x4 x = {a[4 * r4] * f[qb], a[4 * r4 + 1] * f[qb], a[4 * r4 + 2] * f[qb], a[4 * r4 + 3] * f[qb]};
+            slot[(qb * 4 + r4) * 64 + lane] = x;
+          }
+      }
+      lds_barrier();
+      if (wave == 0) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int e = (qb * 4 + r4) * 64 + lane;
+            const f32x4 x1 = ((lds_f32x4*)vs0)[e], x2 = ((lds_f32x4*)((lds_char*)vs0 + 8192))[e],
+                        x3 = ((lds_f32x4*)vs1)[e];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              acc[vb][qb][4 * r4 + t] = acc[vb][qb][4 * r4 + t] * f[qb] + ((x1[t] + x2[t]) + x3[t]);
+          }
+      }
+      lds_barrier();
+    }
+    if (wave != 0) return;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      m_run[qb] = m_all[qb];
+      l_run[qb] = g == 0 ? l_all[qb] : 0.f;  // the epilogue's xhalf_sum gives l_all
+    }
+  }
+
+  // ---- epilogue (as the four-wave kernel's) -----------------------------------
   if (p.out_scale != nullptr) {
     const float os = 1.f / *p.out_scale;
 #pragma unroll
@@ -482,6 +562,13 @@ Variant short_variant(int dqk, int dv, bool lse) {
   if (dqk == 64) return short_variant_of<64, 64, F>();
   if (dqk == 72) return lse ? short_variant_of<72, 72, F>() : short_variant_of<72, 72, M>();
   return lse ? short_variant_of<80, 80, F>() : short_variant_of<80, 80, M>();
+}
+
+Variant short_key_split_variant(int dqk, int dv, bool lse) {
+  Variant v = short_variant(dqk, dv, lse);
+  v.units_per_wg = 1;
+  v.key_split = narrow::kWaves;
+  return v;
 }
 
 }  // namespace va

@@ -514,16 +514,27 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20, r
         pl = __import__("varlen_attention_forward_amd").plan(
             w.head_dim_qk, w.head_dim_v, w.batch, w.num_heads, w.max_seqlen_q, w.max_seqlen_k, w.causal,
             fp8=w.dtype == "e4m3", num_heads_k=w.heads_k)
-        # the same call with max_seqlen_q = 257: unpacked on the four-wave kernel, for comparison
+        # the same call unpacked on the four-wave kernel, for comparison: a looser
+        # max_seqlen_q (257, or 4096 where 257 still leaves a launch small
+        # enough for the short kernel's key split)
+        unpacked_q = None
         if pl["pack_mode"] != 0 or pl["kernel"] == "attn_fwd_short":
+            for mq in (257, 4096):
+                p2 = __import__("varlen_attention_forward_amd").plan(
+                    w.head_dim_qk, w.head_dim_v, w.batch, w.num_heads, mq, w.max_seqlen_k, w.causal,
+                    num_heads_k=w.heads_k)
+                if p2["kernel"] == "attn_fwd_wide" and p2["pack_mode"] == 0:
+                    unpacked_q = mq
+                    break
+        if unpacked_q is not None:
             times = []
             for _ in range(rounds):
                 for i in range(warmup):
-                    launch(copies, i, ns, 257)
+                    launch(copies, i, ns, unpacked_q)
                 torch.cuda.synchronize()
                 ev0.record(stream)
                 for i in range(timed):
-                    launch(copies, i, ns, 257)
+                    launch(copies, i, ns, unpacked_q)
                 ev1.record(stream)
                 torch.cuda.synchronize()
                 times.append(ev0.elapsed_time(ev1) / timed)
@@ -564,6 +575,8 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20, r
         if unpacked is not None:
             row["pack_mode"] = pl["pack_mode"]
             row["kernel"] = pl["kernel"]
+            row["key_split"] = pl["key_split"]
+            row["unpacked_max_seqlen_q"] = unpacked_q
             row["unpacked_kernel_ms_best"] = round(unpacked, 4)
             row["unpacked_tflops_best"] = round(flops / unpacked / 1e9, 2)
         if unsplit is not None:

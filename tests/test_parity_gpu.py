@@ -688,6 +688,7 @@ GRAPH_CASES = {
     "wide_d128_causal": (([300, 77, 1029], [300, 500, 1029], 2, 128, 128), dict(seed=21, causal=True), 1),
     "short_d80_windows": (([64, 17, 64, 40, 0, 64] * 4, [64, 17, 64, 40, 0, 64] * 4, 4, 80, 80), dict(seed=22), 1),
     "split4_192_128": (([256, 64], [5000, 3000], 2, 192, 128), dict(seed=23, causal=True), 4),
+    "key_split_d64": (([1024, 300], [1024, 700], 4, 64, 64), dict(seed=24, causal=True), 1),
 }
 
 
@@ -698,7 +699,8 @@ def test_hip_graph_replay_matches_eager(case):
     graph's memory pool), so it can be captured in a HIP graph: three
     replays, with eager calls between them, reproduce the eager O and LSE bit
     for bit (outputs cleared outside the graph first), for the four-wave
-    kernel, the one-wave short-segment kernel and a split-KV call."""
+    kernel, the one-wave short-segment kernel, its key split on a small
+    launch and a split-KV call."""
     args, kw, splits = GRAPH_CASES[case]
     inp = workloads.make_inputs(*args, **kw)
     d = inp.to(DEV)

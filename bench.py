@@ -519,7 +519,7 @@ def protocol_report(names, rounds: int = 10, warmup: int = 5, timed: int = 20, r
         # enough for the short kernel's key split)
         unpacked_q = None
         if pl["pack_mode"] != 0 or pl["kernel"] == "attn_fwd_short":
-            for mq in (257, 4096):
+            for mq in (257, 4096, 16384):
                 p2 = __import__("varlen_attention_forward_amd").plan(
                     w.head_dim_qk, w.head_dim_v, w.batch, w.num_heads, mq, w.max_seqlen_k, w.causal,
                     num_heads_k=w.heads_k)

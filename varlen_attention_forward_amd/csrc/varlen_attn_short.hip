@@ -27,6 +27,13 @@
 // same QK^T accumulation order, fast-path test, slow path, lazy rescale and
 // PV order, the same epilogue.  The output is therefore bit-identical to an
 // unpacked launch of the four-wave kernel on the same call.
+//
+// Small launches of longer segments (Params::key_split = 4) use the same
+// code with the four waves of a workgroup on one 64-row block instead, each
+// walking a quarter of its key tiles; their (max, sum, accumulator) states
+// are merged through LDS before wave 0's epilogue.  That is the same softmax
+// summed in another order: within rounding of the four-wave kernel, not
+// bit-identical to it.
 #include "attn_common.h"
 #include "wide_tile.h"
 

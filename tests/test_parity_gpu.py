@@ -624,14 +624,17 @@ def test_key_split_small_launches(dims, mode, lens):
         assert np.all(err <= 0), "e4m3 O, max_seqlen_q %d: %.3e over" % (max_q, err.max())
 
 
-def test_short_kernel_strided_views():
+@pytest.mark.parametrize("key_split", [1, 4])
+def test_short_kernel_strided_views(key_split):
     """The short-segment kernel on views: Q and K with a padded head stride,
     V inside an interleaved [T, H, 2 x d] buffer, O written into a strided
     view whose padding stays untouched; bit-identical to the contiguous
-    call."""
-    lq = [64, 17, 0, 64, 1, 50, 64, 33]
+    call.  One wave a segment (at most 64 queries), and the key split of a
+    small launch of longer segments."""
+    lq = [64, 17, 0, 64, 1, 50, 64, 33] if key_split == 1 else [300, 17, 0, 700, 1, 129]
     inp = workloads.make_inputs(lq, lq, 4, 80, 80, seed=77, causal=False, window=(20, 5))
-    assert va.plan(80, 80, len(lq), 4, 64, 64, False)["kernel"] == "attn_fwd_short"
+    p = va.plan(80, 80, len(lq), 4, max(lq), max(lq), False)
+    assert (p["kernel"], p["key_split"]) == ("attn_fwd_short", key_split)
     o_ref, l_ref = run_gpu(inp)
     T = inp.q.shape[0]
 

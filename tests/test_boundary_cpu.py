@@ -179,6 +179,40 @@ def test_plan():
         pkg.plan(96, 96, 1, 1, 10, 10)
 
 
+def test_abi_struct_layouts_match_binding(tmp_path):
+    """The structs of include/varlen_attn.h as a C compiler lays them out
+    (offset and size of every field the binding declares, and each struct's
+    size) are the ctypes structures the binding passes across the C ABI."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = {"va_tensor": B.VaTensor, "va_plan": B.VaPlan}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "varlen_attn.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append('  printf("%s - %%zu %%zu\\n", (size_t)0, sizeof(%s));' % (cname, cname))
+        for field, _ in cls._fields_:
+            lines.append('  printf("%s %s %%zu %%zu\\n", offsetof(%s, %s), sizeof(((%s*)0)->%s));'
+                         % (cname, field, cname, field, cname, field))
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    include = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-std=c99", "-I", include, str(src), "-o", str(exe)], check=True)
+    got = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    for line in filter(None, got):
+        cname, field, off, size = line.split()
+        cls = structs[cname]
+        if field == "-":
+            assert int(size) == ctypes.sizeof(cls), cname
+        else:
+            desc = getattr(cls, field)
+            assert (int(off), int(size)) == (desc.offset, desc.size), (cname, field)
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
 
